@@ -1,0 +1,162 @@
+"""Seeded synthetic inputs for the KDN mixer.
+
+This module holds none of the method's arithmetic: it only draws random
+tensors with the shapes and distributions of the mixer workloads, so that the
+HIP path and the fp64 oracle consume identical values.  It imports nothing
+from the rest of the package.
+
+Recipe (per (b,t,h), numpy PCG64, draws in fp32):
+  q, k ~ N(0, I) then L2-normalised over d_k; v ~ N(0, I);
+  alpha = sigmoid(N(2, 0.5)) per key channel (the per-channel decay);
+  omega = softplus(N(0, 1)) per key channel (Diagonal) or per head (Isotropic);
+  r = softplus(N(0, 1)) per head;  S0 = 0, p0 = b0 = 1.
+bf16 workloads round q, k, v to bf16 (round to nearest even) here, so the
+values both sides read are bit-identical; alpha, omega, r stay fp32.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import numpy as np
+
+SEED_BASE = 20260
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    variant: str          # "diag" | "iso"
+    io: str               # "f32" | "bf16"   (dtype of q, k, v and o)
+    B: int
+    H: int
+    T: int
+    dk: int
+    dv: int
+    chunk: int = 64
+    structure: str = "random"   # "random" | "retrieval" | "decode"
+    steps: int = 0              # decode workloads: tokens per sequence
+    seed: int = SEED_BASE
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+
+# The five mixer workloads.  Shapes: 16 heads of width 128 at hidden size
+# 2048 and a 4K context are the shapes of the KDN pre-training runs; the
+# throughput figure on the pages uses d_model 2048 and batch 4.
+WORKLOADS = {
+    0: Workload("diag-f32-B1H2T256-d64", "diag", "f32", 1, 2, 256, 64, 64, 64,
+                seed=SEED_BASE + 0),
+    1: Workload("iso-bf16-B4H16T2048-d128", "iso", "bf16", 4, 16, 2048, 128, 128,
+                seed=SEED_BASE + 1),
+    2: Workload("diag-bf16-B8H16T4096-d128", "diag", "bf16", 8, 16, 4096, 128, 128,
+                seed=SEED_BASE + 2),
+    3: Workload("diag-bf16-B1H16T65536-d128-retrieval", "diag", "bf16", 1, 16, 65536,
+                128, 128, structure="retrieval", seed=SEED_BASE + 3),
+    4: Workload("decode-bf16-B256H16-d128-1024steps", "both", "bf16", 256, 16, 1, 128,
+                128, structure="decode", steps=1024, seed=SEED_BASE + 4),
+}
+
+
+def workload(i: int, **overrides) -> Workload:
+    w = WORKLOADS[i]
+    return replace(w, **overrides) if overrides else w
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returns fp32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    out = ((bits + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
+    return out.view(np.float32)
+
+
+def _sigmoid(x):
+    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+
+
+def _softplus(x):
+    x = x.astype(np.float64)
+    return (np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))).astype(np.float32)
+
+
+def _unit(x, axis=-1):
+    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=axis, keepdims=True))
+    return (x / np.maximum(n, 1e-30)).astype(np.float32)
+
+
+def _draw_tokens(rng, variant, B, T, H, dk, dv, io):
+    f32 = np.float32
+    q = _unit(rng.standard_normal((B, T, H, dk), dtype=f32))
+    k = _unit(rng.standard_normal((B, T, H, dk), dtype=f32))
+    v = rng.standard_normal((B, T, H, dv), dtype=f32)
+    alpha = _sigmoid(2.0 + 0.5 * rng.standard_normal((B, T, H, dk), dtype=f32))
+    wshape = (B, T, H, dk) if variant == "diag" else (B, T, H)
+    omega = _softplus(rng.standard_normal(wshape, dtype=f32))
+    r = _softplus(rng.standard_normal((B, T, H), dtype=f32))
+    return q, k, v, alpha, omega, r
+
+
+def make_fwd_inputs(w: Workload, variant: Optional[str] = None) -> dict:
+    """Forward inputs for workload ``w`` as fp32 numpy arrays (q, k, v already
+    rounded to bf16 when ``w.io == 'bf16'``) plus S0 / p0 (or b0)."""
+    variant = variant or w.variant
+    assert variant in ("diag", "iso")
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    q, k, v, alpha, omega, r = _draw_tokens(rng, variant, B, T, H, dk, dv, w.io)
+    if w.structure == "retrieval":
+        _insert_retrieval(rng, q, k, v, n_pairs=min(512, T // 2))
+    if w.io == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    out = {"q": q, "k": k, "v": v, "alpha": alpha, "omega": omega, "r": r,
+           "S0": np.zeros((B, H, dk, dv), np.float32)}
+    if variant == "diag":
+        out["p0"] = np.ones((B, H, dk), np.float32)
+    else:
+        out["b0"] = np.ones((B, H), np.float32)
+    return out
+
+
+def _insert_retrieval(rng, q, k, v, n_pairs):
+    """Key-value retrieval structure: per (b,h), ``n_pairs`` unit keys with
+    N(0,1) values are written at distinct positions drawn uniformly from
+    [0, T - n_pairs); the last ``n_pairs`` tokens query those keys in a random
+    order.  Everything else keeps the filler distribution."""
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    for b in range(B):
+        for h in range(H):
+            keys = _unit(rng.standard_normal((n_pairs, dk), dtype=np.float32))
+            vals = rng.standard_normal((n_pairs, dv), dtype=np.float32)
+            pos = rng.choice(T - n_pairs, size=n_pairs, replace=False)
+            k[b, pos, h] = keys
+            v[b, pos, h] = vals
+            perm = rng.permutation(n_pairs)
+            q[b, T - n_pairs:, h] = keys[perm]
+
+
+def make_decode_state(w: Workload, variant: str) -> dict:
+    """Seeded random decode state: S0 ~ N(0,1) iid, p0 (or b0) ~ U[0.1, 1]."""
+    rng = np.random.Generator(np.random.PCG64([w.seed, 0 if variant == "diag" else 1]))
+    S0 = rng.standard_normal((w.B, w.H, w.dk, w.dv), dtype=np.float32)
+    if variant == "diag":
+        var0 = rng.uniform(0.1, 1.0, (w.B, w.H, w.dk)).astype(np.float32)
+    else:
+        var0 = rng.uniform(0.1, 1.0, (w.B, w.H)).astype(np.float32)
+    return {"S0": S0, "var0": var0}
+
+
+def make_decode_step(w: Workload, variant: str, step: int) -> dict:
+    """Inputs of one decode step (one token per sequence), [B,H,D], drawn
+    from a per-step seed so any step can be regenerated on its own."""
+    rng = np.random.Generator(np.random.PCG64([w.seed, 2 if variant == "diag" else 3, step]))
+    q, k, v, alpha, omega, r = _draw_tokens(rng, variant, w.B, 1, w.H, w.dk, w.dv, w.io)
+    sq = lambda x: np.ascontiguousarray(x[:, 0])
+    q, k, v, alpha, omega, r = map(sq, (q, k, v, alpha, omega, r))
+    if w.io == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    return {"q": q, "k": k, "v": v, "alpha": alpha, "omega": omega, "r": r}

@@ -1,0 +1,293 @@
+"""fp64 CPU oracle for the Kalman Delta Network (KDN) mixer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
+code with the HIP library (``kalman_delta_rule_amd``) and never imports it.
+
+Contents
+--------
+* ``diag_fwd`` / ``iso_fwd`` / ``step`` -- the token-by-token recurrences of
+  Diagonal and Isotropic KDN, in plain C (``kdn_oracle.c``), fp64, one
+  independent problem per (batch, head).  See that file for the equations and
+  their citations (KDN reading notes, method part, §2, §4, §5, §7).
+* ``dense_kf`` -- the exact dense-covariance Kalman memory (KDN reading notes,
+  method part §2, Eq. (12)-(17)); numpy, fp64, for tiny d_k only.
+* ``mobius_factors`` / ``mobius_fold_left`` / ``mobius_fold_tree`` /
+  ``mobius_apply`` -- the 2x2 Moebius form of the per-channel variance
+  recurrence (KDN reading notes, method part §6, Eq. (32)-(39)), with the
+  ratio-preserving max-abs rescaling the notes describe for Appendix D.
+* ``gated_delta_rule`` -- the textbook delta-rule family
+  S_t = D_t S_{t-1} + beta_t k_t (v_t - (D_t S_{t-1})^T k_t)^T
+  (KDN reading notes, motivation part §1, the unified form and its table).
+
+Inputs may be any float dtype; they are upcast exactly to float64 (bf16 and
+fp32 values are representable in fp64), so the oracle reads the same values
+the GPU reads.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkdn_oracle.so")
+_lib = None
+
+
+def build_oracle(force: bool = True) -> str:
+    """Compile the C oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+             "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"],
+            check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build_oracle(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        for name in ("kdn_oracle_diag_fwd", "kdn_oracle_iso_fwd"):
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = ([ctypes.c_int] * 5 + [dp] * 8 + [ctypes.c_double]
+                           + [dp] * 5 + [ctypes.c_int])
+        lib.kdn_oracle_max_threads.restype = ctypes.c_int
+        lib.kdn_oracle_max_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().kdn_oracle_max_threads())
+
+
+def _f64(x) -> np.ndarray:
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # a torch tensor on the CPU
+        x = x.detach().to("cpu")
+        x = x.double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def diag_fwd(q, k, v, alpha, omega, r, S0=None, p0=None, mu=None,
+             return_gain: bool = False, nthreads: int = 0) -> dict:
+    """Diagonal KDN forward (KDN reading notes, method part §4-§5).
+
+    Shapes: q,k [B,T,H,dk]; v [B,T,H,dv]; alpha, omega [B,T,H,dk]; r [B,T,H];
+    S0 [B,H,dk,dv] or None (zeros); p0 [B,H,dk] or None (ones); mu defaults
+    to dk.  Returns a dict with o [B,T,H,dv], S [B,H,dk,dv], p [B,H,dk] and,
+    with ``return_gain``, kappa and phat [B,T,H,dk].
+    """
+    q, k, v, alpha, omega, r = map(_f64, (q, k, v, alpha, omega, r))
+    S0, p0 = _f64(S0), _f64(p0)
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    assert q.shape == k.shape == alpha.shape == omega.shape
+    assert v.shape == (B, T, H, dv) and r.shape == (B, T, H)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    if p0 is not None:
+        assert p0.shape == (B, H, dk)
+    mu = float(dk if mu is None else mu)
+    o = np.zeros((B, T, H, dv))
+    S = np.zeros((B, H, dk, dv))
+    p = np.zeros((B, H, dk))
+    kap = np.zeros((B, T, H, dk)) if return_gain else None
+    ph = np.zeros((B, T, H, dk)) if return_gain else None
+    rc = _load().kdn_oracle_diag_fwd(
+        B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega),
+        _ptr(r), _ptr(S0), _ptr(p0), mu, _ptr(o), _ptr(S), _ptr(p),
+        _ptr(kap), _ptr(ph), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("kdn_oracle_diag_fwd failed (%d)" % rc)
+    out = {"o": o, "S": S, "p": p}
+    if return_gain:
+        out["kappa"] = kap
+        out["phat"] = ph
+    return out
+
+
+def iso_fwd(q, k, v, alpha, omega, r, S0=None, b0=None, mu=None,
+            return_gain: bool = False, nthreads: int = 0) -> dict:
+    """Isotropic KDN forward (KDN reading notes, method part §7, Eq. (40)).
+
+    omega is [B,T,H]; b0 is [B,H] or None (ones).  Returns o, S, b and, with
+    ``return_gain``, beta and bhat [B,T,H].
+    """
+    q, k, v, alpha, omega, r = map(_f64, (q, k, v, alpha, omega, r))
+    S0, b0 = _f64(S0), _f64(b0)
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    assert q.shape == k.shape == alpha.shape
+    assert omega.shape == (B, T, H) and r.shape == (B, T, H)
+    assert v.shape == (B, T, H, dv)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    if b0 is not None:
+        assert b0.shape == (B, H)
+    mu = float(dk if mu is None else mu)
+    o = np.zeros((B, T, H, dv))
+    S = np.zeros((B, H, dk, dv))
+    b = np.zeros((B, H))
+    beta = np.zeros((B, T, H)) if return_gain else None
+    bh = np.zeros((B, T, H)) if return_gain else None
+    rc = _load().kdn_oracle_iso_fwd(
+        B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega),
+        _ptr(r), _ptr(S0), _ptr(b0), mu, _ptr(o), _ptr(S), _ptr(b),
+        _ptr(beta), _ptr(bh), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("kdn_oracle_iso_fwd failed (%d)" % rc)
+    out = {"o": o, "S": S, "b": b}
+    if return_gain:
+        out["beta"] = beta
+        out["bhat"] = bh
+    return out
+
+
+def step(variant: str, q, k, v, alpha, omega, r, S, var, mu=None) -> dict:
+    """One decode step: the forward recurrence at T = 1 (KDN reading notes,
+    method part §8: scanned training and token-by-token inference are the same
+    recurrence).  q,k,v,alpha: [B,H,D]; omega [B,H,dk] (diag) or [B,H] (iso);
+    r [B,H]; S [B,H,dk,dv]; var = p [B,H,dk] or b [B,H].  Returns o [B,H,dv]
+    and the new S and variance."""
+    t1 = lambda x: None if x is None else _f64(x)[:, None]
+    if variant == "diag":
+        out = diag_fwd(t1(q), t1(k), t1(v), t1(alpha), t1(omega), t1(r),
+                       S0=S, p0=var, mu=mu)
+        return {"o": out["o"][:, 0], "S": out["S"], "var": out["p"]}
+    if variant == "iso":
+        out = iso_fwd(t1(q), t1(k), t1(v), t1(alpha), t1(omega), t1(r),
+                      S0=S, b0=var, mu=mu)
+        return {"o": out["o"][:, 0], "S": out["S"], "var": out["b"]}
+    raise ValueError("variant must be 'diag' or 'iso'")
+
+
+# --------------------------------------------------------------------------
+# Exact dense Kalman memory (test-only reference for tiny d_k)
+# --------------------------------------------------------------------------
+def dense_kf(k, v, q, D, Omega, r, S0, P0):
+    """Exact dense Kalman associative memory, one head, token by token.
+
+    KDN reading notes, method part §2, Eq. (12)-(17):
+      S^ = D S,  P^ = D P D^T + Omega,  delta = v - S^^T k,
+      kappa = P^ k / (r + k^T P^ k),  S = S^ + kappa delta^T,
+      P = (I - kappa k^T) P^,  o = S^T q.
+    k, q: [T,dk]; v: [T,dv]; D, Omega: [T,dk,dk] (full matrices); r: [T];
+    S0 [dk,dv]; P0 [dk,dk].  Returns o [T,dv], S, P, kappa [T,dk],
+    z [T] (= k^T P^ k) and Phat [T,dk,dk].
+    """
+    k, v, q = _f64(k), _f64(v), _f64(q)
+    D, Omega, r = _f64(D), _f64(Omega), _f64(r)
+    S = _f64(S0).copy()
+    P = _f64(P0).copy()
+    T, dk = k.shape
+    dv = v.shape[1]
+    o = np.zeros((T, dv))
+    kap = np.zeros((T, dk))
+    zs = np.zeros(T)
+    Phats = np.zeros((T, dk, dk))
+    eye = np.eye(dk)
+    for t in range(T):
+        Sh = D[t] @ S
+        Ph = D[t] @ P @ D[t].T + Omega[t]
+        delta = v[t] - Sh.T @ k[t]
+        z = float(k[t] @ Ph @ k[t])
+        kappa = Ph @ k[t] / (r[t] + z)
+        S = Sh + np.outer(kappa, delta)
+        P = (eye - np.outer(kappa, k[t])) @ Ph
+        o[t] = S.T @ q[t]
+        kap[t] = kappa
+        zs[t] = z
+        Phats[t] = Ph
+    return {"o": o, "S": S, "P": P, "kappa": kap, "z": zs, "Phat": Phats}
+
+
+# --------------------------------------------------------------------------
+# 2x2 Moebius form of the per-channel variance recurrence
+# --------------------------------------------------------------------------
+def mobius_factors(alpha, omega, u):
+    """M_t = [[alpha^2, omega], [u alpha^2, 1 + u omega]] for each t
+    (KDN reading notes, method part §6, Eq. (32)-(39)).  Returns [T,2,2]."""
+    a2 = _f64(alpha) ** 2
+    w = _f64(omega)
+    u = _f64(u)
+    M = np.empty(a2.shape + (2, 2))
+    M[..., 0, 0] = a2
+    M[..., 0, 1] = w
+    M[..., 1, 0] = u * a2
+    M[..., 1, 1] = 1.0 + u * w
+    return M
+
+
+def _rescale(M):
+    # homogeneous coordinates: dividing by a positive number keeps n/d
+    return M / np.max(np.abs(M))
+
+
+def mobius_fold_left(Ms):
+    """Compose M_T ... M_1 by left-multiplication in token order, rescaling
+    after every product.  Ms: [T,2,2] with Ms[0] the first token."""
+    P = np.eye(2)
+    for M in Ms:
+        P = _rescale(M @ P)
+    return P
+
+
+def mobius_fold_tree(Ms):
+    """Same product as ``mobius_fold_left`` but with a balanced bracketing:
+    the left half's product is applied first, i.e. prod = R @ L."""
+    n = len(Ms)
+    if n == 0:
+        return np.eye(2)
+    if n == 1:
+        return _rescale(np.array(Ms[0], dtype=np.float64))
+    mid = n // 2
+    L = mobius_fold_tree(Ms[:mid])
+    R = mobius_fold_tree(Ms[mid:])
+    return _rescale(R @ L)
+
+
+def mobius_apply(P, x0):
+    """p = n / d for [n; d] = P [x0; 1]."""
+    n = P[0, 0] * x0 + P[0, 1]
+    d = P[1, 0] * x0 + P[1, 1]
+    return n / d
+
+
+# --------------------------------------------------------------------------
+# Textbook delta-rule family
+# --------------------------------------------------------------------------
+def gated_delta_rule(k, v, q, decay, beta, S0):
+    """S_t = D_t S_{t-1} + beta_t k_t (v_t - (D_t S_{t-1})^T k_t)^T,
+    o_t = S_t^T q_t, with D_t = diag(decay_t) (decay [T,dk]; a scalar per
+    token gives Gated DeltaNet, all ones gives DeltaNet).
+    KDN reading notes, motivation part §1 (unified form and model table)."""
+    k, v, q = _f64(k), _f64(v), _f64(q)
+    decay, beta = _f64(decay), _f64(beta)
+    S = _f64(S0).copy()
+    T = k.shape[0]
+    o = np.zeros((T, v.shape[1]))
+    for t in range(T):
+        DS = decay[t][:, None] * S
+        S = DS + beta[t] * np.outer(k[t], v[t] - DS.T @ k[t])
+        o[t] = S.T @ q[t]
+    return {"o": o, "S": S}
