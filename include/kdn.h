@@ -1,0 +1,172 @@
+/*
+ * kdn.h -- C ABI of the MI355X (gfx950) Kalman Delta Network mixer library.
+ *
+ * The library computes the KDN sequence-mixer forward pass in its two
+ * scan-compatible approximations, Diagonal KDN (d_k variance scalars per
+ * head) and Isotropic KDN (one variance scalar per head), and the single-token
+ * decode step.  The method is defined on the KDN reading notes (page
+ * "Kalman Delta Networks: 不确定性感知的关联记忆"), method part:
+ *   - exact filter it approximates: §2, Eq. (12)-(17);
+ *   - Diagonal KDN predict/gain: §4, Eq. (23)-(30);
+ *   - information scaling mu: §5, Eq. (60)-(65) (gain uses the predicted
+ *     variance; mu only shapes the variance carried to the next token);
+ *   - Moebius form of the variance recurrence and the affine memory scan:
+ *     §6, Eq. (32)-(39), with the Appendix D chunking summarised there;
+ *   - Isotropic KDN: §7, Eq. (40) and Appendix C;
+ *   - parameters alpha (decay), omega (process noise), r (observation
+ *     noise) as inputs, and "scanned training == token-by-token inference":
+ *     §8.
+ *
+ * Per token t and head, with D_t = diag(alpha_t):
+ *   Diagonal:  p^ = alpha^2 (.) p + omega;  z = sum_i p^_i k_i^2;
+ *              kappa = p^ (.) k / (r + z);
+ *              p <- p^ / (1 + (mu/r) k (.) k (.) p^)
+ *   Isotropic: a = mean_i alpha_i^2;  b^ = a b + omega;  n = |k|^2;
+ *              kappa = b^ k / (r + b^ n);  b <- b^ / (1 + mu n b^ / (d_k r))
+ *   Memory (both): S <- D S;  delta = v - S^T k;  S <- S + kappa delta^T;
+ *              o = S^T q   (read after this token's write)
+ *
+ * CONVENTIONS (every entry point)
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never frees caller memory and allocates nothing on the forward or step
+ *     paths; scratch space, where a regime needs it, is the caller's
+ *     `workspace`.
+ *   - Layouts are dense row-major:
+ *       activations q,k [B,T,H,dk], v,o [B,T,H,dv] in the io dtype;
+ *       alpha [B,T,H,dk] fp32; omega [B,T,H,dk] (diag) or [B,T,H] (iso) fp32;
+ *       r [B,T,H] fp32; state S [B,H,dk,dv] fp32 (row i = key channel);
+ *       variances p [B,H,dk] (diag) or b [B,H] (iso) fp32.
+ *   - io dtype: KDN_F32 or KDN_BF16 for q, k, v and o.  Gates, state and
+ *     variances are always fp32.  bf16 runs its chunk contractions on bf16
+ *     matrix cores with fp32 accumulation; fp32 runs them in fp32.
+ *   - Supported sizes: dk in {64, 128} for bf16 and dk = 64 for fp32;
+ *     dv a multiple of 64 (bf16) or 32 (fp32), at most 256; B, H >= 1;
+ *     T >= 0; B*H*T and every tensor below 2^31 elements.
+ *   - Pointers to q, k, v, alpha, omega, o, S0/S_T/S and p0/p_T must be
+ *     16-byte aligned.
+ *   - Preconditions (documented, not checked per element): r > 0,
+ *     0 < alpha <= 1, omega >= 0, p0/b0 > 0, mu >= 0, all finite, and within
+ *     every 64-token chunk the product of alpha over the chunk stays above
+ *     1e-30 in every channel (the chunked memory rescales keys by the
+ *     cumulative decay from the chunk start).  Outside them results are
+ *     unspecified (NaN propagates; nothing faults).
+ *   - Validation is synchronous: on any invalid argument the call returns a
+ *     negative status and launches nothing.  Launch failures return
+ *     KDN_ERR_HIP.  Kernel faults surface at the caller's stream
+ *     synchronisation.  Results are asynchronous on `stream`.
+ *   - Results are deterministic run to run (no floating-point atomics).
+ *   - Inputs are never modified, except S and var_state in kdn_step.
+ *   - kdn_last_error_message() returns a thread-local description of the
+ *     last failure on the calling thread.
+ */
+#ifndef KDN_H
+#define KDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDN_OK = 0,
+    KDN_ERR_INVALID_ARG = -1,
+    KDN_ERR_UNSUPPORTED = -2,
+    KDN_ERR_WORKSPACE = -3,
+    KDN_ERR_HIP = -4
+} kdn_status;
+
+typedef enum { KDN_F32 = 0, KDN_BF16 = 1 } kdn_dtype;
+typedef enum { KDN_DIAG = 0, KDN_ISO = 1 } kdn_variant;
+
+/* Bytes of device workspace kdn_diag_fwd / kdn_iso_fwd need for this shape
+ * (0 when the chosen regime needs none).  Returns 0 for invalid shapes too;
+ * the forward call reports those. */
+size_t kdn_fwd_workspace_size(int variant, int B, int T, int H, int dk, int dv,
+                              int io_dtype);
+
+/*
+ * Diagonal KDN forward over T tokens (KDN reading notes, method part §4-§6;
+ * Appendix D chunking).
+ *   q, k   [B,T,H,dk] io dtype       v, o  [B,T,H,dv] io dtype
+ *   alpha  [B,T,H,dk] fp32 decay      omega [B,T,H,dk] fp32 process noise
+ *   r      [B,T,H]    fp32 observation noise
+ *   S0     [B,H,dk,dv] fp32 initial state, or NULL for zeros
+ *   p0     [B,H,dk]    fp32 initial variances, or NULL for ones
+ *   mu     information scale (the pages' default is dk)
+ *   S_T    [B,H,dk,dv] fp32 final state (required)
+ *   p_T    [B,H,dk]    fp32 final variances (required)
+ *   workspace / workspace_bytes: device scratch of at least
+ *     kdn_fwd_workspace_size(...) bytes (may be NULL when that is 0)
+ *   stream: a hipStream_t (NULL = the null stream)
+ * S_T may alias S0 and p_T may alias p0 (the state is read before it is
+ * overwritten); o must not alias any input.
+ */
+kdn_status kdn_diag_fwd(int B, int T, int H, int dk, int dv, int io_dtype, float mu,
+                        const void* q, const void* k, const void* v,
+                        const float* alpha, const float* omega, const float* r,
+                        const float* S0, const float* p0,
+                        void* o, float* S_T, float* p_T,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Isotropic KDN forward (KDN reading notes, method part §7, Eq. (40);
+ * Appendix C).  Same layouts as kdn_diag_fwd except
+ *   omega  [B,T,H] fp32 (one process-noise scalar per head and token)
+ *   b0     [B,H] fp32 initial variance, or NULL for ones
+ *   b_T    [B,H] fp32 final variance (required)
+ */
+kdn_status kdn_iso_fwd(int B, int T, int H, int dk, int dv, int io_dtype, float mu,
+                       const void* q, const void* k, const void* v,
+                       const float* alpha, const float* omega, const float* r,
+                       const float* S0, const float* b0,
+                       void* o, float* S_T, float* b_T,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step, one token per sequence (KDN reading notes, method part
+ * §8: token-by-token inference runs the same recurrence as the scan).
+ *   variant   KDN_DIAG or KDN_ISO
+ *   q, k [B,H,dk], v, o [B,H,dv] io dtype; alpha [B,H,dk] fp32;
+ *   omega [B,H,dk] (diag) or [B,H] (iso) fp32; r [B,H] fp32
+ *   S         [B,H,dk,dv] fp32, read and overwritten in place
+ *   var_state p [B,H,dk] (diag) or b [B,H] (iso) fp32, in place
+ * Equivalent to the forward call with T = 1, S0 = S_T = S and
+ * p0 = p_T = var_state.
+ */
+kdn_status kdn_step(int variant, int B, int H, int dk, int dv, int io_dtype, float mu,
+                    const void* q, const void* k, const void* v,
+                    const float* alpha, const float* omega, const float* r,
+                    float* S, float* var_state, void* o, void* stream);
+
+/*
+ * Gain scan alone (the variance recurrence and Kalman gain without the
+ * memory), exposed for the chunk-parallel regime's tests and diagnostics.
+ * Inputs as in the forward calls (q, v not needed).  Writes
+ *   kappa [B,T,H,dk] fp32 gain (nullable),
+ *   var_T p_T [B,H,dk] (diag) or b_T [B,H] (iso) fp32 (required).
+ * The scan composes the per-channel 2x2 Moebius maps
+ *   M_t = [[alpha^2, omega], [u alpha^2, 1 + u omega]]
+ * (KDN reading notes, method part §6, Eq. (32)-(39)) within 64-token chunks
+ * with a wavefront-level parallel scan, then carries chunk summaries across
+ * chunks with a second scan, then replays each chunk from its entry
+ * variance.  Needs kdn_gain_workspace_size(...) bytes of workspace.
+ */
+size_t kdn_gain_workspace_size(int variant, int B, int T, int H, int dk);
+kdn_status kdn_gain_scan(int variant, int B, int T, int H, int dk, int io_dtype, float mu,
+                         const void* k, const float* alpha, const float* omega,
+                         const float* r, const float* var0,
+                         float* kappa, float* var_T,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+const char* kdn_status_string(int status);
+const char* kdn_last_error_message(void);
+
+/* Library version, e.g. "kdn-mi355x 0.1.0 gfx950". */
+const char* kdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDN_H */

@@ -1,0 +1,168 @@
+"""Python binding of the KDN C ABI (``include/kdn.h``) over torch tensors.
+
+Same entry-point names as the C library.  This layer only checks tensor
+metadata, allocates outputs / workspace with torch (device memory) and passes
+raw pointers plus torch's current HIP stream; every step of the method runs
+in the library's kernels.  Layouts: activations [B,T,H,D], state [B,H,dk,dv],
+variances [B,H,dk] (Diagonal) or [B,H] (Isotropic).
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import KDN_BF16, KDN_DIAG, KDN_F32, KDN_ISO, KdnError  # noqa: F401
+
+
+def _io_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDN_BF16
+    if t.dtype == torch.float32:
+        return KDN_F32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T):
+    L = _lib.lib()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io = _io_code(q)
+    _need(q, "q", (B, T, H, dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, dv), q.dtype, dev)
+    _need(alpha, "alpha", (B, T, H, dk), torch.float32, dev)
+    wshape = (B, T, H, dk) if variant == KDN_DIAG else (B, T, H)
+    _need(omega, "omega", wshape, torch.float32, dev)
+    _need(r, "r", (B, T, H), torch.float32, dev)
+    vshape = (B, H, dk) if variant == KDN_DIAG else (B, H)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if var0 is not None:
+        _need(var0, "p0" if variant == KDN_DIAG else "b0", vshape, torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", (B, T, H, dv), q.dtype, dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _need(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
+    if var_T is None:
+        var_T = torch.empty(vshape, dtype=torch.float32, device=dev)
+    _need(var_T, "var_T", vshape, torch.float32, dev)
+    mu = float(dk if mu is None else mu)
+    ws_bytes = L.kdn_fwd_workspace_size(variant, B, T, H, dk, dv, io)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    fn = L.kdn_diag_fwd if variant == KDN_DIAG else L.kdn_iso_fwd
+    with torch.cuda.device(dev):
+        st = fn(B, T, H, dk, dv, io, mu, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega),
+                _ptr(r), _ptr(S0), _ptr(var0), _ptr(o), _ptr(S_T), _ptr(var_T), _ptr(ws),
+                ws_bytes, _stream(dev))
+    _lib.check(st)
+    return o, S_T, var_T
+
+
+def kdn_diag_fwd(q, k, v, alpha, omega, r, S0=None, p0=None, mu=None, o=None, S_T=None,
+                 p_T=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Diagonal KDN forward.  Returns (o [B,T,H,dv], S_T [B,H,dk,dv], p_T [B,H,dk])."""
+    return _fwd(KDN_DIAG, q, k, v, alpha, omega, r, S0, p0, mu, o, S_T, p_T)
+
+
+def kdn_iso_fwd(q, k, v, alpha, omega, r, S0=None, b0=None, mu=None, o=None, S_T=None,
+                b_T=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Isotropic KDN forward.  Returns (o [B,T,H,dv], S_T [B,H,dk,dv], b_T [B,H])."""
+    return _fwd(KDN_ISO, q, k, v, alpha, omega, r, S0, b0, mu, o, S_T, b_T)
+
+
+def kdn_step(variant: str, q, k, v, alpha, omega, r, S, var_state, mu=None,
+             o=None) -> torch.Tensor:
+    """One decode step; S [B,H,dk,dv] and var_state are updated in place.
+    ``variant`` is "diag" or "iso".  Returns o [B,H,dv]."""
+    L = _lib.lib()
+    var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    io = _io_code(q)
+    _need(q, "q", (B, H, dk), q.dtype, dev)
+    _need(k, "k", (B, H, dk), q.dtype, dev)
+    _need(v, "v", (B, H, dv), q.dtype, dev)
+    _need(alpha, "alpha", (B, H, dk), torch.float32, dev)
+    _need(omega, "omega", (B, H, dk) if var == KDN_DIAG else (B, H), torch.float32, dev)
+    _need(r, "r", (B, H), torch.float32, dev)
+    _need(S, "S", (B, H, dk, dv), torch.float32, dev)
+    _need(var_state, "var_state", (B, H, dk) if var == KDN_DIAG else (B, H), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", (B, H, dv), q.dtype, dev)
+    mu = float(dk if mu is None else mu)
+    with torch.cuda.device(dev):
+        st = L.kdn_step(var, B, H, dk, dv, io, mu, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                        _ptr(omega), _ptr(r), _ptr(S), _ptr(var_state), _ptr(o), _stream(dev))
+    _lib.check(st)
+    return o
+
+
+def kdn_gain_scan(variant: str, k, alpha, omega, r, var0=None, mu=None,
+                  want_kappa: bool = True):
+    """Gain scan alone.  Returns (kappa [B,T,H,dk] fp32 or None, var_T)."""
+    L = _lib.lib()
+    var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
+    B, T, H, dk = k.shape
+    dev = k.device
+    io = _io_code(k)
+    _need(alpha, "alpha", (B, T, H, dk), torch.float32, dev)
+    _need(omega, "omega", (B, T, H, dk) if var == KDN_DIAG else (B, T, H), torch.float32, dev)
+    _need(r, "r", (B, T, H), torch.float32, dev)
+    vshape = (B, H, dk) if var == KDN_DIAG else (B, H)
+    if var0 is not None:
+        _need(var0, "var0", vshape, torch.float32, dev)
+    if not k.is_contiguous():
+        raise ValueError("k must be contiguous")
+    kappa = torch.empty((B, T, H, dk), dtype=torch.float32, device=dev) if want_kappa else None
+    var_T = torch.empty(vshape, dtype=torch.float32, device=dev)
+    mu = float(dk if mu is None else mu)
+    ws_bytes = L.kdn_gain_workspace_size(var, B, T, H, dk)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = L.kdn_gain_scan(var, B, T, H, dk, io, mu, _ptr(k), _ptr(alpha), _ptr(omega),
+                             _ptr(r), _ptr(var0), _ptr(kappa), _ptr(var_T), _ptr(ws),
+                             ws.numel(), _stream(dev))
+    _lib.check(st)
+    return kappa, var_T
+
+
+def kdn_fwd_workspace_size(variant: str, B, T, H, dk, dv, io_dtype: torch.dtype) -> int:
+    var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
+    io = KDN_BF16 if io_dtype == torch.bfloat16 else KDN_F32
+    return int(_lib.lib().kdn_fwd_workspace_size(var, B, T, H, dk, dv, io))
+
+
+def kdn_version() -> str:
+    return _lib.lib().kdn_version().decode()

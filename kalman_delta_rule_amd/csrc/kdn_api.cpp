@@ -1,0 +1,284 @@
+// kdn_api.cpp -- host side of the C ABI declared in include/kdn.h:
+// synchronous argument validation, regime choice and kernel launch.
+// Nothing here allocates device memory or throws across the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "kdn.h"
+#include "kdn_internal.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+kdn_status fail(kdn_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kdn_status ok()
+{
+    g_msg[0] = '\0';
+    return KDN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kMaxElems = (size_t)1 << 31;
+
+// Shape / dtype rules shared by the forward and step calls.
+kdn_status check_common(int B, int T, int H, int dk, int dv, int io, float mu, bool chunked)
+{
+    if (io != KDN_F32 && io != KDN_BF16)
+        return fail(KDN_ERR_INVALID_ARG, "io_dtype must be KDN_F32 (0) or KDN_BF16 (1), got %d", io);
+    if (B < 1 || H < 1 || T < 0)
+        return fail(KDN_ERR_INVALID_ARG, "need B >= 1, H >= 1, T >= 0 (got B=%d T=%d H=%d)", B, T, H);
+    if (!(mu >= 0.f) || !std::isfinite(mu))
+        return fail(KDN_ERR_INVALID_ARG, "mu must be finite and >= 0 (got %g)", (double)mu);
+    if (chunked) {
+        if (io == KDN_BF16) {
+            if (dk != 64 && dk != 128)
+                return fail(KDN_ERR_UNSUPPORTED, "bf16 forward supports dk in {64, 128}, got %d", dk);
+            if (dv <= 0 || dv % 64 != 0 || dv > 256)
+                return fail(KDN_ERR_UNSUPPORTED,
+                            "bf16 forward supports dv a multiple of 64 up to 256, got %d", dv);
+        } else {
+            if (dk != 64)
+                return fail(KDN_ERR_UNSUPPORTED, "fp32 forward supports dk = 64, got %d", dk);
+            if (dv <= 0 || dv % 32 != 0 || dv > 256)
+                return fail(KDN_ERR_UNSUPPORTED,
+                            "fp32 forward supports dv a multiple of 32 up to 256, got %d", dv);
+        }
+    } else {
+        if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+            return fail(KDN_ERR_UNSUPPORTED, "step supports dk, dv in {64, 128}, got %d, %d", dk, dv);
+    }
+    const size_t tokens = (size_t)B * (size_t)(T > 0 ? T : 1) * (size_t)H;
+    const size_t widest = (size_t)(dk > dv ? dk : dv);
+    if (tokens * widest >= kMaxElems || (size_t)B * H * dk * (size_t)dv >= kMaxElems)
+        return fail(KDN_ERR_UNSUPPORTED, "tensor sizes must stay below 2^31 elements");
+    return KDN_OK;
+}
+
+#define KDN_REQUIRE(ptr, name)                                                   \
+    do {                                                                         \
+        if (!(ptr))                                                              \
+            return fail(KDN_ERR_INVALID_ARG, "%s must not be NULL", name);        \
+    } while (0)
+
+#define KDN_ALIGNED(ptr, name)                                                   \
+    do {                                                                         \
+        if ((ptr) && !aligned16(ptr))                                            \
+            return fail(KDN_ERR_INVALID_ARG, "%s must be 16-byte aligned", name); \
+    } while (0)
+
+kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float mu,
+                    const void* q, const void* k, const void* v, const float* alpha,
+                    const float* omega, const float* r, const float* S0, const float* var0,
+                    void* o, float* S_T, float* var_T, void* workspace,
+                    size_t workspace_bytes, void* stream)
+{
+    kdn_status st = check_common(B, T, H, dk, dv, io, mu, true);
+    if (st != KDN_OK)
+        return st;
+    if (T > 0) {
+        KDN_REQUIRE(q, "q");
+        KDN_REQUIRE(k, "k");
+        KDN_REQUIRE(v, "v");
+        KDN_REQUIRE(alpha, "alpha");
+        KDN_REQUIRE(omega, "omega");
+        KDN_REQUIRE(r, "r");
+        KDN_REQUIRE(o, "o");
+    }
+    KDN_REQUIRE(S_T, "S_T");
+    KDN_REQUIRE(var_T, iso ? "b_T" : "p_T");
+    KDN_ALIGNED(q, "q");
+    KDN_ALIGNED(k, "k");
+    KDN_ALIGNED(v, "v");
+    KDN_ALIGNED(alpha, "alpha");
+    if (!iso)
+        KDN_ALIGNED(omega, "omega");
+    KDN_ALIGNED(o, "o");
+    KDN_ALIGNED(S0, "S0");
+    KDN_ALIGNED(S_T, "S_T");
+    if (!iso) {
+        KDN_ALIGNED(var0, "p0");
+        KDN_ALIGNED(var_T, "p_T");
+    }
+    if (var0 && var0 == var_T)
+        return fail(KDN_ERR_INVALID_ARG, "%s must not alias %s", iso ? "b_T" : "p_T",
+                    iso ? "b0" : "p0");
+    if (o && (o == q || o == k || o == v))
+        return fail(KDN_ERR_INVALID_ARG, "o must not alias q, k or v");
+    if (S0 && S0 != S_T) {
+        const char* s0 = reinterpret_cast<const char*>(S0);
+        const char* st_ = reinterpret_cast<const char*>(S_T);
+        const size_t bytes = (size_t)B * H * dk * dv * sizeof(float);
+        if (s0 < st_ + bytes && st_ < s0 + bytes)
+            return fail(KDN_ERR_INVALID_ARG, "S_T must either equal S0 or not overlap it");
+    }
+    const size_t need = kdn_fwd_workspace_size(iso ? KDN_ISO : KDN_DIAG, B, T, H, dk, dv, io);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                    workspace_bytes);
+    (void)workspace;
+
+    kdn::FwdArgs a{q, k, v, alpha, omega, r, S0, var0, o, S_T, var_T, B, T, H, dk, dv, mu};
+    hipError_t e = kdn::launch_chunk_fwd(a, iso, io, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kdn_fwd_workspace_size(int variant, int B, int T, int H, int dk, int dv, int io_dtype)
+{
+    (void)variant;
+    (void)B;
+    (void)T;
+    (void)H;
+    (void)dk;
+    (void)dv;
+    (void)io_dtype;
+    return 0;  // the walk regime keeps every intermediate on chip
+}
+
+kdn_status kdn_diag_fwd(int B, int T, int H, int dk, int dv, int io_dtype, float mu,
+                        const void* q, const void* k, const void* v, const float* alpha,
+                        const float* omega, const float* r, const float* S0, const float* p0,
+                        void* o, float* S_T, float* p_T, void* workspace,
+                        size_t workspace_bytes, void* stream)
+{
+    return fwd_impl(false, B, T, H, dk, dv, io_dtype, mu, q, k, v, alpha, omega, r, S0, p0, o,
+                    S_T, p_T, workspace, workspace_bytes, stream);
+}
+
+kdn_status kdn_iso_fwd(int B, int T, int H, int dk, int dv, int io_dtype, float mu,
+                       const void* q, const void* k, const void* v, const float* alpha,
+                       const float* omega, const float* r, const float* S0, const float* b0,
+                       void* o, float* S_T, float* b_T, void* workspace,
+                       size_t workspace_bytes, void* stream)
+{
+    return fwd_impl(true, B, T, H, dk, dv, io_dtype, mu, q, k, v, alpha, omega, r, S0, b0, o,
+                    S_T, b_T, workspace, workspace_bytes, stream);
+}
+
+kdn_status kdn_step(int variant, int B, int H, int dk, int dv, int io_dtype, float mu,
+                    const void* q, const void* k, const void* v, const float* alpha,
+                    const float* omega, const float* r, float* S, float* var_state, void* o,
+                    void* stream)
+{
+    if (variant != KDN_DIAG && variant != KDN_ISO)
+        return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
+                    variant);
+    const bool iso = variant == KDN_ISO;
+    kdn_status st = check_common(B, 1, H, dk, dv, io_dtype, mu, false);
+    if (st != KDN_OK)
+        return st;
+    KDN_REQUIRE(q, "q");
+    KDN_REQUIRE(k, "k");
+    KDN_REQUIRE(v, "v");
+    KDN_REQUIRE(alpha, "alpha");
+    KDN_REQUIRE(omega, "omega");
+    KDN_REQUIRE(r, "r");
+    KDN_REQUIRE(S, "S");
+    KDN_REQUIRE(var_state, "var_state");
+    KDN_REQUIRE(o, "o");
+    KDN_ALIGNED(S, "S");
+    if (o == q || o == k || o == v)
+        return fail(KDN_ERR_INVALID_ARG, "o must not alias q, k or v");
+    kdn::StepArgs a{q, k, v, alpha, omega, r, S, var_state, o, B, H, dk, dv, mu};
+    hipError_t e = kdn::launch_step(a, iso, io_dtype, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t kdn_gain_workspace_size(int variant, int B, int T, int H, int dk)
+{
+    if (B < 1 || H < 1 || T < 0 || (dk != 64 && dk != 128))
+        return 0;
+    return kdn::gain_workspace_floats(variant == KDN_ISO, B, T, H, dk) * sizeof(float);
+}
+
+kdn_status kdn_gain_scan(int variant, int B, int T, int H, int dk, int io_dtype, float mu,
+                         const void* k, const float* alpha, const float* omega, const float* r,
+                         const float* var0, float* kappa, float* var_T, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    if (variant != KDN_DIAG && variant != KDN_ISO)
+        return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
+                    variant);
+    const bool iso = variant == KDN_ISO;
+    if (io_dtype != KDN_F32 && io_dtype != KDN_BF16)
+        return fail(KDN_ERR_INVALID_ARG, "io_dtype must be KDN_F32 (0) or KDN_BF16 (1), got %d",
+                    io_dtype);
+    if (B < 1 || H < 1 || T < 0)
+        return fail(KDN_ERR_INVALID_ARG, "need B >= 1, H >= 1, T >= 0");
+    if (dk != 64 && dk != 128)
+        return fail(KDN_ERR_UNSUPPORTED, "gain scan supports dk in {64, 128}, got %d", dk);
+    if (!(mu >= 0.f) || !std::isfinite(mu))
+        return fail(KDN_ERR_INVALID_ARG, "mu must be finite and >= 0");
+    if ((size_t)B * (size_t)(T > 0 ? T : 1) * H * dk >= kMaxElems)
+        return fail(KDN_ERR_UNSUPPORTED, "tensor sizes must stay below 2^31 elements");
+    if (T > 0) {
+        KDN_REQUIRE(k, "k");
+        KDN_REQUIRE(alpha, "alpha");
+        KDN_REQUIRE(omega, "omega");
+        KDN_REQUIRE(r, "r");
+    }
+    KDN_REQUIRE(var_T, "var_T");
+    KDN_ALIGNED(alpha, "alpha");
+    if (var0 && var0 == var_T)
+        return fail(KDN_ERR_INVALID_ARG, "var_T must not alias var0");
+    const size_t need = kdn_gain_workspace_size(variant, B, T, H, dk);
+    if (workspace_bytes < need || !workspace)
+        return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                    workspace_bytes);
+    if (!aligned16(workspace))
+        return fail(KDN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    const size_t nchunks = (size_t)(T + 63) / 64;
+    const size_t width = iso ? 1 : (size_t)dk;
+    float* ws = static_cast<float*>(workspace);
+    kdn::GainArgs a{k,     alpha, omega, r, var0, kappa, var_T, ws,
+                    ws + (size_t)B * H * 4 * width * nchunks, B, T, H, dk, mu};
+    hipError_t e = kdn::launch_gain_scan(a, iso, io_dtype, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+const char* kdn_status_string(int status)
+{
+    switch (status) {
+    case KDN_OK:
+        return "KDN_OK";
+    case KDN_ERR_INVALID_ARG:
+        return "KDN_ERR_INVALID_ARG";
+    case KDN_ERR_UNSUPPORTED:
+        return "KDN_ERR_UNSUPPORTED";
+    case KDN_ERR_WORKSPACE:
+        return "KDN_ERR_WORKSPACE";
+    case KDN_ERR_HIP:
+        return "KDN_ERR_HIP";
+    default:
+        return "KDN_ERR_UNKNOWN";
+    }
+}
+
+const char* kdn_last_error_message(void) { return g_msg; }
+
+const char* kdn_version(void) { return "kdn-mi355x 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+// kdn_common.h -- device-side helpers shared by the KDN kernels (gfx950).
+//
+// Matrix-core conventions used throughout (CDNA 16x16 MFMA, wave64):
+//   accumulator D (16x16 fp32, 4 values per lane): lane l holds
+//       D[4*(l>>4) + r][l & 15],  r = 0..3
+//   "NT" operands: A is [16 rows][K], B is [16 rows][K], both with K
+//   contiguous, so that acc[m][n] += sum_k A[m][k] * B[n][k].
+//     bf16 16x16x32: lane l reads A[l&15][8*(l>>4) .. +7]  (one 16-byte read)
+//     bf16 16x16x16: lane l reads A[l&15][4*(l>>4) .. +3]  (one 8-byte read)
+//     fp32 16x16x4:  lane l reads A[l&15][l>>4]
+//   (same pattern for B with its own rows).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// Fast reciprocal (v_rcp_f32, ~1 ulp).
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Order this wave's LDS writes before its later LDS reads (other lanes of the
+// same wave read what a lane wrote).  No cross-wave effect.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// acc += A[16 x K] * B[16 x K]^T, operands in LDS (K contiguous, row strides
+// lda / ldb in elements).  K must be a multiple of 16 (bf16) or 4 (fp32).
+__device__ __forceinline__ void mma_nt(f32x4& acc, const bf16* A, int lda, const bf16* B,
+                                       int ldb, int K, int lane)
+{
+    const int row = lane & 15;
+    int k0 = 0;
+    for (; k0 + 32 <= K; k0 += 32) {
+        const int kk = k0 + 8 * (lane >> 4);
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(A + row * lda + kk);
+        bf16x8 b = *reinterpret_cast<const bf16x8*>(B + row * ldb + kk);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+    for (; k0 + 16 <= K; k0 += 16) {
+        const int kk = k0 + 4 * (lane >> 4);
+        bf16x4 a = *reinterpret_cast<const bf16x4*>(A + row * lda + kk);
+        bf16x4 b = *reinterpret_cast<const bf16x4*>(B + row * ldb + kk);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void mma_nt(f32x4& acc, const float* A, int lda, const float* B,
+                                       int ldb, int K, int lane)
+{
+    const int row = lane & 15, kq = lane >> 4;
+    for (int k0 = 0; k0 < K; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[row * lda + k0 + kq],
+                                                   B[row * ldb + k0 + kq], acc, 0, 0, 0);
+}
+
+// Same contraction with an fp32 A operand in LDS and a B operand of type T:
+// for bf16 the A values are rounded to bf16 on the fly (K multiple of 16).
+__device__ __forceinline__ void mma_nt_f32a(f32x4& acc, const float* A, int lda, const bf16* B,
+                                            int ldb, int K, int lane)
+{
+    const int row = lane & 15;
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        const int kk = k0 + 4 * (lane >> 4);
+        f32x4 af = *reinterpret_cast<const f32x4*>(A + row * lda + kk);
+        bf16x4 a = bf16x4{static_cast<bf16>(af[0]), static_cast<bf16>(af[1]),
+                          static_cast<bf16>(af[2]), static_cast<bf16>(af[3])};
+        bf16x4 b = *reinterpret_cast<const bf16x4*>(B + row * ldb + kk);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void mma_nt_f32a(f32x4& acc, const float* A, int lda, const float* B,
+                                            int ldb, int K, int lane)
+{
+    mma_nt(acc, A, lda, B, ldb, K, lane);
+}
+
+// Store 4 consecutive values (a transposed accumulator column) as T.
+__device__ __forceinline__ void store4(bf16* p, f32x4 v)
+{
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{static_cast<bf16>(v[0]), static_cast<bf16>(v[1]),
+                                           static_cast<bf16>(v[2]), static_cast<bf16>(v[3])};
+}
+__device__ __forceinline__ void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+// ---------------------------------------------------------------------------
+// 2x2 Moebius maps on homogeneous variance coordinates [n; d] (p = n / d).
+// The per-token factor is M = [[a, w], [u a, 1 + u w]] (predict with decay
+// a = alpha^2 and process noise w, then the information-scaled update with
+// u = mu k^2 / r).  Products compose by LEFT multiplication in token order and
+// are rescaled by 1 / max|entry| (all entries are >= 0, and the rescale keeps
+// every ratio n / d), so fp32 never overflows.
+// ---------------------------------------------------------------------------
+struct Mob {
+    float m00, m01, m10, m11;
+};
+
+__device__ __forceinline__ Mob mob_identity() { return Mob{1.f, 0.f, 0.f, 1.f}; }
+
+// later o earlier  (apply `earlier` first)
+__device__ __forceinline__ Mob mob_compose(const Mob& later, const Mob& earlier)
+{
+    Mob r;
+    r.m00 = later.m00 * earlier.m00 + later.m01 * earlier.m10;
+    r.m01 = later.m00 * earlier.m01 + later.m01 * earlier.m11;
+    r.m10 = later.m10 * earlier.m00 + later.m11 * earlier.m10;
+    r.m11 = later.m10 * earlier.m01 + later.m11 * earlier.m11;
+    const float mx = fmaxf(fmaxf(r.m00, r.m01), fmaxf(r.m10, r.m11));
+    const float s = rcp(mx);
+    r.m00 *= s;
+    r.m01 *= s;
+    r.m10 *= s;
+    r.m11 *= s;
+    return r;
+}
+
+__device__ __forceinline__ float mob_apply(const Mob& m, float x)
+{
+    return (m.m00 * x + m.m01) * rcp(m.m10 * x + m.m11);
+}
+
+// DPP lane moves (GFX9 encodings).  `old` is returned for lanes whose source
+// is outside the pattern, so passing the identity makes those lanes neutral.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_mov(float old, float src)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                           __builtin_bit_cast(int, src), CTRL, ROW_MASK, 0xf,
+                                           false));
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ Mob mob_dpp(const Mob& src)
+{
+    const Mob id = mob_identity();
+    return Mob{dpp_mov<CTRL, ROW_MASK>(id.m00, src.m00), dpp_mov<CTRL, ROW_MASK>(id.m01, src.m01),
+               dpp_mov<CTRL, ROW_MASK>(id.m10, src.m10), dpp_mov<CTRL, ROW_MASK>(id.m11, src.m11)};
+}
+
+// Inclusive wave64 scan of Moebius maps in lane order: lane l ends with
+// M_l o M_{l-1} o ... o M_0.  Six DPP steps: row_shr 1/2/4/8 inside each row
+// of 16 lanes, then row_bcast 15 and row_bcast 31 across rows.
+__device__ __forceinline__ Mob mob_wave_scan_inclusive(Mob x)
+{
+    x = mob_compose(x, mob_dpp<0x111, 0xf>(x));  // row_shr:1
+    x = mob_compose(x, mob_dpp<0x112, 0xf>(x));  // row_shr:2
+    x = mob_compose(x, mob_dpp<0x114, 0xf>(x));  // row_shr:4
+    x = mob_compose(x, mob_dpp<0x118, 0xf>(x));  // row_shr:8
+    x = mob_compose(x, mob_dpp<0x142, 0xa>(x));  // row_bcast:15 -> rows 1, 3
+    x = mob_compose(x, mob_dpp<0x143, 0xc>(x));  // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
+// Exclusive version: lane l gets M_{l-1} o ... o M_0 (identity at lane 0).
+__device__ __forceinline__ Mob mob_wave_shift_right(const Mob& x)
+{
+    return mob_dpp<0x138, 0xf>(x);  // wave_shr:1
+}
+
+}  // namespace kdn

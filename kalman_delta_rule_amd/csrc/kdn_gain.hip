@@ -1,0 +1,294 @@
+// kdn_gain.hip -- the KDN gain scan on its own (variance recurrence + Kalman
+// gain, no memory), gfx950.
+//
+// The per-channel variance recurrence of Diagonal KDN is a fractional-linear
+// (Moebius) map of p_{t-1}; in homogeneous coordinates one token is
+//   M_t = [[alpha^2, omega], [u alpha^2, 1 + u omega]],  u = (mu / r_t) k^2
+// (KDN reading notes, method part §6, Eq. (32)-(39)); Isotropic KDN has the
+// same form for its scalar with alpha^2 -> mean_i alpha_i^2 and
+// u = mu |k|^2 / (d_k r_t) (§7, Eq. (40), Appendix C).  Composition is
+// associative but not commutative, so prefixes are taken in token order by
+// left multiplication.  Following the chunked schedule the notes describe for
+// Appendix D (chunk summaries, an exclusive carry across chunks, replay inside
+// each chunk):
+//   pass 1  summary of every 64-token chunk: Diagonal composes its channel's
+//           64 maps serially in one lane (lanes = channels, coalesced loads);
+//           Isotropic scans the chunk's 64 maps across the lanes of one
+//           wavefront with DPP.
+//   pass 2  carry: one wavefront per (batch, head, channel) scans the chunk
+//           summaries across its lanes with DPP (64 chunks per step, with a
+//           running prefix between steps), giving every chunk's entry
+//           variance and the final variance.
+//   pass 3  (only when kappa is requested) replay each chunk from its entry
+//           variance: p^_t, z_t = sum_i p^_t,i k_t,i^2, kappa = p^ k/(r + z).
+// Every combine rescales by 1/max|entry| (entries are non-negative), which
+// keeps the ratios and avoids fp32 overflow.
+#include "kdn_common.h"
+#include "kdn_internal.h"
+
+namespace kdn {
+
+constexpr int GC = 64;  // tokens per gain chunk
+
+__device__ __forceinline__ Mob mob_mul_raw(const Mob& later, const Mob& earlier)
+{
+    return Mob{later.m00 * earlier.m00 + later.m01 * earlier.m10,
+               later.m00 * earlier.m01 + later.m01 * earlier.m11,
+               later.m10 * earlier.m00 + later.m11 * earlier.m10,
+               later.m10 * earlier.m01 + later.m11 * earlier.m11};
+}
+
+__device__ __forceinline__ Mob mob_normalize(const Mob& r)
+{
+    const float s = rcp(fmaxf(fmaxf(r.m00, r.m01), fmaxf(r.m10, r.m11)));
+    return Mob{r.m00 * s, r.m01 * s, r.m10 * s, r.m11 * s};
+}
+
+// Per-token isotropic factor inputs for the 64 tokens of a chunk, computed by
+// a 256-thread block: 4 threads per token reduce alpha^2 and k^2 over the key
+// channels.  Results land in sa[t] (mean alpha^2) and sn[t] (|k|^2).
+template <typename IO, int DK>
+__device__ __forceinline__ void iso_token_reductions(const GainArgs& a, int bh, int t0,
+                                                     int n_valid, float* sa, float* sn)
+{
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    constexpr int TPT = 4, CPT = DK / TPT;
+    const int t = tid / TPT, part = tid % TPT;
+    const IO* kg = reinterpret_cast<const IO*>(a.k);
+    float xa = 0.f, xn = 0.f;
+    if (t < n_valid) {
+        const size_t off = (((size_t)b * a.T + t0 + t) * a.H + h) * DK + part * CPT;
+#pragma unroll
+        for (int c = 0; c < CPT; c += 4) {
+            const f32x4 al = *reinterpret_cast<const f32x4*>(a.alpha + off + c);
+            xa += al[0] * al[0] + al[1] * al[1] + al[2] * al[2] + al[3] * al[3];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float kv = to_f32(kg[off + c + e]);
+                xn += kv * kv;
+            }
+        }
+    }
+    xa += __shfl_xor(xa, 1);
+    xn += __shfl_xor(xn, 1);
+    xa += __shfl_xor(xa, 2);
+    xn += __shfl_xor(xn, 2);
+    if (part == 0) {
+        sa[t] = (t < n_valid) ? xa * (1.f / DK) : 1.f;
+        sn[t] = xn;
+    }
+}
+
+// ---------------------------------------------------------------- pass 1
+template <typename IO, int DK>
+__global__ __launch_bounds__(DK) void gain_summary_diag(GainArgs a, int nchunks)
+{
+    const int bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+    const int b = bh / a.H, h = bh % a.H, i = threadIdx.x;
+    const int t0 = c * GC, n_valid = min(GC, a.T - t0);
+    const IO* kg = reinterpret_cast<const IO*>(a.k);
+    Mob P = mob_identity();
+    for (int t = 0; t < n_valid; ++t) {
+        const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
+        const float al = a.alpha[tok * DK + i], w = a.omega[tok * DK + i];
+        const float kv = to_f32(kg[tok * DK + i]);
+        const float u = (a.mu / a.r[tok]) * kv * kv;
+        const float a2 = al * al;
+        P = mob_mul_raw(Mob{a2, w, u * a2, 1.f + u * w}, P);
+        if ((t & 3) == 3)
+            P = mob_normalize(P);
+    }
+    P = mob_normalize(P);
+    const size_t base = (size_t)bh * 4 * DK * nchunks + (size_t)i * nchunks + c;
+    const size_t es = (size_t)DK * nchunks;
+    a.summ[base] = P.m00;
+    a.summ[base + es] = P.m01;
+    a.summ[base + 2 * es] = P.m10;
+    a.summ[base + 3 * es] = P.m11;
+}
+
+template <typename IO, int DK>
+__global__ __launch_bounds__(256) void gain_summary_iso(GainArgs a, int nchunks)
+{
+    __shared__ float sa[GC], sn[GC];
+    const int bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+    const int b = bh / a.H, h = bh % a.H;
+    const int t0 = c * GC, n_valid = min(GC, a.T - t0);
+    iso_token_reductions<IO, DK>(a, bh, t0, n_valid, sa, sn);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int t = threadIdx.x;
+        Mob m = mob_identity();
+        if (t < n_valid) {
+            const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
+            const float u = a.mu * sn[t] / ((float)DK * a.r[tok]);
+            const float w = a.omega[tok];
+            m = Mob{sa[t], w, u * sa[t], 1.f + u * w};
+        }
+        const Mob incl = mob_wave_scan_inclusive(m);
+        if (t == 63) {
+            const size_t es = (size_t)nchunks;
+            const size_t base = (size_t)bh * 4 * nchunks + c;
+            a.summ[base] = incl.m00;
+            a.summ[base + es] = incl.m01;
+            a.summ[base + 2 * es] = incl.m10;
+            a.summ[base + 3 * es] = incl.m11;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- pass 2
+// One wavefront per (bh, channel): DPP scan over chunk summaries.
+__global__ __launch_bounds__(64) void gain_carry(GainArgs a, int width, int nchunks)
+{
+    const int row = blockIdx.x;  // bh * width + i
+    const int bh = row / width, i = row % width;
+    const int lane = threadIdx.x;
+    const float p0 = a.var0 ? a.var0[(size_t)bh * width + i] : 1.f;
+    const size_t es = (size_t)width * nchunks;
+    const float* s = a.summ + (size_t)bh * 4 * es + (size_t)i * nchunks;
+    Mob run = mob_identity();  // product of all earlier 64-chunk groups
+    for (int cb = 0; cb < nchunks; cb += 64) {
+        const int c = cb + lane;
+        Mob m = mob_identity();
+        if (c < nchunks)
+            m = Mob{s[c], s[c + es], s[c + 2 * es], s[c + 3 * es]};
+        const Mob incl = mob_wave_scan_inclusive(m);
+        const Mob excl = mob_compose(mob_wave_shift_right(incl), run);
+        if (c < nchunks)
+            a.carry[((size_t)bh * nchunks + c) * width + i] = mob_apply(excl, p0);
+        const Mob tot = Mob{__shfl(incl.m00, 63), __shfl(incl.m01, 63), __shfl(incl.m10, 63),
+                            __shfl(incl.m11, 63)};
+        run = mob_compose(tot, run);
+    }
+    if (lane == 0)
+        a.var_T[(size_t)bh * width + i] = mob_apply(run, p0);
+}
+
+// ---------------------------------------------------------------- pass 3
+template <typename IO, int DK>
+__global__ __launch_bounds__(DK) void gain_replay_diag(GainArgs a, int nchunks)
+{
+    __shared__ float s_ph[GC][DK + 1];
+    __shared__ float s_z[GC];
+    const int bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+    const int b = bh / a.H, h = bh % a.H, i = threadIdx.x;
+    const int t0 = c * GC, n_valid = min(GC, a.T - t0);
+    const IO* kg = reinterpret_cast<const IO*>(a.k);
+    float p = a.carry[((size_t)bh * nchunks + c) * DK + i];
+    float kk[GC];
+#pragma unroll
+    for (int t = 0; t < GC; ++t) {
+        float ph = 0.f, kv = 0.f;
+        if (t < n_valid) {
+            const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
+            const float al = a.alpha[tok * DK + i], w = a.omega[tok * DK + i];
+            kv = to_f32(kg[tok * DK + i]);
+            ph = al * al * p + w;
+            const float u = (a.mu / a.r[tok]) * kv * kv;
+            p = ph * rcp(1.f + u * ph);
+        }
+        kk[t] = kv;
+        s_ph[t][i] = ph;
+    }
+    __syncthreads();
+    if (i < GC) {
+        float z = 0.f;
+        const int t = i;
+        const IO* krow = kg + (((size_t)b * a.T + t0 + t) * a.H + h) * DK;
+        if (t < n_valid)
+            for (int j = 0; j < DK; ++j) {
+                const float kv = to_f32(krow[j]);
+                z += s_ph[t][j] * kv * kv;
+            }
+        s_z[t] = z;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < GC; ++t) {
+        if (t < n_valid) {
+            const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
+            a.kappa[tok * DK + i] = s_ph[t][i] * kk[t] * rcp(a.r[tok] + s_z[t]);
+        }
+    }
+}
+
+template <typename IO, int DK>
+__global__ __launch_bounds__(256) void gain_replay_iso(GainArgs a, int nchunks)
+{
+    __shared__ float sa[GC], sn[GC], sbeta[GC];
+    const int bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+    const int b = bh / a.H, h = bh % a.H;
+    const int t0 = c * GC, n_valid = min(GC, a.T - t0);
+    iso_token_reductions<IO, DK>(a, bh, t0, n_valid, sa, sn);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int t = threadIdx.x;
+        Mob m = mob_identity();
+        float r = 1.f, w = 0.f;
+        if (t < n_valid) {
+            const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
+            r = a.r[tok];
+            w = a.omega[tok];
+            const float u = a.mu * sn[t] / ((float)DK * r);
+            m = Mob{sa[t], w, u * sa[t], 1.f + u * w};
+        }
+        const Mob excl = mob_wave_shift_right(mob_wave_scan_inclusive(m));
+        const float bprev = mob_apply(excl, a.carry[(size_t)bh * nchunks + c]);
+        const float bhat = sa[t] * bprev + w;
+        sbeta[t] = bhat * rcp(r + bhat * sn[t]);
+    }
+    __syncthreads();
+    const IO* kg = reinterpret_cast<const IO*>(a.k);
+    for (int e = threadIdx.x; e < n_valid * DK; e += 256) {
+        const int t = e / DK, i = e % DK;
+        const size_t idx = (((size_t)b * a.T + t0 + t) * a.H + h) * DK + i;
+        a.kappa[idx] = sbeta[t] * to_f32(kg[idx]);
+    }
+}
+
+size_t gain_workspace_floats(bool iso, int B, int T, int H, int dk)
+{
+    const size_t nchunks = (T + GC - 1) / GC;
+    const size_t width = iso ? 1 : (size_t)dk;
+    return (size_t)B * H * nchunks * width * 5;  // 4 summary planes + carries
+}
+
+template <typename IO, int DK>
+static hipError_t launch_gain_t(const GainArgs& a0, bool iso, hipStream_t stream)
+{
+    GainArgs a = a0;
+    const int nchunks = (a.T + GC - 1) / GC;
+    const int BH = a.B * a.H;
+    const int width = iso ? 1 : DK;
+    if (nchunks > 0) {
+        if (iso)
+            hipLaunchKernelGGL((gain_summary_iso<IO, DK>), dim3(BH * nchunks), dim3(256), 0,
+                               stream, a, nchunks);
+        else
+            hipLaunchKernelGGL((gain_summary_diag<IO, DK>), dim3(BH * nchunks), dim3(DK), 0,
+                               stream, a, nchunks);
+    }
+    hipLaunchKernelGGL(gain_carry, dim3(BH * width), dim3(64), 0, stream, a, width, nchunks);
+    if (a.kappa && nchunks > 0) {
+        if (iso)
+            hipLaunchKernelGGL((gain_replay_iso<IO, DK>), dim3(BH * nchunks), dim3(256), 0,
+                               stream, a, nchunks);
+        else
+            hipLaunchKernelGGL((gain_replay_diag<IO, DK>), dim3(BH * nchunks), dim3(DK), 0,
+                               stream, a, nchunks);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gain_scan(const GainArgs& a, bool iso, int io_dtype, hipStream_t stream)
+{
+    if (io_dtype == 1)
+        return a.dk == 128 ? launch_gain_t<bf16, 128>(a, iso, stream)
+                           : launch_gain_t<bf16, 64>(a, iso, stream);
+    return a.dk == 128 ? launch_gain_t<float, 128>(a, iso, stream)
+                       : launch_gain_t<float, 64>(a, iso, stream);
+}
+
+}  // namespace kdn

@@ -1,0 +1,61 @@
+// kdn_internal.h -- argument blocks and launchers shared by the host API and
+// the kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kdn {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* omega;
+    const float* r;
+    const float* S0;    // nullable
+    const float* var0;  // nullable
+    void* o;
+    float* S_T;
+    float* var_T;
+    int B, T, H, dk, dv;
+    float mu;
+};
+
+struct StepArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* omega;
+    const float* r;
+    float* S;
+    float* var;
+    void* o;
+    int B, H, dk, dv;
+    float mu;
+};
+
+struct GainArgs {
+    const void* k;
+    const float* alpha;
+    const float* omega;
+    const float* r;
+    const float* var0;  // nullable
+    float* kappa;       // nullable
+    float* var_T;
+    float* summ;        // workspace: chunk summaries [BH][4][width][nchunks]
+    float* carry;       // workspace: chunk-entry variances [BH][nchunks][width]
+    int B, T, H, dk;
+    float mu;
+};
+
+// value-tile width used by the chunked forward for this io dtype
+int chunk_fwd_value_tile(int io_dtype, int dk);
+hipError_t launch_chunk_fwd(const FwdArgs& a, bool iso, int io_dtype, hipStream_t stream);
+hipError_t launch_step(const StepArgs& a, bool iso, int io_dtype, hipStream_t stream);
+size_t gain_workspace_floats(bool iso, int B, int T, int H, int dk);
+hipError_t launch_gain_scan(const GainArgs& a, bool iso, int io_dtype, hipStream_t stream);
+
+}  // namespace kdn

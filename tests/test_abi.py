@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/kdn.h declares, and rejects invalid arguments synchronously
+(before any launch) with the documented status codes.
+
+The invalid-argument cases pass stand-in pointer values; they are skipped
+when a GPU is visible, so that a validation gap can never turn into a launch
+on fake addresses.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from kalman_delta_rule_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from kalman_delta_rule_amd import build
+        build.build_library()
+    return _lib.lib()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kdn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared_functions()
+    for n in ("kdn_diag_fwd", "kdn_iso_fwd", "kdn_step"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from kalman_delta_rule_amd import _lib
+    names = _declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(L, n), "libkdn.so does not export %s" % n
+    assert set(_lib.EXPORTED) == set(names)
+
+
+def test_version_and_status_strings(L):
+    assert L.kdn_version().decode().startswith("kdn-mi355x")
+    assert L.kdn_status_string(0) == b"KDN_OK"
+    assert L.kdn_status_string(-1) == b"KDN_ERR_INVALID_ARG"
+    assert L.kdn_status_string(-2) == b"KDN_ERR_UNSUPPORTED"
+    assert L.kdn_status_string(-3) == b"KDN_ERR_WORKSPACE"
+    assert L.kdn_status_string(-4) == b"KDN_ERR_HIP"
+    assert L.kdn_status_string(7) == b"KDN_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(L):
+    assert L.kdn_fwd_workspace_size(0, 8, 4096, 16, 128, 128, 1) == 0
+    # gain scan: 4 summary planes + carries per chunk and channel
+    assert L.kdn_gain_workspace_size(0, 1, 128, 2, 64) == 1 * 2 * 2 * 64 * 5 * 4
+    assert L.kdn_gain_workspace_size(1, 1, 128, 2, 64) == 1 * 2 * 2 * 1 * 5 * 4
+    assert L.kdn_gain_workspace_size(0, 1, 128, 2, 96) == 0
+
+
+# ---------------------------------------------------------------------------
+# validation: every case below has exactly one invalid argument
+# ---------------------------------------------------------------------------
+cpu_only = pytest.mark.skipif(
+    __import__("torch").cuda.is_available(),
+    reason="stand-in pointers are only used where no GPU is visible")
+
+P = 1 << 20      # a 16-byte-aligned stand-in address
+MIS = P + 4      # misaligned
+
+
+def _fwd_call(L, variant="diag", **kw):
+    args = dict(B=1, T=64, H=2, dk=64, dv=64, io=1, mu=64.0, q=P, k=P, v=P, alpha=P, omega=P,
+                r=P, S0=None, var0=None, o=P + 4096, S_T=P + 8192, var_T=P + 16384, ws=None,
+                ws_bytes=0, stream=None)
+    args.update(kw)
+    fn = L.kdn_diag_fwd if variant == "diag" else L.kdn_iso_fwd
+    a = args
+    return fn(a["B"], a["T"], a["H"], a["dk"], a["dv"], a["io"], a["mu"], a["q"], a["k"], a["v"],
+              a["alpha"], a["omega"], a["r"], a["S0"], a["var0"], a["o"], a["S_T"], a["var_T"],
+              a["ws"], a["ws_bytes"], a["stream"])
+
+
+@cpu_only
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+@pytest.mark.parametrize("bad,code,needle", [
+    (dict(io=2), -1, "io_dtype"),
+    (dict(B=0), -1, "B >= 1"),
+    (dict(H=0), -1, "H >= 1"),
+    (dict(T=-1), -1, "T >= 0"),
+    (dict(mu=-1.0), -1, "mu"),
+    (dict(mu=float("nan")), -1, "mu"),
+    (dict(dk=96), -2, "dk"),
+    (dict(dv=96), -2, "dv"),
+    (dict(dv=512), -2, "dv"),
+    (dict(io=0, dk=128), -2, "fp32 forward supports dk"),
+    (dict(q=None), -1, "q must not be NULL"),
+    (dict(k=None), -1, "k must not be NULL"),
+    (dict(v=None), -1, "v must not be NULL"),
+    (dict(alpha=None), -1, "alpha"),
+    (dict(omega=None), -1, "omega"),
+    (dict(r=None), -1, "r must not be NULL"),
+    (dict(o=None), -1, "o must not be NULL"),
+    (dict(S_T=None), -1, "S_T"),
+    (dict(var_T=None), -1, "_T must not be NULL"),
+    (dict(q=MIS), -1, "aligned"),
+    (dict(S_T=MIS), -1, "aligned"),
+    (dict(o=P), -1, "alias"),
+    (dict(var0=P + 16384), -1, "alias"),
+    (dict(S0=P + 8192 + 64), -1, "overlap"),
+    (dict(B=1 << 14, T=1 << 14, H=16), -2, "2^31"),
+])
+def test_fwd_validation(L, variant, bad, code, needle):
+    st = _fwd_call(L, variant, **bad)
+    assert st == code
+    assert needle in L.kdn_last_error_message().decode()
+
+
+@cpu_only
+def test_step_validation(L):
+    def step(**kw):
+        a = dict(var=0, B=4, H=2, dk=128, dv=128, io=1, mu=128.0, q=P, k=P, v=P, alpha=P,
+                 omega=P, r=P, S=P + 4096, vs=P + 8192, o=P + 16384)
+        a.update(kw)
+        return L.kdn_step(a["var"], a["B"], a["H"], a["dk"], a["dv"], a["io"], a["mu"], a["q"],
+                          a["k"], a["v"], a["alpha"], a["omega"], a["r"], a["S"], a["vs"], a["o"],
+                          None)
+    assert step(var=3) == -1
+    assert step(dk=32) == -2
+    assert step(dv=256) == -2
+    assert step(S=None) == -1
+    assert step(vs=None) == -1
+    assert step(S=MIS) == -1
+    assert step(o=P) == -1
+    assert step(io=5) == -1
+
+
+@cpu_only
+def test_gain_scan_validation(L):
+    def gs(**kw):
+        a = dict(var=0, B=1, T=64, H=2, dk=64, io=1, mu=64.0, k=P, alpha=P, omega=P, r=P,
+                 var0=None, kappa=None, var_T=P + 4096, ws=P + 8192, wsb=1 << 20)
+        a.update(kw)
+        return L.kdn_gain_scan(a["var"], a["B"], a["T"], a["H"], a["dk"], a["io"], a["mu"], a["k"],
+                               a["alpha"], a["omega"], a["r"], a["var0"], a["kappa"], a["var_T"],
+                               a["ws"], a["wsb"], None)
+    assert gs(var=2) == -1
+    assert gs(dk=32) == -2
+    assert gs(wsb=16) == -3
+    assert gs(ws=None) == -3
+    assert gs(var_T=None) == -1
+    assert gs(alpha=MIS) == -1
+    assert gs(var0=P + 4096) == -1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from kalman_delta_rule_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(_lib.KdnLibraryMissing):
+        _lib.lib()

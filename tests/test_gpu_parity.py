@@ -1,0 +1,206 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+identical seeded inputs.
+
+Small shapes compare every element (several chunks, ragged tails, several
+value tiles); the full workloads compare sampled (batch, head) problems the
+oracle solves one by one, in the launch configuration the benchmark times.
+Bar: relative L2 <= 1e-4 (fp32 q/k/v) or <= 2e-2 (bf16 q/k/v) on o, S_T and
+the final variances.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kalman_delta_rule_amd import api, inputs
+from kdn_testutil import TOL, compare_heads, host, oracle_heads, rel_l2, sample_heads, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a HIP GPU")
+    torch.cuda.init()
+
+
+def _run_fwd(variant, d, mu=None, S0=None, var0=None):
+    fn = api.kdn_diag_fwd if variant == "diag" else api.kdn_iso_fwd
+    kw = {"p0": var0} if variant == "diag" else {"b0": var0}
+    o, S, var = fn(d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], S0=S0, mu=mu, **kw)
+    torch.cuda.synchronize()
+    return o, S, var
+
+
+def _full_compare(ora, variant, io, inp, mu=None, S0=None, var0=None, tag=""):
+    d = to_dev(inp, io)
+    S0d = None if S0 is None else torch.from_numpy(S0).cuda()
+    v0d = None if var0 is None else torch.from_numpy(var0).cuda()
+    o, S, var = _run_fwd(variant, d, mu=mu, S0=S0d, var0=v0d)
+    B, T, H, _ = inp["k"].shape
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    res = oracle_heads(ora, variant, inp, heads, mu=mu, S0=S0, var0=var0)
+    err = compare_heads(res, host(o), host(S), host(var), heads)
+    print("%s %s %s errors %s" % (tag, variant, io, err), flush=True)
+    tol = TOL[io]
+    assert err["o"] <= tol and err["S"] <= tol and err["var"] <= tol, err
+    return err
+
+
+SMALL = [
+    # (B, T, H, dk, dv)
+    (1, 256, 2, 64, 64),
+    (2, 200, 3, 64, 64),
+    (1, 130, 2, 128, 128),
+    (2, 64, 1, 128, 256),
+    (1, 1, 2, 128, 128),
+    (1, 63, 1, 64, 128),
+]
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dT%dH%ddk%ddv%d" % s)
+def test_small_bf16(ora, variant, shape):
+    B, T, H, dk, dv = shape
+    w = inputs.Workload("t", variant, "bf16", B, H, T, dk, dv, seed=101 + T)
+    inp = inputs.make_fwd_inputs(w)
+    _full_compare(ora, variant, "bf16", inp, tag=str(shape))
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+@pytest.mark.parametrize("shape", [(1, 256, 2, 64, 64), (2, 150, 2, 64, 32), (1, 5, 1, 64, 96)],
+                         ids=lambda s: "B%dT%dH%ddk%ddv%d" % s)
+def test_small_f32(ora, variant, shape):
+    B, T, H, dk, dv = shape
+    w = inputs.Workload("t", variant, "f32", B, H, T, dk, dv, seed=7 + T)
+    inp = inputs.make_fwd_inputs(w)
+    _full_compare(ora, variant, "f32", inp, tag=str(shape))
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_nonzero_initial_state_and_mu(ora, variant, io):
+    B, T, H, dk, dv = 2, 100, 2, 64, 64
+    w = inputs.Workload("t", variant, io, B, H, T, dk, dv, seed=55)
+    inp = inputs.make_fwd_inputs(w)
+    rng = np.random.default_rng(56)
+    S0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    var0 = rng.uniform(0.1, 2.0, (B, H, dk) if variant == "diag" else (B, H)).astype(np.float32)
+    for mu in (0.0, 1.0, 300.0):
+        _full_compare(ora, variant, io, inp, mu=mu, S0=S0, var0=var0, tag="mu=%g" % mu)
+
+
+def test_config0_diag_f32(ora):
+    w = inputs.workload(0)
+    _full_compare(ora, "diag", "f32", inputs.make_fwd_inputs(w), tag=w.name)
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+def test_empty_sequence_passes_state_through(variant):
+    B, H, dk, dv = 2, 3, 128, 128
+    rng = np.random.default_rng(3)
+    S0 = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32)).cuda()
+    vshape = (B, H, dk) if variant == "diag" else (B, H)
+    v0 = torch.from_numpy(rng.uniform(0.1, 1, vshape).astype(np.float32)).cuda()
+    z = lambda *s: torch.zeros(s, device="cuda")
+    q = torch.zeros((B, 0, H, dk), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((B, 0, H, dv), dtype=torch.bfloat16, device="cuda")
+    om = z(B, 0, H, dk) if variant == "diag" else z(B, 0, H)
+    d = {"q": q, "k": q, "v": v, "alpha": z(B, 0, H, dk), "omega": om, "r": z(B, 0, H)}
+    o, S, var = _run_fwd(variant, d, S0=S0, var0=v0)
+    assert o.shape == (B, 0, H, dv)
+    assert torch.equal(S, S0) and torch.equal(var, v0)
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+def test_state_output_may_alias_initial_state(ora, variant):
+    B, T, H, dk, dv = 1, 90, 2, 128, 128
+    w = inputs.Workload("t", variant, "bf16", B, H, T, dk, dv, seed=9)
+    inp = inputs.make_fwd_inputs(w)
+    rng = np.random.default_rng(10)
+    S0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    d = to_dev(inp, "bf16")
+    Sdev = torch.from_numpy(S0).cuda()
+    fn = api.kdn_diag_fwd if variant == "diag" else api.kdn_iso_fwd
+    o, S, var = fn(d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], S0=Sdev, S_T=Sdev)
+    torch.cuda.synchronize()
+    assert S.data_ptr() == Sdev.data_ptr()
+    res = oracle_heads(ora, variant, inp, [(0, 0), (0, 1)], S0=S0)
+    err = compare_heads(res, host(o), host(S), host(var), [(0, 0), (0, 1)])
+    assert max(err.values()) <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+def test_deterministic(variant):
+    w = inputs.Workload("t", variant, "bf16", 2, 4, 300, 128, 128, seed=77)
+    d = to_dev(inputs.make_fwd_inputs(w), "bf16")
+    a = _run_fwd(variant, d)
+    b = _run_fwd(variant, d)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+def test_resume_matches_one_pass(ora, variant):
+    # fwd over T1 tokens, then fwd over T2 more from the returned state, equals
+    # the oracle's single pass over T1 + T2 (chunk boundaries differ).
+    B, T, H, dk, dv = 1, 300, 2, 128, 128
+    w = inputs.Workload("t", variant, "bf16", B, H, T, dk, dv, seed=88)
+    inp = inputs.make_fwd_inputs(w)
+    d = to_dev(inp, "bf16")
+    t1 = 97
+    part = lambda dd, s: {k: v[:, s].contiguous() for k, v in dd.items()
+                          if k in ("q", "k", "v", "alpha", "omega", "r")}
+    fn = api.kdn_diag_fwd if variant == "diag" else api.kdn_iso_fwd
+    kw = "p0" if variant == "diag" else "b0"
+    a = part(d, slice(0, t1))
+    o1, S1, v1 = fn(a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"])
+    b = part(d, slice(t1, T))
+    o2, S2, v2 = fn(b["q"], b["k"], b["v"], b["alpha"], b["omega"], b["r"], S0=S1, **{kw: v1})
+    torch.cuda.synchronize()
+    o = torch.cat([o1, o2], dim=1)
+    heads = [(0, 0), (0, 1)]
+    res = oracle_heads(ora, variant, inp, heads)
+    err = compare_heads(res, host(o), host(S2), host(v2), heads)
+    assert max(err.values()) <= TOL["bf16"], err
+
+
+# ---------------------------------------------------------------------------
+# full workloads, sampled (batch, head) problems
+# ---------------------------------------------------------------------------
+def _sampled(ora, widx, n_heads, variant=None):
+    w = inputs.workload(widx)
+    variant = variant or w.variant
+    inp = inputs.make_fwd_inputs(w, variant)
+    d = to_dev(inp, w.io)
+    o, S, var = _run_fwd(variant, d)
+    heads = sample_heads(w.B, w.H, n_heads, seed=widx)
+    oh = host(o[[b for b, _ in heads]][:, :, [h for _, h in heads]])
+    # reassemble the sampled heads into a dict-compatible layout
+    res = oracle_heads(ora, variant, inp, heads)
+    o_s = {(b, h): oh[i, :, i] for i, (b, h) in enumerate(heads)}
+    Sh, vh = host(S), host(var)
+    err = {
+        "o": rel_l2(np.concatenate([o_s[x].ravel() for x in heads]),
+                    np.concatenate([res[x]["o"].ravel() for x in heads])),
+        "S": rel_l2(np.concatenate([Sh[b, h].ravel() for b, h in heads]),
+                    np.concatenate([res[x]["S"].ravel() for x in heads])),
+        "var": rel_l2(np.concatenate([np.ravel(vh[b, h]) for b, h in heads]),
+                      np.concatenate([np.ravel(res[x]["var"]) for x in heads])),
+    }
+    print("%s heads=%s errors %s" % (w.name, heads, err), flush=True)
+    tol = TOL[w.io]
+    assert err["o"] <= tol and err["S"] <= tol and err["var"] <= tol, err
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+
+
+def test_config1_iso_full(ora):
+    _sampled(ora, 1, 6)
+
+
+def test_config2_diag_full(ora):
+    _sampled(ora, 2, 6)
+
+
+def test_config3_long_full(ora):
+    _sampled(ora, 3, 1)
