@@ -1,0 +1,272 @@
+"""Benchmark of the KDN mixer forward on one MI355X.
+
+Default workload: Diagonal KDN forward, bf16 q/k/v with fp32 gates and state,
+B=8, H=16, T=4096, d_k=d_v=128 (the mixer of a hidden-2048 / 16-head layer
+at a 4K context), synthetic seeded inputs resident in HBM before timing.
+One step = one forward call over the whole batch (gain scan, chunked memory
+update, readout, final state).  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+Roofline: achieved = algorithmic bytes per launch / mean launch time (HIP
+events on the launch stream).  Algorithmic bytes read every input once and
+write every output once (per head-token: 3 d s_io + 2 d * 4 + 4 + d s_io for
+Diagonal; plus the final state and variances per head).  `traffic` (HBM bytes
+per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain-copy
+calibration) is read from profiles/ and reported only while the kernel
+sources still hash to what was profiled.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["kdn_chunk.hip", "kdn_common.h", "kdn_step.hip", "kdn_gain.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "kalman_delta_rule_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def alg_bytes_fwd(variant: str, B, T, H, dk, dv, s_io: int) -> int:
+    n_ht = B * T * H
+    if variant == "diag":
+        per_ht = 2 * dk * s_io + dv * s_io + 2 * dk * 4 + 4 + dv * s_io
+        state = B * H * (dk * dv * 4 + dk * 4)
+    else:
+        per_ht = 2 * dk * s_io + dv * s_io + dk * 4 + 4 + 4 + dv * s_io
+        state = B * H * (dk * dv * 4 + 4)
+    return n_ht * per_ht + state
+
+
+def alg_bytes_step(variant: str, B, H, dk, dv, s_io: int) -> int:
+    per_head = 2 * dk * s_io + dv * s_io + dk * 4 + 4 + dv * s_io + 2 * dk * dv * 4
+    per_head += (2 * dk * 4 + dk * 4) if variant == "diag" else (4 + 2 * 4)
+    return B * H * per_head
+
+
+def traffic_for(key: str):
+    """HBM bytes per launch measured by counters, if still valid."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(key)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, variant):
+    """The fp64 oracle on a bounded sample of the same workload: batch row 0
+    (all heads, all tokens).  Reported in the same unit (tokens/s)."""
+    import numpy as np
+    import oracle
+
+    sl = {n: np.ascontiguousarray(inp[n][:1]) for n in ("q", "k", "v", "alpha", "omega", "r")}
+    threads = max(1, min(oracle.max_threads(), w.H))
+    fn = oracle.diag_fwd if variant == "diag" else oracle.iso_fwd
+    t0 = time.perf_counter()
+    fn(sl["q"], sl["k"], sl["v"], sl["alpha"], sl["omega"], sl["r"], nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "batch row 0 of the workload (%d heads x %d tokens, %d of %d rows), "
+                      "fp64 C recurrence, %.1f s wall" % (w.H, w.T, 1, w.B, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--variant", default=None, help="override: diag | iso")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs the KDN mixer on a single "
+              "MI355X (heads and batch shard across GPUs with no communication); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from kalman_delta_rule_amd import api, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP GPU", file=sys.stderr)
+        sys.exit(1)
+    from kalman_delta_rule_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    dev = torch.device("cuda:0")
+    w = inputs.workload(args.workload)
+    if w.structure == "decode":
+        return bench_decode(args, w)
+    variant = args.variant or w.variant
+    print("[bench] generating %s (%s)" % (w.name, variant), file=sys.stderr, flush=True)
+    inp = inputs.make_fwd_inputs(w, variant)
+    io_dt = torch.bfloat16 if w.io == "bf16" else torch.float32
+    d = {}
+    for n in ("q", "k", "v", "alpha", "omega", "r"):
+        t = torch.from_numpy(inp[n])
+        d[n] = (t.to(io_dt) if n in ("q", "k", "v") else t).to(dev)
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    o = torch.empty((B, T, H, dv), dtype=io_dt, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    var_T = torch.empty((B, H, dk) if variant == "diag" else (B, H), dtype=torch.float32,
+                        device=dev)
+    fn = api.kdn_diag_fwd if variant == "diag" else api.kdn_iso_fwd
+    vkw = "p_T" if variant == "diag" else "b_T"
+
+    def step():
+        fn(d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], o=o, S_T=S_T, **{vkw: var_T})
+
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    tokens = B * T
+    value = tokens * args.steps / (ms_total / 1e3)
+    s_io = 2 if w.io == "bf16" else 4
+    alg = alg_bytes_fwd(variant, B, T, H, dk, dv, s_io)
+    achieved = alg / (ms_step / 1e3) / 1e9
+    key = "chunk_fwd_%s_%s_B%dT%dH%dd%d" % (variant, w.io, B, T, H, dk)
+    traffic = traffic_for(key)
+    print("[bench] %d steps: %.3f ms/step (events), wall %.3f s" % (args.steps, ms_step, wall),
+          file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: 3 x 1 GiB device copies done", file=sys.stderr,
+              flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, inp, variant)
+
+    line = {
+        "metric": "KDN mixer fwd tokens/sec at T=%d (1 GPU)" % T,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "variant": variant, "B": B, "T": T, "H": H, "dk": dk,
+                   "dv": dv, "chunk": 64, "io": w.io, "gates": "f32", "state": "f32",
+                   "global_batch": B, "seq_len": T, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "alg_bytes_per_launch": alg, "kernel": "kdn_chunk_fwd_kernel"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_decode(args, w):
+    """Decode workload: `w.steps` consecutive kdn_step calls (one token per
+    sequence each) from a seeded random state, inputs pre-staged."""
+    import torch
+    from kalman_delta_rule_amd import api, inputs
+
+    dev = torch.device("cuda:0")
+    variant = args.variant or "diag"
+    io_dt = torch.bfloat16
+    nsteps = w.steps
+    print("[bench] staging %d decode steps (%s)" % (nsteps, variant), file=sys.stderr, flush=True)
+    st = inputs.make_decode_state(w, variant)
+    S = torch.from_numpy(st["S0"]).to(dev)
+    var = torch.from_numpy(st["var0"]).to(dev)
+    seq = []
+    for s in range(nsteps):
+        x = inputs.make_decode_step(w, variant, s)
+        seq.append({n: (torch.from_numpy(x[n]).to(io_dt) if n in ("q", "k", "v")
+                        else torch.from_numpy(x[n])).to(dev) for n in x})
+    o = torch.empty((w.B, w.H, w.dv), dtype=io_dt, device=dev)
+    for s in range(min(args.warmup, nsteps)):
+        x = seq[s]
+        api.kdn_step(variant, x["q"], x["k"], x["v"], x["alpha"], x["omega"], x["r"], S, var, o=o)
+    torch.cuda.synchronize()
+    S.copy_(torch.from_numpy(st["S0"]).to(dev))
+    var.copy_(torch.from_numpy(st["var0"]).to(dev))
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for x in seq:
+        api.kdn_step(variant, x["q"], x["k"], x["v"], x["alpha"], x["omega"], x["r"], S, var, o=o)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_launch = ms_total / nsteps
+    alg = alg_bytes_step(variant, w.B, w.H, w.dk, w.dv, 2)
+    achieved = alg / (ms_launch / 1e3) / 1e9
+    line = {
+        "metric": "KDN decode tokens/sec (1 GPU)",
+        "value": w.B * nsteps / (ms_total / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": nsteps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_launch,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "variant": variant, "B": w.B, "H": w.H, "dk": w.dk,
+                   "dv": w.dv, "io": "bf16", "state": "f32"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_for("step_%s_B%dH%dd%d" % (variant, w.B, w.H, w.dk)),
+                     "alg_bytes_per_launch": alg, "kernel": "kdn_step_kernel"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -46,7 +46,7 @@
  *     16-byte aligned.
  *   - Preconditions (documented, not checked per element): r > 0,
  *     0 < alpha <= 1, omega >= 0, p0/b0 > 0, mu >= 0, all finite, and within
- *     every 64-token chunk the product of alpha over the chunk stays above
+ *     every 32-token chunk the product of alpha over the chunk stays above
  *     1e-30 in every channel (the chunked memory rescales keys by the
  *     cumulative decay from the chunk start).  Outside them results are
  *     unspecified (NaN propagates; nothing faults).
@@ -99,8 +99,9 @@ size_t kdn_fwd_workspace_size(int variant, int B, int T, int H, int dk, int dv,
  *   workspace / workspace_bytes: device scratch of at least
  *     kdn_fwd_workspace_size(...) bytes (may be NULL when that is 0)
  *   stream: a hipStream_t (NULL = the null stream)
- * S_T may alias S0 and p_T may alias p0 (the state is read before it is
- * overwritten); o must not alias any input.
+ * S_T may alias S0 and p_T may alias p0 exactly (the state is read before
+ * it is overwritten); a partial overlap of either pair, or o aliasing q, k
+ * or v, is rejected with KDN_ERR_INVALID_ARG.
  */
 kdn_status kdn_diag_fwd(int B, int T, int H, int dk, int dv, int io_dtype, float mu,
                         const void* q, const void* k, const void* v,

@@ -113,9 +113,15 @@ kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float
         KDN_ALIGNED(var0, "p0");
         KDN_ALIGNED(var_T, "p_T");
     }
-    if (var0 && var0 == var_T)
-        return fail(KDN_ERR_INVALID_ARG, "%s must not alias %s", iso ? "b_T" : "p_T",
-                    iso ? "b0" : "p0");
+    if (var0 && var0 != var_T) {
+        // each variance is read once at the start and written once at the end
+        // by the same lane, so only exact aliasing is safe
+        const size_t vb = (size_t)B * H * (iso ? 1 : dk) * sizeof(float);
+        const char *a0 = (const char*)var0, *a1 = (const char*)var_T;
+        if (a0 < a1 + vb && a1 < a0 + vb)
+            return fail(KDN_ERR_INVALID_ARG, "%s must either equal %s or not overlap it",
+                        iso ? "b_T" : "p_T", iso ? "b0" : "p0");
+    }
     if (o && (o == q || o == k || o == v))
         return fail(KDN_ERR_INVALID_ARG, "o must not alias q, k or v");
     if (S0 && S0 != S_T) {

@@ -75,6 +75,123 @@ __device__ __forceinline__ void mma_nt(f32x4& acc, const float* A, int lda, cons
                                                    B[row * ldb + k0 + kq], acc, 0, 0, 0);
 }
 
+// Two contractions sharing the B operand:  accA += A0 B^T,  accB += A1 B^T.
+// All fragments of the K loop are read from LDS before the first MFMA is
+// issued, so the LDS latency is paid once per call instead of once per MFMA.
+template <int K>
+__device__ __forceinline__ void mma2_nt(f32x4& acc0, f32x4& acc1, const bf16* A0,
+                                        const bf16* A1, int lda, const bf16* B, int ldb,
+                                        int lane)
+{
+    static_assert(K % 32 == 0, "K multiple of 32");
+    constexpr int NK = K / 32;
+    const int row = lane & 15, kg = 8 * (lane >> 4);
+    bf16x8 a0[NK], a1[NK], b[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        b[k] = *reinterpret_cast<const bf16x8*>(B + row * ldb + 32 * k + kg);
+        a0[k] = *reinterpret_cast<const bf16x8*>(A0 + row * lda + 32 * k + kg);
+        a1[k] = *reinterpret_cast<const bf16x8*>(A1 + row * lda + 32 * k + kg);
+    }
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[k], b[k], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[k], b[k], acc1, 0, 0, 0);
+    }
+}
+
+template <int K>
+__device__ __forceinline__ void mma2_nt(f32x4& acc0, f32x4& acc1, const float* A0,
+                                        const float* A1, int lda, const float* B, int ldb,
+                                        int lane)
+{
+    static_assert(K % 4 == 0, "K multiple of 4");
+    constexpr int NK = K / 4;
+    const int row = lane & 15, kq = lane >> 4;
+    float a0[NK], a1[NK], b[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        b[k] = B[row * ldb + 4 * k + kq];
+        a0[k] = A0[row * lda + 4 * k + kq];
+        a1[k] = A1[row * lda + 4 * k + kq];
+    }
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[k], b[k], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[k], b[k], acc1, 0, 0, 0);
+    }
+}
+
+// Operand fragments of one K-step of a 16x16 MFMA, by element type:
+//   bf16: 16x16x32 (K-step 32, 8 values per lane); fp32: 16x16x4 (K-step 4).
+// frag(base, ld, k0, lane) reads rows (lane & 15) of a [16][K] operand.
+template <typename T>
+struct Frag;
+template <>
+struct Frag<bf16> {
+    using type = bf16x8;
+    static constexpr int KSTEP = 32;
+    static __device__ __forceinline__ type load(const bf16* base, int ld, int k0, int lane)
+    {
+        return *reinterpret_cast<const bf16x8*>(base + (lane & 15) * ld + k0 + 8 * (lane >> 4));
+    }
+    static __device__ __forceinline__ void mma(f32x4& acc, const type& a, const type& b)
+    {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+};
+template <>
+struct Frag<float> {
+    using type = float;
+    static constexpr int KSTEP = 4;
+    static __device__ __forceinline__ type load(const float* base, int ld, int k0, int lane)
+    {
+        return base[(lane & 15) * ld + k0 + (lane >> 4)];
+    }
+    static __device__ __forceinline__ void mma(f32x4& acc, const type& a, const type& b)
+    {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+};
+
+// acc += A * X where A is a 16x16 operand in LDS (rows at A, K = 16
+// contiguous) and X (K x N = 16 x 16) is an accumulator in D layout (lane
+// holds X[4*(l>>4) + r][l & 15]).  For bf16 that layout is exactly the B
+// operand of the 16x16x16 MFMA, so X never leaves registers (it is rounded to
+// bf16, as any MFMA operand); fp32 takes a hop through `scratch` ([16][17]
+// floats of wave-private LDS) because its 16x16x4 B layout differs.
+template <typename T>
+struct AccB;
+template <>
+struct AccB<bf16> {
+    static __device__ __forceinline__ void mma(f32x4& acc, const bf16* A, int lda, const f32x4& x,
+                                               float* scratch, int lane)
+    {
+        (void)scratch;
+        const bf16x4 a = *reinterpret_cast<const bf16x4*>(A + (lane & 15) * lda + 4 * (lane >> 4));
+        const bf16x4 b = bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]),
+                                static_cast<bf16>(x[2]), static_cast<bf16>(x[3])};
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+    }
+};
+template <>
+struct AccB<float> {
+    static __device__ __forceinline__ void mma(f32x4& acc, const float* A, int lda, const f32x4& x,
+                                               float* scratch, int lane)
+    {
+        const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            scratch[(4 * g + r) * 17 + c] = x[r];
+        wave_lds_sync();
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[c * lda + k0 + g],
+                                                       scratch[(k0 + g) * 17 + c], acc, 0, 0, 0);
+        wave_lds_sync();
+    }
+};
+
 // Same contraction with an fp32 A operand in LDS and a B operand of type T:
 // for bf16 the A values are rounded to bf16 on the fly (K multiple of 16).
 __device__ __forceinline__ void mma_nt_f32a(f32x4& acc, const float* A, int lda, const bf16* B,

@@ -5,7 +5,7 @@ tensors with the shapes and distributions of the mixer workloads, so that the
 HIP path and the fp64 oracle consume identical values.  It imports nothing
 from the rest of the package.
 
-Recipe (per (b,t,h), numpy PCG64, draws in fp32):
+Recipe (per (b,t,h), numpy PCG64, draws and transforms in fp32):
   q, k ~ N(0, I) then L2-normalised over d_k; v ~ N(0, I);
   alpha = sigmoid(N(2, 0.5)) per key channel (the per-channel decay);
   omega = softplus(N(0, 1)) per key channel (Diagonal) or per head (Isotropic);
@@ -17,6 +17,9 @@ from __future__ import annotations
 
 from dataclasses import dataclass, replace
 from typing import Optional
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -66,26 +69,29 @@ def workload(i: int, **overrides) -> Workload:
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Round fp32 values to the nearest bf16 (ties to even); returns fp32."""
+    """Round fp32 values to the nearest bf16 (ties to even); returns fp32.
+    uint32 arithmetic cannot wrap for finite inputs (only NaN bit patterns
+    reach the top of the range)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> 16) & 1
-    out = ((bits + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
+    bits = x.view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    out = (bits + (lsb + np.uint32(0x7FFF))) & np.uint32(0xFFFF0000)
     return out.view(np.float32)
 
 
 def _sigmoid(x):
-    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+    x = np.asarray(x, dtype=np.float32)
+    return (np.float32(1.0) / (np.float32(1.0) + np.exp(-x))).astype(np.float32)
 
 
 def _softplus(x):
-    x = x.astype(np.float64)
-    return (np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))).astype(np.float32)
+    x = np.asarray(x, dtype=np.float32)
+    return (np.maximum(x, np.float32(0.0)) + np.log1p(np.exp(-np.abs(x)))).astype(np.float32)
 
 
 def _unit(x, axis=-1):
-    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=axis, keepdims=True))
-    return (x / np.maximum(n, 1e-30)).astype(np.float32)
+    n = np.sqrt(np.sum(np.square(x, dtype=np.float32), axis=axis, keepdims=True))
+    return (x / np.maximum(n, np.float32(1e-30))).astype(np.float32)
 
 
 def _draw_tokens(rng, variant, B, T, H, dk, dv, io):
@@ -93,22 +99,54 @@ def _draw_tokens(rng, variant, B, T, H, dk, dv, io):
     q = _unit(rng.standard_normal((B, T, H, dk), dtype=f32))
     k = _unit(rng.standard_normal((B, T, H, dk), dtype=f32))
     v = rng.standard_normal((B, T, H, dv), dtype=f32)
-    alpha = _sigmoid(2.0 + 0.5 * rng.standard_normal((B, T, H, dk), dtype=f32))
+    alpha = _sigmoid(f32(2.0) + f32(0.5) * rng.standard_normal((B, T, H, dk), dtype=f32))
     wshape = (B, T, H, dk) if variant == "diag" else (B, T, H)
     omega = _softplus(rng.standard_normal(wshape, dtype=f32))
     r = _softplus(rng.standard_normal((B, T, H), dtype=f32))
     return q, k, v, alpha, omega, r
 
 
-def make_fwd_inputs(w: Workload, variant: Optional[str] = None) -> dict:
+TOKEN_BLOCK = 1024   # tokens per independently seeded generation block
+
+
+def make_fwd_inputs(w: Workload, variant: Optional[str] = None, threads: int = 0) -> dict:
     """Forward inputs for workload ``w`` as fp32 numpy arrays (q, k, v already
-    rounded to bf16 when ``w.io == 'bf16'``) plus S0 / p0 (or b0)."""
+    rounded to bf16 when ``w.io == 'bf16'``) plus S0 / p0 (or b0).
+
+    Each (batch row, block of TOKEN_BLOCK tokens) draws from its own PCG64
+    stream seeded by (seed, variant, b, block), so the result does not depend
+    on how many threads generate it."""
     variant = variant or w.variant
     assert variant in ("diag", "iso")
-    rng = np.random.Generator(np.random.PCG64(w.seed))
     B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
-    q, k, v, alpha, omega, r = _draw_tokens(rng, variant, B, T, H, dk, dv, w.io)
+    f32 = np.float32
+    q = np.empty((B, T, H, dk), f32)
+    k = np.empty((B, T, H, dk), f32)
+    v = np.empty((B, T, H, dv), f32)
+    alpha = np.empty((B, T, H, dk), f32)
+    omega = np.empty((B, T, H, dk) if variant == "diag" else (B, T, H), f32)
+    r = np.empty((B, T, H), f32)
+    vcode = 0 if variant == "diag" else 1
+    blocks = [(b, t0) for b in range(B) for t0 in range(0, T, TOKEN_BLOCK)]
+
+    def fill(job):
+        b, t0 = job
+        t1 = min(T, t0 + TOKEN_BLOCK)
+        rng = np.random.Generator(np.random.PCG64([w.seed, vcode, b, t0 // TOKEN_BLOCK]))
+        parts = _draw_tokens(rng, variant, 1, t1 - t0, H, dk, dv, w.io)
+        for dst, src in zip((q, k, v, alpha, omega, r), parts):
+            dst[b:b + 1, t0:t1] = src
+
+    if threads <= 0:
+        threads = min(16, os.cpu_count() or 1)
+    if threads > 1 and len(blocks) > 1:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(fill, blocks))
+    else:
+        for job in blocks:
+            fill(job)
     if w.structure == "retrieval":
+        rng = np.random.Generator(np.random.PCG64([w.seed, vcode, 1 << 20]))
         _insert_retrieval(rng, q, k, v, n_pairs=min(512, T // 2))
     if w.io == "bf16":
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)

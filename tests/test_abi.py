@@ -112,7 +112,6 @@ def _fwd_call(L, variant="diag", **kw):
     (dict(q=MIS), -1, "aligned"),
     (dict(S_T=MIS), -1, "aligned"),
     (dict(o=P), -1, "alias"),
-    (dict(var0=P + 16384), -1, "alias"),
     (dict(S0=P + 8192 + 64), -1, "overlap"),
     (dict(B=1 << 14, T=1 << 14, H=16), -2, "2^31"),
 ])
@@ -120,6 +119,15 @@ def test_fwd_validation(L, variant, bad, code, needle):
     st = _fwd_call(L, variant, **bad)
     assert st == code
     assert needle in L.kdn_last_error_message().decode()
+
+
+@cpu_only
+@pytest.mark.parametrize("variant,offset", [("diag", 16), ("iso", 4)])
+def test_fwd_variance_partial_overlap(L, variant, offset):
+    # exact aliasing of the initial and final variances is allowed, a partial
+    # overlap is not
+    assert _fwd_call(L, variant, var0=P + 16384 + offset) == -1
+    assert "overlap" in L.kdn_last_error_message().decode()
 
 
 @cpu_only

@@ -70,6 +70,7 @@ def test_decode_small(ora, variant, io, dims):
     assert max(err.values()) <= TOL[io], err
 
 
+@pytest.mark.timeout(400)
 @pytest.mark.parametrize("variant", ["diag", "iso"])
 def test_config4_decode_full(ora, variant):
     w = inputs.workload(4)
@@ -115,6 +116,7 @@ def test_gain_scan(ora, variant, io, shape):
     assert err["kappa"] <= 1e-4 and err["var"] <= 1e-4, err
 
 
+@pytest.mark.timeout(400)
 def test_gain_scan_config2_shape(ora):
     w = inputs.workload(2)
     err = _gain_compare(ora, "diag", w, heads=sample_heads(w.B, w.H, 4, seed=2))

@@ -119,13 +119,17 @@ def test_state_output_may_alias_initial_state(ora, variant):
     inp = inputs.make_fwd_inputs(w)
     rng = np.random.default_rng(10)
     S0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    var0 = rng.uniform(0.2, 2.0, (B, H, dk) if variant == "diag" else (B, H)).astype(np.float32)
     d = to_dev(inp, "bf16")
     Sdev = torch.from_numpy(S0).cuda()
+    vdev = torch.from_numpy(var0).cuda()
     fn = api.kdn_diag_fwd if variant == "diag" else api.kdn_iso_fwd
-    o, S, var = fn(d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], S0=Sdev, S_T=Sdev)
+    kw = {"p0": vdev, "p_T": vdev} if variant == "diag" else {"b0": vdev, "b_T": vdev}
+    o, S, var = fn(d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], S0=Sdev, S_T=Sdev,
+                   **kw)
     torch.cuda.synchronize()
-    assert S.data_ptr() == Sdev.data_ptr()
-    res = oracle_heads(ora, variant, inp, [(0, 0), (0, 1)], S0=S0)
+    assert S.data_ptr() == Sdev.data_ptr() and var.data_ptr() == vdev.data_ptr()
+    res = oracle_heads(ora, variant, inp, [(0, 0), (0, 1)], S0=S0, var0=var0)
     err = compare_heads(res, host(o), host(S), host(var), [(0, 0), (0, 1)])
     assert max(err.values()) <= TOL["bf16"], err
 
@@ -194,13 +198,16 @@ def _sampled(ora, widx, n_heads, variant=None):
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
 
 
+@pytest.mark.timeout(400)
 def test_config1_iso_full(ora):
     _sampled(ora, 1, 6)
 
 
+@pytest.mark.timeout(400)
 def test_config2_diag_full(ora):
     _sampled(ora, 2, 6)
 
 
+@pytest.mark.timeout(400)
 def test_config3_long_full(ora):
     _sampled(ora, 3, 1)
