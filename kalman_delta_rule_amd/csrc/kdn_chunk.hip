@@ -1,16 +1,15 @@
-// kdn_chunk.hip -- chunkwise KDN forward ("walk" regime), gfx950.
+// kdn_chunk.hip -- chunkwise KDN forward, gfx950.
 //
-// One workgroup owns one (batch, head, value tile of DVT columns) and walks
-// the sequence in chunks of C = 32 tokens.  The memory state S (dk x DVT,
-// fp32) stays in MFMA accumulators for the whole sequence (held transposed,
-// S^T[j][i]); the variance state stays in registers.
+// One workgroup owns one (batch, head, tile of DVT value columns) and walks
+// the sequence in chunks of C = 16 tokens.  The memory state S (dk x DVT,
+// fp32) lives in MFMA accumulators for the whole sequence; the variance state
+// lives in registers of the chain lanes.
 //
 // Method (KDN reading notes, method part):
 //   gain   §4-§5 (Diagonal):  p^_t = alpha_t^2 p_{t-1} + omega_t,
 //            p_t = p^_t / (1 + (mu / r_t) k_t^2 p^_t)
 //          §7 (Isotropic): a_t = mean alpha^2, b^_t = a_t b_{t-1} + omega_t,
-//            b_t = b^_t / (1 + mu |k_t|^2 b^_t / (d_k r_t)), as a wavefront
-//            scan of 2x2 Moebius maps (§6 Eq. (32)-(39)).
+//            b_t = b^_t / (1 + mu |k_t|^2 b^_t / (d_k r_t))
 //   memory §6: S_t = (I - kappa_t k_t^T) D_t S_{t-1} + kappa_t v_t^T,
 //          kappa_t = p^_t (.) k_t / (r_t + z_t),  z_t = sum_i p^_t,i k_t,i^2,
 //          o_t = S_t^T q_t (read after the write).
@@ -18,137 +17,204 @@
 // G_t = prod_{s<=t} alpha_s the cumulative decay from the chunk start:
 //   Kb = k (.) G,  Ktp = p^ (.) k / G,  Qb = q (.) G
 //   L' = Kb Ktp^T  (diagonal = z_t),  Aqk = tril(Qb Ktp^T) (inclusive)
-//   (diag(r + z) + tril(L', -1)) Delta' = V - Kb S        [Delta' = Delta/(r+z)]
-//   O = Qb S + Aqk Delta',   S <- diag(G_C) (S + Ktp^T Delta')
-// equal to the token recurrence in exact arithmetic.  Ragged tails are padded
-// with identity tokens (k = q = v = 0, alpha = 1, omega = 0, r = 1).
+//   M  = diag(r + z) + tril(L', -1),   T = M^-1
+//   Delta' = T (V - Kb S),   O = Qb S + Aqk Delta',
+//   S <- diag(G_C) (S + Ktp^T Delta')
+// which equals the token recurrence in exact arithmetic.  Ragged tails are
+// padded with identity tokens (k = q = v = 0, alpha = 1, omega = 0, r = 1).
 //
-// Workgroup schedule (warp-specialised, two barriers per chunk):
-//   waves [0, NMM)      "memory" waves: each owns 16 value columns and runs
-//                        the MFMA part of chunk c (L', Aqk, diagonal-block
-//                        inverses recomputed per wave, R, O, triangular solve,
-//                        state update) with wave-private LDS only;
-//   waves NMM..NMM+3    "gain" waves, during the same segment: the serial
-//                        variance / decay recurrence of chunk c+1 (one lane per
-//                        key channel, or the isotropic DPP scan), and the
-//                        loader for v and r of later chunks.  Their raw inputs
-//                        sit in a rolling register buffer refilled one chunk
-//                        ahead, so global latency overlaps a whole segment.
-//   barrier (LDS only: in-flight global prefetches are not waited for)
-//   all waves           elementwise build of Kb, Ktp, Ktp^T, Qb for chunk c+1
-//   barrier
+// Workgroup pipeline, one LDS barrier per step.  In step c:
+//   loader wave   copies the raw inputs of chunk c+5 straight from global
+//                 memory into LDS (no registers), and v of chunk c+2;
+//   chain wave(s) run the serial variance / decay recurrence of chunk c+3
+//                 (one lane per key channel; the isotropic variant reduces
+//                 over channels per token and runs the scalar recurrence);
+//   memory waves  build Kb, Qb, Ktp of chunk c+2 (elementwise), then apply
+//                 chunk c to their 16 value columns on the matrix cores;
+//   factor wave   forms L', Aqk and T = M^-1 of chunk c+1 (matrix cores for
+//                 the products, forward substitution for the inverse).
+// Every buffer is indexed by chunk number modulo its lifetime, so no stage
+// waits for another inside a step.
 #include "kdn_common.h"
 #include "kdn_internal.h"
 
 namespace kdn {
 
-constexpr int CH = 32;  // tokens per chunk
+constexpr int CH = 16;      // tokens per chunk
+constexpr int NSTAGE = 4;   // raw-input slots: in flight (2 steps) -> chain -> elementwise
+constexpr int NOPS = 3;     // operand slots: elementwise -> factor -> memory
+constexpr int NRING = 8;    // per-token scalar rings
+constexpr int LEAD = 5;     // steps between loading a chunk and applying it
 
-// Raw storage of one IO value in a 32-bit register (no conversion at load
-// time, so the load is only waited for where the value is used).
-__device__ __forceinline__ float raw_bits(float x) { return x; }
-__device__ __forceinline__ float raw_bits(bf16 x)
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Direct global -> LDS copy: lane l's 16 (or 4) bytes land at dst + 16 l
+// (4 l).  dst must be uniform over the wave.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* src, void* dst)
 {
-    return __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, x));
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
 }
-template <typename IO>
-__device__ __forceinline__ float from_raw_bits(float r);
-template <>
-__device__ __forceinline__ float from_raw_bits<float>(float r)
+__device__ __forceinline__ void dma4(const void* src, void* dst)
 {
-    return r;
-}
-template <>
-__device__ __forceinline__ float from_raw_bits<bf16>(float r)
-{
-    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, r) << 16);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 4, 0, 0);
 }
 
-template <typename IO>
-struct VecOf;
-template <>
-struct VecOf<bf16> {
-    using type = bf16x8;
-};
-template <>
-struct VecOf<float> {
-    using type = f32x4;
-};
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ void lds_barrier()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+template <typename IO>
+struct Vec16;
+template <>
+struct Vec16<bf16> {
+    using type = bf16x8;
+};
+template <>
+struct Vec16<float> {
+    using type = f32x4;
+};
+
+// 16x16x16 contraction pieces (K = 16) by element type.  An operand fragment
+// holds, for lane (g = l >> 4, c = l & 15), the values X[m = c][k] of an A
+// operand, or X[k][n = c] of a B operand, for the k the lane feeds (bf16: one
+// 16x16x16 MFMA, k = 4 g + e; fp32: four 16x16x4 MFMAs, value s at k = 4 s + g).
+//   lds   : row-major [m or n][k] in LDS (k contiguous)
+//   lds_t : row-major [k][m or n] in LDS (k strided)
+//   acc   : a 16x16 accumulator X in D layout, as the B operand X or the A
+//           operand X^T.  bf16 only rounds (the D layout is the bf16 operand
+//           layout); fp32 goes through a wave-private [16][17] LDS scratch.
+template <typename T>
+struct F16;
+template <>
+struct F16<bf16> {
+    using type = bf16x4;
+    static __device__ __forceinline__ type lds(const bf16* p, int ld, int lane)
+    {
+        return *reinterpret_cast<const bf16x4*>(p + (lane & 15) * ld + 4 * (lane >> 4));
+    }
+    static __device__ __forceinline__ type lds_t(const bf16* p, int ld, int lane)
+    {
+        const bf16* q = p + 4 * (lane >> 4) * ld + (lane & 15);
+        return bf16x4{q[0], q[ld], q[2 * ld], q[3 * ld]};
+    }
+    static __device__ __forceinline__ type acc(const f32x4& x, float* scratch, int lane)
+    {
+        (void)scratch;
+        (void)lane;
+        return bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                      static_cast<bf16>(x[3])};
+    }
+    static __device__ __forceinline__ void mma(f32x4& d, const type& a, const type& b)
+    {
+        d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, d, 0, 0, 0);
+    }
+};
+template <>
+struct F16<float> {
+    struct type {
+        float v[4];
+    };
+    static __device__ __forceinline__ type lds(const float* p, int ld, int lane)
+    {
+        const float* q = p + (lane & 15) * ld + (lane >> 4);
+        return type{{q[0], q[4], q[8], q[12]}};
+    }
+    static __device__ __forceinline__ type lds_t(const float* p, int ld, int lane)
+    {
+        const float* q = p + (lane >> 4) * ld + (lane & 15);
+        return type{{q[0], q[4 * ld], q[8 * ld], q[12 * ld]}};
+    }
+    static __device__ __forceinline__ type acc(const f32x4& x, float* scratch, int lane)
+    {
+        const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            scratch[(4 * g + r) * 17 + c] = x[r];
+        wave_lds_sync();
+        type t;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            t.v[s] = scratch[(4 * s + g) * 17 + c];
+        wave_lds_sync();
+        return t;
+    }
+    static __device__ __forceinline__ void mma(f32x4& d, const type& a, const type& b)
+    {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], d, 0, 0, 0);
+    }
+};
+
 template <typename IO, int DK, int DVT, bool ISO>
 struct ChunkSmem {
     static constexpr int C = CH;
-    static constexpr int NB = C / 16;
-    static constexpr int NMM = DVT >= 64 ? DVT / 32 : DVT / 16;  // memory waves
-    static constexpr int NJ = DVT / 16 / NMM;              // 16-column tiles per memory wave
-    static constexpr int PADE = 16 / sizeof(IO);
-    static constexpr int LD_K = DK + PADE;  // Kb, Ktp, Qb, ShT rows
-    static constexpr int LD_T = C + PADE;   // KtpT, Aqk, Delta rows
-    static constexpr int LD_V = DVT + PADE;
-    static constexpr int LD_L = C + 4;      // fp32 L'
-    static constexpr int LD_B = 16 + PADE;  // 16-wide blocks
-    static constexpr int LD_G = DK + 4;     // fp32 gain staging rows
-    static constexpr int LD_D = 16 + 4;     // fp32 transposed diagonal blocks
-    struct MemWave {
-        alignas(16) float LdT[NB * 16 * LD_D];  // diagonal blocks of L', transposed
-        alignas(16) IO Loff[C * LD_T];          // L' below the diagonal blocks
-        alignas(16) IO Aqk[C * LD_T];
-        alignas(16) IO Tii[NB * 16 * LD_B];
-        alignas(16) IO Delta[NJ * 16 * LD_T];
-        alignas(16) IO Rhs[NJ * 16 * LD_B];
+    static constexpr int NMM = DVT / 16;           // memory waves
+    static constexpr int NCW = ISO ? 1 : DK / 64;  // chain waves
+    static constexpr int PAD = 16 / sizeof(IO);
+    static constexpr int LD_K = DK + PAD;  // Kb, Qb, Ktp rows (matrix-core operands)
+    static constexpr int LD_S = C + PAD;   // T, Aqk rows
+    // raw inputs of one chunk as rows of tokens, unpadded (filled by direct
+    // copies); the chain overwrites alpha with G and (Diagonal) omega with p^
+    struct Stage {
+        alignas(16) float alpha[C * DK];
+        alignas(16) float omega[ISO ? 4 : C * DK];
+        alignas(16) IO k[C * DK];
+        alignas(16) IO q[C * DK];
     };
-    // gain staging [t][i], rewritten in place chunk after chunk:
-    //   A  : alpha (fp32)  -> cumulative decay G
-    //   W  : omega (fp32, Diagonal only)
-    //   Kst: raw k (io dtype)
-    alignas(16) float A[C * LD_G];
-    alignas(16) float W[ISO ? 4 : C * LD_G];
-    alignas(16) IO Kst[C * LD_K];
-    alignas(16) float bhat[C];  // isotropic predicted variance
-    alignas(16) IO Kb[C * LD_K];
-    alignas(16) IO Qb[C * LD_K];
-    // write keys are produced by the gain lanes while the memory waves still
-    // read the previous chunk's: two buffers, indexed by chunk parity
-    alignas(16) IO Ktp[2][C * LD_K];
-    alignas(16) IO KtpT[2][DK * LD_T];
-    alignas(16) IO ShT[DVT * LD_K];
-    alignas(16) IO V[2][C * LD_V];
-    alignas(16) float gC[DK];
-    alignas(16) float rr[4][C];    // r_t ring
-    alignas(16) float murt[4][C];  // mu / r_t ring
-    alignas(16) float wring[4][C]; // isotropic omega_t ring
-    MemWave mw[NMM];
+    struct Ops {
+        alignas(16) IO Kb[C * LD_K];
+        alignas(16) IO Qb[C * LD_K];
+        alignas(16) IO Ktp[C * LD_K];
+        alignas(16) float gC[DK];
+    };
+    struct Fac {
+        alignas(16) IO T[C * LD_S];
+        alignas(16) IO Aqk[C * LD_S];
+    };
+    Stage st[NSTAGE];
+    alignas(16) IO v[3][C * DVT];    // rows of DVT, 16-byte blocks xor-swizzled by row
+    Ops op[NOPS];
+    Fac fac[2];
+    alignas(16) float Mt[C * 20];    // factor: M^T (fp32), rows padded to 20
+    alignas(16) float dinv[C];       // factor: 1 / (r_t + z_t)
+    alignas(16) float rr[NRING][C];  // r_t
+    alignas(16) float wr[NRING][C];  // isotropic omega_t
+    alignas(16) float bh[NRING][C];  // isotropic b^_t
+    alignas(16) float scratch[sizeof(IO) == 4 ? NMM : 1][16 * 17];
 };
 
-// memory waves + 6 gain / loader waves
-#define KDN_CHUNK_THREADS(DVT) (64 * (((DVT) >= 64 ? (DVT) / 32 : (DVT) / 16) + 6))
+#define KDN_CHUNK_THREADS(DK, DVT, ISO) (64 * ((DVT) / 16 + ((ISO) ? 1 : (DK) / 64) + 2))
 
 template <typename IO, int DK, int DVT, bool ISO>
-__global__ __launch_bounds__(KDN_CHUNK_THREADS(DVT)) void kdn_chunk_fwd_kernel(FwdArgs a)
+__global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_fwd_kernel(
+    FwdArgs a)
 {
-    constexpr int C = CH;
-    constexpr int NB = C / 16;
-    using SM0 = ChunkSmem<IO, DK, DVT, ISO>;
-    constexpr int NMM = SM0::NMM;
-    constexpr int NJ = SM0::NJ;
-    constexpr int NW = NMM + 6;
-    constexpr int NT = NW * 64;
-    constexpr int NCH = DK / 64;         // waves for one lane per key channel
-    constexpr int VE = 16 / sizeof(IO);  // IO elements per 16-byte vector
-    constexpr int NV4 = VE / 4;          // fp32 16-byte vectors per unit
-    using VecIO = typename VecOf<IO>::type;
     using SM = ChunkSmem<IO, DK, DVT, ISO>;
+    constexpr int C = CH;
+    constexpr int NMM = SM::NMM;
+    constexpr int NCW = SM::NCW;
+    constexpr int LD_K = SM::LD_K;
+    constexpr int LD_S = SM::LD_S;
+    constexpr int VE = 16 / sizeof(IO);  // IO elements per 16 bytes
     static_assert(sizeof(SM) <= 160 * 1024, "LDS budget");
+    static_assert(DK % 64 == 0 && DVT % 16 == 0, "tile shape");
+    using F = F16<IO>;
+    using FR = Frag<IO>;
+    using VecIO = typename Vec16<IO>::type;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int g4 = lane >> 4, c16 = lane & 15;
 
     // XCD-aware tile order: blocks are dispatched round-robin over the 8
@@ -163,540 +229,411 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DVT)) void kdn_chunk_fwd_kernel(F
     const int b = bh / a.H, h = bh % a.H;
     const int j0 = tile * DVT;
     const int T = a.T, H = a.H, dv = a.dv;
-    const IO* __restrict__ qg = reinterpret_cast<const IO*>(a.q);
-    const IO* __restrict__ kg = reinterpret_cast<const IO*>(a.k);
-    const IO* __restrict__ vg = reinterpret_cast<const IO*>(a.v);
-    IO* __restrict__ og = reinterpret_cast<IO*>(a.o);
-    const size_t ts_k = (size_t)H * DK;  // elements between consecutive tokens
-    const size_t ts_v = (size_t)H * dv;
-    const size_t base_k = ((size_t)b * T * H + h) * DK;
-    const size_t base_v = ((size_t)b * T * H + h) * dv;
-    const size_t base_r = (size_t)b * T * H + h;
     const float mu = a.mu;
     const int nchunks = (T + C - 1) / C;
-    auto n_valid = [&](int cc) { return min(C, T - cc * C); };
+    auto n_valid = [&](int x) { return min(C, T - x * C); };
+    // global offsets (elements) of token t's row for this head
+    auto row_k = [&](int t) { return (((size_t)b * T + t) * H + h) * DK; };
+    auto row_v = [&](int t) { return (((size_t)b * T + t) * H + h) * dv; };
+    auto row_s = [&](int t) { return ((size_t)b * T + t) * H + h; };
 
-    // ---- roles
-    const bool is_mm = wave < NMM;
-    const int gw = wave - NMM;
-    const bool is_chain = !ISO && !is_mm && gw < NCH;
-    const bool is_scan = ISO && !is_mm && gw == 0;
-    const bool is_loader = !is_mm && gw == 5;
-    const int ch_i = (gw * 64 + lane) & (DK - 1);  // chain lane's key channel
-    if (is_chain || is_scan)
-        __builtin_amdgcn_s_setprio(2);  // the serial recurrence is the critical path
-
-    // ------------------------------------------------------------ units
-    // Every gain-side thread owns UPT units of (token t, VE consecutive key
-    // channels); consecutive lanes cover consecutive channels of a token row,
-    // so global loads are coalesced and LDS row accesses are conflict-free.
-    // The memory waves take no units (their registers hold the state).
-    constexpr int NTU = NT - NMM * 64;  // threads sharing the units
-    const int utid = tid - NMM * 64;
-    constexpr int UPR = DK / VE;        // units per token row
-    constexpr int NUNITS = C * UPR;
-    constexpr int UPT = (NUNITS + NTU - 1) / NTU;
-    struct Stage {
-        f32x4 al[NV4], om[NV4];
-        f32x4 kn;  // raw 16 bytes of k
-    };
-    Stage st[UPT];
-    f32x4 kcur[UPT], qcur[UPT];  // raw k, q of the chunk whose operands are built next
-
-    // global -> registers: gates and k of chunk cs (staged later), q of chunk cq
-    auto issue_loads = [&](int cs, int cq) {
-        const int nvs = (cs < nchunks) ? n_valid(cs) : 0;
-        const int nvq = (cq < nchunks) ? n_valid(cq) : 0;
-        const size_t sbase = base_k + (size_t)(cs * C) * ts_k;  // uniform
-        const size_t qbase = base_k + (size_t)(cq * C) * ts_k;
-#pragma unroll
-        for (int m = 0; m < UPT; ++m) {
-            const int u = utid + NTU * m;
-            const int t = u / UPR, i0 = (u % UPR) * VE;
-            const uint32_t off = (uint32_t)(t * ts_k + i0);
-            const bool uval = u < NUNITS;
-#pragma unroll
-            for (int e = 0; e < NV4; ++e) {
-                st[m].al[e] = f32x4{1.f, 1.f, 1.f, 1.f};
-                st[m].om[e] = zero4();
-            }
-            st[m].kn = zero4();
-            qcur[m] = zero4();
-            if (uval && t < nvs) {
-#pragma unroll
-                for (int e = 0; e < NV4; ++e) {
-                    st[m].al[e] = *reinterpret_cast<const f32x4*>(a.alpha + sbase + off + 4 * e);
-                    if (!ISO)
-                        st[m].om[e] =
-                            *reinterpret_cast<const f32x4*>(a.omega + sbase + off + 4 * e);
-                }
-                st[m].kn = *reinterpret_cast<const f32x4*>(kg + sbase + off);
-            }
-            if (uval && t < nvq)
-                qcur[m] = *reinterpret_cast<const f32x4*>(qg + qbase + off);
-        }
-    };
-    // registers -> LDS staging of chunk cs (identity tokens past the end)
-    auto stage_store = [&](int cs) {
-        if (cs >= nchunks)
-            return;
-#pragma unroll
-        for (int m = 0; m < UPT; ++m) {
-            const int u = utid + NTU * m;
-            if (u < NUNITS) {
-                const int t = u / UPR, i0 = (u % UPR) * VE;
-#pragma unroll
-                for (int e = 0; e < NV4; ++e) {
-                    *reinterpret_cast<f32x4*>(&sm.A[t * SM::LD_G + i0 + 4 * e]) = st[m].al[e];
-                    if (!ISO)
-                        *reinterpret_cast<f32x4*>(&sm.W[t * SM::LD_G + i0 + 4 * e]) =
-                            st[m].om[e];
-                }
-                *reinterpret_cast<f32x4*>(&sm.Kst[t * SM::LD_K + i0]) = st[m].kn;
-            }
-        }
-    };
-    // segment 2 (every wave): decayed read keys / queries of chunk cn, then
-    // stage chunk cn + 1 into the slots just read (same thread, same addresses)
-    auto elementwise = [&](int cn) {
-        if (cn < nchunks) {
-#pragma unroll
-            for (int m = 0; m < UPT; ++m) {
-                const int u = utid + NTU * m;
-                if (u < NUNITS) {
-                    const int t = u / UPR, i0 = (u % UPR) * VE;
-                    const VecIO kv = __builtin_bit_cast(VecIO, kcur[m]);
-                    const VecIO qv = __builtin_bit_cast(VecIO, qcur[m]);
-                    VecIO kb, qb;
-#pragma unroll
-                    for (int e = 0; e < VE; ++e) {
-                        const float G = sm.A[t * SM::LD_G + i0 + e];
-                        kb[e] = from_f32<IO>(to_f32(kv[e]) * G);
-                        qb[e] = from_f32<IO>(to_f32(qv[e]) * G);
-                        if (t == C - 1)
-                            sm.gC[i0 + e] = G;
-                    }
-                    *reinterpret_cast<VecIO*>(&sm.Kb[t * SM::LD_K + i0]) = kb;
-                    *reinterpret_cast<VecIO*>(&sm.Qb[t * SM::LD_K + i0]) = qb;
-                }
-            }
-        }
-        stage_store(cn + 1);
-#pragma unroll
-        for (int m = 0; m < UPT; ++m)
-            kcur[m] = st[m].kn;
-    };
-
-    // ------------------------------------------------------------ loader
-    constexpr int PIECES_ROW = DVT / VE;
-    constexpr int NPL = C * PIECES_ROW / 64;  // 16-byte v pieces per loader lane
-    f32x4 vreg[NPL];
-    float rreg = 1.f, wreg = 0.f;
-    auto loader_load = [&](int cv, int cr) {
-        const int nvv = (cv < nchunks) ? n_valid(cv) : 0;
-        const IO* vc = vg + base_v + (size_t)(cv * C) * ts_v;  // uniform
-#pragma unroll
-        for (int m = 0; m < NPL; ++m) {
-            const int p = lane + 64 * m;
-            const int t = p / PIECES_ROW, sg = p % PIECES_ROW;
-            vreg[m] = zero4();
-            if (t < nvv)
-                vreg[m] = *reinterpret_cast<const f32x4*>(vc + (uint32_t)(t * ts_v + j0 + sg * VE));
-        }
-        const int t = cr * C + lane;
-        const bool ok = lane < C && t < T;
-        rreg = ok ? a.r[base_r + (size_t)t * H] : 1.f;
-        if (ISO)
-            wreg = ok ? a.omega[base_r + (size_t)t * H] : 0.f;
-    };
-
-    // ------------------------------------------------------------ prologue
-    if (!is_mm) {
-        issue_loads(0, 0);
-        stage_store(0);
-#pragma unroll
-        for (int m = 0; m < UPT; ++m)
-            kcur[m] = st[m].kn;
-        // staging loads are always issued one whole segment before their use:
-        // gates / k of chunk c+2 and q of chunk c+1 leave at the end of
-        // iteration c-1 and are consumed in the elementwise step of iteration c
-        issue_loads(1, 0);
-    }
-    if (is_loader) {
-        if (lane < C) {
-            const bool ok = lane < T;
-            const float rt = ok ? a.r[base_r + (size_t)lane * H] : 1.f;
-            sm.rr[0][lane] = rt;
-            sm.murt[0][lane] = mu / rt;
-            if (ISO)
-                sm.wring[0][lane] = ok ? a.omega[base_r + (size_t)lane * H] : 0.f;
-        }
-        loader_load(0, 1);
-    }
-
-    // Every role runs the same sequence of barriers: one after the prologue,
-    // then two per iteration c = -1 .. nchunks-1 (s_barrier counts arrivals,
-    // so the roles stay in lockstep while their register live ranges stay
-    // apart).  In iteration c the gain side works on chunk c+1 and stages
-    // chunk c+2 while the memory waves multiply chunk c.
-    if (is_mm) {
-        // ================= memory waves =================
-        // wave owns NJ tiles of 16 value columns: local columns jw + 16 jt + ...
-        const int jw = wave * 16 * NJ;
-        f32x4 Sacc[NJ][DK / 16];
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-            for (int n = 0; n < DK / 16; ++n)
-                Sacc[jt][n] = zero4();
-        // accumulator layout: Sacc[jt][n][r] = S[i = 16 n + 4 g4 + r][j = jw + 16 jt + c16]
+    if (wave < NMM) {
+        // ===================== memory waves =====================
+        // wave w owns value columns jl = 16 w + c16 of the tile; the state
+        // block Sacc[n] holds S[16 n + 4 g4 + r][j0 + jl]
+        const int w = wave;
+        f32x4 Sacc[DK / 16];
         if (a.S0) {
-            const float* S0 = a.S0 + (size_t)bh * DK * dv + j0 + jw + c16;
-#pragma unroll
-            for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-                for (int n = 0; n < DK / 16; ++n)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        Sacc[jt][n][r] = S0[(size_t)(16 * n + 4 * g4 + r) * dv + 16 * jt];
-        }
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-            for (int n = 0; n < DK / 16; ++n)
-                store4(&sm.ShT[(jw + 16 * jt + c16) * SM::LD_K + 16 * n + 4 * g4], Sacc[jt][n]);
-        lds_barrier();
-        auto& P = sm.mw[wave];
-        {
-            lds_barrier();
-            lds_barrier();
-        }
-        for (int c = 0; c < nchunks; ++c) {
-            {
-                const int nv = n_valid(c);
-                const size_t obase = base_v + (size_t)(c * C) * ts_v;  // uniform
-                const IO* Vb = sm.V[c & 1];
-                const IO* Ktpb = sm.Ktp[c & 1];
-                const IO* KtpTb = sm.KtpT[c & 1];
-                // Front contractions of the chunk, fused: every K-step loads the
-                // Kb / Qb row fragments once and uses them for
-                //   L'  = Kb Ktp^T (lower tiles),  Aqk = Qb Ktp^T (lower tiles),
-                //   KS  = Kb S,                    O   = Qb S   (this wave's columns)
-                using FR = Frag<IO>;
-                f32x4 accL[NB][NB], accA[NB][NB], accR[NJ][NB], accO[NJ][NB];
-#pragma unroll
-                for (int mt = 0; mt < NB; ++mt) {
-#pragma unroll
-                    for (int nt = 0; nt < NB; ++nt) {
-                        accL[mt][nt] = zero4();
-                        accA[mt][nt] = zero4();
-                    }
-#pragma unroll
-                    for (int jt = 0; jt < NJ; ++jt) {
-                        accR[jt][mt] = zero4();
-                        accO[jt][mt] = zero4();
-                    }
-                }
-#pragma unroll
-                for (int k0 = 0; k0 < DK; k0 += FR::KSTEP) {
-                    typename FR::type aK[NB], aQ[NB], bT[NB], bS[NJ];
-#pragma unroll
-                    for (int mt = 0; mt < NB; ++mt) {
-                        aK[mt] = FR::load(sm.Kb + 16 * mt * SM::LD_K, SM::LD_K, k0, lane);
-                        aQ[mt] = FR::load(sm.Qb + 16 * mt * SM::LD_K, SM::LD_K, k0, lane);
-                        bT[mt] = FR::load(Ktpb + 16 * mt * SM::LD_K, SM::LD_K, k0, lane);
-                    }
-#pragma unroll
-                    for (int jt = 0; jt < NJ; ++jt)
-                        bS[jt] = FR::load(sm.ShT + (jw + 16 * jt) * SM::LD_K, SM::LD_K, k0, lane);
-#pragma unroll
-                    for (int mt = 0; mt < NB; ++mt) {
-#pragma unroll
-                        for (int nt = 0; nt <= mt; ++nt) {
-                            FR::mma(accL[mt][nt], aK[mt], bT[nt]);
-                            FR::mma(accA[mt][nt], aQ[mt], bT[nt]);
-                        }
-#pragma unroll
-                        for (int jt = 0; jt < NJ; ++jt) {
-                            FR::mma(accR[jt][mt], aK[mt], bS[jt]);
-                            FR::mma(accO[jt][mt], aQ[mt], bS[jt]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int mt = 0; mt < NB; ++mt) {
-#pragma unroll
-                    for (int nt = 0; nt <= mt; ++nt) {
-                        const int s = 16 * nt + c16;
-                        if (nt == mt) {
-                            // diagonal block, kept in fp32 and transposed:
-                            // LdT[s][t] for the column-oriented substitution
-                            *reinterpret_cast<f32x4*>(
-                                &P.LdT[(16 * mt + c16) * SM::LD_D + 4 * g4]) = accL[mt][nt];
-                        }
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int t = 16 * mt + 4 * g4 + r;
-                            if (nt < mt)
-                                P.Loff[t * SM::LD_T + s] = from_f32<IO>(accL[mt][nt][r]);
-                            P.Aqk[t * SM::LD_T + s] =
-                                from_f32<IO>(s <= t ? accA[mt][nt][r] : 0.f);
-                        }
-                    }
-                }
-                // R = V - Kb S
-#pragma unroll
-                for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-                    for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int t = 16 * mt + 4 * g4 + r;
-                            accR[jt][mt][r] =
-                                to_f32(Vb[t * SM::LD_V + jw + 16 * jt + c16]) - accR[jt][mt][r];
-                        }
-                wave_lds_sync();
-                // inverses of the diagonal blocks of diag(r + z) + tril(L', -1)
-                if (g4 < NB) {
-                    // column cc of the inverse of the unit-free lower-triangular
-                    // block M = diag(r + z) + tril(L', -1): forward substitution
-                    // by columns of M (LdT rows), every update independent
-                    const int blk = g4, cc = c16;
-                    const float* Mt = P.LdT + 16 * blk * SM::LD_D;  // Mt[q][r] = M[r][q]
-                    const float* rrc = sm.rr[c & 3] + 16 * blk;
-                    float acc[16], x[16];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[r] = (r == cc) ? 1.f : 0.f;
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        float col[16];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const f32x4 v = *reinterpret_cast<const f32x4*>(Mt + q * SM::LD_D + 4 * e);
-                            col[4 * e] = v[0];
-                            col[4 * e + 1] = v[1];
-                            col[4 * e + 2] = v[2];
-                            col[4 * e + 3] = v[3];
-                        }
-                        x[q] = acc[q] * rcp(rrc[q] + col[q]);
-#pragma unroll
-                        for (int r = q + 1; r < 16; ++r)
-                            acc[r] -= col[r] * x[q];
-                    }
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        P.Tii[(blk * 16 + r) * SM::LD_B + cc] = from_f32<IO>(x[r]);
-                }
-                wave_lds_sync();
-#pragma unroll
-                for (int jt = 0; jt < NJ; ++jt) {
-                    // blocked forward substitution for Delta'
-                    IO* Dj = P.Delta + 16 * jt * SM::LD_T;
-                    IO* Rj = P.Rhs + 16 * jt * SM::LD_B;
-#pragma unroll
-                    for (int blk = 0; blk < NB; ++blk) {
-                        f32x4 acc = zero4();
-#pragma unroll
-                        for (int kb = 0; kb < blk; ++kb)
-                            mma_nt(acc, P.Loff + 16 * blk * SM::LD_T + 16 * kb, SM::LD_T,
-                                   Dj + 16 * kb, SM::LD_T, 16, lane);
-                        store4(Rj + c16 * SM::LD_B + 4 * g4, accR[jt][blk] - acc);
-                        wave_lds_sync();
-                        f32x4 d = zero4();
-                        mma_nt(d, P.Tii + 16 * blk * SM::LD_B, SM::LD_B, Rj, SM::LD_B, 16, lane);
-                        store4(Dj + c16 * SM::LD_T + 16 * blk + 4 * g4, d);
-                        wave_lds_sync();
-                    }
-                    // O += Aqk Delta'  and store
-#pragma unroll
-                    for (int mt = 0; mt < NB; ++mt) {
-                        mma_nt(accO[jt][mt], P.Aqk + 16 * mt * SM::LD_T, SM::LD_T, Dj, SM::LD_T,
-                               16 * (mt + 1), lane);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int t = 16 * mt + 4 * g4 + r;
-                            if (t < nv)
-                                (og + obase)[(uint32_t)(t * ts_v + j0 + jw + 16 * jt + c16)] =
-                                    from_f32<IO>(accO[jt][mt][r]);
-                        }
-                    }
-                    // S <- diag(G_C) (S + Ktp^T Delta'); the bf16 copy S^T feeds
-                    // the next chunk's R / O contractions
-#pragma unroll
-                    for (int n = 0; n < DK / 16; ++n) {
-                        mma_nt(Sacc[jt][n], KtpTb + 16 * n * SM::LD_T, SM::LD_T, Dj, SM::LD_T, C,
-                               lane);
-                        const f32x4 gc = *reinterpret_cast<const f32x4*>(&sm.gC[16 * n + 4 * g4]);
-                        Sacc[jt][n] *= gc;
-                        store4(&sm.ShT[(jw + 16 * jt + c16) * SM::LD_K + 16 * n + 4 * g4],
-                               Sacc[jt][n]);
-                    }
-                }
-            }
-            lds_barrier();
-            lds_barrier();
-        }
-        float* ST = a.S_T + (size_t)bh * DK * dv + j0 + jw + c16;
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
+            const float* S0 = a.S0 + (size_t)bh * DK * dv + j0 + 16 * w + c16;
 #pragma unroll
             for (int n = 0; n < DK / 16; ++n)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    ST[(size_t)(16 * n + 4 * g4 + r) * dv + 16 * jt] = Sacc[jt][n][r];
-    } else if (is_chain) {
-        // ====== Diagonal: per-channel recurrence from the LDS staging ======
-        // lane = key channel; writes G (in place of alpha), the write keys
-        // Ktp = p^ k / G in both layouts
-        float pvar = a.var0 ? a.var0[(size_t)bh * DK + ch_i] : 1.f;
-        lds_barrier();
-        for (int c = -1; c < nchunks; ++c) {
-            const int cn = c + 1;
-            if (cn < nchunks) {
-                const float* mr = sm.murt[cn & 3];
-                IO* Ktpb = sm.Ktp[cn & 1];
-                IO* KtpTb = sm.KtpT[cn & 1];
-                float g = 1.f;
+                    Sacc[n][r] = S0[(size_t)(16 * n + 4 * g4 + r) * dv];
+        } else {
 #pragma unroll
-                for (int t4 = 0; t4 < C; t4 += 4) {
-                    f32x4 kt4;
+            for (int n = 0; n < DK / 16; ++n)
+                Sacc[n] = zero4();
+        }
+        float* scratch = sm.scratch[sizeof(IO) == 4 ? w : 0];
+        IO* __restrict__ og = reinterpret_cast<IO*>(a.o);
+
+        for (int c = -LEAD; c < nchunks; ++c) {
+            // ---- elementwise build of chunk Y = c + 2
+            const int Y = c + 2;
+            if (Y >= 0 && Y < nchunks) {
+                const int nvY = n_valid(Y);
+                auto& st = sm.st[Y % NSTAGE];
+                auto& op = sm.op[Y % NOPS];
+                constexpr int UPR = DK / VE;
+                constexpr int NU = C * UPR;
+                for (int u = w * 64 + lane; u < NU; u += NMM * 64) {
+                    const int t = u / UPR, i0 = (u % UPR) * VE;
+                    const bool ok = t < nvY;
+                    float G[VE], P[VE], kf[VE], qf[VE];
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const int t = t4 + x;
-                        const int o = t * SM::LD_G + ch_i;
-                        const float al = sm.A[o];
-                        const float kv = to_f32(sm.Kst[t * SM::LD_K + ch_i]);
-                        const float ph = al * al * pvar + sm.W[o];
-                        const float u = mr[t] * kv * kv;
-                        pvar = ph * rcp(1.f + u * ph);
-                        g *= al;
-                        sm.A[o] = g;
-                        kt4[x] = ph * kv * rcp(g);
-                        Ktpb[t * SM::LD_K + ch_i] = from_f32<IO>(kt4[x]);
+                    for (int e = 0; e < VE; e += 4) {
+                        const f32x4 gv = *reinterpret_cast<const f32x4*>(&st.alpha[t * DK + i0 + e]);
+                        f32x4 pv;
+                        if constexpr (ISO) {
+                            const float bv = sm.bh[Y % NRING][t];
+                            pv = f32x4{bv, bv, bv, bv};
+                        } else {
+                            pv = *reinterpret_cast<const f32x4*>(&st.omega[t * DK + i0 + e]);
+                        }
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            G[e + x] = gv[x];
+                            P[e + x] = pv[x];
+                        }
                     }
-                    store4(&KtpTb[ch_i * SM::LD_T + t4], kt4);
+                    const VecIO kv = *reinterpret_cast<const VecIO*>(&st.k[t * DK + i0]);
+                    const VecIO qv = *reinterpret_cast<const VecIO*>(&st.q[t * DK + i0]);
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) {
+                        kf[e] = ok ? to_f32(kv[e]) : 0.f;
+                        qf[e] = ok ? to_f32(qv[e]) : 0.f;
+                    }
+                    VecIO kb, qb, kt;
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) {
+                        kb[e] = from_f32<IO>(kf[e] * G[e]);
+                        qb[e] = from_f32<IO>(qf[e] * G[e]);
+                        kt[e] = from_f32<IO>(P[e] * kf[e] * rcp(G[e]));
+                    }
+                    *reinterpret_cast<VecIO*>(&op.Kb[t * LD_K + i0]) = kb;
+                    *reinterpret_cast<VecIO*>(&op.Qb[t * LD_K + i0]) = qb;
+                    *reinterpret_cast<VecIO*>(&op.Ktp[t * LD_K + i0]) = kt;
+                    if (t == C - 1) {
+#pragma unroll
+                        for (int e = 0; e < VE; e += 4)
+                            *reinterpret_cast<f32x4*>(&op.gC[i0 + e]) =
+                                f32x4{G[e], G[e + 1], G[e + 2], G[e + 3]};
+                    }
+                }
+            }
+            // ---- chunk c on the matrix cores
+            if (c >= 0) {
+                const int nv = n_valid(c);
+                const auto& op = sm.op[c % NOPS];
+                const auto& fc = sm.fac[c & 1];
+                const IO* V = sm.v[c % 3];
+                // R = V - Kb S  ([t][j]),  O^T = S^T Qb^T  ([j][t])
+                f32x4 accR = zero4(), accO = zero4();
+#pragma unroll
+                for (int n = 0; n < DK / 16; ++n) {
+                    const typename F::type s = F::acc(Sacc[n], scratch, lane);
+                    const typename F::type kf = F::lds(op.Kb + 16 * n, LD_K, lane);
+                    const typename F::type qf = F::lds(op.Qb + 16 * n, LD_K, lane);
+                    F::mma(accR, kf, s);
+                    F::mma(accO, s, qf);
+                }
+                // v[t][jl]: 16-byte block jl / VE of row t sits at block
+                // (jl / VE) ^ ((t >> 2) & 7) of that row
+                {
+                    const int jl = 16 * w + c16;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 4 * g4 + r;
+                        const int blk = (jl / VE) ^ ((t >> 2) & 7);
+                        const float vv = to_f32(V[t * DVT + blk * VE + (jl % VE)]);
+                        accR[r] = (t < nv ? vv : 0.f) - accR[r];
+                    }
+                }
+                // Delta' = T R
+                f32x4 accD = zero4();
+                F::mma(accD, F::lds(fc.T, LD_S, lane), F::acc(accR, scratch, lane));
+                const typename F::type dfr = F::acc(accD, scratch, lane);
+                // O^T += Delta'^T Aqk^T
+                F::mma(accO, dfr, F::lds(fc.Aqk, LD_S, lane));
+                if (c16 < nv) {
+                    IO* dst = og + row_v(c * C + c16) + j0 + 16 * w + 4 * g4;
+                    if constexpr (sizeof(IO) == 2)
+                        *reinterpret_cast<bf16x4*>(dst) =
+                            bf16x4{static_cast<bf16>(accO[0]), static_cast<bf16>(accO[1]),
+                                   static_cast<bf16>(accO[2]), static_cast<bf16>(accO[3])};
+                    else
+                        *reinterpret_cast<f32x4*>(dst) = accO;
+                }
+                // S <- diag(G_C) (S + Ktp^T Delta')
+#pragma unroll
+                for (int n = 0; n < DK / 16; ++n) {
+                    F::mma(Sacc[n], F::lds_t(op.Ktp + 16 * n, LD_K, lane), dfr);
+                    const f32x4 gc = *reinterpret_cast<const f32x4*>(&op.gC[16 * n + 4 * g4]);
+                    Sacc[n] *= gc;
                 }
             }
             lds_barrier();
-            elementwise(cn);
-            issue_loads(c + 3, cn + 1);
-            lds_barrier();
         }
-        if (tile == 0)
-            a.var_T[(size_t)bh * DK + ch_i] = pvar;
-    } else if (is_scan) {
-        // ====== Isotropic: DPP Moebius scan, then the decay chain ======
-        float pvar = a.var0 ? a.var0[bh] : 1.f;
-        constexpr int SH = DK / 2;   // channels per lane in the reductions
-        constexpr int CPL = DK / 64; // channels per lane in the decay chain
-        lds_barrier();
-        for (int c = -1; c < nchunks; ++c) {
-            const int cn = c + 1;
-            if (cn < nchunks) {
-                {
-                    // per-token reductions, two lanes per token
-                    const int t = lane >> 1, half = lane & 1;
-                    float sa = 0.f, sn = 0.f;
-                    const float* Ar = sm.A + t * SM::LD_G + half * SH;
-                    const IO* Kr = sm.Kst + t * SM::LD_K + half * SH;
+        float* ST = a.S_T + (size_t)bh * DK * dv + j0 + 16 * w + c16;
 #pragma unroll
-                    for (int e = 0; e < SH; e += 4) {
-                        const f32x4 av = *reinterpret_cast<const f32x4*>(Ar + e);
-                        sa += av[0] * av[0] + av[1] * av[1] + av[2] * av[2] + av[3] * av[3];
+        for (int n = 0; n < DK / 16; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ST[(size_t)(16 * n + 4 * g4 + r) * dv] = Sacc[n][r];
+    } else if (wave < NMM + NCW) {
+        __builtin_amdgcn_s_setprio(2);  // the serial recurrence is the critical path
+        if constexpr (!ISO) {
+            // ================ Diagonal chain: lane = key channel ================
+            // writes G over alpha and p^ over omega
+            const int i = (wave - NMM) * 64 + lane;
+            float p = a.var0 ? a.var0[(size_t)bh * DK + i] : 1.f;
+            for (int c = -LEAD; c < nchunks; ++c) {
+                const int X = c + 3;
+                if (X >= 0 && X < nchunks) {
+                    const int nv = n_valid(X);
+                    auto& st = sm.st[X % NSTAGE];
+                    const float* rr = sm.rr[X % NRING];
+                    float al[C], om[C], mk2[C], rv[C];
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        const bool ok = t < nv;
+                        const float kv = to_f32(st.k[t * DK + i]);
+                        al[t] = ok ? st.alpha[t * DK + i] : 1.f;
+                        om[t] = ok ? st.omega[t * DK + i] : 0.f;
+                        mk2[t] = ok ? mu * kv * kv : 0.f;
+                        rv[t] = ok ? rr[t] : 1.f;
+                    }
+                    float g = 1.f;
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        // p = p^ / (1 + mu k^2 p^ / r) = p^ r / (r + mu k^2 p^)
+                        const float ph = al[t] * al[t] * p + om[t];
+                        const float den = mk2[t] * ph + rv[t];
+                        p = ph * rv[t] * rcp(den);
+                        g *= al[t];
+                        st.alpha[t * DK + i] = g;
+                        st.omega[t * DK + i] = ph;
+                    }
+                }
+                lds_barrier();
+            }
+            if (tile == 0)
+                a.var_T[(size_t)bh * DK + i] = p;
+        } else {
+            // ======== Isotropic chain: one wave, DK / 64 channels per lane ========
+            constexpr int CPL = DK / 64;
+            float bvar = a.var0 ? a.var0[bh] : 1.f;
+            for (int c = -LEAD; c < nchunks; ++c) {
+                const int X = c + 3;
+                if (X >= 0 && X < nchunks) {
+                    const int nv = n_valid(X);
+                    auto& st = sm.st[X % NSTAGE];
+                    // per-lane partial sums over its channels; G over alpha
+                    float sa[C], sk[C];
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        sa[t] = 0.f;
+                        sk[t] = 0.f;
                     }
 #pragma unroll
-                    for (int e = 0; e < SH; e += VE) {
-                        const VecIO kv = *reinterpret_cast<const VecIO*>(Kr + e);
+                    for (int cc = 0; cc < CPL; ++cc) {
+                        const int i = lane + 64 * cc;
+                        float g = 1.f;
 #pragma unroll
-                        for (int x = 0; x < VE; ++x) {
-                            const float f = to_f32(kv[x]);
-                            sn += f * f;
+                        for (int t = 0; t < C; ++t) {
+                            const bool ok = t < nv;
+                            const float al = ok ? st.alpha[t * DK + i] : 1.f;
+                            const float kv = ok ? to_f32(st.k[t * DK + i]) : 0.f;
+                            sa[t] += al * al;
+                            sk[t] += kv * kv;
+                            g *= al;
+                            st.alpha[t * DK + i] = g;
                         }
                     }
-                    sa += __shfl_xor(sa, 1);
-                    sn += __shfl_xor(sn, 1);
-                    // padded tokens were staged as alpha = 1, k = 0: a = 1, u = 0
-                    const float at = sa * (1.f / DK);
-                    const float wt = sm.wring[cn & 3][t];
-                    const float ut = sm.murt[cn & 3][t] * sn * (1.f / DK);
-                    const Mob m = (lane & 1) ? Mob{at, wt, ut * at, 1.f + ut * wt} : mob_identity();
-                    // odd lane 2t+1 carries token t; the even lane 2t ends with
-                    // the exclusive prefix (tokens < t)
-                    const Mob incl = mob_wave_scan_inclusive(m);
-                    if ((lane & 1) == 0)
-                        sm.bhat[t] = at * mob_apply(incl, pvar) + wt;
-                    const Mob last = Mob{__shfl(incl.m00, 63), __shfl(incl.m01, 63),
-                                         __shfl(incl.m10, 63), __shfl(incl.m11, 63)};
-                    pvar = mob_apply(last, pvar);
+                    // transpose-reduce over the 64 lanes: each halving step
+                    // keeps half the tokens and adds the partner lane's
+                    // partials of them; lane l ends with token l >> 2
+#pragma unroll
+                    for (int hs = C / 2, m = 32; hs >= 1; hs >>= 1, m >>= 1) {
+                        const bool up = (lane & m) != 0;
+#pragma unroll
+                        for (int j = 0; j < hs; ++j) {
+                            const float ra = __shfl_xor(up ? sa[j] : sa[j + hs], m);
+                            const float rk = __shfl_xor(up ? sk[j] : sk[j + hs], m);
+                            sa[j] = (up ? sa[j + hs] : sa[j]) + ra;
+                            sk[j] = (up ? sk[j + hs] : sk[j]) + rk;
+                        }
+                    }
+                    float ta = sa[0], tk = sk[0];
+                    ta += __shfl_xor(ta, 1);
+                    tk += __shfl_xor(tk, 1);
+                    ta += __shfl_xor(ta, 2);
+                    tk += __shfl_xor(tk, 2);
+                    // scalar recurrence over the chunk (uniform over the wave)
+                    const float* rr = sm.rr[X % NRING];
+                    const float* wr = sm.wr[X % NRING];
+                    float bhv[C];
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        const bool ok = t < nv;
+                        const float A2 = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ta), 4 * t));
+                        const float K2 = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tk), 4 * t));
+                        const float rt = ok ? rr[t] : 1.f;
+                        const float wt = ok ? wr[t] : 0.f;
+                        const float bhat = A2 * (1.f / DK) * bvar + wt;
+                        const float dr = (float)DK * rt;
+                        bvar = bhat * dr * rcp(dr + mu * K2 * bhat);
+                        bhv[t] = bhat;
+                    }
+                    if (lane == 0) {
+#pragma unroll
+                        for (int t = 0; t < C; t += 4)
+                            *reinterpret_cast<f32x4*>(&sm.bh[X % NRING][t]) =
+                                f32x4{bhv[t], bhv[t + 1], bhv[t + 2], bhv[t + 3]};
+                    }
+                }
+                lds_barrier();
+            }
+            if (tile == 0 && lane == 0)
+                a.var_T[bh] = bvar;
+        }
+    } else if (wave == NMM + NCW) {
+        // ===================== factor wave =====================
+        __builtin_amdgcn_s_setprio(2);
+        for (int c = -LEAD; c < nchunks; ++c) {
+            const int Fc = c + 1;
+            if (Fc >= 0 && Fc < nchunks) {
+                const int nv = n_valid(Fc);
+                const auto& op = sm.op[Fc % NOPS];
+                auto& fc = sm.fac[Fc & 1];
+                const float* rr = sm.rr[Fc % NRING];
+                // L'[t][s] = Kb_t . Ktp_s,   Aqk^T[u][t] = Ktp_u . Qb_t
+                f32x4 accL = zero4(), accQ = zero4();
+#pragma unroll
+                for (int k0 = 0; k0 < DK; k0 += FR::KSTEP) {
+                    const typename FR::type kb = FR::load(op.Kb, LD_K, k0, lane);
+                    const typename FR::type kt = FR::load(op.Ktp, LD_K, k0, lane);
+                    const typename FR::type qb = FR::load(op.Qb, LD_K, k0, lane);
+                    FR::mma(accL, kb, kt);
+                    FR::mma(accQ, kt, qb);
+                }
+                // M^T[s][t] = L'[t][s]   (lane holds L'[4 g4 + r][c16])
+                *reinterpret_cast<f32x4*>(&sm.Mt[c16 * 20 + 4 * g4]) = accL;
+                if ((c16 >> 2) == g4) {
+                    const int rs = c16 & 3;
+                    const float z = rs == 0 ? accL[0] : rs == 1 ? accL[1] : rs == 2 ? accL[2] : accL[3];
+                    const float rt = c16 < nv ? rr[c16] : 1.f;
+                    sm.dinv[c16] = rcp(rt + z);
+                }
+                // Aqk[t][u] = Aqk^T[u][t] for u <= t, else 0
+                {
+                    f32x4 aq;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        aq[r] = (4 * g4 + r <= c16) ? accQ[r] : 0.f;
+                    store4(&fc.Aqk[c16 * LD_S + 4 * g4], aq);
                 }
                 wave_lds_sync();
-                // decay chain and write keys Ktp = b^ k / G, CPL channels per lane
-                IO* Ktpb = sm.Ktp[cn & 1];
-                IO* KtpTb = sm.KtpT[cn & 1];
-                float g[CPL];
+                // T = M^-1, column c16 per lane: forward substitution over the
+                // columns of M (rows of M^T)
+                float x[C], acc[C], di[C];
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc)
-                    g[cc] = 1.f;
+                for (int t = 0; t < C; t += 4) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dinv[t]);
+                    di[t] = d4[0];
+                    di[t + 1] = d4[1];
+                    di[t + 2] = d4[2];
+                    di[t + 3] = d4[3];
+                }
 #pragma unroll
-                for (int t4 = 0; t4 < C; t4 += 4) {
-                    f32x4 kt4[CPL];
+                for (int r = 0; r < C; ++r)
+                    acc[r] = (r == c16) ? 1.f : 0.f;
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const int t = t4 + x;
-                        const float bht = sm.bhat[t];
+                for (int qq = 0; qq < C; ++qq) {
+                    x[qq] = acc[qq] * di[qq];
 #pragma unroll
-                        for (int cc = 0; cc < CPL; ++cc) {
-                            const int i = lane + 64 * cc;
-                            const int o = t * SM::LD_G + i;
-                            g[cc] *= sm.A[o];
-                            sm.A[o] = g[cc];
-                            const float kv = to_f32(sm.Kst[t * SM::LD_K + i]);
-                            kt4[cc][x] = bht * kv * rcp(g[cc]);
-                            Ktpb[t * SM::LD_K + i] = from_f32<IO>(kt4[cc][x]);
+                    for (int e = (qq + 1) >> 2; e < 4; ++e) {
+                        const f32x4 m = *reinterpret_cast<const f32x4*>(&sm.Mt[qq * 20 + 4 * e]);
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const int r = 4 * e + r4;
+                            if (r > qq)
+                                acc[r] -= m[r4] * x[qq];
                         }
                     }
+                }
+                if (g4 == 0) {
 #pragma unroll
-                    for (int cc = 0; cc < CPL; ++cc)
-                        store4(&KtpTb[(lane + 64 * cc) * SM::LD_T + t4], kt4[cc]);
+                    for (int r = 0; r < C; ++r)
+                        fc.T[r * LD_S + c16] = from_f32<IO>(x[r]);
                 }
             }
-            lds_barrier();
-            elementwise(cn);
-            issue_loads(c + 3, cn + 1);
             lds_barrier();
         }
-        if (tile == 0 && lane == 0)
-            a.var_T[bh] = pvar;
     } else {
-        // ====== loader (v tile, r, iso omega) and spare waves ======
-        lds_barrier();
-        for (int c = -1; c < nchunks; ++c) {
-            const int cn = c + 1;
-            if (is_loader) {
-                // v of chunk cn -> LDS; r / omega of chunk cn + 1 -> rings;
-                // then prefetch v of cn + 1 and r / omega of cn + 2
-                if (cn < nchunks) {
-                    IO* Vd = sm.V[cn & 1];
+        // ===================== loader wave =====================
+        // direct copies into LDS: raw inputs of chunk c + LEAD, v of chunk c + 2
+        constexpr int LPR_A = DK * 4 / 16;                  // lanes per alpha / omega row
+        constexpr int RPI_A = 64 / LPR_A, NI_A = C / RPI_A; // rows per copy, copies
+        constexpr int LPR_K = DK * (int)sizeof(IO) / 16;    // lanes per k / q row
+        constexpr int RPI_K = 64 / LPR_K, NI_K = C / RPI_K;
+        constexpr int LPR_V = DVT * (int)sizeof(IO) / 16;   // lanes per v tile row
+        constexpr int RPI_V = 64 / LPR_V, NI_V = C / RPI_V;
+        static_assert(LPR_A <= 64 && LPR_K <= 64 && LPR_V == 8 && NI_A >= 1 && NI_K >= 1,
+                      "row / lane split");
+        constexpr int NSTG = NI_A * (ISO ? 1 : 2) + 2 * NI_K + 1 + (ISO ? 1 : 0);
+        constexpr int NVI = NI_V;
+        static_assert(2 * (NSTG + NVI) <= 63, "outstanding copies within the vmcnt range");
+        const float* __restrict__ alg = a.alpha;
+        const float* __restrict__ omg = a.omega;
+        const IO* __restrict__ kg = reinterpret_cast<const IO*>(a.k);
+        const IO* __restrict__ qg = reinterpret_cast<const IO*>(a.q);
+        const IO* __restrict__ vg = reinterpret_cast<const IO*>(a.v);
+        for (int c = -LEAD; c < nchunks; ++c) {
+            const int X = c + LEAD;
+            const bool sv = X < nchunks;
+            const int XV = c + 2;
+            const bool vv = XV >= 0 && XV < nchunks;
+            if (sv) {
+                auto& st = sm.st[X % NSTAGE];
+                const int tb = X * C;
 #pragma unroll
-                    for (int m = 0; m < NPL; ++m) {
-                        const int p = lane + 64 * m;
-                        const int t = p / PIECES_ROW, sg = p % PIECES_ROW;
-                        *reinterpret_cast<f32x4*>(&Vd[t * SM::LD_V + sg * VE]) = vreg[m];
-                    }
+                for (int j = 0; j < NI_A; ++j) {
+                    const int t = min(tb + j * RPI_A + lane / LPR_A, T - 1);
+                    const size_t off = row_k(t) + (lane % LPR_A) * 4;
+                    dma16(alg + off, &st.alpha[j * RPI_A * DK]);
+                    if constexpr (!ISO)
+                        dma16(omg + off, &st.omega[j * RPI_A * DK]);
                 }
-                if (cn + 1 < nchunks && lane < C) {
-                    sm.rr[(cn + 1) & 3][lane] = rreg;
-                    sm.murt[(cn + 1) & 3][lane] = mu / rreg;
-                    if (ISO)
-                        sm.wring[(cn + 1) & 3][lane] = wreg;
+#pragma unroll
+                for (int j = 0; j < NI_K; ++j) {
+                    const int t = min(tb + j * RPI_K + lane / LPR_K, T - 1);
+                    const size_t off = row_k(t) + (lane % LPR_K) * VE;
+                    dma16(kg + off, &st.k[j * RPI_K * DK]);
+                    dma16(qg + off, &st.q[j * RPI_K * DK]);
                 }
-                asm volatile("" ::: "memory");
-                loader_load(cn + 1, cn + 2);
+                if (lane < C) {
+                    const int t = min(tb + lane, T - 1);
+                    dma4(a.r + row_s(t), sm.rr[X % NRING]);
+                    if constexpr (ISO)
+                        dma4(omg + row_s(t), sm.wr[X % NRING]);
+                }
             }
-            lds_barrier();
-            elementwise(cn);
-            issue_loads(c + 3, cn + 1);
+            if (vv) {
+                IO* vdst = sm.v[XV % 3];
+                const int tb = XV * C;
+#pragma unroll
+                for (int j = 0; j < NI_V; ++j) {
+                    // LDS block p = 64 j + lane holds row p / 8 and data
+                    // block (p % 8) ^ ((row >> 2) & 7) of that row
+                    const int p = 64 * j + lane;
+                    const int tl = p / LPR_V;
+                    const int blk = (p % LPR_V) ^ ((tl >> 2) & 7);
+                    const int t = min(tb + tl, T - 1);
+                    dma16(vg + row_v(t) + j0 + blk * VE, vdst + 64 * j * VE);
+                }
+            }
+            if (sv && vv)
+                vm_wait<NSTG + NVI>();
+            else if (sv)
+                vm_wait<NSTG>();
+            else if (vv)
+                vm_wait<NVI>();
+            else
+                vm_wait<0>();
             lds_barrier();
         }
     }
@@ -713,7 +650,7 @@ static hipError_t launch_one(const FwdArgs& a, hipStream_t stream)
     if (e != hipSuccess)
         return e;
     const int nblk = a.B * a.H * (a.dv / DVT);
-    hipLaunchKernelGGL(kern, dim3(nblk), dim3(KDN_CHUNK_THREADS(DVT)), smem, stream, a);
+    hipLaunchKernelGGL(kern, dim3(nblk), dim3(KDN_CHUNK_THREADS(DK, DVT, ISO)), smem, stream, a);
     return hipGetLastError();
 }
 
