@@ -38,6 +38,8 @@
 #include "kdn_common.h"
 #include "kdn_internal.h"
 
+#include <type_traits>
+
 namespace kdn {
 
 constexpr int CH = 16;      // tokens per chunk
@@ -101,10 +103,17 @@ struct F16<bf16> {
     {
         return *reinterpret_cast<const bf16x4*>(p + (lane & 15) * ld + 4 * (lane >> 4));
     }
+    // transpose read (ds_read_b64_tr_b16): inside each group of 16 lanes,
+    // lane j receives element j & 3 of the 8-byte row segments addressed by
+    // lanes 4 e + (j >> 2), e = 0..3; addressing row 4 g + ((l >> 2) & 3),
+    // columns 4 (l & 3) .. +3 therefore yields X[k = 4 g + e][c] in lane (g, c)
     static __device__ __forceinline__ type lds_t(const bf16* p, int ld, int lane)
     {
-        const bf16* q = p + 4 * (lane >> 4) * ld + (lane & 15);
-        return bf16x4{q[0], q[ld], q[2 * ld], q[3 * ld]};
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const bf16* q = p + (4 * (lane >> 4) + ((lane >> 2) & 3)) * ld + 4 * (lane & 3);
+        const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)q);
+        return __builtin_bit_cast(bf16x4, r);
     }
     static __device__ __forceinline__ type acc(const f32x4& x, float* scratch, int lane)
     {
@@ -164,7 +173,7 @@ struct ChunkSmem {
     static constexpr int LD_K = DK + PAD;  // Kb, Qb, Ktp rows (matrix-core operands)
     static constexpr int LD_S = C + PAD;   // T, Aqk rows
     // raw inputs of one chunk as rows of tokens, unpadded (filled by direct
-    // copies); the chain overwrites alpha with G and (Diagonal) omega with p^
+    // copies); the chain overwrites alpha with G and (Diagonal) omega with p^ / G
     struct Stage {
         alignas(16) float alpha[C * DK];
         alignas(16) float omega[ISO ? 4 : C * DK];
@@ -182,7 +191,7 @@ struct ChunkSmem {
         alignas(16) IO Aqk[C * LD_S];
     };
     Stage st[NSTAGE];
-    alignas(16) IO v[3][C * DVT];    // rows of DVT, 16-byte blocks xor-swizzled by row
+    alignas(16) IO v[3][C * DVT];    // rows of DVT, 16-byte block b of row t at b ^ (t & 7)
     Ops op[NOPS];
     Fac fac[2];
     alignas(16) float Mt[C * 20];    // factor: M^T (fp32), rows padded to 20
@@ -190,7 +199,9 @@ struct ChunkSmem {
     alignas(16) float rr[NRING][C];  // r_t
     alignas(16) float wr[NRING][C];  // isotropic omega_t
     alignas(16) float bh[NRING][C];  // isotropic b^_t
-    alignas(16) float scratch[sizeof(IO) == 4 ? NMM : 1][16 * 17];
+    alignas(16) float Tf[C * 20];    // factor: diagonal blocks of T (fp32)
+    // fp32 operand hops: one per memory wave (fp32 io only), then the factor's
+    alignas(16) float scratch[(sizeof(IO) == 4 ? NMM : 0) + 1][16 * 17];
 };
 
 #define KDN_CHUNK_THREADS(DK, DVT, ISO) (64 * ((DVT) / 16 + ((ISO) ? 1 : (DK) / 64) + 2))
@@ -258,109 +269,165 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
         float* scratch = sm.scratch[sizeof(IO) == 4 ? w : 0];
         IO* __restrict__ og = reinterpret_cast<IO*>(a.o);
 
-        for (int c = -LEAD; c < nchunks; ++c) {
-            // ---- elementwise build of chunk Y = c + 2
-            const int Y = c + 2;
-            if (Y >= 0 && Y < nchunks) {
-                const int nvY = n_valid(Y);
-                auto& st = sm.st[Y % NSTAGE];
-                auto& op = sm.op[Y % NOPS];
-                constexpr int UPR = DK / VE;
-                constexpr int NU = C * UPR;
-                for (int u = w * 64 + lane; u < NU; u += NMM * 64) {
-                    const int t = u / UPR, i0 = (u % UPR) * VE;
-                    const bool ok = t < nvY;
-                    float G[VE], P[VE], kf[VE], qf[VE];
+        // elementwise build of Kb, Qb, Ktp (and gC) of chunk Y
+        auto elementwise = [&](auto full_tag, int Y) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            const int nvY = FULL ? C : n_valid(Y);
+            auto& st = sm.st[Y % NSTAGE];
+            auto& op = sm.op[Y % NOPS];
+            constexpr int UPR = DK / VE;
+            constexpr int NU = C * UPR;
 #pragma unroll
-                    for (int e = 0; e < VE; e += 4) {
-                        const f32x4 gv = *reinterpret_cast<const f32x4*>(&st.alpha[t * DK + i0 + e]);
-                        f32x4 pv;
-                        if constexpr (ISO) {
-                            const float bv = sm.bh[Y % NRING][t];
-                            pv = f32x4{bv, bv, bv, bv};
-                        } else {
-                            pv = *reinterpret_cast<const f32x4*>(&st.omega[t * DK + i0 + e]);
-                        }
+            for (int u0 = 0; u0 < NU; u0 += NMM * 64) {
+                const int u = u0 + w * 64 + lane;
+                if (NU % (NMM * 64) != 0 && u >= NU)
+                    break;
+                const int t = u / UPR, i0 = (u % UPR) * VE;
+                const bool ok = FULL || t < nvY;
+                float G[VE], P[VE], kf[VE], qf[VE];
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            G[e + x] = gv[x];
-                            P[e + x] = pv[x];
-                        }
+                for (int e = 0; e < VE; e += 4) {
+                    const f32x4 gv = *reinterpret_cast<const f32x4*>(&st.alpha[t * DK + i0 + e]);
+                    f32x4 pv;
+                    if constexpr (ISO) {
+                        const float bv = sm.bh[Y % NRING][t];
+                        pv = f32x4{bv, bv, bv, bv};
+                    } else {
+                        pv = *reinterpret_cast<const f32x4*>(&st.omega[t * DK + i0 + e]);
                     }
-                    const VecIO kv = *reinterpret_cast<const VecIO*>(&st.k[t * DK + i0]);
-                    const VecIO qv = *reinterpret_cast<const VecIO*>(&st.q[t * DK + i0]);
 #pragma unroll
-                    for (int e = 0; e < VE; ++e) {
-                        kf[e] = ok ? to_f32(kv[e]) : 0.f;
-                        qf[e] = ok ? to_f32(qv[e]) : 0.f;
+                    for (int x = 0; x < 4; ++x) {
+                        G[e + x] = gv[x];
+                        P[e + x] = pv[x];
                     }
-                    VecIO kb, qb, kt;
+                }
+                const VecIO kv = *reinterpret_cast<const VecIO*>(&st.k[t * DK + i0]);
+                const VecIO qv = *reinterpret_cast<const VecIO*>(&st.q[t * DK + i0]);
 #pragma unroll
-                    for (int e = 0; e < VE; ++e) {
-                        kb[e] = from_f32<IO>(kf[e] * G[e]);
-                        qb[e] = from_f32<IO>(qf[e] * G[e]);
+                for (int e = 0; e < VE; ++e) {
+                    kf[e] = ok ? to_f32(kv[e]) : 0.f;
+                    qf[e] = ok ? to_f32(qv[e]) : 0.f;
+                }
+                VecIO kb, qb, kt;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    kb[e] = from_f32<IO>(kf[e] * G[e]);
+                    qb[e] = from_f32<IO>(qf[e] * G[e]);
+                    if constexpr (ISO)
                         kt[e] = from_f32<IO>(P[e] * kf[e] * rcp(G[e]));
-                    }
-                    *reinterpret_cast<VecIO*>(&op.Kb[t * LD_K + i0]) = kb;
-                    *reinterpret_cast<VecIO*>(&op.Qb[t * LD_K + i0]) = qb;
-                    *reinterpret_cast<VecIO*>(&op.Ktp[t * LD_K + i0]) = kt;
-                    if (t == C - 1) {
+                    else
+                        kt[e] = from_f32<IO>(P[e] * kf[e]);  // P = p^ / G
+                }
+                *reinterpret_cast<VecIO*>(&op.Kb[t * LD_K + i0]) = kb;
+                *reinterpret_cast<VecIO*>(&op.Qb[t * LD_K + i0]) = qb;
+                *reinterpret_cast<VecIO*>(&op.Ktp[t * LD_K + i0]) = kt;
+                if (t == C - 1) {
 #pragma unroll
-                        for (int e = 0; e < VE; e += 4)
-                            *reinterpret_cast<f32x4*>(&op.gC[i0 + e]) =
-                                f32x4{G[e], G[e + 1], G[e + 2], G[e + 3]};
-                    }
+                    for (int e = 0; e < VE; e += 4)
+                        *reinterpret_cast<f32x4*>(&op.gC[i0 + e]) =
+                            f32x4{G[e], G[e + 1], G[e + 2], G[e + 3]};
                 }
             }
-            // ---- chunk c on the matrix cores
-            if (c >= 0) {
-                const int nv = n_valid(c);
-                const auto& op = sm.op[c % NOPS];
-                const auto& fc = sm.fac[c & 1];
-                const IO* V = sm.v[c % 3];
-                // R = V - Kb S  ([t][j]),  O^T = S^T Qb^T  ([j][t])
-                f32x4 accR = zero4(), accO = zero4();
+        };
+        // chunk c on the matrix cores: front products, then the rest
+        f32x4 accR, accO;
+        auto mm_front = [&](int c) {
+            const auto& op = sm.op[c % NOPS];
+            // R = Kb S  ([t][j], negated later),  O^T = S^T Qb^T  ([j][t])
+            accR = zero4();
+            accO = zero4();
 #pragma unroll
-                for (int n = 0; n < DK / 16; ++n) {
-                    const typename F::type s = F::acc(Sacc[n], scratch, lane);
-                    const typename F::type kf = F::lds(op.Kb + 16 * n, LD_K, lane);
-                    const typename F::type qf = F::lds(op.Qb + 16 * n, LD_K, lane);
-                    F::mma(accR, kf, s);
-                    F::mma(accO, s, qf);
-                }
-                // v[t][jl]: 16-byte block jl / VE of row t sits at block
-                // (jl / VE) ^ ((t >> 2) & 7) of that row
-                {
+            for (int n = 0; n < DK / 16; ++n) {
+                const typename F::type s = F::acc(Sacc[n], scratch, lane);
+                const typename F::type kf = F::lds(op.Kb + 16 * n, LD_K, lane);
+                const typename F::type qf = F::lds(op.Qb + 16 * n, LD_K, lane);
+                F::mma(accR, kf, s);
+                F::mma(accO, s, qf);
+            }
+        };
+        auto mm_rest = [&](auto full_tag, int c) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            const int nv = FULL ? C : n_valid(c);
+            const auto& op = sm.op[c % NOPS];
+            const auto& fc = sm.fac[c & 1];
+            const IO* V = sm.v[c % 3];
+            // R = V - Kb S.  v[t][j]: 16-byte block j / VE of row t sits at
+            // block (j / VE) ^ (t & 7) of that row
+            {
+                float vv[4];
+                if constexpr (sizeof(IO) == 2) {
+                    // transpose read of the 16 x 16 block (rows t, columns 16 w ..)
+                    const int L = lane;
+                    const int t = 4 * (L >> 4) + ((L >> 2) & 3);
+                    const int col = 16 * w + 4 * (L & 3);
+                    const int pos = (col / VE) ^ (t & 7);
+                    typedef short s16x4 __attribute__((ext_vector_type(4)));
+                    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                    const s16x4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(V + t * DVT + pos * VE + (col % VE)));
+                    const bf16x4 b4 = __builtin_bit_cast(bf16x4, r4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        vv[r] = to_f32(b4[r]);
+                } else {
                     const int jl = 16 * w + c16;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int t = 4 * g4 + r;
-                        const int blk = (jl / VE) ^ ((t >> 2) & 7);
-                        const float vv = to_f32(V[t * DVT + blk * VE + (jl % VE)]);
-                        accR[r] = (t < nv ? vv : 0.f) - accR[r];
+                        vv[r] = to_f32(V[t * DVT + ((jl / VE) ^ (t & 7)) * VE + (jl % VE)]);
                     }
                 }
-                // Delta' = T R
-                f32x4 accD = zero4();
-                F::mma(accD, F::lds(fc.T, LD_S, lane), F::acc(accR, scratch, lane));
-                const typename F::type dfr = F::acc(accD, scratch, lane);
-                // O^T += Delta'^T Aqk^T
-                F::mma(accO, dfr, F::lds(fc.Aqk, LD_S, lane));
-                if (c16 < nv) {
-                    IO* dst = og + row_v(c * C + c16) + j0 + 16 * w + 4 * g4;
-                    if constexpr (sizeof(IO) == 2)
-                        *reinterpret_cast<bf16x4*>(dst) =
-                            bf16x4{static_cast<bf16>(accO[0]), static_cast<bf16>(accO[1]),
-                                   static_cast<bf16>(accO[2]), static_cast<bf16>(accO[3])};
-                    else
-                        *reinterpret_cast<f32x4*>(dst) = accO;
-                }
-                // S <- diag(G_C) (S + Ktp^T Delta')
 #pragma unroll
-                for (int n = 0; n < DK / 16; ++n) {
-                    F::mma(Sacc[n], F::lds_t(op.Ktp + 16 * n, LD_K, lane), dfr);
-                    const f32x4 gc = *reinterpret_cast<const f32x4*>(&op.gC[16 * n + 4 * g4]);
-                    Sacc[n] *= gc;
+                for (int r = 0; r < 4; ++r)
+                    accR[r] = ((FULL || 4 * g4 + r < nv) ? vv[r] : 0.f) - accR[r];
+            }
+            // Delta' = T R
+            f32x4 accD = zero4();
+            F::mma(accD, F::lds(fc.T, LD_S, lane), F::acc(accR, scratch, lane));
+            const typename F::type dfr = F::acc(accD, scratch, lane);
+            // O^T += Delta'^T Aqk^T
+            F::mma(accO, dfr, F::lds(fc.Aqk, LD_S, lane));
+            if (FULL || c16 < nv) {
+                IO* dst = og + row_v(c * C + c16) + j0 + 16 * w + 4 * g4;
+                if constexpr (sizeof(IO) == 2)
+                    *reinterpret_cast<bf16x4*>(dst) =
+                        bf16x4{static_cast<bf16>(accO[0]), static_cast<bf16>(accO[1]),
+                               static_cast<bf16>(accO[2]), static_cast<bf16>(accO[3])};
+                else
+                    *reinterpret_cast<f32x4*>(dst) = accO;
+            }
+            // S <- diag(G_C) (S + Ktp^T Delta')
+#pragma unroll
+            for (int n = 0; n < DK / 16; ++n) {
+                F::mma(Sacc[n], F::lds_t(op.Ktp + 16 * n, LD_K, lane), dfr);
+                const f32x4 gc = *reinterpret_cast<const f32x4*>(&op.gC[16 * n + 4 * g4]);
+                Sacc[n] *= gc;
+            }
+        };
+        const std::integral_constant<bool, true> full{};
+        const std::integral_constant<bool, false> ragged{};
+
+        for (int c = -LEAD; c < nchunks; ++c) {
+            const int Y = c + 2;
+            if (c >= 0 && Y < nchunks && n_valid(Y) == C) {
+                // steady state: both pieces in one block so that the
+                // elementwise work overlaps the matrix-core latency
+                mm_front(c);
+                elementwise(full, Y);
+                mm_rest(full, c);
+            } else {
+                if (Y >= 0 && Y < nchunks) {
+                    if (n_valid(Y) == C)
+                        elementwise(full, Y);
+                    else
+                        elementwise(ragged, Y);
+                }
+                if (c >= 0) {
+                    mm_front(c);
+                    if (n_valid(c) == C)
+                        mm_rest(full, c);
+                    else
+                        mm_rest(ragged, c);
                 }
             }
             lds_barrier();
@@ -375,36 +442,53 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
         __builtin_amdgcn_s_setprio(2);  // the serial recurrence is the critical path
         if constexpr (!ISO) {
             // ================ Diagonal chain: lane = key channel ================
-            // writes G over alpha and p^ over omega
+            // writes G over alpha and p^ / G over omega
             const int i = (wave - NMM) * 64 + lane;
             float p = a.var0 ? a.var0[(size_t)bh * DK + i] : 1.f;
-            for (int c = -LEAD; c < nchunks; ++c) {
-                const int X = c + 3;
-                if (X >= 0 && X < nchunks) {
-                    const int nv = n_valid(X);
-                    auto& st = sm.st[X % NSTAGE];
-                    const float* rr = sm.rr[X % NRING];
-                    float al[C], om[C], mk2[C], rv[C];
+            auto chain = [&](auto full_tag, int X) {
+                constexpr bool FULL = decltype(full_tag)::value;
+                const int nv = FULL ? C : n_valid(X);
+                auto& st = sm.st[X % NSTAGE];
+                const float* rr = sm.rr[X % NRING];
+                // every read is issued before the first use
+                float al[C], om[C], mk2[C], rv[C];
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    const float kv = to_f32(st.k[t * DK + i]);
+                    al[t] = st.alpha[t * DK + i];
+                    om[t] = st.omega[t * DK + i];
+                    mk2[t] = mu * kv * kv;
+                    rv[t] = rr[t];
+                }
+                if constexpr (!FULL) {
 #pragma unroll
                     for (int t = 0; t < C; ++t) {
                         const bool ok = t < nv;
-                        const float kv = to_f32(st.k[t * DK + i]);
-                        al[t] = ok ? st.alpha[t * DK + i] : 1.f;
-                        om[t] = ok ? st.omega[t * DK + i] : 0.f;
-                        mk2[t] = ok ? mu * kv * kv : 0.f;
-                        rv[t] = ok ? rr[t] : 1.f;
+                        al[t] = ok ? al[t] : 1.f;
+                        om[t] = ok ? om[t] : 0.f;
+                        mk2[t] = ok ? mk2[t] : 0.f;
+                        rv[t] = ok ? rv[t] : 1.f;
                     }
-                    float g = 1.f;
+                }
+                float g = 1.f;
 #pragma unroll
-                    for (int t = 0; t < C; ++t) {
-                        // p = p^ / (1 + mu k^2 p^ / r) = p^ r / (r + mu k^2 p^)
-                        const float ph = al[t] * al[t] * p + om[t];
-                        const float den = mk2[t] * ph + rv[t];
-                        p = ph * rv[t] * rcp(den);
-                        g *= al[t];
-                        st.alpha[t * DK + i] = g;
-                        st.omega[t * DK + i] = ph;
-                    }
+                for (int t = 0; t < C; ++t) {
+                    // p = p^ / (1 + mu k^2 p^ / r) = p^ r / (r + mu k^2 p^)
+                    const float ph = al[t] * al[t] * p + om[t];
+                    const float den = mk2[t] * ph + rv[t];
+                    p = ph * rv[t] * rcp(den);
+                    g *= al[t];
+                    st.alpha[t * DK + i] = g;
+                    st.omega[t * DK + i] = ph * rcp(g);  // p^ / G
+                }
+            };
+            for (int c = -LEAD; c < nchunks; ++c) {
+                const int X = c + 3;
+                if (X >= 0 && X < nchunks) {
+                    if (n_valid(X) == C)
+                        chain(std::integral_constant<bool, true>{}, X);
+                    else
+                        chain(std::integral_constant<bool, false>{}, X);
                 }
                 lds_barrier();
             }
@@ -429,23 +513,35 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
 #pragma unroll
                     for (int cc = 0; cc < CPL; ++cc) {
                         const int i = lane + 64 * cc;
+                        float alv[C], kvv[C];
+#pragma unroll
+                        for (int t = 0; t < C; ++t) {
+                            alv[t] = st.alpha[t * DK + i];
+                            kvv[t] = to_f32(st.k[t * DK + i]);
+                        }
+                        if (nv < C) {
+#pragma unroll
+                            for (int t = 0; t < C; ++t) {
+                                alv[t] = t < nv ? alv[t] : 1.f;
+                                kvv[t] = t < nv ? kvv[t] : 0.f;
+                            }
+                        }
                         float g = 1.f;
 #pragma unroll
                         for (int t = 0; t < C; ++t) {
-                            const bool ok = t < nv;
-                            const float al = ok ? st.alpha[t * DK + i] : 1.f;
-                            const float kv = ok ? to_f32(st.k[t * DK + i]) : 0.f;
-                            sa[t] += al * al;
-                            sk[t] += kv * kv;
-                            g *= al;
+                            sa[t] += alv[t] * alv[t];
+                            sk[t] += kvv[t] * kvv[t];
+                            g *= alv[t];
                             st.alpha[t * DK + i] = g;
                         }
                     }
                     // transpose-reduce over the 64 lanes: each halving step
                     // keeps half the tokens and adds the partner lane's
                     // partials of them; lane l ends with token l >> 2
-#pragma unroll
-                    for (int hs = C / 2, m = 32; hs >= 1; hs >>= 1, m >>= 1) {
+                    static_assert(C == 16, "reduction tree shape");
+                    auto halve = [&](auto hs_tag) {
+                        constexpr int hs = decltype(hs_tag)::value;
+                        constexpr int m = 4 * hs;  // partner lane distance
                         const bool up = (lane & m) != 0;
 #pragma unroll
                         for (int j = 0; j < hs; ++j) {
@@ -454,7 +550,11 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
                             sa[j] = (up ? sa[j + hs] : sa[j]) + ra;
                             sk[j] = (up ? sk[j + hs] : sk[j]) + rk;
                         }
-                    }
+                    };
+                    halve(std::integral_constant<int, 8>{});
+                    halve(std::integral_constant<int, 4>{});
+                    halve(std::integral_constant<int, 2>{});
+                    halve(std::integral_constant<int, 1>{});
                     float ta = sa[0], tk = sk[0];
                     ta += __shfl_xor(ta, 1);
                     tk += __shfl_xor(tk, 1);
@@ -463,7 +563,12 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
                     // scalar recurrence over the chunk (uniform over the wave)
                     const float* rr = sm.rr[X % NRING];
                     const float* wr = sm.wr[X % NRING];
-                    float bhv[C];
+                    float bhv[C], rv[C], wv[C];
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        rv[t] = rr[t];
+                        wv[t] = wr[t];
+                    }
 #pragma unroll
                     for (int t = 0; t < C; ++t) {
                         const bool ok = t < nv;
@@ -471,8 +576,8 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
                             float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ta), 4 * t));
                         const float K2 = __builtin_bit_cast(
                             float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tk), 4 * t));
-                        const float rt = ok ? rr[t] : 1.f;
-                        const float wt = ok ? wr[t] : 0.f;
+                        const float rt = ok ? rv[t] : 1.f;
+                        const float wt = ok ? wv[t] : 0.f;
                         const float bhat = A2 * (1.f / DK) * bvar + wt;
                         const float dr = (float)DK * rt;
                         bvar = bhat * dr * rcp(dr + mu * K2 * bhat);
@@ -493,6 +598,7 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
     } else if (wave == NMM + NCW) {
         // ===================== factor wave =====================
         __builtin_amdgcn_s_setprio(2);
+        float* fscratch = sm.scratch[sizeof(IO) == 4 ? NMM : 0];
         for (int c = -LEAD; c < nchunks; ++c) {
             const int Fc = c + 1;
             if (Fc >= 0 && Fc < nchunks) {
@@ -515,7 +621,8 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
                 if ((c16 >> 2) == g4) {
                     const int rs = c16 & 3;
                     const float z = rs == 0 ? accL[0] : rs == 1 ? accL[1] : rs == 2 ? accL[2] : accL[3];
-                    const float rt = c16 < nv ? rr[c16] : 1.f;
+                    const float rraw = rr[c16];
+                    const float rt = c16 < nv ? rraw : 1.f;
                     sm.dinv[c16] = rcp(rt + z);
                 }
                 // Aqk[t][u] = Aqk^T[u][t] for u <= t, else 0
@@ -529,36 +636,86 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
                 wave_lds_sync();
                 // T = M^-1, column c16 per lane: forward substitution over the
                 // columns of M (rows of M^T)
-                float x[C], acc[C], di[C];
+                // T = M^-1 in two levels: the 8 x 8 diagonal blocks by forward
+                // substitution (lane c16: block c16 >> 3, column c16 & 7, over
+                // the columns of M = rows of M^T), then the off-diagonal block
+                // T21 = -T22 M21 T11 on the matrix cores (fp32)
+                {
+                    const int bb = (c16 >> 3) * 8, cc = c16 & 7;
+                    float di[8], Mc[8][8], acc[8], x[8];
+                    {
+                        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dinv[bb]);
+                        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dinv[bb + 4]);
 #pragma unroll
-                for (int t = 0; t < C; t += 4) {
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dinv[t]);
-                    di[t] = d4[0];
-                    di[t + 1] = d4[1];
-                    di[t + 2] = d4[2];
-                    di[t + 3] = d4[3];
-                }
-#pragma unroll
-                for (int r = 0; r < C; ++r)
-                    acc[r] = (r == c16) ? 1.f : 0.f;
-#pragma unroll
-                for (int qq = 0; qq < C; ++qq) {
-                    x[qq] = acc[qq] * di[qq];
-#pragma unroll
-                    for (int e = (qq + 1) >> 2; e < 4; ++e) {
-                        const f32x4 m = *reinterpret_cast<const f32x4*>(&sm.Mt[qq * 20 + 4 * e]);
-#pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) {
-                            const int r = 4 * e + r4;
-                            if (r > qq)
-                                acc[r] -= m[r4] * x[qq];
+                        for (int e = 0; e < 4; ++e) {
+                            di[e] = d0[e];
+                            di[4 + e] = d1[e];
                         }
                     }
-                }
-                if (g4 == 0) {
 #pragma unroll
-                    for (int r = 0; r < C; ++r)
-                        fc.T[r * LD_S + c16] = from_f32<IO>(x[r]);
+                    for (int qq = 0; qq < 7; ++qq)
+#pragma unroll
+                        for (int e = (qq + 1) >> 2; e < 2; ++e) {
+                            const f32x4 m = *reinterpret_cast<const f32x4*>(
+                                &sm.Mt[(bb + qq) * 20 + bb + 4 * e]);
+#pragma unroll
+                            for (int r4 = 0; r4 < 4; ++r4)
+                                Mc[qq][4 * e + r4] = m[r4];
+                        }
+#pragma unroll
+                    for (int r = 0; r < 8; ++r)
+                        acc[r] = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+                    for (int qq = 0; qq < 8; ++qq) {
+                        x[qq] = acc[qq] * di[qq];
+#pragma unroll
+                        for (int r = qq + 1; r < 8; ++r)
+                            acc[r] -= Mc[qq][r] * x[qq];
+                    }
+                    if (g4 == 0) {
+#pragma unroll
+                        for (int r = 0; r < 8; ++r)
+                            sm.Tf[(bb + r) * 20 + bb + cc] = x[r];
+                    }
+                }
+                wave_lds_sync();
+                {
+                    using FF = F16<float>;
+                    // P = M21 T11 :  A[m][k] = M[m][k] = M^T[k][m]  (m >= 8, k < 8)
+                    //                B[k][n] = T11[k][n]            (k, n < 8)
+                    FF::type am = FF::lds_t(sm.Mt, 20, lane);
+                    FF::type bt = FF::lds_t(sm.Tf, 20, lane);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int k = 4 * e + g4;
+                        am.v[e] = (c16 >= 8 && k < 8) ? am.v[e] : 0.f;
+                        bt.v[e] = (k < 8 && c16 < 8) ? bt.v[e] : 0.f;
+                    }
+                    f32x4 accP = zero4();
+                    FF::mma(accP, am, bt);
+                    // T21 = -T22 P :  A[m][k] = T22[m][k] (m, k >= 8), B = P
+                    FF::type a2 = FF::lds(sm.Tf, 20, lane);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int k = 4 * e + g4;
+                        a2.v[e] = (c16 >= 8 && k >= 8) ? a2.v[e] : 0.f;
+                    }
+                    const FF::type bp = FF::acc(accP, fscratch, lane);
+                    f32x4 accT = zero4();
+                    FF::mma(accT, a2, bp);
+                    // T in D layout: lane holds rows 4 g4 + r of column c16
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = 4 * g4 + r, n = c16;
+                        float tv;
+                        if (m >= 8 && n < 8)
+                            tv = -accT[r];
+                        else if ((m >> 3) == (n >> 3) && n <= m)
+                            tv = sm.Tf[m * 20 + n];
+                        else
+                            tv = 0.f;
+                        fc.T[m * LD_S + n] = from_f32<IO>(tv);
+                    }
                 }
             }
             lds_barrier();
@@ -582,6 +739,31 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
         const IO* __restrict__ kg = reinterpret_cast<const IO*>(a.k);
         const IO* __restrict__ qg = reinterpret_cast<const IO*>(a.q);
         const IO* __restrict__ vg = reinterpret_cast<const IO*>(a.v);
+        // per-lane element offsets inside a chunk (32-bit; the chunk base is
+        // uniform); rows past the end of a ragged chunk repeat its last row
+        const uint32_t tsk = (uint32_t)(H * DK), tsv = (uint32_t)(H * dv), tss = (uint32_t)H;
+        auto off_a = [&](int j, int lim) {
+            return (uint32_t)min(j * RPI_A + lane / LPR_A, lim) * tsk + (lane % LPR_A) * 4;
+        };
+        auto off_k = [&](int j, int lim) {
+            return (uint32_t)min(j * RPI_K + lane / LPR_K, lim) * tsk + (lane % LPR_K) * VE;
+        };
+        auto off_v = [&](int j, int lim) {
+            const int p = 64 * j + lane;
+            const int tl = p / LPR_V;
+            const int blk = (p % LPR_V) ^ (tl & 7);
+            return (uint32_t)min(tl, lim) * tsv + blk * VE;
+        };
+        uint32_t oa[NI_A], ok_[NI_K], ov[NI_V];
+#pragma unroll
+        for (int j = 0; j < NI_A; ++j)
+            oa[j] = off_a(j, C - 1);
+#pragma unroll
+        for (int j = 0; j < NI_K; ++j)
+            ok_[j] = off_k(j, C - 1);
+#pragma unroll
+        for (int j = 0; j < NI_V; ++j)
+            ov[j] = off_v(j, C - 1);
         for (int c = -LEAD; c < nchunks; ++c) {
             const int X = c + LEAD;
             const bool sv = X < nchunks;
@@ -590,40 +772,54 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
             if (sv) {
                 auto& st = sm.st[X % NSTAGE];
                 const int tb = X * C;
+                const int lim = n_valid(X) - 1;
+                const size_t cb = row_k(tb);  // uniform
+                const float* ab = alg + cb;
+                const float* wb = omg + cb;
+                const IO* kb = kg + cb;
+                const IO* qb = qg + cb;
+                auto copy_stage = [&](auto full_tag) {
+                    constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-                for (int j = 0; j < NI_A; ++j) {
-                    const int t = min(tb + j * RPI_A + lane / LPR_A, T - 1);
-                    const size_t off = row_k(t) + (lane % LPR_A) * 4;
-                    dma16(alg + off, &st.alpha[j * RPI_A * DK]);
-                    if constexpr (!ISO)
-                        dma16(omg + off, &st.omega[j * RPI_A * DK]);
-                }
+                    for (int j = 0; j < NI_A; ++j) {
+                        const uint32_t o = FULL ? oa[j] : off_a(j, lim);
+                        dma16(ab + o, &st.alpha[j * RPI_A * DK]);
+                        if constexpr (!ISO)
+                            dma16(wb + o, &st.omega[j * RPI_A * DK]);
+                    }
 #pragma unroll
-                for (int j = 0; j < NI_K; ++j) {
-                    const int t = min(tb + j * RPI_K + lane / LPR_K, T - 1);
-                    const size_t off = row_k(t) + (lane % LPR_K) * VE;
-                    dma16(kg + off, &st.k[j * RPI_K * DK]);
-                    dma16(qg + off, &st.q[j * RPI_K * DK]);
-                }
+                    for (int j = 0; j < NI_K; ++j) {
+                        const uint32_t o = FULL ? ok_[j] : off_k(j, lim);
+                        dma16(kb + o, &st.k[j * RPI_K * DK]);
+                        dma16(qb + o, &st.q[j * RPI_K * DK]);
+                    }
+                };
+                if (lim == C - 1)
+                    copy_stage(std::integral_constant<bool, true>{});
+                else
+                    copy_stage(std::integral_constant<bool, false>{});
                 if (lane < C) {
-                    const int t = min(tb + lane, T - 1);
-                    dma4(a.r + row_s(t), sm.rr[X % NRING]);
+                    const uint32_t o = (uint32_t)min(lane, lim) * tss;
+                    const size_t sb = row_s(tb);
+                    dma4(a.r + sb + o, sm.rr[X % NRING]);
                     if constexpr (ISO)
-                        dma4(omg + row_s(t), sm.wr[X % NRING]);
+                        dma4(omg + sb + o, sm.wr[X % NRING]);
                 }
             }
             if (vv) {
                 IO* vdst = sm.v[XV % 3];
-                const int tb = XV * C;
+                const int lim = n_valid(XV) - 1;
+                const IO* vb = vg + row_v(XV * C) + j0;  // uniform
+                // LDS block p = 64 j + lane holds row p / 8 and data block
+                // (p % 8) ^ (row & 7) of that row
+                if (lim == C - 1) {
 #pragma unroll
-                for (int j = 0; j < NI_V; ++j) {
-                    // LDS block p = 64 j + lane holds row p / 8 and data
-                    // block (p % 8) ^ ((row >> 2) & 7) of that row
-                    const int p = 64 * j + lane;
-                    const int tl = p / LPR_V;
-                    const int blk = (p % LPR_V) ^ ((tl >> 2) & 7);
-                    const int t = min(tb + tl, T - 1);
-                    dma16(vg + row_v(t) + j0 + blk * VE, vdst + 64 * j * VE);
+                    for (int j = 0; j < NI_V; ++j)
+                        dma16(vb + ov[j], vdst + 64 * j * VE);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < NI_V; ++j)
+                        dma16(vb + off_v(j, lim), vdst + 64 * j * VE);
                 }
             }
             if (sv && vv)
