@@ -209,7 +209,7 @@ def main():
         "dtype": "bf16" if w.io == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "variant": variant, "B": B, "T": T, "H": H, "dk": dk,
-                   "dv": dv, "chunk": 32, "io": w.io, "gates": "f32", "state": "f32",
+                   "dv": dv, "chunk": 16, "io": w.io, "gates": "f32", "state": "f32",
                    "global_batch": B, "seq_len": T, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

@@ -46,7 +46,7 @@
  *     16-byte aligned.
  *   - Preconditions (documented, not checked per element): r > 0,
  *     0 < alpha <= 1, omega >= 0, p0/b0 > 0, mu >= 0, all finite, and within
- *     every 32-token chunk the product of alpha over the chunk stays above
+ *     every 16-token chunk the product of alpha over the chunk stays above
  *     1e-30 in every channel (the chunked memory rescales keys by the
  *     cumulative decay from the chunk start).  Outside them results are
  *     unspecified (NaN propagates; nothing faults).
