@@ -138,7 +138,9 @@ kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float
     (void)workspace;
 
     kdn::FwdArgs a{q, k, v, alpha, omega, r, S0, var0, o, S_T, var_T, B, T, H, dk, dv, mu};
-    hipError_t e = kdn::launch_chunk_fwd(a, iso, io, reinterpret_cast<hipStream_t>(stream));
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = io == KDN_BF16 ? kdn::launch_walk_fwd(a, iso, hs)
+                                  : kdn::launch_chunk_fwd_f32(a, iso, hs);
     if (e != hipSuccess)
         return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

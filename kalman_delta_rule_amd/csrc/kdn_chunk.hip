@@ -850,21 +850,8 @@ static hipError_t launch_one(const FwdArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-int chunk_fwd_value_tile(int io_dtype, int dk)
+hipError_t launch_chunk_fwd_f32(const FwdArgs& a, bool iso, hipStream_t stream)
 {
-    (void)dk;
-    return io_dtype == 1 ? 64 : 32;
-}
-
-hipError_t launch_chunk_fwd(const FwdArgs& a, bool iso, int io_dtype, hipStream_t stream)
-{
-    if (io_dtype == 1) {
-        if (a.dk == 128)
-            return iso ? launch_one<bf16, 128, 64, true>(a, stream)
-                       : launch_one<bf16, 128, 64, false>(a, stream);
-        return iso ? launch_one<bf16, 64, 64, true>(a, stream)
-                   : launch_one<bf16, 64, 64, false>(a, stream);
-    }
     return iso ? launch_one<float, 64, 32, true>(a, stream)
                : launch_one<float, 64, 32, false>(a, stream);
 }

@@ -51,9 +51,10 @@ struct GainArgs {
     float mu;
 };
 
-// value-tile width used by the chunked forward for this io dtype
-int chunk_fwd_value_tile(int io_dtype, int dk);
-hipError_t launch_chunk_fwd(const FwdArgs& a, bool iso, int io_dtype, hipStream_t stream);
+// chunked forward: bf16 io runs the walk kernel (kdn_walk.hip), fp32 io the
+// fp32 chunk kernel (kdn_chunk.hip)
+hipError_t launch_walk_fwd(const FwdArgs& a, bool iso, hipStream_t stream);
+hipError_t launch_chunk_fwd_f32(const FwdArgs& a, bool iso, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, bool iso, int io_dtype, hipStream_t stream);
 size_t gain_workspace_floats(bool iso, int B, int T, int H, int dk);
 hipError_t launch_gain_scan(const GainArgs& a, bool iso, int io_dtype, hipStream_t stream);

@@ -1,0 +1,835 @@
+// kdn_walk.hip -- chunkwise KDN forward for bf16 q/k/v, gfx950.
+//
+// One workgroup owns one (batch, head, tile of DVT value columns) and walks
+// the sequence in chunks of C = 16 tokens.  The memory state S (dk x DVT,
+// fp32) stays in matrix-core accumulators for the whole sequence; the
+// variance state stays in registers of the builder lanes.
+//
+// Method (KDN reading notes, method part):
+//   gain   §4-§5 (Diagonal):  p^_t = alpha_t^2 p_{t-1} + omega_t,
+//            p_t = p^_t / (1 + (mu / r_t) k_t^2 p^_t)
+//          §7 (Isotropic): a_t = mean alpha^2, b^_t = a_t b_{t-1} + omega_t,
+//            b_t = b^_t / (1 + mu |k_t|^2 b^_t / (d_k r_t))
+//   memory §6: S_t = (I - kappa_t k_t^T) D_t S_{t-1} + kappa_t v_t^T,
+//          kappa_t = p^_t (.) k_t / (r_t + z_t),  z_t = sum_i p^_t,i k_t,i^2,
+//          o_t = S_t^T q_t (read after the write).
+// Chunk form (compact WY, Appendix D as summarised in the notes), with
+// G_t = prod_{s<=t} alpha_s the cumulative decay from the chunk start:
+//   Kb = k (.) G,  Ktp = p^ (.) k / G,  Qb = q (.) G
+//   L' = Kb Ktp^T  (diagonal = z_t),  Aqk = tril(Qb Ktp^T) (inclusive)
+//   M  = diag(r + z) + tril(L', -1),   T = M^-1
+//   Delta' = T (V - Kb S),   O = Qb S + Aqk Delta',
+//   S <- diag(G_C) (S + Ktp^T Delta')
+// which equals the token recurrence in exact arithmetic.  Ragged tails are
+// padded with identity tokens (k = q = v = 0, alpha = 1, omega = 0, r = 1).
+//
+// Diagonal variance in homogeneous form (§6): p = n / d with
+//   n_t = alpha^2 n_{t-1} + omega d_{t-1}       (so p^_t = n_t / d_{t-1})
+//   d_t = d_{t-1} + u_t n_t,  u_t = mu k_t^2 / r_t
+// i.e. the 2x2 Moebius factor [[alpha^2, omega], [u alpha^2, 1 + u omega]]
+// applied to [n; d].  The recurrence needs no division; both coordinates are
+// rescaled by the same power of two every four tokens, which leaves every
+// ratio n / d bit-identical.  Ktp = k n_t / (d_{t-1} G_t) takes the one
+// reciprocal per token and channel, off the recurrence's dependency chain.
+//
+// The memory update uses the compact-WY pair of the notes' Appendix D
+// summary, W = T Kb and U = T V:  Delta' = U - W S.  U does not depend on S,
+// so only W S sits on the chunk-to-chunk dependency chain of S.
+//
+// Workgroup roles, one LDS barrier per step.  In step c:
+//   loader wave    copies the raw inputs (alpha, omega, k, q, r) of chunk
+//                  c + LR straight from global memory into LDS, and v of
+//                  chunk c + 2;
+//   isotropic wave (Isotropic only) reduces alpha^2 and k^2 over channels per
+//                  token of chunk c + 4 and runs the scalar variance
+//                  recurrence;
+//   builder waves  (lane = key channel) run the per-channel recurrence of
+//                  chunk c + 3 and write its bf16 operands Kb, Qb, Ktp and
+//                  G_C to LDS;
+//   factor waves   the first forms L', Aqk and T = M^-1 of chunk c + 2 (one
+//                  lane per column of T, forward substitution); the second
+//                  forms W = T Kb of chunk c + 1 on the matrix cores;
+//   memory waves   apply chunk c to their value columns (2 x 16 each).
+// Every buffer is indexed by chunk number modulo its lifetime, so no role
+// waits for another inside a step.
+#include "kdn_common.h"
+#include "kdn_internal.h"
+
+#include <type_traits>
+
+namespace kdn {
+namespace walk {
+
+constexpr int C = 16;     // tokens per chunk
+constexpr int NRING = 8;  // per-token scalar rings (r, isotropic omega and b^)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Direct global -> LDS copy: lane l's 16 (or 4) bytes land at dst + 16 l
+// (4 l).  dst must be uniform over the wave.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* src, void* dst)
+{
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* dst)
+{
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 4, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane j receives element
+// j & 3 of the 8-byte segments addressed by lanes 4 e + (j >> 2), e = 0..3.
+__device__ __forceinline__ bf16x4 ds_read_tr(const bf16* p)
+{
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b)
+{
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ bf16x4 cvt4(const f32x4& x)
+{
+    return bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                  static_cast<bf16>(x[3])};
+}
+
+__device__ __forceinline__ float bcast(float x, int lane)
+{
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+__device__ __forceinline__ void mfma16(f32x4& d, const bf16x4& a, const bf16x4& b)
+{
+    d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, d, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma32(f32x4& d, const bf16x8& a, const bf16x8& b)
+{
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d, 0, 0, 0);
+}
+
+// Role layout of one workgroup.  Waves are dealt to the four SIMDs round
+// robin, so the order puts the two heaviest roles (builders, memory) on
+// different SIMDs and pairs the factor and loader waves with memory waves.
+template <int DK_, int NB_, int NMW_, bool ISO_>
+struct Cfg {
+    static constexpr int DK = DK_;
+    static constexpr int NB = NB_;    // 16-column blocks per memory wave
+    static constexpr int NMW = NMW_;  // memory waves
+    static constexpr bool ISO = ISO_;
+    static constexpr int DVT = 16 * NB * NMW;
+    static constexpr int NBW = DK / 64;  // builder waves, one lane per key channel
+    static constexpr int W_BLD = NMW;
+    static constexpr int W_FAC = NMW + NBW;  // factor, first wave (T); W_FAC + 1: W = T Kb
+    static constexpr int W_LDR = W_FAC + 2;
+    static constexpr int W_ISO = W_LDR + 1;
+    static constexpr int NWAVES = W_LDR + 1 + (ISO ? 1 : 0);
+    // pipeline leads (steps between a role's work on a chunk and the memory
+    // waves applying it): builders 3, isotropic wave 4, raw copies LR (two
+    // steps in flight before their first reader)
+    static constexpr int LB = 3;
+    static constexpr int LR = ISO ? 6 : 5;
+    static constexpr int NRAW = LR - LB + 1;  // raw-input slots: copy issue .. builders read
+    static constexpr int NOPS = 4;        // operand slots (builders -> factor -> memory)
+    // operands in token-quad layout: element (t, i) at [t >> 2][i][t & 3];
+    // the quad stride is padded by 32 bytes so that the four quads of one
+    // channel sit on different banks
+    static constexpr int QS = DK * 4 + 16;
+    static constexpr int LDF = C + 4;  // Aqk rows (40 bytes)
+};
+
+template <typename CF>
+struct Smem {
+    static constexpr int DK = CF::DK;
+    struct Ops {  // builders -> factor, memory
+        alignas(16) bf16 Kb[4 * CF::QS];
+        alignas(16) bf16 Qb[4 * CF::QS];
+        alignas(16) bf16 Ktp[4 * CF::QS];
+        alignas(16) float gC[DK];
+    };
+    struct Fac {  // second factor wave -> memory
+        alignas(16) bf16 W[4 * CF::QS];
+    };
+    struct Tri {  // first factor wave -> second factor wave, memory
+        alignas(16) float Mt[C * 20];         // M^T (fp32), rows padded to 20
+        alignas(16) float dinv[C];            // 1 / (r_t + z_t)
+        alignas(16) bf16 Tt[C * C];           // T^T (bf16, rows of 32 bytes)
+        alignas(16) bf16 Aqk[C * CF::LDF];    // Aqk (bf16)
+    };
+    struct Raw {  // raw inputs of one chunk, rows of tokens as in global memory
+        alignas(16) float alpha[C * DK];
+        alignas(16) float omega[CF::ISO ? 4 : C * DK];
+        alignas(16) bf16 k[C * DK];
+        alignas(16) bf16 q[C * DK];
+    };
+    // the arrays the memory waves read every step come first, so that their
+    // addresses stay within reach of the LDS instructions' immediate offsets
+    Ops op[CF::NOPS];
+    Fac fac[2];
+    Tri tri[3];
+    alignas(16) bf16 v[3][C * CF::DVT];  // rows of DVT; 16-byte block b of row t at b ^ (t & 7)
+    alignas(16) float rr[NRING][C];  // r_t
+    alignas(16) float wr[NRING][C];  // isotropic omega_t
+    alignas(16) float bh[NRING][C];  // isotropic b^_t
+    Raw raw[CF::NRAW];
+};
+
+// Offset (elements) of the 8-byte segment that lane (g, l16) addresses in a
+// token-quad operand so that ds_read_tr returns, in lane (g, c), the values
+// X[t = c][4 g + e], e = 0..3 (channel offset i0 adds 4 i0 elements).
+template <int QS>
+__device__ __forceinline__ int quad_tr_lane(int lane)
+{
+    const int g = lane >> 4, l16 = lane & 15;
+    return (l16 & 3) * QS + (4 * g + (l16 >> 2)) * 4;
+}
+
+// A / B fragment of one K = 32 step over channels 32 m + {4 g + e, 16 + 4 g + e}
+// (the order in which two 16-row accumulator blocks of S feed the same step)
+__device__ __forceinline__ bf16x8 quad_frag32(const bf16* lane_base, int m)
+{
+    return cat8(ds_read_tr(lane_base + 128 * m), ds_read_tr(lane_base + 128 * m + 64));
+}
+
+template <typename CF>
+__global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArgs a)
+{
+    using SM = Smem<CF>;
+    constexpr int DK = CF::DK;
+    constexpr int NB = CF::NB;
+    constexpr int NMW = CF::NMW;
+    constexpr int DVT = CF::DVT;
+    constexpr int QS = CF::QS;
+    constexpr int LDF = CF::LDF;
+    constexpr int LR = CF::LR;
+    constexpr int LB = CF::LB;
+    constexpr int NRAW = CF::NRAW;
+    constexpr int NOPS = CF::NOPS;
+    constexpr bool ISO = CF::ISO;
+    static_assert(sizeof(SM) <= 160 * 1024, "LDS budget");
+    static_assert(DK % 64 == 0 && DVT % 64 == 0, "tile shape");
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    SM& sm = *reinterpret_cast<SM*>(smem_raw);
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int g4 = lane >> 4, c16 = lane & 15;
+
+    // XCD-aware tile order: blocks are dispatched round-robin over the 8
+    // XCDs, so consecutive logical tiles (the value tiles of one head, which
+    // read the same keys and gates) land on the same XCD / L2.
+    const int ntiles = a.dv / DVT;
+    const int nblk = gridDim.x;
+    int L = blockIdx.x;
+    if ((nblk & 7) == 0)
+        L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    const int bh = L / ntiles, tile = L % ntiles;
+    const int b = bh / a.H, h = bh % a.H;
+    const int j0 = tile * DVT;
+    const int T = a.T, H = a.H, dv = a.dv;
+    const float mu = a.mu;
+    const int nchunks = (T + C - 1) / C;
+    auto n_valid = [&](int x) { return min(C, T - x * C); };
+    auto row_k = [&](int t) { return (((size_t)b * T + t) * H + h) * DK; };
+    auto row_v = [&](int t) { return (((size_t)b * T + t) * H + h) * dv; };
+    auto row_s = [&](int t) { return ((size_t)b * T + t) * H + h; };
+
+    if (wave < NMW) {
+        // ===================== memory waves =====================
+        // block nb of wave w covers value columns jl = 16 (NB w + nb) + c16;
+        // Sacc[nb][n] holds S[16 n + 4 g4 + r][j0 + jl]
+        const int w = wave;
+        f32x4 Sacc[NB][DK / 16];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int col = j0 + 16 * (NB * w + nb) + c16;
+            if (a.S0) {
+                const float* S0 = a.S0 + (size_t)bh * DK * dv + col;
+#pragma unroll
+                for (int n = 0; n < DK / 16; ++n)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Sacc[nb][n][r] = S0[(size_t)(16 * n + 4 * g4 + r) * dv];
+            } else {
+#pragma unroll
+                for (int n = 0; n < DK / 16; ++n)
+                    Sacc[nb][n] = zero4();
+            }
+        }
+        // lane parts of the LDS addresses (elements)
+        const int tr_lane = quad_tr_lane<QS>(lane);   // W, Qb transpose reads
+        const int kt_lane = g4 * QS + c16 * 4;        // Ktp^T rows: quad g4, channel c16
+        const int fr_lane = c16 * LDF + 4 * g4;       // Aqk rows
+        const int tt_lane = (4 * g4 + ((lane >> 2) & 3)) * C + 4 * (lane & 3);  // T^T transpose reads
+        int v_lane[NB];                               // v tile transpose reads
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int t = 4 * g4 + ((lane >> 2) & 3);
+            const int col = 16 * (NB * w + nb) + 4 * (lane & 3);
+            v_lane[nb] = t * DVT + (((col >> 3) ^ (t & 7)) << 3) + (col & 7);
+        }
+        // o rows of this lane (token c16 of each chunk), advanced per chunk
+        const size_t o_step = (size_t)C * H * dv;
+        bf16* orow = reinterpret_cast<bf16*>(a.o) + row_v(min(c16, max(T - 1, 0))) + j0 +
+                     16 * NB * w + 4 * g4;
+
+        auto apply = [&](auto full_tag, int c) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            const int nv = FULL ? C : n_valid(c);
+            const auto& op = sm.op[c & (NOPS - 1)];
+            const auto& fc = sm.fac[c & 1];
+            const auto& tri = sm.tri[c % 3];
+            const bf16* V = sm.v[c % 3];
+            const bf16* wT = fc.W + tr_lane;
+            const bf16* qT = op.Qb + tr_lane;
+            // every LDS operand of the chunk is requested before the first use
+            bf16x8 wf[DK / 32], qf[DK / 32];
+#pragma unroll
+            for (int m = 0; m < DK / 32; ++m) {
+                wf[m] = quad_frag32(wT, m);
+                qf[m] = quad_frag32(qT, m);
+            }
+            const bf16x4 tfr = ds_read_tr(tri.Tt + tt_lane);  // T[t][4 g4 + e]
+            const bf16x4 afr = *reinterpret_cast<const bf16x4*>(tri.Aqk + fr_lane);
+            bf16x4 vfr[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                vfr[nb] = ds_read_tr(V + v_lane[nb]);
+                if constexpr (!FULL) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * g4 + e >= nv)
+                            vfr[nb][e] = static_cast<bf16>(0.f);
+                }
+            }
+            bf16x4 ktf[DK / 16];
+            f32x4 gcf[DK / 16];
+#pragma unroll
+            for (int n = 0; n < DK / 16; ++n) {
+                ktf[n] = *reinterpret_cast<const bf16x4*>(op.Ktp + kt_lane + 64 * n);
+                gcf[n] = *reinterpret_cast<const f32x4*>(&op.gC[16 * n + 4 * g4]);
+            }
+            // U = T V (off the S chain)
+            f32x4 accU[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                accU[nb] = zero4();
+                mfma16(accU[nb], tfr, vfr[nb]);
+            }
+            // front:  X = W S  ([t][j]),   O^T = S^T Qb^T  ([j][t])
+            f32x4 accX[NB], accO[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                accX[nb] = zero4();
+                accO[nb] = zero4();
+            }
+#pragma unroll
+            for (int m = 0; m < DK / 32; ++m) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const bf16x8 s = cat8(cvt4(Sacc[nb][2 * m]), cvt4(Sacc[nb][2 * m + 1]));
+                    mfma32(accX[nb], wf[m], s);
+                    mfma32(accO[nb], s, qf[m]);
+                }
+            }
+            bf16x4 dfr[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                // Delta' = U - W S
+                dfr[nb] = cvt4(accU[nb] - accX[nb]);
+                // O^T += Delta'^T Aqk^T
+                mfma16(accO[nb], dfr[nb], afr);
+                if (FULL || c16 < nv)
+                    *reinterpret_cast<bf16x4*>(orow + 16 * nb) = cvt4(accO[nb]);
+            }
+            // S <- diag(G_C) (S + Ktp^T Delta')
+#pragma unroll
+            for (int n = 0; n < DK / 16; ++n) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    mfma16(Sacc[nb][n], ktf[n], dfr[nb]);
+                    Sacc[nb][n] *= gcf[n];
+                }
+            }
+        };
+        for (int c = -LR; c < nchunks; ++c) {
+            if (c >= 0) {
+                if (n_valid(c) == C)
+                    apply(std::integral_constant<bool, true>{}, c);
+                else
+                    apply(std::integral_constant<bool, false>{}, c);
+                orow += o_step;
+            }
+            lds_barrier();
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float* ST = a.S_T + (size_t)bh * DK * dv + j0 + 16 * (NB * w + nb) + c16;
+#pragma unroll
+            for (int n = 0; n < DK / 16; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    ST[(size_t)(16 * n + 4 * g4 + r) * dv] = Sacc[nb][n][r];
+        }
+    } else if (wave < CF::W_FAC) {
+        // ================ builder waves: lane = key channel ================
+        const int i = (wave - CF::W_BLD) * 64 + lane;
+        // Diagonal: homogeneous variance [n; d];  Isotropic: no state here
+        float vn = (!ISO && a.var0) ? a.var0[(size_t)bh * DK + i] : 1.f;
+        float vd = 1.f;
+        auto build = [&](auto full_tag, int X) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            const int nv = FULL ? C : n_valid(X);
+            const auto& raw = sm.raw[X % NRAW];
+            auto& op = sm.op[X & (NOPS - 1)];
+            // per-token scalars, computed by lanes 0..15 and broadcast:
+            // Diagonal mu / r_t, Isotropic b^_t
+            float tok;
+            if constexpr (ISO)
+                tok = sm.bh[X % NRING][c16];
+            else
+                tok = mu * rcp(sm.rr[X % NRING][c16]);
+            float al[C], om[C], kf[C], qf[C];
+#pragma unroll
+            for (int t = 0; t < C; ++t) {
+                al[t] = raw.alpha[t * DK + i];
+                if constexpr (!ISO)
+                    om[t] = raw.omega[t * DK + i];
+                kf[t] = static_cast<float>(raw.k[t * DK + i]);
+                qf[t] = static_cast<float>(raw.q[t * DK + i]);
+            }
+            if constexpr (!FULL) {
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    const bool ok = t < nv;
+                    al[t] = ok ? al[t] : 1.f;
+                    if constexpr (!ISO)
+                        om[t] = ok ? om[t] : 0.f;
+                    kf[t] = ok ? kf[t] : 0.f;
+                    qf[t] = ok ? qf[t] : 0.f;
+                }
+            }
+            float kb[C], qb[C], kt[C];
+            float G = 1.f;
+            if constexpr (!ISO) {
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    const float u = kf[t] * bcast(tok, t) * kf[t];  // mu k^2 / r
+                    const float n1 = fmaf(om[t], vd, (al[t] * al[t]) * vn);  // p^_t = n1 / vd
+                    G *= al[t];
+                    const float re = rcp(vd * G);
+                    kt[t] = (kf[t] * n1) * re;        // p^_t k_t / G_t
+                    vd = fmaf(u, n1, vd);             // d_t = d_{t-1} + u_t n_t
+                    vn = n1;
+                    kb[t] = kf[t] * G;
+                    qb[t] = qf[t] * G;
+                    if ((t & 3) == 3) {
+                        // rescale [n; d] by 2^-e(d): exact, keeps n / d
+                        const int ex = __builtin_amdgcn_frexp_expf(vd);
+                        vn = __builtin_amdgcn_ldexpf(vn, -ex);
+                        vd = __builtin_amdgcn_ldexpf(vd, -ex);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    G *= al[t];
+                    kb[t] = kf[t] * G;
+                    qb[t] = qf[t] * G;
+                }
+                // 1 / G_t = (prod_{s > t} alpha_s) / G_C
+                const float rgc = rcp(G);
+                float suf = 1.f;
+#pragma unroll
+                for (int t = C - 1; t >= 0; --t) {
+                    kt[t] = bcast(tok, t) * kf[t] * (suf * rgc);
+                    suf *= al[t];
+                }
+            }
+            // token-quad writes: channel i's four tokens 4 tq .. +3 as 8 bytes
+#pragma unroll
+            for (int tq = 0; tq < 4; ++tq) {
+                const int o = tq * QS + i * 4;
+                *reinterpret_cast<bf16x4*>(op.Kb + o) =
+                    bf16x4{static_cast<bf16>(kb[4 * tq]), static_cast<bf16>(kb[4 * tq + 1]),
+                           static_cast<bf16>(kb[4 * tq + 2]), static_cast<bf16>(kb[4 * tq + 3])};
+                *reinterpret_cast<bf16x4*>(op.Qb + o) =
+                    bf16x4{static_cast<bf16>(qb[4 * tq]), static_cast<bf16>(qb[4 * tq + 1]),
+                           static_cast<bf16>(qb[4 * tq + 2]), static_cast<bf16>(qb[4 * tq + 3])};
+                *reinterpret_cast<bf16x4*>(op.Ktp + o) =
+                    bf16x4{static_cast<bf16>(kt[4 * tq]), static_cast<bf16>(kt[4 * tq + 1]),
+                           static_cast<bf16>(kt[4 * tq + 2]), static_cast<bf16>(kt[4 * tq + 3])};
+            }
+            op.gC[i] = G;
+        };
+        for (int c = -LR; c < nchunks; ++c) {
+            const int X = c + LB;
+            if (X >= 0 && X < nchunks) {
+                if (n_valid(X) == C)
+                    build(std::integral_constant<bool, true>{}, X);
+                else
+                    build(std::integral_constant<bool, false>{}, X);
+            }
+            lds_barrier();
+        }
+        if constexpr (!ISO) {
+            if (tile == 0)
+                a.var_T[(size_t)bh * DK + i] = vn / vd;
+        }
+    } else if (wave == CF::W_FAC) {
+        // ============ first factor wave: L', Aqk and T of chunk c + 2 ============
+        const int tr_lane = quad_tr_lane<QS>(lane);
+        for (int c = -LR; c < nchunks; ++c) {
+            const int F = c + 2;
+            if (F >= 0 && F < nchunks) {
+                const int nv = n_valid(F);
+                const auto& op = sm.op[F & (NOPS - 1)];
+                auto& tr = sm.tri[F % 3];
+                const float* rr = sm.rr[F % NRING];
+                bf16x8 kbf[DK / 32], ktf[DK / 32], qbf[DK / 32];
+#pragma unroll
+                for (int m = 0; m < DK / 32; ++m) {
+                    kbf[m] = quad_frag32(op.Kb + tr_lane, m);
+                    ktf[m] = quad_frag32(op.Ktp + tr_lane, m);
+                    qbf[m] = quad_frag32(op.Qb + tr_lane, m);
+                }
+                // L'[t][s] = Kb_t . Ktp_s,   Aqk^T[u][t] = Ktp_u . Qb_t
+                f32x4 accL = zero4(), accQ = zero4();
+#pragma unroll
+                for (int m = 0; m < DK / 32; ++m) {
+                    mfma32(accL, kbf[m], ktf[m]);
+                    mfma32(accQ, ktf[m], qbf[m]);
+                }
+                // M^T[s][t] = L'[t][s]   (lane holds L'[4 g4 + r][c16])
+                *reinterpret_cast<f32x4*>(&tr.Mt[c16 * 20 + 4 * g4]) = accL;
+                if ((c16 >> 2) == g4) {
+                    const int rs = c16 & 3;
+                    const float z = rs == 0 ? accL[0] : rs == 1 ? accL[1] : rs == 2 ? accL[2] : accL[3];
+                    const float rt = c16 < nv ? rr[c16] : 1.f;
+                    tr.dinv[c16] = rcp(rt + z);
+                }
+                // Aqk[t][u] = Aqk^T[u][t] for u <= t, else 0
+                {
+                    f32x4 aq;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        aq[r] = (4 * g4 + r <= c16) ? accQ[r] : 0.f;
+                    *reinterpret_cast<bf16x4*>(&tr.Aqk[c16 * LDF + 4 * g4]) = cvt4(aq);
+                }
+                wave_lds_sync();
+                // T = M^-1, column c16 per lane (every lane group computes the
+                // same columns): M x = e_c by forward substitution, with the
+                // sub-diagonal part of column s of M read as row s of M^T
+                float d[C];
+#pragma unroll
+                for (int q4 = 0; q4 < C / 4; ++q4) {
+                    const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&tr.dinv[4 * q4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        d[4 * q4 + e] = dv4[e];
+                }
+                float x[C], acc[C];
+#pragma unroll
+                for (int t = 0; t < C; ++t)
+                    acc[t] = (t == c16) ? 1.f : 0.f;
+#pragma unroll
+                for (int s = 0; s < C; ++s) {
+                    x[s] = acc[s] * d[s];
+#pragma unroll
+                    for (int q4 = (s + 1) >> 2; q4 < C / 4; ++q4) {
+                        const f32x4 mrow = *reinterpret_cast<const f32x4*>(&tr.Mt[s * 20 + 4 * q4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int t = 4 * q4 + e;
+                            if (t > s)
+                                acc[t] = fmaf(-mrow[e], x[s], acc[t]);
+                        }
+                    }
+                }
+                // row c16 of T^T = column c16 of T
+                if (g4 == 0) {
+                    bf16x8 lo, hi;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        lo[e] = static_cast<bf16>(x[e]);
+                        hi[e] = static_cast<bf16>(x[8 + e]);
+                    }
+                    *reinterpret_cast<bf16x8*>(&tr.Tt[c16 * C]) = lo;
+                    *reinterpret_cast<bf16x8*>(&tr.Tt[c16 * C + 8]) = hi;
+                }
+            }
+            lds_barrier();
+        }
+    } else if (wave == CF::W_FAC + 1) {
+        // ============ second factor wave: W = T Kb of chunk c + 1 ============
+        // A[t][u] = T by a transpose read of T^T,  B[u][i] = Kb (quad segment
+        // u / 4 of channel i), 16 channels per product
+        const int tt_lane = (4 * g4 + ((lane >> 2) & 3)) * C + 4 * (lane & 3);
+        for (int c = -LR; c < nchunks; ++c) {
+            const int F = c + 1;
+            if (F >= 0 && F < nchunks) {
+                const auto& tr = sm.tri[F % 3];
+                const auto& op = sm.op[F & (NOPS - 1)];
+                auto& fc = sm.fac[F & 1];
+                const bf16x4 ta = ds_read_tr(tr.Tt + tt_lane);
+                bf16x4 kbq[DK / 16];
+#pragma unroll
+                for (int n = 0; n < DK / 16; ++n)
+                    kbq[n] = *reinterpret_cast<const bf16x4*>(op.Kb + g4 * QS + (16 * n + c16) * 4);
+#pragma unroll
+                for (int n = 0; n < DK / 16; ++n) {
+                    f32x4 accW = zero4();
+                    mfma16(accW, ta, kbq[n]);
+                    // lane holds W[4 g4 + r][16 n + c16]: quad segment g4 of that channel
+                    *reinterpret_cast<bf16x4*>(fc.W + g4 * QS + (16 * n + c16) * 4) = cvt4(accW);
+                }
+            }
+            lds_barrier();
+        }
+    } else if (wave == CF::W_LDR) {
+        // ===================== loader wave =====================
+        // direct copies into LDS: raw inputs of chunk c + LR, v of chunk c + 2
+        constexpr int VE = 8;                               // bf16 per 16 bytes
+        constexpr int LPR_A = DK * 4 / 16;                  // lanes per alpha / omega row
+        constexpr int RPI_A = 64 / LPR_A, NI_A = C / RPI_A; // rows per copy, copies
+        constexpr int LPR_K = DK * 2 / 16;                  // lanes per k / q row
+        constexpr int RPI_K = 64 / LPR_K, NI_K = C / RPI_K;
+        constexpr int LPR_V = DVT * 2 / 16;                 // lanes per v tile row
+        constexpr int RPI_V = 64 / LPR_V, NI_V = C / RPI_V;
+        static_assert(LPR_A <= 64 && LPR_K <= 64 && LPR_V == 8 && NI_A >= 1 && NI_K >= 1,
+                      "row / lane split");
+        constexpr int NSTG = NI_A * (ISO ? 1 : 2) + 2 * NI_K + 1 + (ISO ? 1 : 0);
+        constexpr int NVI = NI_V;
+        static_assert(NSTG + NVI <= 63, "outstanding copies within the vmcnt range");
+        const float* __restrict__ alg = a.alpha;
+        const float* __restrict__ omg = a.omega;
+        const bf16* __restrict__ kg = reinterpret_cast<const bf16*>(a.k);
+        const bf16* __restrict__ qg = reinterpret_cast<const bf16*>(a.q);
+        const bf16* __restrict__ vg = reinterpret_cast<const bf16*>(a.v);
+        // per-lane element offsets inside a chunk (32-bit; the chunk base is
+        // uniform); rows past the end of a ragged chunk repeat its last row
+        const uint32_t tsk = (uint32_t)(H * DK), tsv = (uint32_t)(H * dv), tss = (uint32_t)H;
+        auto off_a = [&](int j, int lim) {
+            return (uint32_t)min(j * RPI_A + lane / LPR_A, lim) * tsk + (lane % LPR_A) * 4;
+        };
+        auto off_k = [&](int j, int lim) {
+            return (uint32_t)min(j * RPI_K + lane / LPR_K, lim) * tsk + (lane % LPR_K) * VE;
+        };
+        auto off_v = [&](int j, int lim) {
+            const int p = 64 * j + lane;
+            const int tl = p / LPR_V;
+            const int blk = (p % LPR_V) ^ (tl & 7);
+            return (uint32_t)min(tl, lim) * tsv + blk * VE;
+        };
+        uint32_t oa[NI_A], ok_[NI_K], ov[NI_V];
+#pragma unroll
+        for (int j = 0; j < NI_A; ++j)
+            oa[j] = off_a(j, C - 1);
+#pragma unroll
+        for (int j = 0; j < NI_K; ++j)
+            ok_[j] = off_k(j, C - 1);
+#pragma unroll
+        for (int j = 0; j < NI_V; ++j)
+            ov[j] = off_v(j, C - 1);
+        for (int c = -LR; c < nchunks; ++c) {
+            const int X = c + LR;
+            const bool sv = X < nchunks;
+            const int XV = c + 2;
+            const bool vv = XV >= 0 && XV < nchunks;
+            if (sv) {
+                auto& st = sm.raw[X % NRAW];
+                const int tb = X * C;
+                const int lim = n_valid(X) - 1;
+                const size_t cb = row_k(tb);  // uniform
+                const float* ab = alg + cb;
+                const float* wb = omg + cb;
+                const bf16* kb = kg + cb;
+                const bf16* qb = qg + cb;
+                auto copy_stage = [&](auto full_tag) {
+                    constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+                    for (int j = 0; j < NI_A; ++j) {
+                        const uint32_t o = FULL ? oa[j] : off_a(j, lim);
+                        dma16(ab + o, &st.alpha[j * RPI_A * DK]);
+                        if constexpr (!ISO)
+                            dma16(wb + o, &st.omega[j * RPI_A * DK]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < NI_K; ++j) {
+                        const uint32_t o = FULL ? ok_[j] : off_k(j, lim);
+                        dma16(kb + o, &st.k[j * RPI_K * DK]);
+                        dma16(qb + o, &st.q[j * RPI_K * DK]);
+                    }
+                };
+                if (lim == C - 1)
+                    copy_stage(std::integral_constant<bool, true>{});
+                else
+                    copy_stage(std::integral_constant<bool, false>{});
+                if (lane < C) {
+                    const uint32_t o = (uint32_t)min(lane, lim) * tss;
+                    const size_t sb = row_s(tb);
+                    dma4(a.r + sb + o, sm.rr[X % NRING]);
+                    if constexpr (ISO)
+                        dma4(omg + sb + o, sm.wr[X % NRING]);
+                }
+            }
+            if (vv) {
+                bf16* vdst = sm.v[XV % 3];
+                const int lim = n_valid(XV) - 1;
+                const bf16* vb = vg + row_v(XV * C) + j0;  // uniform
+                // LDS block p = 64 j + lane holds row p / 8 and data block
+                // (p % 8) ^ (row & 7) of that row
+                if (lim == C - 1) {
+#pragma unroll
+                    for (int j = 0; j < NI_V; ++j)
+                        dma16(vb + ov[j], vdst + 64 * j * VE);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < NI_V; ++j)
+                        dma16(vb + off_v(j, lim), vdst + 64 * j * VE);
+                }
+            }
+            if (sv && vv)
+                vm_wait<NSTG + NVI>();
+            else if (sv)
+                vm_wait<NSTG>();
+            else if (vv)
+                vm_wait<NVI>();
+            else
+                vm_wait<0>();
+            lds_barrier();
+        }
+    } else if constexpr (ISO) {
+        // ============ isotropic wave: DK / 64 channels per lane ============
+        constexpr int CPL = DK / 64;
+        float bvar = a.var0 ? a.var0[bh] : 1.f;
+        for (int c = -LR; c < nchunks; ++c) {
+            const int X = c + LB + 1;
+            if (X >= 0 && X < nchunks) {
+                const int nv = n_valid(X);
+                const auto& st = sm.raw[X % NRAW];
+                // per-lane partial sums of alpha^2 and k^2 over its channels
+                float sa[C], sk[C];
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    sa[t] = 0.f;
+                    sk[t] = 0.f;
+                }
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    const int i = lane + 64 * cc;
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        const float alv = st.alpha[t * DK + i];
+                        const float kvv = static_cast<float>(st.k[t * DK + i]);
+                        sa[t] += alv * alv;
+                        sk[t] += kvv * kvv;
+                    }
+                }
+                // transpose-reduce over the 64 lanes: each halving step keeps
+                // half the tokens and adds the partner lane's partials of
+                // them; lane l ends with token l >> 2
+                static_assert(C == 16, "reduction tree shape");
+                auto halve = [&](auto hs_tag) {
+                    constexpr int hs = decltype(hs_tag)::value;
+                    constexpr int m = 4 * hs;  // partner lane distance
+                    const bool up = (lane & m) != 0;
+#pragma unroll
+                    for (int j = 0; j < hs; ++j) {
+                        const float lo_a = sa[j], hi_a = sa[j + hs];
+                        const float lo_k = sk[j], hi_k = sk[j + hs];
+                        const float ra = __shfl_xor(up ? lo_a : hi_a, m);
+                        const float rk = __shfl_xor(up ? lo_k : hi_k, m);
+                        sa[j] = (up ? hi_a : lo_a) + ra;
+                        sk[j] = (up ? hi_k : lo_k) + rk;
+                    }
+                };
+                halve(std::integral_constant<int, 8>{});
+                halve(std::integral_constant<int, 4>{});
+                halve(std::integral_constant<int, 2>{});
+                halve(std::integral_constant<int, 1>{});
+                float ta = sa[0], tk = sk[0];
+                ta += __shfl_xor(ta, 1);
+                tk += __shfl_xor(tk, 1);
+                ta += __shfl_xor(ta, 2);
+                tk += __shfl_xor(tk, 2);
+                // scalar recurrence over the chunk (uniform over the wave);
+                // padded tokens (alpha = 1, k = 0) get a = 1, |k|^2 = 0 below
+                const float* rr = sm.rr[X % NRING];
+                const float* wr = sm.wr[X % NRING];
+                float bhv[C], rv[C], wv[C];
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    rv[t] = rr[t];
+                    wv[t] = wr[t];
+                }
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    const bool ok = t < nv;
+                    const float A2 = ok ? bcast(ta, 4 * t) : (float)DK;
+                    const float K2 = ok ? bcast(tk, 4 * t) : 0.f;
+                    const float rt = ok ? rv[t] : 1.f;
+                    const float wt = ok ? wv[t] : 0.f;
+                    const float bhat = A2 * (1.f / DK) * bvar + wt;
+                    const float dr = (float)DK * rt;
+                    bvar = bhat * dr * rcp(dr + mu * K2 * bhat);
+                    bhv[t] = bhat;
+                }
+                if (lane == 0) {
+#pragma unroll
+                    for (int t = 0; t < C; t += 4)
+                        *reinterpret_cast<f32x4*>(&sm.bh[X % NRING][t]) =
+                            f32x4{bhv[t], bhv[t + 1], bhv[t + 2], bhv[t + 3]};
+                }
+            }
+            lds_barrier();
+        }
+        if (tile == 0 && lane == 0)
+            a.var_T[bh] = bvar;
+    }
+}
+
+template <typename CF>
+static hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream)
+{
+    using SM = Smem<CF>;
+    auto kern = kdn_walk_fwd_kernel<CF>;
+    const size_t smem = sizeof(SM);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess)
+        return e;
+    const int nblk = a.B * a.H * (a.dv / CF::DVT);
+    hipLaunchKernelGGL(kern, dim3(nblk), dim3(64 * CF::NWAVES), smem, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace walk
+
+hipError_t launch_walk_fwd(const FwdArgs& a, bool iso, hipStream_t stream)
+{
+    using namespace walk;
+    if (a.dk == 128)
+        return iso ? launch_cfg<Cfg<128, 2, 2, true>>(a, stream)
+                   : launch_cfg<Cfg<128, 2, 2, false>>(a, stream);
+    return iso ? launch_cfg<Cfg<64, 2, 2, true>>(a, stream)
+               : launch_cfg<Cfg<64, 2, 2, false>>(a, stream);
+}
+
+}  // namespace kdn
