@@ -30,12 +30,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["kdn_chunk.hip", "kdn_common.h", "kdn_step.hip", "kdn_gain.hip"]
+# sources each measured kernel is built from (traffic figures go stale when they change)
+KERNEL_SOURCES = {
+    "kdn_walk_fwd_kernel": ["kdn_walk.hip", "kdn_common.h", "kdn_internal.h"],
+    "kdn_chunk_fwd_kernel": ["kdn_chunk.hip", "kdn_common.h", "kdn_internal.h"],
+    "kdn_step_kernel": ["kdn_step.hip", "kdn_common.h", "kdn_internal.h"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for s in KERNEL_SOURCES:
+    for s in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "kalman_delta_rule_amd", "csrc", s), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -58,7 +63,17 @@ def alg_bytes_step(variant: str, B, H, dk, dv, s_io: int) -> int:
     return B * H * per_head
 
 
-def traffic_for(key: str):
+def fwd_kernel_name(io: str) -> str:
+    """The kernel one forward call launches: bf16 io runs the walk kernel,
+    fp32 io the fp32 chunk kernel."""
+    return "kdn_walk_fwd_kernel" if io == "bf16" else "kdn_chunk_fwd_kernel"
+
+
+def traffic_key(kernel: str, workload: str, variant: str) -> str:
+    return "%s:%s:%s" % (kernel, workload, variant)
+
+
+def traffic_for(kernel: str, key: str):
     """HBM bytes per launch measured by counters, if still valid."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -66,7 +81,7 @@ def traffic_for(key: str):
     except (OSError, ValueError):
         return None
     ent = rec.get(key)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -176,8 +191,8 @@ def main():
     s_io = 2 if w.io == "bf16" else 4
     alg = alg_bytes_fwd(variant, B, T, H, dk, dv, s_io)
     achieved = alg / (ms_step / 1e3) / 1e9
-    key = "chunk_fwd_%s_%s_B%dT%dH%dd%d" % (variant, w.io, B, T, H, dk)
-    traffic = traffic_for(key)
+    kname = fwd_kernel_name(w.io)
+    traffic = traffic_for(kname, traffic_key(kname, w.name, variant))
     print("[bench] %d steps: %.3f ms/step (events), wall %.3f s" % (args.steps, ms_step, wall),
           file=sys.stderr, flush=True)
 
@@ -213,7 +228,7 @@ def main():
                    "global_batch": B, "seq_len": T, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "alg_bytes_per_launch": alg, "kernel": "kdn_chunk_fwd_kernel"},
+                     "alg_bytes_per_launch": alg, "kernel": kname},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -275,7 +290,8 @@ def bench_decode(args, w):
                    "dv": w.dv, "io": "bf16", "state": "f32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_for("step_%s_B%dH%dd%d" % (variant, w.B, w.H, w.dk)),
+                     "traffic": traffic_for("kdn_step_kernel",
+                                            traffic_key("kdn_step_kernel", w.name, variant)),
                      "alg_bytes_per_launch": alg, "kernel": "kdn_step_kernel"},
         "cpu_baseline": None,
     }

@@ -68,15 +68,25 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Direct global -> LDS copy: lane l's 16 (or 4) bytes land at dst + 16 l
-// (4 l).  dst must be uniform over the wave.  Completion is tracked by vmcnt.
-__device__ __forceinline__ void dma16(const void* src, void* dst)
+// Direct global -> LDS copy: lane l's 16 (or 4) bytes, read at base + off
+// (base uniform, off the lane's byte offset), land at LDS byte address
+// lds + 16 l (4 l); lds is uniform.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds)
 {
-    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)((const char*)base + off),
+                                     (lds_void_t*)(size_t)lds, 16, 0, 0);
 }
-__device__ __forceinline__ void dma4(const void* src, void* dst)
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds)
 {
-    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)((const char*)base + off),
+                                     (lds_void_t*)(size_t)lds, 4, 0, 0);
+}
+
+// Order this wave's LDS writes before its later LDS reads (lanes read what
+// other lanes of the same wave wrote).  Only LDS operations are waited for.
+__device__ __forceinline__ void lds_wave_sync()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 template <int N>
@@ -532,7 +542,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                         aq[r] = (4 * g4 + r <= c16) ? accQ[r] : 0.f;
                     *reinterpret_cast<bf16x4*>(&tr.Aqk[c16 * LDF + 4 * g4]) = cvt4(aq);
                 }
-                wave_lds_sync();
+                lds_wave_sync();
                 // T = M^-1, column c16 per lane (every lane group computes the
                 // same columns): M x = e_c by forward substitution, with the
                 // sub-diagonal part of column s of M read as row s of M^T
@@ -617,25 +627,25 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         constexpr int NSTG = NI_A * (ISO ? 1 : 2) + 2 * NI_K + 1 + (ISO ? 1 : 0);
         constexpr int NVI = NI_V;
         static_assert(NSTG + NVI <= 63, "outstanding copies within the vmcnt range");
-        const float* __restrict__ alg = a.alpha;
-        const float* __restrict__ omg = a.omega;
-        const bf16* __restrict__ kg = reinterpret_cast<const bf16*>(a.k);
-        const bf16* __restrict__ qg = reinterpret_cast<const bf16*>(a.q);
-        const bf16* __restrict__ vg = reinterpret_cast<const bf16*>(a.v);
-        // per-lane element offsets inside a chunk (32-bit; the chunk base is
-        // uniform); rows past the end of a ragged chunk repeat its last row
-        const uint32_t tsk = (uint32_t)(H * DK), tsv = (uint32_t)(H * dv), tss = (uint32_t)H;
-        auto off_a = [&](int j, int lim) {
-            return (uint32_t)min(j * RPI_A + lane / LPR_A, lim) * tsk + (lane % LPR_A) * 4;
+        // LDS byte addresses of the copy targets (uniform)
+        const uint32_t lds0 = (uint32_t)(size_t)(lds_void_t*)smem_raw;
+        auto lds_addr = [&](const void* p) {
+            return lds0 + (uint32_t)((const unsigned char*)p - smem_raw);
         };
-        auto off_k = [&](int j, int lim) {
-            return (uint32_t)min(j * RPI_K + lane / LPR_K, lim) * tsk + (lane % LPR_K) * VE;
+        // per-lane byte offsets inside a chunk (the chunk base is uniform);
+        // rows past the end of a ragged chunk repeat its last row
+        const uint32_t tsk = (uint32_t)(H * DK), tsv = (uint32_t)(H * dv), tss = (uint32_t)H;
+        auto off_a = [&](int j, int lim) {  // alpha / omega (4 bytes per element)
+            return 4u * ((uint32_t)min(j * RPI_A + lane / LPR_A, lim) * tsk + (lane % LPR_A) * 4);
+        };
+        auto off_k = [&](int j, int lim) {  // k / q (2 bytes per element)
+            return 2u * ((uint32_t)min(j * RPI_K + lane / LPR_K, lim) * tsk + (lane % LPR_K) * VE);
         };
         auto off_v = [&](int j, int lim) {
             const int p = 64 * j + lane;
             const int tl = p / LPR_V;
             const int blk = (p % LPR_V) ^ (tl & 7);
-            return (uint32_t)min(tl, lim) * tsv + blk * VE;
+            return 2u * ((uint32_t)min(tl, lim) * tsv + blk * VE);
         };
         uint32_t oa[NI_A], ok_[NI_K], ov[NI_V];
 #pragma unroll
@@ -653,28 +663,27 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             const int XV = c + 2;
             const bool vv = XV >= 0 && XV < nchunks;
             if (sv) {
-                auto& st = sm.raw[X % NRAW];
+                const auto& st = sm.raw[X % NRAW];
                 const int tb = X * C;
                 const int lim = n_valid(X) - 1;
                 const size_t cb = row_k(tb);  // uniform
-                const float* ab = alg + cb;
-                const float* wb = omg + cb;
-                const bf16* kb = kg + cb;
-                const bf16* qb = qg + cb;
+                const bf16* kb = reinterpret_cast<const bf16*>(a.k) + cb;
+                const bf16* qb = reinterpret_cast<const bf16*>(a.q) + cb;
+                const uint32_t la = lds_addr(st.alpha), lk = lds_addr(st.k), lq = lds_addr(st.q);
                 auto copy_stage = [&](auto full_tag) {
                     constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
                     for (int j = 0; j < NI_A; ++j) {
                         const uint32_t o = FULL ? oa[j] : off_a(j, lim);
-                        dma16(ab + o, &st.alpha[j * RPI_A * DK]);
+                        dma16(a.alpha + cb, o, la + j * RPI_A * DK * 4);
                         if constexpr (!ISO)
-                            dma16(wb + o, &st.omega[j * RPI_A * DK]);
+                            dma16(a.omega + cb, o, lds_addr(st.omega) + j * RPI_A * DK * 4);
                     }
 #pragma unroll
                     for (int j = 0; j < NI_K; ++j) {
                         const uint32_t o = FULL ? ok_[j] : off_k(j, lim);
-                        dma16(kb + o, &st.k[j * RPI_K * DK]);
-                        dma16(qb + o, &st.q[j * RPI_K * DK]);
+                        dma16(kb, o, lk + j * RPI_K * DK * 2);
+                        dma16(qb, o, lq + j * RPI_K * DK * 2);
                     }
                 };
                 if (lim == C - 1)
@@ -682,29 +691,30 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 else
                     copy_stage(std::integral_constant<bool, false>{});
                 if (lane < C) {
-                    const uint32_t o = (uint32_t)min(lane, lim) * tss;
+                    const uint32_t o = 4u * ((uint32_t)min(lane, lim) * tss);
                     const size_t sb = row_s(tb);
-                    dma4(a.r + sb + o, sm.rr[X % NRING]);
+                    dma4(a.r + sb, o, lds_addr(sm.rr[X % NRING]));
                     if constexpr (ISO)
-                        dma4(omg + sb + o, sm.wr[X % NRING]);
+                        dma4(a.omega + sb, o, lds_addr(sm.wr[X % NRING]));
                 }
             }
             if (vv) {
-                bf16* vdst = sm.v[XV % 3];
+                const uint32_t lv = lds_addr(sm.v[XV % 3]);
                 const int lim = n_valid(XV) - 1;
-                const bf16* vb = vg + row_v(XV * C) + j0;  // uniform
+                const bf16* vb = reinterpret_cast<const bf16*>(a.v) + row_v(XV * C) + j0;  // uniform
                 // LDS block p = 64 j + lane holds row p / 8 and data block
                 // (p % 8) ^ (row & 7) of that row
                 if (lim == C - 1) {
 #pragma unroll
                     for (int j = 0; j < NI_V; ++j)
-                        dma16(vb + ov[j], vdst + 64 * j * VE);
+                        dma16(vb, ov[j], lv + 64 * j * 16);
                 } else {
 #pragma unroll
                     for (int j = 0; j < NI_V; ++j)
-                        dma16(vb + off_v(j, lim), vdst + 64 * j * VE);
+                        dma16(vb, off_v(j, lim), lv + 64 * j * 16);
                 }
             }
+            // the copies of the previous step have landed
             if (sv && vv)
                 vm_wait<NSTG + NVI>();
             else if (sv)
