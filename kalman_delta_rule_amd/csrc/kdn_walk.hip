@@ -727,79 +727,160 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         }
     } else if constexpr (ISO) {
         // ============ isotropic wave: DK / 64 channels per lane ============
+        // Per token t of chunk c + 4: a_t = mean_i alpha_t,i^2 and
+        // |k_t|^2, then the scalar variance recurrence; b^_t goes to the
+        // builders.  Lane l sums channels CPL l .. CPL l + CPL - 1 of every
+        // token; a transpose-reduce over the lanes leaves one token's totals
+        // per lane (four lanes per token).
         constexpr int CPL = DK / 64;
-        float bvar = a.var0 ? a.var0[bh] : 1.f;
+        static_assert(CPL == 1 || CPL == 2, "channels per lane");
+        static_assert(C == 16, "reduction tree shape");
+        // Halving steps: a lane keeps half of its token slots and adds the
+        // partner lane's partials of them.  Distances 32 and 16 exchange
+        // slots with v_permlane32_swap / v_permlane16_swap (after the swap
+        // both registers of a lane hold partials of the same token); the
+        // in-row steps pair lanes through DPP row_mirror (l <-> 15 - l) and
+        // row_half_mirror (l <-> 7 - l), then a quad reduction finishes.
+        auto swap32 = [](float& x, float& y) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y),
+                                                            false, false);
+            x = __uint_as_float(r[0]);
+            y = __uint_as_float(r[1]);
+        };
+        auto swap16 = [](float& x, float& y) {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y),
+                                                            false, false);
+            x = __uint_as_float(r[0]);
+            y = __uint_as_float(r[1]);
+        };
+        auto dpp = [](float x, auto ctrl_tag) {
+            constexpr int CTRL = decltype(ctrl_tag)::value;
+            return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+        };
+        using MIRROR = std::integral_constant<int, 0x140>;
+        using HALF_MIRROR = std::integral_constant<int, 0x141>;
+        using QP_1032 = std::integral_constant<int, 0xb1>;  // quad_perm [1,0,3,2]
+        using QP_2301 = std::integral_constant<int, 0x4e>;  // quad_perm [2,3,0,1]
+        const bool up3 = (lane & 8) != 0, up2 = (lane & 4) != 0;
+        // v[16] -> one value per lane; every lane's slots go through the
+        // same network, so the token a lane ends with is fixed
+        auto reduce = [&](float (&v)[C]) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                swap32(v[j], v[j + 8]);
+                v[j] += v[j + 8];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                swap16(v[j], v[j + 4]);
+                v[j] += v[j + 4];
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float keep = up3 ? v[j + 2] : v[j], send = up3 ? v[j] : v[j + 2];
+                v[j] = keep + dpp(send, MIRROR{});
+            }
+            {
+                const float keep = up2 ? v[1] : v[0], send = up2 ? v[0] : v[1];
+                v[0] = keep + dpp(send, HALF_MIRROR{});
+            }
+            float x = v[0];
+            x += dpp(x, QP_1032{});
+            x += dpp(x, QP_2301{});
+            return x;
+        };
+        // the token each lane ends with: run the token numbers through the
+        // same exchanges; tok_lane[t] is a lane holding token t
+        int tok_lane[C], mine_i;
+        {
+            float id[C];
+#pragma unroll
+            for (int t = 0; t < C; ++t)
+                id[t] = (float)t;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                swap32(id[j], id[j + 8]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                swap16(id[j], id[j + 4]);
+            const float mine = up2 ? (up3 ? id[3] : id[1]) : (up3 ? id[2] : id[0]);
+            mine_i = (int)mine;
+#pragma unroll
+            for (int t = 0; t < C; ++t)
+                tok_lane[t] = __builtin_amdgcn_readfirstlane(
+                    (int)__builtin_ctzll(__ballot(mine_i == t)));
+        }
+        const float inv_dk = 1.f / (float)DK;
+        // homogeneous variance b = n / d (see the Diagonal builders):
+        //   n_t = a_t n_{t-1} + omega_t d_{t-1},  d_t = d_{t-1} + u_t n_t,
+        //   u_t = mu |k_t|^2 / (d_k r_t),  b^_t = n_t / d_{t-1}
+        float nn = a.var0 ? a.var0[bh] : 1.f, dd = 1.f;
         for (int c = -LR; c < nchunks; ++c) {
             const int X = c + LB + 1;
             if (X >= 0 && X < nchunks) {
                 const int nv = n_valid(X);
                 const auto& st = sm.raw[X % NRAW];
-                // per-lane partial sums of alpha^2 and k^2 over its channels
+                // all reads first (kept ahead of the arithmetic), then the
+                // per-lane partial sums
                 float sa[C], sk[C];
-#pragma unroll
-                for (int t = 0; t < C; ++t) {
-                    sa[t] = 0.f;
-                    sk[t] = 0.f;
-                }
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    const int i = lane + 64 * cc;
+                if constexpr (CPL == 2) {
+                    float2 al[C];
+                    uint32_t kk[C];
 #pragma unroll
                     for (int t = 0; t < C; ++t) {
-                        const float alv = st.alpha[t * DK + i];
-                        const float kvv = static_cast<float>(st.k[t * DK + i]);
-                        sa[t] += alv * alv;
-                        sk[t] += kvv * kvv;
+                        al[t] = *reinterpret_cast<const float2*>(&st.alpha[t * DK + 2 * lane]);
+                        kk[t] = *reinterpret_cast<const uint32_t*>(&st.k[t * DK + 2 * lane]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        const float k0 = __uint_as_float(kk[t] << 16);
+                        const float k1 = __uint_as_float(kk[t] & 0xffff0000u);
+                        sa[t] = fmaf(al[t].x, al[t].x, al[t].y * al[t].y);
+                        sk[t] = fmaf(k0, k0, k1 * k1);
+                    }
+                } else {
+                    float al[C];
+                    bf16 kv[C];
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        al[t] = st.alpha[t * DK + lane];
+                        kv[t] = st.k[t * DK + lane];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        const float kf = static_cast<float>(kv[t]);
+                        sa[t] = al[t] * al[t];
+                        sk[t] = kf * kf;
                     }
                 }
-                // transpose-reduce over the 64 lanes: each halving step keeps
-                // half the tokens and adds the partner lane's partials of
-                // them; lane l ends with token l >> 2
-                static_assert(C == 16, "reduction tree shape");
-                auto halve = [&](auto hs_tag) {
-                    constexpr int hs = decltype(hs_tag)::value;
-                    constexpr int m = 4 * hs;  // partner lane distance
-                    const bool up = (lane & m) != 0;
+                const float ta = reduce(sa), tk = reduce(sk);
+                // per-token inputs of the recurrence, each formed in a lane
+                // holding that token (padded tokens of a ragged chunk are
+                // identities: a = 1, u = 0, omega = 0)
+                const bool okl = mine_i < nv;
+                const float rl = sm.rr[X % NRING][mine_i], wl = sm.wr[X % NRING][mine_i];
+                const float al = okl ? ta * inv_dk : 1.f;
+                const float ul = okl ? mu * tk * rcp((float)DK * rl) : 0.f;
+                const float wo = okl ? wl : 0.f;
+                // serial recurrence on wave-uniform values
+                float bhv[C];
 #pragma unroll
-                    for (int j = 0; j < hs; ++j) {
-                        const float lo_a = sa[j], hi_a = sa[j + hs];
-                        const float lo_k = sk[j], hi_k = sk[j + hs];
-                        const float ra = __shfl_xor(up ? lo_a : hi_a, m);
-                        const float rk = __shfl_xor(up ? lo_k : hi_k, m);
-                        sa[j] = (up ? hi_a : lo_a) + ra;
-                        sk[j] = (up ? hi_k : lo_k) + rk;
+                for (int t = 0; t < C; ++t) {
+                    const float at = bcast(al, tok_lane[t]);
+                    const float ut = bcast(ul, tok_lane[t]);
+                    const float wt = bcast(wo, tok_lane[t]);
+                    const float dprev = dd;
+                    nn = fmaf(at, nn, wt * dd);
+                    dd = fmaf(ut, nn, dd);
+                    bhv[t] = nn * rcp(dprev);
+                    if ((t & 3) == 3) {
+                        // exact power-of-two rescale of both coordinates
+                        const int e = __builtin_amdgcn_frexp_expf(dd);
+                        nn = __builtin_ldexpf(nn, -e);
+                        dd = __builtin_ldexpf(dd, -e);
                     }
-                };
-                halve(std::integral_constant<int, 8>{});
-                halve(std::integral_constant<int, 4>{});
-                halve(std::integral_constant<int, 2>{});
-                halve(std::integral_constant<int, 1>{});
-                float ta = sa[0], tk = sk[0];
-                ta += __shfl_xor(ta, 1);
-                tk += __shfl_xor(tk, 1);
-                ta += __shfl_xor(ta, 2);
-                tk += __shfl_xor(tk, 2);
-                // scalar recurrence over the chunk (uniform over the wave);
-                // padded tokens (alpha = 1, k = 0) get a = 1, |k|^2 = 0 below
-                const float* rr = sm.rr[X % NRING];
-                const float* wr = sm.wr[X % NRING];
-                float bhv[C], rv[C], wv[C];
-#pragma unroll
-                for (int t = 0; t < C; ++t) {
-                    rv[t] = rr[t];
-                    wv[t] = wr[t];
-                }
-#pragma unroll
-                for (int t = 0; t < C; ++t) {
-                    const bool ok = t < nv;
-                    const float A2 = ok ? bcast(ta, 4 * t) : (float)DK;
-                    const float K2 = ok ? bcast(tk, 4 * t) : 0.f;
-                    const float rt = ok ? rv[t] : 1.f;
-                    const float wt = ok ? wv[t] : 0.f;
-                    const float bhat = A2 * (1.f / DK) * bvar + wt;
-                    const float dr = (float)DK * rt;
-                    bvar = bhat * dr * rcp(dr + mu * K2 * bhat);
-                    bhv[t] = bhat;
                 }
                 if (lane == 0) {
 #pragma unroll
@@ -810,6 +891,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             }
             lds_barrier();
         }
+        const float bvar = nn / dd;
         if (tile == 0 && lane == 0)
             a.var_T[bh] = bvar;
     }
