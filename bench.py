@@ -120,8 +120,10 @@ def cpu_baseline(w, inp, variant):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the defaults run long enough (about 0.1 s of launches) for the GPU clocks
+    # to settle before the timed region
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--variant", default=None, help="override: diag | iso")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -44,12 +44,15 @@
 //                  token of chunk c + 4 and runs the scalar variance
 //                  recurrence;
 //   builder waves  (lane = key channel) run the per-channel recurrence of
-//                  chunk c + 3 and write its bf16 operands Kb, Qb, Ktp and
-//                  G_C to LDS;
-//   factor waves   the first forms L', Aqk and T = M^-1 of chunk c + 2 (one
-//                  lane per column of T, forward substitution); the second
-//                  forms W = T Kb of chunk c + 1 on the matrix cores;
-//   memory waves   apply chunk c to their value columns (2 x 16 each).
+//                  chunk c + 3 and write its bf16 operands to LDS: Ktp and
+//                  G_C, plus Kb and Qb for Isotropic; for Diagonal an
+//                  elementwise wave forms Kb and Qb (two channels per lane);
+//   factor waves   the first forms L', Aqk and the diagonal 8 x 8 blocks of
+//                  T = M^-1 of chunk c + 2 (one lane per column, or per row
+//                  for the lower block); the second forms the off-diagonal
+//                  block, assembles T and forms W = T Kb of chunk c + 1 on
+//                  the matrix cores;
+//   memory waves   apply chunk c to their value columns (16 NB each).
 // Every buffer is indexed by chunk number modulo its lifetime, so no role
 // waits for another inside a step.
 #include "kdn_common.h"
@@ -130,14 +133,24 @@ __device__ __forceinline__ void mfma16(f32x4& d, const bf16x4& a, const bf16x4& 
 {
     d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, d, 0, 0, 0);
 }
+// acc += X^T Y for 16 x 16 fp32 matrices held in the accumulator layout
+// (lane (g, c) holds X[4 g + r][c], r = 0..3).  Step r of the four
+// 16x16x4 products takes k = 4 g + r: lane (g, c) supplies A[c][k] =
+// X[4 g + r][c] and B[k][c] = Y[4 g + r][c].
+__device__ __forceinline__ void mma_tn(f32x4& acc, const f32x4& X, const f32x4& Y)
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[r], Y[r], acc, 0, 0, 0);
+}
 __device__ __forceinline__ void mfma32(f32x4& d, const bf16x8& a, const bf16x8& b)
 {
     d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d, 0, 0, 0);
 }
 
-// Role layout of one workgroup.  Waves are dealt to the four SIMDs round
-// robin, so the order puts the two heaviest roles (builders, memory) on
-// different SIMDs and pairs the factor and loader waves with memory waves.
+// Wave roles of one workgroup.
+enum Role { R_MEM, R_BLD, R_ELT, R_FAC1, R_FAC2, R_LDR, R_ISO };
+
 template <int DK_, int NB_, int NMW_, bool ISO_>
 struct Cfg {
     static constexpr int DK = DK_;
@@ -145,12 +158,38 @@ struct Cfg {
     static constexpr int NMW = NMW_;  // memory waves
     static constexpr bool ISO = ISO_;
     static constexpr int DVT = 16 * NB * NMW;
-    static constexpr int NBW = DK / 64;  // builder waves, one lane per key channel
-    static constexpr int W_BLD = NMW;
-    static constexpr int W_FAC = NMW + NBW;  // factor, first wave (T); W_FAC + 1: W = T Kb
-    static constexpr int W_LDR = W_FAC + 2;
-    static constexpr int W_ISO = W_LDR + 1;
-    static constexpr int NWAVES = W_LDR + 1 + (ISO ? 1 : 0);
+    // builder waves, one lane per key channel.  Diagonal splits the builder
+    // work: these waves run the variance recurrence and form Ktp and G_C,
+    // one more wave (elementwise) forms Kb and Qb
+    static constexpr int NBW = DK / 64;
+    static constexpr bool SPLIT = !ISO;
+    static constexpr int NEW = SPLIT ? 1 : 0;
+    static constexpr int NWAVES = NMW + NBW + NEW + 3 + (ISO ? 1 : 0);
+    // Hardware wave w runs on SIMD w % 4; the layout pairs each heavy role
+    // (memory, builders, first factor) with a light one on its SIMD.
+    // Entry w: role * 8 + index within the role.
+    static constexpr int layout(int w)
+    {
+        if constexpr (DK == 128 && NMW == 2 && !ISO) {
+            constexpr int L[8] = {R_MEM * 8, R_MEM * 8 + 1, R_BLD * 8, R_BLD * 8 + 1,
+                                  R_FAC2 * 8, R_LDR * 8, R_FAC1 * 8, R_ELT * 8};
+            return L[w];
+        } else if constexpr (DK == 128 && NMW == 2 && ISO) {
+            constexpr int L[8] = {R_MEM * 8, R_MEM * 8 + 1, R_FAC1 * 8, R_ISO * 8,
+                                  R_FAC2 * 8, R_LDR * 8, R_BLD * 8, R_BLD * 8 + 1};
+            return L[w];
+        } else {
+            // memory, builders, elementwise, factor, factor, loader, isotropic
+            if (w < NMW)
+                return R_MEM * 8 + w;
+            if (w < NMW + NBW)
+                return R_BLD * 8 + (w - NMW);
+            if (w < NMW + NBW + NEW)
+                return R_ELT * 8;
+            const int k = w - (NMW + NBW + NEW);
+            return (k == 0 ? R_FAC1 : k == 1 ? R_FAC2 : k == 2 ? R_LDR : R_ISO) * 8;
+        }
+    }
     // pipeline leads (steps between a role's work on a chunk and the memory
     // waves applying it): builders 3, isotropic wave 4, raw copies LR (two
     // steps in flight before their first reader)
@@ -178,9 +217,14 @@ struct Smem {
         alignas(16) bf16 W[4 * CF::QS];
     };
     struct Tri {  // first factor wave -> second factor wave, memory
-        alignas(16) float Mt[C * 20];         // M^T (fp32), rows padded to 20
+        alignas(16) float Mt[C * 20];         // M^T (fp32): Mt[s][t] = M[t][s], rows padded to 20
+        alignas(16) float Mr[8 * 20];         // lower-right block of M, indices reversed:
+                                              //   Mr[k][j] = M[15 - k][15 - j]
         alignas(16) float dinv[C];            // 1 / (r_t + z_t)
-        alignas(16) bf16 Tt[C * C];           // T^T (bf16, rows of 32 bytes)
+        alignas(16) float dinvr[8];           // dinv[15 - k]
+        alignas(16) float Xs[C * 8];          // row c < 8: T[7 - j][c] (column c of T11,
+                                              // reversed); row c >= 8: T[c][8 + j] (T22 row)
+        alignas(16) bf16 T[C * C];            // T = M^-1 (bf16, row-major)
         alignas(16) bf16 Aqk[C * CF::LDF];    // Aqk (bf16)
     };
     struct Raw {  // raw inputs of one chunk, rows of tokens as in global memory
@@ -238,7 +282,9 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63;
+    const int slot = CF::layout(threadIdx.x >> 6);
+    const int role = slot >> 3, ridx = slot & 7;
     const int g4 = lane >> 4, c16 = lane & 15;
 
     // XCD-aware tile order: blocks are dispatched round-robin over the 8
@@ -260,11 +306,11 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
     auto row_v = [&](int t) { return (((size_t)b * T + t) * H + h) * dv; };
     auto row_s = [&](int t) { return ((size_t)b * T + t) * H + h; };
 
-    if (wave < NMW) {
+    if (role == R_MEM) {
         // ===================== memory waves =====================
         // block nb of wave w covers value columns jl = 16 (NB w + nb) + c16;
         // Sacc[nb][n] holds S[16 n + 4 g4 + r][j0 + jl]
-        const int w = wave;
+        const int w = ridx;
         f32x4 Sacc[NB][DK / 16];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -286,7 +332,6 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         const int tr_lane = quad_tr_lane<QS>(lane);   // W, Qb transpose reads
         const int kt_lane = g4 * QS + c16 * 4;        // Ktp^T rows: quad g4, channel c16
         const int fr_lane = c16 * LDF + 4 * g4;       // Aqk rows
-        const int tt_lane = (4 * g4 + ((lane >> 2) & 3)) * C + 4 * (lane & 3);  // T^T transpose reads
         int v_lane[NB];                               // v tile transpose reads
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -315,7 +360,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 wf[m] = quad_frag32(wT, m);
                 qf[m] = quad_frag32(qT, m);
             }
-            const bf16x4 tfr = ds_read_tr(tri.Tt + tt_lane);  // T[t][4 g4 + e]
+            const bf16x4 tfr = *reinterpret_cast<const bf16x4*>(tri.T + c16 * C + 4 * g4);  // T[c16][4 g4 + e]
             const bf16x4 afr = *reinterpret_cast<const bf16x4*>(tri.Aqk + fr_lane);
             bf16x4 vfr[NB];
 #pragma unroll
@@ -378,14 +423,18 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 }
             }
         };
-        for (int c = -LR; c < nchunks; ++c) {
-            if (c >= 0) {
-                if (n_valid(c) == C)
-                    apply(std::integral_constant<bool, true>{}, c);
-                else
-                    apply(std::integral_constant<bool, false>{}, c);
-                orow += o_step;
-            }
+        // pipeline fill, the full chunks, then at most one ragged chunk (one
+        // barrier per step as in every role; separate loops keep S in place)
+        for (int c = -LR; c < 0; ++c)
+            lds_barrier();
+        const int nfull = T / C;
+        for (int c = 0; c < nfull; ++c) {
+            apply(std::integral_constant<bool, true>{}, c);
+            orow += o_step;
+            lds_barrier();
+        }
+        if (nfull < nchunks) {
+            apply(std::integral_constant<bool, false>{}, nfull);
             lds_barrier();
         }
 #pragma unroll
@@ -397,9 +446,9 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 for (int r = 0; r < 4; ++r)
                     ST[(size_t)(16 * n + 4 * g4 + r) * dv] = Sacc[nb][n][r];
         }
-    } else if (wave < CF::W_FAC) {
+    } else if (role == R_BLD) {
         // ================ builder waves: lane = key channel ================
-        const int i = (wave - CF::W_BLD) * 64 + lane;
+        const int i = ridx * 64 + lane;
         // Diagonal: homogeneous variance [n; d];  Isotropic: no state here
         float vn = (!ISO && a.var0) ? a.var0[(size_t)bh * DK + i] : 1.f;
         float vd = 1.f;
@@ -422,7 +471,8 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 if constexpr (!ISO)
                     om[t] = raw.omega[t * DK + i];
                 kf[t] = static_cast<float>(raw.k[t * DK + i]);
-                qf[t] = static_cast<float>(raw.q[t * DK + i]);
+                if constexpr (!CF::SPLIT)
+                    qf[t] = static_cast<float>(raw.q[t * DK + i]);
             }
             if constexpr (!FULL) {
 #pragma unroll
@@ -432,23 +482,27 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     if constexpr (!ISO)
                         om[t] = ok ? om[t] : 0.f;
                     kf[t] = ok ? kf[t] : 0.f;
-                    qf[t] = ok ? qf[t] : 0.f;
+                    if constexpr (!CF::SPLIT)
+                        qf[t] = ok ? qf[t] : 0.f;
                 }
             }
             float kb[C], qb[C], kt[C];
             float G = 1.f;
             if constexpr (!ISO) {
+                // with split builders Kb and Qb come from the elementwise wave
 #pragma unroll
                 for (int t = 0; t < C; ++t) {
-                    const float u = kf[t] * bcast(tok, t) * kf[t];  // mu k^2 / r
                     const float n1 = fmaf(om[t], vd, (al[t] * al[t]) * vn);  // p^_t = n1 / vd
+                    const float kn = kf[t] * n1;
                     G *= al[t];
                     const float re = rcp(vd * G);
-                    kt[t] = (kf[t] * n1) * re;        // p^_t k_t / G_t
-                    vd = fmaf(u, n1, vd);             // d_t = d_{t-1} + u_t n_t
+                    kt[t] = kn * re;                             // p^_t k_t / G_t
+                    vd = fmaf(kf[t] * bcast(tok, t), kn, vd);    // d_t = d_{t-1} + (mu k^2 / r) n_t
                     vn = n1;
-                    kb[t] = kf[t] * G;
-                    qb[t] = qf[t] * G;
+                    if constexpr (!CF::SPLIT) {
+                        kb[t] = kf[t] * G;
+                        qb[t] = qf[t] * G;
+                    }
                     if ((t & 3) == 3) {
                         // rescale [n; d] by 2^-e(d): exact, keeps n / d
                         const int ex = __builtin_amdgcn_frexp_expf(vd);
@@ -476,12 +530,14 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
 #pragma unroll
             for (int tq = 0; tq < 4; ++tq) {
                 const int o = tq * QS + i * 4;
-                *reinterpret_cast<bf16x4*>(op.Kb + o) =
-                    bf16x4{static_cast<bf16>(kb[4 * tq]), static_cast<bf16>(kb[4 * tq + 1]),
-                           static_cast<bf16>(kb[4 * tq + 2]), static_cast<bf16>(kb[4 * tq + 3])};
-                *reinterpret_cast<bf16x4*>(op.Qb + o) =
-                    bf16x4{static_cast<bf16>(qb[4 * tq]), static_cast<bf16>(qb[4 * tq + 1]),
-                           static_cast<bf16>(qb[4 * tq + 2]), static_cast<bf16>(qb[4 * tq + 3])};
+                if constexpr (!CF::SPLIT) {
+                    *reinterpret_cast<bf16x4*>(op.Kb + o) =
+                        bf16x4{static_cast<bf16>(kb[4 * tq]), static_cast<bf16>(kb[4 * tq + 1]),
+                               static_cast<bf16>(kb[4 * tq + 2]), static_cast<bf16>(kb[4 * tq + 3])};
+                    *reinterpret_cast<bf16x4*>(op.Qb + o) =
+                        bf16x4{static_cast<bf16>(qb[4 * tq]), static_cast<bf16>(qb[4 * tq + 1]),
+                               static_cast<bf16>(qb[4 * tq + 2]), static_cast<bf16>(qb[4 * tq + 3])};
+                }
                 *reinterpret_cast<bf16x4*>(op.Ktp + o) =
                     bf16x4{static_cast<bf16>(kt[4 * tq]), static_cast<bf16>(kt[4 * tq + 1]),
                            static_cast<bf16>(kt[4 * tq + 2]), static_cast<bf16>(kt[4 * tq + 3])};
@@ -502,7 +558,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             if (tile == 0)
                 a.var_T[(size_t)bh * DK + i] = vn / vd;
         }
-    } else if (wave == CF::W_FAC) {
+    } else if (role == R_FAC1) {
         // ============ first factor wave: L', Aqk and T of chunk c + 2 ============
         const int tr_lane = quad_tr_lane<QS>(lane);
         for (int c = -LR; c < nchunks; ++c) {
@@ -526,13 +582,23 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     mfma32(accL, kbf[m], ktf[m]);
                     mfma32(accQ, ktf[m], qbf[m]);
                 }
-                // M^T[s][t] = L'[t][s]   (lane holds L'[4 g4 + r][c16])
+                // M^T[s][t] = L'[t][s]   (lane holds L'[4 g4 + r][c16]); the
+                // second factor wave reads its lower-left block
                 *reinterpret_cast<f32x4*>(&tr.Mt[c16 * 20 + 4 * g4]) = accL;
+                // lower-right block with both indices reversed
+                if (g4 >= 2 && c16 >= 8) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        tr.Mr[(15 - 4 * g4 - r) * 20 + (15 - c16)] = accL[r];
+                }
                 if ((c16 >> 2) == g4) {
                     const int rs = c16 & 3;
                     const float z = rs == 0 ? accL[0] : rs == 1 ? accL[1] : rs == 2 ? accL[2] : accL[3];
                     const float rt = c16 < nv ? rr[c16] : 1.f;
-                    tr.dinv[c16] = rcp(rt + z);
+                    const float dv = rcp(rt + z);
+                    tr.dinv[c16] = dv;
+                    if (c16 >= 8)
+                        tr.dinvr[15 - c16] = dv;
                 }
                 // Aqk[t][u] = Aqk^T[u][t] for u <= t, else 0
                 {
@@ -543,65 +609,95 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     *reinterpret_cast<bf16x4*>(&tr.Aqk[c16 * LDF + 4 * g4]) = cvt4(aq);
                 }
                 lds_wave_sync();
-                // T = M^-1, column c16 per lane (every lane group computes the
-                // same columns): M x = e_c by forward substitution, with the
-                // sub-diagonal part of column s of M read as row s of M^T
-                float d[C];
+                // Diagonal blocks of T = M^-1, one 8-step substitution per lane
+                // (the four lane groups repeat it):
+                //   c16 < 8:  column c16 of T11 = M11^-1, forward substitution
+                //             with the rows of M11^T;
+                //   c16 >= 8: row c16 - 8 of T22 = column of (M22^T)^-1, a back
+                //             substitution, run forward in reversed indices
+                //             (coefficients Mr, pivots dinvr).
+                // Both read as x[k] = acc[k] d[k];  acc[j] -= cof[k][j] x[k], j > k.
+                const int blk = c16 >> 3, j0 = c16 & 7;
+                const float* cof = blk ? tr.Mr : tr.Mt;
+                const float* dp = blk ? tr.dinvr : tr.dinv;
+                float d[8];
+                {
+                    const f32x4 d0 = *reinterpret_cast<const f32x4*>(dp);
+                    const f32x4 d1 = *reinterpret_cast<const f32x4*>(dp + 4);
 #pragma unroll
-                for (int q4 = 0; q4 < C / 4; ++q4) {
-                    const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&tr.dinv[4 * q4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        d[4 * q4 + e] = dv4[e];
+                    for (int e = 0; e < 4; ++e) {
+                        d[e] = d0[e];
+                        d[4 + e] = d1[e];
+                    }
                 }
-                float x[C], acc[C];
+                const int e0 = blk ? 7 - j0 : j0;
+                float acc[8], x[8];
 #pragma unroll
-                for (int t = 0; t < C; ++t)
-                    acc[t] = (t == c16) ? 1.f : 0.f;
+                for (int j = 0; j < 8; ++j)
+                    acc[j] = (j == e0) ? 1.f : 0.f;
 #pragma unroll
-                for (int s = 0; s < C; ++s) {
-                    x[s] = acc[s] * d[s];
+                for (int k = 0; k < 8; ++k) {
+                    x[k] = acc[k] * d[k];
 #pragma unroll
-                    for (int q4 = (s + 1) >> 2; q4 < C / 4; ++q4) {
-                        const f32x4 mrow = *reinterpret_cast<const f32x4*>(&tr.Mt[s * 20 + 4 * q4]);
+                    for (int q4 = (k + 1) >> 2; q4 < 2; ++q4) {
+                        const f32x4 row = *reinterpret_cast<const f32x4*>(cof + k * 20 + 4 * q4);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const int t = 4 * q4 + e;
-                            if (t > s)
-                                acc[t] = fmaf(-mrow[e], x[s], acc[t]);
+                            const int j = 4 * q4 + e;
+                            if (j > k)
+                                acc[j] = fmaf(-row[e], x[k], acc[j]);
                         }
                     }
                 }
-                // row c16 of T^T = column c16 of T
+                // row c16 of Xs: x reversed (T11: T[7 - j][c16]; T22: x[7 - j] = T[c16][8 + j])
                 if (g4 == 0) {
-                    bf16x8 lo, hi;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        lo[e] = static_cast<bf16>(x[e]);
-                        hi[e] = static_cast<bf16>(x[8 + e]);
-                    }
-                    *reinterpret_cast<bf16x8*>(&tr.Tt[c16 * C]) = lo;
-                    *reinterpret_cast<bf16x8*>(&tr.Tt[c16 * C + 8]) = hi;
+                    *reinterpret_cast<f32x4*>(&tr.Xs[c16 * 8]) = f32x4{x[7], x[6], x[5], x[4]};
+                    *reinterpret_cast<f32x4*>(&tr.Xs[c16 * 8 + 4]) = f32x4{x[3], x[2], x[1], x[0]};
                 }
             }
             lds_barrier();
         }
-    } else if (wave == CF::W_FAC + 1) {
-        // ============ second factor wave: W = T Kb of chunk c + 1 ============
-        // A[t][u] = T by a transpose read of T^T,  B[u][i] = Kb (quad segment
-        // u / 4 of channel i), 16 channels per product
-        const int tt_lane = (4 * g4 + ((lane >> 2) & 3)) * C + 4 * (lane & 3);
+    } else if (role == R_FAC2) {
+        // ======= second factor wave: T21, T and W = T Kb of chunk c + 1 =======
+        // T21 = -T22 M21 T11 on the fp32 matrix cores, both products in the
+        // X^T Y form of mma_tn:
+        //   Q = M21^T T22^T,   R = T11^T (E - Q)  with E the identity on the
+        //   upper-left block;  rows 0..7 of R hold T^T: R[i][j] = T[j][i]
+        //   (T11 for j < 8, T21 for j >= 8).
+        // A-operand fragment of T (lane (g, c): T[c][4 g + e]): R for g < 2,
+        // the T22 row for g >= 2 (zero for c < 8).
+        const bool v11 = c16 < 8 && g4 < 2, v22 = c16 >= 8 && g4 >= 2;
+        const bool v21 = c16 < 8 && g4 >= 2;
+        const int xs_off = c16 * 8 + (c16 < 8 ? 4 - 4 * (g4 & 1) : 4 * (g4 & 1));
         for (int c = -LR; c < nchunks; ++c) {
             const int F = c + 1;
             if (F >= 0 && F < nchunks) {
-                const auto& tr = sm.tri[F % 3];
+                auto& tr = sm.tri[F % 3];
                 const auto& op = sm.op[F & (NOPS - 1)];
                 auto& fc = sm.fac[F & 1];
-                const bf16x4 ta = ds_read_tr(tr.Tt + tt_lane);
+                const f32x4 mt = *reinterpret_cast<const f32x4*>(&tr.Mt[c16 * 20 + 4 * g4]);
+                const f32x4 xv = *reinterpret_cast<const f32x4*>(&tr.Xs[xs_off]);
                 bf16x4 kbq[DK / 16];
 #pragma unroll
                 for (int n = 0; n < DK / 16; ++n)
                     kbq[n] = *reinterpret_cast<const bf16x4*>(op.Kb + g4 * QS + (16 * n + c16) * 4);
+                f32x4 m21, t22t, t11;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    m21[r] = v21 ? mt[r] : 0.f;       // M[4 g + r][c], block (2, 1)
+                    t22t[r] = v22 ? xv[r] : 0.f;      // T22^T[4 g + r - 8][c - 8]
+                    t11[r] = v11 ? xv[3 - r] : 0.f;   // T11[4 g + r][c]
+                }
+                f32x4 q = zero4();
+                mma_tn(q, m21, t22t);
+                f32x4 y;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    y[r] = (4 * g4 + r == c16 && c16 < 8) ? 1.f - q[r] : -q[r];
+                f32x4 rt = zero4();
+                mma_tn(rt, t11, y);
+                const bf16x4 ta = cvt4(g4 < 2 ? rt : t22t);
+                *reinterpret_cast<bf16x4*>(&tr.T[c16 * C + 4 * g4]) = ta;
 #pragma unroll
                 for (int n = 0; n < DK / 16; ++n) {
                     f32x4 accW = zero4();
@@ -612,7 +708,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             }
             lds_barrier();
         }
-    } else if (wave == CF::W_LDR) {
+    } else if (role == R_LDR) {
         // ===================== loader wave =====================
         // direct copies into LDS: raw inputs of chunk c + LR, v of chunk c + 2
         constexpr int VE = 8;                               // bf16 per 16 bytes
@@ -724,6 +820,87 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             else
                 vm_wait<0>();
             lds_barrier();
+        }
+    } else if (role == R_ELT) {
+        // ======= elementwise wave (Diagonal): Kb = k G, Qb = q G of chunk c + 3 =======
+        // lane owns channels CPL lane .. + CPL - 1; G_t = prod_{s <= t} alpha_s
+        if constexpr (CF::SPLIT) {
+            constexpr int CPL = DK / 64;
+            static_assert(CPL == 1 || CPL == 2, "channels per lane");
+            auto build = [&](auto full_tag, int X) {
+                constexpr bool FULL = decltype(full_tag)::value;
+                const int nv = FULL ? C : n_valid(X);
+                const auto& raw = sm.raw[X % NRAW];
+                auto& op = sm.op[X & (NOPS - 1)];
+                float al[CPL][C], kf[CPL][C], qf[CPL][C];
+                if constexpr (CPL == 2) {
+                    float2 a2[C];
+                    uint32_t kk[C], qq[C];
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        a2[t] = *reinterpret_cast<const float2*>(&raw.alpha[t * DK + 2 * lane]);
+                        kk[t] = *reinterpret_cast<const uint32_t*>(&raw.k[t * DK + 2 * lane]);
+                        qq[t] = *reinterpret_cast<const uint32_t*>(&raw.q[t * DK + 2 * lane]);
+                    }
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        al[0][t] = a2[t].x;
+                        al[1][t] = a2[t].y;
+                        kf[0][t] = __uint_as_float(kk[t] << 16);
+                        kf[1][t] = __uint_as_float(kk[t] & 0xffff0000u);
+                        qf[0][t] = __uint_as_float(qq[t] << 16);
+                        qf[1][t] = __uint_as_float(qq[t] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        al[0][t] = raw.alpha[t * DK + lane];
+                        kf[0][t] = static_cast<float>(raw.k[t * DK + lane]);
+                        qf[0][t] = static_cast<float>(raw.q[t * DK + lane]);
+                    }
+                }
+                bf16 kb[CPL][C], qb[CPL][C];
+#pragma unroll
+                for (int e = 0; e < CPL; ++e) {
+                    float G = 1.f;
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        const bool ok = FULL || t < nv;  // padded tokens: alpha = 1, k = q = 0
+                        G *= ok ? al[e][t] : 1.f;
+                        kb[e][t] = static_cast<bf16>(ok ? kf[e][t] * G : 0.f);
+                        qb[e][t] = static_cast<bf16>(ok ? qf[e][t] * G : 0.f);
+                    }
+                }
+                // token-quad writes: the lane's channels are adjacent, so the
+                // four tokens of each sit in one 8 * CPL byte run
+#pragma unroll
+                for (int tq = 0; tq < 4; ++tq) {
+                    const int o = tq * QS + CPL * lane * 4;
+                    if constexpr (CPL == 2) {
+                        *reinterpret_cast<bf16x8*>(op.Kb + o) =
+                            bf16x8{kb[0][4 * tq], kb[0][4 * tq + 1], kb[0][4 * tq + 2], kb[0][4 * tq + 3],
+                                   kb[1][4 * tq], kb[1][4 * tq + 1], kb[1][4 * tq + 2], kb[1][4 * tq + 3]};
+                        *reinterpret_cast<bf16x8*>(op.Qb + o) =
+                            bf16x8{qb[0][4 * tq], qb[0][4 * tq + 1], qb[0][4 * tq + 2], qb[0][4 * tq + 3],
+                                   qb[1][4 * tq], qb[1][4 * tq + 1], qb[1][4 * tq + 2], qb[1][4 * tq + 3]};
+                    } else {
+                        *reinterpret_cast<bf16x4*>(op.Kb + o) =
+                            bf16x4{kb[0][4 * tq], kb[0][4 * tq + 1], kb[0][4 * tq + 2], kb[0][4 * tq + 3]};
+                        *reinterpret_cast<bf16x4*>(op.Qb + o) =
+                            bf16x4{qb[0][4 * tq], qb[0][4 * tq + 1], qb[0][4 * tq + 2], qb[0][4 * tq + 3]};
+                    }
+                }
+            };
+            for (int c = -LR; c < nchunks; ++c) {
+                const int X = c + LB;
+                if (X >= 0 && X < nchunks) {
+                    if (n_valid(X) == C)
+                        build(std::integral_constant<bool, true>{}, X);
+                    else
+                        build(std::integral_constant<bool, false>{}, X);
+                }
+                lds_barrier();
+            }
         }
     } else if constexpr (ISO) {
         // ============ isotropic wave: DK / 64 channels per lane ============
