@@ -86,6 +86,18 @@ def traffic_for(kernel: str, key: str):
     return ent.get("bytes_per_launch")
 
 
+def copy_calibration(dev):
+    """Three plain 1 GiB device-to-device copies: a kernel of known traffic
+    (1 GiB read, 1 GiB written) that scales the HBM traffic counters."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("[bench] copy calibration: 3 x 1 GiB device copies done", file=sys.stderr, flush=True)
+
+
 def cpu_baseline(w, inp, variant):
     """The fp64 oracle, untuned, on the same seeded inputs the GPU consumed.
     The sample is the whole workload (every batch row, head and token) when
@@ -199,13 +211,7 @@ def main():
           file=sys.stderr, flush=True)
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print("[bench] copy calibration: 3 x 1 GiB device copies done", file=sys.stderr,
-              flush=True)
+        copy_calibration(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -273,6 +279,8 @@ def bench_decode(args, w):
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
     ms_launch = ms_total / nsteps
+    if args.copy_calibration:
+        copy_calibration(dev)
     alg = alg_bytes_step(variant, w.B, w.H, w.dk, w.dv, 2)
     achieved = alg / (ms_launch / 1e3) / 1e9
     line = {
