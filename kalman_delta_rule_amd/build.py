@@ -15,6 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkdn.so")
 SOURCES = ["kdn_api.cpp", "kdn_walk.hip", "kdn_chunk.hip", "kdn_step.hip", "kdn_gain.hip"]
+# sources whose kernels use the matrix cores (checked by isa_check)
+MFMA_SOURCES = ["kdn_walk.hip", "kdn_chunk.hip"]
 ARCH = os.environ.get("KDN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -46,8 +48,22 @@ def build_library(verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libkdn.so")
+    probs = run_isa_check(verbose=verbose)
+    if probs:
+        sys.stderr.write("\n".join(probs) + "\n")
+        os.unlink(tmp)
+        raise RuntimeError("matrix-core dependency check failed (see isa_check.py)")
     os.replace(tmp, LIB)
     return LIB
+
+
+def run_isa_check(verbose: bool = False):
+    """Scan the device assembly for matrix-core dependencies the compiler
+    does not pad (isa_check.py); returns the list of problems."""
+    from kalman_delta_rule_amd import isa_check
+    return isa_check.check_sources([os.path.join(CSRC, s) for s in MFMA_SOURCES],
+                                   [os.path.join(ROOT, "include"), CSRC], hipcc(),
+                                   HIPCC_FLAGS, verbose=verbose)
 
 
 if __name__ == "__main__":

@@ -404,12 +404,17 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 }
             }
             bf16x4 dfr[NB];
+            // Aqk^T fragment as a K = 32 operand whose upper 16 k are zero
+            const bf16x8 afr32 = cat8(afr, bf16x4{});
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 // Delta' = U - W S
                 dfr[nb] = cvt4(accU[nb] - accX[nb]);
-                // O^T += Delta'^T Aqk^T
-                mfma16(accO[nb], dfr[nb], afr);
+                // O^T += Delta'^T Aqk^T, issued as a zero-padded K = 32 product:
+                // the accumulator comes from 16x16x32 products, and on gfx950 a
+                // 16x16x16 product reading it as its accumulator needs more
+                // independent instructions in between than are inserted for it
+                mfma32(accO[nb], cat8(dfr[nb], bf16x4{}), afr32);
                 if (FULL || c16 < nv)
                     *reinterpret_cast<bf16x4*>(orow + 16 * nb) = cvt4(accO[nb]);
             }

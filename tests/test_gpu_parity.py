@@ -90,6 +90,30 @@ def test_nonzero_initial_state_and_mu(ora, variant, io):
         _full_compare(ora, variant, io, inp, mu=mu, S0=S0, var0=var0, tag="mu=%g" % mu)
 
 
+def _alpha_regime(regime, shape, seed):
+    """Decay gates for the decay-bookkeeping cases (all satisfy the documented
+    precondition: the alpha product over one 16-token chunk stays above 1e-30)."""
+    rng = np.random.default_rng(seed)
+    if regime == "one":          # no decay at all
+        return np.ones(shape, np.float32)
+    if regime == "strong":       # about 1e-9 per chunk: the cumulative decay restarts every chunk
+        return (1.0 / (1.0 + np.exp(-rng.normal(-1.0, 0.5, shape)))).astype(np.float32)
+    # mixed: half the channels near 1, half decaying fast; restarts at irregular chunks
+    B, T, H, dk = shape
+    mean = np.where(np.arange(dk) % 2 == 0, 4.0, 0.0).astype(np.float32)
+    return (1.0 / (1.0 + np.exp(-(mean + rng.normal(0.0, 0.7, shape))))).astype(np.float32)
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+@pytest.mark.parametrize("regime", ["one", "strong", "mixed"])
+def test_decay_regimes(ora, variant, regime):
+    B, T, H, dk, dv = 1, 300, 2, 128, 128
+    w = inputs.Workload("t", variant, "bf16", B, H, T, dk, dv, seed=71)
+    inp = inputs.make_fwd_inputs(w)
+    inp["alpha"] = _alpha_regime(regime, (B, T, H, dk), seed=72)
+    _full_compare(ora, variant, "bf16", inp, tag=regime)
+
+
 def test_config0_diag_f32(ora):
     w = inputs.workload(0)
     _full_compare(ora, "diag", "f32", inputs.make_fwd_inputs(w), tag=w.name)
