@@ -32,9 +32,11 @@
 // ratio n / d bit-identical.  Ktp = k n_t / (d_{t-1} G_t) takes the one
 // reciprocal per token and channel, off the recurrence's dependency chain.
 //
-// The memory update uses the compact-WY pair of the notes' Appendix D
-// summary, W = T Kb and U = T V:  Delta' = U - W S.  U does not depend on S,
-// so only W S sits on the chunk-to-chunk dependency chain of S.
+// The memory update is the compact-WY correction of the notes' Appendix D
+// summary, Delta' = T (V - Kb S), formed in that order: Kb S costs the same
+// matrix-core work as W S with W = T Kb, and then no W has to be formed or
+// staged.  V - Kb S is a lane-local subtraction, because the accumulator
+// layout of Kb S is the operand layout of V.
 //
 // Workgroup roles, one LDS barrier per step.  In step c:
 //   loader wave    copies the raw inputs (alpha, omega, k, q, r) of chunk
@@ -50,8 +52,8 @@
 //   factor waves   the first forms L', Aqk and the diagonal 8 x 8 blocks of
 //                  T = M^-1 of chunk c + 2 (one lane per column, or per row
 //                  for the lower block); the second forms the off-diagonal
-//                  block, assembles T and forms W = T Kb of chunk c + 1 on
-//                  the matrix cores;
+//                  block on the matrix cores and assembles T of chunk
+//                  c + 1;
 //   memory waves   apply chunk c to their value columns (16 NB each).
 // Every buffer is indexed by chunk number modulo its lifetime, so no role
 // waits for another inside a step.
@@ -213,9 +215,6 @@ struct Smem {
         alignas(16) bf16 Ktp[4 * CF::QS];
         alignas(16) float gC[DK];
     };
-    struct Fac {  // second factor wave -> memory
-        alignas(16) bf16 W[4 * CF::QS];
-    };
     struct Tri {  // first factor wave -> second factor wave, memory
         alignas(16) float Mt[C * 20];         // M^T (fp32): Mt[s][t] = M[t][s], rows padded to 20
         alignas(16) float Mr[8 * 20];         // lower-right block of M, indices reversed:
@@ -236,7 +235,6 @@ struct Smem {
     // the arrays the memory waves read every step come first, so that their
     // addresses stay within reach of the LDS instructions' immediate offsets
     Ops op[CF::NOPS];
-    Fac fac[2];
     Tri tri[3];
     alignas(16) bf16 v[3][C * CF::DVT];  // rows of DVT; 16-byte block b of row t at b ^ (t & 7)
     alignas(16) float rr[NRING][C];  // r_t
@@ -348,16 +346,15 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             constexpr bool FULL = decltype(full_tag)::value;
             const int nv = FULL ? C : n_valid(c);
             const auto& op = sm.op[c & (NOPS - 1)];
-            const auto& fc = sm.fac[c & 1];
             const auto& tri = sm.tri[c % 3];
             const bf16* V = sm.v[c % 3];
-            const bf16* wT = fc.W + tr_lane;
+            const bf16* kT = op.Kb + tr_lane;
             const bf16* qT = op.Qb + tr_lane;
             // every LDS operand of the chunk is requested before the first use
-            bf16x8 wf[DK / 32], qf[DK / 32];
+            bf16x8 kf[DK / 32], qf[DK / 32];
 #pragma unroll
             for (int m = 0; m < DK / 32; ++m) {
-                wf[m] = quad_frag32(wT, m);
+                kf[m] = quad_frag32(kT, m);
                 qf[m] = quad_frag32(qT, m);
             }
             const bf16x4 tfr = *reinterpret_cast<const bf16x4*>(tri.T + c16 * C + 4 * g4);  // T[c16][4 g4 + e]
@@ -380,18 +377,11 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 ktf[n] = *reinterpret_cast<const bf16x4*>(op.Ktp + kt_lane + 64 * n);
                 gcf[n] = *reinterpret_cast<const f32x4*>(&op.gC[16 * n + 4 * g4]);
             }
-            // U = T V (off the S chain)
-            f32x4 accU[NB];
+            // front:  Y = Kb S  ([t][j]),   O^T = S^T Qb^T  ([j][t])
+            f32x4 accY[NB], accO[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                accU[nb] = zero4();
-                mfma16(accU[nb], tfr, vfr[nb]);
-            }
-            // front:  X = W S  ([t][j]),   O^T = S^T Qb^T  ([j][t])
-            f32x4 accX[NB], accO[NB];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                accX[nb] = zero4();
+                accY[nb] = zero4();
                 accO[nb] = zero4();
             }
 #pragma unroll
@@ -399,7 +389,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     const bf16x8 s = cat8(cvt4(Sacc[nb][2 * m]), cvt4(Sacc[nb][2 * m + 1]));
-                    mfma32(accX[nb], wf[m], s);
+                    mfma32(accY[nb], kf[m], s);
                     mfma32(accO[nb], s, qf[m]);
                 }
             }
@@ -408,8 +398,15 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             const bf16x8 afr32 = cat8(afr, bf16x4{});
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                // Delta' = U - W S
-                dfr[nb] = cvt4(accU[nb] - accX[nb]);
+                // Delta' = T (V - Y): lane (g, c) holds V[4 g + e][c] as an
+                // operand and Y[4 g + e][c] as an accumulator
+                f32x4 res;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    res[e] = static_cast<float>(vfr[nb][e]) - accY[nb][e];
+                f32x4 accD = zero4();
+                mfma16(accD, tfr, cvt4(res));
+                dfr[nb] = cvt4(accD);
                 // O^T += Delta'^T Aqk^T, issued as a zero-padded K = 32 product:
                 // the accumulator comes from 16x16x32 products, and on gfx950 a
                 // 16x16x16 product reading it as its accumulator needs more
@@ -663,7 +660,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             lds_barrier();
         }
     } else if (role == R_FAC2) {
-        // ======= second factor wave: T21, T and W = T Kb of chunk c + 1 =======
+        // ============ second factor wave: T21 and T of chunk c + 1 ============
         // T21 = -T22 M21 T11 on the fp32 matrix cores, both products in the
         // X^T Y form of mma_tn:
         //   Q = M21^T T22^T,   R = T11^T (E - Q)  with E the identity on the
@@ -678,14 +675,8 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             const int F = c + 1;
             if (F >= 0 && F < nchunks) {
                 auto& tr = sm.tri[F % 3];
-                const auto& op = sm.op[F & (NOPS - 1)];
-                auto& fc = sm.fac[F & 1];
                 const f32x4 mt = *reinterpret_cast<const f32x4*>(&tr.Mt[c16 * 20 + 4 * g4]);
                 const f32x4 xv = *reinterpret_cast<const f32x4*>(&tr.Xs[xs_off]);
-                bf16x4 kbq[DK / 16];
-#pragma unroll
-                for (int n = 0; n < DK / 16; ++n)
-                    kbq[n] = *reinterpret_cast<const bf16x4*>(op.Kb + g4 * QS + (16 * n + c16) * 4);
                 f32x4 m21, t22t, t11;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -701,15 +692,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     y[r] = (4 * g4 + r == c16 && c16 < 8) ? 1.f - q[r] : -q[r];
                 f32x4 rt = zero4();
                 mma_tn(rt, t11, y);
-                const bf16x4 ta = cvt4(g4 < 2 ? rt : t22t);
-                *reinterpret_cast<bf16x4*>(&tr.T[c16 * C + 4 * g4]) = ta;
-#pragma unroll
-                for (int n = 0; n < DK / 16; ++n) {
-                    f32x4 accW = zero4();
-                    mfma16(accW, ta, kbq[n]);
-                    // lane holds W[4 g4 + r][16 n + c16]: quad segment g4 of that channel
-                    *reinterpret_cast<bf16x4*>(fc.W + g4 * QS + (16 * n + c16) * 4) = cvt4(accW);
-                }
+                *reinterpret_cast<bf16x4*>(&tr.T[c16 * C + 4 * g4]) = cvt4(g4 < 2 ? rt : t22t);
             }
             lds_barrier();
         }
