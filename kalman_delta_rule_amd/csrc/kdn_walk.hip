@@ -39,14 +39,15 @@
 // layout of Kb S is the operand layout of V.
 //
 // Workgroup roles, one LDS barrier per step.  In step c:
-//   loader wave    copies the raw inputs (alpha, omega, k, q, r) of chunk
-//                  c + LR straight from global memory into LDS, and v of
-//                  chunk c + 2;
+//   loader wave    copies the raw inputs (alpha, k, q, r, and Isotropic
+//                  omega) of chunk c + LR straight from global memory into
+//                  LDS, and v of chunk c + 2;
 //   isotropic wave (Isotropic only) reduces alpha^2 and k^2 over channels per
 //                  token of chunk c + 4 and runs the scalar variance
 //                  recurrence;
 //   builder waves  (lane = key channel) run the per-channel recurrence of
-//                  chunk c + 3 and write its bf16 operands to LDS: Ktp and
+//                  chunk c + 3 (Diagonal omega prefetched from global memory
+//                  into registers) and write its bf16 operands to LDS: Ktp and
 //                  G_C, plus Kb and Qb for Isotropic; for Diagonal an
 //                  elementwise wave forms Kb and Qb (two channels per lane);
 //   factor waves   the first forms L', Aqk and the diagonal 8 x 8 blocks of
@@ -92,6 +93,33 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t ld
 __device__ __forceinline__ void lds_wave_sync()
 {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Buffer descriptor over a gate tensor from `base` to its end (`elems`
+// fp32 elements left, clamped to the 2^31 - 1 byte range of the record
+// count): loads through it are range-checked, and reads past the end of the
+// tensor (the rows after the last token of a ragged final chunk) return 0
+// instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gate_rsrc(const float* base, size_t elems)
+{
+    const size_t bytes = elems * sizeof(float);
+    const int nrec = bytes > 0x7fffffffull ? 0x7fffffff : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, nrec, 0x00020000);
+}
+__device__ __forceinline__ float gate_ld1(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0u, 0));
+}
+
+// Start a role that prefetches from global memory into a register ring with
+// nothing in flight.  The wait is free there, and it resets the compiler's
+// count of outstanding memory operations: the mix of operation kinds that
+// may still be pending from code before the role dispatch otherwise turns
+// every later wait in the loop into a full drain, including the prefetch
+// issued just before it.
+__device__ __forceinline__ void settle_counters()
+{
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 template <int N>
@@ -228,7 +256,6 @@ struct Smem {
     };
     struct Raw {  // raw inputs of one chunk, rows of tokens as in global memory
         alignas(16) float alpha[C * DK];
-        alignas(16) float omega[CF::ISO ? 4 : C * DK];
         alignas(16) bf16 k[C * DK];
         alignas(16) bf16 q[C * DK];
     };
@@ -303,6 +330,17 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
     auto row_k = [&](int t) { return (((size_t)b * T + t) * H + h) * DK; };
     auto row_v = [&](int t) { return (((size_t)b * T + t) * H + h) * dv; };
     auto row_s = [&](int t) { return ((size_t)b * T + t) * H + h; };
+    // Range-checked descriptor over gate tensor g from the first token of
+    // chunk x (clamped into the sequence) to the end of the tensor.  With no
+    // chunks at all it covers nothing: every load through it returns 0
+    // without an access.
+    const size_t gate_elems = (size_t)a.B * T * H * DK;
+    auto gate_desc = [&](const float* g, int x) {
+        if (nchunks == 0)
+            return gate_rsrc(g, 0);
+        const size_t cb = row_k(min(max(x, 0), nchunks - 1) * C);
+        return gate_rsrc(g + cb, gate_elems - cb);
+    };
 
     if (role == R_MEM) {
         // ===================== memory waves =====================
@@ -454,7 +492,25 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         // Diagonal: homogeneous variance [n; d];  Isotropic: no state here
         float vn = (!ISO && a.var0) ? a.var0[(size_t)bh * DK + i] : 1.f;
         float vd = 1.f;
-        auto build = [&](auto full_tag, int X) {
+        // Diagonal omega of this lane's channel comes straight from global
+        // memory, OPF chunks ahead, into a register ring of OPF + 1 slots
+        // (16 loads per step, so at most 16 (OPF + 1) - 1 = 63 outstanding)
+        constexpr int OPF = 3;
+        float rw[OPF + 1][ISO ? 1 : C];
+        uint32_t goff[C];
+#pragma unroll
+        for (int t = 0; t < C; ++t)
+            goff[t] = 4u * ((uint32_t)t * (uint32_t)(H * DK) + (uint32_t)i);
+        auto load_omega = [&](auto slot_tag, int X) {
+            if constexpr (!ISO) {
+                constexpr int S = decltype(slot_tag)::value;
+                const auto rom = gate_desc(a.omega, X);
+#pragma unroll
+                for (int t = 0; t < C; ++t)
+                    rw[S][t] = gate_ld1(rom, goff[t]);
+            }
+        };
+        auto build = [&](auto full_tag, int X, const float (&omr)[ISO ? 1 : C]) {
             constexpr bool FULL = decltype(full_tag)::value;
             const int nv = FULL ? C : n_valid(X);
             const auto& raw = sm.raw[X % NRAW];
@@ -471,7 +527,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             for (int t = 0; t < C; ++t) {
                 al[t] = raw.alpha[t * DK + i];
                 if constexpr (!ISO)
-                    om[t] = raw.omega[t * DK + i];
+                    om[t] = omr[t];
                 kf[t] = static_cast<float>(raw.k[t * DK + i]);
                 if constexpr (!CF::SPLIT)
                     qf[t] = static_cast<float>(raw.q[t * DK + i]);
@@ -546,16 +602,39 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             }
             op.gC[i] = G;
         };
-        for (int c = -LR; c < nchunks; ++c) {
+        settle_counters();
+        // slot of chunk X: (X - LB + LR) mod (OPF + 1); the first step
+        // consumes chunk LB - LR from slot 0, so prime chunks LB - LR ..
+        // LB - LR + OPF - 1 into slots 0 .. OPF - 1
+        static_assert(OPF == 3, "four-slot ring");
+        load_omega(std::integral_constant<int, 0>{}, LB - LR);
+        load_omega(std::integral_constant<int, 1>{}, LB - LR + 1);
+        load_omega(std::integral_constant<int, 2>{}, LB - LR + 2);
+        auto step = [&](auto slot_tag, int c) {
+            constexpr int S = decltype(slot_tag)::value;
             const int X = c + LB;
             if (X >= 0 && X < nchunks) {
                 if (n_valid(X) == C)
-                    build(std::integral_constant<bool, true>{}, X);
+                    build(std::integral_constant<bool, true>{}, X, rw[S]);
                 else
-                    build(std::integral_constant<bool, false>{}, X);
+                    build(std::integral_constant<bool, false>{}, X, rw[S]);
             }
+            load_omega(std::integral_constant<int, (S + OPF) % (OPF + 1)>{}, X + OPF);
             lds_barrier();
+        };
+        int c = -LR;
+        for (; c + 3 < nchunks; c += 4) {
+            step(std::integral_constant<int, 0>{}, c);
+            step(std::integral_constant<int, 1>{}, c + 1);
+            step(std::integral_constant<int, 2>{}, c + 2);
+            step(std::integral_constant<int, 3>{}, c + 3);
         }
+        if (c < nchunks)
+            step(std::integral_constant<int, 0>{}, c);
+        if (c + 1 < nchunks)
+            step(std::integral_constant<int, 1>{}, c + 1);
+        if (c + 2 < nchunks)
+            step(std::integral_constant<int, 2>{}, c + 2);
         if constexpr (!ISO) {
             if (tile == 0)
                 a.var_T[(size_t)bh * DK + i] = vn / vd;
@@ -708,7 +787,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         constexpr int RPI_V = 64 / LPR_V, NI_V = C / RPI_V;
         static_assert(LPR_A <= 64 && LPR_K <= 64 && LPR_V == 8 && NI_A >= 1 && NI_K >= 1,
                       "row / lane split");
-        constexpr int NSTG = NI_A * (ISO ? 1 : 2) + 2 * NI_K + 1 + (ISO ? 1 : 0);
+        constexpr int NSTG = NI_A + 2 * NI_K + 1 + (ISO ? 1 : 0);
         constexpr int NVI = NI_V;
         static_assert(NSTG + NVI <= 63, "outstanding copies within the vmcnt range");
         // LDS byte addresses of the copy targets (uniform)
@@ -760,8 +839,6 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     for (int j = 0; j < NI_A; ++j) {
                         const uint32_t o = FULL ? oa[j] : off_a(j, lim);
                         dma16(a.alpha + cb, o, la + j * RPI_A * DK * 4);
-                        if constexpr (!ISO)
-                            dma16(a.omega + cb, o, lds_addr(st.omega) + j * RPI_A * DK * 4);
                     }
 #pragma unroll
                     for (int j = 0; j < NI_K; ++j) {

@@ -55,6 +55,9 @@ SMALL = [
     (2, 64, 1, 128, 256),
     (1, 1, 2, 128, 128),
     (1, 63, 1, 64, 128),
+    # fewer chunks than the gate prefetch distance, and a ragged second chunk
+    (1, 17, 2, 128, 128),
+    (2, 33, 1, 128, 64),
 ]
 
 
