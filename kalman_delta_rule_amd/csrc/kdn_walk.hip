@@ -389,40 +389,44 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         bf16* orow = reinterpret_cast<bf16*>(a.o) + row_v(min(c16, max(T - 1, 0))) + j0 +
                      16 * NB * w + 4 * g4;
 
-        auto apply = [&](auto full_tag, int c) {
+        // operands of one chunk that were written two or more steps before
+        // the memory waves apply it; they are fetched during the previous
+        // step, after that step's own reads have landed, which takes them
+        // out of the read burst after each barrier
+        struct MemOps {
+            bf16x8 kf[DK / 32], qf[DK / 32];  // Kb, Qb transposed fragments
+            bf16x4 afr;                       // Aqk row
+        };
+        auto fetch = [&](int c, MemOps& m) {
+            const auto& op = sm.op[c & (NOPS - 1)];
+#pragma unroll
+            for (int mm = 0; mm < DK / 32; ++mm) {
+                m.kf[mm] = quad_frag32(op.Kb + tr_lane, mm);
+                m.qf[mm] = quad_frag32(op.Qb + tr_lane, mm);
+            }
+            m.afr = *reinterpret_cast<const bf16x4*>(sm.tri[c % 3].Aqk + fr_lane);
+        };
+
+        auto apply = [&](auto full_tag, int c, const MemOps& cur, MemOps& nxt) {
             constexpr bool FULL = decltype(full_tag)::value;
             const int nv = FULL ? C : n_valid(c);
             const auto& op = sm.op[c & (NOPS - 1)];
             const auto& tri = sm.tri[c % 3];
             const bf16* V = sm.v[c % 3];
-            const bf16* kT = op.Kb + tr_lane;
-            const bf16* qT = op.Qb + tr_lane;
-            // every LDS operand of the chunk is requested before the first use
-            bf16x8 kf[DK / 32], qf[DK / 32];
-#pragma unroll
-            for (int m = 0; m < DK / 32; ++m) {
-                kf[m] = quad_frag32(kT, m);
-                qf[m] = quad_frag32(qT, m);
-            }
+            // this step's first reads: T (formed in the previous step) and v
             const bf16x4 tfr = *reinterpret_cast<const bf16x4*>(tri.T + c16 * C + 4 * g4);  // T[c16][4 g4 + e]
-            const bf16x4 afr = *reinterpret_cast<const bf16x4*>(tri.Aqk + fr_lane);
             bf16x4 vfr[NB];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
+            for (int nb = 0; nb < NB; ++nb)
                 vfr[nb] = ds_read_tr(V + v_lane[nb]);
-                if constexpr (!FULL) {
+            reads_issued();
+            if constexpr (!FULL) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (4 * g4 + e >= nv)
                             vfr[nb][e] = static_cast<bf16>(0.f);
-                }
-            }
-            bf16x4 ktf[DK / 16];
-            f32x4 gcf[DK / 16];
-#pragma unroll
-            for (int n = 0; n < DK / 16; ++n) {
-                ktf[n] = *reinterpret_cast<const bf16x4*>(op.Ktp + kt_lane + 64 * n);
-                gcf[n] = *reinterpret_cast<const f32x4*>(&op.gC[16 * n + 4 * g4]);
             }
             // front:  Y = Kb S  ([t][j]),   O^T = S^T Qb^T  ([j][t])
             f32x4 accY[NB], accO[NB];
@@ -436,13 +440,26 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     const bf16x8 s = cat8(cvt4(Sacc[nb][2 * m]), cvt4(Sacc[nb][2 * m + 1]));
-                    mfma32(accY[nb], kf[m], s);
-                    mfma32(accO[nb], s, qf[m]);
+                    mfma32(accY[nb], cur.kf[m], s);
+                    mfma32(accO[nb], s, cur.qf[m]);
                 }
             }
+            // Ktp and G_C for the state update at the end of the step, then the
+            // next chunk's operands behind them
+            reads_issued();
+            bf16x4 ktf[DK / 16];
+            f32x4 gcf[DK / 16];
+#pragma unroll
+            for (int n = 0; n < DK / 16; ++n) {
+                ktf[n] = *reinterpret_cast<const bf16x4*>(op.Ktp + kt_lane + 64 * n);
+                gcf[n] = *reinterpret_cast<const f32x4*>(&op.gC[16 * n + 4 * g4]);
+            }
+            if (c + 1 < nchunks)
+                fetch(c + 1, nxt);
+            reads_issued();
             bf16x4 dfr[NB];
             // Aqk^T fragment as a K = 32 operand whose upper 16 k are zero
-            const bf16x8 afr32 = cat8(afr, bf16x4{});
+            const bf16x8 afr32 = cat8(cur.afr, bf16x4{});
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 // Delta' = T (V - Y): lane (g, c) holds V[4 g + e][c] as an
@@ -472,18 +489,36 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 }
             }
         };
-        // pipeline fill, the full chunks, then at most one ragged chunk (one
-        // barrier per step as in every role; separate loops keep S in place)
+        // pipeline fill, the full chunks (two per iteration, alternating
+        // operand sets), then at most one ragged chunk (one barrier per step
+        // as in every role; separate loops keep S in place)
         for (int c = -LR; c < 0; ++c)
             lds_barrier();
+        MemOps opA, opB;
+        if (nchunks > 0)
+            fetch(0, opA);
         const int nfull = T / C;
-        for (int c = 0; c < nfull; ++c) {
-            apply(std::integral_constant<bool, true>{}, c);
+        int c = 0;
+        for (; c + 1 < nfull; c += 2) {
+            apply(std::integral_constant<bool, true>{}, c, opA, opB);
+            orow += o_step;
+            lds_barrier();
+            apply(std::integral_constant<bool, true>{}, c + 1, opB, opA);
             orow += o_step;
             lds_barrier();
         }
+        bool inB = false;
+        if (c < nfull) {
+            apply(std::integral_constant<bool, true>{}, c, opA, opB);
+            orow += o_step;
+            lds_barrier();
+            inB = true;
+        }
         if (nfull < nchunks) {
-            apply(std::integral_constant<bool, false>{}, nfull);
+            if (inB)
+                apply(std::integral_constant<bool, false>{}, nfull, opB, opA);
+            else
+                apply(std::integral_constant<bool, false>{}, nfull, opA, opB);
             lds_barrier();
         }
 #pragma unroll
