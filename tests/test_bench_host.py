@@ -1,0 +1,66 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU contract, the
+algorithmic byte counts the roofline is priced with, and the rule that
+counter-measured traffic is reported only for the sources it was taken on."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and "--gpus 2" in res.stderr
+    assert res.stdout.strip() == ""
+
+
+@pytest.mark.parametrize("variant,per_ht", [("diag", 2052), ("iso", 1544)])
+def test_bytes_per_head_token(variant, per_ht):
+    # per head-token at d = 128, bf16 io: q, k, v read and o written (2 B
+    # each), fp32 gates (alpha, and omega per channel for Diagonal or per
+    # token for Isotropic) and r
+    B, T, H, d = 1, 1000, 1, 128
+    state = (d * d * 4 + d * 4) if variant == "diag" else (d * d * 4 + 4)
+    assert bench.alg_bytes_fwd(variant, B, T, H, d, d, 2) == T * per_ht + state
+
+
+def test_bytes_config2_forward():
+    # B = 8, H = 16, T = 4096, d = 128: 524,288 head-tokens at 2052 B plus the
+    # final state and variances of 128 heads
+    assert bench.alg_bytes_fwd("diag", 8, 4096, 16, 128, 128, 2) == 1_084_293_120
+
+
+def test_bytes_decode_step():
+    # per head: state read and written (2 d^2 4 B), q, k, v, o, alpha, omega,
+    # r and the variances read and written
+    d = 128
+    per_head = 2 * d * d * 4 + 3 * d * 2 + d * 2 + 2 * d * 4 + 4 + 2 * d * 4
+    assert bench.alg_bytes_step("diag", 256, 16, d, d, 2) == 256 * 16 * per_head
+
+
+def test_forward_kernel_by_io_dtype():
+    assert bench.fwd_kernel_name("bf16") == "kdn_walk_fwd_kernel"
+    assert bench.fwd_kernel_name("f32") == "kdn_chunk_fwd_kernel"
+
+
+def test_traffic_only_for_the_profiled_sources(tmp_path, monkeypatch):
+    kern = "kdn_walk_fwd_kernel"
+    key = bench.traffic_key(kern, "w", "diag")
+    f = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    f.write_text(json.dumps({key: {"source_hash": bench.kernel_source_hash(kern),
+                                   "bytes_per_launch": 123.0}}))
+    assert bench.traffic_for(kern, key) == 123.0
+    f.write_text(json.dumps({key: {"source_hash": "0" * 16, "bytes_per_launch": 123.0}}))
+    assert bench.traffic_for(kern, key) is None
+    assert bench.traffic_for(kern, bench.traffic_key(kern, "other", "diag")) is None
+    f.write_text("not json")
+    assert bench.traffic_for(kern, key) is None
