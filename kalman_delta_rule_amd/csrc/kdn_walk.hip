@@ -374,7 +374,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             }
         }
         // lane parts of the LDS addresses (elements)
-        const int tr_lane = quad_tr_lane<QS>(lane);   // W, Qb transpose reads
+        const int tr_lane = quad_tr_lane<QS>(lane);   // Kb, Qb transpose reads
         const int kt_lane = g4 * QS + c16 * 4;        // Ktp^T rows: quad g4, channel c16
         const int fr_lane = c16 * LDF + 4 * g4;       // Aqk rows
         int v_lane[NB];                               // v tile transpose reads
