@@ -61,8 +61,8 @@ def _load():
         for name in ("kdn_oracle_diag_fwd", "kdn_oracle_iso_fwd"):
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
-            fn.argtypes = ([ctypes.c_int] * 5 + [dp] * 8 + [ctypes.c_double]
-                           + [dp] * 5 + [ctypes.c_int])
+            fn.argtypes = ([ctypes.c_int] * 5 + [dp] * 9 + [ctypes.c_double]
+                           + [dp] * 7 + [ctypes.c_int])
         lib.kdn_oracle_max_threads.restype = ctypes.c_int
         lib.kdn_oracle_max_threads.argtypes = []
         _lib = lib
@@ -88,14 +88,25 @@ def _ptr(a: Optional[np.ndarray]):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def _head_vec(x, H):
+    x = _f64(x)
+    if x is not None:
+        assert x.shape == (H,)
+    return x
+
+
 def diag_fwd(q, k, v, alpha, omega, r, S0=None, p0=None, mu=None,
-             return_gain: bool = False, nthreads: int = 0) -> dict:
+             return_gain: bool = False, nthreads: int = 0,
+             mu_h=None, c0_h=None, return_beta_eff: bool = False) -> dict:
     """Diagonal KDN forward (KDN reading notes, method part §4-§5).
 
     Shapes: q,k [B,T,H,dk]; v [B,T,H,dv]; alpha, omega [B,T,H,dk]; r [B,T,H];
-    S0 [B,H,dk,dv] or None (zeros); p0 [B,H,dk] or None (ones); mu defaults
-    to dk.  Returns a dict with o [B,T,H,dv], S [B,H,dk,dv], p [B,H,dk] and,
-    with ``return_gain``, kappa and phat [B,T,H,dk].
+    S0 [B,H,dk,dv] or None (zeros); p0 [B,H,dk] or None (c0_h[h] per head,
+    or ones); mu defaults to dk, mu_h [H] overrides it per head (method part
+    §8: learned per-head scale and initial covariance).  Returns a dict with
+    o [B,T,H,dv], S [B,H,dk,dv], p [B,H,dk], with ``return_gain`` also kappa
+    and phat [B,T,H,dk], with ``return_beta_eff`` beta_eff [B,T,H] (method
+    part §2: k^T kappa = z / (r + z)).
     """
     q, k, v, alpha, omega, r = map(_f64, (q, k, v, alpha, omega, r))
     S0, p0 = _f64(S0), _f64(p0)
@@ -108,30 +119,36 @@ def diag_fwd(q, k, v, alpha, omega, r, S0=None, p0=None, mu=None,
     if p0 is not None:
         assert p0.shape == (B, H, dk)
     mu = float(dk if mu is None else mu)
+    mu_h, c0_h = _head_vec(mu_h, H), _head_vec(c0_h, H)
     o = np.zeros((B, T, H, dv))
     S = np.zeros((B, H, dk, dv))
     p = np.zeros((B, H, dk))
     kap = np.zeros((B, T, H, dk)) if return_gain else None
     ph = np.zeros((B, T, H, dk)) if return_gain else None
+    be = np.zeros((B, T, H)) if return_beta_eff else None
     rc = _load().kdn_oracle_diag_fwd(
         B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega),
-        _ptr(r), _ptr(S0), _ptr(p0), mu, _ptr(o), _ptr(S), _ptr(p),
-        _ptr(kap), _ptr(ph), int(nthreads))
+        _ptr(r), _ptr(S0), _ptr(p0), _ptr(c0_h), mu, _ptr(mu_h), _ptr(o), _ptr(S), _ptr(p),
+        _ptr(kap), _ptr(ph), _ptr(be), int(nthreads))
     if rc != 0:
         raise RuntimeError("kdn_oracle_diag_fwd failed (%d)" % rc)
     out = {"o": o, "S": S, "p": p}
     if return_gain:
         out["kappa"] = kap
         out["phat"] = ph
+    if return_beta_eff:
+        out["beta_eff"] = be
     return out
 
 
 def iso_fwd(q, k, v, alpha, omega, r, S0=None, b0=None, mu=None,
-            return_gain: bool = False, nthreads: int = 0) -> dict:
+            return_gain: bool = False, nthreads: int = 0,
+            mu_h=None, c0_h=None, return_beta_eff: bool = False) -> dict:
     """Isotropic KDN forward (KDN reading notes, method part §7, Eq. (40)).
 
-    omega is [B,T,H]; b0 is [B,H] or None (ones).  Returns o, S, b and, with
-    ``return_gain``, beta and bhat [B,T,H].
+    omega is [B,T,H]; b0 is [B,H] or None (c0_h[h] per head, or ones);
+    mu_h as in diag_fwd.  Returns o, S, b, with ``return_gain`` also beta and
+    bhat [B,T,H], with ``return_beta_eff`` beta_eff [B,T,H].
     """
     q, k, v, alpha, omega, r = map(_f64, (q, k, v, alpha, omega, r))
     S0, b0 = _f64(S0), _f64(b0)
@@ -145,39 +162,45 @@ def iso_fwd(q, k, v, alpha, omega, r, S0=None, b0=None, mu=None,
     if b0 is not None:
         assert b0.shape == (B, H)
     mu = float(dk if mu is None else mu)
+    mu_h, c0_h = _head_vec(mu_h, H), _head_vec(c0_h, H)
     o = np.zeros((B, T, H, dv))
     S = np.zeros((B, H, dk, dv))
     b = np.zeros((B, H))
     beta = np.zeros((B, T, H)) if return_gain else None
     bh = np.zeros((B, T, H)) if return_gain else None
+    be = np.zeros((B, T, H)) if return_beta_eff else None
     rc = _load().kdn_oracle_iso_fwd(
         B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega),
-        _ptr(r), _ptr(S0), _ptr(b0), mu, _ptr(o), _ptr(S), _ptr(b),
-        _ptr(beta), _ptr(bh), int(nthreads))
+        _ptr(r), _ptr(S0), _ptr(b0), _ptr(c0_h), mu, _ptr(mu_h), _ptr(o), _ptr(S), _ptr(b),
+        _ptr(beta), _ptr(bh), _ptr(be), int(nthreads))
     if rc != 0:
         raise RuntimeError("kdn_oracle_iso_fwd failed (%d)" % rc)
     out = {"o": o, "S": S, "b": b}
     if return_gain:
         out["beta"] = beta
         out["bhat"] = bh
+    if return_beta_eff:
+        out["beta_eff"] = be
     return out
 
 
-def step(variant: str, q, k, v, alpha, omega, r, S, var, mu=None) -> dict:
+def step(variant: str, q, k, v, alpha, omega, r, S, var, mu=None, mu_h=None) -> dict:
     """One decode step: the forward recurrence at T = 1 (KDN reading notes,
     method part §8: scanned training and token-by-token inference are the same
     recurrence).  q,k,v,alpha: [B,H,D]; omega [B,H,dk] (diag) or [B,H] (iso);
-    r [B,H]; S [B,H,dk,dv]; var = p [B,H,dk] or b [B,H].  Returns o [B,H,dv]
-    and the new S and variance."""
+    r [B,H]; S [B,H,dk,dv]; var = p [B,H,dk] or b [B,H]; mu_h [H] or None.
+    Returns o [B,H,dv], the new S and variance, and beta_eff [B,H]."""
     t1 = lambda x: None if x is None else _f64(x)[:, None]
     if variant == "diag":
         out = diag_fwd(t1(q), t1(k), t1(v), t1(alpha), t1(omega), t1(r),
-                       S0=S, p0=var, mu=mu)
-        return {"o": out["o"][:, 0], "S": out["S"], "var": out["p"]}
+                       S0=S, p0=var, mu=mu, mu_h=mu_h, return_beta_eff=True)
+        return {"o": out["o"][:, 0], "S": out["S"], "var": out["p"],
+                "beta_eff": out["beta_eff"][:, 0]}
     if variant == "iso":
         out = iso_fwd(t1(q), t1(k), t1(v), t1(alpha), t1(omega), t1(r),
-                      S0=S, b0=var, mu=mu)
-        return {"o": out["o"][:, 0], "S": out["S"], "var": out["b"]}
+                      S0=S, b0=var, mu=mu, mu_h=mu_h, return_beta_eff=True)
+        return {"o": out["o"][:, 0], "S": out["S"], "var": out["b"],
+                "beta_eff": out["beta_eff"][:, 0]}
     raise ValueError("variant must be 'diag' or 'iso'")
 
 

@@ -28,6 +28,13 @@
  *     memory lines identical to the diagonal variant (per-channel decay)
  *     b_t = b^_t / (1 + u_t b^_t),  u_t = mu |k_t|^2 / (d_k r_t)
  *
+ *   Per-head options (notes Part 2 sec. 8, trained parameters): a learned
+ *   information scale mu_h per head, and a learned initial covariance
+ *   c_{0,h} I per head used when no initial variance is given.
+ *   Diagnostic (notes Part 2 sec. 2): effective write strength
+ *     beta_eff_t = k_t^T kappa_t = z_t / (r_t + z_t),
+ *     z_t = sum_i p^_{t,i} k_{t,i}^2 (Diagonal), b^_t |k_t|^2 (Isotropic).
+ *
  * Layouts (row-major): activations [B,T,H,D]; state S [B,H,dk,dv];
  * variances p [B,H,dk] (diagonal) or b [B,H] (isotropic); gates alpha
  * [B,T,H,dk], omega [B,T,H,dk] (diagonal) or [B,T,H] (isotropic), r [B,T,H].
@@ -52,7 +59,7 @@ static void diag_head(int B, int T, int H, int dk, int dv, int b, int h,
                       const double* alpha, const double* omega,
                       const double* r, double mu,
                       double* S, double* p, double* o,
-                      double* kappa_out, double* phat_out,
+                      double* kappa_out, double* phat_out, double* beff_out,
                       double* ph, double* kap, double* delta)
 {
     (void)B;
@@ -75,6 +82,8 @@ static void diag_head(int B, int T, int H, int dk, int dv, int b, int h,
             z += ph[i] * kt[i] * kt[i];
         for (int i = 0; i < dk; ++i)
             kap[i] = ph[i] * kt[i] / (rt + z);
+        if (beff_out)
+            beff_out[((size_t)b * T + t) * H + h] = z / (rt + z);
 
         /* predicted mean S^ = diag(alpha) S */
         for (int i = 0; i < dk; ++i)
@@ -119,7 +128,7 @@ static void iso_head(int B, int T, int H, int dk, int dv, int b, int h,
                      const double* alpha, const double* omega,
                      const double* r, double mu,
                      double* S, double* bvar, double* o,
-                     double* beta_out, double* bhat_out,
+                     double* beta_out, double* bhat_out, double* beff_out,
                      double* kap, double* delta)
 {
     (void)B;
@@ -173,21 +182,27 @@ static void iso_head(int B, int T, int H, int dk, int dv, int b, int h,
             beta_out[bth] = beta;
         if (bhat_out)
             bhat_out[bth] = bh;
+        if (beff_out)  /* z = k^T (b^ I) k */
+            beff_out[bth] = bh * n / (rt + bh * n);
     }
 }
 
 /*
  * Diagonal KDN forward over [B,T,H] tokens.  S0 (nullable = zeros) and p0
- * (nullable = ones) are the initial state; o, S_T, p_T are written.
+ * (nullable = c0_h[h], or ones without c0_h) are the initial state; o, S_T,
+ * p_T are written.  mu_h (nullable, [H]) overrides mu per head.
  * kappa_out / phat_out (nullable, [B,T,H,dk]) expose the gain and the
- * predicted variance for the tests.  Returns 0, or -1 on bad sizes / memory.
+ * predicted variance for the tests, beff_out (nullable, [B,T,H]) the
+ * effective write strength.  Returns 0, or -1 on bad sizes / memory.
  */
 int kdn_oracle_diag_fwd(int B, int T, int H, int dk, int dv,
                         const double* q, const double* k, const double* v,
                         const double* alpha, const double* omega,
                         const double* r, const double* S0, const double* p0,
-                        double mu, double* o, double* S_T, double* p_T,
-                        double* kappa_out, double* phat_out, int nthreads)
+                        const double* c0_h, double mu, const double* mu_h,
+                        double* o, double* S_T, double* p_T,
+                        double* kappa_out, double* phat_out, double* beff_out,
+                        int nthreads)
 {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
         return -1;
@@ -207,30 +222,33 @@ int kdn_oracle_diag_fwd(int B, int T, int H, int dk, int dv,
         else
             memset(S, 0, sizeof(double) * dk * dv);
         for (int i = 0; i < dk; ++i)
-            p[i] = p0 ? p0[(size_t)bh * dk + i] : 1.0;
+            p[i] = p0 ? p0[(size_t)bh * dk + i] : (c0_h ? c0_h[h] : 1.0);
         double* scratch = (double*)malloc(sizeof(double) * (2 * (size_t)dk + dv));
         if (!scratch) {
             failed = 1;
             continue;
         }
-        diag_head(B, T, H, dk, dv, b, h, q, k, v, alpha, omega, r, mu, S, p, o,
-                  kappa_out, phat_out, scratch, scratch + dk, scratch + 2 * dk);
+        diag_head(B, T, H, dk, dv, b, h, q, k, v, alpha, omega, r, mu_h ? mu_h[h] : mu, S, p, o,
+                  kappa_out, phat_out, beff_out, scratch, scratch + dk, scratch + 2 * dk);
         free(scratch);
     }
     return failed ? -1 : 0;
 }
 
 /*
- * Isotropic KDN forward.  omega is [B,T,H]; b0 (nullable = ones) and b_T are
- * [B,H].  beta_out / bhat_out (nullable, [B,T,H]) expose the scalar gain and
- * the predicted variance for the tests.
+ * Isotropic KDN forward.  omega is [B,T,H]; b0 (nullable = c0_h[h], or ones
+ * without c0_h) and b_T are [B,H]; mu_h as in the Diagonal call.
+ * beta_out / bhat_out / beff_out (nullable, [B,T,H]) expose the scalar gain,
+ * the predicted variance and the effective write strength for the tests.
  */
 int kdn_oracle_iso_fwd(int B, int T, int H, int dk, int dv,
                        const double* q, const double* k, const double* v,
                        const double* alpha, const double* omega,
                        const double* r, const double* S0, const double* b0,
-                       double mu, double* o, double* S_T, double* b_T,
-                       double* beta_out, double* bhat_out, int nthreads)
+                       const double* c0_h, double mu, const double* mu_h,
+                       double* o, double* S_T, double* b_T,
+                       double* beta_out, double* bhat_out, double* beff_out,
+                       int nthreads)
 {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
         return -1;
@@ -248,14 +266,14 @@ int kdn_oracle_iso_fwd(int B, int T, int H, int dk, int dv,
             memcpy(S, S0 + (size_t)bh * dk * dv, sizeof(double) * dk * dv);
         else
             memset(S, 0, sizeof(double) * dk * dv);
-        b_T[bh] = b0 ? b0[bh] : 1.0;
+        b_T[bh] = b0 ? b0[bh] : (c0_h ? c0_h[h] : 1.0);
         double* scratch = (double*)malloc(sizeof(double) * ((size_t)dk + dv));
         if (!scratch) {
             failed = 1;
             continue;
         }
-        iso_head(B, T, H, dk, dv, b, h, q, k, v, alpha, omega, r, mu, S, &b_T[bh], o,
-                 beta_out, bhat_out, scratch, scratch + dk);
+        iso_head(B, T, H, dk, dv, b, h, q, k, v, alpha, omega, r, mu_h ? mu_h[h] : mu, S, &b_T[bh], o,
+                 beta_out, bhat_out, beff_out, scratch, scratch + dk);
         free(scratch);
     }
     return failed ? -1 : 0;

@@ -487,3 +487,86 @@ def test_empty_sequence_returns_initial_state(ora):
                        S0=S0, p0=p0)
     assert out["o"].shape == (1, 0, 2, 3)
     assert np.array_equal(out["S"], S0) and np.array_equal(out["p"], p0)
+
+
+# ---------------------------------------------------------------------------
+# P-m: per-head trained parameters (KDN notes method §8: a learned initial
+# covariance c_{0,h} I and scale mu per head) and the effective write strength
+# (method §2: beta_eff = k^T kappa = z / (r + z))
+# ---------------------------------------------------------------------------
+def _fwd(ora, variant, *args, **kw):
+    if variant == "iso" and "p0" in kw:
+        kw["b0"] = kw.pop("p0")
+    return (ora.diag_fwd if variant == "diag" else ora.iso_fwd)(*args, **kw)
+
+
+def test_beta_eff_equals_dense_kf_write_strength(ora):
+    # axis-aligned keys keep the exact posterior diagonal (pinned above), so
+    # beta_eff must be z / (r + z) with z = k^T P^ k of the dense filter
+    rng = np.random.default_rng(21)
+    T, dk, dv = 50, 4, 3
+    q, _, v, alpha, omega, r = _rand_inputs(rng, 1, T, 1, dk, dv)
+    k = np.zeros((1, T, 1, dk))
+    idx = rng.integers(0, dk, T)
+    k[0, np.arange(T), 0, idx] = 0.3 + 2 * rng.random(T)
+    p0 = 0.2 + rng.random((1, 1, dk))
+    out = ora.diag_fwd(q, k, v, alpha, omega, r, p0=p0, mu=1.0, return_beta_eff=True)
+    D = np.stack([np.diag(a) for a in alpha[0, :, 0]])
+    Om = np.stack([np.diag(w) for w in omega[0, :, 0]])
+    den = ora.dense_kf(k[0, :, 0], v[0, :, 0], q[0, :, 0], D, Om, r[0, :, 0],
+                       np.zeros((dk, dv)), np.diag(p0[0, 0]))
+    ref = den["z"] / (r[0, :, 0] + den["z"])
+    assert np.allclose(out["beta_eff"][0, :, 0], ref, rtol=1e-11, atol=1e-14)
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+def test_beta_eff_is_key_times_gain(ora, variant):
+    rng = np.random.default_rng(22)
+    B, T, H, dk, dv = 2, 40, 3, 6, 5
+    q, k, v, alpha, omega, r = _rand_inputs(rng, B, T, H, dk, dv, variant)
+    k = k * (0.2 + 3 * rng.random((B, T, H, 1)))
+    out = _fwd(ora, variant, q, k, v, alpha, omega, r, return_gain=True,
+               return_beta_eff=True)
+    if variant == "diag":
+        ref = (out["kappa"] * k).sum(-1)
+    else:
+        ref = out["beta"] * (k * k).sum(-1)
+    assert np.allclose(out["beta_eff"], ref, rtol=1e-12, atol=1e-15)
+    assert (out["beta_eff"] >= 0).all() and (out["beta_eff"] < 1).all()
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+def test_per_head_mu_is_each_head_with_its_own_mu(ora, variant):
+    rng = np.random.default_rng(23)
+    B, T, H, dk, dv = 2, 30, 3, 6, 5
+    q, k, v, alpha, omega, r = _rand_inputs(rng, B, T, H, dk, dv, variant)
+    mu_h = np.array([0.5, 6.0, 40.0])
+    full = _fwd(ora, variant, q, k, v, alpha, omega, r, mu_h=mu_h, return_beta_eff=True)
+    var = "p" if variant == "diag" else "b"
+    for h in range(H):
+        sl = lambda x: np.ascontiguousarray(x[:, :, h:h + 1])
+        one = _fwd(ora, variant, sl(q), sl(k), sl(v), sl(alpha), sl(omega), sl(r),
+                   mu=float(mu_h[h]), return_beta_eff=True)
+        assert np.array_equal(full["o"][:, :, h], one["o"][:, :, 0])
+        assert np.array_equal(full["S"][:, h], one["S"][:, 0])
+        assert np.array_equal(full[var][:, h], one[var][:, 0])
+        assert np.array_equal(full["beta_eff"][:, :, h], one["beta_eff"][:, :, 0])
+    flat = _fwd(ora, variant, q, k, v, alpha, omega, r, mu=float(dk))
+    assert not np.allclose(full[var], flat[var])
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+def test_c0_is_a_filled_initial_variance(ora, variant):
+    rng = np.random.default_rng(24)
+    B, T, H, dk, dv = 2, 25, 3, 6, 5
+    q, k, v, alpha, omega, r = _rand_inputs(rng, B, T, H, dk, dv, variant)
+    c0 = np.array([0.3, 1.7, 4.0])
+    a = _fwd(ora, variant, q, k, v, alpha, omega, r, c0_h=c0)
+    shape = (B, H, dk) if variant == "diag" else (B, H)
+    filled = np.ascontiguousarray(np.broadcast_to(
+        c0[None, :, None] if variant == "diag" else c0[None, :], shape))
+    b = _fwd(ora, variant, q, k, v, alpha, omega, r, p0=filled)
+    for key in a:
+        assert np.array_equal(a[key], b[key])
+    ones = _fwd(ora, variant, q, k, v, alpha, omega, r)
+    assert not np.allclose(a["o"], ones["o"])
