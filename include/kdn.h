@@ -141,6 +141,42 @@ kdn_status kdn_step(int variant, int B, int H, int dk, int dv, int io_dtype, flo
                     float* S, float* var_state, void* o, void* stream);
 
 /*
+ * Extended forward (either variant) with the trained per-head parameters of
+ * the end-to-end network (KDN reading notes, method part §8: a learned scalar
+ * initial covariance c_{0,h} I and information scale mu per head) and the
+ * effective write strength diagnostic (method part §2:
+ * beta_eff_t = k_t^T kappa_t = z_t / (r_t + z_t); its distribution is the
+ * results part's §4, Fig. 2).  Arguments as in kdn_diag_fwd / kdn_iso_fwd
+ * (variant KDN_DIAG or KDN_ISO; var0 / var_T are p0 / p_T or b0 / b_T), plus
+ *   mu_h      [H] fp32 device, nullable: information scale of head h (used
+ *             instead of mu; entries must be finite and >= 0, not checked)
+ *   c0_h      [H] fp32 device, nullable: initial variance of head h, every
+ *             channel (Diagonal) or the head's scalar (Isotropic); only
+ *             when var0 is NULL -- giving both is KDN_ERR_INVALID_ARG
+ *   beta_eff  [B,T,H] fp32 device, nullable: written with beta_eff of every
+ *             token; must not alias r, o, S_T or var_T
+ * All three are 4-byte aligned.  With all three NULL the call equals
+ * kdn_diag_fwd / kdn_iso_fwd.  In the bf16 forward z_t is the diagonal of the
+ * chunk's bf16 key product, so beta_eff carries the same bf16 rounding as
+ * the gain it describes.
+ */
+kdn_status kdn_fwd_ex(int variant, int B, int T, int H, int dk, int dv, int io_dtype, float mu,
+                      const float* mu_h, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* omega, const float* r, const float* S0,
+                      const float* var0, const float* c0_h, void* o, float* S_T, float* var_T,
+                      float* beta_eff, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Extended decode step: kdn_step with a per-head information scale mu_h [H]
+ * (nullable, as in kdn_fwd_ex) and the token's effective write strength
+ * beta_eff [B,H] fp32 (nullable).  Same passages as kdn_fwd_ex.
+ */
+kdn_status kdn_step_ex(int variant, int B, int H, int dk, int dv, int io_dtype, float mu,
+                       const float* mu_h, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* omega, const float* r, float* S,
+                       float* var_state, void* o, float* beta_eff, void* stream);
+
+/*
  * Gain scan alone (the variance recurrence and Kalman gain without the
  * memory), exposed for the chunk-parallel regime's tests and diagnostics.
  * Inputs as in the forward calls (q, v not needed).  Writes

@@ -50,6 +50,11 @@ def lib():
         fn.argtypes = fwd_args
     L.kdn_step.restype = i
     L.kdn_step.argtypes = [i] * 6 + [f] + [vp] * 3 + [fp] * 3 + [fp, fp, vp, vp]
+    L.kdn_fwd_ex.restype = i
+    L.kdn_fwd_ex.argtypes = ([i] * 7 + [f] + [fp] + [vp] * 3 + [fp] * 6 + [vp] + [fp] * 3
+                             + [vp, sz, vp])
+    L.kdn_step_ex.restype = i
+    L.kdn_step_ex.argtypes = [i] * 6 + [f] + [fp] + [vp] * 3 + [fp] * 5 + [vp, fp, vp]
     L.kdn_gain_workspace_size.restype = sz
     L.kdn_gain_workspace_size.argtypes = [i] * 5
     L.kdn_gain_scan.restype = i
@@ -65,6 +70,7 @@ def lib():
 
 
 EXPORTED = ("kdn_fwd_workspace_size", "kdn_diag_fwd", "kdn_iso_fwd", "kdn_step",
+            "kdn_fwd_ex", "kdn_step_ex",
             "kdn_gain_workspace_size", "kdn_gain_scan", "kdn_status_string",
             "kdn_last_error_message", "kdn_version")
 

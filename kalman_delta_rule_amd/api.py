@@ -45,7 +45,14 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T):
+def _head_vec(t, name, H, dev):
+    if t is not None:
+        _need(t, name, (H,), torch.float32, dev)
+    return t
+
+
+def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
+         ext: bool = False, mu_h=None, c0_h=None, beta_eff=None):
     L = _lib.lib()
     if q.dim() != 4:
         raise ValueError("q must be [B,T,H,dk]")
@@ -79,6 +86,18 @@ def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T):
     mu = float(dk if mu is None else mu)
     ws_bytes = L.kdn_fwd_workspace_size(variant, B, T, H, dk, dv, io)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    if ext:
+        _head_vec(mu_h, "mu_h", H, dev)
+        _head_vec(c0_h, "c0_h", H, dev)
+        if beta_eff is not None:
+            _need(beta_eff, "beta_eff", (B, T, H), torch.float32, dev)
+        with torch.cuda.device(dev):
+            st = L.kdn_fwd_ex(variant, B, T, H, dk, dv, io, mu, _ptr(mu_h), _ptr(q), _ptr(k),
+                              _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r), _ptr(S0), _ptr(var0),
+                              _ptr(c0_h), _ptr(o), _ptr(S_T), _ptr(var_T), _ptr(beta_eff),
+                              _ptr(ws), ws_bytes, _stream(dev))
+        _lib.check(st)
+        return o, S_T, var_T
     fn = L.kdn_diag_fwd if variant == KDN_DIAG else L.kdn_iso_fwd
     with torch.cuda.device(dev):
         st = fn(B, T, H, dk, dv, io, mu, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega),
@@ -100,8 +119,24 @@ def kdn_iso_fwd(q, k, v, alpha, omega, r, S0=None, b0=None, mu=None, o=None, S_T
     return _fwd(KDN_ISO, q, k, v, alpha, omega, r, S0, b0, mu, o, S_T, b_T)
 
 
+def kdn_fwd_ex(variant: str, q, k, v, alpha, omega, r, S0=None, var0=None, mu=None,
+               mu_h=None, c0_h=None, want_beta_eff: bool = False, o=None, S_T=None,
+               var_T=None):
+    """Forward with per-head mu_h [H] and c0_h [H] (both optional) and the
+    effective write strength.  Returns (o, S_T, var_T, beta_eff [B,T,H] or
+    None)."""
+    var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
+    beta = None
+    if want_beta_eff:
+        B, T, H, _ = q.shape
+        beta = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    o, S_T, var_T = _fwd(var, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
+                         ext=True, mu_h=mu_h, c0_h=c0_h, beta_eff=beta)
+    return o, S_T, var_T, beta
+
+
 def kdn_step(variant: str, q, k, v, alpha, omega, r, S, var_state, mu=None,
-             o=None) -> torch.Tensor:
+             o=None, mu_h=None, beta_eff=None) -> torch.Tensor:
     """One decode step; S [B,H,dk,dv] and var_state are updated in place.
     ``variant`` is "diag" or "iso".  Returns o [B,H,dv]."""
     L = _lib.lib()
@@ -122,6 +157,18 @@ def kdn_step(variant: str, q, k, v, alpha, omega, r, S, var_state, mu=None,
         o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
     _need(o, "o", (B, H, dv), q.dtype, dev)
     mu = float(dk if mu is None else mu)
+    if mu_h is not None or beta_eff is not None:
+        # extended step: per-head information scale and / or the effective
+        # write strength [B,H]
+        _head_vec(mu_h, "mu_h", H, dev)
+        if beta_eff is not None:
+            _need(beta_eff, "beta_eff", (B, H), torch.float32, dev)
+        with torch.cuda.device(dev):
+            st = L.kdn_step_ex(var, B, H, dk, dv, io, mu, _ptr(mu_h), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(alpha), _ptr(omega), _ptr(r), _ptr(S), _ptr(var_state),
+                               _ptr(o), _ptr(beta_eff), _stream(dev))
+        _lib.check(st)
+        return o
     with torch.cuda.device(dev):
         st = L.kdn_step(var, B, H, dk, dv, io, mu, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                         _ptr(omega), _ptr(r), _ptr(S), _ptr(var_state), _ptr(o), _stream(dev))

@@ -80,13 +80,43 @@ kdn_status check_common(int B, int T, int H, int dk, int dv, int io, float mu, b
             return fail(KDN_ERR_INVALID_ARG, "%s must be 16-byte aligned", name); \
     } while (0)
 
+#define KDN_ALIGNED_X(ptr, name)                                                 \
+    do {                                                                         \
+        if ((ptr) && (reinterpret_cast<uintptr_t>(ptr) & 3u))                    \
+            return fail(KDN_ERR_INVALID_ARG, "%s must be 4-byte aligned", name);  \
+    } while (0)
+
+// Per-head options and the diagnostic output of the extended calls.
+struct ExtOpts {
+    const float* mu_h = nullptr;  // [H] or null
+    const float* c0_h = nullptr;  // [H] or null
+    float* beta_eff = nullptr;    // [B,T,H] / [B,H] or null
+};
+
+kdn_status check_ext(const ExtOpts& x, const void* var0, const void* r, const void* o,
+                     const void* S_out, const void* var_out)
+{
+    if (x.c0_h && var0)
+        return fail(KDN_ERR_INVALID_ARG, "give the initial variance either as var0 or as c0_h, not both");
+    KDN_ALIGNED_X(x.mu_h, "mu_h");
+    KDN_ALIGNED_X(x.c0_h, "c0_h");
+    KDN_ALIGNED_X(x.beta_eff, "beta_eff");
+    if (x.beta_eff && (x.beta_eff == r || x.beta_eff == o || x.beta_eff == S_out ||
+                       x.beta_eff == var_out))
+        return fail(KDN_ERR_INVALID_ARG, "beta_eff must not alias r, o, the state or the variances");
+    return KDN_OK;
+}
+
 kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float mu,
                     const void* q, const void* k, const void* v, const float* alpha,
                     const float* omega, const float* r, const float* S0, const float* var0,
                     void* o, float* S_T, float* var_T, void* workspace,
-                    size_t workspace_bytes, void* stream)
+                    size_t workspace_bytes, void* stream, const ExtOpts& x = ExtOpts{})
 {
     kdn_status st = check_common(B, T, H, dk, dv, io, mu, true);
+    if (st != KDN_OK)
+        return st;
+    st = check_ext(x, var0, r, o, S_T, var_T);
     if (st != KDN_OK)
         return st;
     if (T > 0) {
@@ -137,7 +167,8 @@ kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float
                     workspace_bytes);
     (void)workspace;
 
-    kdn::FwdArgs a{q, k, v, alpha, omega, r, S0, var0, o, S_T, var_T, B, T, H, dk, dv, mu};
+    kdn::FwdArgs a{q, k, v, alpha, omega, r, S0, var0, o, S_T, var_T, B, T, H, dk, dv, mu,
+                   x.mu_h, x.c0_h, T > 0 ? x.beta_eff : nullptr};
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = io == KDN_BF16 ? kdn::launch_walk_fwd(a, iso, hs)
                                   : kdn::launch_chunk_fwd_f32(a, iso, hs);
@@ -182,10 +213,14 @@ kdn_status kdn_iso_fwd(int B, int T, int H, int dk, int dv, int io_dtype, float 
                     S_T, b_T, workspace, workspace_bytes, stream);
 }
 
-kdn_status kdn_step(int variant, int B, int H, int dk, int dv, int io_dtype, float mu,
-                    const void* q, const void* k, const void* v, const float* alpha,
-                    const float* omega, const float* r, float* S, float* var_state, void* o,
-                    void* stream)
+}  // extern "C"
+
+namespace {
+
+kdn_status step_impl(int variant, int B, int H, int dk, int dv, int io_dtype, float mu,
+                     const void* q, const void* k, const void* v, const float* alpha,
+                     const float* omega, const float* r, float* S, float* var_state, void* o,
+                     void* stream, const ExtOpts& x = ExtOpts{})
 {
     if (variant != KDN_DIAG && variant != KDN_ISO)
         return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
@@ -206,11 +241,56 @@ kdn_status kdn_step(int variant, int B, int H, int dk, int dv, int io_dtype, flo
     KDN_ALIGNED(S, "S");
     if (o == q || o == k || o == v)
         return fail(KDN_ERR_INVALID_ARG, "o must not alias q, k or v");
-    kdn::StepArgs a{q, k, v, alpha, omega, r, S, var_state, o, B, H, dk, dv, mu};
+    st = check_ext(x, nullptr, r, o, S, var_state);
+    if (st != KDN_OK)
+        return st;
+    kdn::StepArgs a{q, k, v, alpha, omega, r, S, var_state, o, B, H, dk, dv, mu, x.mu_h, x.beta_eff};
     hipError_t e = kdn::launch_step(a, iso, io_dtype, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kdn_status kdn_step(int variant, int B, int H, int dk, int dv, int io_dtype, float mu,
+                    const void* q, const void* k, const void* v, const float* alpha,
+                    const float* omega, const float* r, float* S, float* var_state, void* o,
+                    void* stream)
+{
+    return step_impl(variant, B, H, dk, dv, io_dtype, mu, q, k, v, alpha, omega, r, S, var_state,
+                     o, stream);
+}
+
+kdn_status kdn_fwd_ex(int variant, int B, int T, int H, int dk, int dv, int io_dtype, float mu,
+                      const float* mu_h, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* omega, const float* r, const float* S0,
+                      const float* var0, const float* c0_h, void* o, float* S_T, float* var_T,
+                      float* beta_eff, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (variant != KDN_DIAG && variant != KDN_ISO)
+        return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
+                    variant);
+    ExtOpts x;
+    x.mu_h = mu_h;
+    x.c0_h = c0_h;
+    x.beta_eff = beta_eff;
+    return fwd_impl(variant == KDN_ISO, B, T, H, dk, dv, io_dtype, mu, q, k, v, alpha, omega, r,
+                    S0, var0, o, S_T, var_T, workspace, workspace_bytes, stream, x);
+}
+
+kdn_status kdn_step_ex(int variant, int B, int H, int dk, int dv, int io_dtype, float mu,
+                       const float* mu_h, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* omega, const float* r, float* S,
+                       float* var_state, void* o, float* beta_eff, void* stream)
+{
+    ExtOpts x;
+    x.mu_h = mu_h;
+    x.beta_eff = beta_eff;
+    return step_impl(variant, B, H, dk, dv, io_dtype, mu, q, k, v, alpha, omega, r, S, var_state,
+                     o, stream, x);
 }
 
 size_t kdn_gain_workspace_size(int variant, int B, int T, int H, int dk)

@@ -240,7 +240,8 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
     const int b = bh / a.H, h = bh % a.H;
     const int j0 = tile * DVT;
     const int T = a.T, H = a.H, dv = a.dv;
-    const float mu = a.mu;
+    const float mu = a.mu_h ? a.mu_h[h] : a.mu;
+    const float var_init = a.c0 ? a.c0[h] : 1.f;  // variance when no var0 is given
     const int nchunks = (T + C - 1) / C;
     auto n_valid = [&](int x) { return min(C, T - x * C); };
     // global offsets (elements) of token t's row for this head
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
             // ================ Diagonal chain: lane = key channel ================
             // writes G over alpha and p^ / G over omega
             const int i = (wave - NMM) * 64 + lane;
-            float p = a.var0 ? a.var0[(size_t)bh * DK + i] : 1.f;
+            float p = a.var0 ? a.var0[(size_t)bh * DK + i] : var_init;
             auto chain = [&](auto full_tag, int X) {
                 constexpr bool FULL = decltype(full_tag)::value;
                 const int nv = FULL ? C : n_valid(X);
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
         } else {
             // ======== Isotropic chain: one wave, DK / 64 channels per lane ========
             constexpr int CPL = DK / 64;
-            float bvar = a.var0 ? a.var0[bh] : 1.f;
+            float bvar = a.var0 ? a.var0[bh] : var_init;
             for (int c = -LEAD; c < nchunks; ++c) {
                 const int X = c + 3;
                 if (X >= 0 && X < nchunks) {
@@ -623,7 +624,11 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
                     const float z = rs == 0 ? accL[0] : rs == 1 ? accL[1] : rs == 2 ? accL[2] : accL[3];
                     const float rraw = rr[c16];
                     const float rt = c16 < nv ? rraw : 1.f;
-                    sm.dinv[c16] = rcp(rt + z);
+                    const float dvz = rcp(rt + z);
+                    sm.dinv[c16] = dvz;
+                    // effective write strength of token c16 (one tile writes it)
+                    if (a.beta && tile == 0 && c16 < nv)
+                        a.beta[row_s(Fc * C + c16)] = z * dvz;
                 }
                 // Aqk[t][u] = Aqk^T[u][t] for u <= t, else 0
                 {

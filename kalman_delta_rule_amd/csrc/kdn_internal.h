@@ -21,6 +21,9 @@ struct FwdArgs {
     float* var_T;
     int B, T, H, dk, dv;
     float mu;
+    const float* mu_h;  // nullable [H]: per-head information scale (overrides mu)
+    const float* c0;    // nullable [H]: initial variance of every channel of a head when var0 is null
+    float* beta;        // nullable [B,T,H]: effective write strength z / (r + z)
 };
 
 struct StepArgs {
@@ -35,6 +38,8 @@ struct StepArgs {
     void* o;
     int B, H, dk, dv;
     float mu;
+    const float* mu_h;  // nullable [H]: per-head information scale (overrides mu)
+    float* beta;        // nullable [B,H]: effective write strength z / (r + z)
 };
 
 struct GainArgs {

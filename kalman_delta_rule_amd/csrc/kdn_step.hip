@@ -49,6 +49,7 @@ __global__ __launch_bounds__(STEP_THREADS) void kdn_step_kernel(StepArgs a)
         s[m] = *reinterpret_cast<const f32x4*>(S + (size_t)(rg + RG * m) * DV + 4 * cl);
 
     const float rt = a.r[bh];
+    const float mu = a.mu_h ? a.mu_h[bh % a.H] : a.mu;
     // read the head's scalar variance before any lane overwrites it
     const float bvar = ISO ? a.var[bh] : 0.f;
     // ---- gain (lanes = key channels)
@@ -85,8 +86,11 @@ __global__ __launch_bounds__(STEP_THREADS) void kdn_step_kernel(StepArgs a)
         float kap;
         if (!ISO) {
             const float z = sum0;
-            kap = ph * kv * rcp(rt + z);
-            const float u = (a.mu / rt) * kv * kv;
+            const float dz = rcp(rt + z);
+            kap = ph * kv * dz;
+            if (a.beta && tid == 0)
+                a.beta[bh] = z * dz;
+            const float u = (mu / rt) * kv * kv;
             a.var[(size_t)bh * DK + tid] = ph * rcp(1.f + u * ph);
         } else {
             const float am = sum0 * (1.f / DK), n = sum1;
@@ -94,7 +98,9 @@ __global__ __launch_bounds__(STEP_THREADS) void kdn_step_kernel(StepArgs a)
             const float beta = bh_ * rcp(rt + bh_ * n);
             kap = beta * kv;
             if (tid == 0) {
-                const float u = a.mu * n * rcp((float)DK * rt);
+                if (a.beta)
+                    a.beta[bh] = beta * n;  // z / (r + z) with z = b^ |k|^2
+                const float u = mu * n * rcp((float)DK * rt);
                 a.var[bh] = bh_ * rcp(1.f + u * bh_);
             }
         }

@@ -333,7 +333,8 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
     const int b = bh / a.H, h = bh % a.H;
     const int j0 = tile * DVT;
     const int T = a.T, H = a.H, dv = a.dv;
-    const float mu = a.mu;
+    const float mu = a.mu_h ? a.mu_h[h] : a.mu;
+    const float var_init = a.c0 ? a.c0[h] : 1.f;  // variance when no var0 is given
     const int nchunks = (T + C - 1) / C;
     auto n_valid = [&](int x) { return min(C, T - x * C); };
     auto row_k = [&](int t) { return (((size_t)b * T + t) * H + h) * DK; };
@@ -534,7 +535,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         // ================ builder waves: lane = key channel ================
         const int i = ridx * 64 + lane;
         // Diagonal: homogeneous variance [n; d];  Isotropic: no state here
-        float vn = (!ISO && a.var0) ? a.var0[(size_t)bh * DK + i] : 1.f;
+        float vn = (!ISO && a.var0) ? a.var0[(size_t)bh * DK + i] : var_init;
         float vd = 1.f;
         // Diagonal omega of this lane's channel comes straight from global
         // memory, OPF chunks ahead, into a register ring of OPF + 1 slots
@@ -732,6 +733,9 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     tr.dinv[c16] = dv;
                     if (c16 >= 8)
                         tr.dinvr[15 - c16] = dv;
+                    // effective write strength of token c16 (one tile writes it)
+                    if (a.beta && tile == 0 && c16 < nv)
+                        a.beta[row_s(F * C + c16)] = z * dv;
                 }
                 // Aqk[t][u] = Aqk^T[u][t] for u <= t, else 0
                 {
@@ -1108,7 +1112,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         // homogeneous variance b = n / d (see the Diagonal builders):
         //   n_t = a_t n_{t-1} + omega_t d_{t-1},  d_t = d_{t-1} + u_t n_t,
         //   u_t = mu |k_t|^2 / (d_k r_t),  b^_t = n_t / d_{t-1}
-        float nn = a.var0 ? a.var0[bh] : 1.f, dd = 1.f;
+        float nn = a.var0 ? a.var0[bh] : var_init, dd = 1.f;
         for (int c = -LR; c < nchunks; ++c) {
             const int X = c + LB + 1;
             if (X >= 0 && X < nchunks) {

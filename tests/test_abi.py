@@ -173,3 +173,45 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(_lib.KdnLibraryMissing):
         _lib.lib()
+
+
+def _fwd_ex_call(L, **kw):
+    a = dict(variant=0, B=1, T=64, H=2, dk=64, dv=64, io=1, mu=64.0, mu_h=None, q=P, k=P, v=P,
+             alpha=P, omega=P, r=P, S0=None, var0=None, c0_h=None, o=P + 4096, S_T=P + 8192,
+             var_T=P + 16384, beta=None, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.kdn_fwd_ex(a["variant"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["io"], a["mu"],
+                        a["mu_h"], a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"],
+                        a["S0"], a["var0"], a["c0_h"], a["o"], a["S_T"], a["var_T"], a["beta"],
+                        a["ws"], a["ws_bytes"], a["stream"])
+
+
+@cpu_only
+@pytest.mark.parametrize("bad,code,needle", [
+    (dict(variant=2), -1, "variant"),
+    (dict(var0=P + 32768, c0_h=P + 65536), -1, "either as var0 or as c0_h"),
+    (dict(mu_h=P + 2), -1, "mu_h must be 4-byte aligned"),
+    (dict(c0_h=P + 1), -1, "c0_h must be 4-byte aligned"),
+    (dict(beta=P + 3), -1, "beta_eff must be 4-byte aligned"),
+    (dict(beta=P), -1, "beta_eff must not alias"),
+    (dict(beta=P + 4096), -1, "beta_eff must not alias"),
+    (dict(dk=96), -2, "dk"),
+])
+def test_fwd_ex_validation(L, bad, code, needle):
+    assert _fwd_ex_call(L, **bad) == code
+    assert needle in L.kdn_last_error_message().decode()
+
+
+@cpu_only
+def test_step_ex_validation(L):
+    def step(**kw):
+        a = dict(var=0, B=4, H=2, dk=128, dv=128, io=1, mu=128.0, mu_h=None, q=P, k=P, v=P,
+                 alpha=P, omega=P, r=P, S=P + 4096, vs=P + 8192, o=P + 16384, beta=None)
+        a.update(kw)
+        return L.kdn_step_ex(a["var"], a["B"], a["H"], a["dk"], a["dv"], a["io"], a["mu"],
+                             a["mu_h"], a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"],
+                             a["S"], a["vs"], a["o"], a["beta"], None)
+    assert step(var=5) == -1 and "variant" in L.kdn_last_error_message().decode()
+    assert step(beta=P + 8192) == -1 and "beta_eff" in L.kdn_last_error_message().decode()
+    assert step(mu_h=P + 1) == -1 and "mu_h" in L.kdn_last_error_message().decode()
+    assert step(dv=96) == -2
