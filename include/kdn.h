@@ -177,6 +177,26 @@ kdn_status kdn_step_ex(int variant, int B, int H, int dk, int dv, int io_dtype, 
                        float* var_state, void* o, float* beta_eff, void* stream);
 
 /*
+ * Exact dense-covariance Kalman memory for small d_k (KDN reading notes,
+ * method part §2, Eq. (12)-(17)), with the Diagonal KDN's gates as the
+ * transition D_t = diag(alpha_t) and process noise Omega_t = diag(omega_t):
+ * the filter whose mean-field projection is Diagonal KDN (method part §4).
+ * An ablation and cross-check tool (a serial Riccati step per token), not a
+ * throughput path; the information scale mu does not apply to it.
+ *   q, k   [B,T,H,dk] io dtype       v, o  [B,T,H,dv] io dtype
+ *   alpha, omega [B,T,H,dk] fp32     r     [B,T,H] fp32
+ *   S0 [B,H,dk,dv] fp32 (NULL: zeros),  P0 [B,H,dk,dk] fp32 (NULL: identity)
+ *   S_T, P_T  final state and covariance (required; may alias S0 / P0
+ *             exactly, a partial overlap is KDN_ERR_INVALID_ARG)
+ *   beta_eff  [B,T,H] fp32, nullable: z / (r + z), z = k^T P^ k
+ * dk in {16, 32, 64}, dv in {16, 32, 64, 128}; fp32 arithmetic throughout.
+ */
+kdn_status kdn_dense_fwd(int B, int T, int H, int dk, int dv, int io_dtype, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* omega,
+                         const float* r, const float* S0, const float* P0, void* o, float* S_T,
+                         float* P_T, float* beta_eff, void* stream);
+
+/*
  * Gain scan alone (the variance recurrence and Kalman gain without the
  * memory), exposed for the chunk-parallel regime's tests and diagnostics.
  * Inputs as in the forward calls (q, v not needed).  Writes

@@ -135,6 +135,46 @@ def kdn_fwd_ex(variant: str, q, k, v, alpha, omega, r, S0=None, var0=None, mu=No
     return o, S_T, var_T, beta
 
 
+def kdn_dense_fwd(q, k, v, alpha, omega, r, S0=None, P0=None, want_beta_eff: bool = False,
+                  o=None, S_T=None, P_T=None):
+    """Exact dense-covariance Kalman memory with diag(alpha) / diag(omega)
+    gates, for small d_k.  Returns (o [B,T,H,dv], S_T [B,H,dk,dv],
+    P_T [B,H,dk,dk], beta_eff [B,T,H] or None)."""
+    L = _lib.lib()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    io = _io_code(q)
+    _need(q, "q", (B, T, H, dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, dv), q.dtype, dev)
+    _need(alpha, "alpha", (B, T, H, dk), torch.float32, dev)
+    _need(omega, "omega", (B, T, H, dk), torch.float32, dev)
+    _need(r, "r", (B, T, H), torch.float32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if P0 is not None:
+        _need(P0, "P0", (B, H, dk, dk), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", (B, T, H, dv), q.dtype, dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if P_T is None:
+        P_T = torch.empty((B, H, dk, dk), dtype=torch.float32, device=dev)
+    _need(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
+    _need(P_T, "P_T", (B, H, dk, dk), torch.float32, dev)
+    beta = torch.empty((B, T, H), dtype=torch.float32, device=dev) if want_beta_eff else None
+    with torch.cuda.device(dev):
+        st = L.kdn_dense_fwd(B, T, H, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                             _ptr(omega), _ptr(r), _ptr(S0), _ptr(P0), _ptr(o), _ptr(S_T),
+                             _ptr(P_T), _ptr(beta), _stream(dev))
+    _lib.check(st)
+    return o, S_T, P_T, beta
+
+
 def kdn_step(variant: str, q, k, v, alpha, omega, r, S, var_state, mu=None,
              o=None, mu_h=None, beta_eff=None) -> torch.Tensor:
     """One decode step; S [B,H,dk,dv] and var_state are updated in place.

@@ -281,6 +281,58 @@ kdn_status kdn_fwd_ex(int variant, int B, int T, int H, int dk, int dv, int io_d
                     S0, var0, o, S_T, var_T, workspace, workspace_bytes, stream, x);
 }
 
+kdn_status kdn_dense_fwd(int B, int T, int H, int dk, int dv, int io_dtype, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* omega,
+                         const float* r, const float* S0, const float* P0, void* o, float* S_T,
+                         float* P_T, float* beta_eff, void* stream)
+{
+    if (io_dtype != KDN_F32 && io_dtype != KDN_BF16)
+        return fail(KDN_ERR_INVALID_ARG, "io_dtype must be KDN_F32 (0) or KDN_BF16 (1), got %d",
+                    io_dtype);
+    if (B < 1 || H < 1 || T < 0)
+        return fail(KDN_ERR_INVALID_ARG, "need B >= 1, H >= 1, T >= 0 (got B=%d T=%d H=%d)", B, T, H);
+    if (dk != 16 && dk != 32 && dk != 64)
+        return fail(KDN_ERR_UNSUPPORTED, "dense filter supports dk in {16, 32, 64}, got %d", dk);
+    if (dv != 16 && dv != 32 && dv != 64 && dv != 128)
+        return fail(KDN_ERR_UNSUPPORTED, "dense filter supports dv in {16, 32, 64, 128}, got %d", dv);
+    if ((size_t)B * (size_t)(T > 0 ? T : 1) * H * (size_t)(dk > dv ? dk : dv) >= kMaxElems)
+        return fail(KDN_ERR_UNSUPPORTED, "tensor sizes must stay below 2^31 elements");
+    if (T > 0) {
+        KDN_REQUIRE(q, "q");
+        KDN_REQUIRE(k, "k");
+        KDN_REQUIRE(v, "v");
+        KDN_REQUIRE(alpha, "alpha");
+        KDN_REQUIRE(omega, "omega");
+        KDN_REQUIRE(r, "r");
+        KDN_REQUIRE(o, "o");
+    }
+    KDN_REQUIRE(S_T, "S_T");
+    KDN_REQUIRE(P_T, "P_T");
+    KDN_ALIGNED_X(S0, "S0");
+    KDN_ALIGNED_X(P0, "P0");
+    KDN_ALIGNED_X(S_T, "S_T");
+    KDN_ALIGNED_X(P_T, "P_T");
+    KDN_ALIGNED_X(beta_eff, "beta_eff");
+    if (o && (o == q || o == k || o == v))
+        return fail(KDN_ERR_INVALID_ARG, "o must not alias q, k or v");
+    auto overlap = [](const void* x, const void* y, size_t bytes) {
+        const char *a0 = (const char*)x, *a1 = (const char*)y;
+        return x && y && x != y && a0 < a1 + bytes && a1 < a0 + bytes;
+    };
+    if (overlap(S0, S_T, (size_t)B * H * dk * dv * sizeof(float)))
+        return fail(KDN_ERR_INVALID_ARG, "S_T must either equal S0 or not overlap it");
+    if (overlap(P0, P_T, (size_t)B * H * dk * dk * sizeof(float)))
+        return fail(KDN_ERR_INVALID_ARG, "P_T must either equal P0 or not overlap it");
+    if (beta_eff && (beta_eff == r || (void*)beta_eff == o || beta_eff == S_T || beta_eff == P_T))
+        return fail(KDN_ERR_INVALID_ARG, "beta_eff must not alias r, o, S_T or P_T");
+    kdn::DenseArgs a{q, k, v, alpha, omega, r, S0, P0, o, S_T, P_T, T > 0 ? beta_eff : nullptr,
+                     B, T, H, dk, dv};
+    hipError_t e = kdn::launch_dense_fwd(a, io_dtype, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 kdn_status kdn_step_ex(int variant, int B, int H, int dk, int dv, int io_dtype, float mu,
                        const float* mu_h, const void* q, const void* k, const void* v,
                        const float* alpha, const float* omega, const float* r, float* S,

@@ -42,6 +42,22 @@ struct StepArgs {
     float* beta;        // nullable [B,H]: effective write strength z / (r + z)
 };
 
+struct DenseArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* omega;  // [B,T,H,dk]: diagonal process noise
+    const float* r;
+    const float* S0;     // nullable
+    const float* P0;     // nullable [B,H,dk,dk]: identity when null
+    void* o;
+    float* S_T;
+    float* P_T;          // [B,H,dk,dk]
+    float* beta;         // nullable [B,T,H]
+    int B, T, H, dk, dv;
+};
+
 struct GainArgs {
     const void* k;
     const float* alpha;
@@ -61,6 +77,7 @@ struct GainArgs {
 hipError_t launch_walk_fwd(const FwdArgs& a, bool iso, hipStream_t stream);
 hipError_t launch_chunk_fwd_f32(const FwdArgs& a, bool iso, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, bool iso, int io_dtype, hipStream_t stream);
+hipError_t launch_dense_fwd(const DenseArgs& a, int io_dtype, hipStream_t stream);
 size_t gain_workspace_floats(bool iso, int B, int T, int H, int dk);
 hipError_t launch_gain_scan(const GainArgs& a, bool iso, int io_dtype, hipStream_t stream);
 

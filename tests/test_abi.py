@@ -215,3 +215,26 @@ def test_step_ex_validation(L):
     assert step(beta=P + 8192) == -1 and "beta_eff" in L.kdn_last_error_message().decode()
     assert step(mu_h=P + 1) == -1 and "mu_h" in L.kdn_last_error_message().decode()
     assert step(dv=96) == -2
+
+
+@cpu_only
+def test_dense_fwd_validation(L):
+    def dense(**kw):
+        a = dict(B=1, T=32, H=2, dk=32, dv=64, io=0, q=P, k=P, v=P, alpha=P, omega=P, r=P,
+                 S0=None, P0=None, o=P + 4096, S_T=P + 8192, P_T=P + 65536, beta=None)
+        a.update(kw)
+        return L.kdn_dense_fwd(a["B"], a["T"], a["H"], a["dk"], a["dv"], a["io"], a["q"], a["k"],
+                               a["v"], a["alpha"], a["omega"], a["r"], a["S0"], a["P0"], a["o"],
+                               a["S_T"], a["P_T"], a["beta"], None)
+    msg = lambda: L.kdn_last_error_message().decode()
+    assert dense(dk=128) == -2 and "dk" in msg()
+    assert dense(dv=96) == -2 and "dv" in msg()
+    assert dense(io=3) == -1 and "io_dtype" in msg()
+    assert dense(T=-1) == -1
+    assert dense(q=None) == -1 and "q must not be NULL" in msg()
+    assert dense(P_T=None) == -1 and "P_T" in msg()
+    assert dense(P0=P + 65536 + 64) == -1 and "P_T must either equal P0" in msg()
+    assert dense(S0=P + 8192 + 4) == -1 and "S_T must either equal S0" in msg()
+    assert dense(o=P) == -1 and "alias" in msg()
+    assert dense(beta=P + 4096) == -1 and "beta_eff" in msg()
+    assert dense(S_T=P + 2) == -1 and "aligned" in msg()
