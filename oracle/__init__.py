@@ -10,6 +10,9 @@ Contents
   Diagonal and Isotropic KDN, in plain C (``kdn_oracle.c``), fp64, one
   independent problem per (batch, head).  See that file for the equations and
   their citations (KDN reading notes, method part, §2, §4, §5, §7).
+* ``bwd`` -- the backward pass of both recurrences (reverse-mode derivative,
+  derived in ``kdn_oracle.c`` since the notes print no gradient formulas;
+  pinned in the tests against finite differences of the forward).
 * ``dense_kf`` -- the exact dense-covariance Kalman memory (KDN reading notes,
   method part §2, Eq. (12)-(17)); numpy, fp64, for tiny d_k only.
 * ``mobius_factors`` / ``mobius_fold_left`` / ``mobius_fold_tree`` /
@@ -63,6 +66,9 @@ def _load():
             fn.restype = ctypes.c_int
             fn.argtypes = ([ctypes.c_int] * 5 + [dp] * 9 + [ctypes.c_double]
                            + [dp] * 7 + [ctypes.c_int])
+        lib.kdn_oracle_bwd.restype = ctypes.c_int
+        lib.kdn_oracle_bwd.argtypes = ([ctypes.c_int] * 6 + [dp] * 9 + [ctypes.c_double]
+                                       + [dp] * 13 + [ctypes.c_int])
         lib.kdn_oracle_max_threads.restype = ctypes.c_int
         lib.kdn_oracle_max_threads.argtypes = []
         _lib = lib
@@ -202,6 +208,47 @@ def step(variant: str, q, k, v, alpha, omega, r, S, var, mu=None, mu_h=None) -> 
         return {"o": out["o"][:, 0], "S": out["S"], "var": out["b"],
                 "beta_eff": out["beta_eff"][:, 0]}
     raise ValueError("variant must be 'diag' or 'iso'")
+
+
+def bwd(variant: str, q, k, v, alpha, omega, r, do, S0=None, var0=None, mu=None,
+        mu_h=None, c0_h=None, dS_T=None, dvar_T=None, nthreads: int = 0) -> dict:
+    """Backward of ``diag_fwd`` / ``iso_fwd`` for the loss
+    L = sum(do * o) + sum(dS_T * S_T) + sum(dvar_T * var_T).
+
+    Forward arguments as in those calls (var0 = p0 or b0); do has o's shape,
+    dS_T and dvar_T default to zero.  Returns dq, dk, dv, dalpha, domega, dr
+    (the shapes of the inputs), dS0, dvar0 (shape of the initial variance, also
+    when it came from c0_h or the default) and dmu [B,H], the derivative by the
+    information scale that (b,h) used.
+    """
+    if variant not in ("diag", "iso"):
+        raise ValueError("variant must be 'diag' or 'iso'")
+    iso = variant == "iso"
+    q, k, v, alpha, omega, r, do = map(_f64, (q, k, v, alpha, omega, r, do))
+    S0, var0, dS_T, dvar_T = map(_f64, (S0, var0, dS_T, dvar_T))
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    var_shape = (B, H) if iso else (B, H, dk)
+    assert q.shape == k.shape == alpha.shape and v.shape == do.shape == (B, T, H, dv)
+    assert omega.shape == ((B, T, H) if iso else (B, T, H, dk)) and r.shape == (B, T, H)
+    for x, shp in ((S0, (B, H, dk, dv)), (dS_T, (B, H, dk, dv)), (var0, var_shape),
+                   (dvar_T, var_shape)):
+        assert x is None or x.shape == shp
+    mu = float(dk if mu is None else mu)
+    mu_h, c0_h = _head_vec(mu_h, H), _head_vec(c0_h, H)
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
+           "dalpha": np.zeros_like(alpha), "domega": np.zeros_like(omega),
+           "dr": np.zeros_like(r), "dS0": np.zeros((B, H, dk, dv)),
+           "dvar0": np.zeros(var_shape), "dmu": np.zeros((B, H))}
+    rc = _load().kdn_oracle_bwd(
+        int(iso), B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r),
+        _ptr(S0), _ptr(var0), _ptr(c0_h), mu, _ptr(mu_h), _ptr(do), _ptr(dS_T), _ptr(dvar_T),
+        *[_ptr(out[n]) for n in ("dq", "dk", "dv", "dalpha", "domega", "dr", "dS0", "dvar0",
+                                 "dmu")],
+        int(nthreads))
+    if rc != 0:
+        raise RuntimeError("kdn_oracle_bwd failed (%d)" % rc)
+    return out
 
 
 # --------------------------------------------------------------------------
