@@ -197,6 +197,40 @@ kdn_status kdn_dense_fwd(int B, int T, int H, int dk, int dv, int io_dtype, cons
                          float* P_T, float* beta_eff, void* stream);
 
 /*
+ * Backward pass of Diagonal / Isotropic KDN (the mixer is trained through the
+ * scanned recurrence, KDN reading notes, method part §8; the notes print no
+ * gradient formulas, so this is the reverse-mode derivative of the
+ * recurrences of method part §2, §4-§5 and §7, including the information-
+ * scaled variance update).  It returns the gradients of a loss L given
+ *   d_o     [B,T,H,dv] io dtype: dL/do
+ *   dS_T    [B,H,dk,dv] fp32, nullable (zero): dL/dS_T
+ *   dvar_T  shape of var0, fp32, nullable (zero): dL/dp_T or dL/db_T
+ * for the forward defined by the same arguments as kdn_fwd_ex (variant,
+ * sizes, io_dtype, mu, mu_h, q, k, v, alpha, omega, r, S0, var0, c0_h).
+ * Outputs (device, written in full; none may overlap any other buffer):
+ *   dq, dk [B,T,H,dk] and dv [B,T,H,dv] in the io dtype
+ *   dalpha [B,T,H,dk], domega (the shape of omega), dr [B,T,H] fp32
+ *   dS0 [B,H,dk,dv], dvar0 (shape of var0), dmu [B,H] fp32, each nullable:
+ *     the gradients by the initial state, the initial variance (also when it
+ *     came from c0_h or the default 1; dL/dc0_h sums it over b and, for
+ *     Diagonal, channels) and by the information scale each (b,h) used
+ *     (dL/dmu_h sums it over b)
+ * dk in {64, 128}, dv a multiple of 16 up to 256; fp32 arithmetic whatever
+ * the io type.  The forward is recomputed inside (the gain, then the state
+ * at every 16th token); the workspace (kdn_bwd_workspace_size bytes,
+ * 16-byte aligned) holds that and per-block partial sums.  Asynchronous on
+ * `stream`; validation as for the forward.
+ */
+size_t kdn_bwd_workspace_size(int variant, int B, int T, int H, int dk, int dv);
+kdn_status kdn_bwd(int variant, int B, int T, int H, int dk, int dv, int io_dtype, float mu,
+                   const float* mu_h, const void* q, const void* k, const void* v,
+                   const float* alpha, const float* omega, const float* r, const float* S0,
+                   const float* var0, const float* c0_h, const void* d_o, const float* dS_T,
+                   const float* dvar_T, void* dq, void* dk_out, void* dv_out, float* dalpha,
+                   float* domega, float* dr, float* dS0, float* dvar0, float* dmu,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Gain scan alone (the variance recurrence and Kalman gain without the
  * memory), exposed for the chunk-parallel regime's tests and diagnostics.
  * Inputs as in the forward calls (q, v not needed).  Writes

@@ -12,6 +12,9 @@ from .api import (  # noqa: F401
     KDN_ISO,
     KdnError,
     kdn_diag_fwd,
+    kdn_bwd,
+    kdn_dense_fwd,
+    kdn_fwd_ex,
     kdn_fwd_workspace_size,
     kdn_gain_scan,
     kdn_iso_fwd,
@@ -23,6 +26,9 @@ __all__ = [
     "kdn_diag_fwd",
     "kdn_iso_fwd",
     "kdn_step",
+    "kdn_fwd_ex",
+    "kdn_dense_fwd",
+    "kdn_bwd",
     "kdn_gain_scan",
     "kdn_fwd_workspace_size",
     "kdn_version",

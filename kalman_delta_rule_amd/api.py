@@ -175,6 +175,58 @@ def kdn_dense_fwd(q, k, v, alpha, omega, r, S0=None, P0=None, want_beta_eff: boo
     return o, S_T, P_T, beta
 
 
+def kdn_bwd(variant: str, q, k, v, alpha, omega, r, d_o, S0=None, var0=None, mu=None,
+            mu_h=None, c0_h=None, dS_T=None, dvar_T=None, want_state_grads: bool = True,
+            workspace=None) -> dict:
+    """Backward pass of the forward given by the same arguments (see kdn_fwd_ex)
+    for dL/do = d_o, dL/dS_T = dS_T and dL/dvar_T = dvar_T (both optional).
+    Returns a dict with dq, dk, dv (io dtype), dalpha, domega, dr (fp32) and,
+    with ``want_state_grads``, dS0, dvar0 and dmu [B,H] (fp32)."""
+    L = _lib.lib()
+    var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    io = _io_code(q)
+    iso = var == KDN_ISO
+    var_shape = (B, H) if iso else (B, H, dk)
+    f32 = torch.float32
+    _need(q, "q", (B, T, H, dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, dv), q.dtype, dev)
+    _need(d_o, "d_o", (B, T, H, dv), q.dtype, dev)
+    _need(alpha, "alpha", (B, T, H, dk), f32, dev)
+    _need(omega, "omega", (B, T, H) if iso else (B, T, H, dk), f32, dev)
+    _need(r, "r", (B, T, H), f32, dev)
+    for t, n, shp in ((S0, "S0", (B, H, dk, dv)), (dS_T, "dS_T", (B, H, dk, dv)),
+                      (var0, "var0", var_shape), (dvar_T, "dvar_T", var_shape),
+                      (mu_h, "mu_h", (H,)), (c0_h, "c0_h", (H,))):
+        if t is not None:
+            _need(t, n, shp, f32, dev)
+    mu = float(dk if mu is None else mu)
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+         "dalpha": torch.empty_like(alpha), "domega": torch.empty_like(omega),
+         "dr": torch.empty_like(r)}
+    if want_state_grads:
+        g["dS0"] = torch.empty((B, H, dk, dv), dtype=f32, device=dev)
+        g["dvar0"] = torch.empty(var_shape, dtype=f32, device=dev)
+        g["dmu"] = torch.empty((B, H), dtype=f32, device=dev)
+    need = int(L.kdn_bwd_workspace_size(var, B, T, H, dk, dv))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = L.kdn_bwd(var, B, T, H, dk, dv, io, mu, _ptr(mu_h), _ptr(q), _ptr(k), _ptr(v),
+                       _ptr(alpha), _ptr(omega), _ptr(r), _ptr(S0), _ptr(var0), _ptr(c0_h),
+                       _ptr(d_o), _ptr(dS_T), _ptr(dvar_T), _ptr(g["dq"]), _ptr(g["dk"]),
+                       _ptr(g["dv"]), _ptr(g["dalpha"]), _ptr(g["domega"]), _ptr(g["dr"]),
+                       _ptr(g.get("dS0")), _ptr(g.get("dvar0")), _ptr(g.get("dmu")),
+                       _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check(st)
+    return g
+
+
 def kdn_step(variant: str, q, k, v, alpha, omega, r, S, var_state, mu=None,
              o=None, mu_h=None, beta_eff=None) -> torch.Tensor:
     """One decode step; S [B,H,dk,dv] and var_state are updated in place.

@@ -333,6 +333,126 @@ kdn_status kdn_dense_fwd(int B, int T, int H, int dk, int dv, int io_dtype, cons
     return ok();
 }
 
+size_t kdn_bwd_workspace_size(int variant, int B, int T, int H, int dk, int dv)
+{
+    if ((variant != KDN_DIAG && variant != KDN_ISO) || B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1)
+        return 0;
+    return kdn::bwd_workspace_floats(variant == KDN_ISO, B, T, H, dk, dv) * sizeof(float);
+}
+
+kdn_status kdn_bwd(int variant, int B, int T, int H, int dk, int dv, int io_dtype, float mu,
+                   const float* mu_h, const void* q, const void* k, const void* v,
+                   const float* alpha, const float* omega, const float* r, const float* S0,
+                   const float* var0, const float* c0_h, const void* d_o, const float* dS_T,
+                   const float* dvar_T, void* dq, void* dk_out, void* dv_out, float* dalpha,
+                   float* domega, float* dr, float* dS0, float* dvar0, float* dmu,
+                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (variant != KDN_DIAG && variant != KDN_ISO)
+        return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
+                    variant);
+    if (io_dtype != KDN_F32 && io_dtype != KDN_BF16)
+        return fail(KDN_ERR_INVALID_ARG, "io_dtype must be KDN_F32 (0) or KDN_BF16 (1), got %d",
+                    io_dtype);
+    if (B < 1 || H < 1 || T < 0)
+        return fail(KDN_ERR_INVALID_ARG, "need B >= 1, H >= 1, T >= 0 (got B=%d T=%d H=%d)", B, T, H);
+    if (!(mu >= 0.f) || mu > 3.0e38f)
+        return fail(KDN_ERR_INVALID_ARG, "mu must be finite and >= 0 (got %g)", (double)mu);
+    if (dk != 64 && dk != 128)
+        return fail(KDN_ERR_UNSUPPORTED, "backward supports dk in {64, 128}, got %d", dk);
+    if (dv < 16 || dv > 256 || dv % 16 != 0)
+        return fail(KDN_ERR_UNSUPPORTED, "backward supports dv a multiple of 16 up to 256, got %d", dv);
+    if ((size_t)B * (size_t)(T > 0 ? T : 1) * H * (size_t)(dk > dv ? dk : dv) >= kMaxElems)
+        return fail(KDN_ERR_UNSUPPORTED, "tensor sizes must stay below 2^31 elements");
+    const bool iso = variant == KDN_ISO;
+    if (var0 && c0_h)
+        return fail(KDN_ERR_INVALID_ARG, "give the initial variance either as var0 or as c0_h, not both");
+    if (T > 0) {
+        KDN_REQUIRE(q, "q");
+        KDN_REQUIRE(k, "k");
+        KDN_REQUIRE(v, "v");
+        KDN_REQUIRE(alpha, "alpha");
+        KDN_REQUIRE(omega, "omega");
+        KDN_REQUIRE(r, "r");
+        KDN_REQUIRE(d_o, "d_o");
+        KDN_REQUIRE(dq, "dq");
+        KDN_REQUIRE(dk_out, "dk");
+        KDN_REQUIRE(dv_out, "dv");
+        KDN_REQUIRE(dalpha, "dalpha");
+        KDN_REQUIRE(domega, "domega");
+        KDN_REQUIRE(dr, "dr");
+    }
+    const size_t es = io_dtype == KDN_BF16 ? 2 : 4;
+    const void* io_ptrs[] = {q, k, v, d_o, dq, dk_out, dv_out};
+    const char* io_names[] = {"q", "k", "v", "d_o", "dq", "dk", "dv"};
+    for (int i = 0; i < 7; ++i)
+        if ((uintptr_t)io_ptrs[i] % es)
+            return fail(KDN_ERR_INVALID_ARG, "%s must be aligned to its element size", io_names[i]);
+    KDN_ALIGNED_X(alpha, "alpha");
+    KDN_ALIGNED_X(omega, "omega");
+    KDN_ALIGNED_X(r, "r");
+    KDN_ALIGNED_X(S0, "S0");
+    KDN_ALIGNED_X(var0, "var0");
+    KDN_ALIGNED_X(c0_h, "c0_h");
+    KDN_ALIGNED_X(mu_h, "mu_h");
+    KDN_ALIGNED_X(dS_T, "dS_T");
+    KDN_ALIGNED_X(dvar_T, "dvar_T");
+    KDN_ALIGNED_X(dalpha, "dalpha");
+    KDN_ALIGNED_X(domega, "domega");
+    KDN_ALIGNED_X(dr, "dr");
+    KDN_ALIGNED_X(dS0, "dS0");
+    KDN_ALIGNED_X(dvar0, "dvar0");
+    KDN_ALIGNED_X(dmu, "dmu");
+    // every gradient output must be disjoint from every other buffer
+    const size_t ntok = (size_t)B * T * H, bh = (size_t)B * H;
+    const size_t nvar = iso ? bh : bh * dk;
+    struct Buf { const void* p; size_t n; const char* name; bool out; };
+    const Buf bufs[] = {
+        {q, ntok * dk * es, "q", false}, {k, ntok * dk * es, "k", false},
+        {v, ntok * dv * es, "v", false}, {alpha, ntok * dk * 4, "alpha", false},
+        {omega, (iso ? ntok : ntok * dk) * 4, "omega", false}, {r, ntok * 4, "r", false},
+        {S0, bh * dk * dv * 4, "S0", false}, {var0, nvar * 4, "var0", false},
+        {c0_h, (size_t)H * 4, "c0_h", false}, {mu_h, (size_t)H * 4, "mu_h", false},
+        {d_o, ntok * dv * es, "d_o", false}, {dS_T, bh * dk * dv * 4, "dS_T", false},
+        {dvar_T, nvar * 4, "dvar_T", false}, {workspace, workspace_bytes, "workspace", false},
+        {dq, ntok * dk * es, "dq", true}, {dk_out, ntok * dk * es, "dk", true},
+        {dv_out, ntok * dv * es, "dv", true}, {dalpha, ntok * dk * 4, "dalpha", true},
+        {domega, (iso ? ntok : ntok * dk) * 4, "domega", true}, {dr, ntok * 4, "dr", true},
+        {dS0, bh * dk * dv * 4, "dS0", true}, {dvar0, nvar * 4, "dvar0", true},
+        {dmu, bh * 4, "dmu", true}};
+    const int nbufs = (int)(sizeof(bufs) / sizeof(bufs[0]));
+    for (int i = 0; i < nbufs; ++i) {
+        if (!bufs[i].out || !bufs[i].p || !bufs[i].n)
+            continue;
+        for (int j = 0; j < nbufs; ++j) {
+            if (j == i || !bufs[j].p || !bufs[j].n)
+                continue;
+            const char *a0 = (const char*)bufs[i].p, *a1 = (const char*)bufs[j].p;
+            if (a0 < a1 + bufs[j].n && a1 < a0 + bufs[i].n)
+                return fail(KDN_ERR_INVALID_ARG, "%s must not overlap %s", bufs[i].name,
+                            bufs[j].name);
+        }
+    }
+    const size_t need = kdn::bwd_workspace_floats(iso, B, T, H, dk, dv) * sizeof(float);
+    if (workspace_bytes < need || (need && !workspace))
+        return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                    workspace_bytes);
+    if ((uintptr_t)workspace % 16)
+        return fail(KDN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    kdn::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.omega = omega; a.r = r;
+    a.S0 = S0; a.var0 = var0; a.c0 = c0_h; a.mu_h = mu_h; a.mu = mu;
+    a.go = d_o; a.gS_T = dS_T; a.gvar_T = dvar_T;
+    a.gq = dq; a.gk = dk_out; a.gv = dv_out; a.galpha = dalpha; a.gomega = domega; a.gr = dr;
+    a.gS0 = dS0; a.gvar0 = dvar0; a.gmu = dmu;
+    a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
+    kdn::bwd_carve_workspace(a, iso, static_cast<float*>(workspace));
+    hipError_t e = kdn::launch_bwd(a, iso, io_dtype, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 kdn_status kdn_step_ex(int variant, int B, int H, int dk, int dv, int io_dtype, float mu,
                        const float* mu_h, const void* q, const void* k, const void* v,
                        const float* alpha, const float* omega, const float* r, float* S,

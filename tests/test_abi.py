@@ -238,3 +238,51 @@ def test_dense_fwd_validation(L):
     assert dense(o=P) == -1 and "alias" in msg()
     assert dense(beta=P + 4096) == -1 and "beta_eff" in msg()
     assert dense(S_T=P + 2) == -1 and "aligned" in msg()
+
+
+def test_bwd_validation(L):
+    G = 1 << 28  # every buffer in its own region, far apart
+    names = ["q", "k", "v", "alpha", "omega", "r", "S0", "var0", "c0", "d_o", "dS_T", "dvar_T",
+             "dq", "gk", "gv", "dalpha", "domega", "dr", "dS0", "dvar0", "dmu", "ws"]
+    base = {n: P + (i + 1) * G for i, n in enumerate(names)}
+
+    def bwd(**kw):
+        a = dict(variant=0, B=1, T=40, H=2, dk=128, dv=64, io=1, mu=128.0, mu_h=None)
+        a.update({n: base[n] for n in names})
+        a.update(S0=None, var0=None, c0=None, dS_T=None, dvar_T=None)
+        a.update(kw)
+        ws_bytes = a.pop("ws_bytes", L.kdn_bwd_workspace_size(a["variant"], a["B"], a["T"],
+                                                              a["H"], a["dk"], a["dv"]))
+        return L.kdn_bwd(a["variant"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["io"], a["mu"],
+                         a["mu_h"], a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"],
+                         a["S0"], a["var0"], a["c0"], a["d_o"], a["dS_T"], a["dvar_T"], a["dq"],
+                         a["gk"], a["gv"], a["dalpha"], a["domega"], a["dr"], a["dS0"],
+                         a["dvar0"], a["dmu"], a["ws"], ws_bytes, None)
+    msg = lambda: L.kdn_last_error_message().decode()
+    assert bwd(variant=2) == -1 and "variant" in msg()
+    assert bwd(io=2) == -1 and "io_dtype" in msg()
+    assert bwd(dk=32) == -2 and "dk" in msg()
+    assert bwd(dv=40) == -2 and "dv" in msg()
+    assert bwd(dv=272) == -2
+    assert bwd(mu=-1.0) == -1 and "mu" in msg()
+    assert bwd(q=None) == -1 and "q must not be NULL" in msg()
+    assert bwd(d_o=None) == -1 and "d_o" in msg()
+    assert bwd(dalpha=None) == -1 and "dalpha" in msg()
+    assert bwd(var0=base["var0"], c0=base["c0"]) == -1 and "either" in msg()
+    assert bwd(dq=base["dq"] + 1) == -1 and "aligned" in msg()
+    assert bwd(dr=base["dr"] + 2) == -1 and "aligned" in msg()
+    assert bwd(dq=base["q"]) == -1 and "dq must not overlap q" in msg()
+    assert bwd(dS0=base["ws"] + 64) == -1 and "overlap" in msg()
+    assert bwd(dv=64, dmu=base["dalpha"] + 4) == -1 and "overlap" in msg()
+    assert bwd(ws_bytes=16) == -3 and "workspace" in msg()
+    assert bwd(ws=base["ws"] + 4) == -1 and "16-byte" in msg()
+    # workspace: gain pieces, the state every 16th token, 4 partial row sums
+    # per 16-column block
+    B, T, H, dk, dv = 2, 40, 3, 128, 64
+    ntok, nch, nblk = B * T * H, 3, dv // 16
+    r64 = lambda n: (n + 63) // 64 * 64
+    diag = 2 * r64(ntok * dk) + r64(ntok) + r64(B * H * nch * dk * dv) + r64(4 * nblk * ntok * dk)
+    iso = r64(ntok * 4) + r64(B * H * nch * dk * dv) + r64(4 * nblk * ntok * dk)
+    assert L.kdn_bwd_workspace_size(0, B, T, H, dk, dv) == 4 * diag
+    assert L.kdn_bwd_workspace_size(1, B, T, H, dk, dv) == 4 * iso
+    assert L.kdn_bwd_workspace_size(0, B, 0, H, dk, dv) == 0

@@ -1,0 +1,132 @@
+"""GPU parity of the backward pass (kdn_bwd) against the oracle's backward
+(``oracle.bwd``, the reverse-mode derivative of the recurrences of the KDN
+reading notes, method part §2, §4-§5 and §7, pinned to finite differences of
+the oracle forward) on identical seeded inputs.
+
+Every gradient -- dq, dk, dv, dalpha, domega, dr, dS0, dvar0, dmu -- is
+compared whole, by relative L2: <= 1e-4 with fp32 q/k/v/do, <= 2e-2 with
+bf16 (the kernels compute in fp32 either way; bf16 rounds the dq, dk, dv
+outputs).  Shapes span several 16-token recompute chunks with a ragged last
+chunk, one to sixteen 16-column value blocks, both key widths, and the
+initial state, variance and final-state gradients given or absent.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kalman_delta_rule_amd import api, inputs
+from kdn_testutil import TOL, host, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a HIP GPU")
+    torch.cuda.init()
+
+
+def _case(variant, io, B, T, H, dk, dv, seed, full_state=True):
+    w = inputs.Workload("t", variant, io, B, H, T, dk, dv, seed=seed)
+    x = dict(inputs.make_fwd_inputs(w))
+    for n in ("S0", "p0", "b0"):
+        x.pop(n, None)
+    rng = np.random.default_rng(seed + 1)
+    do = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    if io == "bf16":
+        do = inputs.round_bf16(do)
+    x["do"] = do
+    var_shape = (B, H) if variant == "iso" else (B, H, dk)
+    if full_state:
+        x["S0"] = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+        x["var0"] = rng.uniform(0.2, 1.5, var_shape).astype(np.float32)
+        x["dS_T"] = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+        x["dvar_T"] = rng.standard_normal(var_shape).astype(np.float32)
+    return x
+
+
+def _dev(x, io):
+    out = {}
+    for n, a in x.items():
+        if a is None:
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if n in ("q", "k", "v", "do") and io == "bf16":
+            t = t.to(torch.bfloat16)
+        out[n] = t.cuda()
+    return out
+
+
+def _run(variant, io, x, mu=None, mu_h=None, c0_h=None):
+    d = _dev(x, io)
+    g = api.kdn_bwd(variant, d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], d["do"],
+                    S0=d.get("S0"), var0=d.get("var0"), mu=mu,
+                    mu_h=None if mu_h is None else torch.from_numpy(mu_h).cuda(),
+                    c0_h=None if c0_h is None else torch.from_numpy(c0_h).cuda(),
+                    dS_T=d.get("dS_T"), dvar_T=d.get("dvar_T"))
+    torch.cuda.synchronize()
+    return {n: host(t) for n, t in g.items()}
+
+
+def _oracle(ora, variant, x, mu=None, mu_h=None, c0_h=None):
+    f = lambda n: None if x.get(n) is None else np.asarray(x[n], dtype=np.float64)
+    return ora.bwd(variant, f("q"), f("k"), f("v"), f("alpha"), f("omega"), f("r"), f("do"),
+                   S0=f("S0"), var0=f("var0"), mu=mu, mu_h=f_or(mu_h), c0_h=f_or(c0_h),
+                   dS_T=f("dS_T"), dvar_T=f("dvar_T"))
+
+
+def f_or(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def _check(g, ref, io, tag):
+    err = {n: rel_l2(g[n], ref[n]) for n in ("dq", "dk", "dv", "dalpha", "domega", "dr",
+                                             "dS0", "dvar0", "dmu")}
+    print("bwd %s errors %s" % (tag, {n: "%.2e" % e for n, e in err.items()}), flush=True)
+    assert max(err.values()) <= TOL[io], err
+
+
+CASES = [
+    # (variant, io, B, T, H, dk, dv)
+    ("diag", "f32", 1, 37, 2, 64, 32),
+    ("iso", "f32", 1, 50, 2, 128, 64),
+    ("diag", "f32", 2, 64, 1, 128, 16),
+    ("diag", "bf16", 2, 100, 2, 128, 128),
+    ("iso", "bf16", 1, 90, 3, 128, 128),
+    ("diag", "bf16", 1, 70, 2, 64, 64),
+    ("iso", "bf16", 1, 33, 2, 64, 256),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-%s-B%dT%dH%ddk%ddv%d" % c)
+def test_bwd_matches_oracle(ora, case):
+    variant, io, B, T, H, dk, dv = case
+    x = _case(variant, io, B, T, H, dk, dv, seed=500 + T + dv)
+    mu = 3.0 if variant == "diag" else None
+    _check(_run(variant, io, x, mu=mu), _oracle(ora, variant, x, mu=mu), io, case)
+
+
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+def test_bwd_per_head_mu_c0_without_state(ora, variant):
+    B, T, H, dk, dv = 2, 45, 3, 128, 32
+    x = _case(variant, "bf16", B, T, H, dk, dv, seed=611, full_state=False)
+    mu_h = np.array([1.0, 20.0, 256.0], dtype=np.float32)
+    c0_h = np.array([0.3, 1.0, 2.5], dtype=np.float32)
+    g = _run(variant, "bf16", x, mu_h=mu_h, c0_h=c0_h)
+    ref = _oracle(ora, variant, x, mu_h=mu_h, c0_h=c0_h)
+    _check(g, ref, "bf16", (variant, "mu_h c0_h"))
+
+
+def test_bwd_empty_sequence_passes_adjoints_through():
+    B, H, dk, dv = 2, 2, 128, 64
+    z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt, device="cuda")
+    bf = torch.bfloat16
+    dS_T = torch.randn(B, H, dk, dv, device="cuda")
+    dp_T = torch.randn(B, H, dk, device="cuda")
+    g = api.kdn_bwd("diag", z(B, 0, H, dk, dt=bf), z(B, 0, H, dk, dt=bf), z(B, 0, H, dv, dt=bf),
+                    z(B, 0, H, dk), z(B, 0, H, dk), z(B, 0, H), z(B, 0, H, dv, dt=bf),
+                    dS_T=dS_T, dvar_T=dp_T)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dS0"], dS_T) and torch.equal(g["dvar0"], dp_T)
+    assert torch.equal(g["dmu"], torch.zeros_like(g["dmu"]))
