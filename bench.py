@@ -63,6 +63,19 @@ def alg_bytes_step(variant: str, B, H, dk, dv, s_io: int) -> int:
     return B * H * per_head
 
 
+def alg_bytes_bwd(variant: str, B, T, H, dk, dv, s_io: int) -> int:
+    """Algorithmic HBM bytes of one backward call: q, k, v and do read and dq,
+    dk, dv written in the io dtype; alpha, omega, r read and their gradients
+    written in fp32 (omega per channel for Diagonal, per token for Isotropic);
+    per head the initial-state, initial-variance and information-scale
+    gradients written.  The forward's recomputation and the workspace are the
+    implementation's, not the algorithm's."""
+    w = dk if variant == "diag" else 1
+    per_ht = (4 * dk + 3 * dv) * s_io + 2 * (dk + w) * 4 + 2 * 4
+    per_head = dk * dv * 4 + w * 4 + 4
+    return B * T * H * per_ht + B * H * per_head
+
+
 def fwd_kernel_name(io: str) -> str:
     """The kernel one forward call launches: bf16 io runs the walk kernel,
     fp32 io the fp32 chunk kernel."""
@@ -139,6 +152,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--variant", default=None, help="override: diag | iso")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (kdn_bwd) on the workload instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -182,6 +197,9 @@ def main():
 
     def step():
         fn(d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], o=o, S_T=S_T, **{vkw: var_T})
+
+    if args.bwd:
+        return bench_bwd(args, w, variant, d, io_dt)
 
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -238,6 +256,66 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": alg, "kernel": kname},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_bwd(args, w, variant, d, io_dt):
+    """Backward pass of the forward workload: kdn_bwd with a seeded dL/do and
+    no final-state gradient, its workspace allocated once outside the timed
+    region."""
+    import torch
+    from kalman_delta_rule_amd import _lib, api
+
+    dev = d["q"].device
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    gen = torch.Generator(device="cpu").manual_seed(w.seed + 77)
+    d_o = torch.randn((B, T, H, dv), generator=gen).to(io_dt).to(dev)
+    var = {"diag": 0, "iso": 1}[variant]
+    ws = torch.empty(max(int(_lib.lib().kdn_bwd_workspace_size(var, B, T, H, dk, dv)), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        api.kdn_bwd(variant, d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], d_o,
+                    workspace=ws)
+
+    print("[bench] backward warmup %d (workspace %.2f GB)" % (args.warmup, ws.numel() / 1e9),
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    s_io = 2 if w.io == "bf16" else 4
+    alg = alg_bytes_bwd(variant, B, T, H, dk, dv, s_io)
+    achieved = alg / (ms_step / 1e3) / 1e9
+    line = {
+        "metric": "KDN mixer bwd tokens/sec at T=%d (1 GPU)" % T,
+        "value": B * T * args.steps / (ms_step * args.steps / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "variant": variant, "B": B, "T": T, "H": H, "dk": dk,
+                   "dv": dv, "io": w.io, "pass": "backward"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": alg,
+                     "kernel": "kdn_bwd_gain_fwd + kdn_bwd_mem + kdn_bwd_gain_rev"},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

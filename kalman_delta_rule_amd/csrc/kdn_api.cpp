@@ -383,12 +383,17 @@ kdn_status kdn_bwd(int variant, int B, int T, int H, int dk, int dv, int io_dtyp
         KDN_REQUIRE(dr, "dr");
     }
     const size_t es = io_dtype == KDN_BF16 ? 2 : 4;
-    const void* io_ptrs[] = {q, k, v, d_o, dq, dk_out, dv_out};
-    const char* io_names[] = {"q", "k", "v", "d_o", "dq", "dk", "dv"};
-    for (int i = 0; i < 7; ++i)
+    // inputs are staged with 16-byte copies
+    KDN_ALIGNED(q, "q");
+    KDN_ALIGNED(k, "k");
+    KDN_ALIGNED(v, "v");
+    KDN_ALIGNED(d_o, "d_o");
+    KDN_ALIGNED(alpha, "alpha");
+    const void* io_ptrs[] = {dq, dk_out, dv_out};
+    const char* io_names[] = {"dq", "dk", "dv"};
+    for (int i = 0; i < 3; ++i)
         if ((uintptr_t)io_ptrs[i] % es)
             return fail(KDN_ERR_INVALID_ARG, "%s must be aligned to its element size", io_names[i]);
-    KDN_ALIGNED_X(alpha, "alpha");
     KDN_ALIGNED_X(omega, "omega");
     KDN_ALIGNED_X(r, "r");
     KDN_ALIGNED_X(S0, "S0");

@@ -38,87 +38,328 @@ namespace kdn {
 constexpr int BWD_L = 16;    // tokens per recompute chunk (checkpoint spacing)
 constexpr int BWD_COLS = 16; // value columns per memory workgroup
 
-__device__ __forceinline__ float wave_sum(float x)
+// Lane exchanges in the vector ALU (no LDS round trip).  xor_lane<M>(x) is
+// x of lane l ^ M, for M = 1, 2 (quad permutes) and 4, 8 (a row shift one way
+// for the lanes whose bit M is clear, the other way for the rest, chosen by
+// the bank mask: banks are the four 4-lane groups of a 16-lane row).
+// add_xor<M>(x) = x + (x of lane l ^ M); M = 16 and 32 use gfx950's row-pair
+// and half swaps of two registers holding x, after which each lane holds its
+// own value in one register and its partner's in the other.  Every stage adds a pair commutatively, so a
+// butterfly leaves bitwise-identical sums in all lanes of a group.
+template <int CTRL, int BANK>
+__device__ __forceinline__ float dpp_sel(float old, float src)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        x += __shfl_xor(x, off);
-    return x;
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, src),
+                                                                 CTRL, 0xF, BANK, false));
 }
+
+template <int M>
+__device__ __forceinline__ float xor_lane(float x)
+{
+    if constexpr (M == 1)
+        return dpp_sel<0xB1, 0xF>(x, x);  // quad_perm [1,0,3,2]
+    else if constexpr (M == 2)
+        return dpp_sel<0x4E, 0xF>(x, x);  // quad_perm [2,3,0,1]
+    else if constexpr (M == 4)            // row_shl:4 on banks 0, 2; row_shr:4 on banks 1, 3
+        return dpp_sel<0x114, 0xA>(dpp_sel<0x104, 0x5>(x, x), x);
+    else                                  // row_shl:8 on banks 0, 1; row_shr:8 on banks 2, 3
+        return dpp_sel<0x118, 0xC>(dpp_sel<0x108, 0x3>(x, x), x);
+}
+
+template <int M>
+__device__ __forceinline__ float add_xor(float x)
+{
+    if constexpr (M <= 8) {
+        return x + xor_lane<M>(x);
+    } else {
+        // The swap writes both of its registers; it is issued from inline
+        // assembly because the compiler's builtin for it returns only the first
+        // one here.  The s_nop padding keeps it clear of any VALU hazard, since
+        // the compiler does not look inside the assembly.
+        float a = x, b = x;
+        if constexpr (M == 16)
+            asm volatile("s_nop 4\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 4"
+                         : "+v"(a), "+v"(b));
+        else
+            asm volatile("s_nop 4\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 4"
+                         : "+v"(a), "+v"(b));
+        return a + b;
+    }
+}
+
+// Sum over the lanes whose index differs in bits log2(LO) .. 5 (LO = 1: the
+// whole wave).
+template <int LO>
+__device__ __forceinline__ float sum_lanes_from(float x)
+{
+    if constexpr (LO <= 1)
+        x = add_xor<1>(x);
+    if constexpr (LO <= 2)
+        x = add_xor<2>(x);
+    if constexpr (LO <= 4)
+        x = add_xor<4>(x);
+    if constexpr (LO <= 8)
+        x = add_xor<8>(x);
+    if constexpr (LO <= 16)
+        x = add_xor<16>(x);
+    return add_xor<32>(x);
+}
+
+__device__ __forceinline__ float wave_sum(float x) { return sum_lanes_from<1>(x); }
 
 // ---------------------------------------------------------------------------
 // A: gain forward
 // ---------------------------------------------------------------------------
+constexpr int BWD_PF = 4;  // tokens of inputs in flight in the serial gain kernels
+
+// One token's gain inputs for this lane's channels (lane + 64 c).
+template <int CPL>
+struct GainIn {
+    float al[CPL], kk[CPL], om[CPL];  // om: Diagonal omega per channel
+    float r, omi;                     // omi: Isotropic omega per token
+};
+
 template <typename IO, bool ISO, int CPL>
-__global__ __launch_bounds__(64) void kdn_bwd_gain_fwd_kernel(BwdArgs a)
+__device__ __forceinline__ void gain_in_load(GainIn<CPL>& x, const BwdArgs& a, size_t tok,
+                                             int lane)
 {
     constexpr int DK = 64 * CPL;
+    const IO* kg = reinterpret_cast<const IO*>(a.k);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const size_t e = tok * DK + lane + 64 * c;
+        x.al[c] = a.alpha[e];
+        x.kk[c] = to_f32(kg[e]);
+        if constexpr (!ISO)
+            x.om[c] = a.omega[e];
+    }
+    x.r = a.r[tok];
+    if constexpr (ISO)
+        x.omi = a.omega[tok];
+}
+
+template <typename IO, bool ISO, int CPL>
+__global__ __launch_bounds__(64) void kdn_bwd_gain_fwd_kernel(BwdArgs args)
+{
+    constexpr int DK = 64 * CPL, D = BWD_PF;
+    const BwdArgs a = args;
     const int bh = blockIdx.x, H = a.H, T = a.T;
     const int b = bh / H, h = bh % H, lane = threadIdx.x;
     const float mu = a.mu_h ? a.mu_h[h] : a.mu;
-    const IO* kg = reinterpret_cast<const IO*>(a.k);
+    auto tok_of = [&](int t) __attribute__((always_inline)) { return ((size_t)b * T + t) * H + h; };
+    float p[CPL];
+    float bv = 0.f;
     if constexpr (!ISO) {
-        float p[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
             p[c] = a.var0 ? a.var0[(size_t)bh * DK + lane + 64 * c] : (a.c0 ? a.c0[h] : 1.f);
-        for (int t = 0; t < T; ++t) {
-            const size_t tok = ((size_t)b * T + t) * H + h;
-            const float rt = a.r[tok];
-            float ph[CPL], kk[CPL], zp = 0.f;
+    } else {
+        bv = a.var0 ? a.var0[bh] : (a.c0 ? a.c0[h] : 1.f);
+    }
+    auto step = [&](const GainIn<CPL>& x, int t) __attribute__((always_inline)) {
+        const size_t tok = tok_of(t);
+        if constexpr (!ISO) {
+            float ph[CPL], zp = 0.f;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const size_t e = tok * DK + lane + 64 * c;
-                const float al = a.alpha[e];
-                kk[c] = to_f32(kg[e]);
-                ph[c] = al * al * p[c] + a.omega[e];
-                zp += ph[c] * kk[c] * kk[c];
+                ph[c] = x.al[c] * x.al[c] * p[c] + x.om[c];
+                zp += ph[c] * x.kk[c] * x.kk[c];
             }
-            const float d = rt + wave_sum(zp);
+            const float d = x.r + wave_sum(zp);
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const size_t e = tok * DK + lane + 64 * c;
-                a.kap[e] = ph[c] * kk[c] / d;
+                a.kap[e] = ph[c] * x.kk[c] / d;
                 a.pprev[e] = p[c];
-                p[c] = ph[c] / (1.f + (mu / rt) * kk[c] * kk[c] * ph[c]);
+                p[c] = ph[c] / (1.f + (mu / x.r) * x.kk[c] * x.kk[c] * ph[c]);
             }
             if (lane == 0)
                 a.dd[tok] = d;
-        }
-    } else {
-        float bv = a.var0 ? a.var0[bh] : (a.c0 ? a.c0[h] : 1.f);
-        for (int t = 0; t < T; ++t) {
-            const size_t tok = ((size_t)b * T + t) * H + h;
-            const float rt = a.r[tok];
+        } else {
             float sa = 0.f, sn = 0.f;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const size_t e = tok * DK + lane + 64 * c;
-                const float al = a.alpha[e], kk = to_f32(kg[e]);
-                sa += al * al;
-                sn += kk * kk;
+                sa += x.al[c] * x.al[c];
+                sn += x.kk[c] * x.kk[c];
             }
             const float am = wave_sum(sa) / (float)DK, n = wave_sum(sn);
-            const float bhat = am * bv + a.omega[tok];
-            const float beta = bhat / (rt + bhat * n);
+            const float bhat = am * bv + x.omi;
+            const float beta = bhat / (x.r + bhat * n);
             if (lane == 0) {
                 float4 g = {beta, bv, am, n};
                 *reinterpret_cast<float4*>(a.gsc + tok * 4) = g;
             }
-            bv = bhat / (1.f + mu * n / ((float)DK * rt) * bhat);
+            bv = bhat / (1.f + mu * n / ((float)DK * x.r) * bhat);
         }
+    };
+    // groups of D tokens with the next group's inputs in flight, then a tail
+    GainIn<CPL> ring[D];
+    int t = 0;
+    if (T >= D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            gain_in_load<IO, ISO, CPL>(ring[j], a, tok_of(j), lane);
+    }
+    for (; t + D <= T; t += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const GainIn<CPL> cur = ring[j];
+            if (t + j + D < T)
+                gain_in_load<IO, ISO, CPL>(ring[j], a, tok_of(t + j + D), lane);
+            step(cur, t + j);
+        }
+    }
+    for (; t < T; ++t) {
+        GainIn<CPL> cur;
+        gain_in_load<IO, ISO, CPL>(cur, a, tok_of(t), lane);
+        step(cur, t);
     }
 }
 
 // ---------------------------------------------------------------------------
 // B: memory backward
 // ---------------------------------------------------------------------------
-template <typename IO, bool ISO, int DK>
-__global__ __launch_bounds__(256) void kdn_bwd_mem_kernel(BwdArgs a)
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Direct global -> LDS copy of 16 (4) bytes per lane: lane l's bytes from
+// its own global address land at LDS byte address lds + 16 l (4 l) (lds
+// uniform).  Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds)
 {
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(size_t)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds)
+{
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(size_t)lds, 4, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p)
+{
+    return (uint32_t)(size_t)(const lds_void_t*)p;
+}
+
+// A barrier that orders LDS only: global loads and stores stay in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Every copy and store this wave issued has completed, then a barrier: after
+// it, the whole workgroup's copies into LDS are visible.  The wait is the
+// builtin (not inline assembly) so the compiler's own counter model sees that
+// nothing is outstanding afterwards.
+__device__ __forceinline__ void copies_landed_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// One 16-token chunk of inputs, staged in LDS.  Rows past a ragged chunk's
+// end repeat its last row and are never read.
+template <typename IO, bool ISO, int DK>
+struct BwdStage {
+    float al[BWD_L * DK];                  // alpha
+    float kp[ISO ? BWD_L : BWD_L * DK];    // kappa (Diagonal) / beta (Isotropic)
+    IO kk[BWD_L * DK];                     // k
+    IO qq[BWD_L * DK];                     // q (reverse pass only)
+    IO vv[BWD_L * BWD_COLS];               // v, this block's columns
+    IO dd[BWD_L * BWD_COLS];               // dL/do, this block's columns (reverse only)
+};
+
+// Copies of one 16-token chunk into stage s: tok0 is the chunk's first token
+// index in [B,T,H] order (tokens step by H), rows past `last` repeat row
+// `last`.  Piece p of an array (16 bytes) is copied by thread p + off, whole
+// waves active or idle, so each wave's LDS base is uniform.
+struct StageSrc {
+    const float* alpha;
+    const float* kap;
+    const float* gsc;
+    const void* k;
+    const void* q;
+    const void* v;
+    const void* go;
+    int H, dv;
+};
+
+template <typename IO, bool ISO, int DK>
+__device__ __forceinline__ void bwd_stage_copy(BwdStage<IO, ISO, DK>& s, StageSrc a,
+                                               size_t tok0, int last, int blk, int tid,
+                                               bool rev)
+{
+    constexpr int L = BWD_L, EK = 16 / (int)sizeof(IO);
+    const int lane = tid & 63;
+    const size_t H = (size_t)a.H, dv = (size_t)a.dv;
+    // alpha (and Diagonal kappa): L * DK / 4 pieces
+#pragma unroll
+    for (int p0 = 0; p0 < L * DK / 4; p0 += 256) {
+        const int p = p0 + tid;
+        if (p < L * DK / 4) {
+            const int e = p * 4, tau = min(e / DK, last);
+            const size_t g = (tok0 + tau * H) * DK + e % DK;
+            const uint32_t off = (uint32_t)(p - lane) * 16u;
+            dma16(a.alpha + g, lds_u32(s.al) + off);
+            if constexpr (!ISO)
+                dma16(a.kap + g, lds_u32(s.kp) + off);
+        }
+    }
+    if constexpr (ISO) {
+        if (tid >= 192 && lane < L)
+            dma4(a.gsc + (tok0 + min(lane, last) * H) * 4, lds_u32(s.kp));
+    }
+    // k and q: L * DK / EK pieces
+    const IO* kg = reinterpret_cast<const IO*>(a.k);
+    const IO* qg = reinterpret_cast<const IO*>(a.q);
+#pragma unroll
+    for (int p0 = 0; p0 < L * DK / EK; p0 += 256) {
+        const int p = p0 + tid;
+        if (p < L * DK / EK) {
+            const int e = p * EK, tau = min(e / DK, last);
+            const size_t g = (tok0 + tau * H) * DK + e % DK;
+            const uint32_t off = (uint32_t)(p - lane) * 16u;
+            dma16(kg + g, lds_u32(s.kk) + off);
+            if (rev)
+                dma16(qg + g, lds_u32(s.qq) + off);
+        }
+    }
+    // v and dL/do, this block's columns: L * 16 / EK pieces (32 or 64), by
+    // the second and third waves
+    constexpr int PV = L * BWD_COLS / EK;
+    static_assert(PV <= 64, "one wave copies a chunk of v");
+    const int pv = tid - 64, pd = tid - 128;
+    if (pv >= 0 && pv < PV) {
+        const int e = pv * EK, tau = min(e / BWD_COLS, last);
+        const size_t g = (tok0 + tau * H) * dv + (size_t)blk * BWD_COLS + e % BWD_COLS;
+        dma16(reinterpret_cast<const IO*>(a.v) + g, lds_u32(s.vv));
+    }
+    if (rev && pd >= 0 && pd < PV) {
+        const int e = pd * EK, tau = min(e / BWD_COLS, last);
+        const size_t g = (tok0 + tau * H) * dv + (size_t)blk * BWD_COLS + e % BWD_COLS;
+        dma16(reinterpret_cast<const IO*>(a.go) + g, lds_u32(s.dd));
+    }
+}
+
+template <typename IO, bool ISO, int DK>
+__global__ __launch_bounds__(256) void kdn_bwd_mem_kernel(BwdArgs args)
+{
+    // kernel arguments copied to locals once: nothing below reads them through
+    // a pointer
+    const BwdArgs a = args;
+    const StageSrc src{a.alpha, a.kap, a.gsc, a.k, a.q, a.v, a.go, a.H, a.dv};
+    float* const part = a.part;
+    float* const ckpt = a.ckpt;
     constexpr int TPR = 256 / DK;        // threads per row of S
+    static_assert(TPR == 2 || TPR == 4, "row split");
     constexpr int CPT = BWD_COLS / TPR;  // columns per thread
     constexpr int L = BWD_L;
+    typedef BwdStage<IO, ISO, DK> Stage;
+    // Copies land in stL while the steps read stR; at each chunk boundary stL
+    // is moved to stR.  Two distinct arrays let the compiler see that the
+    // steps' LDS reads never depend on copies in flight, with one instance of
+    // the step code (the kernel's loops stay small for the instruction cache).
+    __shared__ __align__(16) Stage stL;
+    __shared__ __align__(16) Stage stR;
     __shared__ float red[2][4][BWD_COLS];
     __shared__ float dbuf[L][BWD_COLS];
 
@@ -131,91 +372,131 @@ __global__ __launch_bounds__(256) void kdn_bwd_mem_kernel(BwdArgs a)
     const int col0 = blk * BWD_COLS + cb;   // ... in the value dimension
     const int nch = (T + L - 1) / L;
     const size_t ntok = (size_t)a.B * T * H;
-    const IO* qg = reinterpret_cast<const IO*>(a.q);
-    const IO* kg = reinterpret_cast<const IO*>(a.k);
-    const IO* vg = reinterpret_cast<const IO*>(a.v);
-    const IO* dog = reinterpret_cast<const IO*>(a.go);
     IO* dvg = reinterpret_cast<IO*>(a.gv);
-    float* ck = a.ckpt + ((size_t)bh * nblk + blk) * nch * (DK * BWD_COLS) + row * BWD_COLS + cb;
+    float* ck = ckpt + ((size_t)bh * nblk + blk) * nch * (DK * BWD_COLS) + row * BWD_COLS + cb;
+    auto tok_of = [&](int t) __attribute__((always_inline)) { return ((size_t)b * T + t) * H + h; };
+
+    auto stage_copy = [&](Stage& st, int c, bool rev) __attribute__((always_inline)) {
+        bwd_stage_copy<IO, ISO, DK>(st, src, tok_of(c * L), min(L, T - c * L) - 1, blk, tid, rev);
+    };
 
     int slot = 0;
     // sum over all rows of the block, per column; every thread gets the sums
-    // of its CPT columns.  One barrier; the two LDS slots alternate so the
-    // next call's writes never meet this call's reads.
-    auto col_sum = [&](float (&x)[CPT]) {
+    // of its CPT columns.  The two LDS slots alternate so the next call's
+    // writes never meet this call's reads.
+    auto col_sum = [&](float (&x)[CPT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int off = TPR; off < 64; off <<= 1)
-#pragma unroll
-            for (int j = 0; j < CPT; ++j)
-                x[j] += __shfl_xor(x[j], off);
+        for (int j = 0; j < CPT; ++j)
+            x[j] = sum_lanes_from<TPR>(x[j]);
         if (lane < TPR)
 #pragma unroll
             for (int j = 0; j < CPT; ++j)
                 red[slot][wave][cb + j] = x[j];
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int j = 0; j < CPT; ++j)
             x[j] = red[slot][0][cb + j] + red[slot][1][cb + j] + red[slot][2][cb + j] +
                    red[slot][3][cb + j];
         slot ^= 1;
     };
-    auto row_sum = [&](float x) {
-#pragma unroll
-        for (int off = 1; off < TPR; off <<= 1)
-            x += __shfl_xor(x, off);
+    auto row_sum = [&](float x) __attribute__((always_inline)) {
+        x = add_xor<1>(x);
+        if constexpr (TPR == 4)
+            x = add_xor<2>(x);
         return x;
     };
-    auto gain = [&](size_t tok, float kk) {
+    auto gain = [&](const Stage& s, int tau, float kk) __attribute__((always_inline)) {
         if constexpr (ISO)
-            return a.gsc[tok * 4] * kk;
+            return s.kp[tau] * kk;
         else
-            return a.kap[tok * DK + row];
+            return s.kp[tau * DK + row];
     };
 
-    // forward pass: the state at every chunk start
+    // ---- forward pass: the state at every chunk start --------------------
     float s[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
         s[j] = a.S0 ? a.S0[((size_t)bh * DK + row) * dv + col0 + j] : 0.f;
-    for (int t = 0; t < T; ++t) {
-        if ((t & (L - 1)) == 0)
-#pragma unroll
-            for (int j = 0; j < CPT; ++j)
-                ck[(size_t)(t / L) * (DK * BWD_COLS) + j] = s[j];
-        const size_t tok = ((size_t)b * T + t) * H + h;
-        const float al = a.alpha[tok * DK + row], kk = to_f32(kg[tok * DK + row]);
-        const float kap = gain(tok, kk);
-        float x[CPT];
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            s[j] *= al;
-            x[j] = s[j] * kk;
+    // stL -> stR for the arrays a pass reads, 16 bytes per thread and step
+    auto move_stage = [&](bool rev) __attribute__((always_inline)) {
+        auto mv = [&](const void* src, void* dst, int bytes) __attribute__((always_inline)) {
+            const uint4* s4 = reinterpret_cast<const uint4*>(src);
+            uint4* d4 = reinterpret_cast<uint4*>(dst);
+            for (int i = tid; i < bytes / 16; i += 256)
+                d4[i] = s4[i];
+        };
+        mv(stL.al, stR.al, (int)sizeof(stL.al));
+        mv(stL.kp, stR.kp, (int)sizeof(stL.kp));
+        mv(stL.kk, stR.kk, (int)sizeof(stL.kk));
+        mv(stL.vv, stR.vv, (int)sizeof(stL.vv));
+        if (rev) {
+            mv(stL.qq, stR.qq, (int)sizeof(stL.qq));
+            mv(stL.dd, stR.dd, (int)sizeof(stL.dd));
         }
-        col_sum(x);
+    };
+    for (int c = 0; c < nch; ++c) {
+        if (c == 0)
+            stage_copy(stL, 0, false);
+        copies_landed_barrier();  // chunk c in stL; chunk c - 1's readers done with stR
+        move_stage(false);
+        lds_barrier();            // stR holds chunk c; stL is free
+        if (c + 1 < nch)
+            stage_copy(stL, c + 1, false);
+        const Stage& cur = stR;
 #pragma unroll
         for (int j = 0; j < CPT; ++j)
-            s[j] += kap * (to_f32(vg[tok * dv + col0 + j]) - x[j]);
+            ck[(size_t)c * (DK * BWD_COLS) + j] = s[j];
+        const int len = min(L, T - c * L);
+        for (int tau = 0; tau < len; ++tau) {
+            const float al = cur.al[tau * DK + row], kk = to_f32(cur.kk[tau * DK + row]);
+            const float kap = gain(cur, tau, kk);
+            float x[CPT];
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                s[j] *= al;
+                x[j] = s[j] * kk;
+            }
+            col_sum(x);
+#pragma unroll
+            for (int j = 0; j < CPT; ++j)
+                s[j] += kap * (to_f32(cur.vv[tau * BWD_COLS + cb + j]) - x[j]);
+        }
     }
-    __threadfence_block();  // this thread's checkpoint stores before its loads below
 
-    // reverse pass
-    float g[CPT];
+    // ---- reverse pass -----------------------------------------------------
+    float g[CPT], ckn[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
         g[j] = a.gS_T ? a.gS_T[((size_t)bh * DK + row) * dv + col0 + j] : 0.f;
     for (int c = nch - 1; c >= 0; --c) {
-        const int t0 = c * L, len = min(L, T - t0);
+        if (c == nch - 1) {
+            copies_landed_barrier();  // the forward pass's readers are done
+            stage_copy(stL, c, true);
+#pragma unroll
+            for (int j = 0; j < CPT; ++j)
+                ckn[j] = ck[(size_t)c * (DK * BWD_COLS) + j];
+        }
+        copies_landed_barrier();  // chunk c in stL, its checkpoint loaded
+        move_stage(true);
+        lds_barrier();
+        const Stage& cur = stR;
         float st[L + 1][CPT];
 #pragma unroll
         for (int j = 0; j < CPT; ++j)
-            st[0][j] = ck[(size_t)c * (DK * BWD_COLS) + j];
+            st[0][j] = ckn[j];
+        if (c > 0) {
+            stage_copy(stL, c - 1, true);
+#pragma unroll
+            for (int j = 0; j < CPT; ++j)
+                ckn[j] = ck[(size_t)(c - 1) * (DK * BWD_COLS) + j];
+        }
+        const int t0 = c * L, len = min(L, T - t0);
         // recompute the chunk's states and innovations
 #pragma unroll
         for (int tau = 0; tau < L; ++tau) {
             if (tau < len) {
-                const size_t tok = ((size_t)b * T + t0 + tau) * H + h;
-                const float al = a.alpha[tok * DK + row], kk = to_f32(kg[tok * DK + row]);
-                const float kap = gain(tok, kk);
+                const float al = cur.al[tau * DK + row], kk = to_f32(cur.kk[tau * DK + row]);
+                const float kap = gain(cur, tau, kk);
                 float x[CPT];
 #pragma unroll
                 for (int j = 0; j < CPT; ++j)
@@ -223,7 +504,7 @@ __global__ __launch_bounds__(256) void kdn_bwd_mem_kernel(BwdArgs a)
                 col_sum(x);
 #pragma unroll
                 for (int j = 0; j < CPT; ++j) {
-                    const float del = to_f32(vg[tok * dv + col0 + j]) - x[j];
+                    const float del = to_f32(cur.vv[tau * BWD_COLS + cb + j]) - x[j];
                     dbuf[tau][cb + j] = del;  // every row stores the same value
                     st[tau + 1][j] = al * st[tau][j] + kap * del;
                 }
@@ -233,15 +514,15 @@ __global__ __launch_bounds__(256) void kdn_bwd_mem_kernel(BwdArgs a)
 #pragma unroll
         for (int tau = L - 1; tau >= 0; --tau) {
             if (tau < len) {
-                const size_t tok = ((size_t)b * T + t0 + tau) * H + h;
-                const size_t e = tok * DK + row;
-                const float al = a.alpha[e], kk = to_f32(kg[e]), qq = to_f32(qg[e]);
-                const float kap = gain(tok, kk);
+                const size_t tok = tok_of(t0 + tau);
+                const float al = cur.al[tau * DK + row], kk = to_f32(cur.kk[tau * DK + row]);
+                const float qq = to_f32(cur.qq[tau * DK + row]);
+                const float kap = gain(cur, tau, kk);
                 float dov[CPT], y[CPT];
                 float sq = 0.f, sk = 0.f;
 #pragma unroll
                 for (int j = 0; j < CPT; ++j) {
-                    dov[j] = to_f32(dog[tok * dv + col0 + j]);
+                    dov[j] = to_f32(cur.dd[tau * BWD_COLS + cb + j]);
                     g[j] = fmaf(qq, dov[j], g[j]);               // readout o = S^T q
                     sq = fmaf(st[tau + 1][j], dov[j], sq);      // dq = S do
                     sk = fmaf(g[j], dbuf[tau][cb + j], sk);     // kapbar = G delta
@@ -265,7 +546,7 @@ __global__ __launch_bounds__(256) void kdn_bwd_mem_kernel(BwdArgs a)
                 skm = row_sum(skm);
                 sam = row_sum(sam);
                 if (cp == 0) {
-                    float* pp = a.part + ((size_t)blk * ntok + tok) * DK + row;
+                    float* pp = part + ((size_t)blk * ntok + tok) * DK + row;
                     const size_t kstride = (size_t)nblk * ntok * DK;
                     pp[0] = sq;
                     pp[kstride] = sk;
@@ -284,17 +565,94 @@ __global__ __launch_bounds__(256) void kdn_bwd_mem_kernel(BwdArgs a)
 // ---------------------------------------------------------------------------
 // C: gain backward
 // ---------------------------------------------------------------------------
+// Sum of the per-block partials, in parallel over every (token, channel):
+// writes dq and leaves kapbar, the memory's dk and its dalpha summed in the
+// first block's slot of each.
+template <typename IO, int DK>
+__global__ __launch_bounds__(256) void kdn_bwd_merge_kernel(BwdArgs args, int nblk)
+{
+    const BwdArgs a = args;
+    const size_t ntok = (size_t)a.B * a.T * a.H, n4 = ntok * DK / 4;
+    const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i4 >= n4)
+        return;
+    const size_t kstride4 = (size_t)nblk * n4;
+    const float4* p = reinterpret_cast<const float4*>(a.part) + i4;
+    float4 sum[4];
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd)
+        sum[kd] = p[kd * kstride4];
+    for (int bl = 1; bl < nblk; ++bl)
+#pragma unroll
+        for (int kd = 0; kd < 4; ++kd) {
+            const float4 x = p[kd * kstride4 + (size_t)bl * n4];
+            sum[kd].x += x.x;
+            sum[kd].y += x.y;
+            sum[kd].z += x.z;
+            sum[kd].w += x.w;
+        }
+    IO* dq = reinterpret_cast<IO*>(a.gq) + i4 * 4;
+    dq[0] = from_f32<IO>(sum[0].x);
+    dq[1] = from_f32<IO>(sum[0].y);
+    dq[2] = from_f32<IO>(sum[0].z);
+    dq[3] = from_f32<IO>(sum[0].w);
+    float4* w = reinterpret_cast<float4*>(a.part) + i4;
+#pragma unroll
+    for (int kd = 1; kd < 4; ++kd)
+        w[kd * kstride4] = sum[kd];
+}
+
+// One token's inputs of the variance recurrence's adjoint for this lane's
+// channels.
+template <int CPL>
+struct RevIn {
+    float kb[CPL], kmb[CPL], amb[CPL];  // summed kapbar, memory dk, memory dalpha
+    float kk[CPL], al[CPL];
+    float pp[CPL], om[CPL];             // Diagonal: p_{t-1}, omega
+    float r, d;                         // Diagonal: r + z
+    float4 gs;                          // Isotropic: beta, b_{t-1}, mean alpha^2, |k|^2
+    float omi;                          // Isotropic omega
+};
+
 template <typename IO, bool ISO, int CPL>
-__global__ __launch_bounds__(64) void kdn_bwd_gain_rev_kernel(BwdArgs a, int nblk)
+__device__ __forceinline__ void rev_in_load(RevIn<CPL>& x, const BwdArgs& a, size_t tok,
+                                            size_t kstride, int lane)
 {
     constexpr int DK = 64 * CPL;
+    const IO* kg = reinterpret_cast<const IO*>(a.k);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const size_t e = tok * DK + lane + 64 * c;
+        x.kb[c] = a.part[kstride + e];
+        x.kmb[c] = a.part[2 * kstride + e];
+        x.amb[c] = a.part[3 * kstride + e];
+        x.kk[c] = to_f32(kg[e]);
+        x.al[c] = a.alpha[e];
+        if constexpr (!ISO) {
+            x.pp[c] = a.pprev[e];
+            x.om[c] = a.omega[e];
+        }
+    }
+    x.r = a.r[tok];
+    if constexpr (!ISO) {
+        x.d = a.dd[tok];
+    } else {
+        x.gs = *reinterpret_cast<const float4*>(a.gsc + tok * 4);
+        x.omi = a.omega[tok];
+    }
+}
+
+template <typename IO, bool ISO, int CPL>
+__global__ __launch_bounds__(64) void kdn_bwd_gain_rev_kernel(BwdArgs args, int nblk)
+{
+    constexpr int DK = 64 * CPL, D = BWD_PF;
+    const BwdArgs a = args;
     const int bh = blockIdx.x, H = a.H, T = a.T;
     const int b = bh / H, h = bh % H, lane = threadIdx.x;
     const float mu = a.mu_h ? a.mu_h[h] : a.mu;
     const size_t ntok = (size_t)a.B * T * H, kstride = (size_t)nblk * ntok * DK;
-    const IO* kg = reinterpret_cast<const IO*>(a.k);
-    IO* dqg = reinterpret_cast<IO*>(a.gq);
     IO* dkg = reinterpret_cast<IO*>(a.gk);
+    auto tok_of = [&](int t) __attribute__((always_inline)) { return ((size_t)b * T + t) * H + h; };
 
     float pbar[CPL];
 #pragma unroll
@@ -310,45 +668,24 @@ __global__ __launch_bounds__(64) void kdn_bwd_gain_rev_kernel(BwdArgs a, int nbl
         bbar = a.gvar_T ? a.gvar_T[bh] : 0.f;
     }
 
-    for (int t = T - 1; t >= 0; --t) {
-        const size_t tok = ((size_t)b * T + t) * H + h;
-        const float rt = a.r[tok];
-        float kb[CPL], kmb[CPL], amb[CPL], kk[CPL], al[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const size_t e = tok * DK + lane + 64 * c;
-            float qs = 0.f, ks = 0.f, km = 0.f, am = 0.f;
-            for (int bl = 0; bl < nblk; ++bl) {
-                const float* pp = a.part + ((size_t)bl * ntok + tok) * DK + lane + 64 * c;
-                qs += pp[0];
-                ks += pp[kstride];
-                km += pp[2 * kstride];
-                am += pp[3 * kstride];
-            }
-            dqg[e] = from_f32<IO>(qs);
-            kb[c] = ks;
-            kmb[c] = km;
-            amb[c] = am;
-            kk[c] = to_f32(kg[e]);
-            al[c] = a.alpha[e];
-        }
+    auto step = [&](const RevIn<CPL>& x, int t) __attribute__((always_inline)) {
+        const size_t tok = tok_of(t);
+        const float rt = x.r;
         if constexpr (!ISO) {
-            const float d = a.dd[tok];
-            float ph[CPL], pp[CPL], kap[CPL], u[CPL], phb[CPL], ub[CPL];
+            const float d = x.d;
+            float ph[CPL], kap[CPL], ub[CPL], phb[CPL];
             float s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const size_t e = tok * DK + lane + 64 * c;
-                pp[c] = a.pprev[e];
-                ph[c] = al[c] * al[c] * pp[c] + a.omega[e];
-                kap[c] = ph[c] * kk[c] / d;
-                u[c] = (mu / rt) * kk[c] * kk[c];
-                const float den = 1.f + u[c] * ph[c];
+                ph[c] = x.al[c] * x.al[c] * x.pp[c] + x.om[c];
+                kap[c] = ph[c] * x.kk[c] / d;
+                const float u = (mu / rt) * x.kk[c] * x.kk[c];
+                const float den = 1.f + u * ph[c];
                 phb[c] = pbar[c] / (den * den);
                 ub[c] = -pbar[c] * ph[c] * ph[c] / (den * den);
-                s1 += kb[c] * kap[c];
-                s2 += ub[c] * u[c];
-                s3 += ub[c] * kk[c] * kk[c];
+                s1 += x.kb[c] * kap[c];
+                s2 += ub[c] * u;
+                s3 += ub[c] * x.kk[c] * x.kk[c];
             }
             const float dbar = -wave_sum(s1) / d;
             const float rbar = dbar - wave_sum(s2) / rt;
@@ -356,20 +693,20 @@ __global__ __launch_bounds__(64) void kdn_bwd_gain_rev_kernel(BwdArgs a, int nbl
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const size_t e = tok * DK + lane + 64 * c;
-                phb[c] += kb[c] * kk[c] / d + dbar * kk[c] * kk[c];
-                const float kbar = kmb[c] + 2.f * ub[c] * (mu / rt) * kk[c] +
-                                   kb[c] * ph[c] / d + 2.f * dbar * ph[c] * kk[c];
+                const float kk = x.kk[c];
+                phb[c] += x.kb[c] * kk / d + dbar * kk * kk;
+                const float kbar = x.kmb[c] + 2.f * ub[c] * (mu / rt) * kk +
+                                   x.kb[c] * ph[c] / d + 2.f * dbar * ph[c] * kk;
                 dkg[e] = from_f32<IO>(kbar);
-                a.galpha[e] = amb[c] + 2.f * phb[c] * al[c] * pp[c];
+                a.galpha[e] = x.amb[c] + 2.f * phb[c] * x.al[c] * x.pp[c];
                 a.gomega[e] = phb[c];
-                pbar[c] = phb[c] * al[c] * al[c];
+                pbar[c] = phb[c] * x.al[c] * x.al[c];
             }
             if (lane == 0)
                 a.gr[tok] = rbar;
         } else {
-            const float4 gs = *reinterpret_cast<const float4*>(a.gsc + tok * 4);
-            const float beta = gs.x, bprev = gs.y, am = gs.z, n = gs.w;
-            const float bhat = am * bprev + a.omega[tok];
+            const float beta = x.gs.x, bprev = x.gs.y, am = x.gs.z, n = x.gs.w;
+            const float bhat = am * bprev + x.omi;
             const float e = rt + bhat * n;
             const float u = mu * n / ((float)DK * rt);
             const float den = 1.f + u * bhat;
@@ -381,7 +718,7 @@ __global__ __launch_bounds__(64) void kdn_bwd_gain_rev_kernel(BwdArgs a, int nbl
             float sb = 0.f;
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-                sb += kb[c] * kk[c];
+                sb += x.kb[c] * x.kk[c];
             const float betab = wave_sum(sb);
             bhb += betab * rt / (e * e);
             rbar -= betab * bhat / (e * e);
@@ -390,8 +727,8 @@ __global__ __launch_bounds__(64) void kdn_bwd_gain_rev_kernel(BwdArgs a, int nbl
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const size_t ei = tok * DK + lane + 64 * c;
-                dkg[ei] = from_f32<IO>(kmb[c] + beta * kb[c] + 2.f * nb * kk[c]);
-                a.galpha[ei] = amb[c] + 2.f * abar * al[c] / (float)DK;
+                dkg[ei] = from_f32<IO>(x.kmb[c] + beta * x.kb[c] + 2.f * nb * x.kk[c]);
+                a.galpha[ei] = x.amb[c] + 2.f * abar * x.al[c] / (float)DK;
             }
             if (lane == 0) {
                 a.gomega[tok] = bhb;
@@ -399,6 +736,28 @@ __global__ __launch_bounds__(64) void kdn_bwd_gain_rev_kernel(BwdArgs a, int nbl
             }
             bbar = bhb * am;
         }
+    };
+    // groups of D tokens, last first, with the next group's inputs in flight
+    RevIn<CPL> ring[D];
+    int t = T - 1;
+    if (T >= D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            rev_in_load<IO, ISO, CPL>(ring[j], a, tok_of(t - j), kstride, lane);
+    }
+    for (; t - (D - 1) >= 0; t -= D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const RevIn<CPL> cur = ring[j];
+            if (t - j - D >= 0)
+                rev_in_load<IO, ISO, CPL>(ring[j], a, tok_of(t - j - D), kstride, lane);
+            step(cur, t - j);
+        }
+    }
+    for (; t >= 0; --t) {
+        RevIn<CPL> cur;
+        rev_in_load<IO, ISO, CPL>(cur, a, tok_of(t), kstride, lane);
+        step(cur, t);
     }
     if constexpr (!ISO) {
         if (a.gvar0)
@@ -471,6 +830,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
+    const size_t n4 = (size_t)a.B * a.T * a.H * DK / 4;
+    if (n4 > 0) {
+        hipLaunchKernelGGL((kdn_bwd_merge_kernel<IO, DK>), dim3((unsigned)((n4 + 255) / 256)),
+                           dim3(256), 0, stream, a, nblk);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     hipLaunchKernelGGL((kdn_bwd_gain_rev_kernel<IO, ISO, CPL>), dim3(bh), dim3(64), 0, stream, a,
                        nblk);
     return hipGetLastError();

@@ -270,6 +270,8 @@ def test_bwd_validation(L):
     assert bwd(dalpha=None) == -1 and "dalpha" in msg()
     assert bwd(var0=base["var0"], c0=base["c0"]) == -1 and "either" in msg()
     assert bwd(dq=base["dq"] + 1) == -1 and "aligned" in msg()
+    assert bwd(alpha=base["alpha"] + 4) == -1 and "16-byte" in msg()
+    assert bwd(d_o=base["d_o"] + 8) == -1 and "16-byte" in msg()
     assert bwd(dr=base["dr"] + 2) == -1 and "aligned" in msg()
     assert bwd(dq=base["q"]) == -1 and "dq must not overlap q" in msg()
     assert bwd(dS0=base["ws"] + 64) == -1 and "overlap" in msg()

@@ -64,3 +64,16 @@ def test_traffic_only_for_the_profiled_sources(tmp_path, monkeypatch):
     assert bench.traffic_for(kern, bench.traffic_key(kern, "other", "diag")) is None
     f.write_text("not json")
     assert bench.traffic_for(kern, key) is None
+
+
+def test_bytes_backward_per_head_token():
+    # Diagonal, d = 128, bf16: q, k, v, do read and dq, dk, dv written (2 B
+    # each), alpha, omega read and their gradients written (fp32), r and dr;
+    # per head dS0 (d^2 fp32), dp0 (d fp32) and dmu
+    d = 128
+    per_ht = 7 * d * 2 + 4 * d * 4 + 8
+    assert per_ht == 3848
+    assert bench.alg_bytes_bwd("diag", 1, 10, 1, d, d, 2) == 10 * per_ht + d * d * 4 + d * 4 + 4
+    # Isotropic: omega and domega are one fp32 per token
+    per_ht_iso = 7 * d * 2 + 2 * (d + 1) * 4 + 8
+    assert bench.alg_bytes_bwd("iso", 1, 10, 1, d, d, 2) == 10 * per_ht_iso + d * d * 4 + 4 + 4
