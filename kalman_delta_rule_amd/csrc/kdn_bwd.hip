@@ -108,6 +108,20 @@ __device__ __forceinline__ float sum_lanes_from(float x)
 
 __device__ __forceinline__ float wave_sum(float x) { return sum_lanes_from<1>(x); }
 
+// One reduce-scatter step over lane pairs l, l ^ M: of the first N values,
+// the lane whose bit M is clear keeps the lower half and the other lane the
+// upper half, each adding its partner's copy; v[0 .. N/2) hold the result.
+template <int M, int N, int S>
+__device__ __forceinline__ void rs_step(float (&v)[S], bool upper)
+{
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+        const float keep = upper ? v[i + N / 2] : v[i];
+        const float send = upper ? v[i] : v[i + N / 2];
+        v[i] = keep + xor_lane<M>(send);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // A: gain forward
 // ---------------------------------------------------------------------------
@@ -341,7 +355,7 @@ __device__ __forceinline__ void bwd_stage_copy(BwdStage<IO, ISO, DK>& s, StageSr
 }
 
 template <typename IO, bool ISO, int DK>
-__global__ __launch_bounds__(256) void kdn_bwd_mem_kernel(BwdArgs args)
+__global__ __launch_bounds__(256, 2) void kdn_bwd_mem_kernel(BwdArgs args)
 {
     // kernel arguments copied to locals once: nothing below reads them through
     // a pointer
@@ -385,13 +399,26 @@ __global__ __launch_bounds__(256) void kdn_bwd_mem_kernel(BwdArgs args)
     // of its CPT columns.  The two LDS slots alternate so the next call's
     // writes never meet this call's reads.
     auto col_sum = [&](float (&x)[CPT]) __attribute__((always_inline)) {
+        // reduce-scatter over the row bits below 16 (each lane ends with one
+        // of its CPT columns summed over 8 or 4 lanes), all-reduce over lane
+        // bits 4 and 5, then across the four waves through LDS
+        float v[CPT];
 #pragma unroll
         for (int j = 0; j < CPT; ++j)
-            x[j] = sum_lanes_from<TPR>(x[j]);
-        if (lane < TPR)
-#pragma unroll
-            for (int j = 0; j < CPT; ++j)
-                red[slot][wave][cb + j] = x[j];
+            v[j] = x[j];
+        int jl = 0;
+        if constexpr (TPR == 2) {
+            const bool b1 = (lane & 2) != 0;
+            rs_step<2, 8>(v, b1);
+            jl += b1 ? 4 : 0;
+        }
+        const bool b2 = (lane & 4) != 0, b3 = (lane & 8) != 0;
+        rs_step<4, 4>(v, b2);
+        rs_step<8, 2>(v, b3);
+        jl += (b2 ? 2 : 0) + (b3 ? 1 : 0);
+        const float r = add_xor<32>(add_xor<16>(v[0]));
+        if (lane < 16)
+            red[slot][wave][(lane % TPR) * CPT + jl] = r;
         lds_barrier();
 #pragma unroll
         for (int j = 0; j < CPT; ++j)
