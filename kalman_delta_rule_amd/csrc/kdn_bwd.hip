@@ -13,7 +13,8 @@
 //   S^bar = G - k delbar^T, dk -= S^ delbar, dalpha += rowsum(S^bar (.) S_{t-1}),
 //   G <- diag(alpha) S^bar; then the variance recurrence's adjoint per channel.
 //
-// Three kernels, all fp32 arithmetic whatever the io type:
+// Three kernels, all fp32 arithmetic whatever the io type (divisions in the
+// gain recurrences through the hardware reciprocal, as in the forward):
 //   A  gain forward, one wave per (b,h): recomputes kap_t, p_{t-1} and
 //      r + z_t (Isotropic: beta_t, b_{t-1}, mean alpha^2, |k|^2) for every token.
 //   B  memory backward, one 256-thread workgroup per (b,h) and 16-column
@@ -184,9 +185,9 @@ __global__ __launch_bounds__(64) void kdn_bwd_gain_fwd_kernel(BwdArgs args)
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const size_t e = tok * DK + lane + 64 * c;
-                a.kap[e] = ph[c] * x.kk[c] / d;
+                a.kap[e] = ph[c] * x.kk[c] * rcp(d);
                 a.pprev[e] = p[c];
-                p[c] = ph[c] / (1.f + (mu / x.r) * x.kk[c] * x.kk[c] * ph[c]);
+                p[c] = ph[c] * rcp(1.f + (mu / x.r) * x.kk[c] * x.kk[c] * ph[c]);
             }
             if (lane == 0)
                 a.dd[tok] = d;
@@ -705,11 +706,11 @@ __global__ __launch_bounds__(64) void kdn_bwd_gain_rev_kernel(BwdArgs args, int 
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 ph[c] = x.al[c] * x.al[c] * x.pp[c] + x.om[c];
-                kap[c] = ph[c] * x.kk[c] / d;
+                kap[c] = ph[c] * x.kk[c] * rcp(d);
                 const float u = (mu / rt) * x.kk[c] * x.kk[c];
                 const float den = 1.f + u * ph[c];
-                phb[c] = pbar[c] / (den * den);
-                ub[c] = -pbar[c] * ph[c] * ph[c] / (den * den);
+                phb[c] = pbar[c] * rcp(den * den);
+                ub[c] = -pbar[c] * ph[c] * ph[c] * rcp(den * den);
                 s1 += x.kb[c] * kap[c];
                 s2 += ub[c] * u;
                 s3 += ub[c] * x.kk[c] * x.kk[c];
@@ -737,8 +738,8 @@ __global__ __launch_bounds__(64) void kdn_bwd_gain_rev_kernel(BwdArgs args, int 
             const float e = rt + bhat * n;
             const float u = mu * n / ((float)DK * rt);
             const float den = 1.f + u * bhat;
-            float bhb = bbar / (den * den);
-            const float ub = -bbar * bhat * bhat / (den * den);
+            float bhb = bbar * rcp(den * den);
+            const float ub = -bbar * bhat * bhat * rcp(den * den);
             float nb = ub * mu / ((float)DK * rt);
             float rbar = -ub * u / rt;
             mub += ub * n / ((float)DK * rt);
