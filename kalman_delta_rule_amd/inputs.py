@@ -94,22 +94,36 @@ def _unit(x, axis=-1):
     return (x / np.maximum(n, np.float32(1e-30))).astype(np.float32)
 
 
-def _draw_tokens(rng, variant, B, T, H, dk, dv, io):
+def _draw_tokens(rng, variant, B, T, H, dk, dv, io, preact=False):
+    """q, k, v and the gates; with ``preact`` the gates' pre-activations
+    (alpha's, omega's, r's) in place of the gates, from the same draws."""
     f32 = np.float32
     q = _unit(rng.standard_normal((B, T, H, dk), dtype=f32))
     k = _unit(rng.standard_normal((B, T, H, dk), dtype=f32))
     v = rng.standard_normal((B, T, H, dv), dtype=f32)
-    alpha = _sigmoid(f32(2.0) + f32(0.5) * rng.standard_normal((B, T, H, dk), dtype=f32))
+    a_pre = f32(2.0) + f32(0.5) * rng.standard_normal((B, T, H, dk), dtype=f32)
     wshape = (B, T, H, dk) if variant == "diag" else (B, T, H)
-    omega = _softplus(rng.standard_normal(wshape, dtype=f32))
-    r = _softplus(rng.standard_normal((B, T, H), dtype=f32))
-    return q, k, v, alpha, omega, r
+    w_pre = rng.standard_normal(wshape, dtype=f32)
+    r_pre = rng.standard_normal((B, T, H), dtype=f32)
+    if preact:
+        return q, k, v, a_pre, w_pre, r_pre
+    return q, k, v, _sigmoid(a_pre), _softplus(w_pre), _softplus(r_pre)
 
 
 TOKEN_BLOCK = 1024   # tokens per independently seeded generation block
 
 
-def make_fwd_inputs(w: Workload, variant: Optional[str] = None, threads: int = 0) -> dict:
+def make_preact_inputs(w: Workload, variant: Optional[str] = None, threads: int = 0) -> dict:
+    """Inputs of the forward from gate pre-activations: q, k, v as in
+    make_fwd_inputs and, instead of the gates, a_pre [B,T,H,dk], w_pre
+    ([B,T,H,dk] Diagonal, [B,T,H] Isotropic) and r_pre [B,T,H], drawn from the
+    same streams (so sigmoid(a_pre) etc. are the gates make_fwd_inputs draws)
+    and rounded to bf16 when ``w.io == 'bf16'``."""
+    return make_fwd_inputs(w, variant, threads, preact=True)
+
+
+def make_fwd_inputs(w: Workload, variant: Optional[str] = None, threads: int = 0,
+                    preact: bool = False) -> dict:
     """Forward inputs for workload ``w`` as fp32 numpy arrays (q, k, v already
     rounded to bf16 when ``w.io == 'bf16'``) plus S0 / p0 (or b0).
 
@@ -133,7 +147,7 @@ def make_fwd_inputs(w: Workload, variant: Optional[str] = None, threads: int = 0
         b, t0 = job
         t1 = min(T, t0 + TOKEN_BLOCK)
         rng = np.random.Generator(np.random.PCG64([w.seed, vcode, b, t0 // TOKEN_BLOCK]))
-        parts = _draw_tokens(rng, variant, 1, t1 - t0, H, dk, dv, w.io)
+        parts = _draw_tokens(rng, variant, 1, t1 - t0, H, dk, dv, w.io, preact)
         for dst, src in zip((q, k, v, alpha, omega, r), parts):
             dst[b:b + 1, t0:t1] = src
 
@@ -150,6 +164,10 @@ def make_fwd_inputs(w: Workload, variant: Optional[str] = None, threads: int = 0
         _insert_retrieval(rng, q, k, v, n_pairs=min(512, T // 2))
     if w.io == "bf16":
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    if preact:
+        if w.io == "bf16":
+            alpha, omega, r = round_bf16(alpha), round_bf16(omega), round_bf16(r)
+        return {"q": q, "k": k, "v": v, "a_pre": alpha, "w_pre": omega, "r_pre": r}
     out = {"q": q, "k": k, "v": v, "alpha": alpha, "omega": omega, "r": r,
            "S0": np.zeros((B, H, dk, dv), np.float32)}
     if variant == "diag":

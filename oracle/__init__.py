@@ -13,6 +13,9 @@ Contents
 * ``bwd`` -- the backward pass of both recurrences (reverse-mode derivative,
   derived in ``kdn_oracle.c`` since the notes print no gradient formulas;
   pinned in the tests against finite differences of the forward).
+* ``gate_prologue`` -- the gates from their pre-activations (KDN reading
+  notes, method part §8): alpha = sigmoid(a), omega = softplus(w),
+  r = r_min + softplus(rho); numpy, fp64.
 * ``dense_kf`` -- the exact dense-covariance Kalman memory (KDN reading notes,
   method part §2, Eq. (12)-(17)); numpy, fp64, for tiny d_k only.
 * ``mobius_factors`` / ``mobius_fold_left`` / ``mobius_fold_tree`` /
@@ -249,6 +252,19 @@ def bwd(variant: str, q, k, v, alpha, omega, r, do, S0=None, var0=None, mu=None,
     if rc != 0:
         raise RuntimeError("kdn_oracle_bwd failed (%d)" % rc)
     return out
+
+
+def gate_prologue(a_pre, w_pre, r_pre, r_min: float = 0.01) -> dict:
+    """The gates of the end-to-end network from their pre-activations (KDN
+    reading notes, method part §8, where r_min = 0.01): alpha = sigmoid(a),
+    omega = softplus(w) (one per channel for Diagonal, per token for
+    Isotropic), r = r_min + softplus(rho), in fp64.  softplus(x) =
+    log(1 + e^x) is evaluated as max(x, 0) + log1p(e^-|x|), the same value
+    without overflow."""
+    a, w, rho = map(_f64, (a_pre, w_pre, r_pre))
+    softplus = lambda x: np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+    return {"alpha": 1.0 / (1.0 + np.exp(-a)), "omega": softplus(w),
+            "r": float(r_min) + softplus(rho)}
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,51 @@
+"""Pins of the oracle's gate prologue (``oracle.gate_prologue``; KDN reading
+notes, method part §8: alpha = sigmoid(a), omega = softplus(w),
+r = r_min + softplus(rho), r_min = 0.01) against values and identities the
+functions' definitions fix, and of the generator's pre-activation draws."""
+import math
+
+import numpy as np
+
+from kalman_delta_rule_amd import inputs
+
+
+def test_special_values(ora):
+    g = ora.gate_prologue(np.array([0.0]), np.array([0.0]), np.array([0.0]), r_min=0.01)
+    assert g["alpha"][0] == 0.5
+    assert abs(g["omega"][0] - math.log(2.0)) < 1e-15
+    assert abs(g["r"][0] - (0.01 + math.log(2.0))) < 1e-15
+
+
+def test_identities_and_asymptotics(ora):
+    x = np.linspace(-30.0, 30.0, 601)
+    g, gm = ora.gate_prologue(x, x, x, r_min=0.0), ora.gate_prologue(-x, -x, -x, r_min=0.0)
+    np.testing.assert_allclose(g["alpha"] + gm["alpha"], 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(g["omega"] - gm["omega"], x, rtol=0, atol=1e-13)
+    # d softplus / dx = sigmoid(x), by central differences
+    h = 1e-6
+    d = (ora.gate_prologue(x, x + h, x)["omega"] - ora.gate_prologue(x, x - h, x)["omega"]) / (2 * h)
+    np.testing.assert_allclose(d, g["alpha"], rtol=0, atol=1e-8)
+    big = ora.gate_prologue(np.array([800.0]), np.array([800.0]), np.array([-800.0]), r_min=0.01)
+    assert big["alpha"][0] == 1.0 and big["omega"][0] == 800.0 and big["r"][0] == 0.01
+    # the textbook form where it does not overflow
+    y = np.linspace(-20.0, 20.0, 81)
+    np.testing.assert_allclose(ora.gate_prologue(y, y, y, r_min=0.25)["r"],
+                               0.25 + np.log(1.0 + np.exp(y)), rtol=1e-14)
+
+
+def test_preact_draws_are_the_gates_of_the_plain_workload(ora):
+    # same streams: the prologue of the pre-activations gives (to fp32
+    # rounding) the gates make_fwd_inputs draws, with r_min = 0
+    for variant in ("diag", "iso"):
+        w = inputs.Workload("t", variant, "f32", 2, 3, 40, 64, 64, seed=17)
+        pre = inputs.make_preact_inputs(w)
+        plain = inputs.make_fwd_inputs(w)
+        g = ora.gate_prologue(pre["a_pre"], pre["w_pre"], pre["r_pre"], r_min=0.0)
+        for n in ("alpha", "omega", "r"):
+            np.testing.assert_allclose(g[n], plain[n], rtol=2e-6, atol=1e-7)
+        for n in ("q", "k", "v"):
+            assert np.array_equal(pre[n], plain[n])
+    wb = inputs.Workload("t", "diag", "bf16", 1, 2, 20, 64, 64, seed=3)
+    pre = inputs.make_preact_inputs(wb)
+    for n in ("a_pre", "w_pre", "r_pre"):
+        assert np.array_equal(pre[n], inputs.round_bf16(pre[n]))
