@@ -197,6 +197,28 @@ kdn_status kdn_dense_fwd(int B, int T, int H, int dk, int dv, int io_dtype, cons
                          float* P_T, float* beta_eff, void* stream);
 
 /*
+ * Forward from the gates' pre-activations (KDN reading notes, method part
+ * §8: the end-to-end network produces alpha = sigmoid(a), omega =
+ * softplus(w) and r = r_min + softplus(rho) from its projections; the notes
+ * use r_min = 0.01).  Arguments as kdn_fwd_ex, with the gates replaced by
+ *   a_pre  [B,T,H,dk] io dtype (bf16 or fp32, as q/k/v), 16-byte aligned
+ *   w_pre  [B,T,H,dk] (Diagonal) or [B,T,H] (Isotropic), io dtype, 16-byte aligned
+ *   r_pre  [B,T,H] io dtype, 16-byte aligned
+ *   r_min  > 0 and finite (keeps r > 0)
+ * An elementwise pre-pass writes the fp32 gates into the workspace
+ * (kdn_fwd_preact_workspace_size bytes, 16-byte aligned, disjoint from every
+ * argument), then the forward of kdn_fwd_ex runs on them.  Validation
+ * happens before anything is launched.
+ */
+size_t kdn_fwd_preact_workspace_size(int variant, int B, int T, int H, int dk);
+kdn_status kdn_fwd_preact(int variant, int B, int T, int H, int dk, int dv, int io_dtype,
+                          float mu, const float* mu_h, const void* q, const void* k,
+                          const void* v, const void* a_pre, const void* w_pre, const void* r_pre,
+                          float r_min, const float* S0, const float* var0, const float* c0_h,
+                          void* o, float* S_T, float* var_T, float* beta_eff, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Backward pass of Diagonal / Isotropic KDN (the mixer is trained through the
  * scanned recurrence, KDN reading notes, method part §8; the notes print no
  * gradient formulas, so this is the reverse-mode derivative of the

@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     kdn_bwd,
     kdn_dense_fwd,
     kdn_fwd_ex,
+    kdn_fwd_preact,
     kdn_fwd_workspace_size,
     kdn_gain_scan,
     kdn_iso_fwd,
@@ -27,6 +28,7 @@ __all__ = [
     "kdn_iso_fwd",
     "kdn_step",
     "kdn_fwd_ex",
+    "kdn_fwd_preact",
     "kdn_dense_fwd",
     "kdn_bwd",
     "kdn_gain_scan",

@@ -55,6 +55,11 @@ def lib():
                              + [vp, sz, vp])
     L.kdn_dense_fwd.restype = i
     L.kdn_dense_fwd.argtypes = [i] * 6 + [vp] * 3 + [fp] * 5 + [vp] + [fp] * 3 + [vp]
+    L.kdn_fwd_preact_workspace_size.restype = sz
+    L.kdn_fwd_preact_workspace_size.argtypes = [i] * 5
+    L.kdn_fwd_preact.restype = i
+    L.kdn_fwd_preact.argtypes = ([i] * 7 + [f] + [fp] + [vp] * 6 + [f] + [fp] * 3 + [vp]
+                                 + [fp] * 3 + [vp, sz, vp])
     L.kdn_bwd_workspace_size.restype = sz
     L.kdn_bwd_workspace_size.argtypes = [i] * 6
     L.kdn_bwd.restype = i
@@ -78,6 +83,7 @@ def lib():
 
 EXPORTED = ("kdn_fwd_workspace_size", "kdn_diag_fwd", "kdn_iso_fwd", "kdn_step",
             "kdn_fwd_ex", "kdn_step_ex", "kdn_dense_fwd", "kdn_bwd_workspace_size", "kdn_bwd",
+            "kdn_fwd_preact_workspace_size", "kdn_fwd_preact",
             "kdn_gain_workspace_size", "kdn_gain_scan", "kdn_status_string",
             "kdn_last_error_message", "kdn_version")
 

@@ -175,6 +175,53 @@ def kdn_dense_fwd(q, k, v, alpha, omega, r, S0=None, P0=None, want_beta_eff: boo
     return o, S_T, P_T, beta
 
 
+def kdn_fwd_preact(variant: str, q, k, v, a_pre, w_pre, r_pre, r_min: float = 0.01, S0=None,
+                   var0=None, mu=None, mu_h=None, c0_h=None, want_beta_eff: bool = False,
+                   o=None, S_T=None, var_T=None, workspace=None):
+    """Forward from the gates' pre-activations (alpha = sigmoid(a_pre),
+    omega = softplus(w_pre), r = r_min + softplus(r_pre)); pre-activations in
+    the io dtype of q.  Returns (o, S_T, var_T, beta_eff or None)."""
+    L = _lib.lib()
+    var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    io = _io_code(q)
+    iso = var == KDN_ISO
+    f32 = torch.float32
+    _need(q, "q", (B, T, H, dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, dv), q.dtype, dev)
+    _need(a_pre, "a_pre", (B, T, H, dk), q.dtype, dev)
+    _need(w_pre, "w_pre", (B, T, H) if iso else (B, T, H, dk), q.dtype, dev)
+    _need(r_pre, "r_pre", (B, T, H), q.dtype, dev)
+    var_shape = (B, H) if iso else (B, H, dk)
+    for t, n, shp in ((S0, "S0", (B, H, dk, dv)), (var0, "var0", var_shape),
+                      (mu_h, "mu_h", (H,)), (c0_h, "c0_h", (H,))):
+        if t is not None:
+            _need(t, n, shp, f32, dev)
+    mu = float(dk if mu is None else mu)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=f32, device=dev)
+    if var_T is None:
+        var_T = torch.empty(var_shape, dtype=f32, device=dev)
+    beta = torch.empty((B, T, H), dtype=f32, device=dev) if want_beta_eff else None
+    need = int(L.kdn_fwd_preact_workspace_size(var, B, T, H, dk))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = L.kdn_fwd_preact(var, B, T, H, dk, dv, io, mu, _ptr(mu_h), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(a_pre), _ptr(w_pre), _ptr(r_pre), float(r_min), _ptr(S0),
+                              _ptr(var0), _ptr(c0_h), _ptr(o), _ptr(S_T), _ptr(var_T),
+                              _ptr(beta), _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check(st)
+    return o, S_T, var_T, beta
+
+
 def kdn_bwd(variant: str, q, k, v, alpha, omega, r, d_o, S0=None, var0=None, mu=None,
             mu_h=None, c0_h=None, dS_T=None, dvar_T=None, want_state_grads: bool = True,
             workspace=None) -> dict:

@@ -10,6 +10,7 @@
 
 #include "kdn.h"
 #include "kdn_internal.h"
+#include "kdn_ops.h"
 
 namespace {
 
@@ -111,7 +112,8 @@ kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float
                     const void* q, const void* k, const void* v, const float* alpha,
                     const float* omega, const float* r, const float* S0, const float* var0,
                     void* o, float* S_T, float* var_T, void* workspace,
-                    size_t workspace_bytes, void* stream, const ExtOpts& x = ExtOpts{})
+                    size_t workspace_bytes, void* stream, const ExtOpts& x = ExtOpts{},
+                    const kdn::PrologueArgs* pro = nullptr)
 {
     kdn_status st = check_common(B, T, H, dk, dv, io, mu, true);
     if (st != KDN_OK)
@@ -170,6 +172,11 @@ kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float
     kdn::FwdArgs a{q, k, v, alpha, omega, r, S0, var0, o, S_T, var_T, B, T, H, dk, dv, mu,
                    x.mu_h, x.c0_h, T > 0 ? x.beta_eff : nullptr};
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (pro && T > 0) {  // the gates from their pre-activations, into the workspace
+        hipError_t e = kdn::launch_gate_prologue(*pro, io, hs);
+        if (e != hipSuccess)
+            return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
     hipError_t e = io == KDN_BF16 ? kdn::launch_walk_fwd(a, iso, hs)
                                   : kdn::launch_chunk_fwd_f32(a, iso, hs);
     if (e != hipSuccess)
@@ -331,6 +338,79 @@ kdn_status kdn_dense_fwd(int B, int T, int H, int dk, int dv, int io_dtype, cons
     if (e != hipSuccess)
         return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+static size_t round64f(size_t n) { return (n + 63) & ~(size_t)63; }
+
+size_t kdn_fwd_preact_workspace_size(int variant, int B, int T, int H, int dk)
+{
+    if ((variant != KDN_DIAG && variant != KDN_ISO) || B < 1 || H < 1 || T < 0 || dk < 1)
+        return 0;
+    const size_t ntok = (size_t)B * T * H;
+    return (round64f(ntok * dk) + round64f(variant == KDN_ISO ? ntok : ntok * dk) +
+            round64f(ntok)) * sizeof(float);
+}
+
+kdn_status kdn_fwd_preact(int variant, int B, int T, int H, int dk, int dv, int io_dtype,
+                          float mu, const float* mu_h, const void* q, const void* k,
+                          const void* v, const void* a_pre, const void* w_pre, const void* r_pre,
+                          float r_min, const float* S0, const float* var0, const float* c0_h,
+                          void* o, float* S_T, float* var_T, float* beta_eff, void* workspace,
+                          size_t workspace_bytes, void* stream)
+{
+    if (variant != KDN_DIAG && variant != KDN_ISO)
+        return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
+                    variant);
+    if (io_dtype != KDN_F32 && io_dtype != KDN_BF16)
+        return fail(KDN_ERR_INVALID_ARG, "io_dtype must be KDN_F32 (0) or KDN_BF16 (1), got %d",
+                    io_dtype);
+    if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1)
+        return fail(KDN_ERR_INVALID_ARG, "need B >= 1, H >= 1, T >= 0 (got B=%d T=%d H=%d)", B, T, H);
+    if (!(r_min > 0.f) || r_min > 3.0e38f)
+        return fail(KDN_ERR_INVALID_ARG, "r_min must be finite and > 0 (got %g)", (double)r_min);
+    const bool iso = variant == KDN_ISO;
+    if (T > 0) {
+        KDN_REQUIRE(a_pre, "a_pre");
+        KDN_REQUIRE(w_pre, "w_pre");
+        KDN_REQUIRE(r_pre, "r_pre");
+    }
+    KDN_ALIGNED(a_pre, "a_pre");
+    KDN_ALIGNED(w_pre, "w_pre");
+    KDN_ALIGNED(r_pre, "r_pre");
+    const size_t need = kdn_fwd_preact_workspace_size(variant, B, T, H, dk);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                    workspace_bytes);
+    KDN_ALIGNED(workspace, "workspace");
+    // the workspace (which receives the gates) must be disjoint from every argument
+    const size_t es = io_dtype == KDN_BF16 ? 2 : 4;
+    const size_t ntok = (size_t)B * T * H, bh = (size_t)B * H;
+    const size_t nw = iso ? ntok : ntok * dk, nvar = iso ? bh : bh * dk;
+    struct Buf { const void* p; size_t n; const char* name; };
+    const Buf bufs[] = {{q, ntok * dk * es, "q"}, {k, ntok * dk * es, "k"},
+                        {v, ntok * dv * es, "v"}, {a_pre, ntok * dk * es, "a_pre"},
+                        {w_pre, nw * es, "w_pre"}, {r_pre, ntok * es, "r_pre"},
+                        {o, ntok * dv * es, "o"}, {S0, bh * dk * dv * 4, "S0"},
+                        {S_T, bh * dk * dv * 4, "S_T"}, {var0, nvar * 4, "var0"},
+                        {var_T, nvar * 4, "var_T"}, {beta_eff, ntok * 4, "beta_eff"},
+                        {mu_h, (size_t)H * 4, "mu_h"}, {c0_h, (size_t)H * 4, "c0_h"}};
+    if (workspace && need)
+        for (const Buf& b : bufs) {
+            const char *w0 = (const char*)workspace, *b0 = (const char*)b.p;
+            if (b.p && b.n && w0 < b0 + b.n && b0 < w0 + need)
+                return fail(KDN_ERR_INVALID_ARG, "workspace must not overlap %s", b.name);
+        }
+    float* alpha = static_cast<float*>(workspace);
+    float* omega = alpha + round64f(ntok * dk);
+    float* r = omega + round64f(nw);
+    kdn::PrologueArgs pa{a_pre, w_pre, r_pre, alpha, omega, r, ntok * dk, nw, ntok, r_min};
+    ExtOpts x;
+    x.mu_h = mu_h;
+    x.c0_h = c0_h;
+    x.beta_eff = beta_eff;
+    return fwd_impl(iso, B, T, H, dk, dv, io_dtype, mu, q, k, v, T > 0 ? alpha : nullptr,
+                    T > 0 ? omega : nullptr, T > 0 ? r : nullptr, S0, var0, o, S_T, var_T, nullptr,
+                    0, stream, x, &pa);
 }
 
 size_t kdn_bwd_workspace_size(int variant, int B, int T, int H, int dk, int dv)

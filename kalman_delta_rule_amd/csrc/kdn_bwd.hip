@@ -33,6 +33,7 @@
 // token.
 #include "kdn_common.h"
 #include "kdn_internal.h"
+#include "kdn_ops.h"
 
 namespace kdn {
 

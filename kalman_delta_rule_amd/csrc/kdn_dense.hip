@@ -15,6 +15,7 @@
 // phases (inputs, prediction, u and delta, update, readout).
 #include "kdn_common.h"
 #include "kdn_internal.h"
+#include "kdn_ops.h"
 
 namespace kdn {
 

@@ -25,6 +25,7 @@
 // keeps the ratios and avoids fp32 overflow.
 #include "kdn_common.h"
 #include "kdn_internal.h"
+#include "kdn_ops.h"
 
 namespace kdn {
 

@@ -1,0 +1,97 @@
+// kdn_ops.h -- argument blocks and launchers of the dense filter, the gain
+// scan, the backward pass and the gate prologue (the calls beside the forward
+// and decode).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kdn {
+
+struct DenseArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* omega;  // [B,T,H,dk]: diagonal process noise
+    const float* r;
+    const float* S0;     // nullable
+    const float* P0;     // nullable [B,H,dk,dk]: identity when null
+    void* o;
+    float* S_T;
+    float* P_T;          // [B,H,dk,dk]
+    float* beta;         // nullable [B,T,H]
+    int B, T, H, dk, dv;
+};
+
+struct GainArgs {
+    const void* k;
+    const float* alpha;
+    const float* omega;
+    const float* r;
+    const float* var0;  // nullable
+    float* kappa;       // nullable
+    float* var_T;
+    float* summ;        // workspace: chunk summaries [BH][4][width][nchunks]
+    float* carry;       // workspace: chunk-entry variances [BH][nchunks][width]
+    int B, T, H, dk;
+    float mu;
+};
+
+struct BwdArgs {
+    // forward inputs (as in FwdArgs)
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* omega;
+    const float* r;
+    const float* S0;    // nullable
+    const float* var0;  // nullable
+    const float* c0;    // nullable [H]
+    const float* mu_h;  // nullable [H]
+    float mu;
+    // incoming gradients
+    const void* go;       // dL/do, io dtype
+    const float* gS_T;    // nullable
+    const float* gvar_T;  // nullable
+    // outgoing gradients
+    void* gq;
+    void* gk;
+    void* gv;
+    float* galpha;
+    float* gomega;
+    float* gr;
+    float* gS0;   // nullable
+    float* gvar0; // nullable
+    float* gmu;   // nullable [B,H]
+    int B, T, H, dk, dv;
+    // workspace pieces (set by bwd_carve_workspace)
+    float* kap;    // Diagonal [B,T,H,dk]: gain of every token
+    float* pprev;  // Diagonal [B,T,H,dk]: variance before every token
+    float* dd;     // Diagonal [B,T,H]: r + z
+    float* gsc;    // Isotropic [B,T,H,4]: beta, b_{t-1}, mean alpha^2, |k|^2
+    float* ckpt;   // [B*H][dv/16][ceil(T/16)][dk][16]: S at every 16th token
+    float* part;   // [4][dv/16][B*T*H][dk]: per-column-block partial row sums
+};
+
+struct PrologueArgs {
+    const void* a_pre;  // io dtype, n_alpha elements
+    const void* w_pre;  // io dtype, n_omega elements
+    const void* r_pre;  // io dtype, n_r elements
+    float* alpha;
+    float* omega;
+    float* r;
+    size_t n_alpha, n_omega, n_r;
+    float r_min;
+};
+
+hipError_t launch_dense_fwd(const DenseArgs& a, int io_dtype, hipStream_t stream);
+size_t gain_workspace_floats(bool iso, int B, int T, int H, int dk);
+hipError_t launch_gain_scan(const GainArgs& a, bool iso, int io_dtype, hipStream_t stream);
+size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv);
+void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws);
+hipError_t launch_bwd(const BwdArgs& a, bool iso, int io_dtype, hipStream_t stream);
+hipError_t launch_gate_prologue(const PrologueArgs& a, int io_dtype, hipStream_t stream);
+
+}  // namespace kdn
