@@ -57,6 +57,18 @@ def alg_bytes_fwd(variant: str, B, T, H, dk, dv, s_io: int) -> int:
     return n_ht * per_ht + state
 
 
+def alg_bytes_preact(variant: str, B, T, H, dk, dv, s_io: int) -> int:
+    """The forward's algorithmic bytes with the fp32 gates replaced by their
+    pre-activations in the io dtype: q, k, v read, o written, a_pre and
+    w_pre (per channel for Diagonal, per token for Isotropic) and r_pre read,
+    plus the final state and variances."""
+    n_ht = B * T * H
+    w = dk if variant == "diag" else 1
+    per_ht = (2 * dk + dv) * s_io + dv * s_io + (dk + w + 1) * s_io
+    state = B * H * (dk * dv * 4 + w * 4)
+    return n_ht * per_ht + state
+
+
 def alg_bytes_step(variant: str, B, H, dk, dv, s_io: int) -> int:
     per_head = 2 * dk * s_io + dv * s_io + dk * 4 + 4 + dv * s_io + 2 * dk * dv * 4
     per_head += (2 * dk * 4 + dk * 4) if variant == "diag" else (4 + 2 * 4)
@@ -152,6 +164,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--variant", default=None, help="override: diag | iso")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--preact", action="store_true",
+                    help="time the forward from gate pre-activations (kdn_fwd_preact) instead")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (kdn_bwd) on the workload instead")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -180,6 +194,8 @@ def main():
     if w.structure == "decode":
         return bench_decode(args, w)
     variant = args.variant or w.variant
+    if args.preact:
+        return bench_preact(args, w, variant)
     print("[bench] generating %s (%s)" % (w.name, variant), file=sys.stderr, flush=True)
     inp = inputs.make_fwd_inputs(w, variant)
     io_dt = torch.bfloat16 if w.io == "bf16" else torch.float32
@@ -256,6 +272,70 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": alg, "kernel": kname},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_preact(args, w, variant):
+    """Forward from bf16 (or fp32) gate pre-activations: kdn_fwd_preact, its
+    gate workspace allocated once outside the timed region."""
+    import torch
+    from kalman_delta_rule_amd import _lib, api, inputs
+
+    dev = torch.device("cuda:0")
+    print("[bench] generating %s pre-activations (%s)" % (w.name, variant), file=sys.stderr,
+          flush=True)
+    inp = inputs.make_preact_inputs(w, variant)
+    io_dt = torch.bfloat16 if w.io == "bf16" else torch.float32
+    d = {n: torch.from_numpy(inp[n]).to(io_dt).to(dev) for n in inp}
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    var = {"diag": 0, "iso": 1}[variant]
+    ws = torch.empty(max(int(_lib.lib().kdn_fwd_preact_workspace_size(var, B, T, H, dk)), 1),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=io_dt, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    var_T = torch.empty((B, H, dk) if variant == "diag" else (B, H), dtype=torch.float32,
+                        device=dev)
+
+    def step():
+        api.kdn_fwd_preact(variant, d["q"], d["k"], d["v"], d["a_pre"], d["w_pre"], d["r_pre"],
+                           r_min=0.01, o=o, S_T=S_T, var_T=var_T, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    s_io = 2 if w.io == "bf16" else 4
+    alg = alg_bytes_preact(variant, B, T, H, dk, dv, s_io)
+    achieved = alg / (ms_step / 1e3) / 1e9
+    line = {
+        "metric": "KDN mixer fwd from gate pre-activations, tokens/sec at T=%d (1 GPU)" % T,
+        "value": B * T / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "variant": variant, "B": B, "T": T, "H": H, "dk": dk,
+                   "dv": dv, "io": w.io, "gates": "pre-activations", "r_min": 0.01},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": alg,
+                     "kernel": "kdn_gate_prologue (x3) + %s" % fwd_kernel_name(w.io)},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

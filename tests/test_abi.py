@@ -288,3 +288,35 @@ def test_bwd_validation(L):
     assert L.kdn_bwd_workspace_size(0, B, T, H, dk, dv) == 4 * diag
     assert L.kdn_bwd_workspace_size(1, B, T, H, dk, dv) == 4 * iso
     assert L.kdn_bwd_workspace_size(0, B, 0, H, dk, dv) == 0
+
+
+def test_fwd_preact_validation(L):
+    G = 1 << 28
+    names = ["q", "k", "v", "a", "w", "r", "o", "S_T", "var_T", "ws"]
+    base = {n: P + (i + 1) * G for i, n in enumerate(names)}
+
+    def pre(**kw):
+        a = dict(variant=0, B=1, T=40, H=2, dk=128, dv=128, io=1, mu=128.0, r_min=0.01)
+        a.update({n: base[n] for n in names})
+        a.update(kw)
+        ws_bytes = a.pop("ws_bytes", L.kdn_fwd_preact_workspace_size(a["variant"], a["B"], a["T"],
+                                                                     a["H"], a["dk"]))
+        return L.kdn_fwd_preact(a["variant"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["io"],
+                                a["mu"], None, a["q"], a["k"], a["v"], a["a"], a["w"], a["r"],
+                                a["r_min"], None, None, None, a["o"], a["S_T"], a["var_T"], None,
+                                a["ws"], ws_bytes, None)
+    msg = lambda: L.kdn_last_error_message().decode()
+    assert pre(variant=3) == -1 and "variant" in msg()
+    assert pre(r_min=0.0) == -1 and "r_min" in msg()
+    assert pre(r_min=float("nan")) == -1 and "r_min" in msg()
+    assert pre(a=None) == -1 and "a_pre must not be NULL" in msg()
+    assert pre(r=base["r"] + 2) == -1 and "r_pre must be 16-byte aligned" in msg()
+    assert pre(ws_bytes=64) == -3 and "workspace" in msg()
+    assert pre(ws=base["o"] + 256) == -1 and "workspace must not overlap o" in msg()
+    assert pre(ws=base["ws"] + 4) == -1 and "workspace" in msg()
+    # the forward's own checks still apply after the prologue's
+    assert pre(dk=96) == -2 and "dk" in msg()
+    ntok = 1 * 40 * 2
+    r64 = lambda n: (n + 63) // 64 * 64
+    assert L.kdn_fwd_preact_workspace_size(0, 1, 40, 2, 128) == 4 * (2 * r64(ntok * 128) + r64(ntok))
+    assert L.kdn_fwd_preact_workspace_size(1, 1, 40, 2, 128) == 4 * (r64(ntok * 128) + 2 * r64(ntok))

@@ -77,3 +77,13 @@ def test_bytes_backward_per_head_token():
     # Isotropic: omega and domega are one fp32 per token
     per_ht_iso = 7 * d * 2 + 2 * (d + 1) * 4 + 8
     assert bench.alg_bytes_bwd("iso", 1, 10, 1, d, d, 2) == 10 * per_ht_iso + d * d * 4 + 4 + 4
+
+
+def test_bytes_preact_per_head_token():
+    # Diagonal, d = 128, bf16: q, k, v, o and the three pre-activations
+    # (a and w per channel, rho per token) at 2 B -- the ~1540 B/head-token
+    # the fused prologue is priced at
+    d = 128
+    assert bench.alg_bytes_preact("diag", 1, 10, 1, d, d, 2) == 10 * 1538 + d * d * 4 + d * 4
+    # Isotropic: q, k, v, o, a per channel, w and rho per token: (5 d + 2) x 2 B
+    assert bench.alg_bytes_preact("iso", 1, 10, 1, d, d, 2) == 10 * 1284 + d * d * 4 + 4
