@@ -130,3 +130,47 @@ def test_bwd_empty_sequence_passes_adjoints_through():
     torch.cuda.synchronize()
     assert torch.equal(g["dS0"], dS_T) and torch.equal(g["dvar0"], dp_T)
     assert torch.equal(g["dmu"], torch.zeros_like(g["dmu"]))
+
+
+# ---------------------------------------------------------------------------
+# full workloads, sampled (batch, head) problems: the backward of the launch
+# configuration bench.py --bwd times, against the oracle on each sampled
+# head's own slice (heads are independent problems)
+# ---------------------------------------------------------------------------
+def _bwd_full(ora, widx, n_heads):
+    from kdn_testutil import sample_heads
+    w = inputs.workload(widx)
+    x = dict(inputs.make_fwd_inputs(w))
+    for n in ("S0", "p0", "b0"):
+        x.pop(n, None)
+    rng = np.random.default_rng(w.seed + 77)
+    do = rng.standard_normal((w.B, w.T, w.H, w.dv)).astype(np.float32)
+    x["do"] = inputs.round_bf16(do) if w.io == "bf16" else do
+    g = _run(w.variant, w.io, x)
+    heads = sample_heads(w.B, w.H, n_heads, seed=100 + widx)
+    sl = lambda a, b, h: np.ascontiguousarray(a[b:b + 1, :, h:h + 1])
+    refs = {bh: ora.bwd(w.variant, *[sl(x[n], *bh) for n in ("q", "k", "v", "alpha", "omega", "r",
+                                                              "do")])
+            for bh in heads}
+    err = {}
+    for n in ("dq", "dk", "dv", "dalpha", "domega", "dr"):
+        err[n] = rel_l2(np.concatenate([sl(g[n], *bh).ravel() for bh in heads]),
+                        np.concatenate([refs[bh][n].ravel() for bh in heads]))
+    for n in ("dS0", "dvar0", "dmu"):
+        err[n] = rel_l2(np.concatenate([np.ravel(g[n][bh]) for bh in heads]),
+                        np.concatenate([np.ravel(refs[bh][n][0, 0]) for bh in heads]))
+    print("bwd %s heads=%s errors %s" % (w.name, heads, {k: "%.2e" % v for k, v in err.items()}),
+          flush=True)
+    assert max(err.values()) <= TOL[w.io], err
+    for n in ("dq", "dk", "dv", "dalpha", "domega", "dr"):
+        assert np.isfinite(g[n]).all(), n
+
+
+@pytest.mark.timeout(400)
+def test_bwd_config2_diag_full(ora):
+    _bwd_full(ora, 2, 3)
+
+
+@pytest.mark.timeout(400)
+def test_bwd_config1_iso_full(ora):
+    _bwd_full(ora, 1, 3)

@@ -87,3 +87,32 @@ def test_preact_empty_sequence_gives_initial_state():
                                       z(B, 0, H, dk), z(B, 0, H, dk), z(B, 0, H), S0=S0)
     torch.cuda.synchronize()
     assert torch.equal(S, S0) and torch.equal(var, torch.ones_like(var))
+
+
+@pytest.mark.timeout(400)
+def test_preact_config2_full_sampled(ora):
+    # the launch configuration bench.py --preact times, sampled heads against
+    # the oracle prologue + forward on each head's own slice
+    from kdn_testutil import sample_heads
+    w = inputs.workload(2)
+    x = inputs.make_preact_inputs(w)
+    d = _dev(x, w.io)
+    o, S, var, _ = api.kdn_fwd_preact(w.variant, d["q"], d["k"], d["v"], d["a_pre"], d["w_pre"],
+                                      d["r_pre"], r_min=0.01)
+    torch.cuda.synchronize()
+    heads = sample_heads(w.B, w.H, 4, seed=202)
+    sl = lambda a, b, h: np.ascontiguousarray(a[b:b + 1, :, h:h + 1])
+    oh, Sh, vh = host(o), host(S), host(var)
+    eo, es, ev = [], [], []
+    for (b, h) in heads:
+        g = ora.gate_prologue(sl(x["a_pre"], b, h), sl(x["w_pre"], b, h), sl(x["r_pre"], b, h),
+                              r_min=0.01)
+        ref = ora.diag_fwd(sl(x["q"], b, h), sl(x["k"], b, h), sl(x["v"], b, h), g["alpha"],
+                           g["omega"], g["r"])
+        eo.append((oh[b, :, h].ravel(), ref["o"].ravel()))
+        es.append((Sh[b, h].ravel(), ref["S"].ravel()))
+        ev.append((vh[b, h].ravel(), ref["p"].ravel()))
+    err = {n: rel_l2(np.concatenate([a for a, _ in pr]), np.concatenate([r for _, r in pr]))
+           for n, pr in (("o", eo), ("S", es), ("var", ev))}
+    print("preact %s heads=%s errors %s" % (w.name, heads, err), flush=True)
+    assert max(err.values()) <= TOL[w.io], err
