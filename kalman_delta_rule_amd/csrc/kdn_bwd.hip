@@ -282,6 +282,8 @@ struct BwdStage {
     IO qq[BWD_L * DK];                     // q (reverse pass only)
     IO vv[BWD_L * BWD_COLS];               // v, this block's columns
     IO dd[BWD_L * BWD_COLS];               // dL/do, this block's columns (reverse only)
+    float dl[BWD_L * BWD_COLS];            // innovations delta, this block's columns (reverse only)
+    float ck[DK * BWD_COLS];               // the state at the chunk start (reverse only)
 };
 
 // Copies of one 16-token chunk into stage s: tok0 is the chunk's first token
@@ -289,6 +291,8 @@ struct BwdStage {
 // `last`.  Piece p of an array (16 bytes) is copied by thread p + off, whole
 // waves active or idle, so each wave's LDS base is uniform.
 struct StageSrc {
+    const float* dlt;  // this (head, block)'s innovations from the chunk's first token
+    const float* ck;   // this (head, block)'s state at the chunk start, [dk][16]
     const float* alpha;
     const float* kap;
     const float* gsc;
@@ -321,7 +325,7 @@ __device__ __forceinline__ void bwd_stage_copy(BwdStage<IO, ISO, DK>& s, StageSr
         }
     }
     if constexpr (ISO) {
-        if (tid >= 192 && lane < L)
+        if (tid < L)  // first wave
             dma4(a.gsc + (tok0 + min(lane, last) * H) * 4, lds_u32(s.kp));
     }
     // k and q: L * DK / EK pieces
@@ -354,6 +358,22 @@ __device__ __forceinline__ void bwd_stage_copy(BwdStage<IO, ISO, DK>& s, StageSr
         const size_t g = (tok0 + tau * H) * dv + (size_t)blk * BWD_COLS + e % BWD_COLS;
         dma16(reinterpret_cast<const IO*>(a.go) + g, lds_u32(s.dd));
     }
+    // the innovations the forward pass stored, 16 floats per token, contiguous
+    // per (head, block): 64 pieces, by the fourth wave
+    const int pl = tid - 192;
+    if (rev && pl >= 0 && pl < L * BWD_COLS / 4) {
+        const int e = pl * 4, tau = min(e / BWD_COLS, last);
+        dma16(a.dlt + (size_t)tau * BWD_COLS + e % BWD_COLS, lds_u32(s.dl));
+    }
+    // the checkpoint, DK * 16 floats in the same [row][column] order
+    if (rev) {
+#pragma unroll
+        for (int p0 = 0; p0 < DK * BWD_COLS / 4; p0 += 256) {
+            const int p = p0 + tid;
+            if (p < DK * BWD_COLS / 4)
+                dma16(a.ck + (size_t)p * 4, lds_u32(s.ck) + (uint32_t)(p - lane) * 16u);
+        }
+    }
 }
 
 template <typename IO, bool ISO, int DK>
@@ -362,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void kdn_bwd_mem_kernel(BwdArgs args)
     // kernel arguments copied to locals once: nothing below reads them through
     // a pointer
     const BwdArgs a = args;
-    const StageSrc src{a.alpha, a.kap, a.gsc, a.k, a.q, a.v, a.go, a.H, a.dv};
+    const StageSrc src{nullptr, nullptr, a.alpha, a.kap, a.gsc, a.k, a.q, a.v, a.go, a.H, a.dv};
     float* const part = a.part;
     float* const ckpt = a.ckpt;
     constexpr int TPR = 256 / DK;        // threads per row of S
@@ -377,7 +397,6 @@ __global__ __launch_bounds__(256, 2) void kdn_bwd_mem_kernel(BwdArgs args)
     __shared__ __align__(16) Stage stL;
     __shared__ __align__(16) Stage stR;
     __shared__ float red[2][4][BWD_COLS];
-    __shared__ float dbuf[L][BWD_COLS];
 
     const int blk = blockIdx.x, nblk = gridDim.x, bh = blockIdx.y;
     const int H = a.H, T = a.T, dv = a.dv;
@@ -389,11 +408,17 @@ __global__ __launch_bounds__(256, 2) void kdn_bwd_mem_kernel(BwdArgs args)
     const int nch = (T + L - 1) / L;
     const size_t ntok = (size_t)a.B * T * H;
     IO* dvg = reinterpret_cast<IO*>(a.gv);
+    // this (head, block)'s innovations, 16 per token, stored by the forward pass
+    float* const dlt_wg = a.dlt + ((size_t)bh * nblk + blk) * (size_t)T * BWD_COLS;
+    float* const ck_wg = ckpt + ((size_t)bh * nblk + blk) * nch * (DK * BWD_COLS);
     float* ck = ckpt + ((size_t)bh * nblk + blk) * nch * (DK * BWD_COLS) + row * BWD_COLS + cb;
     auto tok_of = [&](int t) __attribute__((always_inline)) { return ((size_t)b * T + t) * H + h; };
 
     auto stage_copy = [&](Stage& st, int c, bool rev) __attribute__((always_inline)) {
-        bwd_stage_copy<IO, ISO, DK>(st, src, tok_of(c * L), min(L, T - c * L) - 1, blk, tid, rev);
+        StageSrc sc = src;
+        sc.dlt = dlt_wg + (size_t)c * L * BWD_COLS;
+        sc.ck = ck_wg + (size_t)c * (DK * BWD_COLS);
+        bwd_stage_copy<IO, ISO, DK>(st, sc, tok_of(c * L), min(L, T - c * L) - 1, blk, tid, rev);
     };
 
     int slot = 0;
@@ -461,6 +486,8 @@ __global__ __launch_bounds__(256, 2) void kdn_bwd_mem_kernel(BwdArgs args)
         if (rev) {
             mv(stL.qq, stR.qq, (int)sizeof(stL.qq));
             mv(stL.dd, stR.dd, (int)sizeof(stL.dd));
+            mv(stL.dl, stR.dl, (int)sizeof(stL.dl));
+            mv(stL.ck, stR.ck, (int)sizeof(stL.ck));
         }
     };
     for (int c = 0; c < nch; ++c) {
@@ -486,58 +513,55 @@ __global__ __launch_bounds__(256, 2) void kdn_bwd_mem_kernel(BwdArgs args)
                 x[j] = s[j] * kk;
             }
             col_sum(x);
+            float del[CPT];
 #pragma unroll
-            for (int j = 0; j < CPT; ++j)
-                s[j] += kap * (to_f32(cur.vv[tau * BWD_COLS + cb + j]) - x[j]);
+            for (int j = 0; j < CPT; ++j) {
+                del[j] = to_f32(cur.vv[tau * BWD_COLS + cb + j]) - x[j];
+                s[j] += kap * del[j];
+            }
+            if (row == 0) {  // every row holds the same innovations
+                float* dst = dlt_wg + (size_t)(c * L + tau) * BWD_COLS + cb;
+#pragma unroll
+                for (int j = 0; j < CPT; j += 4)
+                    *reinterpret_cast<float4*>(dst + j) = {del[j], del[j + 1], del[j + 2], del[j + 3]};
+            }
         }
     }
 
     // ---- reverse pass -----------------------------------------------------
-    float g[CPT], ckn[CPT];
+    float g[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
         g[j] = a.gS_T ? a.gS_T[((size_t)bh * DK + row) * dv + col0 + j] : 0.f;
     for (int c = nch - 1; c >= 0; --c) {
         if (c == nch - 1) {
-            copies_landed_barrier();  // the forward pass's readers are done
+            copies_landed_barrier();  // the forward pass's readers and writers are done
             stage_copy(stL, c, true);
-#pragma unroll
-            for (int j = 0; j < CPT; ++j)
-                ckn[j] = ck[(size_t)c * (DK * BWD_COLS) + j];
         }
-        copies_landed_barrier();  // chunk c in stL, its checkpoint loaded
+        copies_landed_barrier();  // chunk c (inputs, innovations, checkpoint) in stL
         move_stage(true);
         lds_barrier();
         const Stage& cur = stR;
         float st[L + 1][CPT];
 #pragma unroll
         for (int j = 0; j < CPT; ++j)
-            st[0][j] = ckn[j];
-        if (c > 0) {
+            st[0][j] = cur.ck[row * BWD_COLS + cb + j];
+        if (c > 0)
             stage_copy(stL, c - 1, true);
-#pragma unroll
-            for (int j = 0; j < CPT; ++j)
-                ckn[j] = ck[(size_t)(c - 1) * (DK * BWD_COLS) + j];
-        }
         const int t0 = c * L, len = min(L, T - t0);
-        // recompute the chunk's states and innovations
+        // recompute the chunk's states from the stored innovations
 #pragma unroll
         for (int tau = 0; tau < L; ++tau) {
             if (tau < len) {
                 const float al = cur.al[tau * DK + row], kk = to_f32(cur.kk[tau * DK + row]);
                 const float kap = gain(cur, tau, kk);
-                float x[CPT];
 #pragma unroll
                 for (int j = 0; j < CPT; ++j)
-                    x[j] = al * st[tau][j] * kk;
-                col_sum(x);
-#pragma unroll
-                for (int j = 0; j < CPT; ++j) {
-                    const float del = to_f32(cur.vv[tau * BWD_COLS + cb + j]) - x[j];
-                    dbuf[tau][cb + j] = del;  // every row stores the same value
-                    st[tau + 1][j] = al * st[tau][j] + kap * del;
-                }
+                    st[tau + 1][j] = al * st[tau][j] + kap * cur.dl[tau * BWD_COLS + cb + j];
             }
+            // one step's loads at a time: keeps the 17 states the only large
+            // live set (the loop has no barrier to bound the scheduler)
+            __builtin_amdgcn_sched_barrier(0);
         }
         // walk the chunk backwards
 #pragma unroll
@@ -554,7 +578,7 @@ __global__ __launch_bounds__(256, 2) void kdn_bwd_mem_kernel(BwdArgs args)
                     dov[j] = to_f32(cur.dd[tau * BWD_COLS + cb + j]);
                     g[j] = fmaf(qq, dov[j], g[j]);               // readout o = S^T q
                     sq = fmaf(st[tau + 1][j], dov[j], sq);      // dq = S do
-                    sk = fmaf(g[j], dbuf[tau][cb + j], sk);     // kapbar = G delta
+                    sk = fmaf(g[j], cur.dl[tau * BWD_COLS + cb + j], sk);  // kapbar = G delta
                     y[j] = g[j] * kap;
                 }
                 col_sum(y);                                     // delbar = G^T kap
@@ -817,6 +841,7 @@ size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv)
     else
         n += 2 * round64(ntok * dk) + round64(ntok);
     n += round64(bh * nch * dk * dv);        // checkpoints
+    n += round64(ntok * dv);                 // innovations
     n += round64(4 * nblk * ntok * dk);      // partials
     return n;
 }
@@ -840,6 +865,8 @@ void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws)
     }
     a.ckpt = p;
     p += round64(bh * nch * a.dk * a.dv);
+    a.dlt = p;
+    p += round64(ntok * a.dv);
     a.part = p;
 }
 

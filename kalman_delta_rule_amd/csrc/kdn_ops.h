@@ -72,6 +72,7 @@ struct BwdArgs {
     float* dd;     // Diagonal [B,T,H]: r + z
     float* gsc;    // Isotropic [B,T,H,4]: beta, b_{t-1}, mean alpha^2, |k|^2
     float* ckpt;   // [B*H][dv/16][ceil(T/16)][dk][16]: S at every 16th token
+    float* dlt;    // [B*H][dv/16][T][16]: innovations delta of every token
     float* part;   // [4][dv/16][B*T*H][dk]: per-column-block partial row sums
 };
 
