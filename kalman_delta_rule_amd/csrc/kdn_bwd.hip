@@ -15,8 +15,9 @@
 //
 // Three kernels, all fp32 arithmetic whatever the io type (divisions in the
 // gain recurrences through the hardware reciprocal, as in the forward):
-//   A  gain forward, one wave per (b,h): recomputes kap_t, p_{t-1} and
-//      r + z_t (Isotropic: beta_t, b_{t-1}, mean alpha^2, |k|^2) for every token.
+//   A  gain forward recompute by the chunk-parallel Moebius gain scan
+//      (kdn_gain.hip): kap_t, p_{t-1} and r + z_t (Isotropic: beta_t, b_{t-1},
+//      mean alpha^2, |k|^2) for every token.
 //   B  memory backward, one 256-thread workgroup per (b,h) and 16-column
 //      block of the value dimension (the columns of S evolve independently
 //      given the gain).  A forward pass stores S every 16 tokens; then for
@@ -125,113 +126,10 @@ __device__ __forceinline__ void rs_step(float (&v)[S], bool upper)
 }
 
 // ---------------------------------------------------------------------------
-// A: gain forward
+// A: gain forward recompute -- the chunk-parallel Moebius gain scan of
+// kdn_gain.hip (summaries, carry, replay), asked for the backward's outputs
 // ---------------------------------------------------------------------------
-constexpr int BWD_PF = 4;  // tokens of inputs in flight in the serial gain kernels
-
-// One token's gain inputs for this lane's channels (lane + 64 c).
-template <int CPL>
-struct GainIn {
-    float al[CPL], kk[CPL], om[CPL];  // om: Diagonal omega per channel
-    float r, omi;                     // omi: Isotropic omega per token
-};
-
-template <typename IO, bool ISO, int CPL>
-__device__ __forceinline__ void gain_in_load(GainIn<CPL>& x, const BwdArgs& a, size_t tok,
-                                             int lane)
-{
-    constexpr int DK = 64 * CPL;
-    const IO* kg = reinterpret_cast<const IO*>(a.k);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const size_t e = tok * DK + lane + 64 * c;
-        x.al[c] = a.alpha[e];
-        x.kk[c] = to_f32(kg[e]);
-        if constexpr (!ISO)
-            x.om[c] = a.omega[e];
-    }
-    x.r = a.r[tok];
-    if constexpr (ISO)
-        x.omi = a.omega[tok];
-}
-
-template <typename IO, bool ISO, int CPL>
-__global__ __launch_bounds__(64) void kdn_bwd_gain_fwd_kernel(BwdArgs args)
-{
-    constexpr int DK = 64 * CPL, D = BWD_PF;
-    const BwdArgs a = args;
-    const int bh = blockIdx.x, H = a.H, T = a.T;
-    const int b = bh / H, h = bh % H, lane = threadIdx.x;
-    const float mu = a.mu_h ? a.mu_h[h] : a.mu;
-    auto tok_of = [&](int t) __attribute__((always_inline)) { return ((size_t)b * T + t) * H + h; };
-    float p[CPL];
-    float bv = 0.f;
-    if constexpr (!ISO) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-            p[c] = a.var0 ? a.var0[(size_t)bh * DK + lane + 64 * c] : (a.c0 ? a.c0[h] : 1.f);
-    } else {
-        bv = a.var0 ? a.var0[bh] : (a.c0 ? a.c0[h] : 1.f);
-    }
-    auto step = [&](const GainIn<CPL>& x, int t) __attribute__((always_inline)) {
-        const size_t tok = tok_of(t);
-        if constexpr (!ISO) {
-            float ph[CPL], zp = 0.f;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                ph[c] = x.al[c] * x.al[c] * p[c] + x.om[c];
-                zp += ph[c] * x.kk[c] * x.kk[c];
-            }
-            const float d = x.r + wave_sum(zp);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const size_t e = tok * DK + lane + 64 * c;
-                a.kap[e] = ph[c] * x.kk[c] * rcp(d);
-                a.pprev[e] = p[c];
-                p[c] = ph[c] * rcp(1.f + (mu / x.r) * x.kk[c] * x.kk[c] * ph[c]);
-            }
-            if (lane == 0)
-                a.dd[tok] = d;
-        } else {
-            float sa = 0.f, sn = 0.f;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                sa += x.al[c] * x.al[c];
-                sn += x.kk[c] * x.kk[c];
-            }
-            const float am = wave_sum(sa) / (float)DK, n = wave_sum(sn);
-            const float bhat = am * bv + x.omi;
-            const float beta = bhat / (x.r + bhat * n);
-            if (lane == 0) {
-                float4 g = {beta, bv, am, n};
-                *reinterpret_cast<float4*>(a.gsc + tok * 4) = g;
-            }
-            bv = bhat / (1.f + mu * n / ((float)DK * x.r) * bhat);
-        }
-    };
-    // groups of D tokens with the next group's inputs in flight, then a tail
-    GainIn<CPL> ring[D];
-    int t = 0;
-    if (T >= D) {
-#pragma unroll
-        for (int j = 0; j < D; ++j)
-            gain_in_load<IO, ISO, CPL>(ring[j], a, tok_of(j), lane);
-    }
-    for (; t + D <= T; t += D) {
-#pragma unroll
-        for (int j = 0; j < D; ++j) {
-            const GainIn<CPL> cur = ring[j];
-            if (t + j + D < T)
-                gain_in_load<IO, ISO, CPL>(ring[j], a, tok_of(t + j + D), lane);
-            step(cur, t + j);
-        }
-    }
-    for (; t < T; ++t) {
-        GainIn<CPL> cur;
-        gain_in_load<IO, ISO, CPL>(cur, a, tok_of(t), lane);
-        step(cur, t);
-    }
-}
+constexpr int BWD_PF = 4;  // tokens of inputs in flight in the serial gain backward
 
 // ---------------------------------------------------------------------------
 // B: memory backward
@@ -840,6 +738,7 @@ size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv)
         n += round64(ntok * 4);
     else
         n += 2 * round64(ntok * dk) + round64(ntok);
+    n += round64(gain_workspace_floats(iso, B, T, H, dk));  // gain scan summaries and carries
     n += round64(bh * nch * dk * dv);        // checkpoints
     n += round64(ntok * dv);                 // innovations
     n += round64(4 * nblk * ntok * dk);      // partials
@@ -863,6 +762,8 @@ void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws)
         a.dd = p;
         p += round64(ntok);
     }
+    a.gscan = p;
+    p += round64(gain_workspace_floats(iso, a.B, a.T, a.H, a.dk));
     a.ckpt = p;
     p += round64(bh * nch * a.dk * a.dv);
     a.dlt = p;
@@ -876,9 +777,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream)
     constexpr int CPL = DK / 64;
     const int bh = a.B * a.H, nblk = a.dv / BWD_COLS;
     if (a.T > 0) {
-        hipLaunchKernelGGL((kdn_bwd_gain_fwd_kernel<IO, ISO, CPL>), dim3(bh), dim3(64), 0, stream,
-                           a);
-        hipError_t e = hipGetLastError();
+        const int nchunks = (a.T + 63) / 64;
+        const size_t width = ISO ? 1 : (size_t)DK;
+        GainArgs g{a.k, a.alpha, a.omega, a.r, a.var0, ISO ? nullptr : a.kap, nullptr, a.gscan,
+                   a.gscan + (size_t)bh * 4 * width * nchunks, a.B, a.T, a.H, DK, a.mu};
+        g.mu_h = a.mu_h;
+        g.c0 = a.c0;
+        g.pprev = a.pprev;
+        g.dd = a.dd;
+        g.gsc = a.gsc;
+        hipError_t e = launch_gain_scan(g, ISO, sizeof(IO) == 2 ? 1 : 0, stream);
         if (e != hipSuccess)
             return e;
     }

@@ -29,6 +29,8 @@
 
 namespace kdn {
 
+__device__ __forceinline__ float mu_of(const GainArgs& a, int h) { return a.mu_h ? a.mu_h[h] : a.mu; }
+
 constexpr int GC = 64;  // tokens per gain chunk
 
 __device__ __forceinline__ Mob mob_mul_raw(const Mob& later, const Mob& earlier)
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(DK) void gain_summary_diag(GainArgs a, int nchunks)
         const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
         const float al = a.alpha[tok * DK + i], w = a.omega[tok * DK + i];
         const float kv = to_f32(kg[tok * DK + i]);
-        const float u = (a.mu / a.r[tok]) * kv * kv;
+        const float u = (mu_of(a, h) / a.r[tok]) * kv * kv;
         const float a2 = al * al;
         P = mob_mul_raw(Mob{a2, w, u * a2, 1.f + u * w}, P);
         if ((t & 3) == 3)
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256) void gain_summary_iso(GainArgs a, int nchunks)
         Mob m = mob_identity();
         if (t < n_valid) {
             const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
-            const float u = a.mu * sn[t] / ((float)DK * a.r[tok]);
+            const float u = mu_of(a, h) * sn[t] / ((float)DK * a.r[tok]);
             const float w = a.omega[tok];
             m = Mob{sa[t], w, u * sa[t], 1.f + u * w};
         }
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(64) void gain_carry(GainArgs a, int width, int nchu
     const int row = blockIdx.x;  // bh * width + i
     const int bh = row / width, i = row % width;
     const int lane = threadIdx.x;
-    const float p0 = a.var0 ? a.var0[(size_t)bh * width + i] : 1.f;
+    const float p0 = a.var0 ? a.var0[(size_t)bh * width + i] : (a.c0 ? a.c0[bh % a.H] : 1.f);
     const size_t es = (size_t)width * nchunks;
     const float* s = a.summ + (size_t)bh * 4 * es + (size_t)i * nchunks;
     Mob run = mob_identity();  // product of all earlier 64-chunk groups
@@ -164,7 +166,8 @@ __global__ __launch_bounds__(64) void gain_carry(GainArgs a, int width, int nchu
         run = mob_compose(tot, run);
     }
     if (lane == 0)
-        a.var_T[(size_t)bh * width + i] = mob_apply(run, p0);
+        if (a.var_T)
+            a.var_T[(size_t)bh * width + i] = mob_apply(run, p0);
 }
 
 // ---------------------------------------------------------------- pass 3
@@ -187,7 +190,9 @@ __global__ __launch_bounds__(DK) void gain_replay_diag(GainArgs a, int nchunks)
             const float al = a.alpha[tok * DK + i], w = a.omega[tok * DK + i];
             kv = to_f32(kg[tok * DK + i]);
             ph = al * al * p + w;
-            const float u = (a.mu / a.r[tok]) * kv * kv;
+            const float u = (mu_of(a, h) / a.r[tok]) * kv * kv;
+            if (a.pprev)
+                a.pprev[tok * DK + i] = p;
             p = ph * rcp(1.f + u * ph);
         }
         kk[t] = kv;
@@ -211,6 +216,8 @@ __global__ __launch_bounds__(DK) void gain_replay_diag(GainArgs a, int nchunks)
         if (t < n_valid) {
             const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
             a.kappa[tok * DK + i] = s_ph[t][i] * kk[t] * rcp(a.r[tok] + s_z[t]);
+            if (a.dd && i == 0)
+                a.dd[tok] = a.r[tok] + s_z[t];
         }
     }
 }
@@ -232,17 +239,21 @@ __global__ __launch_bounds__(256) void gain_replay_iso(GainArgs a, int nchunks)
             const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
             r = a.r[tok];
             w = a.omega[tok];
-            const float u = a.mu * sn[t] / ((float)DK * r);
+            const float u = mu_of(a, h) * sn[t] / ((float)DK * r);
             m = Mob{sa[t], w, u * sa[t], 1.f + u * w};
         }
         const Mob excl = mob_wave_shift_right(mob_wave_scan_inclusive(m));
         const float bprev = mob_apply(excl, a.carry[(size_t)bh * nchunks + c]);
         const float bhat = sa[t] * bprev + w;
         sbeta[t] = bhat * rcp(r + bhat * sn[t]);
+        if (a.gsc && t < n_valid) {
+            const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
+            *reinterpret_cast<float4*>(a.gsc + tok * 4) = float4{sbeta[t], bprev, sa[t], sn[t]};
+        }
     }
     __syncthreads();
     const IO* kg = reinterpret_cast<const IO*>(a.k);
-    for (int e = threadIdx.x; e < n_valid * DK; e += 256) {
+    for (int e = threadIdx.x; a.kappa && e < n_valid * DK; e += 256) {
         const int t = e / DK, i = e % DK;
         const size_t idx = (((size_t)b * a.T + t0 + t) * a.H + h) * DK + i;
         a.kappa[idx] = sbeta[t] * to_f32(kg[idx]);
@@ -272,7 +283,7 @@ static hipError_t launch_gain_t(const GainArgs& a0, bool iso, hipStream_t stream
                                stream, a, nchunks);
     }
     hipLaunchKernelGGL(gain_carry, dim3(BH * width), dim3(64), 0, stream, a, width, nchunks);
-    if (a.kappa && nchunks > 0) {
+    if ((a.kappa || a.gsc) && nchunks > 0) {
         if (iso)
             hipLaunchKernelGGL((gain_replay_iso<IO, DK>), dim3(BH * nchunks), dim3(256), 0,
                                stream, a, nchunks);

@@ -36,6 +36,12 @@ struct GainArgs {
     float* carry;       // workspace: chunk-entry variances [BH][nchunks][width]
     int B, T, H, dk;
     float mu;
+    // for the backward's recompute (null in the standalone gain scan)
+    const float* mu_h = nullptr;  // [H] per-head information scale
+    const float* c0 = nullptr;    // [H] initial variance when var0 is null
+    float* pprev = nullptr;       // Diagonal [B,T,H,dk]: variance before every token
+    float* dd = nullptr;          // Diagonal [B,T,H]: r + z
+    float* gsc = nullptr;         // Isotropic [B,T,H,4]: beta, b_{t-1}, mean alpha^2, |k|^2
 };
 
 struct BwdArgs {
@@ -71,6 +77,7 @@ struct BwdArgs {
     float* pprev;  // Diagonal [B,T,H,dk]: variance before every token
     float* dd;     // Diagonal [B,T,H]: r + z
     float* gsc;    // Isotropic [B,T,H,4]: beta, b_{t-1}, mean alpha^2, |k|^2
+    float* gscan;  // the gain scan's chunk summaries and carries
     float* ckpt;   // [B*H][dv/16][ceil(T/16)][dk][16]: S at every 16th token
     float* dlt;    // [B*H][dv/16][T][16]: innovations delta of every token
     float* part;   // [4][dv/16][B*T*H][dk]: per-column-block partial row sums

@@ -278,14 +278,16 @@ def test_bwd_validation(L):
     assert bwd(dv=64, dmu=base["dalpha"] + 4) == -1 and "overlap" in msg()
     assert bwd(ws_bytes=16) == -3 and "workspace" in msg()
     assert bwd(ws=base["ws"] + 4) == -1 and "16-byte" in msg()
-    # workspace: gain pieces, the state every 16th token, every token's
-    # innovations, 4 partial row sums per 16-column block
+    # workspace: gain pieces, the gain scan's summaries and carries, the state
+    # every 16th token, every token's innovations, 4 partial row sums per
+    # 16-column block
     B, T, H, dk, dv = 2, 40, 3, 128, 64
     ntok, nch, nblk = B * T * H, 3, dv // 16
     r64 = lambda n: (n + 63) // 64 * 64
     common = r64(B * H * nch * dk * dv) + r64(ntok * dv) + r64(4 * nblk * ntok * dk)
-    diag = 2 * r64(ntok * dk) + r64(ntok) + common
-    iso = r64(ntok * 4) + common
+    scan = lambda width: r64(B * H * 1 * width * 5)  # the gain scan: one 64-token chunk
+    diag = 2 * r64(ntok * dk) + r64(ntok) + scan(dk) + common
+    iso = r64(ntok * 4) + scan(1) + common
     assert L.kdn_bwd_workspace_size(0, B, T, H, dk, dv) == 4 * diag
     assert L.kdn_bwd_workspace_size(1, B, T, H, dk, dv) == 4 * iso
     assert L.kdn_bwd_workspace_size(0, B, 0, H, dk, dv) == 0
