@@ -25,9 +25,10 @@
 //      into registers and walked backwards.  dv is complete per column and
 //      written here; the four row vectors that sum over all columns (dq, kapbar,
 //      dk and dalpha of the memory) are written as per-block partials.
-//   C  gain backward, one wave per (b,h): sums the partials and runs the
-//      variance recurrence's adjoint backwards, writing dq, dk, dalpha,
-//      domega, dr and the initial variance's and information scale's gradients.
+//   C  partial merge (dq and the summed row vectors), then the variance
+//      recurrence's adjoint as a chunked affine scan (summaries, carry,
+//      replay), writing dk, dalpha, domega, dr and the initial variance's and
+//      information scale's gradients.
 // Each thread of B owns one row of S (one key channel) and 8 (d_k = 128) or 4
 // (d_k = 64) columns, so row reductions stay in a lane pair or quad and the
 // column reductions (delta, delbar) cross the workgroup through LDS once per
@@ -129,8 +130,6 @@ __device__ __forceinline__ void rs_step(float (&v)[S], bool upper)
 // A: gain forward recompute -- the chunk-parallel Moebius gain scan of
 // kdn_gain.hip (summaries, carry, replay), asked for the backward's outputs
 // ---------------------------------------------------------------------------
-constexpr int BWD_PF = 4;  // tokens of inputs in flight in the serial gain backward
-
 // ---------------------------------------------------------------------------
 // B: memory backward
 // ---------------------------------------------------------------------------
@@ -553,175 +552,230 @@ __global__ __launch_bounds__(256) void kdn_bwd_merge_kernel(BwdArgs args, int nb
         w[kd * kstride4] = sum[kd];
 }
 
-// One token's inputs of the variance recurrence's adjoint for this lane's
-// channels.
-template <int CPL>
-struct RevIn {
-    float kb[CPL], kmb[CPL], amb[CPL];  // summed kapbar, memory dk, memory dalpha
-    float kk[CPL], al[CPL];
-    float pp[CPL], om[CPL];             // Diagonal: p_{t-1}, omega
-    float r, d;                         // Diagonal: r + z
-    float4 gs;                          // Isotropic: beta, b_{t-1}, mean alpha^2, |k|^2
-    float omi;                          // Isotropic omega
+// The variance recurrence's adjoint is affine in the carried gradient, per
+// channel for Diagonal (pbar_{t-1} = A_t pbar_t + B_t, A_t = alpha^2 / den^2,
+// B_t = alpha^2 (kapbar k / d + dbar k^2)) and per head for Isotropic
+// (bbar_{t-1} = A_t bbar_t + B_t, A_t = a / den^2, B_t = a betabar r / e^2).
+// Everything else a token needs is known beforehand (dbar = -sum kapbar kap
+// / d and betabar = sum kapbar k do not depend on the carried gradient), so
+// it runs as a chunked scan over GR_C-token chunks: summaries (A, B) per
+// chunk and channel, a carry across chunks from the last, and a replay of
+// each chunk from its carried gradient that writes every output.
+constexpr int GR_C = 64;
+
+// Per-token quantities of one chunk in LDS, one thread per channel.
+template <int DK>
+struct GrChunk {
+    float red[GR_C][DK + 1];  // per-token, per-channel terms of a channel sum
+    float tok[GR_C];          // dbar (Diagonal) / betabar (Isotropic) per token
 };
 
-template <typename IO, bool ISO, int CPL>
-__device__ __forceinline__ void rev_in_load(RevIn<CPL>& x, const BwdArgs& a, size_t tok,
-                                            size_t kstride, int lane)
+template <typename IO, bool ISO, int DK>
+__device__ __forceinline__ void gr_load(const BwdArgs& a, size_t kstride, size_t tok, int i,
+                                        float& kb, float& kk, float& al, float& pp, float& om)
 {
-    constexpr int DK = 64 * CPL;
-    const IO* kg = reinterpret_cast<const IO*>(a.k);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const size_t e = tok * DK + lane + 64 * c;
-        x.kb[c] = a.part[kstride + e];
-        x.kmb[c] = a.part[2 * kstride + e];
-        x.amb[c] = a.part[3 * kstride + e];
-        x.kk[c] = to_f32(kg[e]);
-        x.al[c] = a.alpha[e];
-        if constexpr (!ISO) {
-            x.pp[c] = a.pprev[e];
-            x.om[c] = a.omega[e];
-        }
-    }
-    x.r = a.r[tok];
+    const size_t e = tok * DK + i;
+    kb = a.part[kstride + e];
+    kk = to_f32(reinterpret_cast<const IO*>(a.k)[e]);
+    al = a.alpha[e];
     if constexpr (!ISO) {
-        x.d = a.dd[tok];
-    } else {
-        x.gs = *reinterpret_cast<const float4*>(a.gsc + tok * 4);
-        x.omi = a.omega[tok];
+        pp = a.pprev[e];
+        om = a.omega[e];
     }
 }
 
-template <typename IO, bool ISO, int CPL>
-__global__ __launch_bounds__(64) void kdn_bwd_gain_rev_kernel(BwdArgs args, int nblk)
+// Fill g.tok with dbar or betabar for the chunk's nv tokens.
+template <typename IO, bool ISO, int DK>
+__device__ __forceinline__ void gr_token_sums(const BwdArgs& a, GrChunk<DK>& g, size_t kstride,
+                                              size_t tok0, size_t tstride, int nv, int i)
 {
-    constexpr int DK = 64 * CPL, D = BWD_PF;
-    const BwdArgs a = args;
-    const int bh = blockIdx.x, H = a.H, T = a.T;
-    const int b = bh / H, h = bh % H, lane = threadIdx.x;
-    const float mu = a.mu_h ? a.mu_h[h] : a.mu;
-    const size_t ntok = (size_t)a.B * T * H, kstride = (size_t)nblk * ntok * DK;
-    IO* dkg = reinterpret_cast<IO*>(a.gk);
-    auto tok_of = [&](int t) __attribute__((always_inline)) { return ((size_t)b * T + t) * H + h; };
-
-    float pbar[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-        pbar[c] = 0.f;
-    float bbar = 0.f, mub = 0.f;
-    if constexpr (!ISO) {
-        if (a.gvar_T)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                pbar[c] = a.gvar_T[(size_t)bh * DK + lane + 64 * c];
-    } else {
-        bbar = a.gvar_T ? a.gvar_T[bh] : 0.f;
-    }
-
-    auto step = [&](const RevIn<CPL>& x, int t) __attribute__((always_inline)) {
-        const size_t tok = tok_of(t);
-        const float rt = x.r;
+    for (int t = 0; t < nv; ++t) {
+        const size_t tok = tok0 + t * tstride;
+        float kb, kk, al, pp = 0.f, om = 0.f;
+        gr_load<IO, ISO, DK>(a, kstride, tok, i, kb, kk, al, pp, om);
         if constexpr (!ISO) {
-            const float d = x.d;
-            float ph[CPL], kap[CPL], ub[CPL], phb[CPL];
-            float s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                ph[c] = x.al[c] * x.al[c] * x.pp[c] + x.om[c];
-                kap[c] = ph[c] * x.kk[c] * rcp(d);
-                const float u = (mu / rt) * x.kk[c] * x.kk[c];
-                const float den = 1.f + u * ph[c];
-                phb[c] = pbar[c] * rcp(den * den);
-                ub[c] = -pbar[c] * ph[c] * ph[c] * rcp(den * den);
-                s1 += x.kb[c] * kap[c];
-                s2 += ub[c] * u;
-                s3 += ub[c] * x.kk[c] * x.kk[c];
-            }
-            const float dbar = -wave_sum(s1) / d;
-            const float rbar = dbar - wave_sum(s2) / rt;
-            mub += s3 / rt;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const size_t e = tok * DK + lane + 64 * c;
-                const float kk = x.kk[c];
-                phb[c] += x.kb[c] * kk / d + dbar * kk * kk;
-                const float kbar = x.kmb[c] + 2.f * ub[c] * (mu / rt) * kk +
-                                   x.kb[c] * ph[c] / d + 2.f * dbar * ph[c] * kk;
-                dkg[e] = from_f32<IO>(kbar);
-                a.galpha[e] = x.amb[c] + 2.f * phb[c] * x.al[c] * x.pp[c];
-                a.gomega[e] = phb[c];
-                pbar[c] = phb[c] * x.al[c] * x.al[c];
-            }
-            if (lane == 0)
-                a.gr[tok] = rbar;
+            const float ph = al * al * pp + om;
+            g.red[t][i] = kb * ph * kk * rcp(a.dd[tok]);  // kapbar kap
         } else {
-            const float beta = x.gs.x, bprev = x.gs.y, am = x.gs.z, n = x.gs.w;
-            const float bhat = am * bprev + x.omi;
+            g.red[t][i] = kb * kk;
+        }
+    }
+    __syncthreads();
+    if (i < nv) {
+        float sum = 0.f;
+        for (int j = 0; j < DK; ++j)
+            sum += g.red[i][j];
+        const size_t tok = tok0 + i * tstride;
+        g.tok[i] = ISO ? sum : -sum * rcp(a.dd[tok]);
+    }
+    __syncthreads();
+}
+
+// pass 1: each chunk's affine map from the gradient after its last token to
+// the gradient before its first
+template <typename IO, bool ISO, int DK>
+__global__ __launch_bounds__(DK) void kdn_bwd_gr_summary_kernel(BwdArgs args, int nblk, int nchunks)
+{
+    const BwdArgs a = args;
+    __shared__ GrChunk<DK> g;
+    const int bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks, i = threadIdx.x;
+    const int H = a.H, T = a.T, b = bh / H, h = bh % H;
+    const int t0 = c * GR_C, nv = min(GR_C, T - t0);
+    const float mu = a.mu_h ? a.mu_h[h] : a.mu;
+    const size_t kstride = (size_t)nblk * a.B * T * H * DK;
+    const size_t tok0 = ((size_t)b * T + t0) * H + h, tstride = H;
+    gr_token_sums<IO, ISO, DK>(a, g, kstride, tok0, tstride, nv, i);
+    float A = 1.f, Bc = 0.f;
+    for (int t = nv - 1; t >= 0; --t) {
+        const size_t tok = tok0 + t * tstride;
+        const float rt = a.r[tok];
+        float At, Bt;
+        if constexpr (!ISO) {
+            float kb, kk, al, pp, om;
+            gr_load<IO, ISO, DK>(a, kstride, tok, i, kb, kk, al, pp, om);
+            const float d = a.dd[tok], ph = al * al * pp + om;
+            const float den = 1.f + (mu / rt) * kk * kk * ph;
+            const float inv2 = rcp(den * den);
+            At = al * al * inv2;
+            Bt = al * al * (kb * kk * rcp(d) + g.tok[t] * kk * kk);
+        } else {
+            const float4 gs = *reinterpret_cast<const float4*>(a.gsc + tok * 4);
+            const float bhat = gs.z * gs.y + a.omega[tok], n = gs.w;
             const float e = rt + bhat * n;
+            const float den = 1.f + mu * n / ((float)DK * rt) * bhat;
+            At = gs.z * rcp(den * den);
+            Bt = gs.z * g.tok[t] * rt * rcp(e * e);
+        }
+        A = At * A;
+        Bc = At * Bc + Bt;
+    }
+    const size_t width = ISO ? 1 : DK;
+    if (!ISO || i == 0) {
+        const size_t o = (((size_t)bh * nchunks + c) * width + (ISO ? 0 : i)) * 2;
+        a.gr_sum[o] = A;
+        a.gr_sum[o + 1] = Bc;
+    }
+    if (i < nv)
+        a.gr_tok[tok0 + i * tstride] = g.tok[i];
+}
+
+// pass 2: the gradient after every chunk's last token, from the last chunk;
+// the initial variance's gradient at the end
+__global__ __launch_bounds__(256) void kdn_bwd_gr_carry_kernel(BwdArgs args, int width, int nchunks)
+{
+    const BwdArgs a = args;
+    const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;  // (b,h) * width + channel
+    if (row >= (size_t)a.B * a.H * width)
+        return;
+    const size_t bh = row / width, i = row % width;
+    float gbar = a.gvar_T ? a.gvar_T[row] : 0.f;
+    for (int c = nchunks - 1; c >= 0; --c) {
+        const size_t o = (bh * nchunks + c) * width + i;
+        a.gr_carry[o] = gbar;
+        gbar = a.gr_sum[o * 2] * gbar + a.gr_sum[o * 2 + 1];
+    }
+    if (a.gvar0)
+        a.gvar0[row] = gbar;
+}
+
+// pass 3: replay every chunk from its carried gradient, writing dk, dalpha,
+// domega, dr and a partial information-scale gradient per chunk
+template <typename IO, bool ISO, int DK>
+__global__ __launch_bounds__(DK) void kdn_bwd_gr_replay_kernel(BwdArgs args, int nblk, int nchunks)
+{
+    const BwdArgs a = args;
+    __shared__ GrChunk<DK> g;
+    __shared__ float smu[DK / 64];
+    const int bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks, i = threadIdx.x;
+    const int H = a.H, T = a.T, b = bh / H, h = bh % H;
+    const int t0 = c * GR_C, nv = min(GR_C, T - t0);
+    const float mu = a.mu_h ? a.mu_h[h] : a.mu;
+    const size_t kstride = (size_t)nblk * a.B * T * H * DK;
+    const size_t tok0 = ((size_t)b * T + t0) * H + h, tstride = H;
+    IO* dkg = reinterpret_cast<IO*>(a.gk);
+    if (i < nv)
+        g.tok[i] = a.gr_tok[tok0 + i * tstride];
+    __syncthreads();
+    const size_t width = ISO ? 1 : DK;
+    float gbar = a.gr_carry[((size_t)bh * nchunks + c) * width + (ISO ? 0 : i)];
+    float mub = 0.f;
+    for (int t = nv - 1; t >= 0; --t) {
+        const size_t tok = tok0 + t * tstride, e = tok * DK + i;
+        const float rt = a.r[tok];
+        float kb, kk, al, pp = 0.f, om = 0.f;
+        gr_load<IO, ISO, DK>(a, kstride, tok, i, kb, kk, al, pp, om);
+        const float kmb = a.part[2 * kstride + e], amb = a.part[3 * kstride + e];
+        if constexpr (!ISO) {
+            const float d = a.dd[tok], dbar = g.tok[t];
+            const float ph = al * al * pp + om;
+            const float u = (mu / rt) * kk * kk;
+            const float den = 1.f + u * ph, inv2 = rcp(den * den);
+            const float ub = -gbar * ph * ph * inv2;
+            const float phb = gbar * inv2 + kb * kk * rcp(d) + dbar * kk * kk;
+            dkg[e] = from_f32<IO>(kmb + 2.f * ub * (mu / rt) * kk + kb * ph * rcp(d) +
+                                  2.f * dbar * ph * kk);
+            a.galpha[e] = amb + 2.f * phb * al * pp;
+            a.gomega[e] = phb;
+            g.red[t][i] = ub * u;
+            mub += ub * kk * kk / rt;
+            gbar = phb * al * al;
+        } else {
+            const float4 gs = *reinterpret_cast<const float4*>(a.gsc + tok * 4);
+            const float beta = gs.x, bprev = gs.y, am = gs.z, n = gs.w, betab = g.tok[t];
+            const float bhat = am * bprev + a.omega[tok];
+            const float ee = rt + bhat * n;
             const float u = mu * n / ((float)DK * rt);
-            const float den = 1.f + u * bhat;
-            float bhb = bbar * rcp(den * den);
-            const float ub = -bbar * bhat * bhat * rcp(den * den);
-            float nb = ub * mu / ((float)DK * rt);
-            float rbar = -ub * u / rt;
-            mub += ub * n / ((float)DK * rt);
-            float sb = 0.f;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                sb += x.kb[c] * x.kk[c];
-            const float betab = wave_sum(sb);
-            bhb += betab * rt / (e * e);
-            rbar -= betab * bhat / (e * e);
-            nb -= betab * bhat * bhat / (e * e);
+            const float den = 1.f + u * bhat, inv2 = rcp(den * den);
+            const float ub = -gbar * bhat * bhat * inv2;
+            const float bhb = gbar * inv2 + betab * rt * rcp(ee * ee);
+            const float nb = ub * mu / ((float)DK * rt) - betab * bhat * bhat * rcp(ee * ee);
             const float abar = bhb * bprev;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const size_t ei = tok * DK + lane + 64 * c;
-                dkg[ei] = from_f32<IO>(x.kmb[c] + beta * x.kb[c] + 2.f * nb * x.kk[c]);
-                a.galpha[ei] = x.amb[c] + 2.f * abar * x.al[c] / (float)DK;
-            }
-            if (lane == 0) {
+            dkg[e] = from_f32<IO>(kmb + beta * kb + 2.f * nb * kk);
+            a.galpha[e] = amb + 2.f * abar * al / (float)DK;
+            if (i == 0) {
                 a.gomega[tok] = bhb;
-                a.gr[tok] = rbar;
+                a.gr[tok] = -ub * u / rt - betab * bhat * rcp(ee * ee);
+                mub += ub * n / ((float)DK * rt);
             }
-            bbar = bhb * am;
+            gbar = bhb * am;
         }
-    };
-    // groups of D tokens, last first, with the next group's inputs in flight
-    RevIn<CPL> ring[D];
-    int t = T - 1;
-    if (T >= D) {
-#pragma unroll
-        for (int j = 0; j < D; ++j)
-            rev_in_load<IO, ISO, CPL>(ring[j], a, tok_of(t - j), kstride, lane);
-    }
-    for (; t - (D - 1) >= 0; t -= D) {
-#pragma unroll
-        for (int j = 0; j < D; ++j) {
-            const RevIn<CPL> cur = ring[j];
-            if (t - j - D >= 0)
-                rev_in_load<IO, ISO, CPL>(ring[j], a, tok_of(t - j - D), kstride, lane);
-            step(cur, t - j);
-        }
-    }
-    for (; t >= 0; --t) {
-        RevIn<CPL> cur;
-        rev_in_load<IO, ISO, CPL>(cur, a, tok_of(t), kstride, lane);
-        step(cur, t);
     }
     if constexpr (!ISO) {
-        if (a.gvar0)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                a.gvar0[(size_t)bh * DK + lane + 64 * c] = pbar[c];
+        __syncthreads();
+        if (i < nv) {
+            float s2 = 0.f;
+            for (int j = 0; j < DK; ++j)
+                s2 += g.red[i][j];
+            const size_t tok = tok0 + i * tstride;
+            a.gr[tok] = g.tok[i] - s2 / a.r[tok];
+        }
         mub = wave_sum(mub);
+        if ((i & 63) == 0)
+            smu[i >> 6] = mub;
+        __syncthreads();
+        if (i == 0) {
+            float m = 0.f;
+            for (int w = 0; w < DK / 64; ++w)
+                m += smu[w];
+            a.gr_mu[(size_t)bh * nchunks + c] = m;
+        }
     } else {
-        if (a.gvar0 && lane == 0)
-            a.gvar0[bh] = bbar;
+        if (i == 0)
+            a.gr_mu[(size_t)bh * nchunks + c] = mub;
     }
-    if (a.gmu && lane == 0)
-        a.gmu[bh] = mub;
+}
+
+// pass 4: the information scale's gradient per (b,h), summed over chunks
+__global__ __launch_bounds__(256) void kdn_bwd_gr_mu_kernel(BwdArgs args, int nchunks)
+{
+    const BwdArgs a = args;
+    const size_t bh = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (bh >= (size_t)a.B * a.H)
+        return;
+    float m = 0.f;
+    for (int c = 0; c < nchunks; ++c)
+        m += a.gr_mu[bh * nchunks + c];
+    a.gmu[bh] = m;
 }
 
 // ---------------------------------------------------------------------------
@@ -739,6 +793,9 @@ size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv)
     else
         n += 2 * round64(ntok * dk) + round64(ntok);
     n += round64(gain_workspace_floats(iso, B, T, H, dk));  // gain scan summaries and carries
+    const size_t ngc = ((size_t)T + GR_C - 1) / GR_C, width = iso ? 1 : (size_t)dk;
+    n += round64(bh * ngc * width * 2) + round64(bh * ngc * width) + round64(ntok) +
+         round64(bh * ngc);                  // gain backward: summaries, carries, dbar, mu parts
     n += round64(bh * nch * dk * dv);        // checkpoints
     n += round64(ntok * dv);                 // innovations
     n += round64(4 * nblk * ntok * dk);      // partials
@@ -764,6 +821,15 @@ void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws)
     }
     a.gscan = p;
     p += round64(gain_workspace_floats(iso, a.B, a.T, a.H, a.dk));
+    const size_t ngc = ((size_t)a.T + GR_C - 1) / GR_C, width = iso ? 1 : (size_t)a.dk;
+    a.gr_sum = p;
+    p += round64(bh * ngc * width * 2);
+    a.gr_carry = p;
+    p += round64(bh * ngc * width);
+    a.gr_tok = p;
+    p += round64(ntok);
+    a.gr_mu = p;
+    p += round64(bh * ngc);
     a.ckpt = p;
     p += round64(bh * nch * a.dk * a.dv);
     a.dlt = p;
@@ -774,7 +840,6 @@ void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws)
 template <typename IO, bool ISO, int DK>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream)
 {
-    constexpr int CPL = DK / 64;
     const int bh = a.B * a.H, nblk = a.dv / BWD_COLS;
     if (a.T > 0) {
         const int nchunks = (a.T + 63) / 64;
@@ -802,9 +867,32 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream)
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((kdn_bwd_gain_rev_kernel<IO, ISO, CPL>), dim3(bh), dim3(64), 0, stream, a,
-                       nblk);
-    return hipGetLastError();
+    const int ngc = (a.T + GR_C - 1) / GR_C, width = ISO ? 1 : DK;
+    if (ngc > 0) {
+        hipLaunchKernelGGL((kdn_bwd_gr_summary_kernel<IO, ISO, DK>), dim3(bh * ngc), dim3(DK), 0,
+                           stream, a, nblk, ngc);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL(kdn_bwd_gr_carry_kernel, dim3((bh * width + 255) / 256), dim3(256), 0,
+                       stream, a, width, ngc);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    if (ngc > 0) {
+        hipLaunchKernelGGL((kdn_bwd_gr_replay_kernel<IO, ISO, DK>), dim3(bh * ngc), dim3(DK), 0,
+                           stream, a, nblk, ngc);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    if (a.gmu) {
+        hipLaunchKernelGGL(kdn_bwd_gr_mu_kernel, dim3((bh + 255) / 256), dim3(256), 0, stream, a,
+                           ngc);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, bool iso, int io_dtype, hipStream_t stream)

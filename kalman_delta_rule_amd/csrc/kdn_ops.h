@@ -78,6 +78,10 @@ struct BwdArgs {
     float* dd;     // Diagonal [B,T,H]: r + z
     float* gsc;    // Isotropic [B,T,H,4]: beta, b_{t-1}, mean alpha^2, |k|^2
     float* gscan;  // the gain scan's chunk summaries and carries
+    float* gr_sum;   // gain backward: affine map (A, B) per 64-token chunk and channel
+    float* gr_carry; // gain backward: carried gradient after each chunk
+    float* gr_tok;   // gain backward: dbar / betabar per token
+    float* gr_mu;    // gain backward: information-scale gradient per (b,h) and chunk
     float* ckpt;   // [B*H][dv/16][ceil(T/16)][dk][16]: S at every 16th token
     float* dlt;    // [B*H][dv/16][T][16]: innovations delta of every token
     float* part;   // [4][dv/16][B*T*H][dk]: per-column-block partial row sums

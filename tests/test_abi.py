@@ -286,8 +286,11 @@ def test_bwd_validation(L):
     r64 = lambda n: (n + 63) // 64 * 64
     common = r64(B * H * nch * dk * dv) + r64(ntok * dv) + r64(4 * nblk * ntok * dk)
     scan = lambda width: r64(B * H * 1 * width * 5)  # the gain scan: one 64-token chunk
-    diag = 2 * r64(ntok * dk) + r64(ntok) + scan(dk) + common
-    iso = r64(ntok * 4) + scan(1) + common
+    # the gain backward's scan: (A, B) and carry per chunk and width, a
+    # scalar per token, an information-scale part per chunk
+    grad = lambda width: r64(B * H * width * 2) + r64(B * H * width) + r64(ntok) + r64(B * H)
+    diag = 2 * r64(ntok * dk) + r64(ntok) + scan(dk) + grad(dk) + common
+    iso = r64(ntok * 4) + scan(1) + grad(1) + common
     assert L.kdn_bwd_workspace_size(0, B, T, H, dk, dv) == 4 * diag
     assert L.kdn_bwd_workspace_size(1, B, T, H, dk, dv) == 4 * iso
     assert L.kdn_bwd_workspace_size(0, B, 0, H, dk, dv) == 0
