@@ -240,7 +240,7 @@ kdn_status kdn_fwd_preact(int variant, int B, int T, int H, int dk, int dv, int 
  * dk in {64, 128}, dv a multiple of 16 up to 256; fp32 arithmetic whatever
  * the io type.  q, k, v, d_o and alpha are 16-byte aligned, the other fp32
  * arrays 4-byte aligned, dq / dk / dv aligned to their element size.  The forward is recomputed inside (the gain, then the state
- * at every 16th token); the workspace (kdn_bwd_workspace_size bytes,
+ * at every 16th token and every token's innovations); the workspace (kdn_bwd_workspace_size bytes,
  * 16-byte aligned) holds that and per-block partial sums.  Asynchronous on
  * `stream`; validation as for the forward.
  */

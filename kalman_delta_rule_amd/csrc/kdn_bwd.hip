@@ -13,16 +13,17 @@
 //   S^bar = G - k delbar^T, dk -= S^ delbar, dalpha += rowsum(S^bar (.) S_{t-1}),
 //   G <- diag(alpha) S^bar; then the variance recurrence's adjoint per channel.
 //
-// Three kernels, all fp32 arithmetic whatever the io type (divisions in the
+// Three stages, all fp32 arithmetic whatever the io type (divisions in the
 // gain recurrences through the hardware reciprocal, as in the forward):
 //   A  gain forward recompute by the chunk-parallel Moebius gain scan
 //      (kdn_gain.hip): kap_t, p_{t-1} and r + z_t (Isotropic: beta_t, b_{t-1},
 //      mean alpha^2, |k|^2) for every token.
 //   B  memory backward, one 256-thread workgroup per (b,h) and 16-column
 //      block of the value dimension (the columns of S evolve independently
-//      given the gain).  A forward pass stores S every 16 tokens; then for
-//      each 16-token chunk, last first, the chunk's 17 states are recomputed
-//      into registers and walked backwards.  dv is complete per column and
+//      given the gain).  A forward pass stores S every 16 tokens and every
+//      token's innovations; then for each 16-token chunk, last first, the
+//      chunk's 17 states are recomputed into registers (no reduction: the
+//      innovations are known) and walked backwards.  dv is complete per column and
 //      written here; the four row vectors that sum over all columns (dq, kapbar,
 //      dk and dalpha of the memory) are written as per-block partials.
 //   C  partial merge (dq and the summed row vectors), then the variance
@@ -31,8 +32,8 @@
 //      information scale's gradients.
 // Each thread of B owns one row of S (one key channel) and 8 (d_k = 128) or 4
 // (d_k = 64) columns, so row reductions stay in a lane pair or quad and the
-// column reductions (delta, delbar) cross the workgroup through LDS once per
-// token.
+// column reductions (delta in the forward pass, delbar in the reverse walk)
+// cross the workgroup through LDS once per token.
 #include "kdn_common.h"
 #include "kdn_internal.h"
 #include "kdn_ops.h"
