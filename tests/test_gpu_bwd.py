@@ -137,7 +137,7 @@ def test_bwd_empty_sequence_passes_adjoints_through():
 # configuration bench.py --bwd times, against the oracle on each sampled
 # head's own slice (heads are independent problems)
 # ---------------------------------------------------------------------------
-def _bwd_full(ora, widx, n_heads):
+def _bwd_full(ora, widx, n_heads, heads=None):
     from kdn_testutil import sample_heads
     w = inputs.workload(widx)
     x = dict(inputs.make_fwd_inputs(w))
@@ -147,7 +147,7 @@ def _bwd_full(ora, widx, n_heads):
     do = rng.standard_normal((w.B, w.T, w.H, w.dv)).astype(np.float32)
     x["do"] = inputs.round_bf16(do) if w.io == "bf16" else do
     g = _run(w.variant, w.io, x)
-    heads = sample_heads(w.B, w.H, n_heads, seed=100 + widx)
+    heads = heads or sample_heads(w.B, w.H, n_heads, seed=100 + widx)
     sl = lambda a, b, h: np.ascontiguousarray(a[b:b + 1, :, h:h + 1])
     refs = {bh: ora.bwd(w.variant, *[sl(x[n], *bh) for n in ("q", "k", "v", "alpha", "omega", "r",
                                                               "do")])
@@ -174,3 +174,9 @@ def test_bwd_config2_diag_full(ora):
 @pytest.mark.timeout(400)
 def test_bwd_config1_iso_full(ora):
     _bwd_full(ora, 1, 3)
+
+
+@pytest.mark.timeout(600)
+def test_bwd_config3_long_full(ora):
+    # T = 65536: one head (the oracle keeps every state, 8.6 GB for it)
+    _bwd_full(ora, 3, 1, heads=[(0, 11)])
