@@ -8,6 +8,11 @@ update, readout, final state).  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 
+Other modes (same JSON form, not the default): --workload 1 / 3 / 4 (the
+Isotropic, long-sequence and decode workloads), --preact (the forward from
+bf16 gate pre-activations, kdn_fwd_preact) and --bwd (the backward pass,
+kdn_bwd, priced against its own algorithmic bytes).
+
 Roofline: achieved = algorithmic bytes per launch / mean launch time (HIP
 events on the launch stream).  Algorithmic bytes read every input once and
 write every output once (per head-token: 3 d s_io + 2 d * 4 + 4 + d s_io for
