@@ -196,6 +196,24 @@ def test_resume_matches_one_pass(ora, variant):
     assert max(err.values()) <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+@pytest.mark.parametrize("io_cols", [(4, 32, 128), (1, 1, 128), (2, 8, 256)],
+                         ids=lambda x: "B%dH%ddv%d" % x)
+def test_grid_shapes(ora, variant, io_cols):
+    # grids from 2 to 256 workgroups (one per (b, h, 64 value columns)),
+    # d_v up to 256, a ragged chunk: sampled heads against the oracle
+    B, H, dv = io_cols
+    w = inputs.Workload("t", variant, "bf16", B, H, 53, 128, dv, seed=91 + B + H)
+    inp = inputs.make_fwd_inputs(w)
+    d = to_dev(inp, "bf16")
+    o, S, var = _run_fwd(variant, d)
+    heads = sample_heads(B, H, 4, seed=B * H)
+    res = oracle_heads(ora, variant, inp, heads)
+    err = compare_heads(res, host(o), host(S), host(var), heads)
+    print("grid %s %s errors %s" % (variant, io_cols, err), flush=True)
+    assert max(err.values()) <= TOL["bf16"], err
+
+
 # ---------------------------------------------------------------------------
 # full workloads, sampled (batch, head) problems
 # ---------------------------------------------------------------------------
