@@ -16,6 +16,8 @@ Contents
 * ``gate_prologue`` -- the gates from their pre-activations (KDN reading
   notes, method part §8): alpha = sigmoid(a), omega = softplus(w),
   r = r_min + softplus(rho); numpy, fp64.
+* ``bwd_preact`` -- the backward of the forward from pre-activations (the
+  chain rule through the prologue; pinned to finite differences).
 * ``dense_kf`` -- the exact dense-covariance Kalman memory (KDN reading notes,
   method part §2, Eq. (12)-(17)); numpy, fp64, for tiny d_k only.
 * ``mobius_factors`` / ``mobius_fold_left`` / ``mobius_fold_tree`` /
@@ -265,6 +267,23 @@ def gate_prologue(a_pre, w_pre, r_pre, r_min: float = 0.01) -> dict:
     softplus = lambda x: np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
     return {"alpha": 1.0 / (1.0 + np.exp(-a)), "omega": softplus(w),
             "r": float(r_min) + softplus(rho)}
+
+
+def bwd_preact(variant: str, q, k, v, a_pre, w_pre, r_pre, do, r_min: float = 0.01,
+               **kw) -> dict:
+    """Backward of the forward from gate pre-activations (``gate_prologue``
+    followed by ``diag_fwd`` / ``iso_fwd``): ``bwd`` on the gates, then the
+    chain rule through the activations, d sigmoid(a)/da = alpha (1 - alpha)
+    and d softplus(x)/dx = sigmoid(x).  Returns bwd's dict with da_pre, dw_pre
+    and dr_pre in place of dalpha, domega and dr.  Other keyword arguments go
+    to ``bwd``."""
+    g = gate_prologue(a_pre, w_pre, r_pre, r_min)
+    out = bwd(variant, q, k, v, g["alpha"], g["omega"], g["r"], do, **kw)
+    sig = lambda x: 1.0 / (1.0 + np.exp(-_f64(x)))
+    out["da_pre"] = out.pop("dalpha") * g["alpha"] * (1.0 - g["alpha"])
+    out["dw_pre"] = out.pop("domega") * sig(w_pre)
+    out["dr_pre"] = out.pop("dr") * sig(r_pre)
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -49,3 +49,35 @@ def test_preact_draws_are_the_gates_of_the_plain_workload(ora):
     pre = inputs.make_preact_inputs(wb)
     for n in ("a_pre", "w_pre", "r_pre"):
         assert np.array_equal(pre[n], inputs.round_bf16(pre[n]))
+
+
+def test_bwd_preact_matches_finite_differences(ora):
+    # the pre-activations' gradients against central differences of the
+    # oracle's prologue followed by its forward, for L = sum(do * o)
+    for variant in ("diag", "iso"):
+        rng = np.random.default_rng(31 if variant == "diag" else 32)
+        B, T, H, dk, dv = 1, 5, 2, 3, 2
+        q, k = rng.standard_normal((2, B, T, H, dk))
+        v, do = rng.standard_normal((2, B, T, H, dv))
+        a = 1.0 + rng.standard_normal((B, T, H, dk))
+        w = rng.standard_normal((B, T, H) if variant == "iso" else (B, T, H, dk))
+        rho = rng.standard_normal((B, T, H))
+        fn = ora.diag_fwd if variant == "diag" else ora.iso_fwd
+
+        def loss():
+            g = ora.gate_prologue(a, w, rho, r_min=0.05)
+            return float(np.sum(fn(q, k, v, g["alpha"], g["omega"], g["r"])["o"] * do))
+
+        g = ora.bwd_preact(variant, q, k, v, a, w, rho, do, r_min=0.05)
+        for x, name in ((a, "da_pre"), (w, "dw_pre"), (rho, "dr_pre")):
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + 1e-6
+                lp = loss()
+                x[idx] = old - 1e-6
+                lm = loss()
+                x[idx] = old
+                fd[idx] = (lp - lm) / 2e-6
+            scale = max(np.abs(fd).max(), 1e-3)
+            assert np.abs(g[name] - fd).max() <= 1e-6 * scale, (variant, name)
