@@ -254,6 +254,28 @@ kdn_status kdn_bwd(int variant, int B, int T, int H, int dk, int dv, int io_dtyp
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of kdn_fwd_preact: the gradients by the gates' pre-activations
+ * (KDN reading notes, method part §8; d sigmoid(a)/da = alpha (1 - alpha),
+ * d softplus(x)/dx = sigmoid(x)).  Arguments as kdn_bwd with the gates
+ * replaced by a_pre, w_pre, r_pre and r_min as in kdn_fwd_preact, and their
+ * gradients da_pre [B,T,H,dk], dw_pre (shape of w_pre), dr_pre [B,T,H] in
+ * fp32 in place of dalpha, domega, dr.  The prologue writes the gates into the
+ * front of the workspace (kdn_bwd_preact_workspace_size bytes, 16-byte
+ * aligned), kdn_bwd runs on them with the rest of it, then the chain rule is
+ * applied in place.  No output and no part of the workspace may overlap the
+ * pre-activations.
+ */
+size_t kdn_bwd_preact_workspace_size(int variant, int B, int T, int H, int dk, int dv);
+kdn_status kdn_bwd_preact(int variant, int B, int T, int H, int dk, int dv, int io_dtype,
+                          float mu, const float* mu_h, const void* q, const void* k,
+                          const void* v, const void* a_pre, const void* w_pre, const void* r_pre,
+                          float r_min, const float* S0, const float* var0, const float* c0_h,
+                          const void* d_o, const float* dS_T, const float* dvar_T, void* dq,
+                          void* dk_out, void* dv_out, float* da_pre, float* dw_pre, float* dr_pre,
+                          float* dS0, float* dvar0, float* dmu, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Gain scan alone (the variance recurrence and Kalman gain without the
  * memory), exposed for the chunk-parallel regime's tests and diagnostics.
  * Inputs as in the forward calls (q, v not needed).  Writes

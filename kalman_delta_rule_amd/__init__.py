@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     KdnError,
     kdn_diag_fwd,
     kdn_bwd,
+    kdn_bwd_preact,
     kdn_dense_fwd,
     kdn_fwd_ex,
     kdn_fwd_preact,
@@ -31,6 +32,7 @@ __all__ = [
     "kdn_fwd_preact",
     "kdn_dense_fwd",
     "kdn_bwd",
+    "kdn_bwd_preact",
     "kdn_gain_scan",
     "kdn_fwd_workspace_size",
     "kdn_version",

@@ -274,6 +274,54 @@ def kdn_bwd(variant: str, q, k, v, alpha, omega, r, d_o, S0=None, var0=None, mu=
     return g
 
 
+def kdn_bwd_preact(variant: str, q, k, v, a_pre, w_pre, r_pre, d_o, r_min: float = 0.01,
+                   S0=None, var0=None, mu=None, mu_h=None, c0_h=None, dS_T=None, dvar_T=None,
+                   workspace=None) -> dict:
+    """Backward of kdn_fwd_preact: dq, dk, dv (io dtype), da_pre, dw_pre,
+    dr_pre (fp32), dS0, dvar0, dmu."""
+    L = _lib.lib()
+    var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    io = _io_code(q)
+    iso = var == KDN_ISO
+    f32 = torch.float32
+    _need(q, "q", (B, T, H, dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, dv), q.dtype, dev)
+    _need(d_o, "d_o", (B, T, H, dv), q.dtype, dev)
+    _need(a_pre, "a_pre", (B, T, H, dk), q.dtype, dev)
+    _need(w_pre, "w_pre", (B, T, H) if iso else (B, T, H, dk), q.dtype, dev)
+    _need(r_pre, "r_pre", (B, T, H), q.dtype, dev)
+    var_shape = (B, H) if iso else (B, H, dk)
+    for t, n, shp in ((S0, "S0", (B, H, dk, dv)), (dS_T, "dS_T", (B, H, dk, dv)),
+                      (var0, "var0", var_shape), (dvar_T, "dvar_T", var_shape),
+                      (mu_h, "mu_h", (H,)), (c0_h, "c0_h", (H,))):
+        if t is not None:
+            _need(t, n, shp, f32, dev)
+    mu = float(dk if mu is None else mu)
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+         "da_pre": torch.empty(a_pre.shape, dtype=f32, device=dev),
+         "dw_pre": torch.empty(w_pre.shape, dtype=f32, device=dev),
+         "dr_pre": torch.empty(r_pre.shape, dtype=f32, device=dev),
+         "dS0": torch.empty((B, H, dk, dv), dtype=f32, device=dev),
+         "dvar0": torch.empty(var_shape, dtype=f32, device=dev),
+         "dmu": torch.empty((B, H), dtype=f32, device=dev)}
+    need = int(L.kdn_bwd_preact_workspace_size(var, B, T, H, dk, dv))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = L.kdn_bwd_preact(var, B, T, H, dk, dv, io, mu, _ptr(mu_h), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(a_pre), _ptr(w_pre), _ptr(r_pre), float(r_min), _ptr(S0),
+                              _ptr(var0), _ptr(c0_h), _ptr(d_o), _ptr(dS_T), _ptr(dvar_T),
+                              *[_ptr(g[n]) for n in ("dq", "dk", "dv", "da_pre", "dw_pre",
+                                                     "dr_pre", "dS0", "dvar0", "dmu")],
+                              _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check(st)
+    return g
+
+
 def kdn_step(variant: str, q, k, v, alpha, omega, r, S, var_state, mu=None,
              o=None, mu_h=None, beta_eff=None) -> torch.Tensor:
     """One decode step; S [B,H,dk,dv] and var_state are updated in place.

@@ -420,13 +420,15 @@ size_t kdn_bwd_workspace_size(int variant, int B, int T, int H, int dk, int dv)
     return kdn::bwd_workspace_floats(variant == KDN_ISO, B, T, H, dk, dv) * sizeof(float);
 }
 
-kdn_status kdn_bwd(int variant, int B, int T, int H, int dk, int dv, int io_dtype, float mu,
-                   const float* mu_h, const void* q, const void* k, const void* v,
-                   const float* alpha, const float* omega, const float* r, const float* S0,
-                   const float* var0, const float* c0_h, const void* d_o, const float* dS_T,
-                   const float* dvar_T, void* dq, void* dk_out, void* dv_out, float* dalpha,
-                   float* domega, float* dr, float* dS0, float* dvar0, float* dmu,
-                   void* workspace, size_t workspace_bytes, void* stream)
+static kdn_status bwd_impl(int variant, int B, int T, int H, int dk, int dv, int io_dtype,
+                           float mu, const float* mu_h, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* omega, const float* r,
+                           const float* S0, const float* var0, const float* c0_h,
+                           const void* d_o, const float* dS_T, const float* dvar_T, void* dq,
+                           void* dk_out, void* dv_out, float* dalpha, float* domega, float* dr,
+                           float* dS0, float* dvar0, float* dmu, void* workspace,
+                           size_t workspace_bytes, void* stream,
+                           const kdn::PrologueArgs* pro = nullptr)
 {
     if (variant != KDN_DIAG && variant != KDN_ISO)
         return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
@@ -532,10 +534,101 @@ kdn_status kdn_bwd(int variant, int B, int T, int H, int dk, int dv, int io_dtyp
     a.gS0 = dS0; a.gvar0 = dvar0; a.gmu = dmu;
     a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
     kdn::bwd_carve_workspace(a, iso, static_cast<float*>(workspace));
-    hipError_t e = kdn::launch_bwd(a, iso, io_dtype, reinterpret_cast<hipStream_t>(stream));
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (pro && T > 0) {  // the gates from their pre-activations
+        hipError_t e = kdn::launch_gate_prologue(*pro, io_dtype, hs);
+        if (e != hipSuccess)
+            return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    hipError_t e = kdn::launch_bwd(a, iso, io_dtype, hs);
+    if (e == hipSuccess && pro && T > 0)  // and the chain rule back through them
+        e = kdn::launch_gate_epilogue(*pro, dalpha, domega, dr, io_dtype, hs);
     if (e != hipSuccess)
         return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+kdn_status kdn_bwd(int variant, int B, int T, int H, int dk, int dv, int io_dtype, float mu,
+                   const float* mu_h, const void* q, const void* k, const void* v,
+                   const float* alpha, const float* omega, const float* r, const float* S0,
+                   const float* var0, const float* c0_h, const void* d_o, const float* dS_T,
+                   const float* dvar_T, void* dq, void* dk_out, void* dv_out, float* dalpha,
+                   float* domega, float* dr, float* dS0, float* dvar0, float* dmu,
+                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    return bwd_impl(variant, B, T, H, dk, dv, io_dtype, mu, mu_h, q, k, v, alpha, omega, r, S0,
+                    var0, c0_h, d_o, dS_T, dvar_T, dq, dk_out, dv_out, dalpha, domega, dr, dS0,
+                    dvar0, dmu, workspace, workspace_bytes, stream);
+}
+
+size_t kdn_bwd_preact_workspace_size(int variant, int B, int T, int H, int dk, int dv)
+{
+    if ((variant != KDN_DIAG && variant != KDN_ISO) || B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1)
+        return 0;
+    return kdn_fwd_preact_workspace_size(variant, B, T, H, dk) +
+           kdn_bwd_workspace_size(variant, B, T, H, dk, dv);
+}
+
+kdn_status kdn_bwd_preact(int variant, int B, int T, int H, int dk, int dv, int io_dtype,
+                          float mu, const float* mu_h, const void* q, const void* k,
+                          const void* v, const void* a_pre, const void* w_pre, const void* r_pre,
+                          float r_min, const float* S0, const float* var0, const float* c0_h,
+                          const void* d_o, const float* dS_T, const float* dvar_T, void* dq,
+                          void* dk_out, void* dv_out, float* da_pre, float* dw_pre, float* dr_pre,
+                          float* dS0, float* dvar0, float* dmu, void* workspace,
+                          size_t workspace_bytes, void* stream)
+{
+    if (variant != KDN_DIAG && variant != KDN_ISO)
+        return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
+                    variant);
+    if (io_dtype != KDN_F32 && io_dtype != KDN_BF16)
+        return fail(KDN_ERR_INVALID_ARG, "io_dtype must be KDN_F32 (0) or KDN_BF16 (1), got %d",
+                    io_dtype);
+    if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1)
+        return fail(KDN_ERR_INVALID_ARG, "need B >= 1, H >= 1, T >= 0 (got B=%d T=%d H=%d)", B, T, H);
+    if (!(r_min > 0.f) || r_min > 3.0e38f)
+        return fail(KDN_ERR_INVALID_ARG, "r_min must be finite and > 0 (got %g)", (double)r_min);
+    if (T > 0) {
+        KDN_REQUIRE(a_pre, "a_pre");
+        KDN_REQUIRE(w_pre, "w_pre");
+        KDN_REQUIRE(r_pre, "r_pre");
+    }
+    KDN_ALIGNED(a_pre, "a_pre");
+    KDN_ALIGNED(w_pre, "w_pre");
+    KDN_ALIGNED(r_pre, "r_pre");
+    const size_t gates = kdn_fwd_preact_workspace_size(variant, B, T, H, dk);
+    const size_t need = kdn_bwd_preact_workspace_size(variant, B, T, H, dk, dv);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                    workspace_bytes);
+    KDN_ALIGNED(workspace, "workspace");
+    const bool iso = variant == KDN_ISO;
+    const size_t es = io_dtype == KDN_BF16 ? 2 : 4;
+    const size_t ntok = (size_t)B * T * H, nw = iso ? ntok : ntok * dk;
+    // the pre-activations are inputs: no output or workspace may overlap them
+    const struct { const void* p; size_t n; const char* name; } pres[] = {
+        {a_pre, ntok * dk * es, "a_pre"}, {w_pre, nw * es, "w_pre"}, {r_pre, ntok * es, "r_pre"}};
+    const struct { const void* p; size_t n; const char* name; } outs[] = {
+        {workspace, need, "workspace"}, {dq, ntok * dk * es, "dq"}, {dk_out, ntok * dk * es, "dk"},
+        {dv_out, ntok * dv * es, "dv"}, {da_pre, ntok * dk * 4, "da_pre"},
+        {dw_pre, nw * 4, "dw_pre"}, {dr_pre, ntok * 4, "dr_pre"},
+        {dS0, (size_t)B * H * dk * dv * 4, "dS0"}, {dvar0, (iso ? 1 : (size_t)dk) * B * H * 4, "dvar0"},
+        {dmu, (size_t)B * H * 4, "dmu"}};
+    for (const auto& o : outs)
+        for (const auto& p : pres) {
+            const char *a0 = (const char*)o.p, *b0 = (const char*)p.p;
+            if (o.p && p.p && o.n && p.n && a0 < b0 + p.n && b0 < a0 + o.n)
+                return fail(KDN_ERR_INVALID_ARG, "%s must not overlap %s", o.name, p.name);
+        }
+    float* alpha = static_cast<float*>(workspace);
+    float* omega = alpha + round64f(ntok * dk);
+    float* r = omega + round64f(nw);
+    kdn::PrologueArgs pa{a_pre, w_pre, r_pre, alpha, omega, r, ntok * dk, nw, ntok, r_min};
+    return bwd_impl(variant, B, T, H, dk, dv, io_dtype, mu, mu_h, q, k, v,
+                    T > 0 ? alpha : nullptr, T > 0 ? omega : nullptr, T > 0 ? r : nullptr, S0,
+                    var0, c0_h, d_o, dS_T, dvar_T, dq, dk_out, dv_out, da_pre, dw_pre, dr_pre,
+                    dS0, dvar0, dmu, static_cast<char*>(workspace) + gates, workspace_bytes - gates,
+                    stream, &pa);
 }
 
 kdn_status kdn_step_ex(int variant, int B, int H, int dk, int dv, int io_dtype, float mu,

@@ -105,5 +105,7 @@ size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv);
 void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws);
 hipError_t launch_bwd(const BwdArgs& a, bool iso, int io_dtype, hipStream_t stream);
 hipError_t launch_gate_prologue(const PrologueArgs& a, int io_dtype, hipStream_t stream);
+hipError_t launch_gate_epilogue(const PrologueArgs& p, float* da, float* dw, float* dr,
+                                int io_dtype, hipStream_t stream);
 
 }  // namespace kdn

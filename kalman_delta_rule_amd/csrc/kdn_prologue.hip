@@ -96,3 +96,53 @@ hipError_t launch_gate_prologue(const PrologueArgs& a, int io_dtype, hipStream_t
 }
 
 }  // namespace kdn
+
+namespace kdn {
+
+// The gradients of the gates become the gradients of their pre-activations,
+// in place: da *= alpha (1 - alpha), dw *= sigmoid(w), dr *= sigmoid(rho)
+// (d softplus(x)/dx = sigmoid(x)).
+template <typename IO, int ACT>
+__global__ __launch_bounds__(256) void kdn_gate_epilogue_kernel(const float* __restrict__ gate,
+                                                                const IO* __restrict__ pre,
+                                                                float* __restrict__ g, size_t n)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n)
+        return;
+    if constexpr (ACT == 0) {
+        const float al = gate[i];
+        g[i] *= al * (1.f - al);
+    } else {
+        g[i] *= gate_act<0>(to_f32(pre[i]), 0.f);
+    }
+}
+
+template <typename IO, int ACT>
+static hipError_t launch_epi(const float* gate, const void* pre, float* g, size_t n,
+                             hipStream_t stream)
+{
+    if (n == 0 || !g)
+        return hipSuccess;
+    hipLaunchKernelGGL((kdn_gate_epilogue_kernel<IO, ACT>), dim3((unsigned)((n + 255) / 256)),
+                       dim3(256), 0, stream, gate, reinterpret_cast<const IO*>(pre), g, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_epilogue(const PrologueArgs& p, float* da, float* dw, float* dr,
+                                int io_dtype, hipStream_t stream)
+{
+    const bool bf = io_dtype == 1;
+    hipError_t e = bf ? launch_epi<bf16, 0>(p.alpha, nullptr, da, p.n_alpha, stream)
+                      : launch_epi<float, 0>(p.alpha, nullptr, da, p.n_alpha, stream);
+    if (e != hipSuccess)
+        return e;
+    e = bf ? launch_epi<bf16, 1>(nullptr, p.w_pre, dw, p.n_omega, stream)
+           : launch_epi<float, 1>(nullptr, p.w_pre, dw, p.n_omega, stream);
+    if (e != hipSuccess)
+        return e;
+    return bf ? launch_epi<bf16, 1>(nullptr, p.r_pre, dr, p.n_r, stream)
+              : launch_epi<float, 1>(nullptr, p.r_pre, dr, p.n_r, stream);
+}
+
+}  // namespace kdn

@@ -326,3 +326,32 @@ def test_fwd_preact_validation(L):
     r64 = lambda n: (n + 63) // 64 * 64
     assert L.kdn_fwd_preact_workspace_size(0, 1, 40, 2, 128) == 4 * (2 * r64(ntok * 128) + r64(ntok))
     assert L.kdn_fwd_preact_workspace_size(1, 1, 40, 2, 128) == 4 * (r64(ntok * 128) + 2 * r64(ntok))
+
+
+def test_bwd_preact_validation(L):
+    G = 1 << 28
+    names = ["q", "k", "v", "a", "w", "r", "d_o", "dq", "gk", "gv", "da", "dw", "dr", "ws"]
+    base = {n: P + (i + 1) * G for i, n in enumerate(names)}
+
+    def bp(**kw):
+        a = dict(variant=0, B=1, T=40, H=2, dk=128, dv=64, io=1, mu=128.0, r_min=0.01)
+        a.update({n: base[n] for n in names})
+        a.update(kw)
+        ws_bytes = a.pop("ws_bytes", L.kdn_bwd_preact_workspace_size(a["variant"], a["B"], a["T"],
+                                                                     a["H"], a["dk"], a["dv"]))
+        return L.kdn_bwd_preact(a["variant"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["io"],
+                                a["mu"], None, a["q"], a["k"], a["v"], a["a"], a["w"], a["r"],
+                                a["r_min"], None, None, None, a["d_o"], None, None, a["dq"],
+                                a["gk"], a["gv"], a["da"], a["dw"], a["dr"], None, None, None,
+                                a["ws"], ws_bytes, None)
+    msg = lambda: L.kdn_last_error_message().decode()
+    assert bp(r_min=-1.0) == -1 and "r_min" in msg()
+    assert bp(w=None) == -1 and "w_pre must not be NULL" in msg()
+    assert bp(ws_bytes=32) == -3 and "workspace" in msg()
+    assert bp(da=base["a"] + 64) == -1 and "da_pre must not overlap a_pre" in msg()
+    assert bp(dq=base["w"]) == -1 and "overlap" in msg()
+    # the backward's own checks apply to the rest
+    assert bp(dv=40) == -2 and "dv" in msg()
+    assert (L.kdn_bwd_preact_workspace_size(0, 1, 40, 2, 128, 64)
+            == L.kdn_fwd_preact_workspace_size(0, 1, 40, 2, 128)
+            + L.kdn_bwd_workspace_size(0, 1, 40, 2, 128, 64))

@@ -116,3 +116,25 @@ def test_preact_config2_full_sampled(ora):
            for n, pr in (("o", eo), ("S", es), ("var", ev))}
     print("preact %s heads=%s errors %s" % (w.name, heads, err), flush=True)
     assert max(err.values()) <= TOL[w.io], err
+
+
+@pytest.mark.parametrize("case", [("diag", "f32", 1, 37, 2, 64, 32), ("iso", "bf16", 1, 70, 2, 128, 64),
+                                  ("diag", "bf16", 2, 50, 2, 128, 128)],
+                         ids=lambda c: "%s-%s-B%dT%dH%ddk%ddv%d" % c)
+def test_bwd_preact_matches_oracle(ora, case):
+    variant, io, B, T, H, dk, dv = case
+    w = inputs.Workload("t", variant, io, B, H, T, dk, dv, seed=760 + T)
+    x = inputs.make_preact_inputs(w)
+    do = np.random.default_rng(761).standard_normal((B, T, H, dv)).astype(np.float32)
+    x["do"] = inputs.round_bf16(do) if io == "bf16" else do
+    d = _dev(x, io)
+    g = api.kdn_bwd_preact(variant, d["q"], d["k"], d["v"], d["a_pre"], d["w_pre"], d["r_pre"],
+                           d["do"], r_min=0.02)
+    torch.cuda.synchronize()
+    ref = ora.bwd_preact(variant, x["q"], x["k"], x["v"], x["a_pre"], x["w_pre"], x["r_pre"],
+                         x["do"], r_min=0.02)
+    err = {n: rel_l2(host(g[n]), ref[n]) for n in ("dq", "dk", "dv", "da_pre", "dw_pre", "dr_pre",
+                                                   "dS0", "dvar0", "dmu")}
+    print("bwd_preact %s errors %s" % (case, {k_: "%.2e" % v_ for k_, v_ in err.items()}),
+          flush=True)
+    assert max(err.values()) <= TOL[io], err
