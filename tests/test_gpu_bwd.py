@@ -180,3 +180,24 @@ def test_bwd_config1_iso_full(ora):
 def test_bwd_config3_long_full(ora):
     # T = 65536: one head (the oracle keeps every state, 8.6 GB for it)
     _bwd_full(ora, 3, 1, heads=[(0, 11)])
+
+
+@pytest.mark.parametrize("regime", ["mu0", "slow_decay", "fast_decay", "noisy"])
+def test_bwd_regimes(ora, regime):
+    # the backward away from the default gate draws: no information scaling
+    # (mu = 0), decay close to 1 (long memory, large states), fast decay, and
+    # observation noise r much larger than the predicted variance
+    variant, io, B, T, H, dk, dv = "diag", "f32", 1, 90, 2, 128, 64
+    x = _case(variant, io, B, T, H, dk, dv, seed=800 + len(regime))
+    rng = np.random.default_rng(801)
+    mu = None
+    if regime == "mu0":
+        mu = 0.0
+    elif regime == "slow_decay":
+        x["alpha"] = (1.0 - 1e-3 * rng.random(x["alpha"].shape)).astype(np.float32)
+        x["omega"] = (1e-3 * x["omega"]).astype(np.float32)
+    elif regime == "fast_decay":
+        x["alpha"] = (0.3 + 0.3 * rng.random(x["alpha"].shape)).astype(np.float32)
+    else:
+        x["r"] = (20.0 + 10.0 * rng.random(x["r"].shape)).astype(np.float32)
+    _check(_run(variant, io, x, mu=mu), _oracle(ora, variant, x, mu=mu), io, regime)
