@@ -79,9 +79,19 @@ typedef enum {
 typedef enum { KDN_F32 = 0, KDN_BF16 = 1 } kdn_dtype;
 typedef enum { KDN_DIAG = 0, KDN_ISO = 1 } kdn_variant;
 
-/* Bytes of device workspace kdn_diag_fwd / kdn_iso_fwd need for this shape
- * (0 when the chosen regime needs none).  Returns 0 for invalid shapes too;
- * the forward call reports those. */
+/* Bytes of device workspace with which kdn_diag_fwd / kdn_iso_fwd (and
+ * kdn_fwd_ex) run this shape fastest.  The workspace is optional: a call given
+ * less (or NULL) runs the serial walk, with the same results up to rounding.
+ * Nonzero only for bf16 io with dk == dv when the serial walk would fill at
+ * most a quarter of the chip (B*H*dv/64 workgroups) and T splits into 4 or 8
+ * segments of at least 1024 tokens, each a multiple of 64: the state
+ * recurrence is affine in the state over any span of tokens (method part §2
+ * and §6 of the KDN reading notes), so the segments run as independent walks
+ * whose linear and affine parts a short per-head combine chains, and the
+ * segment-entry variances come from the gain scan (method part §6).  The size
+ * is then the gain scan's carries, two segment-variance planes, four
+ * [B*S,H,dk,dv] fp32 state planes and a bf16 copy of v's shape.  Returns 0 for
+ * invalid shapes too; the forward call reports those. */
 size_t kdn_fwd_workspace_size(int variant, int B, int T, int H, int dk, int dv,
                               int io_dtype);
 
@@ -96,8 +106,11 @@ size_t kdn_fwd_workspace_size(int variant, int B, int T, int H, int dk, int dv,
  *   mu     information scale (the pages' default is dk)
  *   S_T    [B,H,dk,dv] fp32 final state (required)
  *   p_T    [B,H,dk]    fp32 final variances (required)
- *   workspace / workspace_bytes: device scratch of at least
- *     kdn_fwd_workspace_size(...) bytes (may be NULL when that is 0)
+ *   workspace / workspace_bytes: optional device scratch, 16-byte aligned;
+ *     with kdn_fwd_workspace_size(...) bytes or more, shapes with few heads
+ *     and long sequences run split over the sequence (NULL: serial walk).
+ *     When it is used it must not overlap any other argument
+ *     (KDN_ERR_INVALID_ARG), and o serves as scratch before its final values.
  *   stream: a hipStream_t (NULL = the null stream)
  * S_T may alias S0 and p_T may alias p0 exactly (the state is read before
  * it is overwritten); a partial overlap of either pair, or o aliasing q, k

@@ -52,7 +52,7 @@ def _head_vec(t, name, H, dev):
 
 
 def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
-         ext: bool = False, mu_h=None, c0_h=None, beta_eff=None):
+         ext: bool = False, mu_h=None, c0_h=None, beta_eff=None, sequence_parallel=True):
     L = _lib.lib()
     if q.dim() != 4:
         raise ValueError("q must be [B,T,H,dk]")
@@ -84,7 +84,8 @@ def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
         var_T = torch.empty(vshape, dtype=torch.float32, device=dev)
     _need(var_T, "var_T", vshape, torch.float32, dev)
     mu = float(dk if mu is None else mu)
-    ws_bytes = L.kdn_fwd_workspace_size(variant, B, T, H, dk, dv, io)
+    # with the workspace, shapes with few heads and long sequences run sequence-parallel
+    ws_bytes = L.kdn_fwd_workspace_size(variant, B, T, H, dk, dv, io) if sequence_parallel else 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     if ext:
         _head_vec(mu_h, "mu_h", H, dev)
@@ -121,17 +122,19 @@ def kdn_iso_fwd(q, k, v, alpha, omega, r, S0=None, b0=None, mu=None, o=None, S_T
 
 def kdn_fwd_ex(variant: str, q, k, v, alpha, omega, r, S0=None, var0=None, mu=None,
                mu_h=None, c0_h=None, want_beta_eff: bool = False, o=None, S_T=None,
-               var_T=None):
+               var_T=None, sequence_parallel: bool = True):
     """Forward with per-head mu_h [H] and c0_h [H] (both optional) and the
     effective write strength.  Returns (o, S_T, var_T, beta_eff [B,T,H] or
-    None)."""
+    None).  sequence_parallel=False withholds the workspace, so that shapes the
+    library would split over the sequence run the serial walk instead."""
     var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
     beta = None
     if want_beta_eff:
         B, T, H, _ = q.shape
         beta = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
     o, S_T, var_T = _fwd(var, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
-                         ext=True, mu_h=mu_h, c0_h=c0_h, beta_eff=beta)
+                         ext=True, mu_h=mu_h, c0_h=c0_h, beta_eff=beta,
+                         sequence_parallel=sequence_parallel)
     return o, S_T, var_T, beta
 
 

@@ -163,11 +163,30 @@ kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float
         if (s0 < st_ + bytes && st_ < s0 + bytes)
             return fail(KDN_ERR_INVALID_ARG, "S_T must either equal S0 or not overlap it");
     }
-    const size_t need = kdn_fwd_workspace_size(iso ? KDN_ISO : KDN_DIAG, B, T, H, dk, dv, io);
-    if (workspace_bytes < need || (need > 0 && !workspace))
-        return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
-                    workspace_bytes);
-    (void)workspace;
+    // the workspace is optional: with the size kdn_fwd_workspace_size names,
+    // shapes with few heads and long sequences run sequence-parallel
+    const int nseg = pro ? 0 : kdn::seqpar_segments(iso, B, T, H, dk, dv, io);
+    const size_t sp_bytes =
+        nseg ? kdn::seqpar_workspace_floats(iso, B, T, H, dk, dv, nseg) * sizeof(float) : 0;
+    const bool seqpar = nseg && workspace && workspace_bytes >= sp_bytes;
+    if (seqpar) {
+        KDN_ALIGNED(workspace, "workspace");
+        const char *w0 = (const char*)workspace, *w1 = w0 + sp_bytes;
+        const size_t ntok = (size_t)B * T * H;
+        const size_t nst = (size_t)B * H * dk * dv * sizeof(float);
+        const size_t nvar = (size_t)B * H * (iso ? 1 : dk) * sizeof(float);
+        const struct { const void* p; size_t n; const char* name; } bufs[] = {
+            {q, ntok * dk * 2, "q"}, {k, ntok * dk * 2, "k"}, {v, ntok * dv * 2, "v"},
+            {alpha, ntok * dk * 4, "alpha"}, {omega, ntok * (iso ? 1 : dk) * 4, "omega"},
+            {r, ntok * 4, "r"}, {o, ntok * dv * 2, "o"}, {S0, nst, "S0"}, {S_T, nst, "S_T"},
+            {var0, nvar, "var0"}, {var_T, nvar, "var_T"}, {x.mu_h, (size_t)H * 4, "mu_h"},
+            {x.c0_h, (size_t)H * 4, "c0_h"}, {x.beta_eff, ntok * 4, "beta_eff"}};
+        for (const auto& b : bufs) {
+            const char* b0 = (const char*)b.p;
+            if (b.p && w0 < b0 + b.n && b0 < w1)
+                return fail(KDN_ERR_INVALID_ARG, "workspace must not overlap %s", b.name);
+        }
+    }
 
     kdn::FwdArgs a{q, k, v, alpha, omega, r, S0, var0, o, S_T, var_T, B, T, H, dk, dv, mu,
                    x.mu_h, x.c0_h, T > 0 ? x.beta_eff : nullptr};
@@ -177,8 +196,9 @@ kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float
         if (e != hipSuccess)
             return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     }
-    hipError_t e = io == KDN_BF16 ? kdn::launch_walk_fwd(a, iso, hs)
-                                  : kdn::launch_chunk_fwd_f32(a, iso, hs);
+    hipError_t e = seqpar ? kdn::launch_seqpar_fwd(a, iso, nseg, static_cast<float*>(workspace), hs)
+                   : io == KDN_BF16 ? kdn::launch_walk_fwd(a, iso, hs)
+                                    : kdn::launch_chunk_fwd_f32(a, iso, hs);
     if (e != hipSuccess)
         return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -190,14 +210,13 @@ extern "C" {
 
 size_t kdn_fwd_workspace_size(int variant, int B, int T, int H, int dk, int dv, int io_dtype)
 {
-    (void)variant;
-    (void)B;
-    (void)T;
-    (void)H;
-    (void)dk;
-    (void)dv;
-    (void)io_dtype;
-    return 0;  // the walk regime keeps every intermediate on chip
+    if (B < 0 || T < 0 || H <= 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+        return 0;
+    const bool iso = variant == KDN_ISO;
+    const int nseg = kdn::seqpar_segments(iso, B, T, H, dk, dv, io_dtype);
+    // zero: the walk keeps every intermediate on chip; otherwise the
+    // sequence-parallel path's segment states and carries
+    return nseg ? kdn::seqpar_workspace_floats(iso, B, T, H, dk, dv, nseg) * sizeof(float) : 0;
 }
 
 kdn_status kdn_diag_fwd(int B, int T, int H, int dk, int dv, int io_dtype, float mu,

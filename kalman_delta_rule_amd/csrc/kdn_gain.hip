@@ -92,15 +92,29 @@ __global__ __launch_bounds__(DK) void gain_summary_diag(GainArgs a, int nchunks)
     const int t0 = c * GC, n_valid = min(GC, a.T - t0);
     const IO* kg = reinterpret_cast<const IO*>(a.k);
     Mob P = mob_identity();
-    for (int t = 0; t < n_valid; ++t) {
-        const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
-        const float al = a.alpha[tok * DK + i], w = a.omega[tok * DK + i];
-        const float kv = to_f32(kg[tok * DK + i]);
-        const float u = (mu_of(a, h) / a.r[tok]) * kv * kv;
-        const float a2 = al * al;
-        P = mob_mul_raw(Mob{a2, w, u * a2, 1.f + u * w}, P);
-        if ((t & 3) == 3)
-            P = mob_normalize(P);
+    // eight tokens' gates are loaded before the product chain that consumes them
+    constexpr int PF = 8;
+    for (int tb = 0; tb < n_valid; tb += PF) {
+        float al[PF], w[PF], kv[PF], rt[PF];
+#pragma unroll
+        for (int e = 0; e < PF; ++e) {
+            const size_t tok = ((size_t)b * a.T + t0 + min(tb + e, n_valid - 1)) * a.H + h;
+            al[e] = a.alpha[tok * DK + i];
+            w[e] = a.omega[tok * DK + i];
+            kv[e] = to_f32(kg[tok * DK + i]);
+            rt[e] = a.r[tok];
+        }
+#pragma unroll
+        for (int e = 0; e < PF; ++e) {
+            const int t = tb + e;
+            if (t < n_valid) {
+                const float u = (mu_of(a, h) / rt[e]) * kv[e] * kv[e];
+                const float a2 = al[e] * al[e];
+                P = mob_mul_raw(Mob{a2, w[e], u * a2, 1.f + u * w[e]}, P);
+                if ((t & 3) == 3)
+                    P = mob_normalize(P);
+            }
+        }
     }
     P = mob_normalize(P);
     const size_t base = (size_t)bh * 4 * DK * nchunks + (size_t)i * nchunks + c;

@@ -108,4 +108,12 @@ hipError_t launch_gate_prologue(const PrologueArgs& a, int io_dtype, hipStream_t
 hipError_t launch_gate_epilogue(const PrologueArgs& p, float* da, float* dw, float* dr,
                                 int io_dtype, hipStream_t stream);
 
+// sequence-parallel bf16 forward for grids that leave most compute units idle
+// (kdn_seqpar.hip): the segment count (0: not eligible), its workspace, and the
+// launch over a workspace of that size
+int seqpar_segments(bool iso, int B, int T, int H, int dk, int dv, int io_dtype);
+size_t seqpar_workspace_floats(bool iso, int B, int T, int H, int dk, int dv, int S);
+struct FwdArgs;
+hipError_t launch_seqpar_fwd(const FwdArgs& a, bool iso, int S, float* ws, hipStream_t stream);
+
 }  // namespace kdn

@@ -58,6 +58,15 @@ def test_version_and_status_strings(L):
 
 def test_workspace_sizes(L):
     assert L.kdn_fwd_workspace_size(0, 8, 4096, 16, 128, 128, 1) == 0
+    # few heads, long sequence: 8 segments; gain scan + 2 variance planes + 4 state
+    # planes + a zero copy of v
+    gain, pin, st, vz = 16 * 1024 * 128 * 5, 8 * 16 * 128, 8 * 16 * 128 * 128, 65536 * 16 * 64
+    assert L.kdn_fwd_workspace_size(0, 1, 65536, 16, 128, 128, 1) == (gain + 2 * pin + 4 * st + vz) * 4
+    gain, pin = 16 * 1024 * 5, 8 * 16
+    assert L.kdn_fwd_workspace_size(1, 1, 65536, 16, 128, 128, 1) == (gain + 2 * pin + 4 * st + vz) * 4
+    assert L.kdn_fwd_workspace_size(0, 1, 65536, 16, 128, 128, 0) == 0   # fp32 io: serial
+    assert L.kdn_fwd_workspace_size(0, 1, 65536, 16, 128, 64, 1) == 0    # dk != dv
+    assert L.kdn_fwd_workspace_size(0, 1, 2048, 16, 128, 128, 1) == 0    # segments too short
     # gain scan: 4 summary planes + carries per chunk and channel
     assert L.kdn_gain_workspace_size(0, 1, 128, 2, 64) == 1 * 2 * 2 * 64 * 5 * 4
     assert L.kdn_gain_workspace_size(1, 1, 128, 2, 64) == 1 * 2 * 2 * 1 * 5 * 4
@@ -128,6 +137,24 @@ def test_fwd_variance_partial_overlap(L, variant, offset):
     # overlap is not
     assert _fwd_call(L, variant, var0=P + 16384 + offset) == -1
     assert "overlap" in L.kdn_last_error_message().decode()
+
+
+@cpu_only
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+def test_fwd_sequence_parallel_workspace_overlap(L, variant):
+    # a shape the library splits over the sequence, given its workspace
+    shape = dict(B=1, T=8192, H=2, dk=128, dv=128)
+    need = L.kdn_fwd_workspace_size(0 if variant == "diag" else 1, 1, 8192, 2, 128, 128, 1)
+    assert need > 0
+    far = 1 << 40
+    kw = dict(shape, q=far, k=far, v=far, alpha=far, omega=far, r=far, o=far + (1 << 32),
+              S_T=far + (2 << 32), var_T=far + (3 << 32), ws_bytes=need)
+    assert _fwd_call(L, variant, ws=far + 64, **kw) == -1
+    assert "workspace must not overlap q" in L.kdn_last_error_message().decode()
+    assert _fwd_call(L, variant, ws=far + (2 << 32) - 64, **kw) == -1
+    assert "workspace must not overlap S_T" in L.kdn_last_error_message().decode()
+    assert _fwd_call(L, variant, ws=far + 4, **kw) == -1
+    assert "aligned" in L.kdn_last_error_message().decode()
 
 
 @cpu_only
