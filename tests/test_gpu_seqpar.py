@@ -128,3 +128,42 @@ def test_seqpar_in_place_state():
     torch.cuda.synchronize()
     assert S2.data_ptr() == S_in.data_ptr()
     assert torch.equal(o, o2) and torch.equal(S, S2) and torch.equal(p, p2)
+
+
+def test_short_workspace_runs_the_serial_walk():
+    # a workspace one byte short of kdn_fwd_workspace_size is ignored: the call
+    # equals the serial walk (same kernels, bit for bit); the full size splits
+    from kalman_delta_rule_amd import _lib
+    L = _lib.lib()
+    B, T, H, d = 1, 8192, 2, 128
+    w = inputs.Workload("t", "diag", "bf16", B, H, T, d, d, seed=970)
+    inp = inputs.make_fwd_inputs(w)
+    # slow decay keeps each segment's linear part M away from zero (with the
+    # workload's decays it underflows within a segment, and the split then
+    # reproduces the serial state bit for bit)
+    inp["alpha"] = _alpha("slow", inp["alpha"].shape, np.random.default_rng(971))
+    dd = to_dev(inp, "bf16")
+    need = api.kdn_fwd_workspace_size("diag", B, T, H, d, d, torch.bfloat16)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ser = _run("diag", dd, False)
+
+    def call(nbytes):
+        o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device="cuda")
+        S = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+        p = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+        st = L.kdn_diag_fwd(B, T, H, d, d, 1, float(d), dd["q"].data_ptr(), dd["k"].data_ptr(),
+                            dd["v"].data_ptr(), dd["alpha"].data_ptr(), dd["omega"].data_ptr(),
+                            dd["r"].data_ptr(), None, None, o.data_ptr(), S.data_ptr(),
+                            p.data_ptr(), ws.data_ptr(), nbytes,
+                            torch.cuda.current_stream().cuda_stream)
+        _lib.check(st)
+        torch.cuda.synchronize()
+        return o, S, p
+
+    short = call(need - 1)
+    assert all(torch.equal(x, y) for x, y in zip(short, ser[:3]))
+    full = call(need)
+    spl = _run("diag", dd, True)
+    assert all(torch.equal(x, y) for x, y in zip(full, spl[:3]))
+    assert not torch.equal(full[1], ser[1])   # the split path really ran
