@@ -196,21 +196,36 @@ __global__ __launch_bounds__(DK) void gain_replay_diag(GainArgs a, int nchunks)
     const IO* kg = reinterpret_cast<const IO*>(a.k);
     float p = a.carry[((size_t)bh * nchunks + c) * DK + i];
     float kk[GC];
+    // eight tokens' gates are loaded before the chain (and the pprev stores,
+    // which the compiler cannot move loads across) consume them
+    constexpr int PF = 8;
 #pragma unroll
-    for (int t = 0; t < GC; ++t) {
-        float ph = 0.f, kv = 0.f;
-        if (t < n_valid) {
-            const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
-            const float al = a.alpha[tok * DK + i], w = a.omega[tok * DK + i];
-            kv = to_f32(kg[tok * DK + i]);
-            ph = al * al * p + w;
-            const float u = (mu_of(a, h) / a.r[tok]) * kv * kv;
-            if (a.pprev)
-                a.pprev[tok * DK + i] = p;
-            p = ph * rcp(1.f + u * ph);
+    for (int tb = 0; tb < GC; tb += PF) {
+        float al8[PF], w8[PF], kv8[PF], r8[PF];
+#pragma unroll
+        for (int e = 0; e < PF; ++e) {
+            const size_t tok = ((size_t)b * a.T + t0 + min(tb + e, n_valid - 1)) * a.H + h;
+            al8[e] = a.alpha[tok * DK + i];
+            w8[e] = a.omega[tok * DK + i];
+            kv8[e] = to_f32(kg[tok * DK + i]);
+            r8[e] = a.r[tok];
         }
-        kk[t] = kv;
-        s_ph[t][i] = ph;
+#pragma unroll
+        for (int e = 0; e < PF; ++e) {
+            const int t = tb + e;
+            float ph = 0.f, kv = 0.f;
+            if (t < n_valid) {
+                const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
+                kv = kv8[e];
+                ph = al8[e] * al8[e] * p + w8[e];
+                const float u = (mu_of(a, h) / r8[e]) * kv * kv;
+                if (a.pprev)
+                    a.pprev[tok * DK + i] = p;
+                p = ph * rcp(1.f + u * ph);
+            }
+            kk[t] = kv;
+            s_ph[t][i] = ph;
+        }
     }
     __syncthreads();
     if (i < GC) {
