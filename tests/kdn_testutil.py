@@ -71,3 +71,33 @@ def sample_heads(B, H, n, seed):
     # always include the first and last problem (edges of the grid mapping)
     chosen = {pairs[0], pairs[-1]} | {pairs[i] for i in idx}
     return sorted(chosen)
+
+
+def per_head_rel(x, ref, head_axes):
+    """Relative L2 of every (b, h) problem: x and ref share a layout whose
+    batch axis is 0 and whose head axis is ``head_axes[1]``; the other axes
+    are summed over.  Returns a [B, H] array."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bax, hax = head_axes
+    red = tuple(a for a in range(ref.ndim) if a not in (bax, hax))
+    num = np.sqrt(np.sum(np.square(x - ref), axis=red)) if red else np.abs(x - ref)
+    den = np.sqrt(np.sum(np.square(ref), axis=red)) if red else np.abs(ref)
+    out = np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+    if hax < bax:
+        out = out.T
+    return out
+
+
+def compare_whole(ref, o, S, var, o_head_axes=(0, 2)):
+    """Relative L2 over the whole tensors o, S_T and the final variances (the
+    metric of the parity bar), plus the worst single (b, h) problem of each
+    as a diagnostic.  ``ref`` holds the oracle's o, S and var (or p / b)."""
+    vref = ref["var"] if "var" in ref else ref.get("p", ref.get("b"))
+    err = {"o": rel_l2(o, ref["o"]), "S": rel_l2(S, ref["S"]), "var": rel_l2(var, vref)}
+    worst = {
+        "o": float(per_head_rel(o, ref["o"], o_head_axes).max()),
+        "S": float(per_head_rel(S, ref["S"], (0, 1)).max()),
+        "var": float(per_head_rel(var, vref, (0, 1)).max()),
+    }
+    return err, worst
