@@ -38,7 +38,9 @@
  *       variances p [B,H,dk] (diag) or b [B,H] (iso) fp32.
  *   - io dtype: KDN_F32 or KDN_BF16 for q, k, v and o.  Gates, state and
  *     variances are always fp32.  bf16 runs its chunk contractions on bf16
- *     matrix cores with fp32 accumulation; fp32 runs them in fp32.
+ *     matrix cores with fp32 accumulation (split-operand products for
+ *     Diagonal unless KDN_MATH_BF16 is given, below); fp32 runs them in
+ *     fp32.
  *   - Supported sizes: dk in {64, 128} for bf16 and dk = 64 for fp32;
  *     dv a multiple of 64 (bf16) or 32 (fp32), at most 256; B, H >= 1;
  *     T >= 0; B*H*T and every tensor below 2^31 elements.
@@ -78,6 +80,33 @@ typedef enum {
 
 typedef enum { KDN_F32 = 0, KDN_BF16 = 1 } kdn_dtype;
 typedef enum { KDN_DIAG = 0, KDN_ISO = 1 } kdn_variant;
+
+/* Contraction precision of the bf16 forward, OR-ed into io_dtype of
+ * kdn_diag_fwd, kdn_iso_fwd, kdn_fwd_ex, kdn_fwd_preact and
+ * kdn_fwd_workspace_size (no other call accepts it; nor KDN_OUT_F32 below).
+ *
+ * By default the Diagonal bf16 forward runs every chunk contraction as three
+ * bf16 matrix-core products of split operands, x = hi + lo with hi = bf16(x)
+ * and lo = bf16(x - hi), summed in fp32 (hi.hi + lo.hi + hi.lo): about 16
+ * significant bits per operand, near fp32 results (~1e-5 relative L2 against
+ * an fp64 reference).  This is the higher-precision Diagonal of the KDN
+ * reading notes (results part §6: the mixer throughput figure ran Diagonal in
+ * FP32 / TF32x3 within a BF16 configuration; conclusions part §2: Diagonal
+ * pays for an extra scan and higher-precision compute).  The Isotropic bf16
+ * forward runs single bf16 products, as the notes ran it.
+ *
+ * KDN_MATH_BF16 makes the Diagonal bf16 forward run single bf16 products as
+ * well: faster, ~4e-3 relative L2 on o.  With fp32 io it is
+ * KDN_ERR_INVALID_ARG. */
+enum { KDN_MATH_BF16 = 0x100 };
+
+/* Output dtype flag, OR-ed into io_dtype of the same forward calls: with bf16
+ * q, k, v, the Diagonal forward's split-product contractions write o in fp32
+ * ([B,T,H,dv] float, 16-byte aligned) instead of rounding it to bf16, so o
+ * keeps the contractions' precision.  KDN_ERR_UNSUPPORTED with Isotropic or
+ * with KDN_MATH_BF16; KDN_ERR_INVALID_ARG with fp32 io (o is fp32 there
+ * already). */
+enum { KDN_OUT_F32 = 0x200 };
 
 /* Bytes of device workspace with which kdn_diag_fwd / kdn_iso_fwd (and
  * kdn_fwd_ex) run this shape fastest.  The workspace is optional: a call given

@@ -14,6 +14,8 @@ LIB_PATH = os.path.join(HERE, "libkdn.so")
 
 KDN_F32, KDN_BF16 = 0, 1
 KDN_DIAG, KDN_ISO = 0, 1
+KDN_MATH_BF16 = 0x100  # OR-ed into io_dtype: single bf16 products in the Diagonal bf16 forward
+KDN_OUT_F32 = 0x200    # OR-ed into io_dtype: fp32 o from bf16 q, k, v (Diagonal, split products)
 
 _lib = None
 

@@ -13,7 +13,8 @@ from typing import Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import KDN_BF16, KDN_DIAG, KDN_F32, KDN_ISO, KdnError  # noqa: F401
+from ._lib import (KDN_BF16, KDN_DIAG, KDN_F32, KDN_ISO, KDN_MATH_BF16, KDN_OUT_F32,  # noqa: F401
+                   KdnError)
 
 
 def _io_code(t: torch.Tensor) -> int:
@@ -41,6 +42,17 @@ def _need(t: torch.Tensor, name: str, shape, dtype, device) -> None:
         raise ValueError("%s must be contiguous" % name)
 
 
+def _math_flag(math: Optional[str]) -> int:
+    """Contraction precision of the bf16 forward: None (the library's
+    default: split-operand products for Diagonal, single bf16 products for
+    Isotropic) or "bf16" (single bf16 products)."""
+    if math is None:
+        return 0
+    if math == "bf16":
+        return KDN_MATH_BF16
+    raise ValueError("math must be None or 'bf16', got %r" % (math,))
+
+
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -52,7 +64,8 @@ def _head_vec(t, name, H, dev):
 
 
 def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
-         ext: bool = False, mu_h=None, c0_h=None, beta_eff=None, sequence_parallel=True):
+         ext: bool = False, mu_h=None, c0_h=None, beta_eff=None, sequence_parallel=True,
+         math=None, o_dtype=None):
     L = _lib.lib()
     if q.dim() != 4:
         raise ValueError("q must be [B,T,H,dk]")
@@ -74,9 +87,10 @@ def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
         _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
     if var0 is not None:
         _need(var0, "p0" if variant == KDN_DIAG else "b0", vshape, torch.float32, dev)
+    o_dtype = q.dtype if o_dtype is None else o_dtype
     if o is None:
-        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
-    _need(o, "o", (B, T, H, dv), q.dtype, dev)
+        o = torch.empty((B, T, H, dv), dtype=o_dtype, device=dev)
+    _need(o, "o", (B, T, H, dv), o_dtype, dev)
     if S_T is None:
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _need(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
@@ -84,6 +98,11 @@ def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
         var_T = torch.empty(vshape, dtype=torch.float32, device=dev)
     _need(var_T, "var_T", vshape, torch.float32, dev)
     mu = float(dk if mu is None else mu)
+    io |= _math_flag(math)
+    if o_dtype != q.dtype:
+        if not (q.dtype == torch.bfloat16 and o_dtype == torch.float32):
+            raise TypeError("o may differ from q's dtype only as fp32 with bf16 inputs")
+        io |= KDN_OUT_F32
     # with the workspace, shapes with few heads and long sequences run sequence-parallel
     ws_bytes = L.kdn_fwd_workspace_size(variant, B, T, H, dk, dv, io) if sequence_parallel else 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
@@ -109,20 +128,24 @@ def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
 
 
 def kdn_diag_fwd(q, k, v, alpha, omega, r, S0=None, p0=None, mu=None, o=None, S_T=None,
-                 p_T=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Diagonal KDN forward.  Returns (o [B,T,H,dv], S_T [B,H,dk,dv], p_T [B,H,dk])."""
-    return _fwd(KDN_DIAG, q, k, v, alpha, omega, r, S0, p0, mu, o, S_T, p_T)
+                 p_T=None, math=None, o_dtype=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Diagonal KDN forward.  Returns (o [B,T,H,dv], S_T [B,H,dk,dv], p_T [B,H,dk]).
+    With bf16 q/k/v the contractions run split-operand products (near fp32)
+    unless math="bf16" asks for single bf16 products; o_dtype=torch.float32
+    then writes o in fp32."""
+    return _fwd(KDN_DIAG, q, k, v, alpha, omega, r, S0, p0, mu, o, S_T, p_T, math=math,
+                o_dtype=o_dtype)
 
 
 def kdn_iso_fwd(q, k, v, alpha, omega, r, S0=None, b0=None, mu=None, o=None, S_T=None,
-                b_T=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+                b_T=None, math=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Isotropic KDN forward.  Returns (o [B,T,H,dv], S_T [B,H,dk,dv], b_T [B,H])."""
-    return _fwd(KDN_ISO, q, k, v, alpha, omega, r, S0, b0, mu, o, S_T, b_T)
+    return _fwd(KDN_ISO, q, k, v, alpha, omega, r, S0, b0, mu, o, S_T, b_T, math=math)
 
 
 def kdn_fwd_ex(variant: str, q, k, v, alpha, omega, r, S0=None, var0=None, mu=None,
                mu_h=None, c0_h=None, want_beta_eff: bool = False, o=None, S_T=None,
-               var_T=None, sequence_parallel: bool = True):
+               var_T=None, sequence_parallel: bool = True, math=None, o_dtype=None):
     """Forward with per-head mu_h [H] and c0_h [H] (both optional) and the
     effective write strength.  Returns (o, S_T, var_T, beta_eff [B,T,H] or
     None).  sequence_parallel=False withholds the workspace, so that shapes the
@@ -134,7 +157,7 @@ def kdn_fwd_ex(variant: str, q, k, v, alpha, omega, r, S0=None, var0=None, mu=No
         beta = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
     o, S_T, var_T = _fwd(var, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
                          ext=True, mu_h=mu_h, c0_h=c0_h, beta_eff=beta,
-                         sequence_parallel=sequence_parallel)
+                         sequence_parallel=sequence_parallel, math=math, o_dtype=o_dtype)
     return o, S_T, var_T, beta
 
 
@@ -180,7 +203,7 @@ def kdn_dense_fwd(q, k, v, alpha, omega, r, S0=None, P0=None, want_beta_eff: boo
 
 def kdn_fwd_preact(variant: str, q, k, v, a_pre, w_pre, r_pre, r_min: float = 0.01, S0=None,
                    var0=None, mu=None, mu_h=None, c0_h=None, want_beta_eff: bool = False,
-                   o=None, S_T=None, var_T=None, workspace=None):
+                   o=None, S_T=None, var_T=None, workspace=None, math=None):
     """Forward from the gates' pre-activations (alpha = sigmoid(a_pre),
     omega = softplus(w_pre), r = r_min + softplus(r_pre)); pre-activations in
     the io dtype of q.  Returns (o, S_T, var_T, beta_eff or None)."""
@@ -217,7 +240,8 @@ def kdn_fwd_preact(variant: str, q, k, v, a_pre, w_pre, r_pre, r_min: float = 0.
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
-        st = L.kdn_fwd_preact(var, B, T, H, dk, dv, io, mu, _ptr(mu_h), _ptr(q), _ptr(k), _ptr(v),
+        st = L.kdn_fwd_preact(var, B, T, H, dk, dv, io | _math_flag(math), mu, _ptr(mu_h),
+                              _ptr(q), _ptr(k), _ptr(v),
                               _ptr(a_pre), _ptr(w_pre), _ptr(r_pre), float(r_min), _ptr(S0),
                               _ptr(var0), _ptr(c0_h), _ptr(o), _ptr(S_T), _ptr(var_T),
                               _ptr(beta), _ptr(workspace), workspace.numel(), _stream(dev))

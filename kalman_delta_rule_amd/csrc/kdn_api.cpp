@@ -87,6 +87,25 @@ kdn_status check_common(int B, int T, int H, int dk, int dv, int io, float mu, b
             return fail(KDN_ERR_INVALID_ARG, "%s must be 4-byte aligned", name);  \
     } while (0)
 
+// The io dtype of a forward call and its contraction-precision flag:
+// KDN_MATH_BF16 (bf16 io only) selects single bf16 products for Diagonal.
+kdn_status split_io(int io_dtype, int& io, bool& math_bf16, bool& out_f32)
+{
+    math_bf16 = (io_dtype & KDN_MATH_BF16) != 0;
+    out_f32 = (io_dtype & KDN_OUT_F32) != 0;
+    io = io_dtype & ~(KDN_MATH_BF16 | KDN_OUT_F32);
+    if (io != KDN_F32 && io != KDN_BF16)
+        return fail(KDN_ERR_INVALID_ARG,
+                    "io_dtype must be KDN_F32 (0) or KDN_BF16 (1), optionally with "
+                    "KDN_MATH_BF16 (0x100) or KDN_OUT_F32 (0x200) for bf16, got %d", io_dtype);
+    if ((math_bf16 || out_f32) && io != KDN_BF16)
+        return fail(KDN_ERR_INVALID_ARG, "KDN_MATH_BF16 and KDN_OUT_F32 apply to bf16 io only");
+    if (out_f32 && math_bf16)
+        return fail(KDN_ERR_UNSUPPORTED, "KDN_OUT_F32 comes with the split-product contractions, "
+                                         "not with KDN_MATH_BF16");
+    return KDN_OK;
+}
+
 // Per-head options and the diagnostic output of the extended calls.
 struct ExtOpts {
     const float* mu_h = nullptr;  // [H] or null
@@ -108,14 +127,21 @@ kdn_status check_ext(const ExtOpts& x, const void* var0, const void* r, const vo
     return KDN_OK;
 }
 
-kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float mu,
+kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io_dtype, float mu,
                     const void* q, const void* k, const void* v, const float* alpha,
                     const float* omega, const float* r, const float* S0, const float* var0,
                     void* o, float* S_T, float* var_T, void* workspace,
                     size_t workspace_bytes, void* stream, const ExtOpts& x = ExtOpts{},
                     const kdn::PrologueArgs* pro = nullptr)
 {
-    kdn_status st = check_common(B, T, H, dk, dv, io, mu, true);
+    int io;
+    bool math_bf16, out_f32;
+    kdn_status st = split_io(io_dtype, io, math_bf16, out_f32);
+    if (st != KDN_OK)
+        return st;
+    if (out_f32 && iso)
+        return fail(KDN_ERR_UNSUPPORTED, "KDN_OUT_F32 is built for the Diagonal forward");
+    st = check_common(B, T, H, dk, dv, io, mu, true);
     if (st != KDN_OK)
         return st;
     st = check_ext(x, var0, r, o, S_T, var_T);
@@ -178,7 +204,7 @@ kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float
         const struct { const void* p; size_t n; const char* name; } bufs[] = {
             {q, ntok * dk * 2, "q"}, {k, ntok * dk * 2, "k"}, {v, ntok * dv * 2, "v"},
             {alpha, ntok * dk * 4, "alpha"}, {omega, ntok * (iso ? 1 : dk) * 4, "omega"},
-            {r, ntok * 4, "r"}, {o, ntok * dv * 2, "o"}, {S0, nst, "S0"}, {S_T, nst, "S_T"},
+            {r, ntok * 4, "r"}, {o, ntok * dv * (out_f32 ? 4 : 2), "o"}, {S0, nst, "S0"}, {S_T, nst, "S_T"},
             {var0, nvar, "var0"}, {var_T, nvar, "var_T"}, {x.mu_h, (size_t)H * 4, "mu_h"},
             {x.c0_h, (size_t)H * 4, "c0_h"}, {x.beta_eff, ntok * 4, "beta_eff"}};
         for (const auto& b : bufs) {
@@ -190,6 +216,9 @@ kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io, float
 
     kdn::FwdArgs a{q, k, v, alpha, omega, r, S0, var0, o, S_T, var_T, B, T, H, dk, dv, mu,
                    x.mu_h, x.c0_h, T > 0 ? x.beta_eff : nullptr};
+    // the Diagonal bf16 walk runs split-operand products unless told otherwise
+    a.split = !iso && io == KDN_BF16 && !math_bf16;
+    a.o_f32 = out_f32;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     if (pro && T > 0) {  // the gates from their pre-activations, into the workspace
         hipError_t e = kdn::launch_gate_prologue(*pro, io, hs);
@@ -213,7 +242,8 @@ size_t kdn_fwd_workspace_size(int variant, int B, int T, int H, int dk, int dv, 
     if (B < 0 || T < 0 || H <= 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128))
         return 0;
     const bool iso = variant == KDN_ISO;
-    const int nseg = kdn::seqpar_segments(iso, B, T, H, dk, dv, io_dtype);
+    const int nseg =
+        kdn::seqpar_segments(iso, B, T, H, dk, dv, io_dtype & ~(KDN_MATH_BF16 | KDN_OUT_F32));
     // zero: the walk keeps every intermediate on chip; otherwise the
     // sequence-parallel path's segment states and carries
     return nseg ? kdn::seqpar_workspace_floats(iso, B, T, H, dk, dv, nseg) * sizeof(float) : 0;
@@ -380,9 +410,11 @@ kdn_status kdn_fwd_preact(int variant, int B, int T, int H, int dk, int dv, int 
     if (variant != KDN_DIAG && variant != KDN_ISO)
         return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
                     variant);
-    if (io_dtype != KDN_F32 && io_dtype != KDN_BF16)
-        return fail(KDN_ERR_INVALID_ARG, "io_dtype must be KDN_F32 (0) or KDN_BF16 (1), got %d",
-                    io_dtype);
+    int io;
+    bool math_bf16, out_f32;
+    kdn_status st = split_io(io_dtype, io, math_bf16, out_f32);
+    if (st != KDN_OK)
+        return st;
     if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1)
         return fail(KDN_ERR_INVALID_ARG, "need B >= 1, H >= 1, T >= 0 (got B=%d T=%d H=%d)", B, T, H);
     if (!(r_min > 0.f) || r_min > 3.0e38f)
@@ -402,14 +434,14 @@ kdn_status kdn_fwd_preact(int variant, int B, int T, int H, int dk, int dv, int 
                     workspace_bytes);
     KDN_ALIGNED(workspace, "workspace");
     // the workspace (which receives the gates) must be disjoint from every argument
-    const size_t es = io_dtype == KDN_BF16 ? 2 : 4;
+    const size_t es = io == KDN_BF16 ? 2 : 4;
     const size_t ntok = (size_t)B * T * H, bh = (size_t)B * H;
     const size_t nw = iso ? ntok : ntok * dk, nvar = iso ? bh : bh * dk;
     struct Buf { const void* p; size_t n; const char* name; };
     const Buf bufs[] = {{q, ntok * dk * es, "q"}, {k, ntok * dk * es, "k"},
                         {v, ntok * dv * es, "v"}, {a_pre, ntok * dk * es, "a_pre"},
                         {w_pre, nw * es, "w_pre"}, {r_pre, ntok * es, "r_pre"},
-                        {o, ntok * dv * es, "o"}, {S0, bh * dk * dv * 4, "S0"},
+                        {o, ntok * dv * (out_f32 ? 4 : es), "o"}, {S0, bh * dk * dv * 4, "S0"},
                         {S_T, bh * dk * dv * 4, "S_T"}, {var0, nvar * 4, "var0"},
                         {var_T, nvar * 4, "var_T"}, {beta_eff, ntok * 4, "beta_eff"},
                         {mu_h, (size_t)H * 4, "mu_h"}, {c0_h, (size_t)H * 4, "c0_h"}};
@@ -600,9 +632,11 @@ kdn_status kdn_bwd_preact(int variant, int B, int T, int H, int dk, int dv, int 
     if (variant != KDN_DIAG && variant != KDN_ISO)
         return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
                     variant);
-    if (io_dtype != KDN_F32 && io_dtype != KDN_BF16)
-        return fail(KDN_ERR_INVALID_ARG, "io_dtype must be KDN_F32 (0) or KDN_BF16 (1), got %d",
-                    io_dtype);
+    int io;
+    bool math_bf16, out_f32;
+    kdn_status st = split_io(io_dtype, io, math_bf16, out_f32);
+    if (st != KDN_OK)
+        return st;
     if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1)
         return fail(KDN_ERR_INVALID_ARG, "need B >= 1, H >= 1, T >= 0 (got B=%d T=%d H=%d)", B, T, H);
     if (!(r_min > 0.f) || r_min > 3.0e38f)

@@ -24,6 +24,8 @@ struct FwdArgs {
     const float* mu_h;  // nullable [H]: per-head information scale (overrides mu)
     const float* c0;    // nullable [H]: initial variance of every channel of a head when var0 is null
     float* beta;        // nullable [B,T,H]: effective write strength z / (r + z)
+    bool split = false; // bf16 Diagonal walk: split-bf16 products (three per contraction)
+    bool o_f32 = false; // with split: o is fp32 although q, k, v are bf16
 };
 
 struct StepArgs {

@@ -156,10 +156,10 @@ __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b)
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// round to nearest even, two values per conversion instruction
 __device__ __forceinline__ bf16x4 cvt4(const f32x4& x)
 {
-    return bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
-                  static_cast<bf16>(x[3])};
+    return __builtin_convertvector(x, bf16x4);
 }
 
 __device__ __forceinline__ float bcast(float x, int lane)
@@ -190,12 +190,22 @@ __device__ __forceinline__ void mfma32(f32x4& d, const bf16x8& a, const bf16x8& 
 // Wave roles of one workgroup.
 enum Role { R_MEM, R_BLD, R_ELT, R_FAC1, R_FAC2, R_LDR, R_ISO };
 
-template <int DK_, int NB_, int NMW_, bool ISO_>
+template <int DK_, int NB_, int NMW_, bool ISO_, bool X3_ = false, bool OF32_ = false>
 struct Cfg {
     static constexpr int DK = DK_;
     static constexpr int NB = NB_;    // 16-column blocks per memory wave
     static constexpr int NMW = NMW_;  // memory waves
     static constexpr bool ISO = ISO_;
+    // split products (Diagonal only): every matrix-core operand is a pair of
+    // bf16 values hi + lo with lo = bf16(x - hi), and every contraction is the
+    // three bf16 products hi.hi + lo.hi + hi.lo accumulated in fp32, which
+    // carries about 16 significant bits per operand instead of 8
+    static constexpr bool X3 = X3_;
+    static_assert(!(X3_ && ISO_), "split products are built for the Diagonal variant");
+    // o written in fp32 (split products only): the output keeps the
+    // contractions' precision instead of rounding to bf16
+    static constexpr bool OF32 = OF32_;
+    static_assert(!OF32_ || X3_, "fp32 output comes with split products");
     static constexpr int DVT = 16 * NB * NMW;
     // builder waves, one lane per key channel.  Diagonal splits the builder
     // work: these waves run the variance recurrence and form Ktp and G_C,
@@ -209,7 +219,11 @@ struct Cfg {
     // Entry w: role * 8 + index within the role.
     static constexpr int layout(int w)
     {
-        if constexpr (DK == 128 && NMW == 2 && !ISO) {
+        if constexpr (DK == 128 && NMW == 2 && !ISO && X3_) {
+            constexpr int L[8] = {R_MEM * 8, R_MEM * 8 + 1, R_BLD * 8, R_BLD * 8 + 1,
+                                  R_FAC2 * 8, R_LDR * 8, R_FAC1 * 8, R_ELT * 8};
+            return L[w];
+        } else if constexpr (DK == 128 && NMW == 2 && !ISO) {
             constexpr int L[8] = {R_MEM * 8, R_MEM * 8 + 1, R_BLD * 8, R_BLD * 8 + 1,
                                   R_FAC2 * 8, R_LDR * 8, R_FAC1 * 8, R_ELT * 8};
             return L[w];
@@ -279,6 +293,68 @@ struct Smem {
     Raw raw[CF::NRAW];
 };
 
+// LDS of the split-product walk.  Kb and Qb (hi and lo) live from the
+// elementwise wave's write (step X - 3) to the memory waves' fetch during step
+// X - 1, so three slots suffice; Ktp (hi and lo) and G_C are read by the memory
+// waves in step X itself and keep four.  The second factor wave forms Aqk one
+// step later than in the single-product walk, so the memory waves read it with
+// T after the barrier.
+template <typename CF>
+struct SmemX3 {
+    static constexpr int DK = CF::DK;
+    struct KQ {  // elementwise wave -> first factor wave, second factor wave, memory
+        alignas(16) bf16 Kb[4 * CF::QS];
+        alignas(16) bf16 Kl[4 * CF::QS];
+        alignas(16) bf16 Qb[4 * CF::QS];
+        alignas(16) bf16 Ql[4 * CF::QS];
+    };
+    struct KT {  // builders -> factor waves, memory
+        alignas(16) bf16 Ktp[4 * CF::QS];
+        alignas(16) bf16 Ktl[4 * CF::QS];
+        alignas(16) float gC[DK];
+    };
+    struct Tri {
+        alignas(16) float Mt[C * 20];
+        alignas(16) float Mr[8 * 20];
+        alignas(16) float dinv[C];
+        alignas(16) float dinvr[8];
+        alignas(16) float Xs[C * 8];
+        alignas(16) bf16 T[C * C];
+        alignas(16) bf16 Tl[C * C];
+        alignas(16) bf16 Aqk[C * CF::LDF];
+        alignas(16) bf16 Aql[C * CF::LDF];
+    };
+    struct Raw {
+        alignas(16) float alpha[C * DK];
+        alignas(16) bf16 k[C * DK];
+        alignas(16) bf16 q[C * DK];
+    };
+    KT kt[4];
+    Tri tri[3];
+    alignas(16) bf16 v[3][C * CF::DVT];
+    alignas(16) float rr[NRING][C];
+    alignas(16) float wr[NRING][C];
+    alignas(16) float bh[NRING][C];
+    KQ kq[3];
+    Raw raw[CF::NRAW];
+};
+
+// hi / lo halves of a split operand: hi = bf16(x), lo = bf16(x - hi), both
+// rounded to nearest even; hi is widened back by a shift or a mask of its
+// packed pair, so four values take 12 vector instructions
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split4(const f32x4& x, bf16x4& hi, bf16x4& lo)
+{
+    hi = cvt4(x);
+    const u32x2 w = __builtin_bit_cast(u32x2, hi);
+    f32x4 r;
+    r[0] = x[0] - __uint_as_float(w[0] << 16);
+    r[1] = x[1] - __uint_as_float(w[0] & 0xffff0000u);
+    r[2] = x[2] - __uint_as_float(w[1] << 16);
+    r[3] = x[3] - __uint_as_float(w[1] & 0xffff0000u);
+    lo = cvt4(r);
+}
+
 // Offset (elements) of the 8-byte segment that lane (g, l16) addresses in a
 // token-quad operand so that ds_read_tr returns, in lane (g, c), the values
 // X[t = c][4 g + e], e = 0..3 (channel offset i0 adds 4 i0 elements).
@@ -299,7 +375,7 @@ __device__ __forceinline__ bf16x8 quad_frag32(const bf16* lane_base, int m)
 template <typename CF>
 __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArgs a)
 {
-    using SM = Smem<CF>;
+    using SM = std::conditional_t<CF::X3, SmemX3<CF>, Smem<CF>>;
     constexpr int DK = CF::DK;
     constexpr int NB = CF::NB;
     constexpr int NMW = CF::NMW;
@@ -387,9 +463,157 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         }
         // o rows of this lane (token c16 of each chunk), advanced per chunk
         const size_t o_step = (size_t)C * H * dv;
-        bf16* orow = reinterpret_cast<bf16*>(a.o) + row_v(min(c16, max(T - 1, 0))) + j0 +
-                     16 * NB * w + 4 * g4;
+        const size_t o_el = row_v(min(c16, max(T - 1, 0))) + j0 + 16 * NB * w + 4 * g4;
+        bf16* orow = reinterpret_cast<bf16*>(reinterpret_cast<char*>(a.o) +
+                                             o_el * (CF::OF32 ? sizeof(float) : sizeof(bf16)));
 
+        if constexpr (CF::X3) {
+            // ---- split products: Kb and Qb (hi, lo) of chunk c + 1 are
+            // fetched during step c, into the registers the front products of
+            // chunk c have just consumed; T and Aqk (hi, lo) are read after
+            // the barrier with v
+            struct MemOpsX {
+                bf16x8 kh[DK / 32], kl[DK / 32], qh[DK / 32], ql[DK / 32];
+            };
+            auto fetchx = [&](int c, MemOpsX& m) {
+                const auto& kq = sm.kq[c % 3];
+#pragma unroll
+                for (int mm = 0; mm < DK / 32; ++mm) {
+                    m.kh[mm] = quad_frag32(kq.Kb + tr_lane, mm);
+                    m.kl[mm] = quad_frag32(kq.Kl + tr_lane, mm);
+                    m.qh[mm] = quad_frag32(kq.Qb + tr_lane, mm);
+                    m.ql[mm] = quad_frag32(kq.Ql + tr_lane, mm);
+                }
+            };
+            const bf16x4 z4{};
+            auto applyx = [&](auto full_tag, int c, MemOpsX& m) {
+                constexpr bool FULL = decltype(full_tag)::value;
+                const int nv = FULL ? C : n_valid(c);
+                const auto& kt = sm.kt[c & 3];
+                const auto& tri = sm.tri[c % 3];
+                const bf16* V = sm.v[c % 3];
+                const bf16x4 th = *reinterpret_cast<const bf16x4*>(tri.T + c16 * C + 4 * g4);
+                const bf16x4 tl = *reinterpret_cast<const bf16x4*>(tri.Tl + c16 * C + 4 * g4);
+                const bf16x4 ah = *reinterpret_cast<const bf16x4*>(tri.Aqk + fr_lane);
+                const bf16x4 al = *reinterpret_cast<const bf16x4*>(tri.Aql + fr_lane);
+                bf16x4 vfr[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    vfr[nb] = ds_read_tr(V + v_lane[nb]);
+                reads_issued();
+                if constexpr (!FULL) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * g4 + e >= nv)
+                                vfr[nb][e] = static_cast<bf16>(0.f);
+                }
+                // front: Y = Kb S, O^T = S^T Qb^T, each as hi.hi + lo.hi + hi.lo
+                f32x4 accY[NB], accO[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    accY[nb] = zero4();
+                    accO[nb] = zero4();
+                }
+                // S's next 32 rows are split while the current 32 rows'
+                // products run, so vector and matrix work can overlap
+                auto split_rows = [&](int mm, bf16x8 (&sh)[NB], bf16x8 (&sl)[NB]) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        bf16x4 h0, l0, h1, l1;
+                        split4(Sacc[nb][2 * mm], h0, l0);
+                        split4(Sacc[nb][2 * mm + 1], h1, l1);
+                        sh[nb] = cat8(h0, h1);
+                        sl[nb] = cat8(l0, l1);
+                    }
+                };
+                bf16x8 sh[NB], sl[NB];
+                split_rows(0, sh, sl);
+                reads_issued();
+#pragma unroll
+                for (int mm = 0; mm < DK / 32; ++mm) {
+                    bf16x8 nh[NB], nl[NB];
+                    if (mm + 1 < DK / 32)
+                        split_rows(mm + 1, nh, nl);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        mfma32(accY[nb], m.kh[mm], sh[nb]);
+                        mfma32(accO[nb], sh[nb], m.qh[mm]);
+                        mfma32(accY[nb], m.kl[mm], sh[nb]);
+                        mfma32(accO[nb], sh[nb], m.ql[mm]);
+                        mfma32(accY[nb], m.kh[mm], sl[nb]);
+                        mfma32(accO[nb], sl[nb], m.qh[mm]);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        sh[nb] = nh[nb];
+                        sl[nb] = nl[nb];
+                    }
+                }
+                bf16x4 kth[DK / 16], ktl[DK / 16];
+                f32x4 gcf[DK / 16];
+#pragma unroll
+                for (int n = 0; n < DK / 16; ++n) {
+                    kth[n] = *reinterpret_cast<const bf16x4*>(kt.Ktp + kt_lane + 64 * n);
+                    ktl[n] = *reinterpret_cast<const bf16x4*>(kt.Ktl + kt_lane + 64 * n);
+                    gcf[n] = *reinterpret_cast<const f32x4*>(&kt.gC[16 * n + 4 * g4]);
+                }
+                bf16x4 dh[NB], dl[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    f32x4 res;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        res[e] = static_cast<float>(vfr[nb][e]) - accY[nb][e];
+                    bf16x4 rh, rl;
+                    split4(res, rh, rl);
+                    f32x4 accD = zero4();
+                    mfma32(accD, cat8(th, tl), cat8(rh, rh));
+                    mfma32(accD, cat8(th, z4), cat8(rl, z4));
+                    split4(accD, dh[nb], dl[nb]);
+                    mfma32(accO[nb], cat8(dh[nb], dl[nb]), cat8(ah, ah));
+                    mfma32(accO[nb], cat8(dh[nb], z4), cat8(al, z4));
+                    if (FULL || c16 < nv) {
+                        if constexpr (CF::OF32)
+                            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(orow) + 16 * nb) = accO[nb];
+                        else
+                            *reinterpret_cast<bf16x4*>(orow + 16 * nb) = cvt4(accO[nb]);
+                    }
+                }
+                reads_issued();
+                if (c + 1 < nchunks)
+                    fetchx(c + 1, m);
+                reads_issued();
+#pragma unroll
+                for (int n = 0; n < DK / 16; ++n) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        mfma32(Sacc[nb][n], cat8(kth[n], ktl[n]), cat8(dh[nb], dh[nb]));
+                        mfma32(Sacc[nb][n], cat8(kth[n], z4), cat8(dl[nb], z4));
+                        Sacc[nb][n] *= gcf[n];
+                    }
+                }
+            };
+            for (int c = -LR; c < 0; ++c)
+                lds_barrier();
+            MemOpsX ops;
+            if (nchunks > 0)
+                fetchx(0, ops);
+            const int nfull = T / C;
+            // o advances one chunk of rows per step (twice the elements' bytes
+            // with fp32 output, counted in bf16 units)
+            const size_t ostep = CF::OF32 ? 2 * o_step : o_step;
+            for (int c = 0; c < nfull; ++c) {
+                applyx(std::integral_constant<bool, true>{}, c, ops);
+                orow += ostep;
+                lds_barrier();
+            }
+            if (nfull < nchunks) {
+                applyx(std::integral_constant<bool, false>{}, nfull, ops);
+                lds_barrier();
+            }
+        } else {
         // operands of one chunk that were written two or more steps before
         // the memory waves apply it; they are fetched during the previous
         // step, after that step's own reads have landed, which takes them
@@ -522,6 +746,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 apply(std::integral_constant<bool, false>{}, nfull, opA, opB);
             lds_barrier();
         }
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             float* ST = a.S_T + (size_t)bh * DK * dv + j0 + 16 * (NB * w + nb) + c16;
@@ -559,7 +784,6 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             constexpr bool FULL = decltype(full_tag)::value;
             const int nv = FULL ? C : n_valid(X);
             const auto& raw = sm.raw[X % NRAW];
-            auto& op = sm.op[X & (NOPS - 1)];
             // per-token scalars, computed by lanes 0..15 and broadcast:
             // Diagonal mu / r_t, Isotropic b^_t
             const float tokr = ISO ? sm.bh[X % NRING][c16] : sm.rr[X % NRING][c16];
@@ -638,22 +862,36 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 }
             }
             // token-quad writes: channel i's four tokens 4 tq .. +3 as 8 bytes
+            if constexpr (CF::X3) {
+                auto& ks = sm.kt[X & 3];
 #pragma unroll
-            for (int tq = 0; tq < 4; ++tq) {
-                const int o = tq * QS + i * 4;
-                if constexpr (!CF::SPLIT) {
-                    *reinterpret_cast<bf16x4*>(op.Kb + o) =
-                        bf16x4{static_cast<bf16>(kb[4 * tq]), static_cast<bf16>(kb[4 * tq + 1]),
-                               static_cast<bf16>(kb[4 * tq + 2]), static_cast<bf16>(kb[4 * tq + 3])};
-                    *reinterpret_cast<bf16x4*>(op.Qb + o) =
-                        bf16x4{static_cast<bf16>(qb[4 * tq]), static_cast<bf16>(qb[4 * tq + 1]),
-                               static_cast<bf16>(qb[4 * tq + 2]), static_cast<bf16>(qb[4 * tq + 3])};
+                for (int tq = 0; tq < 4; ++tq) {
+                    const int o = tq * QS + i * 4;
+                    bf16x4 hi, lo;
+                    split4(f32x4{kt[4 * tq], kt[4 * tq + 1], kt[4 * tq + 2], kt[4 * tq + 3]}, hi, lo);
+                    *reinterpret_cast<bf16x4*>(ks.Ktp + o) = hi;
+                    *reinterpret_cast<bf16x4*>(ks.Ktl + o) = lo;
                 }
-                *reinterpret_cast<bf16x4*>(op.Ktp + o) =
-                    bf16x4{static_cast<bf16>(kt[4 * tq]), static_cast<bf16>(kt[4 * tq + 1]),
-                           static_cast<bf16>(kt[4 * tq + 2]), static_cast<bf16>(kt[4 * tq + 3])};
+                ks.gC[i] = G;
+            } else {
+                auto& op = sm.op[X & (NOPS - 1)];
+#pragma unroll
+                for (int tq = 0; tq < 4; ++tq) {
+                    const int o = tq * QS + i * 4;
+                    if constexpr (!CF::SPLIT) {
+                        *reinterpret_cast<bf16x4*>(op.Kb + o) =
+                            bf16x4{static_cast<bf16>(kb[4 * tq]), static_cast<bf16>(kb[4 * tq + 1]),
+                                   static_cast<bf16>(kb[4 * tq + 2]), static_cast<bf16>(kb[4 * tq + 3])};
+                        *reinterpret_cast<bf16x4*>(op.Qb + o) =
+                            bf16x4{static_cast<bf16>(qb[4 * tq]), static_cast<bf16>(qb[4 * tq + 1]),
+                                   static_cast<bf16>(qb[4 * tq + 2]), static_cast<bf16>(qb[4 * tq + 3])};
+                    }
+                    *reinterpret_cast<bf16x4*>(op.Ktp + o) =
+                        bf16x4{static_cast<bf16>(kt[4 * tq]), static_cast<bf16>(kt[4 * tq + 1]),
+                               static_cast<bf16>(kt[4 * tq + 2]), static_cast<bf16>(kt[4 * tq + 3])};
+                }
+                op.gC[i] = G;
             }
-            op.gC[i] = G;
         };
         settle_counters();
         // slot of chunk X: (X - LB + LR) mod (OPF + 1); the first step
@@ -699,22 +937,45 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             const int F = c + 2;
             if (F >= 0 && F < nchunks) {
                 const int nv = n_valid(F);
-                const auto& op = sm.op[F & (NOPS - 1)];
                 auto& tr = sm.tri[F % 3];
                 const float* rr = sm.rr[F % NRING];
-                bf16x8 kbf[DK / 32], ktf[DK / 32], qbf[DK / 32];
-#pragma unroll
-                for (int m = 0; m < DK / 32; ++m) {
-                    kbf[m] = quad_frag32(op.Kb + tr_lane, m);
-                    ktf[m] = quad_frag32(op.Ktp + tr_lane, m);
-                    qbf[m] = quad_frag32(op.Qb + tr_lane, m);
-                }
                 // L'[t][s] = Kb_t . Ktp_s,   Aqk^T[u][t] = Ktp_u . Qb_t
                 f32x4 accL = zero4(), accQ = zero4();
+                if constexpr (CF::X3) {
+                    // L' only (Aqk is the second factor wave's), as
+                    // hi.hi + (lo.hi + hi.lo), the small terms summed first
+                    const auto& kq = sm.kq[F % 3];
+                    const auto& ks = sm.kt[F & 3];
+                    bf16x8 kbh[DK / 32], kbl[DK / 32], kth[DK / 32], ktl[DK / 32];
 #pragma unroll
-                for (int m = 0; m < DK / 32; ++m) {
-                    mfma32(accL, kbf[m], ktf[m]);
-                    mfma32(accQ, ktf[m], qbf[m]);
+                    for (int m = 0; m < DK / 32; ++m) {
+                        kbh[m] = quad_frag32(kq.Kb + tr_lane, m);
+                        kbl[m] = quad_frag32(kq.Kl + tr_lane, m);
+                        kth[m] = quad_frag32(ks.Ktp + tr_lane, m);
+                        ktl[m] = quad_frag32(ks.Ktl + tr_lane, m);
+                    }
+                    f32x4 accS = zero4();
+#pragma unroll
+                    for (int m = 0; m < DK / 32; ++m) {
+                        mfma32(accL, kbh[m], kth[m]);
+                        mfma32(accS, kbl[m], kth[m]);
+                        mfma32(accS, kbh[m], ktl[m]);
+                    }
+                    accL += accS;
+                } else {
+                    const auto& op = sm.op[F & (NOPS - 1)];
+                    bf16x8 kbf[DK / 32], ktf[DK / 32], qbf[DK / 32];
+#pragma unroll
+                    for (int m = 0; m < DK / 32; ++m) {
+                        kbf[m] = quad_frag32(op.Kb + tr_lane, m);
+                        ktf[m] = quad_frag32(op.Ktp + tr_lane, m);
+                        qbf[m] = quad_frag32(op.Qb + tr_lane, m);
+                    }
+#pragma unroll
+                    for (int m = 0; m < DK / 32; ++m) {
+                        mfma32(accL, kbf[m], ktf[m]);
+                        mfma32(accQ, ktf[m], qbf[m]);
+                    }
                 }
                 // M^T[s][t] = L'[t][s]   (lane holds L'[4 g4 + r][c16]); the
                 // second factor wave reads its lower-left block
@@ -738,7 +999,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                         a.beta[row_s(F * C + c16)] = z * dv;
                 }
                 // Aqk[t][u] = Aqk^T[u][t] for u <= t, else 0
-                {
+                if constexpr (!CF::X3) {
                     f32x4 aq;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -806,6 +1067,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         const bool v11 = c16 < 8 && g4 < 2, v22 = c16 >= 8 && g4 >= 2;
         const bool v21 = c16 < 8 && g4 >= 2;
         const int xs_off = c16 * 8 + (c16 < 8 ? 4 - 4 * (g4 & 1) : 4 * (g4 & 1));
+        const int tr_lane = quad_tr_lane<QS>(lane);
         for (int c = -LR; c < nchunks; ++c) {
             const int F = c + 1;
             if (F >= 0 && F < nchunks) {
@@ -827,7 +1089,41 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     y[r] = (4 * g4 + r == c16 && c16 < 8) ? 1.f - q[r] : -q[r];
                 f32x4 rt = zero4();
                 mma_tn(rt, t11, y);
-                *reinterpret_cast<bf16x4*>(&tr.T[c16 * C + 4 * g4]) = cvt4(g4 < 2 ? rt : t22t);
+                if constexpr (CF::X3) {
+                    bf16x4 hi, lo;
+                    split4(g4 < 2 ? rt : t22t, hi, lo);
+                    *reinterpret_cast<bf16x4*>(&tr.T[c16 * C + 4 * g4]) = hi;
+                    *reinterpret_cast<bf16x4*>(&tr.Tl[c16 * C + 4 * g4]) = lo;
+                    // Aqk of the same chunk: Aqk^T[u][t] = Ktp_u . Qb_t in split
+                    // products, then Aqk[t][u] for u <= t (hi and lo)
+                    const auto& kq = sm.kq[F % 3];
+                    const auto& ks = sm.kt[F & 3];
+                    bf16x8 qbh[DK / 32], qbl[DK / 32], kth[DK / 32], ktl[DK / 32];
+#pragma unroll
+                    for (int m = 0; m < DK / 32; ++m) {
+                        qbh[m] = quad_frag32(kq.Qb + tr_lane, m);
+                        qbl[m] = quad_frag32(kq.Ql + tr_lane, m);
+                        kth[m] = quad_frag32(ks.Ktp + tr_lane, m);
+                        ktl[m] = quad_frag32(ks.Ktl + tr_lane, m);
+                    }
+                    f32x4 accQ = zero4(), accS = zero4();
+#pragma unroll
+                    for (int m = 0; m < DK / 32; ++m) {
+                        mfma32(accQ, kth[m], qbh[m]);
+                        mfma32(accS, ktl[m], qbh[m]);
+                        mfma32(accS, kth[m], qbl[m]);
+                    }
+                    accQ += accS;
+                    f32x4 aq;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        aq[r] = (4 * g4 + r <= c16) ? accQ[r] : 0.f;
+                    split4(aq, hi, lo);
+                    *reinterpret_cast<bf16x4*>(&tr.Aqk[c16 * LDF + 4 * g4]) = hi;
+                    *reinterpret_cast<bf16x4*>(&tr.Aql[c16 * LDF + 4 * g4]) = lo;
+                } else {
+                    *reinterpret_cast<bf16x4*>(&tr.T[c16 * C + 4 * g4]) = cvt4(g4 < 2 ? rt : t22t);
+                }
             }
             lds_barrier();
         }
@@ -952,7 +1248,19 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 constexpr bool FULL = decltype(full_tag)::value;
                 const int nv = FULL ? C : n_valid(X);
                 const auto& raw = sm.raw[X % NRAW];
-                auto& op = sm.op[X & (NOPS - 1)];
+                // destinations: Kb, Qb (and their lo halves with split products)
+                bf16 *dKb, *dQb, *dKl = nullptr, *dQl = nullptr;
+                if constexpr (CF::X3) {
+                    auto& kq = sm.kq[X % 3];
+                    dKb = kq.Kb;
+                    dQb = kq.Qb;
+                    dKl = kq.Kl;
+                    dQl = kq.Ql;
+                } else {
+                    auto& op = sm.op[X & (NOPS - 1)];
+                    dKb = op.Kb;
+                    dQb = op.Qb;
+                }
                 float al[CPL][C], kf[CPL][C], qf[CPL][C];
                 if constexpr (CPL == 2) {
                     float2 a2[C];
@@ -980,7 +1288,8 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                         qf[0][t] = static_cast<float>(raw.q[t * DK + lane]);
                     }
                 }
-                bf16 kb[CPL][C], qb[CPL][C];
+                bf16 kb[CPL][C], qb[CPL][C], kl[CPL][C], ql[CPL][C];
+                float xk[CPL][C], xq[CPL][C];
 #pragma unroll
                 for (int e = 0; e < CPL; ++e) {
                     float G = 1.f;
@@ -988,27 +1297,55 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     for (int t = 0; t < C; ++t) {
                         const bool ok = FULL || t < nv;  // padded tokens: alpha = 1, k = q = 0
                         G *= ok ? al[e][t] : 1.f;
-                        kb[e][t] = static_cast<bf16>(ok ? kf[e][t] * G : 0.f);
-                        qb[e][t] = static_cast<bf16>(ok ? qf[e][t] * G : 0.f);
+                        xk[e][t] = ok ? kf[e][t] * G : 0.f;
+                        xq[e][t] = ok ? qf[e][t] * G : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < CPL; ++e) {
+#pragma unroll
+                    for (int t = 0; t < C; t += 4) {
+                        const f32x4 k4{xk[e][t], xk[e][t + 1], xk[e][t + 2], xk[e][t + 3]};
+                        const f32x4 q4{xq[e][t], xq[e][t + 1], xq[e][t + 2], xq[e][t + 3]};
+                        bf16x4 kh, qh, klo, qlo;
+                        if constexpr (CF::X3) {
+                            split4(k4, kh, klo);
+                            split4(q4, qh, qlo);
+                        } else {
+                            kh = cvt4(k4);
+                            qh = cvt4(q4);
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            kb[e][t + j] = kh[j];
+                            qb[e][t + j] = qh[j];
+                            if constexpr (CF::X3) {
+                                kl[e][t + j] = klo[j];
+                                ql[e][t + j] = qlo[j];
+                            }
+                        }
                     }
                 }
                 // token-quad writes: the lane's channels are adjacent, so the
                 // four tokens of each sit in one 8 * CPL byte run
-#pragma unroll
-                for (int tq = 0; tq < 4; ++tq) {
+                auto put = [&](bf16* dst, const bf16 (&x)[CPL][C], int tq) {
                     const int o = tq * QS + CPL * lane * 4;
                     if constexpr (CPL == 2) {
-                        *reinterpret_cast<bf16x8*>(op.Kb + o) =
-                            bf16x8{kb[0][4 * tq], kb[0][4 * tq + 1], kb[0][4 * tq + 2], kb[0][4 * tq + 3],
-                                   kb[1][4 * tq], kb[1][4 * tq + 1], kb[1][4 * tq + 2], kb[1][4 * tq + 3]};
-                        *reinterpret_cast<bf16x8*>(op.Qb + o) =
-                            bf16x8{qb[0][4 * tq], qb[0][4 * tq + 1], qb[0][4 * tq + 2], qb[0][4 * tq + 3],
-                                   qb[1][4 * tq], qb[1][4 * tq + 1], qb[1][4 * tq + 2], qb[1][4 * tq + 3]};
+                        *reinterpret_cast<bf16x8*>(dst + o) =
+                            bf16x8{x[0][4 * tq], x[0][4 * tq + 1], x[0][4 * tq + 2], x[0][4 * tq + 3],
+                                   x[1][4 * tq], x[1][4 * tq + 1], x[1][4 * tq + 2], x[1][4 * tq + 3]};
                     } else {
-                        *reinterpret_cast<bf16x4*>(op.Kb + o) =
-                            bf16x4{kb[0][4 * tq], kb[0][4 * tq + 1], kb[0][4 * tq + 2], kb[0][4 * tq + 3]};
-                        *reinterpret_cast<bf16x4*>(op.Qb + o) =
-                            bf16x4{qb[0][4 * tq], qb[0][4 * tq + 1], qb[0][4 * tq + 2], qb[0][4 * tq + 3]};
+                        *reinterpret_cast<bf16x4*>(dst + o) =
+                            bf16x4{x[0][4 * tq], x[0][4 * tq + 1], x[0][4 * tq + 2], x[0][4 * tq + 3]};
+                    }
+                };
+#pragma unroll
+                for (int tq = 0; tq < 4; ++tq) {
+                    put(dKb, kb, tq);
+                    put(dQb, qb, tq);
+                    if constexpr (CF::X3) {
+                        put(dKl, kl, tq);
+                        put(dQl, ql, tq);
                     }
                 }
             };
@@ -1198,7 +1535,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
 template <typename CF>
 static hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream)
 {
-    using SM = Smem<CF>;
+    using SM = std::conditional_t<CF::X3, SmemX3<CF>, Smem<CF>>;
     auto kern = kdn_walk_fwd_kernel<CF>;
     const size_t smem = sizeof(SM);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1215,11 +1552,17 @@ static hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream)
 hipError_t launch_walk_fwd(const FwdArgs& a, bool iso, hipStream_t stream)
 {
     using namespace walk;
-    if (a.dk == 128)
-        return iso ? launch_cfg<Cfg<128, 2, 2, true>>(a, stream)
-                   : launch_cfg<Cfg<128, 2, 2, false>>(a, stream);
-    return iso ? launch_cfg<Cfg<64, 2, 2, true>>(a, stream)
-               : launch_cfg<Cfg<64, 2, 2, false>>(a, stream);
+    if (iso)
+        return a.dk == 128 ? launch_cfg<Cfg<128, 2, 2, true>>(a, stream)
+                           : launch_cfg<Cfg<64, 2, 2, true>>(a, stream);
+    if (a.split && a.o_f32)
+        return a.dk == 128 ? launch_cfg<Cfg<128, 2, 2, false, true, true>>(a, stream)
+                           : launch_cfg<Cfg<64, 2, 2, false, true, true>>(a, stream);
+    if (a.split)
+        return a.dk == 128 ? launch_cfg<Cfg<128, 2, 2, false, true>>(a, stream)
+                           : launch_cfg<Cfg<64, 2, 2, false, true>>(a, stream);
+    return a.dk == 128 ? launch_cfg<Cfg<128, 2, 2, false>>(a, stream)
+                       : launch_cfg<Cfg<64, 2, 2, false>>(a, stream);
 }
 
 }  // namespace kdn

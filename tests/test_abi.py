@@ -131,6 +131,43 @@ def test_fwd_validation(L, variant, bad, code, needle):
 
 
 @cpu_only
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+@pytest.mark.parametrize("bad,code,needle", [
+    (dict(io=0x100), -1, "bf16 io only"),            # KDN_MATH_BF16 with fp32 io
+    (dict(io=0x200), -1, "bf16 io only"),            # KDN_OUT_F32 with fp32 io
+    (dict(io=0x301), -2, "KDN_OUT_F32 comes with"),  # both flags
+    (dict(io=0x401), -1, "io_dtype"),                # an unknown flag
+])
+def test_fwd_precision_flag_validation(L, variant, bad, code, needle):
+    st = _fwd_call(L, variant, **bad)
+    assert st == code
+    assert needle in L.kdn_last_error_message().decode()
+
+
+@cpu_only
+def test_fwd_out_f32_is_diagonal_only(L):
+    assert _fwd_call(L, "iso", io=0x201) == -2
+    assert "Diagonal" in L.kdn_last_error_message().decode()
+
+
+@cpu_only
+def test_fwd_out_f32_widens_the_output_overlap_check(L):
+    # split over the sequence with its workspace: with fp32 o the workspace
+    # must clear the twice larger output
+    shape = dict(B=1, T=8192, H=2, dk=128, dv=128)
+    need = L.kdn_fwd_workspace_size(0, 1, 8192, 2, 128, 128, 0x201)
+    assert need == L.kdn_fwd_workspace_size(0, 1, 8192, 2, 128, 128, 1) > 0
+    far = 1 << 40
+    o = far + (1 << 32)
+    obytes_bf16 = 8192 * 2 * 128 * 2
+    kw = dict(shape, q=far, k=far, v=far, alpha=far, omega=far, r=far, o=o,
+              S_T=far + (2 << 32), var_T=far + (3 << 32), ws_bytes=need)
+    # just past where a bf16 o would end, inside the fp32 o
+    assert _fwd_call(L, "diag", io=0x201, ws=o + obytes_bf16, **kw) == -1
+    assert "workspace must not overlap o" in L.kdn_last_error_message().decode()
+
+
+@cpu_only
 @pytest.mark.parametrize("variant,offset", [("diag", 16), ("iso", 4)])
 def test_fwd_variance_partial_overlap(L, variant, offset):
     # exact aliasing of the initial and final variances is allowed, a partial
