@@ -4,9 +4,13 @@ Default workload: Diagonal KDN forward, bf16 q/k/v with fp32 gates and state,
 B=8, H=16, T=4096, d_k=d_v=128 (the mixer of a hidden-2048 / 16-head layer
 at a 4K context), synthetic seeded inputs resident in HBM before timing.
 One step = one forward call over the whole batch (gain scan, chunked memory
-update, readout, final state).  Prints ONE JSON line.
+update, readout, final state).  Prints ONE JSON line.  The Diagonal forward
+runs its chunk contractions as split-bf16 products (three bf16 products of
+hi / lo operand halves, fp32 accumulation), the higher-precision Diagonal the
+KDN reading notes' throughput figure used; --math bf16 times the
+single-product contractions instead.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--math split|bf16]
 
 Other modes (same JSON form, not the default): --workload 1 / 3 / 4 (the
 Isotropic, long-sequence and decode workloads), --preact (the forward from
@@ -14,7 +18,8 @@ bf16 gate pre-activations, kdn_fwd_preact) and --bwd (the backward pass,
 kdn_bwd, priced against its own algorithmic bytes).
 
 Roofline: achieved = algorithmic bytes per launch / mean launch time (HIP
-events on the launch stream).  Algorithmic bytes read every input once and
+events on the launch stream, one pair per launch: the median launch is
+reported beside the mean).  Algorithmic bytes read every input once and
 write every output once (per head-token: 3 d s_io + 2 d * 4 + 4 + d s_io for
 Diagonal; plus the final state and variances per head).  `traffic` (HBM bytes
 per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain-copy
@@ -34,6 +39,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_FLOPS = 2.5e15  # MI355X dense bf16 matrix peak, published
+LLC_BYTES = 256 * 2**20         # MI355X last-level (Infinity) cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # sources each measured kernel is built from (traffic figures go stale when they change)
 KERNEL_SOURCES = {
@@ -99,8 +106,8 @@ def fwd_kernel_name(io: str) -> str:
     return "kdn_walk_fwd_kernel" if io == "bf16" else "kdn_chunk_fwd_kernel"
 
 
-def traffic_key(kernel: str, workload: str, variant: str) -> str:
-    return "%s:%s:%s" % (kernel, workload, variant)
+def traffic_key(kernel: str, workload: str, variant: str, mode: str = "") -> str:
+    return "%s:%s:%s" % (kernel, workload, variant) + (":" + mode if mode else "")
 
 
 def traffic_for(kernel: str, key: str):
@@ -128,14 +135,27 @@ def copy_calibration(dev):
     print("[bench] copy calibration: 3 x 1 GiB device copies done", file=sys.stderr, flush=True)
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, variant):
-    """The fp64 oracle, untuned, on the same seeded inputs the GPU consumed.
-    The sample is the whole workload (every batch row, head and token) when
-    the oracle finishes it in about half a minute of CPU time, else the
-    leading batch rows that fit; reported in the GPU's unit (tokens/s)."""
+    """The fp64 oracle, untuned, on the same seeded inputs the GPU consumed,
+    timed on the host: all cores (OpenMP over the independent (batch, head)
+    problems) on the whole workload when it finishes in about half a minute
+    of CPU time, else on the leading batch rows that fit, and one thread on
+    one batch row.  Reported in the GPU's unit (tokens/s)."""
     import numpy as np
     import oracle
 
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     threads = max(1, min(oracle.max_threads(), w.B * w.H))
     fn = oracle.diag_fwd if variant == "diag" else oracle.iso_fwd
     names = ("q", "k", "v", "alpha", "omega", "r")
@@ -153,10 +173,59 @@ def cpu_baseline(w, inp, variant):
             break
         rows = max(1, int(n * 2))
     tokens = done_rows * w.T
+    # one thread on one batch row (H heads x T tokens)
+    sl = {k: np.ascontiguousarray(inp[k][:1]) for k in names}
+    t0 = time.perf_counter()
+    fn(*(sl[k] for k in names), nthreads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": tokens / dt_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d batch rows of the workload (%d heads x %d tokens each), fp64 C "
                       "token recurrence with OpenMP over heads, %.2f s wall"
-                      % (done_rows, w.B, w.H, w.T, dt_total)}
+                      % (done_rows, w.B, w.H, w.T, dt_total),
+            "nproc": nproc, "cpu_model": _cpu_model(),
+            "single_thread": {"value": w.T / dt1, "unit": "tokens/s",
+                              "sample": "1 batch row (%d heads x %d tokens), 1 thread, %.2f s wall"
+                                        % (w.H, w.T, dt1)}}
+
+
+def time_launches(launch, stream, steps, warmup):
+    """W untimed launches, then exactly K timed ones with an event pair
+    around each (recorded on the launch stream) and around all of them;
+    synchronised on both sides.  Returns (total ms, per-launch ms, wall s)."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(steps):
+        launch()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]), per, wall
+
+
+def input_sets(alg_bytes: int) -> int:
+    """Input sets a forward is timed over: one when its bytes exceed the
+    last-level cache, else enough (at most 4) that the sets together span
+    three times the cache."""
+    if alg_bytes >= LLC_BYTES:
+        return 1
+    return int(min(4, -(-3 * LLC_BYTES // alg_bytes)))
+
+
+def mfma_flops_fwd(B, T, H, dk, dv, split: bool) -> int:
+    """bf16 matrix-core flops of one forward as the walk kernel contracts it
+    (16-token chunks): per head-token 2 dk dv for each of Kb S, Qb S and the
+    state update, 2 C dk for L' and Aqk, 2 C dv for T (V - Kb S) and Aqk D';
+    the split-product path does each three times."""
+    C = 16
+    per_ht = 6 * dk * dv + 4 * C * (dk + dv)
+    return B * T * H * per_ht * (3 if split else 1)
 
 
 def main():
@@ -175,6 +244,9 @@ def main():
                     help="time the backward pass (kdn_bwd) on the workload instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--math", choices=("split", "bf16"), default="split",
+                    help="Diagonal bf16 contractions: split-bf16 products (default) or single "
+                         "bf16 products")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -201,53 +273,57 @@ def main():
     variant = args.variant or w.variant
     if args.preact:
         return bench_preact(args, w, variant)
-    print("[bench] generating %s (%s)" % (w.name, variant), file=sys.stderr, flush=True)
-    inp = inputs.make_fwd_inputs(w, variant)
     io_dt = torch.bfloat16 if w.io == "bf16" else torch.float32
-    d = {}
-    for n in ("q", "k", "v", "alpha", "omega", "r"):
-        t = torch.from_numpy(inp[n])
-        d[n] = (t.to(io_dt) if n in ("q", "k", "v") else t).to(dev)
     B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
-    o = torch.empty((B, T, H, dv), dtype=io_dt, device=dev)
-    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    var_T = torch.empty((B, H, dk) if variant == "diag" else (B, H), dtype=torch.float32,
-                        device=dev)
-    fn = api.kdn_diag_fwd if variant == "diag" else api.kdn_iso_fwd
-    vkw = "p_T" if variant == "diag" else "b_T"
-
-    def step():
-        fn(d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], o=o, S_T=S_T, **{vkw: var_T})
-
-    if args.bwd:
-        return bench_bwd(args, w, variant, d, io_dt)
-
-    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
-    tokens = B * T
-    value = tokens * args.steps / (ms_total / 1e3)
     s_io = 2 if w.io == "bf16" else 4
     alg = alg_bytes_fwd(variant, B, T, H, dk, dv, s_io)
+    # a workload whose inputs would stay in the 256 MB last-level cache is timed
+    # over several input sets in turn (each its own seed), so every launch
+    # reads its inputs from HBM
+    nsets = 1 if args.bwd else input_sets(alg)
+
+    def upload(inp):
+        d = {}
+        for n in ("q", "k", "v", "alpha", "omega", "r"):
+            t = torch.from_numpy(inp[n])
+            d[n] = (t.to(io_dt) if n in ("q", "k", "v") else t).to(dev)
+        return d
+
+    print("[bench] generating %s (%s), %d input set(s)" % (w.name, variant, nsets),
+          file=sys.stderr, flush=True)
+    inp = inputs.make_fwd_inputs(w, variant)
+    sets = [upload(inp)]
+    for i in range(1, nsets):
+        sets.append(upload(inputs.make_fwd_inputs(inputs.workload(args.workload,
+                                                                  seed=w.seed + 1000 * i),
+                                                  variant)))
+    if args.bwd:
+        return bench_bwd(args, w, variant, sets[0], io_dt)
+    split = variant == "diag" and w.io == "bf16" and args.math == "split"
+    math = None if (split or w.io != "bf16") else "bf16"
+    # arguments checked and marshalled once; each step is one library call
+    launchers = [api.fwd_launcher(variant, d["q"], d["k"], d["v"], d["alpha"], d["omega"],
+                                  d["r"], math=math)[1] for d in sets]
+    turn = [0]
+
+    def step():
+        launchers[turn[0] % nsets]()
+        turn[0] += 1
+
+    stream = torch.cuda.current_stream(dev)
+    print("[bench] warmup %d, %d timed steps" % (args.warmup, args.steps), file=sys.stderr,
+          flush=True)
+    ms_total, per, wall = time_launches(step, stream, args.steps, args.warmup)
+    ms_step = ms_total / args.steps
+    ms_med = sorted(per)[len(per) // 2]
+    tokens = B * T
+    value = tokens * args.steps / (ms_total / 1e3)
     achieved = alg / (ms_step / 1e3) / 1e9
     kname = fwd_kernel_name(w.io)
-    traffic = traffic_for(kname, traffic_key(kname, w.name, variant))
-    print("[bench] %d steps: %.3f ms/step (events), wall %.3f s" % (args.steps, ms_step, wall),
-          file=sys.stderr, flush=True)
+    mode = "split" if split else ("bf16" if w.io == "bf16" else "f32")
+    traffic = traffic_for(kname, traffic_key(kname, w.name, variant, mode))
+    print("[bench] %d steps: %.4f ms/step mean, %.4f median (events), wall %.3f s"
+          % (args.steps, ms_step, ms_med, wall), file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         copy_calibration(dev)
@@ -257,6 +333,7 @@ def main():
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, inp, variant)
 
+    flops = mfma_flops_fwd(B, T, H, dk, dv, split) if w.io == "bf16" else None
     line = {
         "metric": "KDN mixer fwd tokens/sec at T=%d (1 GPU); %% of MFMA/HBM roofline" % T,
         "value": value,
@@ -265,17 +342,25 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_median": ms_med,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.io == "bf16" else "f32",
+        "dtype": {"split": "bf16x3", "bf16": "bf16", "f32": "f32"}[mode],
         "data": "synthetic",
         "config": {"workload": w.name, "variant": variant, "B": B, "T": T, "H": H, "dk": dk,
                    "dv": dv, "chunk": 16, "io": w.io, "gates": "f32", "state": "f32",
-                   "global_batch": B, "seq_len": T, "parallelism": "single-gpu"},
+                   "contractions": {"split": "split-bf16: hi.hi + lo.hi + hi.lo, fp32 accumulate",
+                                    "bf16": "bf16 products, fp32 accumulate",
+                                    "f32": "fp32 products"}[mode],
+                   "global_batch": B, "seq_len": T, "parallelism": "single-gpu",
+                   "input_sets": nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "alg_bytes_per_launch": alg, "kernel": kname},
+                     "alg_bytes_per_launch": alg, "kernel": kname,
+                     "mfma_bf16_flops_per_launch": flops,
+                     "mfma_bf16_frac": (flops / (ms_step / 1e3) / MFMA_BF16_PEAK_FLOPS
+                                        if flops else None)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -10,7 +10,10 @@ from .api import (  # noqa: F401
     KDN_DIAG,
     KDN_F32,
     KDN_ISO,
+    KDN_MATH_BF16,
+    KDN_OUT_F32,
     KdnError,
+    fwd_launcher,
     kdn_diag_fwd,
     kdn_bwd,
     kdn_bwd_preact,
@@ -36,5 +39,6 @@ __all__ = [
     "kdn_gain_scan",
     "kdn_fwd_workspace_size",
     "kdn_version",
+    "fwd_launcher",
     "KdnError",
 ]

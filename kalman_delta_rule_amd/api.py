@@ -65,7 +65,10 @@ def _head_vec(t, name, H, dev):
 
 def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
          ext: bool = False, mu_h=None, c0_h=None, beta_eff=None, sequence_parallel=True,
-         math=None, o_dtype=None):
+         math=None, o_dtype=None, prepare=False):
+    """Checks the tensors, allocates what is missing, and launches the
+    forward (or, with ``prepare``, returns (outputs, launch) where launch()
+    repeats the call on the same tensors and stream without re-checking)."""
     L = _lib.lib()
     if q.dim() != 4:
         raise ValueError("q must be [B,T,H,dk]")
@@ -111,19 +114,26 @@ def _fwd(variant: int, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T,
         _head_vec(c0_h, "c0_h", H, dev)
         if beta_eff is not None:
             _need(beta_eff, "beta_eff", (B, T, H), torch.float32, dev)
-        with torch.cuda.device(dev):
-            st = L.kdn_fwd_ex(variant, B, T, H, dk, dv, io, mu, _ptr(mu_h), _ptr(q), _ptr(k),
-                              _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r), _ptr(S0), _ptr(var0),
-                              _ptr(c0_h), _ptr(o), _ptr(S_T), _ptr(var_T), _ptr(beta_eff),
-                              _ptr(ws), ws_bytes, _stream(dev))
-        _lib.check(st)
-        return o, S_T, var_T
-    fn = L.kdn_diag_fwd if variant == KDN_DIAG else L.kdn_iso_fwd
-    with torch.cuda.device(dev):
-        st = fn(B, T, H, dk, dv, io, mu, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega),
+        fn = L.kdn_fwd_ex
+        args = (variant, B, T, H, dk, dv, io, mu, _ptr(mu_h), _ptr(q), _ptr(k), _ptr(v),
+                _ptr(alpha), _ptr(omega), _ptr(r), _ptr(S0), _ptr(var0), _ptr(c0_h), _ptr(o),
+                _ptr(S_T), _ptr(var_T), _ptr(beta_eff), _ptr(ws), ws_bytes)
+    else:
+        fn = L.kdn_diag_fwd if variant == KDN_DIAG else L.kdn_iso_fwd
+        args = (B, T, H, dk, dv, io, mu, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega),
                 _ptr(r), _ptr(S0), _ptr(var0), _ptr(o), _ptr(S_T), _ptr(var_T), _ptr(ws),
-                ws_bytes, _stream(dev))
-    _lib.check(st)
+                ws_bytes)
+    stream = _stream(dev)
+    keep = (q, k, v, alpha, omega, r, S0, var0, o, S_T, var_T, mu_h, c0_h, beta_eff, ws)
+
+    def launch():
+        _lib.check(fn(*args, stream))
+        return keep  # the tensors stay alive as long as the launcher does
+
+    if prepare:
+        return (o, S_T, var_T), launch
+    with torch.cuda.device(dev):
+        launch()
     return o, S_T, var_T
 
 
@@ -135,6 +145,17 @@ def kdn_diag_fwd(q, k, v, alpha, omega, r, S0=None, p0=None, mu=None, o=None, S_
     then writes o in fp32."""
     return _fwd(KDN_DIAG, q, k, v, alpha, omega, r, S0, p0, mu, o, S_T, p_T, math=math,
                 o_dtype=o_dtype)
+
+
+def fwd_launcher(variant: str, q, k, v, alpha, omega, r, S0=None, var0=None, mu=None,
+                 o=None, S_T=None, var_T=None, math=None, o_dtype=None):
+    """Check the arguments once and return ((o, S_T, var_T), launch): each
+    launch() runs the same forward (kdn_diag_fwd / kdn_iso_fwd) on the same
+    tensors and on the stream that was current here, without re-checking or
+    allocating (a workspace the shape needs is allocated once, now)."""
+    var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
+    return _fwd(var, q, k, v, alpha, omega, r, S0, var0, mu, o, S_T, var_T, math=math,
+                o_dtype=o_dtype, prepare=True)
 
 
 def kdn_iso_fwd(q, k, v, alpha, omega, r, S0=None, b0=None, mu=None, o=None, S_T=None,

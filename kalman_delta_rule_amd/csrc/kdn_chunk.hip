@@ -846,8 +846,7 @@ static hipError_t launch_one(const FwdArgs& a, hipStream_t stream)
     using SM = ChunkSmem<IO, DK, DVT, ISO>;
     auto kern = kdn_chunk_fwd_kernel<IO, DK, DVT, ISO>;
     const size_t smem = sizeof(SM);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipError_t e = set_lds_limit_once(kern, smem);
     if (e != hipSuccess)
         return e;
     const int nblk = a.B * a.H * (a.dv / DVT);

@@ -5,7 +5,30 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <atomic>
+#include <stdint.h>
+
 namespace kdn {
+
+// Raise a kernel's dynamic-LDS limit to `bytes`, once per device and kernel
+// (the attribute holds for the process); later launches skip the call.
+template <typename Kernel>
+hipError_t set_lds_limit_once(Kernel kern, size_t bytes)
+{
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit))
+        return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess && bit)
+        done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 struct FwdArgs {
     const void* q;

@@ -1538,8 +1538,7 @@ static hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream)
     using SM = std::conditional_t<CF::X3, SmemX3<CF>, Smem<CF>>;
     auto kern = kdn_walk_fwd_kernel<CF>;
     const size_t smem = sizeof(SM);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipError_t e = set_lds_limit_once(kern, smem);
     if (e != hipSuccess)
         return e;
     const int nblk = a.B * a.H * (a.dv / CF::DVT);

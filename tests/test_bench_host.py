@@ -87,3 +87,23 @@ def test_bytes_preact_per_head_token():
     assert bench.alg_bytes_preact("diag", 1, 10, 1, d, d, 2) == 10 * 1538 + d * d * 4 + d * 4
     # Isotropic: q, k, v, o, a per channel, w and rho per token: (5 d + 2) x 2 B
     assert bench.alg_bytes_preact("iso", 1, 10, 1, d, d, 2) == 10 * 1284 + d * d * 4 + 4
+
+
+def test_mfma_flops_per_head_token():
+    # d = 128, 16-token chunks: 6 d^2 for the three state contractions and
+    # 4 C (dk + dv) for L', Aqk, T (V - Kb S) and Aqk D'; the split-product
+    # path does each three times
+    assert bench.mfma_flops_fwd(1, 1, 1, 128, 128, False) == 6 * 128 * 128 + 4 * 16 * 256
+    assert bench.mfma_flops_fwd(8, 4096, 16, 128, 128, True) == 3 * 524288 * 114688
+
+
+def test_input_sets_rotate_cache_sized_workloads():
+    # the Isotropic B4 H16 T2048 forward (207 MB) fits the 256 MB cache: four
+    # sets; the B8 H16 T4096 Diagonal one (1.08 GB) does not: one
+    assert bench.input_sets(bench.alg_bytes_fwd("iso", 4, 2048, 16, 128, 128, 2)) == 4
+    assert bench.input_sets(bench.alg_bytes_fwd("diag", 8, 4096, 16, 128, 128, 2)) == 1
+
+
+def test_traffic_key_names_the_contraction_mode():
+    assert bench.traffic_key("k", "w", "diag", "split") == "k:w:diag:split"
+    assert bench.traffic_key("k", "w", "diag") == "k:w:diag"
