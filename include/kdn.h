@@ -337,6 +337,26 @@ kdn_status kdn_gain_scan(int variant, int B, int T, int H, int dk, int io_dtype,
                          float* kappa, float* var_T,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The gain scan above without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and validation
+ * as kdn_gain_scan; its scratch (the chunk summaries and carries) is a static
+ * device array of kdn_gain_scan_static_max_bytes() bytes (32 MiB) that every
+ * GPU the library runs on holds from the library's load until the process
+ * ends.  A shape whose kdn_gain_workspace_size exceeds that returns
+ * KDN_ERR_WORKSPACE and launches nothing.  The call allocates nothing.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents (nothing in it needs clearing: each call writes what it reads), so
+ * calls that overlap on one GPU (concurrent streams, or threads without
+ * ordering) race: order them on one stream.
+ */
+size_t kdn_gain_scan_static_max_bytes(void);
+kdn_status kdn_gain_scan_static(int variant, int B, int T, int H, int dk, int io_dtype, float mu,
+                                const void* k, const float* alpha, const float* omega,
+                                const float* r, const float* var0, float* kappa, float* var_T,
+                                void* stream);
+
 const char* kdn_status_string(int status);
 const char* kdn_last_error_message(void);
 

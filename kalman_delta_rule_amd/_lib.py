@@ -78,6 +78,10 @@ def lib():
     L.kdn_gain_workspace_size.argtypes = [i] * 5
     L.kdn_gain_scan.restype = i
     L.kdn_gain_scan.argtypes = [i] * 6 + [f] + [vp] + [fp] * 4 + [fp, fp, vp, sz, vp]
+    L.kdn_gain_scan_static_max_bytes.restype = sz
+    L.kdn_gain_scan_static_max_bytes.argtypes = []
+    L.kdn_gain_scan_static.restype = i
+    L.kdn_gain_scan_static.argtypes = [i] * 6 + [f] + [vp] + [fp] * 4 + [fp, fp, vp]
     L.kdn_status_string.restype = ctypes.c_char_p
     L.kdn_status_string.argtypes = [i]
     L.kdn_last_error_message.restype = ctypes.c_char_p
@@ -92,7 +96,8 @@ EXPORTED = ("kdn_fwd_workspace_size", "kdn_diag_fwd", "kdn_iso_fwd", "kdn_step",
             "kdn_fwd_ex", "kdn_step_ex", "kdn_dense_fwd", "kdn_bwd_workspace_size", "kdn_bwd",
             "kdn_fwd_preact_workspace_size", "kdn_fwd_preact",
             "kdn_bwd_preact_workspace_size", "kdn_bwd_preact",
-            "kdn_gain_workspace_size", "kdn_gain_scan", "kdn_status_string",
+            "kdn_gain_workspace_size", "kdn_gain_scan", "kdn_gain_scan_static_max_bytes",
+            "kdn_gain_scan_static", "kdn_status_string",
             "kdn_last_error_message", "kdn_version")
 
 

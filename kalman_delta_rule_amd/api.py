@@ -440,6 +440,37 @@ def kdn_gain_scan(variant: str, k, alpha, omega, r, var0=None, mu=None,
     return kappa, var_T
 
 
+def kdn_gain_scan_static(variant: str, k, alpha, omega, r, var0=None, mu=None, kappa=None,
+                         var_T=None):
+    """Gain scan through the allocation-free entry point: its scratch is the
+    library's static device array, so the call itself allocates nothing (give
+    kappa and var_T to allocate nothing here either; kappa may be None to skip
+    the gain).  Returns (kappa, var_T)."""
+    L = _lib.lib()
+    var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
+    B, T, H, dk = k.shape
+    dev = k.device
+    io = _io_code(k)
+    _need(k, "k", (B, T, H, dk), k.dtype, dev)
+    _need(alpha, "alpha", (B, T, H, dk), torch.float32, dev)
+    _need(omega, "omega", (B, T, H, dk) if var == KDN_DIAG else (B, T, H), torch.float32, dev)
+    _need(r, "r", (B, T, H), torch.float32, dev)
+    vshape = (B, H, dk) if var == KDN_DIAG else (B, H)
+    if var0 is not None:
+        _need(var0, "var0", vshape, torch.float32, dev)
+    if kappa is not None:
+        _need(kappa, "kappa", (B, T, H, dk), torch.float32, dev)
+    if var_T is None:
+        var_T = torch.empty(vshape, dtype=torch.float32, device=dev)
+    _need(var_T, "var_T", vshape, torch.float32, dev)
+    mu = float(dk if mu is None else mu)
+    with torch.cuda.device(dev):
+        st = L.kdn_gain_scan_static(var, B, T, H, dk, io, mu, _ptr(k), _ptr(alpha), _ptr(omega),
+                                    _ptr(r), _ptr(var0), _ptr(kappa), _ptr(var_T), _stream(dev))
+    _lib.check(st)
+    return kappa, var_T
+
+
 def kdn_fwd_workspace_size(variant: str, B, T, H, dk, dv, io_dtype: torch.dtype) -> int:
     var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
     io = KDN_BF16 if io_dtype == torch.bfloat16 else KDN_F32

@@ -703,15 +703,18 @@ size_t kdn_gain_workspace_size(int variant, int B, int T, int H, int dk)
     return kdn::gain_workspace_floats(variant == KDN_ISO, B, T, H, dk) * sizeof(float);
 }
 
-kdn_status kdn_gain_scan(int variant, int B, int T, int H, int dk, int io_dtype, float mu,
-                         const void* k, const float* alpha, const float* omega, const float* r,
-                         const float* var0, float* kappa, float* var_T, void* workspace,
-                         size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the gain scan's two entry points.
+kdn_status gain_check(int variant, int B, int T, int H, int dk, int io_dtype, float mu,
+                      const void* k, const float* alpha, const float* omega, const float* r,
+                      const float* var0, const float* var_T)
 {
     if (variant != KDN_DIAG && variant != KDN_ISO)
         return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
                     variant);
-    const bool iso = variant == KDN_ISO;
     if (io_dtype != KDN_F32 && io_dtype != KDN_BF16)
         return fail(KDN_ERR_INVALID_ARG, "io_dtype must be KDN_F32 (0) or KDN_BF16 (1), got %d",
                     io_dtype);
@@ -733,21 +736,72 @@ kdn_status kdn_gain_scan(int variant, int B, int T, int H, int dk, int io_dtype,
     KDN_ALIGNED(alpha, "alpha");
     if (var0 && var0 == var_T)
         return fail(KDN_ERR_INVALID_ARG, "var_T must not alias var0");
-    const size_t need = kdn_gain_workspace_size(variant, B, T, H, dk);
-    if (workspace_bytes < need || !workspace)
-        return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
-                    workspace_bytes);
-    if (!aligned16(workspace))
-        return fail(KDN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return KDN_OK;
+}
+
+kdn_status gain_launch(int variant, int B, int T, int H, int dk, int io_dtype, float mu,
+                       const void* k, const float* alpha, const float* omega, const float* r,
+                       const float* var0, float* kappa, float* var_T, float* ws, void* stream)
+{
+    const bool iso = variant == KDN_ISO;
     const size_t nchunks = (size_t)(T + 63) / 64;
     const size_t width = iso ? 1 : (size_t)dk;
-    float* ws = static_cast<float*>(workspace);
     kdn::GainArgs a{k,     alpha, omega, r, var0, kappa, var_T, ws,
                     ws + (size_t)B * H * 4 * width * nchunks, B, T, H, dk, mu};
     hipError_t e = kdn::launch_gain_scan(a, iso, io_dtype, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kdn_status kdn_gain_scan(int variant, int B, int T, int H, int dk, int io_dtype, float mu,
+                         const void* k, const float* alpha, const float* omega, const float* r,
+                         const float* var0, float* kappa, float* var_T, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    kdn_status st = gain_check(variant, B, T, H, dk, io_dtype, mu, k, alpha, omega, r, var0, var_T);
+    if (st != KDN_OK)
+        return st;
+    const size_t need = kdn_gain_workspace_size(variant, B, T, H, dk);
+    if (workspace_bytes < need || !workspace)
+        return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                    workspace_bytes);
+    if (!aligned16(workspace))
+        return fail(KDN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return gain_launch(variant, B, T, H, dk, io_dtype, mu, k, alpha, omega, r, var0, kappa, var_T,
+                       static_cast<float*>(workspace), stream);
+}
+
+size_t kdn_gain_scan_static_max_bytes(void)
+{
+    return kdn::gain_static_scratch_floats() * sizeof(float);
+}
+
+kdn_status kdn_gain_scan_static(int variant, int B, int T, int H, int dk, int io_dtype, float mu,
+                                const void* k, const float* alpha, const float* omega,
+                                const float* r, const float* var0, float* kappa, float* var_T,
+                                void* stream)
+{
+    kdn_status st = gain_check(variant, B, T, H, dk, io_dtype, mu, k, alpha, omega, r, var0, var_T);
+    if (st != KDN_OK)
+        return st;
+    const size_t need = kdn_gain_workspace_size(variant, B, T, H, dk);
+    const size_t have = kdn_gain_scan_static_max_bytes();
+    if (need > have)
+        return fail(KDN_ERR_WORKSPACE,
+                    "this shape needs %zu bytes of scratch; the static scratch of "
+                    "kdn_gain_scan_static holds %zu (use kdn_gain_scan with a workspace)",
+                    need, have);
+    float* ws = nullptr;
+    hipError_t e = kdn::gain_static_scratch(&ws);
+    if (e != hipSuccess)
+        return fail(KDN_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+    return gain_launch(variant, B, T, H, dk, io_dtype, mu, k, alpha, omega, r, var0, kappa, var_T,
+                       ws, stream);
 }
 
 const char* kdn_status_string(int status)

@@ -24,6 +24,8 @@
 // Every combine rescales by 1/max|entry| (entries are non-negative), which
 // keeps the ratios and avoids fp32 overflow.
 #include "kdn_common.h"
+
+#include <mutex>
 #include "kdn_internal.h"
 #include "kdn_ops.h"
 
@@ -287,6 +289,38 @@ __global__ __launch_bounds__(256) void gain_replay_iso(GainArgs a, int nchunks)
         const size_t idx = (((size_t)b * a.T + t0 + t) * a.H + h) * DK + i;
         a.kappa[idx] = sbeta[t] * to_f32(kg[idx]);
     }
+}
+
+// Scratch of the allocation-free gain scan (kdn_gain_scan_static): one copy
+// per device, resident from the module's load until the process ends.  Host
+// code reaches it only through the device address hipGetSymbolAddress returns
+// (looked up once per device); the array's own name is a host-side stand-in.
+constexpr size_t kGainStaticFloats = (size_t)8 << 20;  // 32 MiB
+static __device__ __align__(256) float scratch[kGainStaticFloats];
+
+size_t gain_static_scratch_floats() { return kGainStaticFloats; }
+
+hipError_t gain_static_scratch(float** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = static_cast<float*>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 size_t gain_workspace_floats(bool iso, int B, int T, int H, int dk)

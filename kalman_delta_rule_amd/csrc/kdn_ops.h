@@ -100,6 +100,10 @@ struct PrologueArgs {
 
 hipError_t launch_dense_fwd(const DenseArgs& a, int io_dtype, hipStream_t stream);
 size_t gain_workspace_floats(bool iso, int B, int T, int H, int dk);
+// the allocation-free gain scan's static scratch: its size in floats, and its
+// device address on the current device
+size_t gain_static_scratch_floats();
+hipError_t gain_static_scratch(float** ptr);
 hipError_t launch_gain_scan(const GainArgs& a, bool iso, int io_dtype, hipStream_t stream);
 size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv);
 void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws);

@@ -419,3 +419,22 @@ def test_bwd_preact_validation(L):
     assert (L.kdn_bwd_preact_workspace_size(0, 1, 40, 2, 128, 64)
             == L.kdn_fwd_preact_workspace_size(0, 1, 40, 2, 128)
             + L.kdn_bwd_workspace_size(0, 1, 40, 2, 128, 64))
+
+
+@cpu_only
+def test_gain_scan_static_validation(L):
+    # the allocation-free gain scan checks like kdn_gain_scan, then rejects a
+    # shape whose scratch exceeds its static array, before any launch
+    assert L.kdn_gain_scan_static_max_bytes() == 32 << 20
+    ok = dict(variant=0, B=1, T=65536, H=16, dk=128, io=1, mu=128.0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.kdn_gain_scan_static(a["variant"], a["B"], a["T"], a["H"], a["dk"], a["io"],
+                                      a["mu"], P, P, P, P, None, None, P + 4096, None)
+    assert call() == -3
+    assert "static scratch" in L.kdn_last_error_message().decode()
+    assert call(variant=2) == -1
+    assert call(dk=96) == -2
+    assert call(io=2) == -1
+    assert call(mu=-1.0) == -1
