@@ -463,6 +463,8 @@ def bench_bwd(args, w, variant, d, io_dt):
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
+    if args.copy_calibration:
+        copy_calibration(dev)
     s_io = 2 if w.io == "bf16" else 4
     alg = alg_bytes_bwd(variant, B, T, H, dk, dv, s_io)
     achieved = alg / (ms_step / 1e3) / 1e9

@@ -559,6 +559,9 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     ktl[n] = *reinterpret_cast<const bf16x4*>(kt.Ktl + kt_lane + 64 * n);
                     gcf[n] = *reinterpret_cast<const f32x4*>(&kt.gC[16 * n + 4 * g4]);
                 }
+                // Delta' = T (V - Y) and O^T += Delta'^T Aqk^T: hi.hi + lo.hi as
+                // one K = 32 product, hi.lo as a K = 32 product with a zero
+                // upper half, so every accumulation chain stays on one opcode
                 bf16x4 dh[NB], dl[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
@@ -581,10 +584,13 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                             *reinterpret_cast<bf16x4*>(orow + 16 * nb) = cvt4(accO[nb]);
                     }
                 }
+                // the next chunk's Kb and Qb, once the front, Delta' and O no
+                // longer hold registers; they land behind the state update
                 reads_issued();
                 if (c + 1 < nchunks)
                     fetchx(c + 1, m);
                 reads_issued();
+                // S <- diag(G_C) (S + Ktp^T Delta')
 #pragma unroll
                 for (int n = 0; n < DK / 16; ++n) {
 #pragma unroll
