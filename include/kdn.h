@@ -141,9 +141,13 @@ size_t kdn_fwd_workspace_size(int variant, int B, int T, int H, int dk, int dv,
  *     When it is used it must not overlap any other argument
  *     (KDN_ERR_INVALID_ARG), and o serves as scratch before its final values.
  *   stream: a hipStream_t (NULL = the null stream)
- * S_T may alias S0 and p_T may alias p0 exactly (the state is read before
- * it is overwritten); a partial overlap of either pair, or o aliasing q, k
- * or v, is rejected with KDN_ERR_INVALID_ARG.
+ * S_T may alias S0 exactly (each workgroup reads its own columns of the
+ * state before it overwrites them).  p_T may alias p0 exactly only when
+ * dv <= 64 for bf16 io (dv <= 32 for fp32), i.e. one workgroup per head: with
+ * more, every value-tile workgroup reads the initial variances and nothing
+ * orders that read before the first tile's final write, so the call returns
+ * KDN_ERR_INVALID_ARG (use separate p0 / p_T buffers).  A partial overlap of
+ * either pair, or o aliasing q, k or v, is rejected with KDN_ERR_INVALID_ARG.
  */
 kdn_status kdn_diag_fwd(int B, int T, int H, int dk, int dv, int io_dtype, float mu,
                         const void* q, const void* k, const void* v,

@@ -171,9 +171,20 @@ kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io_dtype,
         KDN_ALIGNED(var0, "p0");
         KDN_ALIGNED(var_T, "p_T");
     }
+    // Every value-tile workgroup of a head (dv / 64 of them for bf16 io,
+    // dv / 32 for fp32) reads the head's initial variances when it starts,
+    // and only the first tile writes the final ones when it ends; nothing
+    // orders a later tile's start after that write.  So the variances may
+    // alias in place only where one workgroup walks each head.
+    const int vtile = io == KDN_BF16 ? 64 : 32;
+    if (var0 && var0 == var_T && dv > vtile)
+        return fail(KDN_ERR_INVALID_ARG,
+                    "%s may alias %s only when dv <= %d (one workgroup per head); give a "
+                    "separate %s buffer", iso ? "b_T" : "p_T", iso ? "b0" : "p0", vtile,
+                    iso ? "b_T" : "p_T");
     if (var0 && var0 != var_T) {
-        // each variance is read once at the start and written once at the end
-        // by the same lane, so only exact aliasing is safe
+        // each variance is read at the start and written at the end, so a
+        // partial overlap is never safe
         const size_t vb = (size_t)B * H * (iso ? 1 : dk) * sizeof(float);
         const char *a0 = (const char*)var0, *a1 = (const char*)var_T;
         if (a0 < a1 + vb && a1 < a0 + vb)

@@ -168,6 +168,17 @@ def test_fwd_out_f32_widens_the_output_overlap_check(L):
 
 
 @cpu_only
+@pytest.mark.parametrize("variant", ["diag", "iso"])
+def test_fwd_variance_in_place_needs_one_tile(L, variant):
+    # exact aliasing of the variances is refused when several value-tile
+    # workgroups read them (dv > 64 for bf16, dv > 32 for fp32)
+    assert _fwd_call(L, variant, dv=128, var0=P + 16384) == -1
+    assert "only when dv <= 64" in L.kdn_last_error_message().decode()
+    assert _fwd_call(L, variant, io=0, dv=64, var0=P + 16384) == -1
+    assert "only when dv <= 32" in L.kdn_last_error_message().decode()
+
+
+@cpu_only
 @pytest.mark.parametrize("variant,offset", [("diag", 16), ("iso", 4)])
 def test_fwd_variance_partial_overlap(L, variant, offset):
     # exact aliasing of the initial and final variances is allowed, a partial

@@ -146,8 +146,11 @@ def test_empty_sequence_passes_state_through(variant):
 
 
 @pytest.mark.parametrize("variant", ["diag", "iso"])
-def test_state_output_may_alias_initial_state(ora, variant):
-    B, T, H, dk, dv = 1, 90, 2, 128, 128
+@pytest.mark.parametrize("dv", [64, 128])
+def test_state_output_may_alias_initial_state(ora, variant, dv):
+    # S_T may alias S0 at any width; the variances in place only with one
+    # workgroup per head (dv = 64 for bf16), else separate buffers
+    B, T, H, dk = 1, 90, 2, 128
     w = inputs.Workload("t", variant, "bf16", B, H, T, dk, dv, seed=9)
     inp = inputs.make_fwd_inputs(w)
     rng = np.random.default_rng(10)
@@ -156,15 +159,21 @@ def test_state_output_may_alias_initial_state(ora, variant):
     d = to_dev(inp, "bf16")
     Sdev = torch.from_numpy(S0).cuda()
     vdev = torch.from_numpy(var0).cuda()
+    vout = vdev if dv == 64 else torch.empty_like(vdev)
     fn = api.kdn_diag_fwd if variant == "diag" else api.kdn_iso_fwd
-    kw = {"p0": vdev, "p_T": vdev} if variant == "diag" else {"b0": vdev, "b_T": vdev}
+    kw = {"p0": vdev, "p_T": vout} if variant == "diag" else {"b0": vdev, "b_T": vout}
     o, S, var = fn(d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], S0=Sdev, S_T=Sdev,
                    **kw)
     torch.cuda.synchronize()
-    assert S.data_ptr() == Sdev.data_ptr() and var.data_ptr() == vdev.data_ptr()
+    assert S.data_ptr() == Sdev.data_ptr() and var.data_ptr() == vout.data_ptr()
     res = oracle_heads(ora, variant, inp, [(0, 0), (0, 1)], S0=S0, var0=var0)
     err = compare_heads(res, host(o), host(S), host(var), [(0, 0), (0, 1)])
     assert max(err.values()) <= TOL["bf16"], err
+    if dv == 128:
+        # in-place variances are refused, before any launch
+        with pytest.raises(api.KdnError, match="only when dv <= 64"):
+            fn(d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], S0=Sdev, S_T=Sdev,
+               **({"p0": vdev, "p_T": vdev} if variant == "diag" else {"b0": vdev, "b_T": vdev}))
 
 
 @pytest.mark.parametrize("variant", ["diag", "iso"])

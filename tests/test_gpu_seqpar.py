@@ -114,7 +114,8 @@ def test_seqpar_per_head_options_match_serial(variant):
 
 
 def test_seqpar_in_place_state():
-    # S_T may equal S0 and var_T var0 on the split path too
+    # S_T may equal S0 on the split path too (the variances in place only
+    # with one workgroup per head, which d = 128 is not)
     B, T, H, d = 1, 8192, 2, 128
     w = inputs.Workload("t", "diag", "bf16", B, H, T, d, d, seed=960)
     dd = to_dev(inputs.make_fwd_inputs(w), "bf16")
@@ -124,7 +125,7 @@ def test_seqpar_in_place_state():
     o, S, p, _ = _run("diag", dd, True, S0=S0.clone(), var0=p0.clone())
     S_in, p_in = S0.clone(), p0.clone()
     o2, S2, p2, _ = api.kdn_fwd_ex("diag", dd["q"], dd["k"], dd["v"], dd["alpha"], dd["omega"],
-                                   dd["r"], S0=S_in, var0=p_in, S_T=S_in, var_T=p_in)
+                                   dd["r"], S0=S_in, var0=p_in, S_T=S_in)
     torch.cuda.synchronize()
     assert S2.data_ptr() == S_in.data_ptr()
     assert torch.equal(o, o2) and torch.equal(S, S2) and torch.equal(p, p2)
