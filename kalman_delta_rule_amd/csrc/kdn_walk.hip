@@ -551,14 +551,12 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                         sl[nb] = nl[nb];
                     }
                 }
-                bf16x4 kth[DK / 16], ktl[DK / 16];
-                f32x4 gcf[DK / 16];
-#pragma unroll
-                for (int n = 0; n < DK / 16; ++n) {
-                    kth[n] = *reinterpret_cast<const bf16x4*>(kt.Ktp + kt_lane + 64 * n);
-                    ktl[n] = *reinterpret_cast<const bf16x4*>(kt.Ktl + kt_lane + 64 * n);
-                    gcf[n] = *reinterpret_cast<const f32x4*>(&kt.gC[16 * n + 4 * g4]);
-                }
+                // the next chunk's Kb and Qb, into the registers the front has
+                // just consumed
+                reads_issued();
+                if (c + 1 < nchunks)
+                    fetchx(c + 1, m);
+                reads_issued();
                 // Delta' = T (V - Y) and O^T += Delta'^T Aqk^T: hi.hi + lo.hi as
                 // one K = 32 product, hi.lo as a K = 32 product with a zero
                 // upper half, so every accumulation chain stays on one opcode
@@ -584,20 +582,30 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                             *reinterpret_cast<bf16x4*>(orow + 16 * nb) = cvt4(accO[nb]);
                     }
                 }
-                // the next chunk's Kb and Qb, once the front, Delta' and O no
-                // longer hold registers; they land behind the state update
-                reads_issued();
-                if (c + 1 < nchunks)
-                    fetchx(c + 1, m);
-                reads_issued();
-                // S <- diag(G_C) (S + Ktp^T Delta')
+                // S <- diag(G_C) (S + Ktp^T Delta'), Ktp and G_C of 16 rows at a
+                // time read two blocks ahead of their products
+                constexpr int PD = 2;
+                bf16x4 kth[PD + 1], ktl[PD + 1];
+                f32x4 gcf[PD + 1];
+                auto ldk = [&](int n, int s) {
+                    kth[s] = *reinterpret_cast<const bf16x4*>(kt.Ktp + kt_lane + 64 * n);
+                    ktl[s] = *reinterpret_cast<const bf16x4*>(kt.Ktl + kt_lane + 64 * n);
+                    gcf[s] = *reinterpret_cast<const f32x4*>(&kt.gC[16 * n + 4 * g4]);
+                };
+#pragma unroll
+                for (int n = 0; n < PD; ++n)
+                    ldk(n, n);
 #pragma unroll
                 for (int n = 0; n < DK / 16; ++n) {
+                    if (n + PD < DK / 16)
+                        ldk(n + PD, (n + PD) % (PD + 1));
+                    reads_issued();
+                    const int s = n % (PD + 1);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        mfma32(Sacc[nb][n], cat8(kth[n], ktl[n]), cat8(dh[nb], dh[nb]));
-                        mfma32(Sacc[nb][n], cat8(kth[n], z4), cat8(dl[nb], z4));
-                        Sacc[nb][n] *= gcf[n];
+                        mfma32(Sacc[nb][n], cat8(kth[s], ktl[s]), cat8(dh[nb], dh[nb]));
+                        mfma32(Sacc[nb][n], cat8(kth[s], z4), cat8(dl[nb], z4));
+                        Sacc[nb][n] *= gcf[s];
                     }
                 }
             };
