@@ -14,8 +14,9 @@ single-product contractions instead.
 
 Other modes (same JSON form, not the default): --workload 1 / 3 / 4 (the
 Isotropic, long-sequence and decode workloads), --preact (the forward from
-bf16 gate pre-activations, kdn_fwd_preact) and --bwd (the backward pass,
-kdn_bwd, priced against its own algorithmic bytes).
+bf16 gate pre-activations, kdn_fwd_preact), --bwd (the backward pass,
+kdn_bwd, priced against its own algorithmic bytes) and --gain (the gain scan
+alone, kdn_gain_scan with kappa).
 
 Roofline: achieved = algorithmic bytes per launch / mean launch time (HIP
 events on the launch stream, one pair per launch: the median launch is
@@ -242,6 +243,8 @@ def main():
                     help="time the forward from gate pre-activations (kdn_fwd_preact) instead")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (kdn_bwd) on the workload instead")
+    ap.add_argument("--gain", action="store_true",
+                    help="time the gain scan alone (kdn_gain_scan, with kappa) on the workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--math", choices=("split", "bf16"), default="split",
@@ -280,7 +283,7 @@ def main():
     # a workload whose inputs would stay in the 256 MB last-level cache is timed
     # over several input sets in turn (each its own seed), so every launch
     # reads its inputs from HBM
-    nsets = 1 if args.bwd else input_sets(alg)
+    nsets = 1 if (args.bwd or args.gain) else input_sets(alg)
 
     def upload(inp):
         d = {}
@@ -299,6 +302,8 @@ def main():
                                                   variant)))
     if args.bwd:
         return bench_bwd(args, w, variant, sets[0], io_dt)
+    if args.gain:
+        return bench_gain(args, w, variant, sets[0])
     split = variant == "diag" and w.io == "bf16" and args.math == "split"
     math = None if (split or w.io != "bf16") else "bf16"
     # arguments checked and marshalled once; each step is one library call
@@ -425,6 +430,75 @@ def bench_preact(args, w, variant):
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "alg_bytes_per_launch": alg,
                      "kernel": "kdn_gate_prologue (x3) + %s" % fwd_kernel_name(w.io)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def alg_bytes_gain(variant: str, B, T, H, dk, s_io: int) -> int:
+    """Gain scan with kappa: k, alpha, omega (per channel for Diagonal, per
+    head for Isotropic) and r read once, kappa (fp32) written once, plus the
+    final variances."""
+    om = dk * 4 if variant == "diag" else 4
+    per_ht = dk * s_io + dk * 4 + om + 4 + dk * 4
+    return B * T * H * per_ht + B * H * (dk if variant == "diag" else 1) * 4
+
+
+def bench_gain(args, w, variant, d):
+    """The gain scan on its own (kdn_gain_scan with kappa), outputs and
+    workspace allocated once outside the timed region."""
+    import torch
+    from kalman_delta_rule_amd import _lib
+
+    L = _lib.lib()
+    dev = d["k"].device
+    B, T, H, dk = w.B, w.T, w.H, w.dk
+    var = {"diag": 0, "iso": 1}[variant]
+    io = 1 if w.io == "bf16" else 0
+    kappa = torch.empty((B, T, H, dk), dtype=torch.float32, device=dev)
+    var_T = torch.empty((B, H, dk) if variant == "diag" else (B, H), dtype=torch.float32,
+                        device=dev)
+    ws_bytes = int(L.kdn_gain_workspace_size(var, B, T, H, dk))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    h = stream.cuda_stream
+    ptrs = [d[n].data_ptr() for n in ("k", "alpha", "omega", "r")]
+
+    def step():
+        _lib.check(L.kdn_gain_scan(var, B, T, H, dk, io, float(dk), *ptrs, None,
+                                   kappa.data_ptr(), var_T.data_ptr(), ws.data_ptr(), ws.numel(),
+                                   h))
+
+    print("[bench] gain scan warmup %d, %d timed steps" % (args.warmup, args.steps),
+          file=sys.stderr, flush=True)
+    ms_total, per, wall = time_launches(step, stream, args.steps, args.warmup)
+    ms_step = ms_total / args.steps
+    ms_med = sorted(per)[len(per) // 2]
+    if args.copy_calibration:
+        copy_calibration(dev)
+    s_io = 2 if w.io == "bf16" else 4
+    alg = alg_bytes_gain(variant, B, T, H, dk, s_io)
+    achieved = alg / (ms_step / 1e3) / 1e9
+    line = {
+        "metric": "KDN gain scan tokens/sec at T=%d (1 GPU)" % T,
+        "value": B * T / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "ms_per_step_median": ms_med,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "variant": variant, "B": B, "T": T, "H": H, "dk": dk,
+                   "io": w.io, "pass": "gain scan with kappa"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": alg,
+                     "kernel": "gain_summary + gain_carry + gain_replay"},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

@@ -112,15 +112,17 @@ enum { KDN_OUT_F32 = 0x200 };
  * kdn_fwd_ex) run this shape fastest.  The workspace is optional: a call given
  * less (or NULL) runs the serial walk, with the same results up to rounding.
  * Nonzero only for bf16 io with dk == dv when the serial walk would fill at
- * most a quarter of the chip (B*H*dv/64 workgroups) and T splits into 4 or 8
+ * most a quarter of the chip (B*H*dv/64 workgroups against 256 compute
+ * units, MI355X's count, taken as fixed so that the size is a pure function
+ * of the shape, whatever the device) and T splits into 4 or 8
  * segments of at least 1024 tokens, each a multiple of 64: the state
  * recurrence is affine in the state over any span of tokens (method part §2
  * and §6 of the KDN reading notes), so the segments run as independent walks
  * whose linear and affine parts a short per-head combine chains, and the
  * segment-entry variances come from the gain scan (method part §6).  The size
- * is then the gain scan's carries, two segment-variance planes, four
- * [B*S,H,dk,dv] fp32 state planes and a bf16 copy of v's shape.  Returns 0 for
- * invalid shapes too; the forward call reports those. */
+ * is then the gain scan's carries, two segment-variance planes and four
+ * [B*S,H,dk,dv] fp32 state planes.  Returns 0 for invalid shapes too; the
+ * forward call reports those. */
 size_t kdn_fwd_workspace_size(int variant, int B, int T, int H, int dk, int dv,
                               int io_dtype);
 
@@ -139,7 +141,7 @@ size_t kdn_fwd_workspace_size(int variant, int B, int T, int H, int dk, int dv,
  *     with kdn_fwd_workspace_size(...) bytes or more, shapes with few heads
  *     and long sequences run split over the sequence (NULL: serial walk).
  *     When it is used it must not overlap any other argument
- *     (KDN_ERR_INVALID_ARG), and o serves as scratch before its final values.
+ *     (KDN_ERR_INVALID_ARG).
  *   stream: a hipStream_t (NULL = the null stream)
  * S_T may alias S0 exactly (each workgroup reads its own columns of the
  * state before it overwrites them).  p_T may alias p0 exactly only when

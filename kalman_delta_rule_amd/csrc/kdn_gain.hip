@@ -15,12 +15,14 @@
 //           64 maps serially in one lane (lanes = channels, coalesced loads);
 //           Isotropic scans the chunk's 64 maps across the lanes of one
 //           wavefront with DPP.
-//   pass 2  carry: one wavefront per (batch, head, channel) scans the chunk
-//           summaries across its lanes with DPP (64 chunks per step, with a
-//           running prefix between steps), giving every chunk's entry
-//           variance and the final variance.
+//   pass 2  carry: one lane per (batch, head, channel) applies the chunk
+//           summaries to the variance in chunk order (a 2x2 map of a scalar
+//           per chunk, loads running eight chunks ahead), giving every
+//           chunk's entry variance and the final variance.
 //   pass 3  (only when kappa is requested) replay each chunk from its entry
 //           variance: p^_t, z_t = sum_i p^_t,i k_t,i^2, kappa = p^ k/(r + z).
+// Summaries are stored chunk-major, [B H][chunk][4][width], so that pass 1
+// writes whole rows and pass 2 reads them with lanes on adjacent channels.
 // Every combine rescales by 1/max|entry| (entries are non-negative), which
 // keeps the ratios and avoids fp32 overflow.
 #include "kdn_common.h"
@@ -119,12 +121,11 @@ __global__ __launch_bounds__(DK) void gain_summary_diag(GainArgs a, int nchunks)
         }
     }
     P = mob_normalize(P);
-    const size_t base = (size_t)bh * 4 * DK * nchunks + (size_t)i * nchunks + c;
-    const size_t es = (size_t)DK * nchunks;
-    a.summ[base] = P.m00;
-    a.summ[base + es] = P.m01;
-    a.summ[base + 2 * es] = P.m10;
-    a.summ[base + 3 * es] = P.m11;
+    float* out = a.summ + ((size_t)bh * nchunks + c) * 4 * DK + i;
+    out[0] = P.m00;
+    out[DK] = P.m01;
+    out[2 * DK] = P.m10;
+    out[3 * DK] = P.m11;
 }
 
 template <typename IO, int DK>
@@ -147,57 +148,64 @@ __global__ __launch_bounds__(256) void gain_summary_iso(GainArgs a, int nchunks)
         }
         const Mob incl = mob_wave_scan_inclusive(m);
         if (t == 63) {
-            const size_t es = (size_t)nchunks;
-            const size_t base = (size_t)bh * 4 * nchunks + c;
-            a.summ[base] = incl.m00;
-            a.summ[base + es] = incl.m01;
-            a.summ[base + 2 * es] = incl.m10;
-            a.summ[base + 3 * es] = incl.m11;
+            float* out = a.summ + ((size_t)bh * nchunks + c) * 4;
+            out[0] = incl.m00;
+            out[1] = incl.m01;
+            out[2] = incl.m10;
+            out[3] = incl.m11;
         }
     }
 }
 
 // ---------------------------------------------------------------- pass 2
-// One wavefront per (bh, channel): DPP scan over chunk summaries.
+// One lane per (bh, channel), 64 channels per wavefront: p entering chunk c,
+// then p <- (m00 p + m01) / (m10 p + m11) with chunk c's summary.
 __global__ __launch_bounds__(64) void gain_carry(GainArgs a, int width, int nchunks)
 {
-    const int row = blockIdx.x;  // bh * width + i
-    const int bh = row / width, i = row % width;
-    const int lane = threadIdx.x;
-    const float p0 = a.var0 ? a.var0[(size_t)bh * width + i] : (a.c0 ? a.c0[bh % a.H] : 1.f);
-    const size_t es = (size_t)width * nchunks;
-    const float* s = a.summ + (size_t)bh * 4 * es + (size_t)i * nchunks;
-    Mob run = mob_identity();  // product of all earlier 64-chunk groups
-    for (int cb = 0; cb < nchunks; cb += 64) {
-        const int c = cb + lane;
-        Mob m = mob_identity();
-        if (c < nchunks)
-            m = Mob{s[c], s[c + es], s[c + 2 * es], s[c + 3 * es]};
-        const Mob incl = mob_wave_scan_inclusive(m);
-        const Mob excl = mob_compose(mob_wave_shift_right(incl), run);
-        if (c < nchunks)
-            a.carry[((size_t)bh * nchunks + c) * width + i] = mob_apply(excl, p0);
-        const Mob tot = Mob{__shfl(incl.m00, 63), __shfl(incl.m01, 63), __shfl(incl.m10, 63),
-                            __shfl(incl.m11, 63)};
-        run = mob_compose(tot, run);
+    const int groups = (width + 63) / 64;
+    const int bh = blockIdx.x / groups, i = (blockIdx.x % groups) * 64 + threadIdx.x;
+    if (i >= width)
+        return;
+    float p = a.var0 ? a.var0[(size_t)bh * width + i] : (a.c0 ? a.c0[bh % a.H] : 1.f);
+    const float* s = a.summ + (size_t)bh * nchunks * 4 * width + i;
+    float* out = a.carry + (size_t)bh * nchunks * width + i;
+    constexpr int PF = 8;
+    for (int c0 = 0; c0 < nchunks; c0 += PF) {
+        float m[PF][4];
+#pragma unroll
+        for (int e = 0; e < PF; ++e) {
+            const float* sc = s + (size_t)min(c0 + e, nchunks - 1) * 4 * width;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                m[e][j] = sc[j * width];
+        }
+#pragma unroll
+        for (int e = 0; e < PF; ++e) {
+            if (c0 + e < nchunks) {
+                out[(size_t)(c0 + e) * width] = p;
+                p = mob_apply(Mob{m[e][0], m[e][1], m[e][2], m[e][3]}, p);
+            }
+        }
     }
-    if (lane == 0)
-        if (a.var_T)
-            a.var_T[(size_t)bh * width + i] = mob_apply(run, p0);
+    if (a.var_T)
+        a.var_T[(size_t)bh * width + i] = p;
 }
 
 // ---------------------------------------------------------------- pass 3
 template <typename IO, int DK>
 __global__ __launch_bounds__(DK) void gain_replay_diag(GainArgs a, int nchunks)
 {
-    __shared__ float s_ph[GC][DK + 1];
-    __shared__ float s_z[GC];
+    // s_w[t][i] = p^_t,i k_t,i^2 (rows padded to keep 16-byte reads aligned);
+    // z_t is the sum of row t, taken by DK / 64 lanes per token
+    constexpr int LDW = DK + 4, NH = DK / 64;
+    __shared__ __align__(16) float s_w[GC][LDW];
+    __shared__ float s_zp[NH][GC];
     const int bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
     const int b = bh / a.H, h = bh % a.H, i = threadIdx.x;
     const int t0 = c * GC, n_valid = min(GC, a.T - t0);
     const IO* kg = reinterpret_cast<const IO*>(a.k);
     float p = a.carry[((size_t)bh * nchunks + c) * DK + i];
-    float kk[GC];
+    float num[GC];  // p^_t k_t of this lane's channel (kappa's numerator)
     // eight tokens' gates are loaded before the chain (and the pprev stores,
     // which the compiler cannot move loads across) consume them
     constexpr int PF = 8;
@@ -225,30 +233,35 @@ __global__ __launch_bounds__(DK) void gain_replay_diag(GainArgs a, int nchunks)
                     a.pprev[tok * DK + i] = p;
                 p = ph * rcp(1.f + u * ph);
             }
-            kk[t] = kv;
-            s_ph[t][i] = ph;
+            num[t] = ph * kv;
+            s_w[t][i] = num[t] * kv;
         }
     }
     __syncthreads();
-    if (i < GC) {
+    {
+        // lane (part, t): channels 64 part .. 64 part + 63 of token t
+        const int t = i % GC, part = i / GC;
+        const float* row = &s_w[t][64 * part];
         float z = 0.f;
-        const int t = i;
-        const IO* krow = kg + (((size_t)b * a.T + t0 + t) * a.H + h) * DK;
-        if (t < n_valid)
-            for (int j = 0; j < DK; ++j) {
-                const float kv = to_f32(krow[j]);
-                z += s_ph[t][j] * kv * kv;
-            }
-        s_z[t] = z;
+#pragma unroll
+        for (int j = 0; j < 64; j += 4) {
+            const float4 w4 = *reinterpret_cast<const float4*>(row + j);
+            z += (w4.x + w4.y) + (w4.z + w4.w);
+        }
+        s_zp[part][t] = z;
     }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < GC; ++t) {
         if (t < n_valid) {
             const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
-            a.kappa[tok * DK + i] = s_ph[t][i] * kk[t] * rcp(a.r[tok] + s_z[t]);
+            float z = s_zp[0][t];
+#pragma unroll
+            for (int q = 1; q < NH; ++q)
+                z += s_zp[q][t];
+            a.kappa[tok * DK + i] = num[t] * rcp(a.r[tok] + z);
             if (a.dd && i == 0)
-                a.dd[tok] = a.r[tok] + s_z[t];
+                a.dd[tok] = a.r[tok] + z;
         }
     }
 }
@@ -345,7 +358,8 @@ static hipError_t launch_gain_t(const GainArgs& a0, bool iso, hipStream_t stream
             hipLaunchKernelGGL((gain_summary_diag<IO, DK>), dim3(BH * nchunks), dim3(DK), 0,
                                stream, a, nchunks);
     }
-    hipLaunchKernelGGL(gain_carry, dim3(BH * width), dim3(64), 0, stream, a, width, nchunks);
+    hipLaunchKernelGGL(gain_carry, dim3(BH * ((width + 63) / 64)), dim3(64), 0, stream, a, width,
+                       nchunks);
     if ((a.kappa || a.gsc) && nchunks > 0) {
         if (iso)
             hipLaunchKernelGGL((gain_replay_iso<IO, DK>), dim3(BH * nchunks), dim3(256), 0,

@@ -49,6 +49,9 @@ struct FwdArgs {
     float* beta;        // nullable [B,T,H]: effective write strength z / (r + z)
     bool split = false; // bf16 Diagonal walk: split-bf16 products (three per contraction)
     bool o_f32 = false; // with split: o is fp32 although q, k, v are bf16
+    // bf16 walk only: 0 = full forward; 1 = state only (S_T and var_T; q and o
+    // are not touched); 2 = state only with v taken as zero (v not touched)
+    int state_only = 0;
 };
 
 struct StepArgs {

@@ -32,7 +32,7 @@ struct GainArgs {
     const float* var0;  // nullable
     float* kappa;       // nullable
     float* var_T;
-    float* summ;        // workspace: chunk summaries [BH][4][width][nchunks]
+    float* summ;        // workspace: chunk summaries [BH][nchunks][4][width]
     float* carry;       // workspace: chunk-entry variances [BH][nchunks][width]
     int B, T, H, dk;
     float mu;

@@ -10,15 +10,18 @@
 // segments, a [B, T, H] tensor read as [B*S, T/S, H] makes the segments
 // independent problems for the walk kernel:
 //   1. gain scan: the variance entering every 64-token chunk;
-//   2. walk from a zero state: N of every segment;
-//   3. walk with v = 0 from S_in = I: M of every segment (d_k = d_v).  (A walk
-//      from I on the real v gives M + N, but recovering M by subtracting N
-//      loses M's precision where N dominates, as without decay.)
+//   2. state-only walk from a zero state: N of every segment (no q read, no
+//      o written);
+//   3. state-only walk with v = 0 (not read) from S_in = I: M of every segment
+//      (d_k = d_v).  (A walk from I on the real v gives M + N, but recovering
+//      M by subtracting N loses M's precision where N dominates, as without
+//      decay.)
 //   4. combine per head: S_in(s+1) = M(s) S_in(s) + N(s), from the caller's S0;
-//   5. walk from S_in(s): the outputs o (and beta_eff).
-// Three walks over S times as many workgroups.  The final state is the
-// combine's last S_out, the final variance the gain scan's.  All three walks
-// start each segment from the same variance, so they apply the same gains.
+//   5. full walk from S_in(s): the outputs o (and beta_eff).
+// Three walks over S times as many workgroups, two of them reading only the
+// keys and gates (and v for N).  The final state is the combine's last S_out,
+// the final variance the gain scan's.  All three walks start each segment
+// from the same variance, so they apply the same gains.
 #include "kdn_common.h"
 #include "kdn_internal.h"
 #include "kdn_ops.h"
@@ -51,15 +54,7 @@ size_t seqpar_workspace_floats(bool iso, int B, int T, int H, int dk, int dv, in
     size_t n = r64(gain_workspace_floats(iso, B, T, H, dk));
     n += 2 * r64(bs * H * width);                    // segment-entry variances, scratch
     n += 4 * r64(st);                                // N, M, S_in, identity
-    n += r64(((size_t)B * T * H * dv * 2 + 3) / 4);  // v = 0 (bf16)
     return n;
-}
-
-__global__ __launch_bounds__(256) void sp_zero16_kernel(uint4* p, size_t n16)
-{
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n16)
-        p[i] = uint4{0u, 0u, 0u, 0u};
 }
 
 __global__ __launch_bounds__(256) void sp_identity_kernel(float* I, size_t n, int D)
@@ -159,9 +154,6 @@ hipError_t launch_seqpar_fwd(const FwdArgs& a, bool iso, int S, float* ws, hipSt
     float* Sin = p;
     p += r64(st);
     float* Ib = p;
-    p += r64(st);
-    void* vzero = p;
-    const size_t vbytes = (size_t)B * T * H * DV * 2;
 
     // 1. the variance entering every chunk (and the final variance)
     GainArgs g{a.k, a.alpha, a.omega, a.r, a.var0, nullptr, a.var_T, gscan,
@@ -175,8 +167,6 @@ hipError_t launch_seqpar_fwd(const FwdArgs& a, bool iso, int S, float* ws, hipSt
     hipLaunchKernelGGL(sp_gather_var_kernel, dim3((unsigned)((npin + 255) / 256)), dim3(256), 0,
                        stream, (const float*)(gscan + (size_t)B * H * 4 * width * nchunks), pin, B,
                        H, S, (int)width, nchunks, seg_chunks);
-    hipLaunchKernelGGL(sp_zero16_kernel, dim3((unsigned)((vbytes / 16 + 255) / 256)), dim3(256),
-                       0, stream, reinterpret_cast<uint4*>(vzero), vbytes / 16);
     hipLaunchKernelGGL(sp_identity_kernel, dim3((unsigned)((st + 255) / 256)), dim3(256), 0, stream,
                        Ib, st, DK);
     if ((e = hipGetLastError()) != hipSuccess)
@@ -189,16 +179,18 @@ hipError_t launch_seqpar_fwd(const FwdArgs& a, bool iso, int S, float* ws, hipSt
     w.c0 = nullptr;
     w.var_T = vscr;
     w.beta = nullptr;
-    // 2. N: from a zero state (o is scratch here)
-    w.S0 = nullptr;
-    w.S_T = Nb;
-    if ((e = launch_walk_fwd(w, iso, stream)) != hipSuccess)
+    // 2. N: from a zero state, the state only
+    FwdArgs wn = w;
+    wn.S0 = nullptr;
+    wn.S_T = Nb;
+    wn.state_only = 1;
+    if ((e = launch_walk_fwd(wn, iso, stream)) != hipSuccess)
         return e;
-    // 3. M: v = 0 from the identity
+    // 3. M: v = 0 from the identity, the state only
     FwdArgs wm = w;
-    wm.v = vzero;
     wm.S0 = Ib;
     wm.S_T = Mb;
+    wm.state_only = 2;
     if ((e = launch_walk_fwd(wm, iso, stream)) != hipSuccess)
         return e;
     // 4. every segment's entry state and the final state

@@ -190,7 +190,8 @@ __device__ __forceinline__ void mfma32(f32x4& d, const bf16x8& a, const bf16x8& 
 // Wave roles of one workgroup.
 enum Role { R_MEM, R_BLD, R_ELT, R_FAC1, R_FAC2, R_LDR, R_ISO };
 
-template <int DK_, int NB_, int NMW_, bool ISO_, bool X3_ = false, bool OF32_ = false>
+template <int DK_, int NB_, int NMW_, bool ISO_, bool X3_ = false, bool OF32_ = false,
+          int SO_ = 0>
 struct Cfg {
     static constexpr int DK = DK_;
     static constexpr int NB = NB_;    // 16-column blocks per memory wave
@@ -206,6 +207,12 @@ struct Cfg {
     // contractions' precision instead of rounding to bf16
     static constexpr bool OF32 = OF32_;
     static_assert(!OF32_ || X3_, "fp32 output comes with split products");
+    // state-only walks (S_T and the variance, no outputs): SO_ = 1 reads no q
+    // and writes no o; SO_ = 2 also takes v = 0 without reading it, so that
+    // the innovation is -Kb S
+    static constexpr bool NOQ = SO_ > 0;
+    static constexpr bool NOV = SO_ == 2;
+    static_assert(SO_ >= 0 && SO_ <= 2 && !(SO_ && OF32_), "state-only mode");
     static constexpr int DVT = 16 * NB * NMW;
     // builder waves, one lane per key channel.  Diagonal splits the builder
     // work: these waves run the variance recurrence and form Ktp and G_C,
@@ -481,8 +488,10 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 for (int mm = 0; mm < DK / 32; ++mm) {
                     m.kh[mm] = quad_frag32(kq.Kb + tr_lane, mm);
                     m.kl[mm] = quad_frag32(kq.Kl + tr_lane, mm);
-                    m.qh[mm] = quad_frag32(kq.Qb + tr_lane, mm);
-                    m.ql[mm] = quad_frag32(kq.Ql + tr_lane, mm);
+                    if constexpr (!CF::NOQ) {
+                        m.qh[mm] = quad_frag32(kq.Qb + tr_lane, mm);
+                        m.ql[mm] = quad_frag32(kq.Ql + tr_lane, mm);
+                    }
                 }
             };
             const bf16x4 z4{};
@@ -494,14 +503,17 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 const bf16* V = sm.v[c % 3];
                 const bf16x4 th = *reinterpret_cast<const bf16x4*>(tri.T + c16 * C + 4 * g4);
                 const bf16x4 tl = *reinterpret_cast<const bf16x4*>(tri.Tl + c16 * C + 4 * g4);
-                const bf16x4 ah = *reinterpret_cast<const bf16x4*>(tri.Aqk + fr_lane);
-                const bf16x4 al = *reinterpret_cast<const bf16x4*>(tri.Aql + fr_lane);
+                bf16x4 ah{}, al{};
+                if constexpr (!CF::NOQ) {
+                    ah = *reinterpret_cast<const bf16x4*>(tri.Aqk + fr_lane);
+                    al = *reinterpret_cast<const bf16x4*>(tri.Aql + fr_lane);
+                }
                 bf16x4 vfr[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    vfr[nb] = ds_read_tr(V + v_lane[nb]);
+                    vfr[nb] = CF::NOV ? bf16x4{} : ds_read_tr(V + v_lane[nb]);
                 reads_issued();
-                if constexpr (!FULL) {
+                if constexpr (!FULL && !CF::NOV) {
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -539,11 +551,14 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         mfma32(accY[nb], m.kh[mm], sh[nb]);
-                        mfma32(accO[nb], sh[nb], m.qh[mm]);
+                        if constexpr (!CF::NOQ)
+                            mfma32(accO[nb], sh[nb], m.qh[mm]);
                         mfma32(accY[nb], m.kl[mm], sh[nb]);
-                        mfma32(accO[nb], sh[nb], m.ql[mm]);
+                        if constexpr (!CF::NOQ)
+                            mfma32(accO[nb], sh[nb], m.ql[mm]);
                         mfma32(accY[nb], m.kh[mm], sl[nb]);
-                        mfma32(accO[nb], sl[nb], m.qh[mm]);
+                        if constexpr (!CF::NOQ)
+                            mfma32(accO[nb], sl[nb], m.qh[mm]);
                     }
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
@@ -566,13 +581,15 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     f32x4 res;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        res[e] = static_cast<float>(vfr[nb][e]) - accY[nb][e];
+                        res[e] = CF::NOV ? -accY[nb][e] : static_cast<float>(vfr[nb][e]) - accY[nb][e];
                     bf16x4 rh, rl;
                     split4(res, rh, rl);
                     f32x4 accD = zero4();
                     mfma32(accD, cat8(th, tl), cat8(rh, rh));
                     mfma32(accD, cat8(th, z4), cat8(rl, z4));
                     split4(accD, dh[nb], dl[nb]);
+                    if constexpr (CF::NOQ)
+                        continue;
                     mfma32(accO[nb], cat8(dh[nb], dl[nb]), cat8(ah, ah));
                     mfma32(accO[nb], cat8(dh[nb], z4), cat8(al, z4));
                     if (FULL || c16 < nv) {
@@ -641,9 +658,11 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
 #pragma unroll
             for (int mm = 0; mm < DK / 32; ++mm) {
                 m.kf[mm] = quad_frag32(op.Kb + tr_lane, mm);
-                m.qf[mm] = quad_frag32(op.Qb + tr_lane, mm);
+                if constexpr (!CF::NOQ)
+                    m.qf[mm] = quad_frag32(op.Qb + tr_lane, mm);
             }
-            m.afr = *reinterpret_cast<const bf16x4*>(sm.tri[c % 3].Aqk + fr_lane);
+            if constexpr (!CF::NOQ)
+                m.afr = *reinterpret_cast<const bf16x4*>(sm.tri[c % 3].Aqk + fr_lane);
         };
 
         auto apply = [&](auto full_tag, int c, const MemOps& cur, MemOps& nxt) {
@@ -657,9 +676,9 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             bf16x4 vfr[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                vfr[nb] = ds_read_tr(V + v_lane[nb]);
+                vfr[nb] = CF::NOV ? bf16x4{} : ds_read_tr(V + v_lane[nb]);
             reads_issued();
-            if constexpr (!FULL) {
+            if constexpr (!FULL && !CF::NOV) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -680,7 +699,8 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 for (int nb = 0; nb < NB; ++nb) {
                     const bf16x8 s = cat8(cvt4(Sacc[nb][2 * m]), cvt4(Sacc[nb][2 * m + 1]));
                     mfma32(accY[nb], cur.kf[m], s);
-                    mfma32(accO[nb], s, cur.qf[m]);
+                    if constexpr (!CF::NOQ)
+                        mfma32(accO[nb], s, cur.qf[m]);
                 }
             }
             // Ktp and G_C for the state update at the end of the step, then the
@@ -698,7 +718,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             reads_issued();
             bf16x4 dfr[NB];
             // Aqk^T fragment as a K = 32 operand whose upper 16 k are zero
-            const bf16x8 afr32 = cat8(cur.afr, bf16x4{});
+            const bf16x8 afr32 = CF::NOQ ? bf16x8{} : cat8(cur.afr, bf16x4{});
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 // Delta' = T (V - Y): lane (g, c) holds V[4 g + e][c] as an
@@ -706,10 +726,12 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 f32x4 res;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    res[e] = static_cast<float>(vfr[nb][e]) - accY[nb][e];
+                    res[e] = CF::NOV ? -accY[nb][e] : static_cast<float>(vfr[nb][e]) - accY[nb][e];
                 f32x4 accD = zero4();
                 mfma16(accD, tfr, cvt4(res));
                 dfr[nb] = cvt4(accD);
+                if constexpr (CF::NOQ)
+                    continue;
                 // O^T += Delta'^T Aqk^T, issued as a zero-padded K = 32 product:
                 // the accumulator comes from 16x16x32 products, and on gfx950 a
                 // 16x16x16 product reading it as its accumulator needs more
@@ -807,7 +829,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             for (int t = 0; t < C; ++t) {
                 al[t] = raw.alpha[t * DK + i];
                 kr[t] = raw.k[t * DK + i];
-                if constexpr (!CF::SPLIT)
+                if constexpr (!CF::SPLIT && !CF::NOQ)
                     qr[t] = raw.q[t * DK + i];
             }
             // (Diagonal only: the Isotropic builders measured faster with the
@@ -820,7 +842,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 if constexpr (!ISO)
                     om[t] = omr[t];
                 kf[t] = static_cast<float>(kr[t]);
-                if constexpr (!CF::SPLIT)
+                if constexpr (!CF::SPLIT && !CF::NOQ)
                     qf[t] = static_cast<float>(qr[t]);
             }
             if constexpr (!FULL) {
@@ -831,7 +853,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     if constexpr (!ISO)
                         om[t] = ok ? om[t] : 0.f;
                     kf[t] = ok ? kf[t] : 0.f;
-                    if constexpr (!CF::SPLIT)
+                    if constexpr (!CF::SPLIT && !CF::NOQ)
                         qf[t] = ok ? qf[t] : 0.f;
                 }
             }
@@ -864,7 +886,8 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 for (int t = 0; t < C; ++t) {
                     G *= al[t];
                     kb[t] = kf[t] * G;
-                    qb[t] = qf[t] * G;
+                    if constexpr (!CF::NOQ)
+                        qb[t] = qf[t] * G;
                 }
                 // 1 / G_t = (prod_{s > t} alpha_s) / G_C
                 const float rgc = rcp(G);
@@ -896,9 +919,10 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                         *reinterpret_cast<bf16x4*>(op.Kb + o) =
                             bf16x4{static_cast<bf16>(kb[4 * tq]), static_cast<bf16>(kb[4 * tq + 1]),
                                    static_cast<bf16>(kb[4 * tq + 2]), static_cast<bf16>(kb[4 * tq + 3])};
-                        *reinterpret_cast<bf16x4*>(op.Qb + o) =
-                            bf16x4{static_cast<bf16>(qb[4 * tq]), static_cast<bf16>(qb[4 * tq + 1]),
-                                   static_cast<bf16>(qb[4 * tq + 2]), static_cast<bf16>(qb[4 * tq + 3])};
+                        if constexpr (!CF::NOQ)
+                            *reinterpret_cast<bf16x4*>(op.Qb + o) =
+                                bf16x4{static_cast<bf16>(qb[4 * tq]), static_cast<bf16>(qb[4 * tq + 1]),
+                                       static_cast<bf16>(qb[4 * tq + 2]), static_cast<bf16>(qb[4 * tq + 3])};
                     }
                     *reinterpret_cast<bf16x4*>(op.Ktp + o) =
                         bf16x4{static_cast<bf16>(kt[4 * tq]), static_cast<bf16>(kt[4 * tq + 1]),
@@ -983,12 +1007,14 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     for (int m = 0; m < DK / 32; ++m) {
                         kbf[m] = quad_frag32(op.Kb + tr_lane, m);
                         ktf[m] = quad_frag32(op.Ktp + tr_lane, m);
-                        qbf[m] = quad_frag32(op.Qb + tr_lane, m);
+                        if constexpr (!CF::NOQ)
+                            qbf[m] = quad_frag32(op.Qb + tr_lane, m);
                     }
 #pragma unroll
                     for (int m = 0; m < DK / 32; ++m) {
                         mfma32(accL, kbf[m], ktf[m]);
-                        mfma32(accQ, ktf[m], qbf[m]);
+                        if constexpr (!CF::NOQ)
+                            mfma32(accQ, ktf[m], qbf[m]);
                     }
                 }
                 // M^T[s][t] = L'[t][s]   (lane holds L'[4 g4 + r][c16]); the
@@ -1013,7 +1039,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                         a.beta[row_s(F * C + c16)] = z * dv;
                 }
                 // Aqk[t][u] = Aqk^T[u][t] for u <= t, else 0
-                if constexpr (!CF::X3) {
+                if constexpr (!CF::X3 && !CF::NOQ) {
                     f32x4 aq;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -1108,33 +1134,35 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     split4(g4 < 2 ? rt : t22t, hi, lo);
                     *reinterpret_cast<bf16x4*>(&tr.T[c16 * C + 4 * g4]) = hi;
                     *reinterpret_cast<bf16x4*>(&tr.Tl[c16 * C + 4 * g4]) = lo;
-                    // Aqk of the same chunk: Aqk^T[u][t] = Ktp_u . Qb_t in split
-                    // products, then Aqk[t][u] for u <= t (hi and lo)
-                    const auto& kq = sm.kq[F % 3];
-                    const auto& ks = sm.kt[F & 3];
-                    bf16x8 qbh[DK / 32], qbl[DK / 32], kth[DK / 32], ktl[DK / 32];
+                    if constexpr (!CF::NOQ) {
+                        // Aqk of the same chunk: Aqk^T[u][t] = Ktp_u . Qb_t in split
+                        // products, then Aqk[t][u] for u <= t (hi and lo)
+                        const auto& kq = sm.kq[F % 3];
+                        const auto& ks = sm.kt[F & 3];
+                        bf16x8 qbh[DK / 32], qbl[DK / 32], kth[DK / 32], ktl[DK / 32];
 #pragma unroll
-                    for (int m = 0; m < DK / 32; ++m) {
-                        qbh[m] = quad_frag32(kq.Qb + tr_lane, m);
-                        qbl[m] = quad_frag32(kq.Ql + tr_lane, m);
-                        kth[m] = quad_frag32(ks.Ktp + tr_lane, m);
-                        ktl[m] = quad_frag32(ks.Ktl + tr_lane, m);
+                        for (int m = 0; m < DK / 32; ++m) {
+                            qbh[m] = quad_frag32(kq.Qb + tr_lane, m);
+                            qbl[m] = quad_frag32(kq.Ql + tr_lane, m);
+                            kth[m] = quad_frag32(ks.Ktp + tr_lane, m);
+                            ktl[m] = quad_frag32(ks.Ktl + tr_lane, m);
+                        }
+                        f32x4 accQ = zero4(), accS = zero4();
+#pragma unroll
+                        for (int m = 0; m < DK / 32; ++m) {
+                            mfma32(accQ, kth[m], qbh[m]);
+                            mfma32(accS, ktl[m], qbh[m]);
+                            mfma32(accS, kth[m], qbl[m]);
+                        }
+                        accQ += accS;
+                        f32x4 aq;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            aq[r] = (4 * g4 + r <= c16) ? accQ[r] : 0.f;
+                        split4(aq, hi, lo);
+                        *reinterpret_cast<bf16x4*>(&tr.Aqk[c16 * LDF + 4 * g4]) = hi;
+                        *reinterpret_cast<bf16x4*>(&tr.Aql[c16 * LDF + 4 * g4]) = lo;
                     }
-                    f32x4 accQ = zero4(), accS = zero4();
-#pragma unroll
-                    for (int m = 0; m < DK / 32; ++m) {
-                        mfma32(accQ, kth[m], qbh[m]);
-                        mfma32(accS, ktl[m], qbh[m]);
-                        mfma32(accS, kth[m], qbl[m]);
-                    }
-                    accQ += accS;
-                    f32x4 aq;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        aq[r] = (4 * g4 + r <= c16) ? accQ[r] : 0.f;
-                    split4(aq, hi, lo);
-                    *reinterpret_cast<bf16x4*>(&tr.Aqk[c16 * LDF + 4 * g4]) = hi;
-                    *reinterpret_cast<bf16x4*>(&tr.Aql[c16 * LDF + 4 * g4]) = lo;
                 } else {
                     *reinterpret_cast<bf16x4*>(&tr.T[c16 * C + 4 * g4]) = cvt4(g4 < 2 ? rt : t22t);
                 }
@@ -1153,7 +1181,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         constexpr int RPI_V = 64 / LPR_V, NI_V = C / RPI_V;
         static_assert(LPR_A <= 64 && LPR_K <= 64 && LPR_V == 8 && NI_A >= 1 && NI_K >= 1,
                       "row / lane split");
-        constexpr int NSTG = NI_A + 2 * NI_K + 1 + (ISO ? 1 : 0);
+        constexpr int NSTG = NI_A + (CF::NOQ ? 1 : 2) * NI_K + 1 + (ISO ? 1 : 0);
         constexpr int NVI = NI_V;
         static_assert(NSTG + NVI <= 63, "outstanding copies within the vmcnt range");
         // LDS byte addresses of the copy targets (uniform)
@@ -1190,7 +1218,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             const int X = c + LR;
             const bool sv = X < nchunks;
             const int XV = c + 2;
-            const bool vv = XV >= 0 && XV < nchunks;
+            const bool vv = !CF::NOV && XV >= 0 && XV < nchunks;
             if (sv) {
                 const auto& st = sm.raw[X % NRAW];
                 const int tb = X * C;
@@ -1210,7 +1238,8 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     for (int j = 0; j < NI_K; ++j) {
                         const uint32_t o = FULL ? ok_[j] : off_k(j, lim);
                         dma16(kb, o, lk + j * RPI_K * DK * 2);
-                        dma16(qb, o, lq + j * RPI_K * DK * 2);
+                        if constexpr (!CF::NOQ)
+                            dma16(qb, o, lq + j * RPI_K * DK * 2);
                     }
                 };
                 if (lim == C - 1)
@@ -1283,7 +1312,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     for (int t = 0; t < C; ++t) {
                         a2[t] = *reinterpret_cast<const float2*>(&raw.alpha[t * DK + 2 * lane]);
                         kk[t] = *reinterpret_cast<const uint32_t*>(&raw.k[t * DK + 2 * lane]);
-                        qq[t] = *reinterpret_cast<const uint32_t*>(&raw.q[t * DK + 2 * lane]);
+                        qq[t] = CF::NOQ ? 0u : *reinterpret_cast<const uint32_t*>(&raw.q[t * DK + 2 * lane]);
                     }
 #pragma unroll
                     for (int t = 0; t < C; ++t) {
@@ -1299,7 +1328,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     for (int t = 0; t < C; ++t) {
                         al[0][t] = raw.alpha[t * DK + lane];
                         kf[0][t] = static_cast<float>(raw.k[t * DK + lane]);
-                        qf[0][t] = static_cast<float>(raw.q[t * DK + lane]);
+                        qf[0][t] = CF::NOQ ? 0.f : static_cast<float>(raw.q[t * DK + lane]);
                     }
                 }
                 bf16 kb[CPL][C], qb[CPL][C], kl[CPL][C], ql[CPL][C];
@@ -1356,10 +1385,12 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
 #pragma unroll
                 for (int tq = 0; tq < 4; ++tq) {
                     put(dKb, kb, tq);
-                    put(dQb, qb, tq);
+                    if constexpr (!CF::NOQ)
+                        put(dQb, qb, tq);
                     if constexpr (CF::X3) {
                         put(dKl, kl, tq);
-                        put(dQl, ql, tq);
+                        if constexpr (!CF::NOQ)
+                            put(dQl, ql, tq);
                     }
                 }
             };
@@ -1562,9 +1593,31 @@ static hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream)
 
 }  // namespace walk
 
+namespace walk {
+
+// state-only walks: SO = 1 (no q, no o) or 2 (also v = 0)
+template <int SO>
+static hipError_t launch_state_only(const FwdArgs& a, bool iso, hipStream_t stream)
+{
+    if (iso)
+        return a.dk == 128 ? launch_cfg<Cfg<128, 2, 2, true, false, false, SO>>(a, stream)
+                           : launch_cfg<Cfg<64, 2, 2, true, false, false, SO>>(a, stream);
+    if (a.split)
+        return a.dk == 128 ? launch_cfg<Cfg<128, 2, 2, false, true, false, SO>>(a, stream)
+                           : launch_cfg<Cfg<64, 2, 2, false, true, false, SO>>(a, stream);
+    return a.dk == 128 ? launch_cfg<Cfg<128, 2, 2, false, false, false, SO>>(a, stream)
+                       : launch_cfg<Cfg<64, 2, 2, false, false, false, SO>>(a, stream);
+}
+
+}  // namespace walk
+
 hipError_t launch_walk_fwd(const FwdArgs& a, bool iso, hipStream_t stream)
 {
     using namespace walk;
+    if (a.state_only == 1)
+        return launch_state_only<1>(a, iso, stream);
+    if (a.state_only == 2)
+        return launch_state_only<2>(a, iso, stream);
     if (iso)
         return a.dk == 128 ? launch_cfg<Cfg<128, 2, 2, true>>(a, stream)
                            : launch_cfg<Cfg<64, 2, 2, true>>(a, stream);

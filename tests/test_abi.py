@@ -59,11 +59,11 @@ def test_version_and_status_strings(L):
 def test_workspace_sizes(L):
     assert L.kdn_fwd_workspace_size(0, 8, 4096, 16, 128, 128, 1) == 0
     # few heads, long sequence: 8 segments; gain scan + 2 variance planes + 4 state
-    # planes + a zero copy of v
-    gain, pin, st, vz = 16 * 1024 * 128 * 5, 8 * 16 * 128, 8 * 16 * 128 * 128, 65536 * 16 * 64
-    assert L.kdn_fwd_workspace_size(0, 1, 65536, 16, 128, 128, 1) == (gain + 2 * pin + 4 * st + vz) * 4
+    # planes (the walk that forms M takes v = 0 without reading it: no zero copy)
+    gain, pin, st = 16 * 1024 * 128 * 5, 8 * 16 * 128, 8 * 16 * 128 * 128
+    assert L.kdn_fwd_workspace_size(0, 1, 65536, 16, 128, 128, 1) == (gain + 2 * pin + 4 * st) * 4
     gain, pin = 16 * 1024 * 5, 8 * 16
-    assert L.kdn_fwd_workspace_size(1, 1, 65536, 16, 128, 128, 1) == (gain + 2 * pin + 4 * st + vz) * 4
+    assert L.kdn_fwd_workspace_size(1, 1, 65536, 16, 128, 128, 1) == (gain + 2 * pin + 4 * st) * 4
     assert L.kdn_fwd_workspace_size(0, 1, 65536, 16, 128, 128, 0) == 0   # fp32 io: serial
     assert L.kdn_fwd_workspace_size(0, 1, 65536, 16, 128, 64, 1) == 0    # dk != dv
     assert L.kdn_fwd_workspace_size(0, 1, 2048, 16, 128, 128, 1) == 0    # segments too short

@@ -168,3 +168,23 @@ def test_short_workspace_runs_the_serial_walk():
     spl = _run("diag", dd, True)
     assert all(torch.equal(x, y) for x, y in zip(full, spl[:3]))
     assert not torch.equal(full[1], ser[1])   # the split path really ran
+
+
+@pytest.mark.timeout(600)
+def test_seqpar_config3_shape_iso_slow_decay(ora):
+    """Isotropic at the long-sequence shape (B1 H16 T65536 d128) with slow
+    decays, so that the segments' linear parts M carry the combine: whole
+    tensors against the oracle."""
+    w = inputs.workload(3)
+    inp = inputs.make_fwd_inputs(w, "iso")
+    inp["alpha"] = _alpha("slow", inp["alpha"].shape, np.random.default_rng(3201))
+    B, T, H, dk = inp["k"].shape
+    assert _split("iso", B, T, H, dk, inp["v"].shape[-1])
+    ref = ora.iso_fwd(*(inp[n] for n in ("q", "k", "v", "alpha", "omega", "r")))
+    d = to_dev(inp, "bf16")
+    o, S, b, _ = _run("iso", d, True)
+    from kdn_testutil import compare_whole
+    err, worst = compare_whole(ref, host(o), host(S), host(b))
+    print(w.name, "iso slow decay, split over the sequence: rel-L2", err, "worst (b,h)", worst,
+          flush=True)
+    assert max(err.values()) <= TOL["bf16"] and max(worst.values()) <= TOL["bf16"], (err, worst)
