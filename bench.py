@@ -48,6 +48,7 @@ KERNEL_SOURCES = {
     "kdn_walk_fwd_kernel": ["kdn_walk.hip", "kdn_common.h", "kdn_internal.h"],
     "kdn_chunk_fwd_kernel": ["kdn_chunk.hip", "kdn_common.h", "kdn_internal.h"],
     "kdn_step_kernel": ["kdn_step.hip", "kdn_common.h", "kdn_internal.h"],
+    "kdn_gain_scan": ["kdn_gain.hip", "kdn_common.h", "kdn_ops.h"],
 }
 
 
@@ -496,7 +497,9 @@ def bench_gain(args, w, variant, d):
         "config": {"workload": w.name, "variant": variant, "B": B, "T": T, "H": H, "dk": dk,
                    "io": w.io, "pass": "gain scan with kappa"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_for("kdn_gain_scan",
+                                            traffic_key("kdn_gain_scan", w.name, variant)),
                      "alg_bytes_per_launch": alg,
                      "kernel": "gain_summary + gain_carry + gain_replay"},
         "cpu_baseline": None,

@@ -47,11 +47,18 @@
  *   - Pointers to q, k, v, alpha, omega, o, S0/S_T/S and p0/p_T must be
  *     16-byte aligned.
  *   - Preconditions (documented, not checked per element): r > 0,
- *     0 < alpha <= 1, omega >= 0, p0/b0 > 0, mu >= 0, all finite, and within
- *     every 16-token chunk the product of alpha over the chunk stays above
- *     1e-30 in every channel (the chunked memory rescales keys by the
- *     cumulative decay from the chunk start).  Outside them results are
- *     unspecified (NaN propagates; nothing faults).
+ *     0 <= alpha <= 1, omega >= 0, p0/b0 > 0, mu >= 0, all finite.  Outside
+ *     them results are unspecified (NaN propagates; nothing faults).
+ *   - Strong decay in the chunked forwards (every call here but kdn_step):
+ *     the chunk products pair the cumulative decay G_t from a 16-token
+ *     chunk's start with its reciprocal.  Where a channel's chunk decays by
+ *     more than 2^100 the kernels measure G from a power-of-two reference
+ *     inside the chunk (exact up to rounding) down to a chunk product of
+ *     2^-224 (about 4e-68).  Below that, fp32 cannot span the chunk: every
+ *     alpha of that channel and chunk under 2^-14 (zero included) is taken
+ *     as 2^-14 in the memory decay (the variance recurrence keeps the true
+ *     alpha), which leaves at most 2^-14 of the previous state row per such
+ *     token where the method would leave alpha of it.
  *   - Validation is synchronous: on any invalid argument the call returns a
  *     negative status and launches nothing.  Launch failures return
  *     KDN_ERR_HIP.  Kernel faults surface at the caller's stream
@@ -256,7 +263,9 @@ kdn_status kdn_dense_fwd(int B, int T, int H, int dk, int dv, int io_dtype, cons
  * An elementwise pre-pass writes the fp32 gates into the workspace
  * (kdn_fwd_preact_workspace_size bytes, 16-byte aligned, disjoint from every
  * argument), then the forward of kdn_fwd_ex runs on them.  Validation
- * happens before anything is launched.
+ * happens before anything is launched.  Every finite pre-activation is
+ * accepted: a very negative a gives a small or zero alpha (sigmoid saturates
+ * to 0 below about -88), which the strong-decay rule above covers.
  */
 size_t kdn_fwd_preact_workspace_size(int variant, int B, int T, int H, int dk);
 kdn_status kdn_fwd_preact(int variant, int B, int T, int H, int dk, int dv, int io_dtype,

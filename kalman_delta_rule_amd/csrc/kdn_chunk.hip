@@ -179,12 +179,16 @@ struct ChunkSmem {
         alignas(16) float omega[ISO ? 4 : C * DK];
         alignas(16) IO k[C * DK];
         alignas(16) IO q[C * DK];
+        alignas(16) float cS[DK];  // per-channel decay reference c (a power of two)
+        int cfl[4];                // per chain wave: some c != 1 in this chunk
     };
     struct Ops {
         alignas(16) IO Kb[C * LD_K];
         alignas(16) IO Qb[C * LD_K];
         alignas(16) IO Ktp[C * LD_K];
         alignas(16) float gC[DK];
+        alignas(16) float cS[DK];
+        int cfl;
     };
     struct Fac {
         alignas(16) IO T[C * LD_S];
@@ -324,9 +328,19 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
                 *reinterpret_cast<VecIO*>(&op.Ktp[t * LD_K + i0]) = kt;
                 if (t == C - 1) {
 #pragma unroll
-                    for (int e = 0; e < VE; e += 4)
+                    for (int e = 0; e < VE; e += 4) {
                         *reinterpret_cast<f32x4*>(&op.gC[i0 + e]) =
                             f32x4{G[e], G[e + 1], G[e + 2], G[e + 3]};
+                        *reinterpret_cast<f32x4*>(&op.cS[i0 + e]) =
+                            *reinterpret_cast<const f32x4*>(&st.cS[i0 + e]);
+                    }
+                    if (i0 == 0) {
+                        int f = 0;
+#pragma unroll
+                        for (int x = 0; x < NCW; ++x)
+                            f |= st.cfl[x];
+                        op.cfl = f;
+                    }
                 }
             }
         };
@@ -334,6 +348,14 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
         f32x4 accR, accO;
         auto mm_front = [&](int c) {
             const auto& op = sm.op[c % NOPS];
+            // a chunk whose decay takes a reference c != 1 (Kb, Qb from G / c,
+            // Ktp from c / G) is applied to diag(c) S; its G_C / c brings the
+            // state back to S
+            if (__builtin_amdgcn_readfirstlane(op.cfl)) {
+#pragma unroll
+                for (int n = 0; n < DK / 16; ++n)
+                    Sacc[n] *= *reinterpret_cast<const f32x4*>(&op.cS[16 * n + 4 * g4]);
+            }
             // R = Kb S  ([t][j], negated later),  O^T = S^T Qb^T  ([j][t])
             accR = zero4();
             accO = zero4();
@@ -471,17 +493,38 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
                         rv[t] = ok ? rv[t] : 1.f;
                     }
                 }
-                float g = 1.f;
+                // g = G_t / c: c = 1 unless the chunk's plain product of
+                // alphas falls below 2^-100 (decay_plain_ok, decay_ref)
+                float af[C], g = 1.f;
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    af[t] = al[t];
+                    g *= al[t];
+                }
+                DecayRef ref{false, 0};
+                if (__ballot(!decay_plain_ok(g)) != 0) {
+                    if (!decay_plain_ok(g)) {
+                        ref = decay_ref(al);
+#pragma unroll
+                        for (int t = 0; t < C; ++t)
+                            af[t] = decay_alpha(ref, al[t]);
+                    }
+                }
+                g = __builtin_amdgcn_ldexpf(1.f, -ref.m);
 #pragma unroll
                 for (int t = 0; t < C; ++t) {
                     // p = p^ / (1 + mu k^2 p^ / r) = p^ r / (r + mu k^2 p^)
                     const float ph = al[t] * al[t] * p + om[t];
                     const float den = mk2[t] * ph + rv[t];
                     p = ph * rv[t] * rcp(den);
-                    g *= al[t];
+                    g *= af[t];
                     st.alpha[t * DK + i] = g;
-                    st.omega[t * DK + i] = ph * rcp(g);  // p^ / G
+                    st.omega[t * DK + i] = ph * rcp(g);  // p^ c / G
                 }
+                st.cS[i] = __builtin_amdgcn_ldexpf(1.f, ref.m);
+                const bool any = __ballot(ref.m != 0) != 0;
+                if (lane == 0)
+                    st.cfl[wave - NMM] = any;
             };
             for (int c = -LEAD; c < nchunks; ++c) {
                 const int X = c + 3;
@@ -504,8 +547,9 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
                 if (X >= 0 && X < nchunks) {
                     const int nv = n_valid(X);
                     auto& st = sm.st[X % NSTAGE];
-                    // per-lane partial sums over its channels; G over alpha
+                    // per-lane partial sums over its channels; G / c over alpha
                     float sa[C], sk[C];
+                    bool anyc = false;
 #pragma unroll
                     for (int t = 0; t < C; ++t) {
                         sa[t] = 0.f;
@@ -527,14 +571,37 @@ __global__ __launch_bounds__(KDN_CHUNK_THREADS(DK, DVT, ISO), 1) void kdn_chunk_
                                 kvv[t] = t < nv ? kvv[t] : 0.f;
                             }
                         }
-                        float g = 1.f;
+                        // g = G_t / c (decay_plain_ok, decay_ref)
+                        float af[C], g = 1.f;
+#pragma unroll
+                        for (int t = 0; t < C; ++t) {
+                            af[t] = alv[t];
+                            g *= alv[t];
+                        }
+                        DecayRef ref{false, 0};
+                        if (__ballot(!decay_plain_ok(g)) != 0) {
+                            if (!decay_plain_ok(g)) {
+                                ref = decay_ref(alv);
+#pragma unroll
+                                for (int t = 0; t < C; ++t)
+                                    af[t] = decay_alpha(ref, alv[t]);
+                            }
+                        }
+                        g = __builtin_amdgcn_ldexpf(1.f, -ref.m);
 #pragma unroll
                         for (int t = 0; t < C; ++t) {
                             sa[t] += alv[t] * alv[t];
                             sk[t] += kvv[t] * kvv[t];
-                            g *= alv[t];
+                            g *= af[t];
                             st.alpha[t * DK + i] = g;
                         }
+                        st.cS[i] = __builtin_amdgcn_ldexpf(1.f, ref.m);
+                        anyc |= ref.m != 0;
+                    }
+                    {
+                        const bool any = __ballot(anyc) != 0;
+                        if (lane == 0)
+                            st.cfl[0] = any;
                     }
                     // transpose-reduce over the 64 lanes: each halving step
                     // keeps half the tokens and adds the partner lane's

@@ -36,6 +36,57 @@ __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x);
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Decay reference of one 16-token chunk and channel (chunked forward
+// kernels).  The chunk products pair G_t / c with c / G_s (Kb, Qb against
+// Ktp), so both must stay finite and normal for every t, s of the chunk,
+// G_t in [G_15, 1].  L = sum_t (e_t - 1), with e_t
+// the binary exponent of alpha_t, is an integer with 2^L <= G_15 < 2^(L + 16).
+//   L >= -100:  c = 1 (G_t and 1 / G_t within 2^100 of one);
+//   else:       c = 2^ceil(L / 2), which puts G_t / c and c / G_t within
+//               2^(L / 2) of one, at most 2^112 away for L >= -224;
+//   L < -224:   the chunk decays by more than fp32 can span; every alpha of the
+//               channel below 2^-14 is raised to 2^-14 for the memory decay
+//               (the variance recurrence keeps the true alpha), which brings
+//               L to -224 or above and perturbs the state by at most 2^-14 of
+//               its previous value per raised token.
+// An alpha below 2^-120 (zero included) counts as below the floor.  The rule
+// applies where the chunk's plain fp32 product of alphas (multiplied in token
+// order from 1) is below 2^-100 (decay_plain_ok); elsewhere c = 1, which the
+// kernels take without evaluating L.
+constexpr float kAlphaFloor = 0x1p-14f;
+constexpr int kLFree = -100, kLFloor = -224, kEFloor = -14;
+__device__ __forceinline__ int decay_lb(float a)
+{
+    return a >= 0x1p-120f ? __builtin_amdgcn_frexp_expf(a) - 1 : -1000;
+}
+struct DecayRef {
+    bool floor;  // alphas raised to kAlphaFloor for the memory decay
+    int m;       // c = 2^m, m <= 0
+};
+template <int N>
+__device__ __forceinline__ DecayRef decay_ref(const float (&al)[N])
+{
+    static_assert(N == 16, "the bounds above assume 16 tokens");
+    int L = 0;
+#pragma unroll
+    for (int t = 0; t < N; ++t)
+        L += decay_lb(al[t]);
+    DecayRef r{L < kLFloor, 0};
+    if (r.floor) {
+        L = 0;
+#pragma unroll
+        for (int t = 0; t < N; ++t)
+            L += max(decay_lb(al[t]), kEFloor);
+    }
+    r.m = L >= kLFree ? 0 : -((-L) >> 1);
+    return r;
+}
+__device__ __forceinline__ bool decay_plain_ok(float product) { return product >= 0x1p-100f; }
+__device__ __forceinline__ float decay_alpha(const DecayRef& r, float a)
+{
+    return r.floor ? fmaxf(a, kAlphaFloor) : a;
+}
+
 // Order this wave's LDS writes before its later LDS reads (other lanes of the
 // same wave read what a lane wrote).  No cross-wave effect.
 __device__ __forceinline__ void wave_lds_sync()

@@ -17,12 +17,13 @@
 //           wavefront with DPP.
 //   pass 2  carry: one lane per (batch, head, channel) applies the chunk
 //           summaries to the variance in chunk order (a 2x2 map of a scalar
-//           per chunk, loads running eight chunks ahead), giving every
-//           chunk's entry variance and the final variance.
+//           per chunk, loads running 24 chunks ahead), giving every chunk's
+//           entry variance and the final variance.
 //   pass 3  (only when kappa is requested) replay each chunk from its entry
 //           variance: p^_t, z_t = sum_i p^_t,i k_t,i^2, kappa = p^ k/(r + z).
-// Summaries are stored chunk-major, [B H][chunk][4][width], so that pass 1
-// writes whole rows and pass 2 reads them with lanes on adjacent channels.
+// Summaries are stored chunk-major, [B H][chunk][width][4] (one 16-byte map per
+// channel), so that pass 1 writes whole rows and pass 2 reads them with lanes
+// on adjacent channels.
 // Every combine rescales by 1/max|entry| (entries are non-negative), which
 // keeps the ratios and avoids fp32 overflow.
 #include "kdn_common.h"
@@ -121,11 +122,8 @@ __global__ __launch_bounds__(DK) void gain_summary_diag(GainArgs a, int nchunks)
         }
     }
     P = mob_normalize(P);
-    float* out = a.summ + ((size_t)bh * nchunks + c) * 4 * DK + i;
-    out[0] = P.m00;
-    out[DK] = P.m01;
-    out[2 * DK] = P.m10;
-    out[3 * DK] = P.m11;
+    *reinterpret_cast<float4*>(a.summ + (((size_t)bh * nchunks + c) * DK + i) * 4) =
+        float4{P.m00, P.m01, P.m10, P.m11};
 }
 
 template <typename IO, int DK>
@@ -147,19 +145,17 @@ __global__ __launch_bounds__(256) void gain_summary_iso(GainArgs a, int nchunks)
             m = Mob{sa[t], w, u * sa[t], 1.f + u * w};
         }
         const Mob incl = mob_wave_scan_inclusive(m);
-        if (t == 63) {
-            float* out = a.summ + ((size_t)bh * nchunks + c) * 4;
-            out[0] = incl.m00;
-            out[1] = incl.m01;
-            out[2] = incl.m10;
-            out[3] = incl.m11;
-        }
+        if (t == 63)
+            *reinterpret_cast<float4*>(a.summ + ((size_t)bh * nchunks + c) * 4) =
+                float4{incl.m00, incl.m01, incl.m10, incl.m11};
     }
 }
 
 // ---------------------------------------------------------------- pass 2
 // One lane per (bh, channel), 64 channels per wavefront: p entering chunk c,
-// then p <- (m00 p + m01) / (m10 p + m11) with chunk c's summary.
+// then p <- (m00 p + m01) / (m10 p + m11) with chunk c's summary.  The maps
+// are read PF chunks ahead through a register ring, so the serial chain does
+// not wait on memory.
 __global__ __launch_bounds__(64) void gain_carry(GainArgs a, int width, int nchunks)
 {
     const int groups = (width + 63) / 64;
@@ -167,23 +163,26 @@ __global__ __launch_bounds__(64) void gain_carry(GainArgs a, int width, int nchu
     if (i >= width)
         return;
     float p = a.var0 ? a.var0[(size_t)bh * width + i] : (a.c0 ? a.c0[bh % a.H] : 1.f);
-    const float* s = a.summ + (size_t)bh * nchunks * 4 * width + i;
+    const float4* s = reinterpret_cast<const float4*>(a.summ) + (size_t)bh * nchunks * width + i;
     float* out = a.carry + (size_t)bh * nchunks * width + i;
-    constexpr int PF = 8;
+    constexpr int PF = 24;
+    float4 ring[PF];
+    // chunk indices clamped into the sequence (no chunks: no reads at all)
+    auto load = [&](int c) { return s[(size_t)min(c, nchunks - 1) * width]; };
+    if (nchunks > 0) {
+#pragma unroll
+        for (int e = 0; e < PF; ++e)
+            ring[e] = load(e);
+    }
     for (int c0 = 0; c0 < nchunks; c0 += PF) {
-        float m[PF][4];
 #pragma unroll
         for (int e = 0; e < PF; ++e) {
-            const float* sc = s + (size_t)min(c0 + e, nchunks - 1) * 4 * width;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                m[e][j] = sc[j * width];
-        }
-#pragma unroll
-        for (int e = 0; e < PF; ++e) {
-            if (c0 + e < nchunks) {
-                out[(size_t)(c0 + e) * width] = p;
-                p = mob_apply(Mob{m[e][0], m[e][1], m[e][2], m[e][3]}, p);
+            const int c = c0 + e;
+            const float4 m = ring[e];
+            ring[e] = load(c + PF);
+            if (c < nchunks) {
+                out[(size_t)c * width] = p;
+                p = mob_apply(Mob{m.x, m.y, m.z, m.w}, p);
             }
         }
     }

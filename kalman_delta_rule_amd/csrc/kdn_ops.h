@@ -32,7 +32,7 @@ struct GainArgs {
     const float* var0;  // nullable
     float* kappa;       // nullable
     float* var_T;
-    float* summ;        // workspace: chunk summaries [BH][nchunks][4][width]
+    float* summ;        // workspace: chunk summaries [BH][nchunks][width][4]
     float* carry;       // workspace: chunk-entry variances [BH][nchunks][width]
     int B, T, H, dk;
     float mu;

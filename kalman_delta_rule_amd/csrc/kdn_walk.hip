@@ -16,6 +16,9 @@
 // Chunk form (compact WY, Appendix D as summarised in the notes), with
 // G_t = prod_{s<=t} alpha_s the cumulative decay from the chunk start:
 //   Kb = k (.) G,  Ktp = p^ (.) k / G,  Qb = q (.) G
+// (G taken relative to a per-channel power of two c where a chunk decays by
+// more than 2^100: Kb, Qb from G / c, Ktp from c / G, the chunk applied to
+// diag(c) S and G_C / c bringing it back; see decay_ref)
 //   L' = Kb Ktp^T  (diagonal = z_t),  Aqk = tril(Qb Ktp^T) (inclusive)
 //   M  = diag(r + z) + tril(L', -1),   T = M^-1
 //   Delta' = T (V - Kb S),   O = Qb S + Aqk Delta',
@@ -62,6 +65,10 @@
 #include "kdn_internal.h"
 
 #include <type_traits>
+
+// The roles' step bodies are lambdas; each must be inlined into the kernel
+// (an outlined call spills the role's registers to scratch on every step).
+#define KDN_INLINE __attribute__((always_inline))
 
 namespace kdn {
 namespace walk {
@@ -272,6 +279,8 @@ struct Smem {
         alignas(16) bf16 Qb[4 * CF::QS];
         alignas(16) bf16 Ktp[4 * CF::QS];
         alignas(16) float gC[DK];
+        alignas(16) float cS[DK];  // per-channel decay reference c (a power of two)
+        int cfl[4];                // per builder wave: some c != 1 in this chunk
     };
     struct Tri {  // first factor wave -> second factor wave, memory
         alignas(16) float Mt[C * 20];         // M^T (fp32): Mt[s][t] = M[t][s], rows padded to 20
@@ -319,6 +328,8 @@ struct SmemX3 {
         alignas(16) bf16 Ktp[4 * CF::QS];
         alignas(16) bf16 Ktl[4 * CF::QS];
         alignas(16) float gC[DK];
+        alignas(16) float cS[DK];
+        int cfl[4];
     };
     struct Tri {
         alignas(16) float Mt[C * 20];
@@ -457,6 +468,32 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     Sacc[nb][n] = zero4();
             }
         }
+        // A chunk whose decay takes a reference c != 1 (its Kb, Qb hold G / c
+        // and its Ktp c / G) is applied to diag(c) S (its flag arrives with its
+        // operands, fetched during the step before), and its G_C / c brings
+        // the state back to S at the end of the step.
+        // (bit w of the flag: builder wave w, channels 64 w .. 64 w + 63)
+        auto chunk_flag = [&](const int (&cfl)[4]) KDN_INLINE {
+            int f = cfl[0];
+#pragma unroll
+            for (int w2 = 1; w2 < CF::NBW; ++w2)
+                f |= cfl[w2] << w2;
+            return f;
+        };
+        auto scale_state = [&](int flag, const float* cS) KDN_INLINE {
+#pragma unroll
+            for (int w2 = 0; w2 < CF::NBW; ++w2) {
+                if (flag & (1 << w2)) {
+#pragma unroll
+                    for (int n = 4 * w2; n < 4 * w2 + 4; ++n) {
+                        const f32x4 cs = *reinterpret_cast<const f32x4*>(&cS[16 * n + 4 * g4]);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            Sacc[nb][n] *= cs;
+                    }
+                }
+            }
+        };
         // lane parts of the LDS addresses (elements)
         const int tr_lane = quad_tr_lane<QS>(lane);   // Kb, Qb transpose reads
         const int kt_lane = g4 * QS + c16 * 4;        // Ktp^T rows: quad g4, channel c16
@@ -481,9 +518,11 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             // the barrier with v
             struct MemOpsX {
                 bf16x8 kh[DK / 32], kl[DK / 32], qh[DK / 32], ql[DK / 32];
+                int cfl;  // the chunk's decay-reference flag
             };
-            auto fetchx = [&](int c, MemOpsX& m) {
+            auto fetchx = [&](int c, MemOpsX& m) KDN_INLINE {
                 const auto& kq = sm.kq[c % 3];
+                m.cfl = chunk_flag(sm.kt[c & 3].cfl);
 #pragma unroll
                 for (int mm = 0; mm < DK / 32; ++mm) {
                     m.kh[mm] = quad_frag32(kq.Kb + tr_lane, mm);
@@ -495,12 +534,13 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 }
             };
             const bf16x4 z4{};
-            auto applyx = [&](auto full_tag, int c, MemOpsX& m) {
+            auto applyx = [&](auto full_tag, int c, MemOpsX& m) KDN_INLINE {
                 constexpr bool FULL = decltype(full_tag)::value;
                 const int nv = FULL ? C : n_valid(c);
                 const auto& kt = sm.kt[c & 3];
                 const auto& tri = sm.tri[c % 3];
                 const bf16* V = sm.v[c % 3];
+                const int cfl = m.cfl;
                 const bf16x4 th = *reinterpret_cast<const bf16x4*>(tri.T + c16 * C + 4 * g4);
                 const bf16x4 tl = *reinterpret_cast<const bf16x4*>(tri.Tl + c16 * C + 4 * g4);
                 bf16x4 ah{}, al{};
@@ -530,7 +570,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 }
                 // S's next 32 rows are split while the current 32 rows'
                 // products run, so vector and matrix work can overlap
-                auto split_rows = [&](int mm, bf16x8 (&sh)[NB], bf16x8 (&sl)[NB]) {
+                auto split_rows = [&](int mm, bf16x8 (&sh)[NB], bf16x8 (&sl)[NB]) KDN_INLINE {
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         bf16x4 h0, l0, h1, l1;
@@ -540,6 +580,8 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                         sl[nb] = cat8(l0, l1);
                     }
                 };
+                if (const int f = __builtin_amdgcn_readfirstlane(cfl))
+                    scale_state(f, kt.cS);
                 bf16x8 sh[NB], sl[NB];
                 split_rows(0, sh, sl);
                 reads_issued();
@@ -604,7 +646,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 constexpr int PD = 2;
                 bf16x4 kth[PD + 1], ktl[PD + 1];
                 f32x4 gcf[PD + 1];
-                auto ldk = [&](int n, int s) {
+                auto ldk = [&](int n, int s) KDN_INLINE {
                     kth[s] = *reinterpret_cast<const bf16x4*>(kt.Ktp + kt_lane + 64 * n);
                     ktl[s] = *reinterpret_cast<const bf16x4*>(kt.Ktl + kt_lane + 64 * n);
                     gcf[s] = *reinterpret_cast<const f32x4*>(&kt.gC[16 * n + 4 * g4]);
@@ -652,9 +694,11 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         struct MemOps {
             bf16x8 kf[DK / 32], qf[DK / 32];  // Kb, Qb transposed fragments
             bf16x4 afr;                       // Aqk row
+            int cfl;                          // decay-reference flag
         };
-        auto fetch = [&](int c, MemOps& m) {
+        auto fetch = [&](int c, MemOps& m) KDN_INLINE {
             const auto& op = sm.op[c & (NOPS - 1)];
+            m.cfl = chunk_flag(op.cfl);
 #pragma unroll
             for (int mm = 0; mm < DK / 32; ++mm) {
                 m.kf[mm] = quad_frag32(op.Kb + tr_lane, mm);
@@ -665,12 +709,13 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 m.afr = *reinterpret_cast<const bf16x4*>(sm.tri[c % 3].Aqk + fr_lane);
         };
 
-        auto apply = [&](auto full_tag, int c, const MemOps& cur, MemOps& nxt) {
+        auto apply = [&](auto full_tag, int c, const MemOps& cur, MemOps& nxt) KDN_INLINE {
             constexpr bool FULL = decltype(full_tag)::value;
             const int nv = FULL ? C : n_valid(c);
             const auto& op = sm.op[c & (NOPS - 1)];
             const auto& tri = sm.tri[c % 3];
             const bf16* V = sm.v[c % 3];
+            const int cfl = cur.cfl;
             // this step's first reads: T (formed in the previous step) and v
             const bf16x4 tfr = *reinterpret_cast<const bf16x4*>(tri.T + c16 * C + 4 * g4);  // T[c16][4 g4 + e]
             bf16x4 vfr[NB];
@@ -686,6 +731,8 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                         if (4 * g4 + e >= nv)
                             vfr[nb][e] = static_cast<bf16>(0.f);
             }
+            if (const int f = __builtin_amdgcn_readfirstlane(cfl))
+                scale_state(f, op.cS);
             // front:  Y = Kb S  ([t][j]),   O^T = S^T Qb^T  ([j][t])
             f32x4 accY[NB], accO[NB];
 #pragma unroll
@@ -807,7 +854,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
 #pragma unroll
         for (int t = 0; t < C; ++t)
             goff[t] = 4u * ((uint32_t)t * (uint32_t)(H * DK) + (uint32_t)i);
-        auto load_omega = [&](auto slot_tag, int X) {
+        auto load_omega = [&](auto slot_tag, int X) KDN_INLINE {
             if constexpr (!ISO) {
                 constexpr int S = decltype(slot_tag)::value;
                 const auto rom = gate_desc(a.omega, X);
@@ -816,7 +863,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     rw[S][t] = gate_ld1(rom, goff[t]);
             }
         };
-        auto build = [&](auto full_tag, int X, const float (&omr)[ISO ? 1 : C]) {
+        auto build = [&](auto full_tag, int X, const float (&omr)[ISO ? 1 : C]) KDN_INLINE {
             constexpr bool FULL = decltype(full_tag)::value;
             const int nv = FULL ? C : n_valid(X);
             const auto& raw = sm.raw[X % NRAW];
@@ -858,7 +905,12 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 }
             }
             float kb[C], qb[C], kt[C];
+            // the chunk's decay, G = G_t / c: first with c = 1 (the plain
+            // product); channels whose chunk decays past 2^-100 take their
+            // reference (decay_plain_ok, decay_ref) and are recomputed, which a
+            // wave skips when none of its channels needs it
             float G = 1.f;
+            float kn_s[C], vd_s[C];  // Diagonal: p^_t k_t vd_{t-1} and vd_{t-1}
             if constexpr (!ISO) {
                 // with split builders Kb and Qb come from the elementwise wave
 #pragma unroll
@@ -866,14 +918,11 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     const float n1 = fmaf(om[t], vd, (al[t] * al[t]) * vn);  // p^_t = n1 / vd
                     const float kn = kf[t] * n1;
                     G *= al[t];
-                    const float re = rcp(vd * G);
-                    kt[t] = kn * re;                             // p^_t k_t / G_t
+                    kt[t] = kn * rcp(vd * G);                    // p^_t k_t c / G_t
+                    kn_s[t] = kn;
+                    vd_s[t] = vd;
                     vd = fmaf(kf[t] * bcast(tok, t), kn, vd);    // d_t = d_{t-1} + (mu k^2 / r) n_t
                     vn = n1;
-                    if constexpr (!CF::SPLIT) {
-                        kb[t] = kf[t] * G;
-                        qb[t] = qf[t] * G;
-                    }
                     if ((t & 3) == 3) {
                         // rescale [n; d] by 2^-e(d): exact, keeps n / d
                         const int ex = __builtin_amdgcn_frexp_expf(vd);
@@ -889,13 +938,36 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     if constexpr (!CF::NOQ)
                         qb[t] = qf[t] * G;
                 }
-                // 1 / G_t = (prod_{s > t} alpha_s) / G_C
-                const float rgc = rcp(G);
-                float suf = 1.f;
+            }
+            DecayRef ref{false, 0};
+            bool any = false;  // some channel of this wave takes c != 1
+            if (__ballot(!decay_plain_ok(G)) != 0) {
+                if (!decay_plain_ok(G)) {
+                    ref = decay_ref(al);
+                    G = __builtin_amdgcn_ldexpf(1.f, -ref.m);
+#pragma unroll
+                    for (int t = 0; t < C; ++t) {
+                        G *= decay_alpha(ref, al[t]);
+                        if constexpr (!ISO) {
+                            kt[t] = kn_s[t] * rcp(vd_s[t] * G);
+                        } else {
+                            kb[t] = kf[t] * G;
+                            if constexpr (!CF::NOQ)
+                                qb[t] = qf[t] * G;
+                        }
+                    }
+                }
+                any = __ballot(ref.m != 0) != 0;
+            }
+            if constexpr (ISO) {
+                // c / G_t = (c / G_C) prod_{s > t} alpha_s, accumulated from
+                // c / G_C down, so every partial product stays in the
+                // reference's range
+                float suf = rcp(G);
 #pragma unroll
                 for (int t = C - 1; t >= 0; --t) {
-                    kt[t] = bcast(tok, t) * kf[t] * (suf * rgc);
-                    suf *= al[t];
+                    kt[t] = bcast(tok, t) * kf[t] * suf;
+                    suf *= decay_alpha(ref, al[t]);
                 }
             }
             // token-quad writes: channel i's four tokens 4 tq .. +3 as 8 bytes
@@ -910,6 +982,11 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                     *reinterpret_cast<bf16x4*>(ks.Ktl + o) = lo;
                 }
                 ks.gC[i] = G;
+                // c of this wave's channels, read only under this wave's flag
+                if (any)
+                    ks.cS[i] = __builtin_amdgcn_ldexpf(1.f, ref.m);
+                if (lane == 0)
+                    ks.cfl[ridx] = any;
             } else {
                 auto& op = sm.op[X & (NOPS - 1)];
 #pragma unroll
@@ -929,6 +1006,10 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                                static_cast<bf16>(kt[4 * tq + 2]), static_cast<bf16>(kt[4 * tq + 3])};
                 }
                 op.gC[i] = G;
+                if (any)
+                    op.cS[i] = __builtin_amdgcn_ldexpf(1.f, ref.m);
+                if (lane == 0)
+                    op.cfl[ridx] = any;
             }
         };
         settle_counters();
@@ -939,7 +1020,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         load_omega(std::integral_constant<int, 0>{}, LB - LR);
         load_omega(std::integral_constant<int, 1>{}, LB - LR + 1);
         load_omega(std::integral_constant<int, 2>{}, LB - LR + 2);
-        auto step = [&](auto slot_tag, int c) {
+        auto step = [&](auto slot_tag, int c) KDN_INLINE {
             constexpr int S = decltype(slot_tag)::value;
             const int X = c + LB;
             if (X >= 0 && X < nchunks) {
@@ -1227,7 +1308,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 const bf16* kb = reinterpret_cast<const bf16*>(a.k) + cb;
                 const bf16* qb = reinterpret_cast<const bf16*>(a.q) + cb;
                 const uint32_t la = lds_addr(st.alpha), lk = lds_addr(st.k), lq = lds_addr(st.q);
-                auto copy_stage = [&](auto full_tag) {
+                auto copy_stage = [&](auto full_tag) KDN_INLINE {
                     constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
                     for (int j = 0; j < NI_A; ++j) {
@@ -1287,7 +1368,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         if constexpr (CF::SPLIT) {
             constexpr int CPL = DK / 64;
             static_assert(CPL == 1 || CPL == 2, "channels per lane");
-            auto build = [&](auto full_tag, int X) {
+            auto build = [&](auto full_tag, int X) KDN_INLINE {
                 constexpr bool FULL = decltype(full_tag)::value;
                 const int nv = FULL ? C : n_valid(X);
                 const auto& raw = sm.raw[X % NRAW];
@@ -1333,15 +1414,45 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 }
                 bf16 kb[CPL][C], qb[CPL][C], kl[CPL][C], ql[CPL][C];
                 float xk[CPL][C], xq[CPL][C];
+                // G_t / c with each channel's decay reference, taken as in the
+                // builders from the same alphas: the plain product first, the
+                // channels past 2^-100 recomputed (padded tokens: alpha = 1,
+                // k = q = 0)
+                bool slow[CPL];
 #pragma unroll
                 for (int e = 0; e < CPL; ++e) {
                     float G = 1.f;
 #pragma unroll
                     for (int t = 0; t < C; ++t) {
-                        const bool ok = FULL || t < nv;  // padded tokens: alpha = 1, k = q = 0
+                        const bool ok = FULL || t < nv;
                         G *= ok ? al[e][t] : 1.f;
                         xk[e][t] = ok ? kf[e][t] * G : 0.f;
                         xq[e][t] = ok ? qf[e][t] * G : 0.f;
+                    }
+                    slow[e] = !decay_plain_ok(G);
+                }
+                bool any_slow = false;
+#pragma unroll
+                for (int e = 0; e < CPL; ++e)
+                    any_slow |= slow[e];
+                if (__ballot(any_slow) != 0) {
+#pragma unroll
+                    for (int e = 0; e < CPL; ++e) {
+                        if (slow[e]) {
+                            float a1[C];
+#pragma unroll
+                            for (int t = 0; t < C; ++t)
+                                a1[t] = (FULL || t < nv) ? raw.alpha[t * DK + CPL * lane + e] : 1.f;
+                            const DecayRef ref = decay_ref(a1);
+                            float G = __builtin_amdgcn_ldexpf(1.f, -ref.m);
+#pragma unroll
+                            for (int t = 0; t < C; ++t) {
+                                const bool ok = FULL || t < nv;
+                                G *= decay_alpha(ref, a1[t]);
+                                xk[e][t] = ok ? kf[e][t] * G : 0.f;
+                                xq[e][t] = ok ? qf[e][t] * G : 0.f;
+                            }
+                        }
                     }
                 }
 #pragma unroll
@@ -1371,7 +1482,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 }
                 // token-quad writes: the lane's channels are adjacent, so the
                 // four tokens of each sit in one 8 * CPL byte run
-                auto put = [&](bf16* dst, const bf16 (&x)[CPL][C], int tq) {
+                auto put = [&](bf16* dst, const bf16 (&x)[CPL][C], int tq) KDN_INLINE {
                     const int o = tq * QS + CPL * lane * 4;
                     if constexpr (CPL == 2) {
                         *reinterpret_cast<bf16x8*>(dst + o) =
@@ -1444,7 +1555,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         const bool up3 = (lane & 8) != 0, up2 = (lane & 4) != 0;
         // v[16] -> one value per lane; every lane's slots go through the
         // same network, so the token a lane ends with is fixed
-        auto reduce = [&](float (&v)[C]) {
+        auto reduce = [&](float (&v)[C]) KDN_INLINE {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 swap32(v[j], v[j + 8]);

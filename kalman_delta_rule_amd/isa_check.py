@@ -17,6 +17,10 @@ occurrence, so that a code change cannot bring it back silently:
 
 Wait states are counted along every path from the producing product (each
 instruction counts one, ``s_nop N`` counts N + 1), following branches.
+
+It also rejects any function call in these sources' device code
+(``s_swappc_b64``): their kernels keep each role's work inlined, and an
+outlined call spills the caller's live registers to scratch on every step.
 """
 from __future__ import annotations
 
@@ -129,6 +133,11 @@ def find_hazards(instrs: List[str], min_ws: int = MIN_WAIT_STATES) -> List[Tuple
     return out
 
 
+def find_calls(instrs: List[str]) -> List[str]:
+    """Function calls (outlined device functions) in one body."""
+    return [ins for ins in instrs if ins.startswith("s_swappc_b64") or ins.startswith("s_call_b64")]
+
+
 def device_asm(src: str, include_dirs: List[str], hipcc: str, flags: List[str]) -> str:
     """gfx950 assembly of one source file (device side only)."""
     cmd = ([hipcc] + [f for f in flags if f not in ("-shared", "-fPIC")]
@@ -146,6 +155,9 @@ def check_sources(sources: List[str], include_dirs: List[str], hipcc: str,
     for src in sources:
         kernels = parse_kernels(device_asm(src, include_dirs, hipcc, flags))
         for name, instrs in kernels.items():
+            for call in find_calls(instrs):
+                problems.append("%s %s: device-side call '%s' (an outlined function)"
+                                % (os.path.basename(src), name[:60], call))
             hz = find_hazards(instrs)
             if verbose:
                 print("isa-check %s: %s (%d products): %d hazard(s)"

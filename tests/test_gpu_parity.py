@@ -272,3 +272,65 @@ def test_config2_diag_full(ora, math):
 @pytest.mark.parametrize("math", MATHS)
 def test_config3_long_full(ora, math):
     _whole(ora, 3, math=math)
+
+
+def _alpha_small(regime, shape, seed):
+    """Gates whose product over one 16-token chunk falls below 2^-100 in a
+    quarter of the channels (every fourth), the others sigmoid(N(2, 1)):
+      mid   alpha in [1e-3, 1e-2] (chunk products 1e-48 .. 1e-32): the chunk
+            kernels take a power-of-two reference c, results exact to rounding;
+      tiny  alpha in [1e-6, 1e-3] (products down to 1e-96, beyond fp32's span in
+            some chunks): alphas below 2^-14 are raised to 2^-14 there;
+      zero  alpha = 0 at a tenth of the tokens, else in [1e-2, 1]: the exact
+            reset, where the raised alpha leaves 2^-14 of the previous state."""
+    rng = np.random.default_rng(seed)
+    B, T, H, dk = shape
+    base = 1.0 / (1.0 + np.exp(-rng.normal(2.0, 1.0, shape)))
+    if regime == "mid":
+        small = 10.0 ** rng.uniform(-3.0, -2.0, shape)
+    elif regime == "tiny":
+        small = 10.0 ** rng.uniform(-6.0, -3.0, shape)
+    else:
+        small = np.where(rng.random(shape) < 0.1, 0.0, 10.0 ** rng.uniform(-2.0, 0.0, shape))
+    sel = (np.arange(dk) % 4 == 1)[None, None, None, :]
+    return np.where(sel, small, base).astype(np.float32)
+
+
+# bars: the regime with a reference only is held to the path's usual bar; the
+# raised alphas perturb a state row by at most 2^-14 (6.1e-5) of its previous
+# value per raised token, which the fp32-equivalent paths' bar is widened to
+# cover (2e-4); the single-product paths keep their bf16 bar
+SMALL_ALPHA_CASES = [
+    # (variant, io, math, dk)
+    ("diag", "bf16", None, 128),
+    ("diag", "bf16", "bf16", 128),
+    ("iso", "bf16", None, 128),
+    ("diag", "f32", None, 64),
+    ("iso", "f32", None, 64),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_ALPHA_CASES, ids=lambda c: "%s-%s-%s-dk%d" % c)
+@pytest.mark.parametrize("regime", ["mid", "tiny", "zero"])
+def test_small_alpha(ora, case, regime):
+    variant, io, math, dk = case
+    B, T, H, dv = 1, 300, 2, dk
+    w = inputs.Workload("t", variant, io, B, H, T, dk, dv, seed=81)
+    inp = inputs.make_fwd_inputs(w)
+    inp["alpha"] = _alpha_small(regime, (B, T, H, dk), seed=82)
+    d = to_dev(inp, io)
+    exact32 = io == "f32" or (variant == "diag" and math is None)
+    kw = {"o_dtype": torch.float32} if (io == "bf16" and exact32) else {}
+    o, S, var, _ = api.kdn_fwd_ex(variant, d["q"], d["k"], d["v"], d["alpha"], d["omega"],
+                                  d["r"], math=math, **kw)
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    res = oracle_heads(ora, variant, inp, heads)
+    err = compare_heads(res, host(o), host(S), host(var), heads)
+    print(regime, case, err, flush=True)
+    assert all(np.isfinite(host(x)).all() for x in (o, S, var))
+    if not exact32:
+        tol = TOL["bf16"]
+    else:
+        tol = 1e-4 if regime == "mid" else 2e-4
+    assert max(err.values()) <= tol, err

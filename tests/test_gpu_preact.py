@@ -138,3 +138,43 @@ def test_bwd_preact_matches_oracle(ora, case):
     print("bwd_preact %s errors %s" % (case, {k_: "%.2e" % v_ for k_, v_ in err.items()}),
           flush=True)
     assert max(err.values()) <= TOL[io], err
+
+
+@pytest.mark.parametrize("variant,io,dk", [("diag", "bf16", 128), ("iso", "bf16", 128),
+                                           ("diag", "f32", 64)],
+                         ids=lambda x: str(x))
+def test_preact_very_negative_gates(ora, variant, io, dk):
+    """a_pre in [-12, -5] in every fourth channel (alpha from 6e-6 to 7e-3:
+    16-token chunk products down to about 1e-84, past fp32's span) and
+    a_pre = -200 (alpha exactly 0 after the sigmoid saturates) at a tenth of
+    its tokens.  The forward's strong-decay rule raises alphas below 2^-14 to
+    2^-14 in chunks that fp32 cannot span, a relative perturbation of at most
+    6.1e-5 of a state row per raised token: fp32-equivalent paths are held
+    to 2e-4 here, the single-product bf16 paths to their usual bar."""
+    B, T, H, dv = 1, 200, 2, dk
+    w = inputs.Workload("t", variant, io, B, H, T, dk, dv, seed=741)
+    x = inputs.make_preact_inputs(w)
+    rng = np.random.default_rng(742)
+    sel = (np.arange(dk) % 4 == 3)[None, None, None, :]
+    neg = rng.uniform(-12.0, -5.0, x["a_pre"].shape)
+    neg = np.where(rng.random(x["a_pre"].shape) < 0.1, -200.0, neg)
+    x["a_pre"] = np.where(sel, neg, x["a_pre"]).astype(np.float32)
+    if io == "bf16":   # the values the device sees
+        x["a_pre"] = inputs.round_bf16(x["a_pre"])
+    d = _dev(x, io)
+    split = io == "bf16" and variant == "diag"
+    o, S, var, _ = api.kdn_fwd_preact(variant, d["q"], d["k"], d["v"], d["a_pre"], d["w_pre"],
+                                      d["r_pre"], r_min=0.01)
+    torch.cuda.synchronize()
+    g = ora.gate_prologue(x["a_pre"], x["w_pre"], x["r_pre"], r_min=0.01)
+    fn = ora.diag_fwd if variant == "diag" else ora.iso_fwd
+    ref = fn(x["q"], x["k"], x["v"], g["alpha"], g["omega"], g["r"])
+    rv = ref["p"] if variant == "diag" else ref["b"]
+    err = {"S": rel_l2(host(S), ref["S"]), "var": rel_l2(host(var), rv),
+           "o": rel_l2(host(o), ref["o"])}
+    print("very negative a_pre", variant, io, err, flush=True)
+    assert all(np.isfinite(host(t)).all() for t in (o, S, var))
+    tol = 2e-4 if (io == "f32" or split) else TOL[io]
+    assert err["S"] <= tol and err["var"] <= tol, err
+    # o in bf16 carries its own rounding
+    assert err["o"] <= (TOL["bf16"] if io == "bf16" else tol), err

@@ -42,3 +42,10 @@ def test_parses_kernel_bodies():
                       "\ts_endpgm", ".Lfunc_end0:"])
     ks = isa_check.parse_kernels(text)
     assert list(ks) == ["_Z3fooPf"] and ks["_Z3fooPf"][0].startswith("v_mfma")
+
+
+def test_flags_device_side_calls():
+    body = ["s_getpc_b64 s[0:1]", "s_add_u32 s0, s0, fn@rel32@lo+4",
+            "s_swappc_b64 s[30:31], s[0:1]", "s_endpgm"]
+    assert isa_check.find_calls(body) == ["s_swappc_b64 s[30:31], s[0:1]"]
+    assert isa_check.find_calls(["v_add_u32_e32 v1, 1, v2", "s_endpgm"]) == []
