@@ -341,9 +341,10 @@ kdn_status kdn_bwd_preact(int variant, int B, int T, int H, int dk, int dv, int 
  * The scan composes the per-channel 2x2 Moebius maps
  *   M_t = [[alpha^2, omega], [u alpha^2, 1 + u omega]]
  * (KDN reading notes, method part §6, Eq. (32)-(39)) within 64-token chunks
- * with a wavefront-level parallel scan, then carries chunk summaries across
- * chunks with a second scan, then replays each chunk from its entry
- * variance.  Needs kdn_gain_workspace_size(...) bytes of workspace.
+ * (one lane per channel for Diagonal, a wavefront scan over the tokens for
+ * Isotropic), then applies the chunk summaries to the variance in chunk order
+ * to get every chunk's entry variance, then replays each chunk from it.
+ * Needs kdn_gain_workspace_size(...) bytes of workspace.
  */
 size_t kdn_gain_workspace_size(int variant, int B, int T, int H, int dk);
 kdn_status kdn_gain_scan(int variant, int B, int T, int H, int dk, int io_dtype, float mu,

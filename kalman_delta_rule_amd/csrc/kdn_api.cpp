@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 
 #include "kdn.h"
 #include "kdn_internal.h"
@@ -35,6 +36,24 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr size_t kMaxElems = (size_t)1 << 31;
 
+// true when the product of the (non-negative) factors stays below 2^31; each
+// partial product is compared before the next multiplication, so no
+// intermediate can wrap around
+static bool below_2_31(std::initializer_list<size_t> factors)
+{
+    size_t p = 1;
+    for (size_t f : factors) {
+        if (f == 0)
+            return true;
+        if (f >= kMaxElems || p >= kMaxElems / f + 1)
+            return false;
+        p *= f;
+        if (p >= kMaxElems)
+            return false;
+    }
+    return true;
+}
+
 // Shape / dtype rules shared by the forward and step calls.
 kdn_status check_common(int B, int T, int H, int dk, int dv, int io, float mu, bool chunked)
 {
@@ -62,9 +81,9 @@ kdn_status check_common(int B, int T, int H, int dk, int dv, int io, float mu, b
         if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
             return fail(KDN_ERR_UNSUPPORTED, "step supports dk, dv in {64, 128}, got %d, %d", dk, dv);
     }
-    const size_t tokens = (size_t)B * (size_t)(T > 0 ? T : 1) * (size_t)H;
     const size_t widest = (size_t)(dk > dv ? dk : dv);
-    if (tokens * widest >= kMaxElems || (size_t)B * H * dk * (size_t)dv >= kMaxElems)
+    if (!below_2_31({(size_t)B, (size_t)(T > 0 ? T : 1), (size_t)H, widest}) ||
+        !below_2_31({(size_t)B, (size_t)H, (size_t)dk, (size_t)dv}))
         return fail(KDN_ERR_UNSUPPORTED, "tensor sizes must stay below 2^31 elements");
     return KDN_OK;
 }
@@ -250,7 +269,8 @@ extern "C" {
 
 size_t kdn_fwd_workspace_size(int variant, int B, int T, int H, int dk, int dv, int io_dtype)
 {
-    if (B < 0 || T < 0 || H <= 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+    if (B < 0 || T < 0 || H <= 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128) ||
+        !below_2_31({(size_t)B, (size_t)(T > 0 ? T : 1), (size_t)H, (size_t)(dk > dv ? dk : dv)}))
         return 0;
     const bool iso = variant == KDN_ISO;
     const int nseg =
@@ -362,7 +382,7 @@ kdn_status kdn_dense_fwd(int B, int T, int H, int dk, int dv, int io_dtype, cons
         return fail(KDN_ERR_UNSUPPORTED, "dense filter supports dk in {16, 32, 64}, got %d", dk);
     if (dv != 16 && dv != 32 && dv != 64 && dv != 128)
         return fail(KDN_ERR_UNSUPPORTED, "dense filter supports dv in {16, 32, 64, 128}, got %d", dv);
-    if ((size_t)B * (size_t)(T > 0 ? T : 1) * H * (size_t)(dk > dv ? dk : dv) >= kMaxElems)
+    if (!below_2_31({(size_t)B, (size_t)(T > 0 ? T : 1), (size_t)H, (size_t)(dk > dv ? dk : dv)}))
         return fail(KDN_ERR_UNSUPPORTED, "tensor sizes must stay below 2^31 elements");
     if (T > 0) {
         KDN_REQUIRE(q, "q");
@@ -404,7 +424,8 @@ static size_t round64f(size_t n) { return (n + 63) & ~(size_t)63; }
 
 size_t kdn_fwd_preact_workspace_size(int variant, int B, int T, int H, int dk)
 {
-    if ((variant != KDN_DIAG && variant != KDN_ISO) || B < 1 || H < 1 || T < 0 || dk < 1)
+    if ((variant != KDN_DIAG && variant != KDN_ISO) || B < 1 || H < 1 || T < 0 || dk < 1 ||
+        !below_2_31({(size_t)B, (size_t)(T > 0 ? T : 1), (size_t)H, (size_t)dk}))
         return 0;
     const size_t ntok = (size_t)B * T * H;
     return (round64f(ntok * dk) + round64f(variant == KDN_ISO ? ntok : ntok * dk) +
@@ -477,7 +498,8 @@ kdn_status kdn_fwd_preact(int variant, int B, int T, int H, int dk, int dv, int 
 
 size_t kdn_bwd_workspace_size(int variant, int B, int T, int H, int dk, int dv)
 {
-    if ((variant != KDN_DIAG && variant != KDN_ISO) || B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1)
+    if ((variant != KDN_DIAG && variant != KDN_ISO) || B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1 ||
+        !below_2_31({(size_t)B, (size_t)(T > 0 ? T : 1), (size_t)H, (size_t)(dk > dv ? dk : dv)}))
         return 0;
     return kdn::bwd_workspace_floats(variant == KDN_ISO, B, T, H, dk, dv) * sizeof(float);
 }
@@ -506,7 +528,7 @@ static kdn_status bwd_impl(int variant, int B, int T, int H, int dk, int dv, int
         return fail(KDN_ERR_UNSUPPORTED, "backward supports dk in {64, 128}, got %d", dk);
     if (dv < 16 || dv > 256 || dv % 16 != 0)
         return fail(KDN_ERR_UNSUPPORTED, "backward supports dv a multiple of 16 up to 256, got %d", dv);
-    if ((size_t)B * (size_t)(T > 0 ? T : 1) * H * (size_t)(dk > dv ? dk : dv) >= kMaxElems)
+    if (!below_2_31({(size_t)B, (size_t)(T > 0 ? T : 1), (size_t)H, (size_t)(dk > dv ? dk : dv)}))
         return fail(KDN_ERR_UNSUPPORTED, "tensor sizes must stay below 2^31 elements");
     const bool iso = variant == KDN_ISO;
     if (var0 && c0_h)
@@ -709,7 +731,8 @@ kdn_status kdn_step_ex(int variant, int B, int H, int dk, int dv, int io_dtype, 
 
 size_t kdn_gain_workspace_size(int variant, int B, int T, int H, int dk)
 {
-    if (B < 1 || H < 1 || T < 0 || (dk != 64 && dk != 128))
+    if (B < 1 || H < 1 || T < 0 || (dk != 64 && dk != 128) ||
+        !below_2_31({(size_t)B, (size_t)(T > 0 ? T : 1), (size_t)H, (size_t)dk}))
         return 0;
     return kdn::gain_workspace_floats(variant == KDN_ISO, B, T, H, dk) * sizeof(float);
 }
@@ -735,7 +758,7 @@ kdn_status gain_check(int variant, int B, int T, int H, int dk, int io_dtype, fl
         return fail(KDN_ERR_UNSUPPORTED, "gain scan supports dk in {64, 128}, got %d", dk);
     if (!(mu >= 0.f) || !std::isfinite(mu))
         return fail(KDN_ERR_INVALID_ARG, "mu must be finite and >= 0");
-    if ((size_t)B * (size_t)(T > 0 ? T : 1) * H * dk >= kMaxElems)
+    if (!below_2_31({(size_t)B, (size_t)(T > 0 ? T : 1), (size_t)H, (size_t)dk}))
         return fail(KDN_ERR_UNSUPPORTED, "tensor sizes must stay below 2^31 elements");
     if (T > 0) {
         KDN_REQUIRE(k, "k");

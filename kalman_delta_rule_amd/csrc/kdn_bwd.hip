@@ -40,8 +40,6 @@
 
 namespace kdn {
 
-constexpr int BWD_L = 16;    // tokens per recompute chunk (checkpoint spacing)
-constexpr int BWD_COLS = 16; // value columns per memory workgroup
 
 // Lane exchanges in the vector ALU (no LDS round trip).  xor_lane<M>(x) is
 // x of lane l ^ M, for M = 1, 2 (quad permutes) and 4, 8 (a row shift one way
@@ -562,7 +560,6 @@ __global__ __launch_bounds__(256) void kdn_bwd_merge_kernel(BwdArgs args, int nb
 // it runs as a chunked scan over GR_C-token chunks: summaries (A, B) per
 // chunk and channel, a carry across chunks from the last, and a replay of
 // each chunk from its carried gradient that writes every output.
-constexpr int GR_C = 64;
 
 // Per-token quantities of one chunk in LDS, one thread per channel.
 template <int DK>
@@ -782,62 +779,6 @@ __global__ __launch_bounds__(256) void kdn_bwd_gr_mu_kernel(BwdArgs args, int nc
 // ---------------------------------------------------------------------------
 // workspace and launch
 // ---------------------------------------------------------------------------
-static size_t round64(size_t n) { return (n + 63) & ~(size_t)63; }
-
-size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv)
-{
-    const size_t ntok = (size_t)B * T * H, bh = (size_t)B * H;
-    const size_t nch = ((size_t)T + BWD_L - 1) / BWD_L, nblk = (size_t)dv / BWD_COLS;
-    size_t n = 0;
-    if (iso)
-        n += round64(ntok * 4);
-    else
-        n += 2 * round64(ntok * dk) + round64(ntok);
-    n += round64(gain_workspace_floats(iso, B, T, H, dk));  // gain scan summaries and carries
-    const size_t ngc = ((size_t)T + GR_C - 1) / GR_C, width = iso ? 1 : (size_t)dk;
-    n += round64(bh * ngc * width * 2) + round64(bh * ngc * width) + round64(ntok) +
-         round64(bh * ngc);                  // gain backward: summaries, carries, dbar, mu parts
-    n += round64(bh * nch * dk * dv);        // checkpoints
-    n += round64(ntok * dv);                 // innovations
-    n += round64(4 * nblk * ntok * dk);      // partials
-    return n;
-}
-
-void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws)
-{
-    const size_t ntok = (size_t)a.B * a.T * a.H, bh = (size_t)a.B * a.H;
-    const size_t nch = ((size_t)a.T + BWD_L - 1) / BWD_L, nblk = (size_t)a.dv / BWD_COLS;
-    float* p = ws;
-    a.kap = a.pprev = a.dd = a.gsc = nullptr;
-    if (iso) {
-        a.gsc = p;
-        p += round64(ntok * 4);
-    } else {
-        a.kap = p;
-        p += round64(ntok * a.dk);
-        a.pprev = p;
-        p += round64(ntok * a.dk);
-        a.dd = p;
-        p += round64(ntok);
-    }
-    a.gscan = p;
-    p += round64(gain_workspace_floats(iso, a.B, a.T, a.H, a.dk));
-    const size_t ngc = ((size_t)a.T + GR_C - 1) / GR_C, width = iso ? 1 : (size_t)a.dk;
-    a.gr_sum = p;
-    p += round64(bh * ngc * width * 2);
-    a.gr_carry = p;
-    p += round64(bh * ngc * width);
-    a.gr_tok = p;
-    p += round64(ntok);
-    a.gr_mu = p;
-    p += round64(bh * ngc);
-    a.ckpt = p;
-    p += round64(bh * nch * a.dk * a.dv);
-    a.dlt = p;
-    p += round64(ntok * a.dv);
-    a.part = p;
-}
-
 template <typename IO, bool ISO, int DK>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream)
 {

@@ -36,7 +36,7 @@ namespace kdn {
 
 __device__ __forceinline__ float mu_of(const GainArgs& a, int h) { return a.mu_h ? a.mu_h[h] : a.mu; }
 
-constexpr int GC = 64;  // tokens per gain chunk
+constexpr int GC = GAIN_CHUNK;  // tokens per gain chunk
 
 __device__ __forceinline__ Mob mob_mul_raw(const Mob& later, const Mob& earlier)
 {
@@ -307,10 +307,7 @@ __global__ __launch_bounds__(256) void gain_replay_iso(GainArgs a, int nchunks)
 // per device, resident from the module's load until the process ends.  Host
 // code reaches it only through the device address hipGetSymbolAddress returns
 // (looked up once per device); the array's own name is a host-side stand-in.
-constexpr size_t kGainStaticFloats = (size_t)8 << 20;  // 32 MiB
-static __device__ __align__(256) float scratch[kGainStaticFloats];
-
-size_t gain_static_scratch_floats() { return kGainStaticFloats; }
+static __device__ __align__(256) float scratch[GAIN_STATIC_FLOATS];
 
 hipError_t gain_static_scratch(float** ptr)
 {
@@ -333,13 +330,6 @@ hipError_t gain_static_scratch(float** ptr)
     }
     *ptr = addr[dev];
     return hipSuccess;
-}
-
-size_t gain_workspace_floats(bool iso, int B, int T, int H, int dk)
-{
-    const size_t nchunks = (T + GC - 1) / GC;
-    const size_t width = iso ? 1 : (size_t)dk;
-    return (size_t)B * H * nchunks * width * 5;  // 4 summary planes + carries
 }
 
 template <typename IO, int DK>

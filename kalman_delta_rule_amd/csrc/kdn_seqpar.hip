@@ -28,34 +28,7 @@
 
 namespace kdn {
 
-constexpr int SP_MAX = 8;  // segments at most
-
 static size_t r64(size_t n) { return (n + 63) & ~(size_t)63; }
-
-int seqpar_segments(bool iso, int B, int T, int H, int dk, int dv, int io_dtype)
-{
-    (void)iso;
-    if (io_dtype != 1 || dk != dv || T <= 0)
-        return 0;
-    const long ncu = 256;  // MI355X compute units; a fixed figure keeps the size a pure function
-    const long tiles = (long)B * H * (dv / 64);
-    // worth it when the segments multiply the workgroups by 4 or more
-    // (three walks of T/S tokens against one of T) and stay long
-    for (int s = SP_MAX; s >= 4; s >>= 1)
-        if (tiles * s <= ncu && T % (64 * s) == 0 && T / s >= 1024)
-            return s;
-    return 0;
-}
-
-size_t seqpar_workspace_floats(bool iso, int B, int T, int H, int dk, int dv, int S)
-{
-    const size_t bs = (size_t)B * S, width = iso ? 1 : (size_t)dk;
-    const size_t st = bs * H * (size_t)dk * dv;
-    size_t n = r64(gain_workspace_floats(iso, B, T, H, dk));
-    n += 2 * r64(bs * H * width);                    // segment-entry variances, scratch
-    n += 4 * r64(st);                                // N, M, S_in, identity
-    return n;
-}
 
 __global__ __launch_bounds__(256) void sp_identity_kernel(float* I, size_t n, int D)
 {
