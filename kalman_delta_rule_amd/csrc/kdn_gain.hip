@@ -15,10 +15,12 @@
 //           64 maps serially in one lane (lanes = channels, coalesced loads);
 //           Isotropic scans the chunk's 64 maps across the lanes of one
 //           wavefront with DPP.
-//   pass 2  carry: one lane per (batch, head, channel) applies the chunk
-//           summaries to the variance in chunk order (a 2x2 map of a scalar
-//           per chunk, loads running 24 chunks ahead), giving every chunk's
-//           entry variance and the final variance.
+//   pass 2  carry: one lane per (batch, head, channel) and eight runs of
+//           chunks per lane's channel: each run's maps are composed, the runs
+//           before a run are applied to the initial variance, then each run
+//           applies its chunk summaries to the variance in chunk order (a 2x2
+//           map of a scalar per chunk), giving every chunk's entry variance
+//           and the final variance.
 //   pass 3  (only when kappa is requested) replay each chunk from its entry
 //           variance: p^_t, z_t = sum_i p^_t,i k_t,i^2, kappa = p^ k/(r + z).
 // Summaries are stored chunk-major, [B H][chunk][width][4] (one 16-byte map per
@@ -28,6 +30,7 @@
 // keeps the ratios and avoids fp32 overflow.
 #include "kdn_common.h"
 
+#include <algorithm>
 #include <mutex>
 #include "kdn_internal.h"
 #include "kdn_ops.h"
@@ -152,41 +155,86 @@ __global__ __launch_bounds__(256) void gain_summary_iso(GainArgs a, int nchunks)
 }
 
 // ---------------------------------------------------------------- pass 2
-// One lane per (bh, channel), 64 channels per wavefront: p entering chunk c,
-// then p <- (m00 p + m01) / (m10 p + m11) with chunk c's summary.  The maps
-// are read PF chunks ahead through a register ring, so the serial chain does
-// not wait on memory.
-__global__ __launch_bounds__(64) void gain_carry(GainArgs a, int width, int nchunks)
+// One lane per (bh, channel), 64 channels per wavefront, up to CARRY_WAVES
+// wavefronts per workgroup (one per 64 chunks: blockDim.x / 64 of them), each
+// over its own contiguous run of chunks: every
+// wave composes its run's maps into one (normalised products, later on the
+// left), the waves exchange those through LDS so that wave w applies the runs
+// before its own to the initial variance, then each wave walks its run again,
+// p entering chunk c, then p <- (m00 p + m01) / (m10 p + m11) with chunk c's
+// summary.  Two serial passes over nchunks / waves maps instead of one over
+// nchunks; maps are read PF chunks ahead through a register ring.
+constexpr int CARRY_WAVES = 8;
+__global__ __launch_bounds__(64 * CARRY_WAVES) void gain_carry(GainArgs a, int width, int nchunks)
 {
+    __shared__ float4 run_map[CARRY_WAVES][64];
     const int groups = (width + 63) / 64;
-    const int bh = blockIdx.x / groups, i = (blockIdx.x % groups) * 64 + threadIdx.x;
-    if (i >= width)
-        return;
-    float p = a.var0 ? a.var0[(size_t)bh * width + i] : (a.c0 ? a.c0[bh % a.H] : 1.f);
-    const float4* s = reinterpret_cast<const float4*>(a.summ) + (size_t)bh * nchunks * width + i;
-    float* out = a.carry + (size_t)bh * nchunks * width + i;
+    const int bh = blockIdx.x / groups, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int i = (blockIdx.x % groups) * 64 + lane;
+    const bool live = i < width;
+    const int nwave = blockDim.x >> 6;
+    const int per = (nchunks + nwave - 1) / nwave;
+    const int c_begin = min(nchunks, wv * per), c_end = min(nchunks, c_begin + per);
+    const int ic = live ? i : 0;  // lanes past the last channel read channel 0 and store nothing
+    const float4* s = reinterpret_cast<const float4*>(a.summ) + (size_t)bh * nchunks * width + ic;
     constexpr int PF = 24;
     float4 ring[PF];
-    // chunk indices clamped into the sequence (no chunks: no reads at all)
-    auto load = [&](int c) { return s[(size_t)min(c, nchunks - 1) * width]; };
-    if (nchunks > 0) {
+    // chunk indices clamped into the run (an empty run reads nothing)
+    auto load = [&](int c) { return s[(size_t)min(c, c_end - 1) * width]; };
+    auto prime = [&]() {
+        if (c_begin < c_end) {
 #pragma unroll
-        for (int e = 0; e < PF; ++e)
-            ring[e] = load(e);
-    }
-    for (int c0 = 0; c0 < nchunks; c0 += PF) {
+            for (int e = 0; e < PF; ++e)
+                ring[e] = load(c_begin + e);
+        }
+    };
+    // 1. this run's composed map (the last wave's is not needed)
+    Mob run = mob_identity();
+    const int c_comp_end = wv + 1 < nwave ? c_end : c_begin;
+    if (c_begin < c_comp_end)
+        prime();
+    for (int c0 = c_begin; c0 < c_comp_end; c0 += PF) {
 #pragma unroll
         for (int e = 0; e < PF; ++e) {
             const int c = c0 + e;
             const float4 m = ring[e];
             ring[e] = load(c + PF);
-            if (c < nchunks) {
-                out[(size_t)c * width] = p;
+            if (c < c_comp_end) {
+                run = mob_mul_raw(Mob{m.x, m.y, m.z, m.w}, run);
+                if ((e & 3) == 3)
+                    run = mob_normalize(run);
+            }
+        }
+    }
+    run = mob_normalize(run);
+    run_map[wv][lane] = float4{run.m00, run.m01, run.m10, run.m11};
+    __syncthreads();
+    // 2. the variance entering this run
+    float p = live ? (a.var0 ? a.var0[(size_t)bh * width + i] : (a.c0 ? a.c0[bh % a.H] : 1.f)) : 1.f;
+    for (int w2 = 0; w2 < wv; ++w2) {
+        const float4 m = run_map[w2][lane];
+        p = mob_apply(Mob{m.x, m.y, m.z, m.w}, p);
+    }
+    // 3. every chunk's entry variance
+    float* out = a.carry + (size_t)bh * nchunks * width + ic;
+    prime();
+    for (int c0 = c_begin; c0 < c_end; c0 += PF) {
+#pragma unroll
+        for (int e = 0; e < PF; ++e) {
+            const int c = c0 + e;
+            const float4 m = ring[e];
+            ring[e] = load(c + PF);
+            if (c < c_end) {
+                if (live)
+                    out[(size_t)c * width] = p;
                 p = mob_apply(Mob{m.x, m.y, m.z, m.w}, p);
             }
         }
     }
-    if (a.var_T)
+    // the last run ends with the final variance (the first wave when there
+    // are no chunks at all)
+    const int last = nchunks > 0 ? (nchunks - 1) / per : 0;
+    if (live && wv == last && a.var_T)
         a.var_T[(size_t)bh * width + i] = p;
 }
 
@@ -347,8 +395,9 @@ static hipError_t launch_gain_t(const GainArgs& a0, bool iso, hipStream_t stream
             hipLaunchKernelGGL((gain_summary_diag<IO, DK>), dim3(BH * nchunks), dim3(DK), 0,
                                stream, a, nchunks);
     }
-    hipLaunchKernelGGL(gain_carry, dim3(BH * ((width + 63) / 64)), dim3(64), 0, stream, a, width,
-                       nchunks);
+    const int carry_waves = std::min(CARRY_WAVES, std::max(1, nchunks / 64));
+    hipLaunchKernelGGL(gain_carry, dim3(BH * ((width + 63) / 64)), dim3(64 * carry_waves), 0,
+                       stream, a, width, nchunks);
     if ((a.kappa || a.gsc) && nchunks > 0) {
         if (iso)
             hipLaunchKernelGGL((gain_replay_iso<IO, DK>), dim3(BH * nchunks), dim3(256), 0,
