@@ -393,22 +393,47 @@ def bench_preact(args, w, variant):
     var_T = torch.empty((B, H, dk) if variant == "diag" else (B, H), dtype=torch.float32,
                         device=dev)
 
+    mth = "bf16" if (args.math == "bf16" and variant == "diag" and w.io == "bf16") else None
+
     def step():
         api.kdn_fwd_preact(variant, d["q"], d["k"], d["v"], d["a_pre"], d["w_pre"], d["r_pre"],
-                           r_min=0.01, o=o, S_T=S_T, var_T=var_T, workspace=ws)
+                           r_min=0.01, o=o, S_T=S_T, var_T=var_T, workspace=ws, math=mth)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # for comparison, the same result in two calls: the gates into HBM
+    # (kdn_gates_from_preact), then the forward reading them (kdn_fwd_ex)
+    L = _lib.lib()
+    f32 = torch.float32
+    g_al = torch.empty((B, T, H, dk), dtype=f32, device=dev)
+    g_om = torch.empty(tuple(d["w_pre"].shape), dtype=f32, device=dev)
+    g_r = torch.empty((B, T, H), dtype=f32, device=dev)
+    io_code = 1 if w.io == "bf16" else 0
+
+    def step_two_calls():
+        st = L.kdn_gates_from_preact(var, B, T, H, dk, io_code, d["a_pre"].data_ptr(),
+                                     d["w_pre"].data_ptr(), d["r_pre"].data_ptr(), 0.01,
+                                     g_al.data_ptr(), g_om.data_ptr(), g_r.data_ptr(),
+                                     torch.cuda.current_stream(dev).cuda_stream)
+        _lib.check(st)
+        api.kdn_fwd_ex(variant, d["q"], d["k"], d["v"], g_al, g_om, g_r, o=o, S_T=S_T,
+                       var_T=var_T, math=mth)
+
     stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(steps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps
+
+    ms_two = timed(step_two_calls, max(args.steps // 2, 1), max(args.warmup // 2, 1))
+    ms_step = timed(step, args.steps, args.warmup)
     s_io = 2 if w.io == "bf16" else 4
     alg = alg_bytes_preact(variant, B, T, H, dk, dv, s_io)
     achieved = alg / (ms_step / 1e3) / 1e9
@@ -426,12 +451,21 @@ def bench_preact(args, w, variant):
         "dtype": "bf16" if w.io == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "variant": variant, "B": B, "T": T, "H": H, "dk": dk,
-                   "dv": dv, "io": w.io, "gates": "pre-activations", "r_min": 0.01},
+                   "dv": dv, "io": w.io, "gates": "pre-activations", "r_min": 0.01,
+                   "contractions": ("bf16 products, fp32 accumulate" if mth == "bf16" or
+                                    variant == "iso" else "split-bf16 products, fp32 accumulate")
+                   if w.io == "bf16" else "fp32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "alg_bytes_per_launch": alg,
-                     "kernel": "kdn_gate_prologue (x3) + %s" % fwd_kernel_name(w.io)},
+                     "kernel": ("kdn_gate_prologue (r%s) + %s reading a_pre%s" % (
+                         ", omega" if variant == "iso" else "", fwd_kernel_name(w.io),
+                         "" if variant == "iso" else " and w_pre") if w.io == "bf16" else
+                         "kdn_gate_prologue (x3) + %s" % fwd_kernel_name(w.io))},
         "cpu_baseline": None,
+        # the same result from kdn_gates_from_preact + kdn_fwd_ex (gates
+        # through HBM), timed in the same run
+        "two_calls_ms_per_step": ms_two,
     }
     print(json.dumps(line), flush=True)
 

@@ -260,10 +260,16 @@ kdn_status kdn_dense_fwd(int B, int T, int H, int dk, int dv, int io_dtype, cons
  *   w_pre  [B,T,H,dk] (Diagonal) or [B,T,H] (Isotropic), io dtype, 16-byte aligned
  *   r_pre  [B,T,H] io dtype, 16-byte aligned
  *   r_min  > 0 and finite (keeps r > 0)
- * An elementwise pre-pass writes the fp32 gates into the workspace
+ * With bf16 io (and fp32 o not requested) the forward reads a_pre (and the
+ * Diagonal w_pre) itself and forms alpha (and omega) on chip, with the
+ * arithmetic of kdn_gates_from_preact; only r (and the Isotropic per-token
+ * omega) pass through the workspace.  With fp32 io an elementwise pre-pass
+ * writes all three gates into the workspace and the forward of kdn_fwd_ex
+ * runs on them.  Either way the result equals, bit for bit, kdn_fwd_ex on
+ * the gates kdn_gates_from_preact returns.  The workspace
  * (kdn_fwd_preact_workspace_size bytes, 16-byte aligned, disjoint from every
- * argument), then the forward of kdn_fwd_ex runs on them.  Validation
- * happens before anything is launched.  Every finite pre-activation is
+ * argument) is sized for the fp32 gates.  Validation happens before anything
+ * is launched.  Every finite pre-activation is
  * accepted: a very negative a gives a small or zero alpha (sigmoid saturates
  * to 0 below about -88), which the strong-decay rule above covers.
  */
@@ -274,6 +280,25 @@ kdn_status kdn_fwd_preact(int variant, int B, int T, int H, int dk, int dv, int 
                           float r_min, const float* S0, const float* var0, const float* c0_h,
                           void* o, float* S_T, float* var_T, float* beta_eff, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * The gates alone from their pre-activations (KDN reading notes, method part
+ * §8), as the forward from pre-activations forms them:
+ *   alpha = sigmoid(a_pre)           [B,T,H,dk]
+ *   omega = softplus(w_pre)          [B,T,H,dk] (Diagonal) or [B,T,H] (Isotropic)
+ *   r     = r_min + softplus(r_pre)  [B,T,H]
+ * Pre-activations in io_dtype (KDN_F32 or KDN_BF16, no flags), outputs fp32;
+ * every pointer device memory, 16-byte aligned, non-null when T > 0, and no
+ * output overlaps any input or other output.  r_min > 0 and finite.  The
+ * sigmoid and softplus use the hardware exp2 / log2 (~1 ulp each; softplus
+ * through log1p as log(u) e / (u - 1), u = 1 + e); the same operations form
+ * the gates inside the bf16 forward, so its results equal kdn_fwd_ex's on
+ * these gates bit for bit.  Asynchronous on `stream`.
+ */
+kdn_status kdn_gates_from_preact(int variant, int B, int T, int H, int dk, int io_dtype,
+                                 const void* a_pre, const void* w_pre, const void* r_pre,
+                                 float r_min, float* alpha, float* omega, float* r,
+                                 void* stream);
 
 /*
  * Backward pass of Diagonal / Isotropic KDN (the mixer is trained through the

@@ -20,6 +20,7 @@ from .api import (  # noqa: F401
     kdn_dense_fwd,
     kdn_fwd_ex,
     kdn_fwd_preact,
+    kdn_gates_from_preact,
     kdn_fwd_workspace_size,
     kdn_gain_scan,
     kdn_iso_fwd,
@@ -33,6 +34,7 @@ __all__ = [
     "kdn_step",
     "kdn_fwd_ex",
     "kdn_fwd_preact",
+    "kdn_gates_from_preact",
     "kdn_dense_fwd",
     "kdn_bwd",
     "kdn_bwd_preact",

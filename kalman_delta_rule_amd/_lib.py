@@ -62,6 +62,8 @@ def lib():
     L.kdn_fwd_preact.restype = i
     L.kdn_fwd_preact.argtypes = ([i] * 7 + [f] + [fp] + [vp] * 6 + [f] + [fp] * 3 + [vp]
                                  + [fp] * 3 + [vp, sz, vp])
+    L.kdn_gates_from_preact.restype = i
+    L.kdn_gates_from_preact.argtypes = [i] * 6 + [vp] * 3 + [f] + [fp] * 3 + [vp]
     L.kdn_bwd_preact_workspace_size.restype = sz
     L.kdn_bwd_preact_workspace_size.argtypes = [i] * 6
     L.kdn_bwd_preact.restype = i
@@ -94,7 +96,7 @@ def lib():
 
 EXPORTED = ("kdn_fwd_workspace_size", "kdn_diag_fwd", "kdn_iso_fwd", "kdn_step",
             "kdn_fwd_ex", "kdn_step_ex", "kdn_dense_fwd", "kdn_bwd_workspace_size", "kdn_bwd",
-            "kdn_fwd_preact_workspace_size", "kdn_fwd_preact",
+            "kdn_fwd_preact_workspace_size", "kdn_fwd_preact", "kdn_gates_from_preact",
             "kdn_bwd_preact_workspace_size", "kdn_bwd_preact",
             "kdn_gain_workspace_size", "kdn_gain_scan", "kdn_gain_scan_static_max_bytes",
             "kdn_gain_scan_static", "kdn_status_string",

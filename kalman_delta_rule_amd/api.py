@@ -270,6 +270,31 @@ def kdn_fwd_preact(variant: str, q, k, v, a_pre, w_pre, r_pre, r_min: float = 0.
     return o, S_T, var_T, beta
 
 
+def kdn_gates_from_preact(variant: str, a_pre, w_pre, r_pre, r_min: float = 0.01):
+    """The gates (alpha, omega, r), fp32, from their pre-activations, with the
+    arithmetic the forward from pre-activations uses (kdn_fwd_ex on these
+    gates equals kdn_fwd_preact bit for bit)."""
+    L = _lib.lib()
+    var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
+    if a_pre.dim() != 4:
+        raise ValueError("a_pre must be [B,T,H,dk]")
+    B, T, H, dk = a_pre.shape
+    dev = a_pre.device
+    io = _io_code(a_pre)
+    iso = var == KDN_ISO
+    _need(w_pre, "w_pre", (B, T, H) if iso else (B, T, H, dk), a_pre.dtype, dev)
+    _need(r_pre, "r_pre", (B, T, H), a_pre.dtype, dev)
+    f32 = torch.float32
+    alpha = torch.empty((B, T, H, dk), dtype=f32, device=dev)
+    omega = torch.empty(tuple(w_pre.shape), dtype=f32, device=dev)
+    r = torch.empty((B, T, H), dtype=f32, device=dev)
+    with torch.cuda.device(dev):
+        st = L.kdn_gates_from_preact(var, B, T, H, dk, io, _ptr(a_pre), _ptr(w_pre), _ptr(r_pre),
+                                     float(r_min), _ptr(alpha), _ptr(omega), _ptr(r), _stream(dev))
+    _lib.check(st)
+    return alpha, omega, r
+
+
 def kdn_bwd(variant: str, q, k, v, alpha, omega, r, d_o, S0=None, var0=None, mu=None,
             mu_h=None, c0_h=None, dS_T=None, dvar_T=None, want_state_grads: bool = True,
             workspace=None) -> dict:

@@ -250,10 +250,26 @@ kdn_status fwd_impl(bool iso, int B, int T, int H, int dk, int dv, int io_dtype,
     a.split = !iso && io == KDN_BF16 && !math_bf16;
     a.o_f32 = out_f32;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    if (pro && T > 0) {  // the gates from their pre-activations, into the workspace
-        hipError_t e = kdn::launch_gate_prologue(*pro, io, hs);
+    // From pre-activations, the bf16 walk reads a (and Diagonal w) itself and
+    // forms alpha (and omega) on chip; the per-token gates (r, Isotropic
+    // omega) and every gate of the fp32 path come from the gate pass, into
+    // the workspace.
+    const bool fused = pro && io == KDN_BF16 && !out_f32 && T > 0;
+    const bool fuse_omega = fused && !iso;
+    if (pro && T > 0) {
+        kdn::PrologueArgs p = *pro;
+        if (fused)
+            p.n_alpha = 0;
+        if (fuse_omega)
+            p.n_omega = 0;
+        hipError_t e = kdn::launch_gate_prologue(p, io, hs);
         if (e != hipSuccess)
             return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    if (fused) {
+        a.a_pre = pro->a_pre;
+        if (fuse_omega)
+            a.w_pre = pro->w_pre;
     }
     hipError_t e = seqpar ? kdn::launch_seqpar_fwd(a, iso, nseg, static_cast<float*>(workspace), hs)
                    : io == KDN_BF16 ? kdn::launch_walk_fwd(a, iso, hs)
@@ -494,6 +510,61 @@ kdn_status kdn_fwd_preact(int variant, int B, int T, int H, int dk, int dv, int 
     return fwd_impl(iso, B, T, H, dk, dv, io_dtype, mu, q, k, v, T > 0 ? alpha : nullptr,
                     T > 0 ? omega : nullptr, T > 0 ? r : nullptr, S0, var0, o, S_T, var_T, nullptr,
                     0, stream, x, &pa);
+}
+
+kdn_status kdn_gates_from_preact(int variant, int B, int T, int H, int dk, int io_dtype,
+                                 const void* a_pre, const void* w_pre, const void* r_pre,
+                                 float r_min, float* alpha, float* omega, float* r,
+                                 void* stream)
+{
+    if (variant != KDN_DIAG && variant != KDN_ISO)
+        return fail(KDN_ERR_INVALID_ARG, "variant must be KDN_DIAG (0) or KDN_ISO (1), got %d",
+                    variant);
+    if (io_dtype != KDN_F32 && io_dtype != KDN_BF16)
+        return fail(KDN_ERR_INVALID_ARG, "io_dtype must be KDN_F32 (0) or KDN_BF16 (1), got %d",
+                    io_dtype);
+    if (B < 1 || H < 1 || T < 0 || dk < 1)
+        return fail(KDN_ERR_INVALID_ARG, "need B >= 1, H >= 1, T >= 0, dk >= 1 (got B=%d T=%d H=%d dk=%d)",
+                    B, T, H, dk);
+    if (!below_2_31({(size_t)B, (size_t)(T > 0 ? T : 1), (size_t)H, (size_t)dk}))
+        return fail(KDN_ERR_UNSUPPORTED, "tensor sizes must stay below 2^31 elements");
+    if (!(r_min > 0.f) || r_min > 3.0e38f)
+        return fail(KDN_ERR_INVALID_ARG, "r_min must be finite and > 0 (got %g)", (double)r_min);
+    if (T == 0)
+        return ok();
+    KDN_REQUIRE(a_pre, "a_pre");
+    KDN_REQUIRE(w_pre, "w_pre");
+    KDN_REQUIRE(r_pre, "r_pre");
+    KDN_REQUIRE(alpha, "alpha");
+    KDN_REQUIRE(omega, "omega");
+    KDN_REQUIRE(r, "r");
+    KDN_ALIGNED(a_pre, "a_pre");
+    KDN_ALIGNED(w_pre, "w_pre");
+    KDN_ALIGNED(r_pre, "r_pre");
+    KDN_ALIGNED(alpha, "alpha");
+    KDN_ALIGNED(omega, "omega");
+    KDN_ALIGNED(r, "r");
+    const bool iso = variant == KDN_ISO;
+    const size_t es = io_dtype == KDN_BF16 ? 2 : 4;
+    const size_t ntok = (size_t)B * T * H, na = ntok * dk, nw = iso ? ntok : na;
+    struct Buf { const void* p; size_t n; const char* name; };
+    const Buf bufs[] = {{a_pre, na * es, "a_pre"}, {w_pre, nw * es, "w_pre"},
+                        {r_pre, ntok * es, "r_pre"}, {alpha, na * 4, "alpha"},
+                        {omega, nw * 4, "omega"}, {r, ntok * 4, "r"}};
+    for (int x = 3; x < 6; ++x)
+        for (int y = 0; y < 6; ++y) {
+            if (x == y)
+                continue;
+            const char *a0 = (const char*)bufs[x].p, *b0 = (const char*)bufs[y].p;
+            if (a0 < b0 + bufs[y].n && b0 < a0 + bufs[x].n)
+                return fail(KDN_ERR_INVALID_ARG, "%s must not overlap %s", bufs[x].name,
+                            bufs[y].name);
+        }
+    kdn::PrologueArgs pa{a_pre, w_pre, r_pre, alpha, omega, r, na, nw, ntok, r_min};
+    hipError_t e = kdn::launch_gate_prologue(pa, io_dtype, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(KDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 size_t kdn_bwd_workspace_size(int variant, int B, int T, int H, int dk, int dv)

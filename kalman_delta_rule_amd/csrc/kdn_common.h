@@ -34,6 +34,33 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf1
 // Fast reciprocal (v_rcp_f32, ~1 ulp).
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// Gates from their pre-activations (KDN reading notes, method part §8:
+// alpha = sigmoid(a), omega = softplus(w), r = r_min + softplus(rho)).  Every
+// kernel that forms a gate calls these, written with explicit hardware
+// operations (v_exp_f32 / v_log_f32 are base 2, ~1 ulp each) and no
+// multiply-add the compiler could contract, so that the separate gate pass
+// and the forward that reads pre-activations itself produce the same bits.
+//   sigmoid(x) = 1 / (1 + 2^(-x log2 e)), saturating to 0 or 1;
+//   softplus(x) = max(x, 0) + log1p(e), e = 2^(-|x| log2 e) in (0, 1], which
+//   equals log(1 + e^x) without overflow.  log1p(e) is log(u) e / (u - 1) with
+//   u = 1 + e (Goldberg, "What every computer scientist should know about
+//   floating-point arithmetic", Thm. 4): u - 1 is exact and the ratio cancels
+//   the rounding of u, so small e keeps its relative accuracy; u == 1 gives e.
+constexpr float kLog2e = 1.44269504088896341f, kLn2 = 0.693147180559945309f;
+__device__ __forceinline__ float gate_sigmoid(float x)
+{
+    return rcp(1.f + __builtin_amdgcn_exp2f(x * -kLog2e));
+}
+__device__ __forceinline__ float gate_softplus(float x, float add)
+{
+    const float e = __builtin_amdgcn_exp2f(fabsf(x) * -kLog2e);
+    const float u = 1.f + e;
+    const float l1p = u == 1.f ? e : (__builtin_amdgcn_logf(u) * kLn2) * (e * rcp(u - 1.f));
+    return (add + fmaxf(x, 0.f)) + l1p;
+}
+// a bf16 value held in the low 16 bits of a 32-bit word, widened to fp32
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Decay reference of one 16-token chunk and channel (chunked forward

@@ -52,6 +52,12 @@ struct FwdArgs {
     // bf16 walk only: 0 = full forward; 1 = state only (S_T and var_T; q and o
     // are not touched); 2 = state only with v taken as zero (v not touched)
     int state_only = 0;
+    // bf16 walk, full forward only: the gates' bf16 pre-activations, read by
+    // the walk itself (alpha = sigmoid(a_pre), Diagonal omega =
+    // softplus(w_pre), layouts as alpha and omega); alpha, and Diagonal
+    // omega, are then not read.  r, and Isotropic omega, stay fp32 gates.
+    const void* a_pre = nullptr;
+    const void* w_pre = nullptr;
 };
 
 struct StepArgs {

@@ -6,32 +6,22 @@
 // r = r_min + softplus(rho).  An elementwise, HBM-bound pass: each thread
 // turns 8 consecutive pre-activations (16 bytes of bf16 or 32 of fp32) into
 // 8 fp32 gates, and the forward then reads the gates as usual.
-// softplus(x) = max(x, 0) + log1p(exp(-|x|)), which equals log(1 + e^x)
-// without overflow; sigmoid(x) = 1 / (1 + exp(-x)) saturates to 0 or 1.
-// Both use the hardware exp2 / log2 (about 1 ulp each).  log1p(e) is
-// evaluated as log(u) * e / (u - 1), u = 1 + e (Goldberg, "What every
-// computer scientist should know about floating-point arithmetic", Thm. 4):
-// u - 1 is exact, and the ratio cancels the rounding of u, so small e keeps
-// its relative accuracy; u == 1 gives e itself.
+// The activations are the shared gate_sigmoid / gate_softplus, so that
+// these gates equal, bit for bit, the ones the bf16 forward forms itself
+// when it reads the pre-activations directly.
 #include "kdn_common.h"
 #include "kdn_internal.h"
 #include "kdn_ops.h"
 
 namespace kdn {
 
-__device__ __forceinline__ float log1p_of_small(float e)  // e in [0, 1]
-{
-    const float u = 1.f + e;
-    return u == 1.f ? e : __logf(u) * (e * rcp(u - 1.f));
-}
-
 template <int ACT>
 __device__ __forceinline__ float gate_act(float x, float add)
 {
     if constexpr (ACT == 0)
-        return rcp(1.f + __expf(-x));
+        return gate_sigmoid(x);
     else
-        return add + fmaxf(x, 0.f) + log1p_of_small(__expf(-fabsf(x)));
+        return gate_softplus(x, add);
 }
 
 template <typename IO, int ACT>

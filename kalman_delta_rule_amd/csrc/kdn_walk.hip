@@ -102,20 +102,24 @@ __device__ __forceinline__ void lds_wave_sync()
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// Buffer descriptor over a gate tensor from `base` to its end (`elems`
-// fp32 elements left, clamped to the 2^31 - 1 byte range of the record
-// count): loads through it are range-checked, and reads past the end of the
-// tensor (the rows after the last token of a ragged final chunk) return 0
-// instead of touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t gate_rsrc(const float* base, size_t elems)
+// Buffer descriptor over a gate tensor from `base` to its end (`bytes` left,
+// clamped to the 2^31 - 1 byte range of the record count): loads through it
+// are range-checked, and reads past the end of the tensor (the rows after the
+// last token of a ragged final chunk) return 0 instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gate_rsrc(const void* base, size_t bytes)
 {
-    const size_t bytes = elems * sizeof(float);
     const int nrec = bytes > 0x7fffffffull ? 0x7fffffff : (int)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, nrec, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
 }
 __device__ __forceinline__ float gate_ld1(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0u, 0));
+}
+// a bf16 gate pre-activation, zero-extended into the low half of the result
+// (kept as the bit pattern of a float until it is used)
+__device__ __forceinline__ float gate_ld1_bf16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0u, 0));
 }
 
 // Start a role that prefetches from global memory into a register ring with
@@ -198,7 +202,7 @@ __device__ __forceinline__ void mfma32(f32x4& d, const bf16x8& a, const bf16x8& 
 enum Role { R_MEM, R_BLD, R_ELT, R_FAC1, R_FAC2, R_LDR, R_ISO };
 
 template <int DK_, int NB_, int NMW_, bool ISO_, bool X3_ = false, bool OF32_ = false,
-          int SO_ = 0>
+          int SO_ = 0, int PRE_ = 0>
 struct Cfg {
     static constexpr int DK = DK_;
     static constexpr int NB = NB_;    // 16-column blocks per memory wave
@@ -220,6 +224,16 @@ struct Cfg {
     static constexpr bool NOQ = SO_ > 0;
     static constexpr bool NOV = SO_ == 2;
     static_assert(SO_ >= 0 && SO_ <= 2 && !(SO_ && OF32_), "state-only mode");
+    // gates from their bf16 pre-activations (PRE_ = 1: alpha, for
+    // Isotropic; 2: alpha and the Diagonal omega): the loader copies a (the
+    // pre-activation of alpha) into the second half of a raw slot's alpha
+    // array and turns it into alpha = sigmoid(a) in place one step later;
+    // with PRE_ = 2 the Diagonal builders load w and form omega = softplus(w)
+    // themselves.  The per-token gates (r, Isotropic omega) arrive as fp32.
+    static constexpr bool PRE = PRE_ > 0;
+    static constexpr bool PREW = PRE_ == 2;
+    static_assert(PRE_ >= 0 && PRE_ <= 2 && !(PRE_ && (SO_ || OF32_)) && !(PREW && ISO_),
+                  "pre-activation mode");
     static constexpr int DVT = 16 * NB * NMW;
     // builder waves, one lane per key channel.  Diagonal splits the builder
     // work: these waves run the variance recurrence and form Ktp and G_C,
@@ -229,13 +243,18 @@ struct Cfg {
     static constexpr int NEW = SPLIT ? 1 : 0;
     static constexpr int NWAVES = NMW + NBW + NEW + 3 + (ISO ? 1 : 0);
     // Hardware wave w runs on SIMD w % 4; the layout pairs each heavy role
-    // (memory, builders, first factor) with a light one on its SIMD.
+    // (memory, builders, first factor) with a lighter one on its SIMD.  With
+    // split products the memory waves set the step, and the SIMDs they run
+    // on take the two factor waves (measured: 3% faster than the loader
+    // beside a memory wave, and 5% with pre-activations, whose sigmoids the
+    // loader evaluates); single products keep the first factor wave beside a
+    // builder (measured faster there).
     // Entry w: role * 8 + index within the role.
     static constexpr int layout(int w)
     {
         if constexpr (DK == 128 && NMW == 2 && !ISO && X3_) {
             constexpr int L[8] = {R_MEM * 8, R_MEM * 8 + 1, R_BLD * 8, R_BLD * 8 + 1,
-                                  R_FAC2 * 8, R_LDR * 8, R_FAC1 * 8, R_ELT * 8};
+                                  R_FAC2 * 8, R_FAC1 * 8, R_LDR * 8, R_ELT * 8};
             return L[w];
         } else if constexpr (DK == 128 && NMW == 2 && !ISO) {
             constexpr int L[8] = {R_MEM * 8, R_MEM * 8 + 1, R_BLD * 8, R_BLD * 8 + 1,
@@ -439,11 +458,12 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
     // chunks at all it covers nothing: every load through it returns 0
     // without an access.
     const size_t gate_elems = (size_t)a.B * T * H * DK;
-    auto gate_desc = [&](const float* g, int x) {
+    auto gate_desc = [&](const void* g, int x) {
+        constexpr size_t es = CF::PREW ? 2 : 4;  // bf16 pre-activations or fp32 gates
         if (nchunks == 0)
             return gate_rsrc(g, 0);
         const size_t cb = row_k(min(max(x, 0), nchunks - 1) * C);
-        return gate_rsrc(g + cb, gate_elems - cb);
+        return gate_rsrc((const char*)g + es * cb, es * (gate_elems - cb));
     };
 
     if (role == R_MEM) {
@@ -850,17 +870,25 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         // (16 loads per step, so at most 16 (OPF + 1) - 1 = 63 outstanding)
         constexpr int OPF = 3;
         float rw[OPF + 1][ISO ? 1 : C];
+        // (with pre-activations: w as bf16 bits, turned into omega at use)
         uint32_t goff[C];
 #pragma unroll
         for (int t = 0; t < C; ++t)
-            goff[t] = 4u * ((uint32_t)t * (uint32_t)(H * DK) + (uint32_t)i);
+            goff[t] = (CF::PREW ? 2u : 4u) * ((uint32_t)t * (uint32_t)(H * DK) + (uint32_t)i);
         auto load_omega = [&](auto slot_tag, int X) KDN_INLINE {
             if constexpr (!ISO) {
                 constexpr int S = decltype(slot_tag)::value;
-                const auto rom = gate_desc(a.omega, X);
+                if constexpr (CF::PREW) {
+                    const auto rom = gate_desc(a.w_pre, X);
 #pragma unroll
-                for (int t = 0; t < C; ++t)
-                    rw[S][t] = gate_ld1(rom, goff[t]);
+                    for (int t = 0; t < C; ++t)
+                        rw[S][t] = gate_ld1_bf16(rom, goff[t]);
+                } else {
+                    const auto rom = gate_desc(a.omega, X);
+#pragma unroll
+                    for (int t = 0; t < C; ++t)
+                        rw[S][t] = gate_ld1(rom, goff[t]);
+                }
             }
         };
         auto build = [&](auto full_tag, int X, const float (&omr)[ISO ? 1 : C]) KDN_INLINE {
@@ -886,7 +914,9 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             const float tok = ISO ? tokr : mu * rcp(tokr);
 #pragma unroll
             for (int t = 0; t < C; ++t) {
-                if constexpr (!ISO)
+                if constexpr (CF::PREW)
+                    om[t] = gate_softplus(bf16_bits_to_f32(__float_as_uint(omr[t])), 0.f);
+                else if constexpr (!ISO)
                     om[t] = omr[t];
                 kf[t] = static_cast<float>(kr[t]);
                 if constexpr (!CF::SPLIT && !CF::NOQ)
@@ -1262,7 +1292,7 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
         constexpr int RPI_V = 64 / LPR_V, NI_V = C / RPI_V;
         static_assert(LPR_A <= 64 && LPR_K <= 64 && LPR_V == 8 && NI_A >= 1 && NI_K >= 1,
                       "row / lane split");
-        constexpr int NSTG = NI_A + (CF::NOQ ? 1 : 2) * NI_K + 1 + (ISO ? 1 : 0);
+        constexpr int NSTG = (CF::PRE ? NI_K : NI_A) + (CF::NOQ ? 1 : 2) * NI_K + 1 + (ISO ? 1 : 0);
         constexpr int NVI = NI_V;
         static_assert(NSTG + NVI <= 63, "outstanding copies within the vmcnt range");
         // LDS byte addresses of the copy targets (uniform)
@@ -1310,10 +1340,21 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 const uint32_t la = lds_addr(st.alpha), lk = lds_addr(st.k), lq = lds_addr(st.q);
                 auto copy_stage = [&](auto full_tag) KDN_INLINE {
                     constexpr bool FULL = decltype(full_tag)::value;
+                    if constexpr (CF::PRE) {
+                        // a (bf16, laid out as k) into the second half of the
+                        // alpha array
+                        const bf16* ab = reinterpret_cast<const bf16*>(a.a_pre) + cb;
 #pragma unroll
-                    for (int j = 0; j < NI_A; ++j) {
-                        const uint32_t o = FULL ? oa[j] : off_a(j, lim);
-                        dma16(a.alpha + cb, o, la + j * RPI_A * DK * 4);
+                        for (int j = 0; j < NI_K; ++j) {
+                            const uint32_t o = FULL ? ok_[j] : off_k(j, lim);
+                            dma16(ab, o, la + C * DK * 2 + j * RPI_K * DK * 2);
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < NI_A; ++j) {
+                            const uint32_t o = FULL ? oa[j] : off_a(j, lim);
+                            dma16(a.alpha + cb, o, la + j * RPI_A * DK * 4);
+                        }
                     }
 #pragma unroll
                     for (int j = 0; j < NI_K; ++j) {
@@ -1360,6 +1401,32 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 vm_wait<NVI>();
             else
                 vm_wait<0>();
+            if constexpr (CF::PRE) {
+                // alpha = sigmoid(a) of the chunk copied in the previous step
+                // (landed: only this step's copies are still in flight), in
+                // place: every lane reads its four-value groups of a before
+                // any lane writes, and the wave's LDS operations run in order
+                const int Y = c + LR - 1;
+                if (Y >= 0 && Y < nchunks) {
+                    float* dst = sm.raw[Y % NRAW].alpha;
+                    const float* src = dst + C * DK / 2;
+                    constexpr int NG = C * DK / 256;  // groups of four per lane
+                    float2 pv[NG];
+#pragma unroll
+                    for (int m = 0; m < NG; ++m)
+                        pv[m] = *reinterpret_cast<const float2*>(src + 2 * (64 * m + lane));
+                    lds_wave_sync();
+#pragma unroll
+                    for (int m = 0; m < NG; ++m) {
+                        const uint32_t w0 = __float_as_uint(pv[m].x), w1 = __float_as_uint(pv[m].y);
+                        const f32x4 g{gate_sigmoid(__uint_as_float(w0 << 16)),
+                                      gate_sigmoid(__uint_as_float(w0 & 0xffff0000u)),
+                                      gate_sigmoid(__uint_as_float(w1 << 16)),
+                                      gate_sigmoid(__uint_as_float(w1 & 0xffff0000u))};
+                        *reinterpret_cast<f32x4*>(dst + 4 * (64 * m + lane)) = g;
+                    }
+                }
+            }
             lds_barrier();
         }
     } else if (role == R_ELT) {
@@ -1725,6 +1792,20 @@ static hipError_t launch_state_only(const FwdArgs& a, bool iso, hipStream_t stre
 hipError_t launch_walk_fwd(const FwdArgs& a, bool iso, hipStream_t stream)
 {
     using namespace walk;
+    if (a.a_pre) {
+        if (a.state_only || a.o_f32)
+            return hipErrorInvalidValue;
+        if (iso)
+            return a.dk == 128 ? launch_cfg<Cfg<128, 2, 2, true, false, false, 0, 1>>(a, stream)
+                               : launch_cfg<Cfg<64, 2, 2, true, false, false, 0, 1>>(a, stream);
+        if (!a.w_pre)
+            return hipErrorInvalidValue;
+        if (a.split)
+            return a.dk == 128 ? launch_cfg<Cfg<128, 2, 2, false, true, false, 0, 2>>(a, stream)
+                               : launch_cfg<Cfg<64, 2, 2, false, true, false, 0, 2>>(a, stream);
+        return a.dk == 128 ? launch_cfg<Cfg<128, 2, 2, false, false, false, 0, 2>>(a, stream)
+                           : launch_cfg<Cfg<64, 2, 2, false, false, false, 0, 2>>(a, stream);
+    }
     if (a.state_only == 1)
         return launch_state_only<1>(a, iso, stream);
     if (a.state_only == 2)

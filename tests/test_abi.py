@@ -403,6 +403,34 @@ def test_fwd_preact_validation(L):
     assert L.kdn_fwd_preact_workspace_size(1, 1, 40, 2, 128) == 4 * (r64(ntok * 128) + 2 * r64(ntok))
 
 
+@cpu_only
+def test_gates_from_preact_validation(L):
+    G = 1 << 28
+    names = ["a", "w", "r", "alpha", "omega", "rr"]
+    base = {n: P + (i + 1) * G for i, n in enumerate(names)}
+
+    def gp(**kw):
+        a = dict(variant=0, B=1, T=40, H=2, dk=128, io=1, r_min=0.01)
+        a.update({n: base[n] for n in names})
+        a.update(kw)
+        return L.kdn_gates_from_preact(a["variant"], a["B"], a["T"], a["H"], a["dk"], a["io"],
+                                       a["a"], a["w"], a["r"], a["r_min"], a["alpha"],
+                                       a["omega"], a["rr"], None)
+    msg = lambda: L.kdn_last_error_message().decode()
+    assert gp(variant=2) == -1 and "variant" in msg()
+    assert gp(io=1 | 0x100) == -1 and "io_dtype" in msg()
+    assert gp(r_min=0.0) == -1 and "r_min" in msg()
+    assert gp(dk=0) == -1
+    assert gp(a=None) == -1 and "a_pre must not be NULL" in msg()
+    assert gp(omega=None) == -1 and "omega must not be NULL" in msg()
+    assert gp(alpha=base["alpha"] + 8) == -1 and "alpha must be 16-byte aligned" in msg()
+    # alpha [1,40,2,128] fp32 is 40 KiB: an omega 16 KiB after it overlaps
+    assert gp(omega=base["alpha"] + 16384) == -1 and "overlap" in msg()
+    assert gp(rr=base["a"] + 64) == -1 and "r must not overlap a_pre" in msg()
+    # nothing to do, nothing read
+    assert gp(T=0, a=None, w=None, r=None, alpha=None, omega=None, rr=None) == 0
+
+
 def test_bwd_preact_validation(L):
     G = 1 << 28
     names = ["q", "k", "v", "a", "w", "r", "d_o", "dq", "gk", "gv", "da", "dw", "dr", "ws"]

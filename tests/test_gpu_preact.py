@@ -79,6 +79,64 @@ def test_preact_equals_forward_on_the_same_gates():
     assert rel_l2(host(o1), host(o2)) < 2e-3
 
 
+FUSED_CASES = [
+    # (variant, math, B, T, H, dk, dv): the bf16 forward forms alpha (and
+    # Diagonal omega) from the pre-activations on chip
+    ("diag", None, 2, 150, 3, 128, 128),
+    ("diag", "bf16", 2, 150, 3, 128, 128),
+    ("iso", None, 1, 97, 2, 128, 256),
+    ("diag", None, 1, 70, 2, 64, 64),
+    ("diag", "bf16", 1, 33, 2, 64, 128),
+    ("iso", None, 2, 50, 1, 64, 64),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "%s-%s-B%dT%dH%ddk%ddv%d" % c)
+def test_fused_preact_equals_forward_on_its_gates(case):
+    """kdn_fwd_preact (pre-activations read by the walk) against kdn_fwd_ex on
+    the gates kdn_gates_from_preact returns: equal bit for bit, with per-head
+    mu, an initial state and variance, and beta_eff."""
+    variant, math, B, T, H, dk, dv = case
+    w = inputs.Workload("t", variant, "bf16", B, H, T, dk, dv, seed=770 + T + dk)
+    x = inputs.make_preact_inputs(w)
+    d = _dev(x, "bf16")
+    rng = np.random.default_rng(771)
+    mu_h = torch.from_numpy(rng.uniform(1.0, 150.0, H).astype(np.float32)).cuda()
+    S0 = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32)).cuda()
+    vs = (B, H) if variant == "iso" else (B, H, dk)
+    var0 = torch.from_numpy(rng.uniform(0.1, 2.0, vs).astype(np.float32)).cuda()
+    fused = api.kdn_fwd_preact(variant, d["q"], d["k"], d["v"], d["a_pre"], d["w_pre"],
+                               d["r_pre"], r_min=0.03, S0=S0, var0=var0, mu_h=mu_h,
+                               want_beta_eff=True, math=math)
+    al, om, r = api.kdn_gates_from_preact(variant, d["a_pre"], d["w_pre"], d["r_pre"], r_min=0.03)
+    ref = api.kdn_fwd_ex(variant, d["q"], d["k"], d["v"], al, om, r, S0=S0, var0=var0, mu_h=mu_h,
+                         want_beta_eff=True, math=math)
+    torch.cuda.synchronize()
+    for name, a_, b_ in zip(("o", "S_T", "var_T", "beta_eff"), fused, ref):
+        assert torch.equal(a_, b_), (name, rel_l2(host(a_).ravel(), host(b_).ravel()))
+
+
+def test_gates_from_preact_match_oracle(ora):
+    """The gates on their own against the oracle's fp64 prologue: ~1 ulp
+    hardware exp2 / log2 / rcp, so a few fp32 ulps relative."""
+    for variant, io in (("diag", "bf16"), ("iso", "bf16"), ("diag", "f32")):
+        w = inputs.Workload("t", variant, io, 2, 3, 45, 64, 64, seed=780)
+        x = inputs.make_preact_inputs(w)
+        x["a_pre"] = x["a_pre"] * 8.0   # saturating sigmoids and large softplus arguments too
+        x["w_pre"] = x["w_pre"] * 8.0
+        if io == "bf16":
+            x = {n: inputs.round_bf16(a) for n, a in x.items()}
+        d = _dev(x, io)
+        g = api.kdn_gates_from_preact(variant, d["a_pre"], d["w_pre"], d["r_pre"], r_min=0.02)
+        torch.cuda.synchronize()
+        ref = ora.gate_prologue(x["a_pre"], x["w_pre"], x["r_pre"], r_min=0.02)
+        for name, got in zip(("alpha", "omega", "r"), g):
+            want = np.asarray(ref[name], dtype=np.float64)
+            rel = np.abs(host(got).astype(np.float64) - want) / np.maximum(np.abs(want), 1e-30)
+            print(variant, io, name, "max rel err %.2e" % rel.max(), flush=True)
+            assert rel.max() < 4e-6, (variant, io, name, rel.max())
+
+
 def test_preact_empty_sequence_gives_initial_state():
     B, H, dk, dv = 2, 2, 128, 64
     z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device="cuda")
@@ -99,7 +157,12 @@ def test_preact_config2_full_sampled(ora):
     d = _dev(x, w.io)
     o, S, var, _ = api.kdn_fwd_preact(w.variant, d["q"], d["k"], d["v"], d["a_pre"], d["w_pre"],
                                       d["r_pre"], r_min=0.01)
+    # the whole tensors equal the forward on the gates the gate pass forms
+    g = api.kdn_gates_from_preact(w.variant, d["a_pre"], d["w_pre"], d["r_pre"], r_min=0.01)
+    o2, S2, var2, _ = api.kdn_fwd_ex(w.variant, d["q"], d["k"], d["v"], *g)
     torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S, S2) and torch.equal(var, var2)
+    del g, o2, S2, var2
     heads = sample_heads(w.B, w.H, 4, seed=202)
     sl = lambda a, b, h: np.ascontiguousarray(a[b:b + 1, :, h:h + 1])
     oh, Sh, vh = host(o), host(S), host(var)
