@@ -137,6 +137,15 @@ static void other_checks()
     EXPECT(kdn_fwd_preact(KDN_DIAG, 1, 64, 2, 64, 64, KDN_BF16, 64.f, nullptr, at(P), at(P), at(P), at(P),
                           at(P), at(P), 0.01f, nullptr, nullptr, nullptr, at(dq), fat(dk), fat(dv), nullptr,
                           at(ws), pws, nullptr) == KDN_ERR_HIP);
+    // the gates alone
+    EXPECT(kdn_gates_from_preact(KDN_DIAG, 1, 64, 2, 64, KDN_BF16, at(P), at(P), at(P), -1.f, fat(dq),
+                                 fat(dk), fat(dv), nullptr) == KDN_ERR_INVALID_ARG);
+    EXPECT(kdn_gates_from_preact(KDN_ISO, 1, 64, 2, 64, KDN_BF16, at(P), at(P), at(P), 0.01f, fat(dq),
+                                 fat(dq + 64), fat(dv), nullptr) == KDN_ERR_INVALID_ARG && said("overlap"));
+    EXPECT(kdn_gates_from_preact(KDN_ISO, 1 << 30, 1 << 30, 1 << 30, 64, KDN_BF16, at(P), at(P), at(P),
+                                 0.01f, fat(dq), fat(dk), fat(dv), nullptr) == KDN_ERR_UNSUPPORTED);
+    EXPECT(kdn_gates_from_preact(KDN_DIAG, 1, 64, 2, 64, KDN_BF16, at(P), at(P + 65536), at(P + 131072),
+                                 0.01f, fat(dq), fat(dk), fat(dv), nullptr) == KDN_ERR_HIP);
     // dense filter
     EXPECT(kdn_dense_fwd(1, 64, 2, 96, 64, KDN_BF16, at(P), at(P), at(P), fat(P), fat(P), fat(P), nullptr,
                          nullptr, at(dq), fat(dk), fat(dv), nullptr, nullptr) == KDN_ERR_UNSUPPORTED);
