@@ -321,10 +321,13 @@ kdn_status kdn_gates_from_preact(int variant, int B, int T, int H, int dk, int i
  *     (dL/dmu_h sums it over b)
  * dk in {64, 128}, dv a multiple of 16 up to 256; fp32 arithmetic whatever
  * the io type.  q, k, v, d_o and alpha are 16-byte aligned, the other fp32
- * arrays 4-byte aligned, dq / dk / dv aligned to their element size.  The forward is recomputed inside (the gain, then the state
- * at every 16th token and every token's innovations); the workspace (kdn_bwd_workspace_size bytes,
- * 16-byte aligned) holds that and per-block partial sums.  Asynchronous on
- * `stream`; validation as for the forward.
+ * arrays 4-byte aligned, dq / dk / dv aligned to their element size.  The
+ * forward is recomputed inside: the gain, then the state at every 16th token.
+ * With dv a multiple of 64 the memory part runs in 16-token chunks on the
+ * matrix cores (fp32 products); otherwise token by token from stored
+ * innovations.  The workspace (kdn_bwd_workspace_size bytes, 16-byte aligned)
+ * holds those and per-column-block partial sums.  Deterministic (no atomics).
+ * Asynchronous on `stream`; validation as for the forward.
  */
 size_t kdn_bwd_workspace_size(int variant, int B, int T, int H, int dk, int dv);
 kdn_status kdn_bwd(int variant, int B, int T, int H, int dk, int dv, int io_dtype, float mu,

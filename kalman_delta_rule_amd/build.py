@@ -15,10 +15,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkdn.so")
 SOURCES = ["kdn_api.cpp", "kdn_walk.hip", "kdn_chunk.hip", "kdn_step.hip", "kdn_gain.hip",
-           "kdn_dense.hip", "kdn_bwd.hip",
+           "kdn_dense.hip", "kdn_bwd.hip", "kdn_bwd_chunk.hip",
            "kdn_prologue.hip", "kdn_seqpar.hip", "kdn_plan.cpp"]
 # sources whose kernels use the matrix cores (checked by isa_check)
-MFMA_SOURCES = ["kdn_walk.hip", "kdn_chunk.hip"]
+MFMA_SOURCES = ["kdn_walk.hip", "kdn_chunk.hip", "kdn_bwd_chunk.hip"]
 ARCH = os.environ.get("KDN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

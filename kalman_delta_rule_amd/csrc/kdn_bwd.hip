@@ -782,7 +782,8 @@ __global__ __launch_bounds__(256) void kdn_bwd_gr_mu_kernel(BwdArgs args, int nc
 template <typename IO, bool ISO, int DK>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream)
 {
-    const int bh = a.B * a.H, nblk = a.dv / BWD_COLS;
+    const bool chunked = bwd_chunked(DK, a.dv);
+    const int bh = a.B * a.H, nblk = a.dv / (chunked ? BWD_CHUNK_COLS : BWD_COLS);
     if (a.T > 0) {
         const int nchunks = (a.T + 63) / 64;
         const size_t width = ISO ? 1 : (size_t)DK;
@@ -797,12 +798,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream)
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((kdn_bwd_mem_kernel<IO, ISO, DK>), dim3(nblk, bh), dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (chunked) {
+        e = launch_bwd_chunk_mem(a, ISO, sizeof(IO) == 2 ? 1 : 0, stream);
+    } else {
+        hipLaunchKernelGGL((kdn_bwd_mem_kernel<IO, ISO, DK>), dim3(nblk, bh), dim3(256), 0, stream,
+                           a);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess)
         return e;
     const size_t n4 = (size_t)a.B * a.T * a.H * DK / 4;
-    if (n4 > 0) {
+    if (n4 > 0 && !chunked) {  // the chunked path sums its blocks itself
         hipLaunchKernelGGL((kdn_bwd_merge_kernel<IO, DK>), dim3((unsigned)((n4 + 255) / 256)),
                            dim3(256), 0, stream, a, nblk);
         e = hipGetLastError();

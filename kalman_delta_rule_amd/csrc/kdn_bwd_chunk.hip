@@ -1,0 +1,731 @@
+// kdn_bwd_chunk.hip -- the memory part of the KDN backward in 16-token chunks
+// on the matrix cores (fp32 16x16x4 products), gfx950.
+//
+// Given the gains kap_t (the gain recompute of kdn_bwd.hip), the memory
+// recurrence of method part §2 / §4-§5 (Diagonal) and §7 (Isotropic, where
+// kap_t = beta_t k_t),
+//   S_t = D_t S_{t-1} + kap_t delta_t^T,  delta_t = v_t - (D_t S_{t-1})^T k_t,
+//   o_t = S_t^T q_t,
+// is, over a 16-token chunk with G_t = prod_{s <= t} alpha_s (per channel),
+// Kb = k G, Qb = q G, Kt = kap / G (rows = tokens) and chunk-start state S0
+// (the compact-WY form of Appendix D):
+//   delta = T (V - Kb S0),  T = (I + tril(Kb Kt^T, -1))^-1,
+//   O = Qb S0 + A delta,     A = tril(Qb Kt^T),
+//   S_C = diag(G_15) (S0 + Kt^T delta).
+// Its reverse, for incoming dO and dS_C, with E = diag(G_15) dS_C:
+//   ddelta = Kt E + A^T dO,  dR = T^T ddelta,  dV = dR,
+//   dS0 = E + Qb^T dO - Kb^T dR                      (carried to the chunk before),
+//   dL = -tril(dR delta^T, -1),  dA = tril(dO delta^T),
+//   dKb = dL Kt - dR S0^T,  dQb = dA Kt + dO S0^T,  dKt = dL^T Kb + dA^T Qb + delta E^T,
+// and per token and channel dq = dQb G, dk = dKb G, kapbar = dKt / G,
+//   dG_t = dKb k + dQb q - kapbar Kt  (+ rowsum(dS_C . X) at t = 15, X = S0 + Kt^T delta),
+//   dalpha_s = sum_{t >= s} dG_t G_t / alpha_s = G_{s-1} W_s,  W_s = dG_s + alpha_{s+1} W_{s+1},
+// the last form free of divisions by alpha.  Each chunk channel takes the decay
+// reference of the forward (a power of two c, G' = G / c, S0' = c S0, floored
+// alphas below 2^-224 of chunk decay; the chunk formulas hold with the primed
+// quantities and dS0 = c dS0'); where the floor raises an alpha, its memory
+// gradient is that of the raised value (zero).
+//
+// One workgroup of four waves per (batch, head, 64 value columns).  A forward
+// pass over the chunks stores every chunk-start state (this block's columns);
+// the reverse pass then takes the chunks last first.  The carried state (and
+// then its adjoint) stays in accumulators, split by key channels over the
+// waves; products that contract over key channels or tokens take their
+// operands from LDS.  Everything per token and key channel is linear in
+// dKb, dQb, dKt and the rowsum term, which sum over the value columns: each
+// block writes its partials of those, and a second kernel (one thread per
+// chunk and channel) sums the blocks and forms dq, kapbar and the memory's
+// dk and dalpha, the last through the recurrence above.
+#include "kdn_common.h"
+#include "kdn_internal.h"
+#include "kdn_ops.h"
+
+namespace kdn {
+namespace cbwd {
+
+constexpr int C = 16;       // tokens per chunk
+constexpr int NC = 64;      // value columns per workgroup
+constexpr int LC = NC + 4;  // row stride of the [.][NC] arrays
+constexpr int LM = C + 1;   // row stride of the 16 x 16 matrices
+
+template <int DK>
+struct Smem {
+    static constexpr int LK = DK + 4;
+    float Kb[C][LK];   // k G'
+    float Qb[C][LK];   // q G'
+    float Kt[C][LK];   // kap / G'
+    float S0[DK][LC];  // c S0, this block's columns
+    float E[DK][LC];   // the carried state / adjoint (G'_15 dS_C while a reverse chunk uses it)
+    float V[C][LC];
+    float dO[C][LC];
+    float D[C][LC];    // delta
+    float mR[C][LC];   // -dR
+    float Tm[C][LM];
+    float Am[C][LM];
+    float dLm[C][LM];  // also the powers of M while T is formed
+    float dAm[C][LM];
+    float Mp[2][C][LM];  // Kb Kt^T over each half of the key channels
+    float cS[DK];      // c per channel
+    float gL[DK];      // G'_15 per channel
+    // the chunk's per-channel inputs as loaded (rows of tokens), read back
+    // one channel per thread for the factors
+    float inA[C][DK];  // alpha
+    float inP[C][DK];  // kappa (Diagonal); beta in inP[t][0] (Isotropic)
+    uint4 inK[2 * C * DK * 4 / 16];  // k, then q, in the io type: [2][C][DK] (room for fp32)
+};
+
+// One chunk channel's decay reference and cumulative decays (the forward's
+// rule, the same operations in both kernels here): g[0] = 1 / c, g[t + 1] =
+// G'_t; alf[t] the decay the memory applies (floored where the reference
+// floors), bit t of `raised` set where the floor raised alpha_t.  Tokens
+// past a ragged end are al = 1.
+struct ChanDecay {
+    float g[C + 1];
+    float alf[C];
+    uint32_t raised;
+    int m;
+};
+__device__ __forceinline__ void chan_decay(const float (&al)[C], ChanDecay& d)
+{
+    float P = 1.f;
+#pragma unroll
+    for (int t = 0; t < C; ++t)
+        P *= al[t];
+    DecayRef ref{false, 0};
+    if (!decay_plain_ok(P))
+        ref = decay_ref(al);
+    d.m = ref.m;
+    d.raised = 0;
+    float G = __builtin_amdgcn_ldexpf(1.f, -ref.m);
+    d.g[0] = G;
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+        const float ad = decay_alpha(ref, al[t]);
+        d.raised |= (ad != al[t] ? 1u : 0u) << t;
+        d.alf[t] = ad;
+        G *= ad;
+        d.g[t + 1] = G;
+    }
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Direct global -> LDS copy: lane l's 16 bytes from its own global address
+// land at LDS byte address lds + 16 l (lds uniform); completion is tracked by
+// vmcnt.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds)
+{
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(size_t)lds, 16, 0, 0);
+}
+__device__ __forceinline__ uint32_t lds_u32(const void* p)
+{
+    return (uint32_t)(size_t)(const lds_void_t*)p;
+}
+
+// acc[m][n] += sum_k A(m, k) B(k, n) over K (multiple of 4), operands in LDS:
+// A(m, k) = A[m am + k ak], B(k, n) = B[k bk + n bn]; the 16x16x4 product
+// takes A(lane & 15, k0 + (lane >> 4)) and B(k0 + (lane >> 4), lane & 15).
+// The operands are read sixteen steps at a time, ahead of their products.
+template <int K>
+__device__ __forceinline__ void mmk(f32x4& acc, const float* A, int am, int ak, const float* B,
+                                    int bk, int bn, int lane)
+{
+    const int i = lane & 15, g = lane >> 4;
+    constexpr int NS = K / 4, BS = NS < 16 ? NS : 16;
+#pragma unroll
+    for (int s0 = 0; s0 < NS; s0 += BS) {
+        float a[BS], b[BS];
+#pragma unroll
+        for (int s = 0; s < BS; ++s) {
+            a[s] = A[i * am + (4 * (s0 + s) + g) * ak];
+            b[s] = B[(4 * (s0 + s) + g) * bk + i * bn];
+        }
+#pragma unroll
+        for (int s = 0; s < BS; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    }
+}
+
+// acc += A X with X a 16 x 16 accumulator (lane holds X[4 (lane >> 4) + r][lane & 15]):
+// step r contracts over k = 4 g + r, g = 0..3, which is exactly the lane's
+// own X[r] as the B operand.
+__device__ __forceinline__ void mm_acc(f32x4& acc, const float* A, int am, int ak, const f32x4& X,
+                                       int lane)
+{
+    const int i = lane & 15, g = lane >> 4;
+    float a[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        a[r] = A[i * am + (4 * g + r) * ak];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], X[r], acc, 0, 0, 0);
+}
+
+// an accumulator tile to / from LDS: element (4 g + r, i) at p[(4 g + r) ld + i]
+__device__ __forceinline__ void tile_store(float* p, int ld, const f32x4& x, int lane)
+{
+    const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        p[(4 * g + r) * ld + i] = x[r];
+}
+__device__ __forceinline__ f32x4 tile_load(const float* p, int ld, int lane)
+{
+    const int i = lane & 15, g = lane >> 4;
+    f32x4 x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        x[r] = p[(4 * g + r) * ld + i];
+    return x;
+}
+
+// Sum over the 16 lanes of a row (lanes 16 g .. 16 g + 15), in every lane of
+// it, by DPP exchanges in the vector ALU: lane l ^ 8 and l ^ 4 through a row
+// shift one way for the lanes whose bit is clear and the other way for the
+// rest (chosen by the bank mask: banks are the four 4-lane groups of a row),
+// then the quad permutes [2,3,0,1] and [1,0,3,2].
+template <int CTRL, int BANK>
+__device__ __forceinline__ float dpp_sel(float old, float src)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, src),
+                                                                 CTRL, 0xF, BANK, false));
+}
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp_sel<0x118, 0xC>(dpp_sel<0x108, 0x3>(x, x), x);  // + lane ^ 8
+    x += dpp_sel<0x114, 0xA>(dpp_sel<0x104, 0x5>(x, x), x);  // + lane ^ 4
+    x += dpp_sel<0x4E, 0xF>(x, x);                           // + lane ^ 2
+    x += dpp_sel<0xB1, 0xF>(x, x);                           // + lane ^ 1
+    return x;
+}
+
+// A barrier that orders LDS only: global loads and stores stay in flight
+// (a full __syncthreads would wait for every store of the chunk).  The
+// kernel reads no global memory that another wave wrote, except the
+// chunk-start states, which a full barrier between the passes orders.
+__device__ __forceinline__ void barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <typename IO, bool ISO, int DK>
+__global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
+{
+    const BwdArgs a = args;
+    using SM = Smem<DK>;
+    static_assert(sizeof(SM) <= 160 * 1024, "LDS budget");
+    constexpr int LK = SM::LK;
+    constexpr int CT = DK / 64;               // 16-channel tiles per wave
+    constexpr int NCK = DK * NC / (4 * 256);  // chunk-start state pieces (4 floats) per thread
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    SM& sm = *reinterpret_cast<SM*>(smem_raw);
+
+    const int blk = blockIdx.x, nblk = gridDim.x, bh = blockIdx.y;
+    const int H = a.H, T = a.T, dv = a.dv;
+    const int b = bh / H, h = bh % H;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int i16 = lane & 15, g4 = lane >> 4;
+    const int col0 = blk * NC;       // first value column of this block
+    const int chw = w * (DK / 4);    // first key channel of this wave's state rows
+    const int nch = (T + C - 1) / C;
+    const size_t ntok = (size_t)a.B * T * H;
+    const size_t ks = (size_t)nblk * ntok * DK;  // stride between the partial arrays
+    auto tok_of = [&](int t) { return ((size_t)b * T + t) * H + h; };
+    float* const ck_wg = a.ckpt + ((size_t)bh * nblk + blk) * (size_t)nch * (DK * NC);
+    const IO* kg = reinterpret_cast<const IO*>(a.k);
+    const IO* qg = reinterpret_cast<const IO*>(a.q);
+    const IO* vg = reinterpret_cast<const IO*>(a.v);
+    const IO* og = reinterpret_cast<const IO*>(a.go);
+    IO* dvg = reinterpret_cast<IO*>(a.gv);
+    const bool chth = tid < DK;   // one key channel per thread for the factors
+    const int ch = tid;
+    const int et = (tid * 4) / NC, ec = (tid * 4) % NC;  // this thread's 4 elements of a [C][NC] block
+
+    // the chunk's inputs: the rows of alpha, kappa, k and q copied straight
+    // from global memory into the staging arrays (16 bytes per lane, each
+    // wave a share of the pieces), V and dO through registers as fp32; the
+    // caller waits for the copies before its barrier
+    auto stage = [&](int c, bool rev) {
+        const int t0 = c * C, len = min(C, T - t0);
+        constexpr int EK = 16 / (int)sizeof(IO);  // io elements per 16 bytes
+        auto copy_rows = [&](const void* src, int esz, void* dst) {
+            const int per = 16 / esz, np = C * DK / per;
+            for (int p0 = 64 * w; p0 < np; p0 += 256) {
+                const int p = p0 + lane, e = p * per, t = e / DK, i = e % DK;
+                const size_t g = tok_of(t0 + min(t, len - 1)) * DK + i;
+                dma16((const char*)src + g * esz,
+                      lds_u32(dst) + (uint32_t)p0 * 16u);
+            }
+        };
+        copy_rows(a.alpha, 4, &sm.inA[0][0]);
+        if constexpr (!ISO)
+            copy_rows(a.kap, 4, &sm.inP[0][0]);
+        static_assert(2 * C * DK * sizeof(IO) <= sizeof(sm.inK), "staging size");
+        copy_rows(kg, (int)sizeof(IO), &sm.inK[0]);
+        if (rev)
+            copy_rows(qg, (int)sizeof(IO), reinterpret_cast<char*>(&sm.inK[0]) + C * DK * sizeof(IO));
+        (void)EK;
+        if constexpr (ISO)
+            if (tid < C)
+                sm.inP[tid][0] = a.gsc[tok_of(t0 + min(tid, len - 1)) * 4];
+        const bool okr = et < len;
+        const size_t r = tok_of(t0 + min(et, len - 1)) * dv + col0 + ec;
+        float vv[4], oo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            vv[j] = to_f32(vg[r + j]);
+            oo[j] = rev ? to_f32(og[r + j]) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sm.V[et][ec + j] = okr ? vv[j] : 0.f;
+            if (rev)
+                sm.dO[et][ec + j] = okr ? oo[j] : 0.f;
+        }
+        // the copies have landed (and every earlier memory operation of
+        // this wave has completed)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    auto factors = [&](int c, bool rev) {
+        const int t0 = c * C, len = min(C, T - t0);
+        if (chth) {
+            const IO* sk = reinterpret_cast<const IO*>(&sm.inK[0]);
+            float al[C], kk[C], qq[C], kap[C];
+#pragma unroll
+            for (int t = 0; t < C; ++t) {
+                al[t] = sm.inA[t][ch];
+                kk[t] = to_f32(sk[t * DK + ch]);
+                qq[t] = rev ? to_f32(sk[C * DK + t * DK + ch]) : 0.f;
+                kap[t] = ISO ? sm.inP[t][0] : sm.inP[t][ch];
+            }
+#pragma unroll
+            for (int t = 0; t < C; ++t) {
+                const bool ok = t < len;
+                al[t] = ok ? al[t] : 1.f;
+                kk[t] = ok ? kk[t] : 0.f;
+                qq[t] = ok ? qq[t] : 0.f;
+                kap[t] = ok ? (ISO ? kap[t] * kk[t] : kap[t]) : 0.f;
+            }
+            ChanDecay d;
+            chan_decay(al, d);
+#pragma unroll
+            for (int t = 0; t < C; ++t) {
+                const float G = d.g[t + 1];
+                sm.Kb[t][ch] = kk[t] * G;
+                sm.Qb[t][ch] = qq[t] * G;
+                sm.Kt[t][ch] = kap[t] * rcp(G);
+            }
+            sm.cS[ch] = __builtin_amdgcn_ldexpf(1.f, d.m);
+            sm.gL[ch] = d.g[C];
+        }
+    };
+    // M = Kb Kt^T, by waves 2 and 3 over half of the key channels each
+    auto form_M_parts = [&]() {
+        if (w >= 2) {
+            const int k0 = (w - 2) * (DK / 2);
+            f32x4 m = zero4();
+            mmk<DK / 2>(m, &sm.Kb[0][k0], LK, 1, &sm.Kt[0][k0], 1, LK, lane);
+            tile_store(&sm.Mp[w - 2][0][0], LM, m, lane);
+        }
+    };
+    // After form_M_parts and a barrier: wave 0 forms T = (I + M)^-1 with
+    // M = tril(Kb Kt^T, -1) nilpotent, (I + M)^-1 = (I - M)(I + M^2)(I + M^4)
+    // (I + M^8), each factor a 16x16 product on the matrix cores (the powers of
+    // M through LDS); meanwhile waves 1-3 form R = V - Kb (c S0) for the four
+    // column tiles (wave 1 two of them) into mR.
+    auto form_T_and_R = [&]() {
+        if (w == 0) {
+            f32x4 m = tile_load(&sm.Mp[0][0][0], LM, lane) + tile_load(&sm.Mp[1][0][0], LM, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                m[r] = 4 * g4 + r > i16 ? m[r] : 0.f;
+            f32x4 tt;  // I - M
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                tt[r] = (4 * g4 + r == i16 ? 1.f : 0.f) - m[r];
+            f32x4 pw = m;  // M^(2^j)
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                tile_store(&sm.dLm[0][0], LM, pw, lane);
+                wave_lds_sync();
+                f32x4 sq = zero4();
+                mm_acc(sq, &sm.dLm[0][0], LM, 1, pw, lane);  // M^(2^(j+1))
+                wave_lds_sync();
+                tile_store(&sm.dLm[0][0], LM, sq, lane);
+                wave_lds_sync();
+                const f32x4 tp = tt;
+                mm_acc(tt, &sm.dLm[0][0], LM, 1, tp, lane);  // (I + M^(2^(j+1))) tt
+                wave_lds_sync();
+                pw = sq;
+            }
+            tile_store(&sm.Tm[0][0], LM, tt, lane);
+        } else {
+            auto form_R = [&](int n) {
+                f32x4 p = zero4();
+                mmk<DK>(p, &sm.Kb[0][0], LK, 1, &sm.S0[0][16 * n], LC, 1, lane);
+                tile_store(&sm.mR[0][16 * n], LC, tile_load(&sm.V[0][16 * n], LC, lane) - p, lane);
+            };
+            if (w == 1) {
+                form_R(0);
+                form_R(1);
+            } else {
+                form_R(w);
+            }
+        }
+    };
+    // delta = T R for column tile w, into LDS
+    auto form_delta = [&]() {
+        f32x4 d = zero4();
+        mmk<C>(d, &sm.Tm[0][0], LM, 1, &sm.mR[0][16 * w], LC, 1, lane);
+        tile_store(&sm.D[0][16 * w], LC, d, lane);
+    };
+    // the state rows this wave holds: tile (j, n) = channels chw + 16 j + 4 g + r, columns 16 n + i
+    auto state_rows = [&](int j) { return chw + 16 * j; };
+
+    // The carried state (forward pass) and its adjoint (reverse pass) live in
+    // the E array, unscaled, each wave owning the rows of its channels.
+    auto state_init = [&](const float* src) {
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                f32x4 x;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = state_rows(j) + 4 * g4 + r;
+                    x[r] = src ? src[((size_t)bh * DK + row) * dv + col0 + 16 * n + i16] : 0.f;
+                }
+                tile_store(&sm.E[state_rows(j)][16 * n], LC, x, lane);
+            }
+    };
+
+    // ---------------- forward pass: every chunk-start state ----------------
+    state_init(a.S0);
+    for (int c = 0; c < nch; ++c) {
+        stage(c, false);
+        barrier();  // inputs staged, V
+        factors(c, false);
+        barrier();  // factors, cS
+        form_M_parts();
+        // c S0 into LDS; the chunk-start state to the workspace
+        float* ckc = ck_wg + (size_t)c * (DK * NC);
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                f32x4 x = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = state_rows(j) + 4 * g4 + r;
+                    ckc[row * NC + 16 * n + i16] = x[r];
+                    x[r] *= sm.cS[row];
+                }
+                tile_store(&sm.S0[state_rows(j)][16 * n], LC, x, lane);
+            }
+        barrier();  // M parts, c S0
+        form_T_and_R();
+        barrier();  // T, R
+        form_delta();
+        barrier();  // delta
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                // S_C = G'_15 (c S0 + Kt^T delta)
+                f32x4 x = tile_load(&sm.S0[state_rows(j)][16 * n], LC, lane);
+                mmk<C>(x, &sm.Kt[0][state_rows(j)], 1, LK, &sm.D[0][16 * n], LC, 1, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x[r] *= sm.gL[state_rows(j) + 4 * g4 + r];
+                tile_store(&sm.E[state_rows(j)][16 * n], LC, x, lane);
+            }
+        barrier();  // readers of this chunk's factors done
+    }
+
+    // every chunk-start state stored is visible to the whole workgroup
+    __syncthreads();
+
+    // ---------------- reverse pass ----------------
+    state_init(a.gS_T);
+    for (int c = nch - 1; c >= 0; --c) {
+        const int t0 = c * C, len = min(C, T - t0);
+        {
+            // the chunk-start state's loads go out first, so that their
+            // latency overlaps the inputs' loads
+            const float4* src = reinterpret_cast<const float4*>(ck_wg + (size_t)c * (DK * NC));
+            float4 ck[NCK];
+#pragma unroll
+            for (int j = 0; j < NCK; ++j)
+                ck[j] = src[tid + 256 * j];
+            stage(c, true);
+            barrier();  // inputs staged, V, dO
+            factors(c, true);
+            barrier();  // factors, cS, gL
+#pragma unroll
+            for (int j = 0; j < NCK; ++j) {
+                const int e = 4 * (tid + 256 * j), row = e / NC, cc = e % NC;
+                const float cs = sm.cS[row];
+                sm.S0[row][cc] = ck[j].x * cs;
+                sm.S0[row][cc + 1] = ck[j].y * cs;
+                sm.S0[row][cc + 2] = ck[j].z * cs;
+                sm.S0[row][cc + 3] = ck[j].w * cs;
+            }
+        }
+        // E = G'_15 dS_C, in place (this wave's rows)
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                f32x4 x = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x[r] *= sm.gL[state_rows(j) + 4 * g4 + r];
+                tile_store(&sm.E[state_rows(j)][16 * n], LC, x, lane);
+            }
+        form_M_parts();
+        if (w == 1) {
+            f32x4 m = zero4();
+            mmk<DK>(m, &sm.Qb[0][0], LK, 1, &sm.Kt[0][0], 1, LK, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                sm.Am[t][i16] = t >= i16 ? m[r] : 0.f;
+            }
+        }
+        barrier();  // c S0, M parts, A, E
+        form_T_and_R();
+        barrier();  // T, R
+        form_delta();
+        barrier();  // delta
+        {
+            // rowsum over this block's columns of dS_C . X = (E . X) / G'_15,
+            // X = c S0 + Kt^T delta: the partial of the last token's dG (array 3)
+#pragma unroll
+            for (int j = 0; j < CT; ++j) {
+                float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int n = 0; n < 4; ++n) {
+                    f32x4 x = tile_load(&sm.S0[state_rows(j)][16 * n], LC, lane);
+                    mmk<C>(x, &sm.Kt[0][state_rows(j)], 1, LK, &sm.D[0][16 * n], LC, 1, lane);
+                    const f32x4 e = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        rs[r] = fmaf(e[r], x[r], rs[r]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = state_rows(j) + 4 * g4 + r;
+                    const float sum = row16_sum(rs[r]) * rcp(sm.gL[row]);
+                    if (i16 == 0)
+                        a.part[3 * ks + ((size_t)blk * ntok + tok_of(t0 + len - 1)) * DK + row] = sum;
+                }
+            }
+            // ddelta = Kt E + A^T dO, dR = T^T ddelta (column tile w)
+            f32x4 dd = zero4();
+            mmk<DK>(dd, &sm.Kt[0][0], LK, 1, &sm.E[0][16 * w], LC, 1, lane);
+            mmk<C>(dd, &sm.Am[0][0], 1, LM, &sm.dO[0][16 * w], LC, 1, lane);
+            f32x4 dR = zero4();
+            mm_acc(dR, &sm.Tm[0][0], 1, LM, dd, lane);
+            tile_store(&sm.mR[0][16 * w], LC, -dR, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                if (t < len)
+                    dvg[tok_of(t0 + t) * dv + col0 + 16 * w + i16] = from_f32<IO>(dR[r]);
+            }
+        }
+        barrier();  // -dR; every wave's reads of all E rows done
+        // delta E^T for this wave's channels (their E rows, before the update)
+        f32x4 gKt[CT];
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            gKt[j] = zero4();
+            mmk<NC>(gKt[j], &sm.D[0][0], LC, 1, &sm.E[state_rows(j)][0], 1, LC, lane);
+        }
+        // dS0' = E + Qb^T dO + Kb^T (-dR), then dS0 = c dS0', carried in E
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                f32x4 x = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
+                mmk<C>(x, &sm.Qb[0][state_rows(j)], 1, LK, &sm.dO[0][16 * n], LC, 1, lane);
+                mmk<C>(x, &sm.Kb[0][state_rows(j)], 1, LK, &sm.mR[0][16 * n], LC, 1, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x[r] *= sm.cS[state_rows(j) + 4 * g4 + r];
+                tile_store(&sm.E[state_rows(j)][16 * n], LC, x, lane);
+            }
+        if (w == 0) {
+            f32x4 m = zero4();  // -dR delta^T, strictly lower
+            mmk<NC>(m, &sm.mR[0][0], LC, 1, &sm.D[0][0], 1, LC, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                sm.dLm[t][i16] = t > i16 ? m[r] : 0.f;
+            }
+        } else if (w == 1) {
+            f32x4 m = zero4();  // dO delta^T, lower with the diagonal
+            mmk<NC>(m, &sm.dO[0][0], LC, 1, &sm.D[0][0], 1, LC, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                sm.dAm[t][i16] = t >= i16 ? m[r] : 0.f;
+            }
+        }
+        barrier();  // dL, dA
+        // the rest of the row-space products for this wave's channels, one
+        // 16-channel tile at a time, and their partials (arrays 0, 1, 2:
+        // dKb', dQb', dKt')
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            const int c0 = state_rows(j);
+            f32x4 gKb = zero4(), gQb = zero4();
+            mmk<NC>(gKb, &sm.mR[0][0], LC, 1, &sm.S0[c0][0], 1, LC, lane);  // -dR (c S0)^T
+            mmk<C>(gKb, &sm.dLm[0][0], LM, 1, &sm.Kt[0][c0], LK, 1, lane);  // + dL Kt
+            mmk<NC>(gQb, &sm.dO[0][0], LC, 1, &sm.S0[c0][0], 1, LC, lane);  // dO (c S0)^T
+            mmk<C>(gQb, &sm.dAm[0][0], LM, 1, &sm.Kt[0][c0], LK, 1, lane);  // + dA Kt
+            mmk<C>(gKt[j], &sm.dLm[0][0], 1, LM, &sm.Kb[0][c0], LK, 1, lane);  // + dL^T Kb
+            mmk<C>(gKt[j], &sm.dAm[0][0], 1, LM, &sm.Qb[0][c0], LK, 1, lane);  // + dA^T Qb
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                if (t < len) {
+                    float* pp = a.part + ((size_t)blk * ntok + tok_of(t0 + t)) * DK + c0 + i16;
+                    pp[0] = gKb[r];
+                    pp[ks] = gQb[r];
+                    pp[2 * ks] = gKt[j][r];
+                }
+            }
+        }
+        barrier();  // the next chunk's inputs overwrite the LDS arrays
+    }
+    if (a.gS0) {
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const f32x4 x = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = state_rows(j) + 4 * g4 + r;
+                    a.gS0[((size_t)bh * DK + row) * dv + col0 + 16 * n + i16] = x[r];
+                }
+            }
+    }
+}
+
+// Sum of the column blocks' partials and the per-channel finishing, one
+// thread per (chunk, key channel): with G' recomputed from alpha by the rule
+// the memory kernel used, and the summed dKb', dQb', dKt' and rowsum term R,
+//   dq = dQb' G',  dk (memory) = dKb' G',  kapbar = dKt' / G',
+//   dG'_t = dKb' k + dQb' q - kapbar Kt'  (+ R at the chunk's last token),
+//   dalpha_s = G'_{s-1} W_s,  W_s = dG'_s + alpha_{s+1} W_{s+1}  (zero where the floor raised alpha).
+// dq is written in the io type; kapbar, dk and dalpha go to block 0 of
+// arrays 1, 2, 3 (where the gain backward reads them), after this thread
+// has read every partial of its own tokens there.
+template <typename IO, bool ISO, int DK>
+__global__ __launch_bounds__(DK) void kdn_bwd_chunk_finish_kernel(BwdArgs args, int nblk)
+{
+    const BwdArgs a = args;
+    const int nch = (a.T + C - 1) / C;
+    const int bh = blockIdx.x / nch, c = blockIdx.x % nch, ch = threadIdx.x;
+    const int b = bh / a.H, h = bh % a.H;
+    const int t0 = c * C, len = min(C, a.T - t0);
+    const size_t ntok = (size_t)a.B * a.T * a.H, ks = (size_t)nblk * ntok * DK;
+    auto tok_of = [&](int t) { return ((size_t)b * a.T + t0 + t) * a.H + h; };
+    const IO* kg = reinterpret_cast<const IO*>(a.k);
+    const IO* qg = reinterpret_cast<const IO*>(a.q);
+    float al[C], kk[C], qq[C], kap[C];
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+        const size_t e = tok_of(min(t, len - 1)) * DK + ch;
+        al[t] = a.alpha[e];
+        kk[t] = to_f32(kg[e]);
+        qq[t] = to_f32(qg[e]);
+        kap[t] = ISO ? a.gsc[tok_of(min(t, len - 1)) * 4] : a.kap[e];
+    }
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+        const bool ok = t < len;
+        al[t] = ok ? al[t] : 1.f;
+        kk[t] = ok ? kk[t] : 0.f;
+        qq[t] = ok ? qq[t] : 0.f;
+        kap[t] = ok ? (ISO ? kap[t] * kk[t] : kap[t]) : 0.f;
+    }
+    ChanDecay d;
+    chan_decay(al, d);
+    float dG[C];
+    IO* dq = reinterpret_cast<IO*>(a.gq);
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+        dG[t] = 0.f;
+        if (t < len) {
+            const size_t e = tok_of(t) * DK + ch;
+            float skb = 0.f, sqb = 0.f, skt = 0.f, srs = 0.f;
+            for (int bl = 0; bl < nblk; ++bl) {
+                const float* p = a.part + (size_t)bl * ntok * DK + e;
+                skb += p[0];
+                sqb += p[ks];
+                skt += p[2 * ks];
+                if (t == len - 1)
+                    srs += p[3 * ks];
+            }
+            const float G = d.g[t + 1], iG = rcp(G);
+            const float kbar = skt * iG;
+            dG[t] = skb * kk[t] + sqb * qq[t] - kbar * (kap[t] * iG) + srs;
+            dq[e] = from_f32<IO>(sqb * G);
+            a.part[ks + e] = kbar;
+            a.part[2 * ks + e] = skb * G;
+        }
+    }
+    float W = 0.f;
+#pragma unroll
+    for (int s = C - 1; s >= 0; --s) {
+        if (s < len) {
+            W = dG[s] + (s + 1 < len ? d.alf[s + 1] * W : 0.f);
+            a.part[3 * ks + tok_of(s) * DK + ch] = ((d.raised >> s) & 1u) ? 0.f : d.g[s] * W;
+        }
+    }
+}
+
+template <typename IO, bool ISO, int DK>
+static hipError_t launch_t(const BwdArgs& a, hipStream_t stream)
+{
+    auto kern = kdn_bwd_chunk_kernel<IO, ISO, DK>;
+    const size_t smem = sizeof(Smem<DK>);
+    hipError_t e = set_lds_limit_once(kern, smem);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(kern, dim3(a.dv / NC, a.B * a.H), dim3(256), smem, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int nch = (a.T + C - 1) / C;
+    if (nch > 0) {
+        hipLaunchKernelGGL((kdn_bwd_chunk_finish_kernel<IO, ISO, DK>), dim3(a.B * a.H * nch),
+                           dim3(DK), 0, stream, a, a.dv / NC);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace cbwd
+
+hipError_t launch_bwd_chunk_mem(const BwdArgs& a, bool iso, int io_dtype, hipStream_t stream)
+{
+    using namespace cbwd;
+    const bool bf = io_dtype == 1;
+    if (a.dk == 128) {
+        if (iso)
+            return bf ? launch_t<bf16, true, 128>(a, stream) : launch_t<float, true, 128>(a, stream);
+        return bf ? launch_t<bf16, false, 128>(a, stream) : launch_t<float, false, 128>(a, stream);
+    }
+    if (iso)
+        return bf ? launch_t<bf16, true, 64>(a, stream) : launch_t<float, true, 64>(a, stream);
+    return bf ? launch_t<bf16, false, 64>(a, stream) : launch_t<float, false, 64>(a, stream);
+}
+
+}  // namespace kdn

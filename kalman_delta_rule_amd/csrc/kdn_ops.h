@@ -113,6 +113,11 @@ size_t gain_workspace_floats(bool iso, int B, int T, int H, int dk);
 size_t gain_static_scratch_floats();
 hipError_t gain_static_scratch(float** ptr);
 hipError_t launch_gain_scan(const GainArgs& a, bool iso, int io_dtype, hipStream_t stream);
+// the backward's memory part runs in 16-token chunks on the matrix cores
+// (kdn_bwd_chunk.hip) for these shapes, token by token otherwise
+bool bwd_chunked(int dk, int dv);
+constexpr int BWD_CHUNK_COLS = 64;  // value columns per chunked memory workgroup
+hipError_t launch_bwd_chunk_mem(const BwdArgs& a, bool iso, int io_dtype, hipStream_t stream);
 size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv);
 void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws);
 hipError_t launch_bwd(const BwdArgs& a, bool iso, int io_dtype, hipStream_t stream);

@@ -52,10 +52,17 @@ size_t seqpar_workspace_floats(bool iso, int B, int T, int H, int dk, int dv, in
 }
 
 // ------------------------------------------------------------- backward
+bool bwd_chunked(int dk, int dv)
+{
+    return (dk == 64 || dk == 128) && dv >= BWD_CHUNK_COLS && dv % BWD_CHUNK_COLS == 0;
+}
+
 size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv)
 {
     const size_t ntok = (size_t)B * T * H, bh = (size_t)B * H;
-    const size_t nch = ((size_t)T + BWD_L - 1) / BWD_L, nblk = (size_t)dv / BWD_COLS;
+    const bool chunked = bwd_chunked(dk, dv);
+    const size_t nch = ((size_t)T + BWD_L - 1) / BWD_L,
+                 nblk = (size_t)dv / (chunked ? BWD_CHUNK_COLS : BWD_COLS);
     size_t n = 0;
     if (iso)
         n += round64(ntok * 4);
@@ -66,7 +73,8 @@ size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv)
     n += round64(bh * ngc * width * 2) + round64(bh * ngc * width) + round64(ntok) +
          round64(bh * ngc);                  // gain backward: summaries, carries, dbar, mu parts
     n += round64(bh * nch * dk * dv);        // checkpoints
-    n += round64(ntok * dv);                 // innovations
+    if (!chunked)
+        n += round64(ntok * dv);             // innovations
     n += round64(4 * nblk * ntok * dk);      // partials
     return n;
 }
@@ -74,7 +82,8 @@ size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv)
 void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws)
 {
     const size_t ntok = (size_t)a.B * a.T * a.H, bh = (size_t)a.B * a.H;
-    const size_t nch = ((size_t)a.T + BWD_L - 1) / BWD_L, nblk = (size_t)a.dv / BWD_COLS;
+    const bool chunked = bwd_chunked(a.dk, a.dv);
+    const size_t nch = ((size_t)a.T + BWD_L - 1) / BWD_L;
     float* p = ws;
     a.kap = a.pprev = a.dd = a.gsc = nullptr;
     if (iso) {
@@ -101,8 +110,11 @@ void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws)
     p += round64(bh * ngc);
     a.ckpt = p;
     p += round64(bh * nch * a.dk * a.dv);
-    a.dlt = p;
-    p += round64(ntok * a.dv);
+    a.dlt = nullptr;
+    if (!chunked) {
+        a.dlt = p;
+        p += round64(ntok * a.dv);
+    }
     a.part = p;
 }
 

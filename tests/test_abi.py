@@ -354,21 +354,26 @@ def test_bwd_validation(L):
     assert bwd(ws_bytes=16) == -3 and "workspace" in msg()
     assert bwd(ws=base["ws"] + 4) == -1 and "16-byte" in msg()
     # workspace: gain pieces, the gain scan's summaries and carries, the state
-    # every 16th token, every token's innovations, 4 partial row sums per
-    # 16-column block
-    B, T, H, dk, dv = 2, 40, 3, 128, 64
-    ntok, nch, nblk = B * T * H, 3, dv // 16
+    # every 16th token, 4 partial row sums per value-column block (64 columns
+    # for the chunked memory backward, dv a multiple of 64; 16 columns and
+    # every token's innovations for the token-serial one)
+    B, T, H, dk = 2, 40, 3, 128
+    ntok, nch = B * T * H, 3
     r64 = lambda n: (n + 63) // 64 * 64
-    common = r64(B * H * nch * dk * dv) + r64(ntok * dv) + r64(4 * nblk * ntok * dk)
-    scan = lambda width: r64(B * H * 1 * width * 5)  # the gain scan: one 64-token chunk
-    # the gain backward's scan: (A, B) and carry per chunk and width, a
-    # scalar per token, an information-scale part per chunk
-    grad = lambda width: r64(B * H * width * 2) + r64(B * H * width) + r64(ntok) + r64(B * H)
-    diag = 2 * r64(ntok * dk) + r64(ntok) + scan(dk) + grad(dk) + common
-    iso = r64(ntok * 4) + scan(1) + grad(1) + common
-    assert L.kdn_bwd_workspace_size(0, B, T, H, dk, dv) == 4 * diag
-    assert L.kdn_bwd_workspace_size(1, B, T, H, dk, dv) == 4 * iso
-    assert L.kdn_bwd_workspace_size(0, B, 0, H, dk, dv) == 0
+    for dv in (64, 128, 32, 48):
+        chunked = dv % 64 == 0
+        nblk = dv // (64 if chunked else 16)
+        common = (r64(B * H * nch * dk * dv) + (0 if chunked else r64(ntok * dv))
+                  + r64(4 * nblk * ntok * dk))
+        scan = lambda width: r64(B * H * 1 * width * 5)  # the gain scan: one 64-token chunk
+        # the gain backward's scan: (A, B) and carry per chunk and width, a
+        # scalar per token, an information-scale part per chunk
+        grad = lambda width: r64(B * H * width * 2) + r64(B * H * width) + r64(ntok) + r64(B * H)
+        diag = 2 * r64(ntok * dk) + r64(ntok) + scan(dk) + grad(dk) + common
+        iso = r64(ntok * 4) + scan(1) + grad(1) + common
+        assert L.kdn_bwd_workspace_size(0, B, T, H, dk, dv) == 4 * diag, dv
+        assert L.kdn_bwd_workspace_size(1, B, T, H, dk, dv) == 4 * iso, dv
+    assert L.kdn_bwd_workspace_size(0, B, 0, H, dk, 64) == 0
 
 
 def test_fwd_preact_validation(L):

@@ -182,7 +182,7 @@ def test_bwd_config3_long_full(ora):
     _bwd_full(ora, 3, 1, heads=[(0, 11)])
 
 
-@pytest.mark.parametrize("regime", ["mu0", "slow_decay", "fast_decay", "noisy"])
+@pytest.mark.parametrize("regime", ["mu0", "slow_decay", "fast_decay", "noisy", "strong_decay"])
 def test_bwd_regimes(ora, regime):
     # the backward away from the default gate draws: no information scaling
     # (mu = 0), decay close to 1 (long memory, large states), fast decay, and
@@ -198,6 +198,13 @@ def test_bwd_regimes(ora, regime):
         x["omega"] = (1e-3 * x["omega"]).astype(np.float32)
     elif regime == "fast_decay":
         x["alpha"] = (0.3 + 0.3 * rng.random(x["alpha"].shape)).astype(np.float32)
+    elif regime == "strong_decay":
+        # every fourth channel decays by 3e-4 .. 1e-2 per token: 16-token
+        # products of 2^-192 .. 2^-106, so the chunked memory backward takes
+        # its decay reference (no floor) on those channels
+        sel = (np.arange(dk) % 4 == 1)[None, None, None, :]
+        strong = 10.0 ** rng.uniform(-3.5, -2.0, x["alpha"].shape)
+        x["alpha"] = np.where(sel, strong, x["alpha"]).astype(np.float32)
     else:
         x["r"] = (20.0 + 10.0 * rng.random(x["r"].shape)).astype(np.float32)
     _check(_run(variant, io, x, mu=mu), _oracle(ora, variant, x, mu=mu), io, regime)
