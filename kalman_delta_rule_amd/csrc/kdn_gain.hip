@@ -22,7 +22,9 @@
 //           map of a scalar per chunk), giving every chunk's entry variance
 //           and the final variance.
 //   pass 3  (only when kappa is requested) replay each chunk from its entry
-//           variance: p^_t, z_t = sum_i p^_t,i k_t,i^2, kappa = p^ k/(r + z).
+//           variance: p^_t, z_t = sum_i p^_t,i k_t,i^2, kappa = p^ k/(r + z);
+//           Diagonal takes its chunk in four 16-token pieces, so that its LDS
+//           tile of p^ k^2 stays small and more workgroups share a compute unit.
 // Summaries are stored chunk-major, [B H][chunk][width][4] (one 16-byte map per
 // channel), so that pass 1 writes whole rows and pass 2 reads them with lanes
 // on adjacent channels.
@@ -242,73 +244,83 @@ __global__ __launch_bounds__(64 * CARRY_WAVES) void gain_carry(GainArgs a, int w
 template <typename IO, int DK>
 __global__ __launch_bounds__(DK) void gain_replay_diag(GainArgs a, int nchunks)
 {
-    // s_w[t][i] = p^_t,i k_t,i^2 (rows padded to keep 16-byte reads aligned);
-    // z_t is the sum of row t, taken by DK / 64 lanes per token
-    constexpr int LDW = DK + 4, NH = DK / 64;
-    __shared__ __align__(16) float s_w[GC][LDW];
-    __shared__ float s_zp[NH][GC];
+    // The chunk in NQ pieces of HT tokens (a small LDS tile, so that more
+    // workgroups fit on a compute unit): s_w[t][i] = p^_t,i k_t,i^2 (rows
+    // padded to keep 16-byte reads aligned); z_t is the sum of row t, taken
+    // by NP lanes per token
+    constexpr int NQ = 4, HT = GC / NQ, LDW = DK + 4, NP = DK / HT, CPP = DK / NP;
+    static_assert(NP * HT == DK, "one lane per (part, token) in the reduction");
+    __shared__ __align__(16) float s_w[HT][LDW];
+    __shared__ float s_zp[NP][HT];
     const int bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
     const int b = bh / a.H, h = bh % a.H, i = threadIdx.x;
     const int t0 = c * GC, n_valid = min(GC, a.T - t0);
     const IO* kg = reinterpret_cast<const IO*>(a.k);
     float p = a.carry[((size_t)bh * nchunks + c) * DK + i];
-    float num[GC];  // p^_t k_t of this lane's channel (kappa's numerator)
     // eight tokens' gates are loaded before the chain (and the pprev stores,
     // which the compiler cannot move loads across) consume them
     constexpr int PF = 8;
 #pragma unroll
-    for (int tb = 0; tb < GC; tb += PF) {
-        float al8[PF], w8[PF], kv8[PF], r8[PF];
+    for (int hf = 0; hf < NQ; ++hf) {
+        float num[HT];  // p^_t k_t of this lane's channel (kappa's numerator)
 #pragma unroll
-        for (int e = 0; e < PF; ++e) {
-            const size_t tok = ((size_t)b * a.T + t0 + min(tb + e, n_valid - 1)) * a.H + h;
-            al8[e] = a.alpha[tok * DK + i];
-            w8[e] = a.omega[tok * DK + i];
-            kv8[e] = to_f32(kg[tok * DK + i]);
-            r8[e] = a.r[tok];
+        for (int tb = 0; tb < HT; tb += PF) {
+            float al8[PF], w8[PF], kv8[PF], r8[PF];
+#pragma unroll
+            for (int e = 0; e < PF; ++e) {
+                const int t = hf * HT + tb + e;
+                const size_t tok = ((size_t)b * a.T + t0 + min(t, n_valid - 1)) * a.H + h;
+                al8[e] = a.alpha[tok * DK + i];
+                w8[e] = a.omega[tok * DK + i];
+                kv8[e] = to_f32(kg[tok * DK + i]);
+                r8[e] = a.r[tok];
+            }
+#pragma unroll
+            for (int e = 0; e < PF; ++e) {
+                const int tl = tb + e, t = hf * HT + tl;
+                float ph = 0.f, kv = 0.f;
+                if (t < n_valid) {
+                    const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
+                    kv = kv8[e];
+                    ph = al8[e] * al8[e] * p + w8[e];
+                    const float u = (mu_of(a, h) / r8[e]) * kv * kv;
+                    if (a.pprev)
+                        a.pprev[tok * DK + i] = p;
+                    p = ph * rcp(1.f + u * ph);
+                }
+                num[tl] = ph * kv;
+                s_w[tl][i] = num[tl] * kv;
+            }
         }
+        __syncthreads();
+        {
+            // lane (part, t): channels CPP part .. CPP part + CPP - 1 of token t
+            const int t = i % HT, part = i / HT;
+            {
+                const float* row = &s_w[t][CPP * part];
+                float z = 0.f;
 #pragma unroll
-        for (int e = 0; e < PF; ++e) {
-            const int t = tb + e;
-            float ph = 0.f, kv = 0.f;
+                for (int j = 0; j < CPP; j += 4) {
+                    const float4 w4 = *reinterpret_cast<const float4*>(row + j);
+                    z += (w4.x + w4.y) + (w4.z + w4.w);
+                }
+                s_zp[part][t] = z;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int tl = 0; tl < HT; ++tl) {
+            const int t = hf * HT + tl;
             if (t < n_valid) {
                 const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
-                kv = kv8[e];
-                ph = al8[e] * al8[e] * p + w8[e];
-                const float u = (mu_of(a, h) / r8[e]) * kv * kv;
-                if (a.pprev)
-                    a.pprev[tok * DK + i] = p;
-                p = ph * rcp(1.f + u * ph);
+                float z = s_zp[0][tl];
+#pragma unroll
+                for (int q = 1; q < NP; ++q)
+                    z += s_zp[q][tl];
+                a.kappa[tok * DK + i] = num[tl] * rcp(a.r[tok] + z);
+                if (a.dd && i == 0)
+                    a.dd[tok] = a.r[tok] + z;
             }
-            num[t] = ph * kv;
-            s_w[t][i] = num[t] * kv;
-        }
-    }
-    __syncthreads();
-    {
-        // lane (part, t): channels 64 part .. 64 part + 63 of token t
-        const int t = i % GC, part = i / GC;
-        const float* row = &s_w[t][64 * part];
-        float z = 0.f;
-#pragma unroll
-        for (int j = 0; j < 64; j += 4) {
-            const float4 w4 = *reinterpret_cast<const float4*>(row + j);
-            z += (w4.x + w4.y) + (w4.z + w4.w);
-        }
-        s_zp[part][t] = z;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < GC; ++t) {
-        if (t < n_valid) {
-            const size_t tok = ((size_t)b * a.T + t0 + t) * a.H + h;
-            float z = s_zp[0][t];
-#pragma unroll
-            for (int q = 1; q < NH; ++q)
-                z += s_zp[q][t];
-            a.kappa[tok * DK + i] = num[t] * rcp(a.r[tok] + z);
-            if (a.dd && i == 0)
-                a.dd[tok] = a.r[tok] + z;
         }
     }
 }
