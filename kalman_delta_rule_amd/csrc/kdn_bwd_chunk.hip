@@ -126,24 +126,30 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p)
 // acc[m][n] += sum_k A(m, k) B(k, n) over K (multiple of 4), operands in LDS:
 // A(m, k) = A[m am + k ak], B(k, n) = B[k bk + n bn]; the 16x16x4 product
 // takes A(lane & 15, k0 + (lane >> 4)) and B(k0 + (lane >> 4), lane & 15).
-// The operands are read sixteen steps at a time, ahead of their products.
+// Software-pipelined: the operands of step s + D are read before the
+// product of step s is issued (scheduling barriers keep that order), so each
+// product finds its operands landed; at most 2 D LDS reads are in flight,
+// within the 4-bit count of outstanding LDS operations.
 template <int K>
 __device__ __forceinline__ void mmk(f32x4& acc, const float* A, int am, int ak, const float* B,
                                     int bk, int bn, int lane)
 {
     const int i = lane & 15, g = lane >> 4;
-    constexpr int NS = K / 4, BS = NS < 16 ? NS : 16;
+    constexpr int NS = K / 4, D = NS < 6 ? NS : 6;
+    float a[NS], b[NS];
 #pragma unroll
-    for (int s0 = 0; s0 < NS; s0 += BS) {
-        float a[BS], b[BS];
+    for (int s = 0; s < D; ++s) {
+        a[s] = A[i * am + (4 * s + g) * ak];
+        b[s] = B[(4 * s + g) * bk + i * bn];
+    }
 #pragma unroll
-        for (int s = 0; s < BS; ++s) {
-            a[s] = A[i * am + (4 * (s0 + s) + g) * ak];
-            b[s] = B[(4 * (s0 + s) + g) * bk + i * bn];
+    for (int s = 0; s < NS; ++s) {
+        if (s + D < NS) {
+            a[s + D] = A[i * am + (4 * (s + D) + g) * ak];
+            b[s + D] = B[(4 * (s + D) + g) * bk + i * bn];
         }
-#pragma unroll
-        for (int s = 0; s < BS; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
     }
 }
 
