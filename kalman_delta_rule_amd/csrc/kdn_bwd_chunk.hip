@@ -40,6 +40,8 @@
 #include "kdn_internal.h"
 #include "kdn_ops.h"
 
+#include <type_traits>
+
 namespace kdn {
 namespace cbwd {
 
@@ -59,11 +61,12 @@ struct Smem {
     float V[C][LC];
     float dO[C][LC];
     float D[C][LC];    // delta
-    float mR[C][LC];   // -dR
+    float mR[C][LC];   // a partial of Kb (c S0) while delta is formed, then -dR
+    float Rp[2][C][LC];  // the other two partials of Kb (c S0)
     float Tm[C][LM];
     float Am[C][LM];
     float dLm[C][LM];  // also the powers of M while T is formed
-    float dAm[C][LM];
+    float dAm[C][LM];  // also half of Qb Kt^T while A is formed
     float Mp[2][C][LM];  // Kb Kt^T over each half of the key channels
     float cS[DK];      // c per channel
     float gL[DK];      // G'_15 per channel
@@ -106,21 +109,6 @@ __device__ __forceinline__ void chan_decay(const float (&al)[C], ChanDecay& d)
         G *= ad;
         d.g[t + 1] = G;
     }
-}
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
-// Direct global -> LDS copy: lane l's 16 bytes from its own global address
-// land at LDS byte address lds + 16 l (lds uniform); completion is tracked by
-// vmcnt.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds)
-{
-    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(size_t)lds, 16, 0, 0);
-}
-__device__ __forceinline__ uint32_t lds_u32(const void* p)
-{
-    return (uint32_t)(size_t)(const lds_void_t*)p;
 }
 
 // acc[m][n] += sum_k A(m, k) B(k, n) over K (multiple of 4), operands in LDS:
@@ -217,6 +205,37 @@ __device__ __forceinline__ void barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// A row-major [token][channel] array of a chunk in 16-byte pieces, NP of
+// them, dealt to the 256 threads: thread (w, lane) takes pieces
+// 64 w + 256 j + lane.  rows_load reads them from global memory into
+// registers (row(e) gives the global element index of element e of the
+// chunk), rows_store writes them to LDS in the same row-major order.  The
+// loads are unconditional, so that the pieces stay in registers.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int NP, int NR, typename Row>
+__device__ __forceinline__ void rows_load(u32x4 (&dst)[NR], const void* src, int esz, int w,
+                                          int lane, Row row)
+{
+    const int per = 16 / esz;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        // a wave past the last piece loads the last piece (and stores nothing)
+        const int p = min(64 * w + 256 * j + lane, NP - 1);
+        dst[j] = *reinterpret_cast<const u32x4*>((const char*)src + row(p * per) * esz);
+    }
+}
+template <int NP, int NR>
+__device__ __forceinline__ void rows_store(void* dst, const u32x4 (&src)[NR], int w, int lane)
+{
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        const int p0 = 64 * w + 256 * j;
+        if (p0 < NP)
+            reinterpret_cast<u32x4*>(dst)[p0 + lane] = src[j];
+    }
+}
+
 template <typename IO, bool ISO, int DK>
 __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
 {
@@ -250,50 +269,64 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     const int ch = tid;
     const int et = (tid * 4) / NC, ec = (tid * 4) % NC;  // this thread's 4 elements of a [C][NC] block
 
-    // the chunk's inputs: the rows of alpha, kappa, k and q copied straight
-    // from global memory into the staging arrays (16 bytes per lane, each
-    // wave a share of the pieces), V and dO through registers as fp32; the
-    // caller waits for the copies before its barrier
-    auto stage = [&](int c, bool rev) {
+    // The chunk's inputs, loaded one chunk ahead into registers (16 bytes
+    // per lane and piece of a row-major [token][channel] array, each wave a
+    // share of the pieces), as soon as the factors of the chunk before have
+    // read the staging arrays, and written to LDS at the start of their
+    // chunk.  (A direct global -> LDS copy would make every later LDS access
+    // of the wave wait for it: the compiler cannot tell the copy's LDS
+    // destination from the arrays the chunk works on.)
+    constexpr int NPA = C * DK * 4 / 16, NPK = C * DK * (int)sizeof(IO) / 16;  // pieces per array
+    constexpr int RA = (NPA + 255) / 256, RK = (NPK + 255) / 256;              // per lane
+    u32x4 ra[RA], rp[RA], rk[RK], rq[RK];
+    // four consecutive io elements of V and dO, kept packed until they land
+    // (unpacking at the load would wait for it)
+    using Raw4 = typename std::conditional<sizeof(IO) == 2, u32x2, u32x4>::type;
+    auto raw_f32 = [](const Raw4& x, int j) {
+        if constexpr (sizeof(IO) == 2)
+            return __uint_as_float((j & 1) ? (x[j >> 1] & 0xffff0000u) : (x[j >> 1] << 16));
+        else
+            return __uint_as_float(x[j]);
+    };
+    Raw4 vraw, oraw;
+    float braw = 0.f;
+    bool vok = false;
+    auto issue = [&](int c, bool rev) {
         const int t0 = c * C, len = min(C, T - t0);
-        constexpr int EK = 16 / (int)sizeof(IO);  // io elements per 16 bytes
-        auto copy_rows = [&](const void* src, int esz, void* dst) {
-            const int per = 16 / esz, np = C * DK / per;
-            for (int p0 = 64 * w; p0 < np; p0 += 256) {
-                const int p = p0 + lane, e = p * per, t = e / DK, i = e % DK;
-                const size_t g = tok_of(t0 + min(t, len - 1)) * DK + i;
-                dma16((const char*)src + g * esz,
-                      lds_u32(dst) + (uint32_t)p0 * 16u);
-            }
-        };
-        copy_rows(a.alpha, 4, &sm.inA[0][0]);
+        auto row = [&](int e) { return tok_of(t0 + min(e / DK, len - 1)) * DK + e % DK; };
+        rows_load<NPA>(ra, a.alpha, 4, w, lane, row);
         if constexpr (!ISO)
-            copy_rows(a.kap, 4, &sm.inP[0][0]);
+            rows_load<NPA>(rp, a.kap, 4, w, lane, row);
         static_assert(2 * C * DK * sizeof(IO) <= sizeof(sm.inK), "staging size");
-        copy_rows(kg, (int)sizeof(IO), &sm.inK[0]);
+        rows_load<NPK>(rk, kg, (int)sizeof(IO), w, lane, row);
         if (rev)
-            copy_rows(qg, (int)sizeof(IO), reinterpret_cast<char*>(&sm.inK[0]) + C * DK * sizeof(IO));
-        (void)EK;
+            rows_load<NPK>(rq, qg, (int)sizeof(IO), w, lane, row);
         if constexpr (ISO)
             if (tid < C)
-                sm.inP[tid][0] = a.gsc[tok_of(t0 + min(tid, len - 1)) * 4];
-        const bool okr = et < len;
+                braw = a.gsc[tok_of(t0 + min(tid, len - 1)) * 4];
+        vok = et < len;
         const size_t r = tok_of(t0 + min(et, len - 1)) * dv + col0 + ec;
-        float vv[4], oo[4];
+        vraw = *reinterpret_cast<const Raw4*>(vg + r);
+        if (rev)
+            oraw = *reinterpret_cast<const Raw4*>(og + r);
+    };
+    // the issued inputs into LDS (V and dO as fp32); the caller's barrier follows
+    auto land = [&](bool rev) {
+        rows_store<NPA>(&sm.inA[0][0], ra, w, lane);
+        if constexpr (!ISO)
+            rows_store<NPA>(&sm.inP[0][0], rp, w, lane);
+        rows_store<NPK>(&sm.inK[0], rk, w, lane);
+        if (rev)
+            rows_store<NPK>(reinterpret_cast<char*>(&sm.inK[0]) + C * DK * sizeof(IO), rq, w, lane);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            vv[j] = to_f32(vg[r + j]);
-            oo[j] = rev ? to_f32(og[r + j]) : 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sm.V[et][ec + j] = okr ? vv[j] : 0.f;
+            sm.V[et][ec + j] = vok ? raw_f32(vraw, j) : 0.f;
             if (rev)
-                sm.dO[et][ec + j] = okr ? oo[j] : 0.f;
+                sm.dO[et][ec + j] = vok ? raw_f32(oraw, j) : 0.f;
         }
-        // the copies have landed (and every earlier memory operation of
-        // this wave has completed)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (ISO)
+            if (tid < C)
+                sm.inP[tid][0] = braw;
     };
     auto factors = [&](int c, bool rev) {
         const int t0 = c * C, len = min(C, T - t0);
@@ -337,13 +370,32 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             tile_store(&sm.Mp[w - 2][0][0], LM, m, lane);
         }
     };
+    // Qb Kt^T (reverse pass), by waves 0 and 1 over half of the key
+    // channels each, into Am and dAm; wave 0 sums them into A after the barrier
+    auto form_A_parts = [&]() {
+        if (w < 2) {
+            const int k0 = w * (DK / 2);
+            f32x4 m = zero4();
+            mmk<DK / 2>(m, &sm.Qb[0][k0], LK, 1, &sm.Kt[0][k0], 1, LK, lane);
+            tile_store(w == 0 ? &sm.Am[0][0] : &sm.dAm[0][0], LM, m, lane);
+        }
+    };
     // After form_M_parts and a barrier: wave 0 forms T = (I + M)^-1 with
     // M = tril(Kb Kt^T, -1) nilpotent, (I + M)^-1 = (I - M)(I + M^2)(I + M^4)
     // (I + M^8), each factor a 16x16 product on the matrix cores (the powers of
-    // M through LDS); meanwhile waves 1-3 form R = V - Kb (c S0) for the four
-    // column tiles (wave 1 two of them) into mR.
-    auto form_T_and_R = [&]() {
+    // M through LDS), and in the reverse pass A = tril(Qb Kt^T) from its two
+    // halves; meanwhile waves 1-3 form the products Kb (c S0) over a third of
+    // the key channels each, for all four column tiles (into mR, Rp[0], Rp[1]).
+    constexpr int KQ = ((DK / 4 + 2) / 3) * 4;  // key channels of waves 1 and 2 (wave 3: the rest)
+    auto form_T_and_R = [&](bool rev) {
         if (w == 0) {
+            if (rev) {
+                f32x4 m = tile_load(&sm.Am[0][0], LM, lane) + tile_load(&sm.dAm[0][0], LM, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    m[r] = 4 * g4 + r >= i16 ? m[r] : 0.f;
+                tile_store(&sm.Am[0][0], LM, m, lane);
+            }
             f32x4 m = tile_load(&sm.Mp[0][0][0], LM, lane) + tile_load(&sm.Mp[1][0][0], LM, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -369,23 +421,36 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             }
             tile_store(&sm.Tm[0][0], LM, tt, lane);
         } else {
-            auto form_R = [&](int n) {
-                f32x4 p = zero4();
-                mmk<DK>(p, &sm.Kb[0][0], LK, 1, &sm.S0[0][16 * n], LC, 1, lane);
-                tile_store(&sm.mR[0][16 * n], LC, tile_load(&sm.V[0][16 * n], LC, lane) - p, lane);
+            auto part = [&](auto kc, int k0, float* dst) {
+                constexpr int K = decltype(kc)::value;
+#pragma unroll
+                for (int n = 0; n < 4; ++n) {
+                    f32x4 p = zero4();
+                    mmk<K>(p, &sm.Kb[0][k0], LK, 1, &sm.S0[k0][16 * n], LC, 1, lane);
+                    tile_store(dst + 16 * n, LC, p, lane);
+                }
             };
-            if (w == 1) {
-                form_R(0);
-                form_R(1);
-            } else {
-                form_R(w);
-            }
+            if (w == 1)
+                part(std::integral_constant<int, KQ>{}, 0, &sm.mR[0][0]);
+            else if (w == 2)
+                part(std::integral_constant<int, KQ>{}, KQ, &sm.Rp[0][0][0]);
+            else
+                part(std::integral_constant<int, DK - 2 * KQ>{}, 2 * KQ, &sm.Rp[1][0][0]);
         }
     };
-    // delta = T R for column tile w, into LDS
+    // delta = T (V - Kb (c S0)) for column tile w, into LDS
     auto form_delta = [&]() {
         f32x4 d = zero4();
-        mmk<C>(d, &sm.Tm[0][0], LM, 1, &sm.mR[0][16 * w], LC, 1, lane);
+        float ta[4], rb[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int k = 4 * s + g4, col = 16 * w + i16;
+            ta[s] = sm.Tm[i16][k];
+            rb[s] = sm.V[k][col] - ((sm.mR[k][col] + sm.Rp[0][k][col]) + sm.Rp[1][k][col]);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            d = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[s], rb[s], d, 0, 0, 0);
         tile_store(&sm.D[0][16 * w], LC, d, lane);
     };
     // the state rows this wave holds: tile (j, n) = channels chw + 16 j + 4 g + r, columns 16 n + i
@@ -410,11 +475,15 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
 
     // ---------------- forward pass: every chunk-start state ----------------
     state_init(a.S0);
+    if (nch > 0)
+        issue(0, false);
     for (int c = 0; c < nch; ++c) {
-        stage(c, false);
+        land(false);
         barrier();  // inputs staged, V
         factors(c, false);
-        barrier();  // factors, cS
+        barrier();  // factors, cS; the staging arrays are free
+        if (c + 1 < nch)
+            issue(c + 1, false);
         form_M_parts();
         // c S0 into LDS; the chunk-start state to the workspace
         float* ckc = ck_wg + (size_t)c * (DK * NC);
@@ -432,7 +501,7 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
                 tile_store(&sm.S0[state_rows(j)][16 * n], LC, x, lane);
             }
         barrier();  // M parts, c S0
-        form_T_and_R();
+        form_T_and_R(false);
         barrier();  // T, R
         form_delta();
         barrier();  // delta
@@ -456,30 +525,34 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
 
     // ---------------- reverse pass ----------------
     state_init(a.gS_T);
+    // this block's chunk-start states, loaded one chunk ahead with the inputs
+    float4 ck[NCK];
+    auto issue_rev = [&](int c) {
+        const float4* src = reinterpret_cast<const float4*>(ck_wg + (size_t)c * (DK * NC));
+#pragma unroll
+        for (int j = 0; j < NCK; ++j)
+            ck[j] = src[tid + 256 * j];
+        issue(c, true);
+    };
+    if (nch > 0)
+        issue_rev(nch - 1);
     for (int c = nch - 1; c >= 0; --c) {
         const int t0 = c * C, len = min(C, T - t0);
-        {
-            // the chunk-start state's loads go out first, so that their
-            // latency overlaps the inputs' loads
-            const float4* src = reinterpret_cast<const float4*>(ck_wg + (size_t)c * (DK * NC));
-            float4 ck[NCK];
+        land(true);
+        barrier();  // inputs staged, V, dO
+        factors(c, true);
+        barrier();  // factors, cS, gL; the staging arrays are free
 #pragma unroll
-            for (int j = 0; j < NCK; ++j)
-                ck[j] = src[tid + 256 * j];
-            stage(c, true);
-            barrier();  // inputs staged, V, dO
-            factors(c, true);
-            barrier();  // factors, cS, gL
-#pragma unroll
-            for (int j = 0; j < NCK; ++j) {
-                const int e = 4 * (tid + 256 * j), row = e / NC, cc = e % NC;
-                const float cs = sm.cS[row];
-                sm.S0[row][cc] = ck[j].x * cs;
-                sm.S0[row][cc + 1] = ck[j].y * cs;
-                sm.S0[row][cc + 2] = ck[j].z * cs;
-                sm.S0[row][cc + 3] = ck[j].w * cs;
-            }
+        for (int j = 0; j < NCK; ++j) {
+            const int e = 4 * (tid + 256 * j), row = e / NC, cc = e % NC;
+            const float cs = sm.cS[row];
+            sm.S0[row][cc] = ck[j].x * cs;
+            sm.S0[row][cc + 1] = ck[j].y * cs;
+            sm.S0[row][cc + 2] = ck[j].z * cs;
+            sm.S0[row][cc + 3] = ck[j].w * cs;
         }
+        if (c > 0)
+            issue_rev(c - 1);
         // E = G'_15 dS_C, in place (this wave's rows)
 #pragma unroll
         for (int j = 0; j < CT; ++j)
@@ -492,17 +565,9 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
                 tile_store(&sm.E[state_rows(j)][16 * n], LC, x, lane);
             }
         form_M_parts();
-        if (w == 1) {
-            f32x4 m = zero4();
-            mmk<DK>(m, &sm.Qb[0][0], LK, 1, &sm.Kt[0][0], 1, LK, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g4 + r;
-                sm.Am[t][i16] = t >= i16 ? m[r] : 0.f;
-            }
-        }
-        barrier();  // c S0, M parts, A, E
-        form_T_and_R();
+        form_A_parts();
+        barrier();  // c S0, M parts, A parts, E
+        form_T_and_R(true);
         barrier();  // T, R
         form_delta();
         barrier();  // delta
