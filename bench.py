@@ -244,6 +244,9 @@ def main():
                     help="time the forward from gate pre-activations (kdn_fwd_preact) instead")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (kdn_bwd) on the workload instead")
+    ap.add_argument("--bwd-serial", action="store_true",
+                    help="with --bwd: a workspace one byte short of kdn_bwd_workspace_size, so "
+                         "that shapes the backward splits over the sequence run without the split")
     ap.add_argument("--gain", action="store_true",
                     help="time the gain scan alone (kdn_gain_scan, with kappa) on the workload")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -553,8 +556,8 @@ def bench_bwd(args, w, variant, d, io_dt):
     gen = torch.Generator(device="cpu").manual_seed(w.seed + 77)
     d_o = torch.randn((B, T, H, dv), generator=gen).to(io_dt).to(dev)
     var = {"diag": 0, "iso": 1}[variant]
-    ws = torch.empty(max(int(_lib.lib().kdn_bwd_workspace_size(var, B, T, H, dk, dv)), 1),
-                     dtype=torch.uint8, device=dev)
+    need = int(_lib.lib().kdn_bwd_workspace_size(var, B, T, H, dk, dv))
+    ws = torch.empty(max(need - (1 if args.bwd_serial else 0), 1), dtype=torch.uint8, device=dev)
 
     def step():
         api.kdn_bwd(variant, d["q"], d["k"], d["v"], d["alpha"], d["omega"], d["r"], d_o,
@@ -593,7 +596,8 @@ def bench_bwd(args, w, variant, d, io_dt):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "variant": variant, "B": B, "T": T, "H": H, "dk": dk,
-                   "dv": dv, "io": w.io, "pass": "backward"},
+                   "dv": dv, "io": w.io, "pass": "backward",
+                   "workspace": "short by one byte" if args.bwd_serial else "full"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "alg_bytes_per_launch": alg,

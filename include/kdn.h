@@ -326,8 +326,17 @@ kdn_status kdn_gates_from_preact(int variant, int B, int T, int H, int dk, int i
  * With dv a multiple of 64 the memory part runs in 16-token chunks on the
  * matrix cores (fp32 products); otherwise token by token from stored
  * innovations.  The workspace (kdn_bwd_workspace_size bytes, 16-byte aligned)
- * holds those and per-column-block partial sums.  Deterministic (no atomics).
- * Asynchronous on `stream`; validation as for the forward.
+ * holds those and per-column-block partial sums.  Diagonal shapes with
+ * dk = dv whose B*H*(dv/64) workgroups fill at most half of the chip and
+ * whose T splits into 2, 4 or 8 segments of at least 1024 tokens (each a
+ * multiple of 64) run split over the sequence with bf16 io: the state map
+ * over a span is affine (method part §2, §6), so the reverse pass carries
+ * the state adjoint into a segment from its right as M^T dS + (the
+ * segment's own part), and the segments run side by side (their entry
+ * states from the forward walk with split-bf16 products).  For those shapes
+ * kdn_bwd_workspace_size includes the split's planes; a smaller workspace of
+ * at least the rest runs the same call without the split.  Deterministic (no
+ * atomics).  Asynchronous on `stream`; validation as for the forward.
  */
 size_t kdn_bwd_workspace_size(int variant, int B, int T, int H, int dk, int dv);
 kdn_status kdn_bwd(int variant, int B, int T, int H, int dk, int dv, int io_dtype, float mu,

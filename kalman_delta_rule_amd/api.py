@@ -301,7 +301,10 @@ def kdn_bwd(variant: str, q, k, v, alpha, omega, r, d_o, S0=None, var0=None, mu=
     """Backward pass of the forward given by the same arguments (see kdn_fwd_ex)
     for dL/do = d_o, dL/dS_T = dS_T and dL/dvar_T = dvar_T (both optional).
     Returns a dict with dq, dk, dv (io dtype), dalpha, domega, dr (fp32) and,
-    with ``want_state_grads``, dS0, dvar0 and dmu [B,H] (fp32)."""
+    with ``want_state_grads``, dS0, dvar0 and dmu [B,H] (fp32).  A given
+    ``workspace`` (uint8) is passed as it is: the library requires its base
+    size and splits the sequence (bf16 io, few heads) only when it holds all
+    of kdn_bwd_workspace_size; without one, that size is allocated."""
     L = _lib.lib()
     var = {"diag": KDN_DIAG, "iso": KDN_ISO}[variant]
     if q.dim() != 4:
@@ -333,8 +336,8 @@ def kdn_bwd(variant: str, q, k, v, alpha, omega, r, d_o, S0=None, var0=None, mu=
         g["dS0"] = torch.empty((B, H, dk, dv), dtype=f32, device=dev)
         g["dvar0"] = torch.empty(var_shape, dtype=f32, device=dev)
         g["dmu"] = torch.empty((B, H), dtype=f32, device=dev)
-    need = int(L.kdn_bwd_workspace_size(var, B, T, H, dk, dv))
-    if workspace is None or workspace.numel() < need:
+    if workspace is None:
+        need = int(L.kdn_bwd_workspace_size(var, B, T, H, dk, dv))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
         st = L.kdn_bwd(var, B, T, H, dk, dv, io, mu, _ptr(mu_h), _ptr(q), _ptr(k), _ptr(v),

@@ -572,7 +572,11 @@ size_t kdn_bwd_workspace_size(int variant, int B, int T, int H, int dk, int dv)
     if ((variant != KDN_DIAG && variant != KDN_ISO) || B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1 ||
         !below_2_31({(size_t)B, (size_t)(T > 0 ? T : 1), (size_t)H, (size_t)(dk > dv ? dk : dv)}))
         return 0;
-    return kdn::bwd_workspace_floats(variant == KDN_ISO, B, T, H, dk, dv) * sizeof(float);
+    const bool iso = variant == KDN_ISO;
+    const int nseg = kdn::bwd_segments(iso, B, T, H, dk, dv);
+    return (kdn::bwd_workspace_floats(iso, B, T, H, dk, dv) +
+            (nseg ? kdn::bwd_seg_workspace_floats(iso, B, T, H, dk, nseg) : 0)) *
+           sizeof(float);
 }
 
 static kdn_status bwd_impl(int variant, int B, int T, int H, int dk, int dv, int io_dtype,
@@ -675,10 +679,17 @@ static kdn_status bwd_impl(int variant, int B, int T, int H, int dk, int dv, int
                             bufs[j].name);
         }
     }
+    // the base workspace is required; the split over the sequence (bf16 io,
+    // shapes that leave most compute units idle) runs when the workspace also
+    // holds its planes
     const size_t need = kdn::bwd_workspace_floats(iso, B, T, H, dk, dv) * sizeof(float);
     if (workspace_bytes < need || (need && !workspace))
         return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
                     workspace_bytes);
+    const int nseg = io_dtype == KDN_BF16 ? kdn::bwd_segments(iso, B, T, H, dk, dv) : 0;
+    const size_t seg_bytes =
+        nseg ? kdn::bwd_seg_workspace_floats(iso, B, T, H, dk, nseg) * sizeof(float) : 0;
+    const bool split = nseg && workspace_bytes - need >= seg_bytes;
     if ((uintptr_t)workspace % 16)
         return fail(KDN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     kdn::BwdArgs a{};
@@ -689,6 +700,10 @@ static kdn_status bwd_impl(int variant, int B, int T, int H, int dk, int dv, int
     a.gS0 = dS0; a.gvar0 = dvar0; a.gmu = dmu;
     a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
     kdn::bwd_carve_workspace(a, iso, static_cast<float*>(workspace));
+    if (split) {
+        a.nseg = nseg;
+        a.segws = static_cast<float*>(workspace) + need / sizeof(float);
+    }
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     if (pro && T > 0) {  // the gates from their pre-activations
         hipError_t e = kdn::launch_gate_prologue(*pro, io_dtype, hs);

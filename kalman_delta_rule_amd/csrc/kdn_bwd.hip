@@ -800,7 +800,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream)
     }
     hipError_t e;
     if (chunked) {
-        e = launch_bwd_chunk_mem(a, ISO, sizeof(IO) == 2 ? 1 : 0, stream);
+        e = a.nseg ? launch_seqpar_bwd_mem(a, ISO, stream)
+                   : launch_bwd_chunk_mem(a, ISO, sizeof(IO) == 2 ? 1 : 0, false, stream);
     } else {
         hipLaunchKernelGGL((kdn_bwd_mem_kernel<IO, ISO, DK>), dim3(nblk, bh), dim3(256), 0, stream,
                            a);

@@ -236,7 +236,12 @@ __device__ __forceinline__ void rows_store(void* dst, const u32x4 (&src)[NR], in
     }
 }
 
-template <typename IO, bool ISO, int DK>
+// ADJ: the adjoint only.  No forward pass and no per-token output: the
+// reverse pass carries dS from gS_T (zero when null) back through the chunks
+// (E, dO, the factors, T and A only) and writes the adjoint at the start into
+// gS0.  The sequence split of the backward uses it for each segment's adjoint
+// from its own outputs.
+template <typename IO, bool ISO, int DK, bool ADJ>
 __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
 {
     const BwdArgs a = args;
@@ -306,7 +311,8 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
                 braw = a.gsc[tok_of(t0 + min(tid, len - 1)) * 4];
         vok = et < len;
         const size_t r = tok_of(t0 + min(et, len - 1)) * dv + col0 + ec;
-        vraw = *reinterpret_cast<const Raw4*>(vg + r);
+        if (!ADJ)
+            vraw = *reinterpret_cast<const Raw4*>(vg + r);
         if (rev)
             oraw = *reinterpret_cast<const Raw4*>(og + r);
     };
@@ -320,7 +326,8 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             rows_store<NPK>(reinterpret_cast<char*>(&sm.inK[0]) + C * DK * sizeof(IO), rq, w, lane);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            sm.V[et][ec + j] = vok ? raw_f32(vraw, j) : 0.f;
+            if (!ADJ)
+                sm.V[et][ec + j] = vok ? raw_f32(vraw, j) : 0.f;
             if (rev)
                 sm.dO[et][ec + j] = vok ? raw_f32(oraw, j) : 0.f;
         }
@@ -420,7 +427,7 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
                 pw = sq;
             }
             tile_store(&sm.Tm[0][0], LM, tt, lane);
-        } else {
+        } else if (!ADJ) {
             auto part = [&](auto kc, int k0, float* dst) {
                 constexpr int K = decltype(kc)::value;
 #pragma unroll
@@ -474,64 +481,68 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     };
 
     // ---------------- forward pass: every chunk-start state ----------------
-    state_init(a.S0);
-    if (nch > 0)
-        issue(0, false);
-    for (int c = 0; c < nch; ++c) {
-        land(false);
-        barrier();  // inputs staged, V
-        factors(c, false);
-        barrier();  // factors, cS; the staging arrays are free
-        if (c + 1 < nch)
-            issue(c + 1, false);
-        form_M_parts();
-        // c S0 into LDS; the chunk-start state to the workspace
-        float* ckc = ck_wg + (size_t)c * (DK * NC);
+    if constexpr (!ADJ) {
+        state_init(a.S0);
+        if (nch > 0)
+            issue(0, false);
+        for (int c = 0; c < nch; ++c) {
+            land(false);
+            barrier();  // inputs staged, V
+            factors(c, false);
+            barrier();  // factors, cS; the staging arrays are free
+            if (c + 1 < nch)
+                issue(c + 1, false);
+            form_M_parts();
+            // c S0 into LDS; the chunk-start state to the workspace
+            float* ckc = ck_wg + (size_t)c * (DK * NC);
 #pragma unroll
-        for (int j = 0; j < CT; ++j)
+            for (int j = 0; j < CT; ++j)
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                f32x4 x = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
+                for (int n = 0; n < 4; ++n) {
+                    f32x4 x = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = state_rows(j) + 4 * g4 + r;
-                    ckc[row * NC + 16 * n + i16] = x[r];
-                    x[r] *= sm.cS[row];
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = state_rows(j) + 4 * g4 + r;
+                        ckc[row * NC + 16 * n + i16] = x[r];
+                        x[r] *= sm.cS[row];
+                    }
+                    tile_store(&sm.S0[state_rows(j)][16 * n], LC, x, lane);
                 }
-                tile_store(&sm.S0[state_rows(j)][16 * n], LC, x, lane);
-            }
-        barrier();  // M parts, c S0
-        form_T_and_R(false);
-        barrier();  // T, R
-        form_delta();
-        barrier();  // delta
+            barrier();  // M parts, c S0
+            form_T_and_R(false);
+            barrier();  // T, R
+            form_delta();
+            barrier();  // delta
 #pragma unroll
-        for (int j = 0; j < CT; ++j)
+            for (int j = 0; j < CT; ++j)
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                // S_C = G'_15 (c S0 + Kt^T delta)
-                f32x4 x = tile_load(&sm.S0[state_rows(j)][16 * n], LC, lane);
-                mmk<C>(x, &sm.Kt[0][state_rows(j)], 1, LK, &sm.D[0][16 * n], LC, 1, lane);
+                for (int n = 0; n < 4; ++n) {
+                    // S_C = G'_15 (c S0 + Kt^T delta)
+                    f32x4 x = tile_load(&sm.S0[state_rows(j)][16 * n], LC, lane);
+                    mmk<C>(x, &sm.Kt[0][state_rows(j)], 1, LK, &sm.D[0][16 * n], LC, 1, lane);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    x[r] *= sm.gL[state_rows(j) + 4 * g4 + r];
-                tile_store(&sm.E[state_rows(j)][16 * n], LC, x, lane);
-            }
-        barrier();  // readers of this chunk's factors done
-    }
+                    for (int r = 0; r < 4; ++r)
+                        x[r] *= sm.gL[state_rows(j) + 4 * g4 + r];
+                    tile_store(&sm.E[state_rows(j)][16 * n], LC, x, lane);
+                }
+            barrier();  // readers of this chunk's factors done
+        }
 
-    // every chunk-start state stored is visible to the whole workgroup
-    __syncthreads();
+        // every chunk-start state stored is visible to the whole workgroup
+        __syncthreads();
+    }
 
     // ---------------- reverse pass ----------------
     state_init(a.gS_T);
     // this block's chunk-start states, loaded one chunk ahead with the inputs
     float4 ck[NCK];
     auto issue_rev = [&](int c) {
-        const float4* src = reinterpret_cast<const float4*>(ck_wg + (size_t)c * (DK * NC));
+        if constexpr (!ADJ) {
+            const float4* src = reinterpret_cast<const float4*>(ck_wg + (size_t)c * (DK * NC));
 #pragma unroll
-        for (int j = 0; j < NCK; ++j)
-            ck[j] = src[tid + 256 * j];
+            for (int j = 0; j < NCK; ++j)
+                ck[j] = src[tid + 256 * j];
+        }
         issue(c, true);
     };
     if (nch > 0)
@@ -542,14 +553,16 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
         barrier();  // inputs staged, V, dO
         factors(c, true);
         barrier();  // factors, cS, gL; the staging arrays are free
+        if constexpr (!ADJ) {
 #pragma unroll
-        for (int j = 0; j < NCK; ++j) {
-            const int e = 4 * (tid + 256 * j), row = e / NC, cc = e % NC;
-            const float cs = sm.cS[row];
-            sm.S0[row][cc] = ck[j].x * cs;
-            sm.S0[row][cc + 1] = ck[j].y * cs;
-            sm.S0[row][cc + 2] = ck[j].z * cs;
-            sm.S0[row][cc + 3] = ck[j].w * cs;
+            for (int j = 0; j < NCK; ++j) {
+                const int e = 4 * (tid + 256 * j), row = e / NC, cc = e % NC;
+                const float cs = sm.cS[row];
+                sm.S0[row][cc] = ck[j].x * cs;
+                sm.S0[row][cc + 1] = ck[j].y * cs;
+                sm.S0[row][cc + 2] = ck[j].z * cs;
+                sm.S0[row][cc + 3] = ck[j].w * cs;
+            }
         }
         if (c > 0)
             issue_rev(c - 1);
@@ -569,13 +582,15 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
         barrier();  // c S0, M parts, A parts, E
         form_T_and_R(true);
         barrier();  // T, R
-        form_delta();
-        barrier();  // delta
+        if constexpr (!ADJ) {
+            form_delta();
+            barrier();  // delta
+        }
         {
             // rowsum over this block's columns of dS_C . X = (E . X) / G'_15,
             // X = c S0 + Kt^T delta: the partial of the last token's dG (array 3)
 #pragma unroll
-            for (int j = 0; j < CT; ++j) {
+            for (int j = 0; j < (ADJ ? 0 : CT); ++j) {
                 float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int n = 0; n < 4; ++n) {
@@ -604,7 +619,7 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * g4 + r;
-                if (t < len)
+                if (!ADJ && t < len)
                     dvg[tok_of(t0 + t) * dv + col0 + 16 * w + i16] = from_f32<IO>(dR[r]);
             }
         }
@@ -614,7 +629,8 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
 #pragma unroll
         for (int j = 0; j < CT; ++j) {
             gKt[j] = zero4();
-            mmk<NC>(gKt[j], &sm.D[0][0], LC, 1, &sm.E[state_rows(j)][0], 1, LC, lane);
+            if (!ADJ)
+                mmk<NC>(gKt[j], &sm.D[0][0], LC, 1, &sm.E[state_rows(j)][0], 1, LC, lane);
         }
         // dS0' = E + Qb^T dO + Kb^T (-dR), then dS0 = c dS0', carried in E
 #pragma unroll
@@ -629,6 +645,10 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
                     x[r] *= sm.cS[state_rows(j) + 4 * g4 + r];
                 tile_store(&sm.E[state_rows(j)][16 * n], LC, x, lane);
             }
+        if constexpr (ADJ) {
+            barrier();  // the next chunk's inputs overwrite the LDS arrays
+            continue;
+        }
         if (w == 0) {
             f32x4 m = zero4();  // -dR delta^T, strictly lower
             mmk<NC>(m, &sm.mR[0][0], LC, 1, &sm.D[0][0], 1, LC, lane);
@@ -763,9 +783,15 @@ __global__ __launch_bounds__(DK) void kdn_bwd_chunk_finish_kernel(BwdArgs args, 
 }
 
 template <typename IO, bool ISO, int DK>
-static hipError_t launch_t(const BwdArgs& a, hipStream_t stream)
+static hipError_t launch_t(const BwdArgs& a, bool adj, hipStream_t stream)
 {
-    auto kern = kdn_bwd_chunk_kernel<IO, ISO, DK>;
+    auto kern = kdn_bwd_chunk_kernel<IO, ISO, DK, false>;
+    if (adj) {  // the sequence split runs Diagonal with bf16 io only
+        if constexpr (sizeof(IO) == 2 && !ISO)
+            kern = kdn_bwd_chunk_kernel<IO, ISO, DK, true>;
+        else
+            return hipErrorInvalidValue;
+    }
     const size_t smem = sizeof(Smem<DK>);
     hipError_t e = set_lds_limit_once(kern, smem);
     if (e != hipSuccess)
@@ -775,7 +801,7 @@ static hipError_t launch_t(const BwdArgs& a, hipStream_t stream)
     if (e != hipSuccess)
         return e;
     const int nch = (a.T + C - 1) / C;
-    if (nch > 0) {
+    if (nch > 0 && !adj) {
         hipLaunchKernelGGL((kdn_bwd_chunk_finish_kernel<IO, ISO, DK>), dim3(a.B * a.H * nch),
                            dim3(DK), 0, stream, a, a.dv / NC);
         e = hipGetLastError();
@@ -785,18 +811,21 @@ static hipError_t launch_t(const BwdArgs& a, hipStream_t stream)
 
 }  // namespace cbwd
 
-hipError_t launch_bwd_chunk_mem(const BwdArgs& a, bool iso, int io_dtype, hipStream_t stream)
+hipError_t launch_bwd_chunk_mem(const BwdArgs& a, bool iso, int io_dtype, bool adj,
+                                hipStream_t stream)
 {
     using namespace cbwd;
     const bool bf = io_dtype == 1;
     if (a.dk == 128) {
         if (iso)
-            return bf ? launch_t<bf16, true, 128>(a, stream) : launch_t<float, true, 128>(a, stream);
-        return bf ? launch_t<bf16, false, 128>(a, stream) : launch_t<float, false, 128>(a, stream);
+            return bf ? launch_t<bf16, true, 128>(a, adj, stream)
+                      : launch_t<float, true, 128>(a, adj, stream);
+        return bf ? launch_t<bf16, false, 128>(a, adj, stream)
+                  : launch_t<float, false, 128>(a, adj, stream);
     }
     if (iso)
-        return bf ? launch_t<bf16, true, 64>(a, stream) : launch_t<float, true, 64>(a, stream);
-    return bf ? launch_t<bf16, false, 64>(a, stream) : launch_t<float, false, 64>(a, stream);
+        return bf ? launch_t<bf16, true, 64>(a, adj, stream) : launch_t<float, true, 64>(a, adj, stream);
+    return bf ? launch_t<bf16, false, 64>(a, adj, stream) : launch_t<float, false, 64>(a, adj, stream);
 }
 
 }  // namespace kdn

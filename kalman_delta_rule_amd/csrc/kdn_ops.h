@@ -93,6 +93,10 @@ struct BwdArgs {
     float* ckpt;   // [B*H][dv/16][ceil(T/16)][dk][16]: S at every 16th token
     float* dlt;    // [B*H][dv/16][T][16]: innovations delta of every token
     float* part;   // [4][dv/16][B*T*H][dk]: per-column-block partial row sums
+    // the split over the sequence (kdn_seqpar.hip): segments (0: none) and
+    // their workspace
+    int nseg = 0;
+    float* segws = nullptr;
 };
 
 struct PrologueArgs {
@@ -117,9 +121,18 @@ hipError_t launch_gain_scan(const GainArgs& a, bool iso, int io_dtype, hipStream
 // (kdn_bwd_chunk.hip) for these shapes, token by token otherwise
 bool bwd_chunked(int dk, int dv);
 constexpr int BWD_CHUNK_COLS = 64;  // value columns per chunked memory workgroup
-hipError_t launch_bwd_chunk_mem(const BwdArgs& a, bool iso, int io_dtype, hipStream_t stream);
+// adj: the adjoint only (no forward pass, no per-token outputs; bf16 io)
+hipError_t launch_bwd_chunk_mem(const BwdArgs& a, bool iso, int io_dtype, bool adj,
+                                hipStream_t stream);
 size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv);
 void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws);
+// the backward's split over the sequence (kdn_seqpar.hip): the segment count
+// for a shape (0: not eligible; the split itself runs with bf16 io only), the
+// workspace it adds behind bwd_workspace_floats, and its memory part (after
+// the gain scan, in place of launch_bwd_chunk_mem)
+int bwd_segments(bool iso, int B, int T, int H, int dk, int dv);
+size_t bwd_seg_workspace_floats(bool iso, int B, int T, int H, int dk, int S);
+hipError_t launch_seqpar_bwd_mem(const BwdArgs& a, bool iso, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, bool iso, int io_dtype, hipStream_t stream);
 hipError_t launch_gate_prologue(const PrologueArgs& a, int io_dtype, hipStream_t stream);
 hipError_t launch_gate_epilogue(const PrologueArgs& p, float* da, float* dw, float* dr,

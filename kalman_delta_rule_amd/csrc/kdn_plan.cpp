@@ -51,6 +51,38 @@ size_t seqpar_workspace_floats(bool iso, int B, int T, int H, int dk, int dv, in
     return n;
 }
 
+// ------------------------------------------------- backward split over the sequence
+int bwd_segments(bool iso, int B, int T, int H, int dk, int dv)
+{
+    // Diagonal only: the segment-entry states come from the forward walk,
+    // whose Isotropic form runs single bf16 products (the Diagonal one splits
+    // its operands, ~1e-5 relative), below the backward's fp32 accuracy
+    if (iso || dk != dv || !bwd_chunked(dk, dv) || T <= 0)
+        return 0;
+    const long ncu = 256;  // MI355X compute units, as for the forward
+    if (B < 1 || H < 1 || (long)B * H > ncu)
+        return 0;
+    const long tiles = (long)B * H * (dv / BWD_CHUNK_COLS);
+    // the chunked backward's step is several times the forward walk's, so
+    // doubling the workgroups already pays for the state walks and the
+    // adjoint pass the split adds
+    for (int s = SP_MAX; s >= 2; s >>= 1)
+        if (tiles * s <= ncu && T % (64 * s) == 0 && T / s >= 1024)
+            return s;
+    return 0;
+}
+
+size_t bwd_seg_workspace_floats(bool iso, int B, int T, int H, int dk, int S)
+{
+    (void)T;
+    const size_t bs = (size_t)B * S, width = iso ? 1 : (size_t)dk;
+    const size_t st = bs * H * (size_t)dk * dk;
+    // segment-entry variances and a scratch plane; N, M, the segment-entry
+    // states, the identity, each segment's own adjoint and the adjoint
+    // entering it from the right
+    return 2 * r64(bs * H * width) + 6 * r64(st);
+}
+
 // ------------------------------------------------------------- backward
 bool bwd_chunked(int dk, int dv)
 {

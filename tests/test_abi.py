@@ -374,6 +374,25 @@ def test_bwd_validation(L):
         assert L.kdn_bwd_workspace_size(0, B, T, H, dk, dv) == 4 * diag, dv
         assert L.kdn_bwd_workspace_size(1, B, T, H, dk, dv) == 4 * iso, dv
     assert L.kdn_bwd_workspace_size(0, B, 0, H, dk, 64) == 0
+    # the backward split over the sequence (Diagonal, d_k = d_v, few heads,
+    # long T) adds two variance planes and six state planes of the segments
+    # (config 3's shape: 8 segments; T = 2048 with 16 or 64 heads: 2)
+    def base(iso, B, T, H, dk, dv):
+        ntok, nch, ngc = B * T * H, (T + 15) // 16, (T + 63) // 64
+        width = 1 if iso else dk
+        pieces = r64(ntok * 4) if iso else 2 * r64(ntok * dk) + r64(ntok)
+        return (pieces + r64(B * H * ngc * width * 5) + r64(B * H * ngc * width * 2)
+                + r64(B * H * ngc * width) + r64(ntok) + r64(B * H * ngc)
+                + r64(B * H * nch * dk * dv) + r64(4 * (dv // 64) * ntok * dk))
+    for (B, T, H, d, S) in ((1, 65536, 16, 128, 8), (1, 2048, 16, 128, 2), (4, 2048, 16, 128, 2),
+                            (1, 8192, 1, 64, 8), (1, 4096, 2, 64, 4)):
+        seg = 2 * r64(B * S * H * d) + 6 * r64(B * S * H * d * d)
+        assert L.kdn_bwd_workspace_size(0, B, T, H, d, d) == 4 * (base(False, B, T, H, d, d) + seg)
+        assert L.kdn_bwd_workspace_size(1, B, T, H, d, d) == 4 * base(True, B, T, H, d, d)
+    # not split: the grid already fills the chip, segments would be shorter
+    # than 1024 tokens, or T does not divide
+    for (B, T, H, d) in ((8, 4096, 16, 128), (1, 1024, 2, 128), (1, 4160, 2, 128)):
+        assert L.kdn_bwd_workspace_size(0, B, T, H, d, d) == 4 * base(False, B, T, H, d, d)
 
 
 def test_fwd_preact_validation(L):
