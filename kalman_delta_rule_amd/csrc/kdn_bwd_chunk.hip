@@ -157,6 +157,31 @@ __device__ __forceinline__ void mm_acc(f32x4& acc, const float* A, int am, int a
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], X[r], acc, 0, 0, 0);
 }
 
+// Several products as one software pipeline of NS fp32 16x16x4 steps: step
+// s reads this lane's operands through op(s, a, b) (A(lane & 15, k) and
+// B(k, lane & 15) for the step's k = 4 s' + (lane >> 4)) and accumulates into
+// acc[slot(s)]; the operands of step s + D are read before the product of
+// step s is issued, across the products' boundaries (a product of its own
+// would drain the pipeline and wait for its first operands).  s is a
+// constant in every call, so op and slot fold to plain LDS reads and a
+// fixed register tile.
+template <int NS, int NA, typename Op, typename Slot>
+__device__ __forceinline__ void mm_stream(f32x4 (&acc)[NA], Op op, Slot slot)
+{
+    constexpr int D = NS < 6 ? NS : 6;
+    float a[NS], b[NS];
+#pragma unroll
+    for (int s = 0; s < D; ++s)
+        op(s, a[s], b[s]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        if (s + D < NS)
+            op(s + D, a[s + D], b[s + D]);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[slot(s)] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc[slot(s)], 0, 0, 0);
+    }
+}
+
 // an accumulator tile to / from LDS: element (4 g + r, i) at p[(4 g + r) ld + i]
 __device__ __forceinline__ void tile_store(float* p, int ld, const f32x4& x, int lane)
 {
@@ -252,6 +277,13 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     constexpr int NCK = DK * NC / (4 * 256);  // chunk-start state pieces (4 floats) per thread
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
+    // distances in floats between arrays of equal shape, for choosing one by
+    // an offset (a choice between two LDS pointers compiles poorly)
+    constexpr int OFF_KB_QB = (int)((offsetof(SM, Kb) - offsetof(SM, Qb)) / sizeof(float));
+    constexpr int OFF_MR_DO = (int)((offsetof(SM, mR) - offsetof(SM, dO)) / sizeof(float));
+    constexpr int OFF_RP0_MR = (int)((offsetof(SM, Rp) - offsetof(SM, mR)) / sizeof(float));
+    constexpr int OFF_RP1_MR = OFF_RP0_MR + C * LC;
+    constexpr int OFF_DAM_AM = (int)((offsetof(SM, dAm) - offsetof(SM, Am)) / sizeof(float));
 
     const int blk = blockIdx.x, nblk = gridDim.x, bh = blockIdx.y;
     const int H = a.H, T = a.T, dv = a.dv;
@@ -384,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             const int k0 = w * (DK / 2);
             f32x4 m = zero4();
             mmk<DK / 2>(m, &sm.Qb[0][k0], LK, 1, &sm.Kt[0][k0], 1, LK, lane);
-            tile_store(w == 0 ? &sm.Am[0][0] : &sm.dAm[0][0], LM, m, lane);
+            tile_store(&sm.Am[0][0] + (w == 0 ? 0 : OFF_DAM_AM), LM, m, lane);
         }
     };
     // After form_M_parts and a barrier: wave 0 forms T = (I + M)^-1 with
@@ -440,9 +472,9 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             if (w == 1)
                 part(std::integral_constant<int, KQ>{}, 0, &sm.mR[0][0]);
             else if (w == 2)
-                part(std::integral_constant<int, KQ>{}, KQ, &sm.Rp[0][0][0]);
+                part(std::integral_constant<int, KQ>{}, KQ, &sm.mR[0][0] + OFF_RP0_MR);
             else
-                part(std::integral_constant<int, DK - 2 * KQ>{}, 2 * KQ, &sm.Rp[1][0][0]);
+                part(std::integral_constant<int, DK - 2 * KQ>{}, 2 * KQ, &sm.mR[0][0] + OFF_RP1_MR);
         }
     };
     // delta = T (V - Kb (c S0)) for column tile w, into LDS
@@ -587,19 +619,57 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             barrier();  // delta
         }
         {
-            // rowsum over this block's columns of dS_C . X = (E . X) / G'_15,
-            // X = c S0 + Kt^T delta: the partial of the last token's dG (array 3)
+            // One stream: X' = c S0 + Kt^T delta for this wave's state tiles
+            // (slots 0 .. 4 CT - 1; not in the adjoint-only mode), then
+            // ddelta = Kt E + A^T dO for column tile w (slot 4 CT).  (The
+            // fp32-io d_k = 128 instantiation runs them as separate products:
+            // the stream there makes this ROCm compiler fail on an invalid
+            // operand in its instruction selection.)
+            constexpr bool STREAM5 = !(sizeof(IO) == 4 && DK == 128);
+            constexpr int NX = ADJ ? 0 : 4 * CT * (C / 4);
+            f32x4 acc[4 * CT + 1];
+#pragma unroll
+            for (int q = 0; q < 4 * CT; ++q)
+                acc[q] = ADJ ? zero4() : tile_load(&sm.S0[state_rows(q / 4)][16 * (q % 4)], LC, lane);
+            acc[4 * CT] = zero4();
+            if constexpr (STREAM5) {
+                mm_stream<NX + DK / 4 + C / 4>(
+                    acc,
+                    [&](int st, float& av, float& bv) {
+                        if (st < NX) {  // Kt^T delta, tile q = (j, n)
+                            const int q = st / 4, k = 4 * (st % 4) + g4;
+                            av = sm.Kt[k][state_rows(q / 4) + i16];
+                            bv = sm.D[k][16 * (q % 4) + i16];
+                        } else if (st < NX + DK / 4) {  // Kt E
+                            const int k = 4 * (st - NX) + g4;
+                            av = sm.Kt[i16][k];
+                            bv = sm.E[k][16 * w + i16];
+                        } else {  // A^T dO
+                            const int k = 4 * (st - NX - DK / 4) + g4;
+                            av = sm.Am[k][i16];
+                            bv = sm.dO[k][16 * w + i16];
+                        }
+                    },
+                    [&](int st) { return st < NX ? st / 4 : 4 * CT; });
+            } else {
+#pragma unroll
+                for (int q = 0; q < (ADJ ? 0 : 4 * CT); ++q)
+                    mmk<C>(acc[q], &sm.Kt[0][state_rows(q / 4)], 1, LK, &sm.D[0][16 * (q % 4)], LC,
+                           1, lane);
+                mmk<DK>(acc[4 * CT], &sm.Kt[0][0], LK, 1, &sm.E[0][16 * w], LC, 1, lane);
+                mmk<C>(acc[4 * CT], &sm.Am[0][0], 1, LM, &sm.dO[0][16 * w], LC, 1, lane);
+            }
+            // rowsum over this block's columns of dS_C . X = (E . X') / G'_15:
+            // the partial of the last token's dG (array 3)
 #pragma unroll
             for (int j = 0; j < (ADJ ? 0 : CT); ++j) {
                 float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int n = 0; n < 4; ++n) {
-                    f32x4 x = tile_load(&sm.S0[state_rows(j)][16 * n], LC, lane);
-                    mmk<C>(x, &sm.Kt[0][state_rows(j)], 1, LK, &sm.D[0][16 * n], LC, 1, lane);
                     const f32x4 e = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        rs[r] = fmaf(e[r], x[r], rs[r]);
+                        rs[r] = fmaf(e[r], acc[4 * j + n][r], rs[r]);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -609,12 +679,9 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
                         a.part[3 * ks + ((size_t)blk * ntok + tok_of(t0 + len - 1)) * DK + row] = sum;
                 }
             }
-            // ddelta = Kt E + A^T dO, dR = T^T ddelta (column tile w)
-            f32x4 dd = zero4();
-            mmk<DK>(dd, &sm.Kt[0][0], LK, 1, &sm.E[0][16 * w], LC, 1, lane);
-            mmk<C>(dd, &sm.Am[0][0], 1, LM, &sm.dO[0][16 * w], LC, 1, lane);
+            // dR = T^T ddelta
             f32x4 dR = zero4();
-            mm_acc(dR, &sm.Tm[0][0], 1, LM, dd, lane);
+            mm_acc(dR, &sm.Tm[0][0], 1, LM, acc[4 * CT], lane);
             tile_store(&sm.mR[0][16 * w], LC, -dR, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -624,70 +691,129 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             }
         }
         barrier();  // -dR; every wave's reads of all E rows done
-        // delta E^T for this wave's channels (their E rows, before the update)
-        f32x4 gKt[CT];
-#pragma unroll
-        for (int j = 0; j < CT; ++j) {
-            gKt[j] = zero4();
-            if (!ADJ)
-                mmk<NC>(gKt[j], &sm.D[0][0], LC, 1, &sm.E[state_rows(j)][0], 1, LC, lane);
-        }
-        // dS0' = E + Qb^T dO + Kb^T (-dR), then dS0 = c dS0', carried in E
+        // One stream: delta E^T for this wave's channels (slots 0 .. CT - 1,
+        // from their E rows before the update; not in the adjoint-only mode),
+        // dS0' = E + Qb^T dO + Kb^T (-dR) for its state tiles (slots CT ..
+        // 5 CT - 1), and on waves 0 and 1 the strictly lower -dR delta^T (dL)
+        // and the lower dO delta^T (dA) (slot 5 CT).
+        constexpr int NG = ADJ ? 0 : CT * (NC / 4);  // delta E^T steps
+        constexpr int NU = 4 * CT * (2 * C / 4);     // state-adjoint steps
+        f32x4 g6[5 * CT + 1];
 #pragma unroll
         for (int j = 0; j < CT; ++j)
+            g6[j] = zero4();
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                f32x4 x = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
-                mmk<C>(x, &sm.Qb[0][state_rows(j)], 1, LK, &sm.dO[0][16 * n], LC, 1, lane);
-                mmk<C>(x, &sm.Kb[0][state_rows(j)], 1, LK, &sm.mR[0][16 * n], LC, 1, lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    x[r] *= sm.cS[state_rows(j) + 4 * g4 + r];
-                tile_store(&sm.E[state_rows(j)][16 * n], LC, x, lane);
+        for (int q = 0; q < 4 * CT; ++q)
+            g6[CT + q] = tile_load(&sm.E[state_rows(q / 4)][16 * (q % 4)], LC, lane);
+        g6[5 * CT] = zero4();
+        auto op6 = [&](int st, float& av, float& bv) {
+            if (st < NG) {  // delta E^T, tile j
+                const int j = st / (NC / 4), k = 4 * (st % (NC / 4)) + g4;
+                av = sm.D[i16][k];
+                bv = sm.E[state_rows(j) + i16][k];
+            } else if (st < NG + NU) {  // Qb^T dO, then Kb^T (-dR), tile q = (j, n)
+                const int u = st - NG, q = u / 8, h = u % 8, k = 4 * (h % 4) + g4;
+                const int row = state_rows(q / 4) + i16, col = 16 * (q % 4) + i16;
+                // Qb / Kb and dO / -dR by an offset from one array (same shapes)
+                const float* qk = &sm.Qb[0][0] + (h < 4 ? 0 : OFF_KB_QB);
+                const float* om = &sm.dO[0][0] + (h < 4 ? 0 : OFF_MR_DO);
+                av = qk[k * LK + row];
+                bv = om[k * LC + col];
+            } else {  // (-dR or dO) delta^T
+                const int k = 4 * (st - NG - NU) + g4;
+                const float* om = &sm.dO[0][0] + (w == 0 ? OFF_MR_DO : 0);
+                av = om[i16 * LC + k];
+                bv = sm.D[i16][k];
             }
+        };
+        auto slot6 = [&](int st) {
+            return st < NG ? st / (NC / 4) : st < NG + NU ? CT + (st - NG) / 8 : 5 * CT;
+        };
+        if (!ADJ && w < 2)
+            mm_stream<NG + NU + NC / 4>(g6, op6, slot6);
+        else
+            mm_stream<NG + NU>(g6, op6, slot6);
+#pragma unroll
+        for (int q = 0; q < 4 * CT; ++q) {
+            f32x4 x = g6[CT + q];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                x[r] *= sm.cS[state_rows(q / 4) + 4 * g4 + r];
+            tile_store(&sm.E[state_rows(q / 4)][16 * (q % 4)], LC, x, lane);
+        }
         if constexpr (ADJ) {
             barrier();  // the next chunk's inputs overwrite the LDS arrays
             continue;
         }
-        if (w == 0) {
-            f32x4 m = zero4();  // -dR delta^T, strictly lower
-            mmk<NC>(m, &sm.mR[0][0], LC, 1, &sm.D[0][0], 1, LC, lane);
+        if (w < 2) {
+            const f32x4 m = g6[5 * CT];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * g4 + r;
-                sm.dLm[t][i16] = t > i16 ? m[r] : 0.f;
-            }
-        } else if (w == 1) {
-            f32x4 m = zero4();  // dO delta^T, lower with the diagonal
-            mmk<NC>(m, &sm.dO[0][0], LC, 1, &sm.D[0][0], 1, LC, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g4 + r;
-                sm.dAm[t][i16] = t >= i16 ? m[r] : 0.f;
+                if (w == 0)
+                    sm.dLm[t][i16] = t > i16 ? m[r] : 0.f;
+                else
+                    sm.dAm[t][i16] = t >= i16 ? m[r] : 0.f;
             }
         }
         barrier();  // dL, dA
-        // the rest of the row-space products for this wave's channels, one
-        // 16-channel tile at a time, and their partials (arrays 0, 1, 2:
-        // dKb', dQb', dKt')
+        // One stream: the rest of the row-space products for this wave's
+        // channels, per 16-channel tile j: dKb' = -dR (c S0)^T + dL Kt (slot
+        // 3 j), dQb' = dO (c S0)^T + dA Kt (slot 3 j + 1), dKt' += dL^T Kb +
+        // dA^T Qb (slot 3 j + 2); then their partials (arrays 0, 1, 2)
+        f32x4 g7[3 * CT];
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            g7[3 * j] = zero4();
+            g7[3 * j + 1] = zero4();
+            g7[3 * j + 2] = g6[j];
+        }
+        constexpr int PJ = 2 * (NC / 4) + 4 * (C / 4);  // steps per tile
+        mm_stream<CT * PJ>(
+            g7,
+            [&](int st, float& av, float& bv) {
+                const int c0 = state_rows(st / PJ), u = st % PJ;
+                if (u < NC / 4) {  // -dR (c S0)^T
+                    const int k = 4 * u + g4;
+                    av = sm.mR[i16][k];
+                    bv = sm.S0[c0 + i16][k];
+                } else if (u < NC / 4 + C / 4) {  // dL Kt
+                    const int k = 4 * (u - NC / 4) + g4;
+                    av = sm.dLm[i16][k];
+                    bv = sm.Kt[k][c0 + i16];
+                } else if (u < 2 * (NC / 4) + C / 4) {  // dO (c S0)^T
+                    const int k = 4 * (u - NC / 4 - C / 4) + g4;
+                    av = sm.dO[i16][k];
+                    bv = sm.S0[c0 + i16][k];
+                } else if (u < 2 * (NC / 4) + 2 * (C / 4)) {  // dA Kt
+                    const int k = 4 * (u - 2 * (NC / 4) - C / 4) + g4;
+                    av = sm.dAm[i16][k];
+                    bv = sm.Kt[k][c0 + i16];
+                } else if (u < 2 * (NC / 4) + 3 * (C / 4)) {  // dL^T Kb
+                    const int k = 4 * (u - 2 * (NC / 4) - 2 * (C / 4)) + g4;
+                    av = sm.dLm[k][i16];
+                    bv = sm.Kb[k][c0 + i16];
+                } else {  // dA^T Qb
+                    const int k = 4 * (u - 2 * (NC / 4) - 3 * (C / 4)) + g4;
+                    av = sm.dAm[k][i16];
+                    bv = sm.Qb[k][c0 + i16];
+                }
+            },
+            [&](int st) {
+                const int j = st / PJ, u = st % PJ;
+                return 3 * j + (u < NC / 4 + C / 4 ? 0 : u < 2 * (NC / 4) + 2 * (C / 4) ? 1 : 2);
+            });
 #pragma unroll
         for (int j = 0; j < CT; ++j) {
             const int c0 = state_rows(j);
-            f32x4 gKb = zero4(), gQb = zero4();
-            mmk<NC>(gKb, &sm.mR[0][0], LC, 1, &sm.S0[c0][0], 1, LC, lane);  // -dR (c S0)^T
-            mmk<C>(gKb, &sm.dLm[0][0], LM, 1, &sm.Kt[0][c0], LK, 1, lane);  // + dL Kt
-            mmk<NC>(gQb, &sm.dO[0][0], LC, 1, &sm.S0[c0][0], 1, LC, lane);  // dO (c S0)^T
-            mmk<C>(gQb, &sm.dAm[0][0], LM, 1, &sm.Kt[0][c0], LK, 1, lane);  // + dA Kt
-            mmk<C>(gKt[j], &sm.dLm[0][0], 1, LM, &sm.Kb[0][c0], LK, 1, lane);  // + dL^T Kb
-            mmk<C>(gKt[j], &sm.dAm[0][0], 1, LM, &sm.Qb[0][c0], LK, 1, lane);  // + dA^T Qb
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * g4 + r;
                 if (t < len) {
                     float* pp = a.part + ((size_t)blk * ntok + tok_of(t0 + t)) * DK + c0 + i16;
-                    pp[0] = gKb[r];
-                    pp[ks] = gQb[r];
-                    pp[2 * ks] = gKt[j][r];
+                    pp[0] = g7[3 * j][r];
+                    pp[ks] = g7[3 * j + 1][r];
+                    pp[2 * ks] = g7[3 * j + 2][r];
                 }
             }
         }
