@@ -165,21 +165,30 @@ __device__ __forceinline__ void mm_acc(f32x4& acc, const float* A, int am, int a
 // would drain the pipeline and wait for its first operands).  s is a
 // constant in every call, so op and slot fold to plain LDS reads and a
 // fixed register tile.
-template <int NS, int NA, typename Op, typename Slot>
-__device__ __forceinline__ void mm_stream(f32x4 (&acc)[NA], Op op, Slot slot)
+// An op may also read a factor c for the A value, which the step applies
+// (scale(s) true) only when it issues the product, once the reads are in.
+template <int NS, int NA, typename Op, typename Slot, typename Scale>
+__device__ __forceinline__ void mm_stream(f32x4 (&acc)[NA], Op op, Slot slot, Scale scale)
 {
     constexpr int D = NS < 6 ? NS : 6;
-    float a[NS], b[NS];
+    float a[NS], b[NS], c[NS];
 #pragma unroll
     for (int s = 0; s < D; ++s)
-        op(s, a[s], b[s]);
+        op(s, a[s], b[s], c[s]);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         if (s + D < NS)
-            op(s + D, a[s + D], b[s + D]);
+            op(s + D, a[s + D], b[s + D], c[s + D]);
         __builtin_amdgcn_sched_barrier(0);
-        acc[slot(s)] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc[slot(s)], 0, 0, 0);
+        const float av = scale(s) ? a[s] * c[s] : a[s];
+        acc[slot(s)] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b[s], acc[slot(s)], 0, 0, 0);
     }
+}
+template <int NS, int NA, typename Op, typename Slot>
+__device__ __forceinline__ void mm_stream(f32x4 (&acc)[NA], Op op, Slot slot)
+{
+    mm_stream<NS>(acc, [&](int s, float& a, float& b, float&) { op(s, a, b); }, slot,
+                  [](int) { return false; });
 }
 
 // an accumulator tile to / from LDS: element (4 g + r, i) at p[(4 g + r) ld + i]
@@ -545,18 +554,27 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             barrier();  // T, R
             form_delta();
             barrier();  // delta
+            f32x4 xs[4 * CT];
 #pragma unroll
-            for (int j = 0; j < CT; ++j)
+            for (int q = 0; q < 4 * CT; ++q)
+                xs[q] = tile_load(&sm.S0[state_rows(q / 4)][16 * (q % 4)], LC, lane);
+            // S_C = G'_15 (c S0 + Kt^T delta), the state tiles q = (j, n) as one stream
+            mm_stream<4 * CT * (C / 4)>(
+                xs,
+                [&](int st, float& av, float& bv) {
+                    const int q = st / 4, k = 4 * (st % 4) + g4;
+                    av = sm.Kt[k][state_rows(q / 4) + i16];
+                    bv = sm.D[k][16 * (q % 4) + i16];
+                },
+                [&](int st) { return st / 4; });
 #pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    // S_C = G'_15 (c S0 + Kt^T delta)
-                    f32x4 x = tile_load(&sm.S0[state_rows(j)][16 * n], LC, lane);
-                    mmk<C>(x, &sm.Kt[0][state_rows(j)], 1, LK, &sm.D[0][16 * n], LC, 1, lane);
+            for (int q = 0; q < 4 * CT; ++q) {
+                f32x4 x = xs[q];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        x[r] *= sm.gL[state_rows(j) + 4 * g4 + r];
-                    tile_store(&sm.E[state_rows(j)][16 * n], LC, x, lane);
-                }
+                for (int r = 0; r < 4; ++r)
+                    x[r] *= sm.gL[state_rows(q / 4) + 4 * g4 + r];
+                tile_store(&sm.E[state_rows(q / 4)][16 * (q % 4)], LC, x, lane);
+            }
             barrier();  // readers of this chunk's factors done
         }
 
@@ -598,17 +616,8 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
         }
         if (c > 0)
             issue_rev(c - 1);
-        // E = G'_15 dS_C, in place (this wave's rows)
-#pragma unroll
-        for (int j = 0; j < CT; ++j)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                f32x4 x = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    x[r] *= sm.gL[state_rows(j) + 4 * g4 + r];
-                tile_store(&sm.E[state_rows(j)][16 * n], LC, x, lane);
-            }
+        // E holds dS_C; its uses below apply E = G'_15 dS_C themselves
+        // (the operand Kt G'_15, the delta E^T result, the dS0 update)
         form_M_parts();
         form_A_parts();
         barrier();  // c S0, M parts, A parts, E
@@ -627,22 +636,30 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             // operand in its instruction selection.)
             constexpr bool STREAM5 = !(sizeof(IO) == 4 && DK == 128);
             constexpr int NX = ADJ ? 0 : 4 * CT * (C / 4);
-            f32x4 acc[4 * CT + 1];
+            f32x4 acc[4 * CT + 1], es[4 * CT];
 #pragma unroll
-            for (int q = 0; q < 4 * CT; ++q)
+            for (int q = 0; q < 4 * CT; ++q) {
                 acc[q] = ADJ ? zero4() : tile_load(&sm.S0[state_rows(q / 4)][16 * (q % 4)], LC, lane);
+                es[q] = ADJ ? zero4() : tile_load(&sm.E[state_rows(q / 4)][16 * (q % 4)], LC, lane);
+            }
             acc[4 * CT] = zero4();
+            // T^T for dR = T^T ddelta, read ahead: A(m, k) = T(k, m), k = 4 g + r
+            float tA[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                tA[r] = sm.Tm[4 * g4 + r][i16];
             if constexpr (STREAM5) {
                 mm_stream<NX + DK / 4 + C / 4>(
                     acc,
-                    [&](int st, float& av, float& bv) {
+                    [&](int st, float& av, float& bv, float& cv) {
                         if (st < NX) {  // Kt^T delta, tile q = (j, n)
                             const int q = st / 4, k = 4 * (st % 4) + g4;
                             av = sm.Kt[k][state_rows(q / 4) + i16];
                             bv = sm.D[k][16 * (q % 4) + i16];
-                        } else if (st < NX + DK / 4) {  // Kt E
+                        } else if (st < NX + DK / 4) {  // Kt E = (Kt G'_15) dS_C
                             const int k = 4 * (st - NX) + g4;
                             av = sm.Kt[i16][k];
+                            cv = sm.gL[k];
                             bv = sm.E[k][16 * w + i16];
                         } else {  // A^T dO
                             const int k = 4 * (st - NX - DK / 4) + g4;
@@ -650,38 +667,52 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
                             bv = sm.dO[k][16 * w + i16];
                         }
                     },
-                    [&](int st) { return st < NX ? st / 4 : 4 * CT; });
+                    [&](int st) { return st < NX ? st / 4 : 4 * CT; },
+                    [&](int st) { return st >= NX && st < NX + DK / 4; });
             } else {
 #pragma unroll
                 for (int q = 0; q < (ADJ ? 0 : 4 * CT); ++q)
                     mmk<C>(acc[q], &sm.Kt[0][state_rows(q / 4)], 1, LK, &sm.D[0][16 * (q % 4)], LC,
                            1, lane);
-                mmk<DK>(acc[4 * CT], &sm.Kt[0][0], LK, 1, &sm.E[0][16 * w], LC, 1, lane);
-                mmk<C>(acc[4 * CT], &sm.Am[0][0], 1, LM, &sm.dO[0][16 * w], LC, 1, lane);
+                mm_stream<DK / 4 + C / 4>(
+                    acc,
+                    [&](int st, float& av, float& bv, float& cv) {
+                        if (st < DK / 4) {  // Kt E = (Kt G'_15) dS_C
+                            const int k = 4 * st + g4;
+                            av = sm.Kt[i16][k];
+                            cv = sm.gL[k];
+                            bv = sm.E[k][16 * w + i16];
+                        } else {  // A^T dO
+                            const int k = 4 * (st - DK / 4) + g4;
+                            av = sm.Am[k][i16];
+                            bv = sm.dO[k][16 * w + i16];
+                        }
+                    },
+                    [&](int) { return 4 * CT; }, [&](int st) { return st < DK / 4; });
             }
-            // rowsum over this block's columns of dS_C . X = (E . X') / G'_15:
-            // the partial of the last token's dG (array 3)
+            // rowsum over this block's columns of dS_C . X': the partial of
+            // the last token's dG (array 3)
 #pragma unroll
             for (int j = 0; j < (ADJ ? 0 : CT); ++j) {
                 float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    const f32x4 e = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
+                for (int n = 0; n < 4; ++n)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        rs[r] = fmaf(e[r], acc[4 * j + n][r], rs[r]);
-                }
+                        rs[r] = fmaf(es[4 * j + n][r], acc[4 * j + n][r], rs[r]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = state_rows(j) + 4 * g4 + r;
-                    const float sum = row16_sum(rs[r]) * rcp(sm.gL[row]);
+                    const float sum = row16_sum(rs[r]);
                     if (i16 == 0)
                         a.part[3 * ks + ((size_t)blk * ntok + tok_of(t0 + len - 1)) * DK + row] = sum;
                 }
             }
-            // dR = T^T ddelta
+            // dR = T^T ddelta, ddelta's accumulator as the B operand
             f32x4 dR = zero4();
-            mm_acc(dR, &sm.Tm[0][0], 1, LM, acc[4 * CT], lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dR = __builtin_amdgcn_mfma_f32_16x16x4f32(tA[r], acc[4 * CT][r], dR, 0, 0, 0);
             tile_store(&sm.mR[0][16 * w], LC, -dR, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -702,9 +733,13 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
 #pragma unroll
         for (int j = 0; j < CT; ++j)
             g6[j] = zero4();
+        // dS_C tiles, read now and added as E = G'_15 dS_C after the stream
+        f32x4 es[4 * CT];
 #pragma unroll
-        for (int q = 0; q < 4 * CT; ++q)
-            g6[CT + q] = tile_load(&sm.E[state_rows(q / 4)][16 * (q % 4)], LC, lane);
+        for (int q = 0; q < 4 * CT; ++q) {
+            es[q] = tile_load(&sm.E[state_rows(q / 4)][16 * (q % 4)], LC, lane);
+            g6[CT + q] = zero4();
+        }
         g6[5 * CT] = zero4();
         auto op6 = [&](int st, float& av, float& bv) {
             if (st < NG) {  // delta E^T, tile j
@@ -735,10 +770,12 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             mm_stream<NG + NU>(g6, op6, slot6);
 #pragma unroll
         for (int q = 0; q < 4 * CT; ++q) {
-            f32x4 x = g6[CT + q];
+            f32x4 x;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                x[r] *= sm.cS[state_rows(q / 4) + 4 * g4 + r];
+            for (int r = 0; r < 4; ++r) {
+                const int row = state_rows(q / 4) + 4 * g4 + r;
+                x[r] = sm.cS[row] * fmaf(sm.gL[row], es[q][r], g6[CT + q][r]);
+            }
             tile_store(&sm.E[state_rows(q / 4)][16 * (q % 4)], LC, x, lane);
         }
         if constexpr (ADJ) {
@@ -766,7 +803,8 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
         for (int j = 0; j < CT; ++j) {
             g7[3 * j] = zero4();
             g7[3 * j + 1] = zero4();
-            g7[3 * j + 2] = g6[j];
+            // delta E^T = (delta dS_C^T) G'_15, by the channel of the lane's column
+            g7[3 * j + 2] = g6[j] * sm.gL[state_rows(j) + i16];
         }
         constexpr int PJ = 2 * (NC / 4) + 4 * (C / 4);  // steps per tile
         mm_stream<CT * PJ>(
