@@ -658,7 +658,11 @@ __global__ __launch_bounds__(DK) void kdn_bwd_gr_summary_kernel(BwdArgs args, in
 }
 
 // pass 2: the gradient after every chunk's last token, from the last chunk;
-// the initial variance's gradient at the end
+// the initial variance's gradient at the end.  The chain is serial in the
+// chunks, but its maps are not: they are read GU chunks ahead into a second
+// register set while the current GU are applied, so a long sequence waits
+// for memory once per GU chunks rather than once per chunk.
+constexpr int GU = 16;
 __global__ __launch_bounds__(256) void kdn_bwd_gr_carry_kernel(BwdArgs args, int width, int nchunks)
 {
     const BwdArgs a = args;
@@ -666,11 +670,29 @@ __global__ __launch_bounds__(256) void kdn_bwd_gr_carry_kernel(BwdArgs args, int
     if (row >= (size_t)a.B * a.H * width)
         return;
     const size_t bh = row / width, i = row % width;
+    const float2* maps = reinterpret_cast<const float2*>(a.gr_sum);
+    auto at = [&](int c) { return (bh * nchunks + c) * width + i; };
+    float2 cur[GU], nxt[GU];
+    auto fetch = [&](float2 (&dst)[GU], int top) {
+#pragma unroll
+        for (int u = 0; u < GU; ++u)
+            dst[u] = top - u >= 0 ? maps[at(top - u)] : make_float2(1.f, 0.f);
+    };
     float gbar = a.gvar_T ? a.gvar_T[row] : 0.f;
-    for (int c = nchunks - 1; c >= 0; --c) {
-        const size_t o = (bh * nchunks + c) * width + i;
-        a.gr_carry[o] = gbar;
-        gbar = a.gr_sum[o * 2] * gbar + a.gr_sum[o * 2 + 1];
+    fetch(cur, nchunks - 1);
+    for (int top = nchunks - 1; top >= 0; top -= GU) {
+        if (top - GU >= 0)
+            fetch(nxt, top - GU);
+#pragma unroll
+        for (int u = 0; u < GU; ++u) {
+            if (top - u >= 0) {
+                a.gr_carry[at(top - u)] = gbar;
+                gbar = cur[u].x * gbar + cur[u].y;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < GU; ++u)
+            cur[u] = nxt[u];
     }
     if (a.gvar0)
         a.gvar0[row] = gbar;
@@ -763,17 +785,27 @@ __global__ __launch_bounds__(DK) void kdn_bwd_gr_replay_kernel(BwdArgs args, int
     }
 }
 
-// pass 4: the information scale's gradient per (b,h), summed over chunks
+// pass 4: the information scale's gradient per (b,h), summed over chunks:
+// one workgroup per (b,h), each thread a strided share of the chunks, then a
+// fixed-order tree over the threads (deterministic)
 __global__ __launch_bounds__(256) void kdn_bwd_gr_mu_kernel(BwdArgs args, int nchunks)
 {
     const BwdArgs a = args;
-    const size_t bh = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (bh >= (size_t)a.B * a.H)
-        return;
+    const size_t bh = blockIdx.x;
+    const int t = threadIdx.x;
+    __shared__ float part[256];
     float m = 0.f;
-    for (int c = 0; c < nchunks; ++c)
+    for (int c = t; c < nchunks; c += 256)
         m += a.gr_mu[bh * nchunks + c];
-    a.gmu[bh] = m;
+    part[t] = m;
+    __syncthreads();
+    for (int n = 128; n > 0; n >>= 1) {
+        if (t < n)
+            part[t] += part[t + n];
+        __syncthreads();
+    }
+    if (t == 0)
+        a.gmu[bh] = part[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -838,8 +870,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream)
             return e;
     }
     if (a.gmu) {
-        hipLaunchKernelGGL(kdn_bwd_gr_mu_kernel, dim3((bh + 255) / 256), dim3(256), 0, stream, a,
-                           ngc);
+        hipLaunchKernelGGL(kdn_bwd_gr_mu_kernel, dim3(bh), dim3(256), 0, stream, a, ngc);
         e = hipGetLastError();
     }
     return e;
