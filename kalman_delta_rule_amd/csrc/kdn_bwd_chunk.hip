@@ -42,6 +42,10 @@
 
 #include <type_traits>
 
+// lambdas that must not become calls (a call would pass the captures through
+// scratch memory)
+#define KDN_INLINE __attribute__((always_inline))
+
 namespace kdn {
 namespace cbwd {
 
@@ -311,8 +315,10 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     const IO* vg = reinterpret_cast<const IO*>(a.v);
     const IO* og = reinterpret_cast<const IO*>(a.go);
     IO* dvg = reinterpret_cast<IO*>(a.gv);
-    const bool chth = tid < DK;   // one key channel per thread for the factors
-    const int ch = tid;
+    // the factors: 256 / DK threads per key channel (one per wave group of
+    // DK / 64 waves), each its channel's decays and a share of the tokens
+    constexpr int FP = 256 / DK, FT = C / FP;  // threads per channel, tokens per thread
+    const int ch = (w % (DK / 64)) * 64 + lane, fpart = w / (DK / 64);  // fpart wave-uniform
     const int et = (tid * 4) / NC, ec = (tid * 4) % NC;  // this thread's 4 elements of a [C][NC] block
 
     // The chunk's inputs, loaded one chunk ahead into registers (16 bytes
@@ -376,38 +382,51 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             if (tid < C)
                 sm.inP[tid][0] = braw;
     };
-    auto factors = [&](int c, bool rev) {
+    auto factors_part = [&](auto part_tag, int c, bool rev) KDN_INLINE {
+        constexpr int tb = decltype(part_tag)::value * FT;  // this thread's first token
         const int t0 = c * C, len = min(C, T - t0);
-        if (chth) {
-            const IO* sk = reinterpret_cast<const IO*>(&sm.inK[0]);
-            float al[C], kk[C], qq[C], kap[C];
+        const IO* sk = reinterpret_cast<const IO*>(&sm.inK[0]);
+        float al[C], kk[FT], qq[FT], kap[FT];
 #pragma unroll
-            for (int t = 0; t < C; ++t) {
-                al[t] = sm.inA[t][ch];
-                kk[t] = to_f32(sk[t * DK + ch]);
-                qq[t] = rev ? to_f32(sk[C * DK + t * DK + ch]) : 0.f;
-                kap[t] = ISO ? sm.inP[t][0] : sm.inP[t][ch];
-            }
+        for (int t = 0; t < C; ++t)
+            al[t] = t < len ? sm.inA[t][ch] : 1.f;
 #pragma unroll
-            for (int t = 0; t < C; ++t) {
-                const bool ok = t < len;
-                al[t] = ok ? al[t] : 1.f;
-                kk[t] = ok ? kk[t] : 0.f;
-                qq[t] = ok ? qq[t] : 0.f;
-                kap[t] = ok ? (ISO ? kap[t] * kk[t] : kap[t]) : 0.f;
-            }
-            ChanDecay d;
-            chan_decay(al, d);
+        for (int u = 0; u < FT; ++u) {
+            const int t = tb + u;
+            const bool ok = t < len;
+            const float kv = to_f32(sk[t * DK + ch]);
+            const float pv = ISO ? sm.inP[t][0] : sm.inP[t][ch];
+            kk[u] = ok ? kv : 0.f;
+            qq[u] = ok && rev ? to_f32(sk[C * DK + t * DK + ch]) : 0.f;
+            kap[u] = ok ? (ISO ? pv * kv : pv) : 0.f;
+        }
+        ChanDecay d;
+        chan_decay(al, d);  // every thread of the channel: the same operations
 #pragma unroll
-            for (int t = 0; t < C; ++t) {
-                const float G = d.g[t + 1];
-                sm.Kb[t][ch] = kk[t] * G;
-                sm.Qb[t][ch] = qq[t] * G;
-                sm.Kt[t][ch] = kap[t] * rcp(G);
-            }
+        for (int u = 0; u < FT; ++u) {
+            const float G = d.g[tb + u + 1];
+            sm.Kb[tb + u][ch] = kk[u] * G;
+            sm.Qb[tb + u][ch] = qq[u] * G;
+            sm.Kt[tb + u][ch] = kap[u] * rcp(G);
+        }
+        if (tb == 0) {
             sm.cS[ch] = __builtin_amdgcn_ldexpf(1.f, d.m);
             sm.gL[ch] = d.g[C];
         }
+    };
+    auto factors = [&](int c, bool rev) KDN_INLINE {
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2 % FP>;
+        using I3 = std::integral_constant<int, 3 % FP>;
+        if (fpart == 0)
+            factors_part(I0{}, c, rev);
+        else if (fpart == 1)
+            factors_part(I1{}, c, rev);
+        else if (fpart == 2)
+            factors_part(I2{}, c, rev);
+        else
+            factors_part(I3{}, c, rev);
     };
     // M = Kb Kt^T, by waves 2 and 3 over half of the key channels each
     auto form_M_parts = [&]() {
