@@ -322,7 +322,9 @@ kdn_status kdn_gates_from_preact(int variant, int B, int T, int H, int dk, int i
  * dk in {64, 128}, dv a multiple of 16 up to 256; fp32 arithmetic whatever
  * the io type.  q, k, v, d_o and alpha are 16-byte aligned, the other fp32
  * arrays 4-byte aligned, dq / dk / dv aligned to their element size.  The
- * forward is recomputed inside: the gain, then the state at every 16th token.
+ * forward is recomputed inside: the gain, then the state at every 16th token
+ * (Diagonal with bf16 io and dv a multiple of 64: by the forward walk with
+ * split-bf16 products, ~1e-5 relative; otherwise in fp32 products).
  * With dv a multiple of 64 the memory part runs in 16-token chunks on the
  * matrix cores (fp32 products); otherwise token by token from stored
  * innovations.  The workspace (kdn_bwd_workspace_size bytes, 16-byte aligned)

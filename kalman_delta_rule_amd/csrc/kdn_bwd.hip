@@ -832,8 +832,43 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream)
     }
     hipError_t e;
     if (chunked) {
-        e = a.nseg ? launch_seqpar_bwd_mem(a, ISO, stream)
-                   : launch_bwd_chunk_mem(a, ISO, sizeof(IO) == 2 ? 1 : 0, false, stream);
+        if (a.nseg) {
+            e = launch_seqpar_bwd_mem(a, ISO, stream);
+        } else if (!ISO && sizeof(IO) == 2 && a.T > 0) {
+            // Diagonal with bf16 io: the chunk-start states from the forward
+            // walk (state only, split-bf16 products, ~1e-5 relative), in place
+            // of the chunk kernel's own fp32 forward pass
+            FwdArgs w{};
+            w.q = a.q;
+            w.k = a.k;
+            w.v = a.v;
+            w.alpha = a.alpha;
+            w.omega = a.omega;
+            w.r = a.r;
+            w.S0 = a.S0;
+            w.var0 = a.var0;
+            w.c0 = a.c0;
+            w.mu = a.mu;
+            w.mu_h = a.mu_h;
+            w.S_T = a.walk_S;
+            w.var_T = a.walk_p;
+            w.B = a.B;
+            w.T = a.T;
+            w.H = a.H;
+            w.dk = DK;
+            w.dv = a.dv;
+            w.split = true;
+            w.state_only = 1;
+            w.ckpt = a.ckpt;
+            e = launch_walk_fwd(w, false, stream);
+            if (e != hipSuccess)
+                return e;
+            BwdArgs ac = a;
+            ac.ckpt_given = true;
+            e = launch_bwd_chunk_mem(ac, ISO, 1, false, stream);
+        } else {
+            e = launch_bwd_chunk_mem(a, ISO, sizeof(IO) == 2 ? 1 : 0, false, stream);
+        }
     } else {
         hipLaunchKernelGGL((kdn_bwd_mem_kernel<IO, ISO, DK>), dim3(nblk, bh), dim3(256), 0, stream,
                            a);

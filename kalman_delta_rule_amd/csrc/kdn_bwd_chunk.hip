@@ -541,7 +541,8 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     };
 
     // ---------------- forward pass: every chunk-start state ----------------
-    if constexpr (!ADJ) {
+    // (not when the caller's forward walk has stored the chunk-start states)
+    if (!ADJ && !a.ckpt_given) {
         state_init(a.S0);
         if (nch > 0)
             issue(0, false);
@@ -553,19 +554,19 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             if (c + 1 < nch)
                 issue(c + 1, false);
             form_M_parts();
-            // c S0 into LDS; the chunk-start state to the workspace
+            // c S0 into LDS; the chunk-start state to the workspace (rows in
+            // fours: the lane's four rows of a tile are one 16-byte store)
             float* ckc = ck_wg + (size_t)c * (DK * NC);
 #pragma unroll
             for (int j = 0; j < CT; ++j)
 #pragma unroll
                 for (int n = 0; n < 4; ++n) {
                     f32x4 x = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
+                    const int rq = (state_rows(j) + 4 * g4) / 4;
+                    *reinterpret_cast<f32x4*>(ckc + (rq * NC + 16 * n + i16) * 4) = x;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = state_rows(j) + 4 * g4 + r;
-                        ckc[row * NC + 16 * n + i16] = x[r];
-                        x[r] *= sm.cS[row];
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        x[r] *= sm.cS[state_rows(j) + 4 * g4 + r];
                     tile_store(&sm.S0[state_rows(j)][16 * n], LC, x, lane);
                 }
             barrier();  // M parts, c S0
@@ -625,12 +626,12 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
         if constexpr (!ADJ) {
 #pragma unroll
             for (int j = 0; j < NCK; ++j) {
-                const int e = 4 * (tid + 256 * j), row = e / NC, cc = e % NC;
-                const float cs = sm.cS[row];
-                sm.S0[row][cc] = ck[j].x * cs;
-                sm.S0[row][cc + 1] = ck[j].y * cs;
-                sm.S0[row][cc + 2] = ck[j].z * cs;
-                sm.S0[row][cc + 3] = ck[j].w * cs;
+                // piece p: rows 4 (p / NC) .. + 3 of column p % NC
+                const int p = tid + 256 * j, row = 4 * (p / NC), cc = p % NC;
+                sm.S0[row][cc] = ck[j].x * sm.cS[row];
+                sm.S0[row + 1][cc] = ck[j].y * sm.cS[row + 1];
+                sm.S0[row + 2][cc] = ck[j].z * sm.cS[row + 2];
+                sm.S0[row + 3][cc] = ck[j].w * sm.cS[row + 3];
             }
         }
         if (c > 0)

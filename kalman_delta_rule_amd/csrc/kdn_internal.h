@@ -58,6 +58,10 @@ struct FwdArgs {
     // omega, are then not read.  r, and Isotropic omega, stay fp32 gates.
     const void* a_pre = nullptr;
     const void* w_pre = nullptr;
+    // split-product Diagonal walk with state_only = 1 only, nullable: the
+    // state at the start of every 16-token chunk, per (b, h, 64-column tile)
+    // and chunk a [dk / 4][64][4] fp32 block (rows in fours)
+    float* ckpt = nullptr;
 };
 
 struct StepArgs {

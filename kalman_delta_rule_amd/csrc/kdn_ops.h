@@ -90,7 +90,11 @@ struct BwdArgs {
     float* gr_carry; // gain backward: carried gradient after each chunk
     float* gr_tok;   // gain backward: dbar / betabar per token
     float* gr_mu;    // gain backward: information-scale gradient per (b,h) and chunk
-    float* ckpt;   // [B*H][dv/16][ceil(T/16)][dk][16]: S at every 16th token
+    float* ckpt;   // S at every 16th token: token-serial path [B*H][dv/16][ceil(T/16)][dk][16];
+                   // chunked path [B*H][dv/64][ceil(T/16)][dk/4][64][4] (rows in fours)
+    bool ckpt_given = false;  // chunked path: ckpt already holds every chunk-start state
+    float* walk_S = nullptr;  // Diagonal chunked path: the checkpoint walk's final state
+    float* walk_p = nullptr;  // and final variance (not outputs)
     float* dlt;    // [B*H][dv/16][T][16]: innovations delta of every token
     float* part;   // [4][dv/16][B*T*H][dk]: per-column-block partial row sums
     // the split over the sequence (kdn_seqpar.hip): segments (0: none) and

@@ -107,6 +107,8 @@ size_t bwd_workspace_floats(bool iso, int B, int T, int H, int dk, int dv)
     n += round64(bh * nch * dk * dv);        // checkpoints
     if (!chunked)
         n += round64(ntok * dv);             // innovations
+    if (chunked && !iso && T > 0)            // the checkpoint walk's final state and variance
+        n += round64(bh * dk * dv) + round64(bh * dk);
     n += round64(4 * nblk * ntok * dk);      // partials
     return n;
 }
@@ -146,6 +148,13 @@ void bwd_carve_workspace(BwdArgs& a, bool iso, float* ws)
     if (!chunked) {
         a.dlt = p;
         p += round64(ntok * a.dv);
+    }
+    a.walk_S = a.walk_p = nullptr;
+    if (chunked && !iso && a.T > 0) {
+        a.walk_S = p;
+        p += round64(bh * a.dk * a.dv);
+        a.walk_p = p;
+        p += round64(bh * a.dk);
     }
     a.part = p;
 }

@@ -349,11 +349,20 @@ hipError_t launch_seqpar_bwd_mem(const BwdArgs& a, bool iso, hipStream_t stream)
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     // 6. the per-token gradients, every segment from its entry state and
-    // incoming adjoint
+    // incoming adjoint; the chunk-start states from a state-only walk of the
+    // segments from their entry states
+    FwdArgs wc = w;
+    wc.S0 = Sin;
+    wc.S_T = Nb;  // not needed again
+    wc.state_only = 1;
+    wc.ckpt = a.ckpt;
+    if ((e = launch_walk_fwd(wc, iso, stream)) != hipSuccess)
+        return e;
     BwdArgs vf = v;
     vf.S0 = Sin;
     vf.gS_T = Xin;
     vf.gS0 = nullptr;
+    vf.ckpt_given = true;
     return launch_bwd_chunk_mem(vf, iso, 1, false, stream);
 }
 

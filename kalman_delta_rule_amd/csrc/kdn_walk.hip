@@ -221,6 +221,7 @@ struct Cfg {
     // state-only walks (S_T and the variance, no outputs): SO_ = 1 reads no q
     // and writes no o; SO_ = 2 also takes v = 0 without reading it, so that
     // the innovation is -Kb S
+    static constexpr int SO = SO_;
     static constexpr bool NOQ = SO_ > 0;
     static constexpr bool NOV = SO_ == 2;
     static_assert(SO_ >= 0 && SO_ <= 2 && !(SO_ && OF32_), "state-only mode");
@@ -536,6 +537,15 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
             // fetched during step c, into the registers the front products of
             // chunk c have just consumed; T and Aqk (hi, lo) are read after
             // the barrier with v
+            // The state-only walk from the real v (SO = 1) can also store the
+            // state at every chunk start (the backward's checkpoints): per
+            // (b, h, tile) and chunk a [DK / 4][DVT][4] block, rows in fours,
+            // so each accumulator tile is one 16-byte store per lane.
+            float* ck = nullptr;
+            if constexpr (CF::SO == 1)
+                if (a.ckpt)
+                    ck = a.ckpt + ((size_t)bh * ntiles + tile) * nchunks * (size_t)(DK * DVT) +
+                         (size_t)(g4 * DVT + 16 * NB * w + c16) * 4;
             struct MemOpsX {
                 bf16x8 kh[DK / 32], kl[DK / 32], qh[DK / 32], ql[DK / 32];
                 int cfl;  // the chunk's decay-reference flag
@@ -561,6 +571,16 @@ __global__ __launch_bounds__(64 * CF::NWAVES, 1) void kdn_walk_fwd_kernel(FwdArg
                 const auto& tri = sm.tri[c % 3];
                 const bf16* V = sm.v[c % 3];
                 const int cfl = m.cfl;
+                if constexpr (CF::SO == 1) {
+                    if (ck) {  // the chunk-start state, before any decay reference
+                        float* p = ck + (size_t)c * (DK * DVT);
+#pragma unroll
+                        for (int n = 0; n < DK / 16; ++n)
+#pragma unroll
+                            for (int nb = 0; nb < NB; ++nb)
+                                *reinterpret_cast<f32x4*>(p + (4 * n * DVT + 16 * nb) * 4) = Sacc[nb][n];
+                    }
+                }
                 const bf16x4 th = *reinterpret_cast<const bf16x4*>(tri.T + c16 * C + 4 * g4);
                 const bf16x4 tl = *reinterpret_cast<const bf16x4*>(tri.Tl + c16 * C + 4 * g4);
                 bf16x4 ah{}, al{};
@@ -1792,6 +1812,9 @@ static hipError_t launch_state_only(const FwdArgs& a, bool iso, hipStream_t stre
 hipError_t launch_walk_fwd(const FwdArgs& a, bool iso, hipStream_t stream)
 {
     using namespace walk;
+    // chunk-start states: the split-product Diagonal state-only walk only
+    if (a.ckpt && (iso || !a.split || a.state_only != 1 || a.a_pre))
+        return hipErrorInvalidValue;
     if (a.a_pre) {
         if (a.state_only || a.o_f32)
             return hipErrorInvalidValue;

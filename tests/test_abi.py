@@ -369,7 +369,9 @@ def test_bwd_validation(L):
         # the gain backward's scan: (A, B) and carry per chunk and width, a
         # scalar per token, an information-scale part per chunk
         grad = lambda width: r64(B * H * width * 2) + r64(B * H * width) + r64(ntok) + r64(B * H)
-        diag = 2 * r64(ntok * dk) + r64(ntok) + scan(dk) + grad(dk) + common
+        # Diagonal chunked: the checkpoint walk's final state and variance
+        walk = r64(B * H * dk * dv) + r64(B * H * dk) if chunked else 0
+        diag = 2 * r64(ntok * dk) + r64(ntok) + scan(dk) + grad(dk) + common + walk
         iso = r64(ntok * 4) + scan(1) + grad(1) + common
         assert L.kdn_bwd_workspace_size(0, B, T, H, dk, dv) == 4 * diag, dv
         assert L.kdn_bwd_workspace_size(1, B, T, H, dk, dv) == 4 * iso, dv
@@ -381,9 +383,10 @@ def test_bwd_validation(L):
         ntok, nch, ngc = B * T * H, (T + 15) // 16, (T + 63) // 64
         width = 1 if iso else dk
         pieces = r64(ntok * 4) if iso else 2 * r64(ntok * dk) + r64(ntok)
+        walk = 0 if iso else r64(B * H * dk * dv) + r64(B * H * dk)
         return (pieces + r64(B * H * ngc * width * 5) + r64(B * H * ngc * width * 2)
                 + r64(B * H * ngc * width) + r64(ntok) + r64(B * H * ngc)
-                + r64(B * H * nch * dk * dv) + r64(4 * (dv // 64) * ntok * dk))
+                + r64(B * H * nch * dk * dv) + r64(4 * (dv // 64) * ntok * dk) + walk)
     for (B, T, H, d, S) in ((1, 65536, 16, 128, 8), (1, 2048, 16, 128, 2), (4, 2048, 16, 128, 2),
                             (1, 8192, 1, 64, 8), (1, 4096, 2, 64, 4)):
         seg = 2 * r64(B * S * H * d) + 6 * r64(B * S * H * d * d)
