@@ -182,12 +182,17 @@ def test_bwd_config3_long_full(ora):
     _bwd_full(ora, 3, 1, heads=[(0, 11)])
 
 
-@pytest.mark.parametrize("regime", ["mu0", "slow_decay", "fast_decay", "noisy", "strong_decay"])
-def test_bwd_regimes(ora, regime):
+@pytest.mark.parametrize("regime,io", [("mu0", "f32"), ("slow_decay", "f32"), ("fast_decay", "f32"),
+                                       ("noisy", "f32"), ("strong_decay", "f32"),
+                                       ("slow_decay", "bf16"), ("strong_decay", "bf16")])
+def test_bwd_regimes(ora, regime, io):
     # the backward away from the default gate draws: no information scaling
     # (mu = 0), decay close to 1 (long memory, large states), fast decay, and
-    # observation noise r much larger than the predicted variance
-    variant, io, B, T, H, dk, dv = "diag", "f32", 1, 90, 2, 128, 64
+    # observation noise r much larger than the predicted variance.  With bf16
+    # io the Diagonal chunk-start states come from the forward walk (which
+    # takes its own decay reference on the strongly decaying channels), with
+    # fp32 io from the chunk kernel's fp32 forward pass.
+    variant, B, T, H, dk, dv = "diag", 1, 90, 2, 128, 64
     x = _case(variant, io, B, T, H, dk, dv, seed=800 + len(regime))
     rng = np.random.default_rng(801)
     mu = None
