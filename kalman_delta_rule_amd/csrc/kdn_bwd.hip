@@ -18,7 +18,11 @@
 //   A  gain forward recompute by the chunk-parallel Moebius gain scan
 //      (kdn_gain.hip): kap_t, p_{t-1} and r + z_t (Isotropic: beta_t, b_{t-1},
 //      mean alpha^2, |k|^2) for every token.
-//   B  memory backward, one 256-thread workgroup per (b,h) and 16-column
+//   B  memory backward.  With dv a multiple of 64 in 16-token chunks on the
+//      matrix cores (kdn_bwd_chunk.hip; for Diagonal with bf16 io its
+//      chunk-start states come from the state-only forward walk, and few-head
+//      long shapes split over the sequence, kdn_seqpar.hip).  Otherwise token
+//      by token here: one 256-thread workgroup per (b,h) and 16-column
 //      block of the value dimension (the columns of S evolve independently
 //      given the gain).  A forward pass stores S every 16 tokens and every
 //      token's innovations; then for each 16-token chunk, last first, the
@@ -26,7 +30,8 @@
 //      innovations are known) and walked backwards.  dv is complete per column and
 //      written here; the four row vectors that sum over all columns (dq, kapbar,
 //      dk and dalpha of the memory) are written as per-block partials.
-//   C  partial merge (dq and the summed row vectors), then the variance
+//   C  partial merge (dq and the summed row vectors; the chunked path's own
+//      finishing kernel does this), then the variance
 //      recurrence's adjoint as a chunked affine scan (summaries, carry,
 //      replay), writing dk, dalpha, domega, dr and the initial variance's and
 //      information scale's gradients.

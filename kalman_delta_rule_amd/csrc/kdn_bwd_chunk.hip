@@ -27,11 +27,15 @@
 // gradient is that of the raised value (zero).
 //
 // One workgroup of four waves per (batch, head, 64 value columns).  A forward
-// pass over the chunks stores every chunk-start state (this block's columns);
-// the reverse pass then takes the chunks last first.  The carried state (and
-// then its adjoint) stays in accumulators, split by key channels over the
-// waves; products that contract over key channels or tokens take their
-// operands from LDS.  Everything per token and key channel is linear in
+// pass over the chunks stores every chunk-start state (this block's columns;
+// skipped when the caller's state-only forward walk has stored them), then
+// the reverse pass takes the chunks last first.  The carried state (and then
+// its adjoint) stays in LDS, each wave owning the rows of its key channels;
+// every product is an fp32 16x16x4 matrix-core product with operands from
+// LDS (or an accumulator tile as the B operand over its own row index), the
+// products of a phase run as one software pipeline (mm_stream), and a
+// chunk's inputs are loaded into registers one chunk ahead.  Everything per
+// token and key channel is linear in
 // dKb, dQb, dKt and the rowsum term, which sum over the value columns: each
 // block writes its partials of those, and a second kernel (one thread per
 // chunk and channel) sums the blocks and forms dq, kapbar and the memory's
