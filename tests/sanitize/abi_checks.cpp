@@ -129,6 +129,17 @@ static void other_checks()
     EXPECT(kdn_bwd(KDN_DIAG, 1, 64, 2, 64, 64, KDN_BF16, 64.f, nullptr, at(P), at(P), at(P), fat(P), fat(P),
                    fat(P), nullptr, nullptr, nullptr, at(P), nullptr, nullptr, at(dq), at(dk), at(dv),
                    fat(da), fat(dw), fat(dr), nullptr, nullptr, nullptr, at(ws), bws, nullptr) == KDN_ERR_HIP);
+    // a shape the backward splits over the sequence (2 segments of 1024
+    // tokens): its full workspace, and one byte short of it (the same call
+    // without the split), both reach the launch
+    const size_t sws = kdn_bwd_workspace_size(KDN_DIAG, 1, 2048, 2, 64, 64);
+    EXPECT(sws > kdn_bwd_workspace_size(KDN_ISO, 1, 2048, 2, 64, 64));
+    const size_t wbs[2] = {sws, sws - 1};
+    for (const size_t wb : wbs)
+        EXPECT(kdn_bwd(KDN_DIAG, 1, 2048, 2, 64, 64, KDN_BF16, 64.f, nullptr, at(P), at(P), at(P), fat(P),
+                       fat(P), fat(P), nullptr, nullptr, nullptr, at(P), nullptr, nullptr, at(dq), at(dk),
+                       at(dv), fat(da), fat(dw), fat(dr), fat(ws), nullptr, nullptr, at(ws + (1ull << 27)),
+                       wb, nullptr) == KDN_ERR_HIP);
     // forward from pre-activations
     const size_t pws = kdn_fwd_preact_workspace_size(KDN_DIAG, 1, 64, 2, 64);
     EXPECT(kdn_fwd_preact(KDN_DIAG, 1, 64, 2, 64, 64, KDN_BF16, 64.f, nullptr, at(P), at(P), at(P), at(P),
