@@ -609,13 +609,20 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     // ---------------- reverse pass ----------------
     state_init(a.gS_T);
     // this block's chunk-start states, loaded one chunk ahead with the inputs
-    float4 ck[NCK];
+    // Thread (tid / 16, tid % 16) takes the four columns 4 (tid % 16) .. + 3
+    // of row quads tid / 16 + 16 jq: four 16-byte pieces per quad, which it
+    // writes to LDS as four 16-byte rows (a 4 x 4 transpose in registers).
+    static_assert(NCK % 4 == 0 && NC == 64, "chunk-start state pieces");
+    f32x4 ck[NCK];
+    const int ck_cg = tid % 16, ck_rq = tid / 16;
     auto issue_rev = [&](int c) {
         if constexpr (!ADJ) {
-            const float4* src = reinterpret_cast<const float4*>(ck_wg + (size_t)c * (DK * NC));
+            const f32x4* src = reinterpret_cast<const f32x4*>(ck_wg + (size_t)c * (DK * NC));
 #pragma unroll
-            for (int j = 0; j < NCK; ++j)
-                ck[j] = src[tid + 256 * j];
+            for (int jq = 0; jq < NCK / 4; ++jq)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    ck[4 * jq + u] = src[(ck_rq + 16 * jq) * NC + 4 * ck_cg + u];
         }
         issue(c, true);
     };
@@ -629,14 +636,13 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
         barrier();  // factors, cS, gL; the staging arrays are free
         if constexpr (!ADJ) {
 #pragma unroll
-            for (int j = 0; j < NCK; ++j) {
-                // piece p: rows 4 (p / NC) .. + 3 of column p % NC
-                const int p = tid + 256 * j, row = 4 * (p / NC), cc = p % NC;
-                sm.S0[row][cc] = ck[j].x * sm.cS[row];
-                sm.S0[row + 1][cc] = ck[j].y * sm.cS[row + 1];
-                sm.S0[row + 2][cc] = ck[j].z * sm.cS[row + 2];
-                sm.S0[row + 3][cc] = ck[j].w * sm.cS[row + 3];
-            }
+            for (int jq = 0; jq < NCK / 4; ++jq)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * (ck_rq + 16 * jq) + r;
+                    const f32x4 v{ck[4 * jq][r], ck[4 * jq + 1][r], ck[4 * jq + 2][r], ck[4 * jq + 3][r]};
+                    *reinterpret_cast<f32x4*>(&sm.S0[row][4 * ck_cg]) = v * sm.cS[row];
+                }
         }
         if (c > 0)
             issue_rev(c - 1);
