@@ -78,6 +78,7 @@ struct Smem {
     float Mp[2][C][LM];  // Kb Kt^T over each half of the key channels
     float cS[DK];      // c per channel
     float gL[DK];      // G'_15 per channel
+    float rsum[DK];    // the last token's rowsum, its (c S0) part (the wave's own rows)
     // the chunk's per-channel inputs as loaded (rows of tokens), read back
     // one channel per thread for the factors
     float inA[C][DK];  // alpha
@@ -658,91 +659,58 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             barrier();  // delta
         }
         {
-            // One stream: X' = c S0 + Kt^T delta for this wave's state tiles
-            // (slots 0 .. 4 CT - 1; not in the adjoint-only mode), then
-            // ddelta = Kt E + A^T dO for column tile w (slot 4 CT).  (The
-            // fp32-io d_k = 128 instantiation runs them as separate products:
-            // the stream there makes this ROCm compiler fail on an invalid
-            // operand in its instruction selection.)
-            constexpr bool STREAM5 = !(sizeof(IO) == 4 && DK == 128);
-            constexpr int NX = ADJ ? 0 : 4 * CT * (C / 4);
-            f32x4 acc[4 * CT + 1], es[4 * CT];
+            // ddelta = Kt E + A^T dO for column tile w, as one stream.  The
+            // last token's dG also takes rowsum(dS_C . X'), X' = c S0 + Kt^T
+            // delta, over this block's columns; by linearity it is
+            // rowsum(dS_C . c S0) (here, into rsum) plus sum_t Kt[t] (delta
+            // dS_C^T)[t], which the next phase's delta E^T product gives.
+            if constexpr (!ADJ) {
 #pragma unroll
-            for (int q = 0; q < 4 * CT; ++q) {
-                acc[q] = ADJ ? zero4() : tile_load(&sm.S0[state_rows(q / 4)][16 * (q % 4)], LC, lane);
-                es[q] = ADJ ? zero4() : tile_load(&sm.E[state_rows(q / 4)][16 * (q % 4)], LC, lane);
+                for (int j = 0; j < CT; ++j) {
+                    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int n = 0; n < 4; ++n) {
+                        const f32x4 e = tile_load(&sm.E[state_rows(j)][16 * n], LC, lane);
+                        const f32x4 x = tile_load(&sm.S0[state_rows(j)][16 * n], LC, lane);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            rs[r] = fmaf(e[r], x[r], rs[r]);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float sum = row16_sum(rs[r]);
+                        if (i16 == 0)
+                            sm.rsum[state_rows(j) + 4 * g4 + r] = sum;
+                    }
+                }
             }
-            acc[4 * CT] = zero4();
+            f32x4 acc[1];
+            acc[0] = zero4();
             // T^T for dR = T^T ddelta, read ahead: A(m, k) = T(k, m), k = 4 g + r
             float tA[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 tA[r] = sm.Tm[4 * g4 + r][i16];
-            if constexpr (STREAM5) {
-                mm_stream<NX + DK / 4 + C / 4>(
-                    acc,
-                    [&](int st, float& av, float& bv, float& cv) {
-                        if (st < NX) {  // Kt^T delta, tile q = (j, n)
-                            const int q = st / 4, k = 4 * (st % 4) + g4;
-                            av = sm.Kt[k][state_rows(q / 4) + i16];
-                            bv = sm.D[k][16 * (q % 4) + i16];
-                        } else if (st < NX + DK / 4) {  // Kt E = (Kt G'_15) dS_C
-                            const int k = 4 * (st - NX) + g4;
-                            av = sm.Kt[i16][k];
-                            cv = sm.gL[k];
-                            bv = sm.E[k][16 * w + i16];
-                        } else {  // A^T dO
-                            const int k = 4 * (st - NX - DK / 4) + g4;
-                            av = sm.Am[k][i16];
-                            bv = sm.dO[k][16 * w + i16];
-                        }
-                    },
-                    [&](int st) { return st < NX ? st / 4 : 4 * CT; },
-                    [&](int st) { return st >= NX && st < NX + DK / 4; });
-            } else {
-#pragma unroll
-                for (int q = 0; q < (ADJ ? 0 : 4 * CT); ++q)
-                    mmk<C>(acc[q], &sm.Kt[0][state_rows(q / 4)], 1, LK, &sm.D[0][16 * (q % 4)], LC,
-                           1, lane);
-                mm_stream<DK / 4 + C / 4>(
-                    acc,
-                    [&](int st, float& av, float& bv, float& cv) {
-                        if (st < DK / 4) {  // Kt E = (Kt G'_15) dS_C
-                            const int k = 4 * st + g4;
-                            av = sm.Kt[i16][k];
-                            cv = sm.gL[k];
-                            bv = sm.E[k][16 * w + i16];
-                        } else {  // A^T dO
-                            const int k = 4 * (st - DK / 4) + g4;
-                            av = sm.Am[k][i16];
-                            bv = sm.dO[k][16 * w + i16];
-                        }
-                    },
-                    [&](int) { return 4 * CT; }, [&](int st) { return st < DK / 4; });
-            }
-            // rowsum over this block's columns of dS_C . X': the partial of
-            // the last token's dG (array 3)
-#pragma unroll
-            for (int j = 0; j < (ADJ ? 0 : CT); ++j) {
-                float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int n = 0; n < 4; ++n)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        rs[r] = fmaf(es[4 * j + n][r], acc[4 * j + n][r], rs[r]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = state_rows(j) + 4 * g4 + r;
-                    const float sum = row16_sum(rs[r]);
-                    if (i16 == 0)
-                        a.part[3 * ks + ((size_t)blk * ntok + tok_of(t0 + len - 1)) * DK + row] = sum;
-                }
-            }
+            mm_stream<DK / 4 + C / 4>(
+                acc,
+                [&](int st, float& av, float& bv, float& cv) {
+                    if (st < DK / 4) {  // Kt E = (Kt G'_15) dS_C
+                        const int k = 4 * st + g4;
+                        av = sm.Kt[i16][k];
+                        cv = sm.gL[k];
+                        bv = sm.E[k][16 * w + i16];
+                    } else {  // A^T dO
+                        const int k = 4 * (st - DK / 4) + g4;
+                        av = sm.Am[k][i16];
+                        bv = sm.dO[k][16 * w + i16];
+                    }
+                },
+                [&](int) { return 0; }, [&](int st) { return st < DK / 4; });
             // dR = T^T ddelta, ddelta's accumulator as the B operand
             f32x4 dR = zero4();
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                dR = __builtin_amdgcn_mfma_f32_16x16x4f32(tA[r], acc[4 * CT][r], dR, 0, 0, 0);
+                dR = __builtin_amdgcn_mfma_f32_16x16x4f32(tA[r], acc[0][r], dR, 0, 0, 0);
             tile_store(&sm.mR[0][16 * w], LC, -dR, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -828,6 +796,29 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
         // channels, per 16-channel tile j: dKb' = -dR (c S0)^T + dL Kt (slot
         // 3 j), dQb' = dO (c S0)^T + dA Kt (slot 3 j + 1), dKt' += dL^T Kb +
         // dA^T Qb (slot 3 j + 2); then their partials (arrays 0, 1, 2)
+        // the last token's rowsum: its (c S0) part plus sum_t Kt[t][k] (delta
+        // dS_C^T)[t][k] (the sum over t: four rows in the lane, then the
+        // four lane groups), for channel k = this wave's row of lane i16
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            float v = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                v = fmaf(sm.Kt[4 * g4 + r][state_rows(j) + i16], g6[j][r], v);
+            // lanes l and l ^ 32, then l and l ^ 16: with both operands v,
+            // each swap leaves the lane's and its partner's value in the pair
+            const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                              false, false);
+            v = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+            const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                              false, false);
+            v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+            if (g4 == 0) {
+                const int row = state_rows(j) + i16;
+                a.part[3 * ks + ((size_t)blk * ntok + tok_of(t0 + len - 1)) * DK + row] =
+                    sm.rsum[row] + v;
+            }
+        }
         f32x4 g7[3 * CT];
 #pragma unroll
         for (int j = 0; j < CT; ++j) {
