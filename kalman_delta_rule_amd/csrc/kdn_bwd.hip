@@ -588,19 +588,35 @@ __device__ __forceinline__ void gr_load(const BwdArgs& a, size_t kstride, size_t
 }
 
 // Fill g.tok with dbar or betabar for the chunk's nv tokens.
+// The token loops of the gain backward take GT tokens at a time: every load
+// of a batch is issued before any of its values is used, so a chunk waits
+// for memory once per batch rather than once per token.
+constexpr int GT = 8;
+
 template <typename IO, bool ISO, int DK>
 __device__ __forceinline__ void gr_token_sums(const BwdArgs& a, GrChunk<DK>& g, size_t kstride,
                                               size_t tok0, size_t tstride, int nv, int i)
 {
-    for (int t = 0; t < nv; ++t) {
-        const size_t tok = tok0 + t * tstride;
-        float kb, kk, al, pp = 0.f, om = 0.f;
-        gr_load<IO, ISO, DK>(a, kstride, tok, i, kb, kk, al, pp, om);
-        if constexpr (!ISO) {
-            const float ph = al * al * pp + om;
-            g.red[t][i] = kb * ph * kk * rcp(a.dd[tok]);  // kapbar kap
-        } else {
-            g.red[t][i] = kb * kk;
+    for (int tb = 0; tb < nv; tb += GT) {
+        float kb[GT], kk[GT], al[GT], pp[GT], om[GT], dd[GT];
+#pragma unroll
+        for (int u = 0; u < GT; ++u) {
+            const size_t tok = tok0 + min(tb + u, nv - 1) * tstride;
+            pp[u] = om[u] = 0.f;
+            gr_load<IO, ISO, DK>(a, kstride, tok, i, kb[u], kk[u], al[u], pp[u], om[u]);
+            dd[u] = ISO ? 1.f : a.dd[tok];
+        }
+#pragma unroll
+        for (int u = 0; u < GT; ++u) {
+            const int t = tb + u;
+            if (t < nv) {
+                if constexpr (!ISO) {
+                    const float ph = al[u] * al[u] * pp[u] + om[u];
+                    g.red[t][i] = kb[u] * ph * kk[u] * rcp(dd[u]);  // kapbar kap
+                } else {
+                    g.red[t][i] = kb[u] * kk[u];
+                }
+            }
         }
     }
     __syncthreads();
@@ -629,28 +645,44 @@ __global__ __launch_bounds__(DK) void kdn_bwd_gr_summary_kernel(BwdArgs args, in
     const size_t tok0 = ((size_t)b * T + t0) * H + h, tstride = H;
     gr_token_sums<IO, ISO, DK>(a, g, kstride, tok0, tstride, nv, i);
     float A = 1.f, Bc = 0.f;
-    for (int t = nv - 1; t >= 0; --t) {
-        const size_t tok = tok0 + t * tstride;
-        const float rt = a.r[tok];
-        float At, Bt;
-        if constexpr (!ISO) {
-            float kb, kk, al, pp, om;
-            gr_load<IO, ISO, DK>(a, kstride, tok, i, kb, kk, al, pp, om);
-            const float d = a.dd[tok], ph = al * al * pp + om;
-            const float den = 1.f + (mu / rt) * kk * kk * ph;
-            const float inv2 = rcp(den * den);
-            At = al * al * inv2;
-            Bt = al * al * (kb * kk * rcp(d) + g.tok[t] * kk * kk);
-        } else {
-            const float4 gs = *reinterpret_cast<const float4*>(a.gsc + tok * 4);
-            const float bhat = gs.z * gs.y + a.omega[tok], n = gs.w;
-            const float e = rt + bhat * n;
-            const float den = 1.f + mu * n / ((float)DK * rt) * bhat;
-            At = gs.z * rcp(den * den);
-            Bt = gs.z * g.tok[t] * rt * rcp(e * e);
+    for (int tb = nv - 1; tb >= 0; tb -= GT) {
+        // the batch's loads (tokens tb, tb - 1, .., clamped at 0), then its maps
+        float rt[GT], kb[GT], kk[GT], al[GT], pp[GT], om[GT], dd[GT];
+        float4 gs[GT];
+#pragma unroll
+        for (int u = 0; u < GT; ++u) {
+            const size_t tok = tok0 + max(tb - u, 0) * tstride;
+            rt[u] = a.r[tok];
+            if constexpr (!ISO) {
+                gr_load<IO, ISO, DK>(a, kstride, tok, i, kb[u], kk[u], al[u], pp[u], om[u]);
+                dd[u] = a.dd[tok];
+            } else {
+                gs[u] = *reinterpret_cast<const float4*>(a.gsc + tok * 4);
+                om[u] = a.omega[tok];
+            }
         }
-        A = At * A;
-        Bc = At * Bc + Bt;
+#pragma unroll
+        for (int u = 0; u < GT; ++u) {
+            const int t = tb - u;
+            if (t < 0)
+                break;
+            float At, Bt;
+            if constexpr (!ISO) {
+                const float ph = al[u] * al[u] * pp[u] + om[u];
+                const float den = 1.f + (mu / rt[u]) * kk[u] * kk[u] * ph;
+                const float inv2 = rcp(den * den);
+                At = al[u] * al[u] * inv2;
+                Bt = al[u] * al[u] * (kb[u] * kk[u] * rcp(dd[u]) + g.tok[t] * kk[u] * kk[u]);
+            } else {
+                const float bhat = gs[u].z * gs[u].y + om[u], n = gs[u].w;
+                const float e = rt[u] + bhat * n;
+                const float den = 1.f + mu * n / ((float)DK * rt[u]) * bhat;
+                At = gs[u].z * rcp(den * den);
+                Bt = gs[u].z * g.tok[t] * rt[u] * rcp(e * e);
+            }
+            A = At * A;
+            Bc = At * Bc + Bt;
+        }
     }
     const size_t width = ISO ? 1 : DK;
     if (!ISO || i == 0) {
@@ -724,33 +756,54 @@ __global__ __launch_bounds__(DK) void kdn_bwd_gr_replay_kernel(BwdArgs args, int
     const size_t width = ISO ? 1 : DK;
     float gbar = a.gr_carry[((size_t)bh * nchunks + c) * width + (ISO ? 0 : i)];
     float mub = 0.f;
-    for (int t = nv - 1; t >= 0; --t) {
+    for (int tb = nv - 1; tb >= 0; tb -= GT) {
+      // the batch's loads (tokens tb, tb - 1, .., clamped at 0), then its tokens
+      float rt_[GT], kb_[GT], kk_[GT], al_[GT], pp_[GT], om_[GT], kmb_[GT], amb_[GT], dd_[GT];
+      float4 gs_[GT];
+#pragma unroll
+      for (int u = 0; u < GT; ++u) {
+          const size_t tok = tok0 + max(tb - u, 0) * tstride, e = tok * DK + i;
+          rt_[u] = a.r[tok];
+          pp_[u] = om_[u] = 0.f;
+          gr_load<IO, ISO, DK>(a, kstride, tok, i, kb_[u], kk_[u], al_[u], pp_[u], om_[u]);
+          kmb_[u] = a.part[2 * kstride + e];
+          amb_[u] = a.part[3 * kstride + e];
+          if constexpr (!ISO) {
+              dd_[u] = a.dd[tok];
+          } else {
+              gs_[u] = *reinterpret_cast<const float4*>(a.gsc + tok * 4);
+              om_[u] = a.omega[tok];
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < GT; ++u) {
+        const int t = tb - u;
+        if (t < 0)
+            break;
         const size_t tok = tok0 + t * tstride, e = tok * DK + i;
-        const float rt = a.r[tok];
-        float kb, kk, al, pp = 0.f, om = 0.f;
-        gr_load<IO, ISO, DK>(a, kstride, tok, i, kb, kk, al, pp, om);
-        const float kmb = a.part[2 * kstride + e], amb = a.part[3 * kstride + e];
+        const float rt = rt_[u], kb = kb_[u], kk = kk_[u], al = al_[u], pp = pp_[u], om = om_[u];
+        const float kmb = kmb_[u], amb = amb_[u];
         if constexpr (!ISO) {
-            const float d = a.dd[tok], dbar = g.tok[t];
+            const float d = dd_[u], dbar = g.tok[t];
             const float ph = al * al * pp + om;
-            const float u = (mu / rt) * kk * kk;
-            const float den = 1.f + u * ph, inv2 = rcp(den * den);
+            const float uu = (mu / rt) * kk * kk;
+            const float den = 1.f + uu * ph, inv2 = rcp(den * den);
             const float ub = -gbar * ph * ph * inv2;
             const float phb = gbar * inv2 + kb * kk * rcp(d) + dbar * kk * kk;
             dkg[e] = from_f32<IO>(kmb + 2.f * ub * (mu / rt) * kk + kb * ph * rcp(d) +
                                   2.f * dbar * ph * kk);
             a.galpha[e] = amb + 2.f * phb * al * pp;
             a.gomega[e] = phb;
-            g.red[t][i] = ub * u;
+            g.red[t][i] = ub * uu;
             mub += ub * kk * kk / rt;
             gbar = phb * al * al;
         } else {
-            const float4 gs = *reinterpret_cast<const float4*>(a.gsc + tok * 4);
+            const float4 gs = gs_[u];
             const float beta = gs.x, bprev = gs.y, am = gs.z, n = gs.w, betab = g.tok[t];
-            const float bhat = am * bprev + a.omega[tok];
+            const float bhat = am * bprev + om;
             const float ee = rt + bhat * n;
-            const float u = mu * n / ((float)DK * rt);
-            const float den = 1.f + u * bhat, inv2 = rcp(den * den);
+            const float uu = mu * n / ((float)DK * rt);
+            const float den = 1.f + uu * bhat, inv2 = rcp(den * den);
             const float ub = -gbar * bhat * bhat * inv2;
             const float bhb = gbar * inv2 + betab * rt * rcp(ee * ee);
             const float nb = ub * mu / ((float)DK * rt) - betab * bhat * bhat * rcp(ee * ee);
@@ -759,11 +812,12 @@ __global__ __launch_bounds__(DK) void kdn_bwd_gr_replay_kernel(BwdArgs args, int
             a.galpha[e] = amb + 2.f * abar * al / (float)DK;
             if (i == 0) {
                 a.gomega[tok] = bhb;
-                a.gr[tok] = -ub * u / rt - betab * bhat * rcp(ee * ee);
+                a.gr[tok] = -ub * uu / rt - betab * bhat * rcp(ee * ee);
                 mub += ub * n / ((float)DK * rt);
             }
             gbar = bhb * am;
         }
+      }
     }
     if constexpr (!ISO) {
         __syncthreads();
