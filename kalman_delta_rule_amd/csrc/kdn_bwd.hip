@@ -643,8 +643,54 @@ __global__ __launch_bounds__(DK) void kdn_bwd_gr_summary_kernel(BwdArgs args, in
     const float mu = a.mu_h ? a.mu_h[h] : a.mu;
     const size_t kstride = (size_t)nblk * a.B * T * H * DK;
     const size_t tok0 = ((size_t)b * T + t0) * H + h, tstride = H;
-    gr_token_sums<IO, ISO, DK>(a, g, kstride, tok0, tstride, nv, i);
     float A = 1.f, Bc = 0.f;
+    if constexpr (!ISO) {
+        // One pass over the chunk's data: the token sums' terms and, per
+        // token, the map's pieces At = alpha^2 / den^2, B1 = alpha^2 kapbar k
+        // / d and Ct = alpha^2 k^2 (Bt = B1 + dbar Ct once the sums are in),
+        // kept in registers for the reverse composition.
+        float At[GR_C], B1[GR_C], Ct[GR_C];
+#pragma unroll
+        for (int tb = 0; tb < GR_C; tb += GT) {
+            float kb[GT], kk[GT], al[GT], pp[GT], om[GT], dd[GT], rt[GT];
+#pragma unroll
+            for (int u = 0; u < GT; ++u) {
+                const size_t tok = tok0 + min(tb + u, nv - 1) * tstride;
+                gr_load<IO, ISO, DK>(a, kstride, tok, i, kb[u], kk[u], al[u], pp[u], om[u]);
+                dd[u] = a.dd[tok];
+                rt[u] = a.r[tok];
+            }
+#pragma unroll
+            for (int u = 0; u < GT; ++u) {
+                const int t = tb + u;
+                const float ph = al[u] * al[u] * pp[u] + om[u], id = rcp(dd[u]);
+                if (t < nv)
+                    g.red[t][i] = kb[u] * ph * kk[u] * id;  // kapbar kap
+                const float den = 1.f + (mu / rt[u]) * kk[u] * kk[u] * ph;
+                const float a2 = al[u] * al[u];
+                At[t] = a2 * rcp(den * den);
+                B1[t] = a2 * (kb[u] * kk[u] * id);
+                Ct[t] = a2 * (kk[u] * kk[u]);
+            }
+        }
+        __syncthreads();
+        if (i < nv) {
+            float sum = 0.f;
+            for (int j = 0; j < DK; ++j)
+                sum += g.red[i][j];
+            g.tok[i] = -sum * rcp(a.dd[tok0 + i * tstride]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = GR_C - 1; t >= 0; --t) {
+            if (t < nv) {
+                const float Bt = B1[t] + g.tok[t] * Ct[t];
+                A = At[t] * A;
+                Bc = At[t] * Bc + Bt;
+            }
+        }
+    } else {
+    gr_token_sums<IO, ISO, DK>(a, g, kstride, tok0, tstride, nv, i);
     for (int tb = nv - 1; tb >= 0; tb -= GT) {
         // the batch's loads (tokens tb, tb - 1, .., clamped at 0), then its maps
         float rt[GT], kb[GT], kk[GT], al[GT], pp[GT], om[GT], dd[GT];
@@ -683,6 +729,7 @@ __global__ __launch_bounds__(DK) void kdn_bwd_gr_summary_kernel(BwdArgs args, in
             A = At * A;
             Bc = At * Bc + Bt;
         }
+    }
     }
     const size_t width = ISO ? 1 : DK;
     if (!ISO || i == 0) {
