@@ -257,8 +257,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs the KDN mixer on a single "
-              "MI355X (heads and batch shard across GPUs with no communication); "
+        print("bench.py measures one GPU only: the KDN mixer runs on a single MI355X "
+              "(heads and batch rows would shard across GPUs with no communication); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
