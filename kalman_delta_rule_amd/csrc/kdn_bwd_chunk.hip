@@ -256,7 +256,7 @@ __device__ __forceinline__ void barrier()
 // loads are unconditional, so that the pieces stay in registers.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-template <int NP, int NR, typename Row>
+template <int NP, int NT, int NR, typename Row>
 __device__ __forceinline__ void rows_load(u32x4 (&dst)[NR], const void* src, int esz, int w,
                                           int lane, Row row)
 {
@@ -264,16 +264,16 @@ __device__ __forceinline__ void rows_load(u32x4 (&dst)[NR], const void* src, int
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
         // a wave past the last piece loads the last piece (and stores nothing)
-        const int p = min(64 * w + 256 * j + lane, NP - 1);
+        const int p = min(64 * w + NT * j + lane, NP - 1);
         dst[j] = *reinterpret_cast<const u32x4*>((const char*)src + row(p * per) * esz);
     }
 }
-template <int NP, int NR>
+template <int NP, int NT, int NR>
 __device__ __forceinline__ void rows_store(void* dst, const u32x4 (&src)[NR], int w, int lane)
 {
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
-        const int p0 = 64 * w + 256 * j;
+        const int p0 = 64 * w + NT * j;
         if (p0 < NP)
             reinterpret_cast<u32x4*>(dst)[p0 + lane] = src[j];
     }
@@ -284,15 +284,17 @@ __device__ __forceinline__ void rows_store(void* dst, const u32x4 (&src)[NR], in
 // (E, dO, the factors, T and A only) and writes the adjoint at the start into
 // gS0.  The sequence split of the backward uses it for each segment's adjoint
 // from its own outputs.
-template <typename IO, bool ISO, int DK, bool ADJ>
-__global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
+template <typename IO, bool ISO, int DK, bool ADJ, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
 {
     const BwdArgs a = args;
     using SM = Smem<DK>;
     static_assert(sizeof(SM) <= 160 * 1024, "LDS budget");
     constexpr int LK = SM::LK;
-    constexpr int CT = DK / 64;               // 16-channel tiles per wave
-    constexpr int NCK = DK * NC / (4 * 256);  // chunk-start state pieces (4 floats) per thread
+    constexpr int NT = 64 * NW;               // threads
+    constexpr int CT = DK / (16 * NW);        // 16-channel tiles per wave
+    static_assert(CT >= 1, "a wave holds at least one 16-row tile of the state");
+    constexpr int NCK = DK * NC / (4 * NT);   // chunk-start state pieces (4 floats) per thread
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
     // distances in floats between arrays of equal shape, for choosing one by
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int i16 = lane & 15, g4 = lane >> 4;
     const int col0 = blk * NC;       // first value column of this block
-    const int chw = w * (DK / 4);    // first key channel of this wave's state rows
+    const int chw = w * (DK / NW);   // first key channel of this wave's state rows
     const int nch = (T + C - 1) / C;
     const size_t ntok = (size_t)a.B * T * H;
     const size_t ks = (size_t)nblk * ntok * DK;  // stride between the partial arrays
@@ -322,9 +324,11 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     IO* dvg = reinterpret_cast<IO*>(a.gv);
     // the factors: 256 / DK threads per key channel (one per wave group of
     // DK / 64 waves), each its channel's decays and a share of the tokens
-    constexpr int FP = 256 / DK, FT = C / FP;  // threads per channel, tokens per thread
+    constexpr int FP = NT / DK, FT = C / FP;  // threads per channel, tokens per thread
     const int ch = (w % (DK / 64)) * 64 + lane, fpart = w / (DK / 64);  // fpart wave-uniform
-    const int et = (tid * 4) / NC, ec = (tid * 4) % NC;  // this thread's 4 elements of a [C][NC] block
+    // V and dO: the first 256 threads, 4 elements each of a [C][NC] block
+    const bool vth = tid < C * NC / 4;
+    const int et = (tid * 4) / NC, ec = (tid * 4) % NC;
 
     // The chunk's inputs, loaded one chunk ahead into registers (16 bytes
     // per lane and piece of a row-major [token][channel] array, each wave a
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     // of the wave wait for it: the compiler cannot tell the copy's LDS
     // destination from the arrays the chunk works on.)
     constexpr int NPA = C * DK * 4 / 16, NPK = C * DK * (int)sizeof(IO) / 16;  // pieces per array
-    constexpr int RA = (NPA + 255) / 256, RK = (NPK + 255) / 256;              // per lane
+    constexpr int RA = (NPA + NT - 1) / NT, RK = (NPK + NT - 1) / NT;          // per lane
     u32x4 ra[RA], rp[RA], rk[RK], rq[RK];
     // four consecutive io elements of V and dO, kept packed until they land
     // (unpacking at the load would wait for it)
@@ -351,17 +355,18 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     auto issue = [&](int c, bool rev) {
         const int t0 = c * C, len = min(C, T - t0);
         auto row = [&](int e) { return tok_of(t0 + min(e / DK, len - 1)) * DK + e % DK; };
-        rows_load<NPA>(ra, a.alpha, 4, w, lane, row);
+        rows_load<NPA, NT>(ra, a.alpha, 4, w, lane, row);
         if constexpr (!ISO)
-            rows_load<NPA>(rp, a.kap, 4, w, lane, row);
+            rows_load<NPA, NT>(rp, a.kap, 4, w, lane, row);
         static_assert(2 * C * DK * sizeof(IO) <= sizeof(sm.inK), "staging size");
-        rows_load<NPK>(rk, kg, (int)sizeof(IO), w, lane, row);
+        rows_load<NPK, NT>(rk, kg, (int)sizeof(IO), w, lane, row);
         if (rev)
-            rows_load<NPK>(rq, qg, (int)sizeof(IO), w, lane, row);
+            rows_load<NPK, NT>(rq, qg, (int)sizeof(IO), w, lane, row);
         if constexpr (ISO)
             if (tid < C)
                 braw = a.gsc[tok_of(t0 + min(tid, len - 1)) * 4];
         vok = et < len;
+        // (threads past the block load a clamped in-range row and store nothing)
         const size_t r = tok_of(t0 + min(et, len - 1)) * dv + col0 + ec;
         if (!ADJ)
             vraw = *reinterpret_cast<const Raw4*>(vg + r);
@@ -370,18 +375,20 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     };
     // the issued inputs into LDS (V and dO as fp32); the caller's barrier follows
     auto land = [&](bool rev) {
-        rows_store<NPA>(&sm.inA[0][0], ra, w, lane);
+        rows_store<NPA, NT>(&sm.inA[0][0], ra, w, lane);
         if constexpr (!ISO)
-            rows_store<NPA>(&sm.inP[0][0], rp, w, lane);
-        rows_store<NPK>(&sm.inK[0], rk, w, lane);
+            rows_store<NPA, NT>(&sm.inP[0][0], rp, w, lane);
+        rows_store<NPK, NT>(&sm.inK[0], rk, w, lane);
         if (rev)
-            rows_store<NPK>(reinterpret_cast<char*>(&sm.inK[0]) + C * DK * sizeof(IO), rq, w, lane);
+            rows_store<NPK, NT>(reinterpret_cast<char*>(&sm.inK[0]) + C * DK * sizeof(IO), rq, w, lane);
+        if (vth) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (!ADJ)
-                sm.V[et][ec + j] = vok ? raw_f32(vraw, j) : 0.f;
-            if (rev)
-                sm.dO[et][ec + j] = vok ? raw_f32(oraw, j) : 0.f;
+            for (int j = 0; j < 4; ++j) {
+                if (!ADJ)
+                    sm.V[et][ec + j] = vok ? raw_f32(vraw, j) : 0.f;
+                if (rev)
+                    sm.dO[et][ec + j] = vok ? raw_f32(oraw, j) : 0.f;
+            }
         }
         if constexpr (ISO)
             if (tid < C)
@@ -435,7 +442,7 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     };
     // M = Kb Kt^T, by waves 2 and 3 over half of the key channels each
     auto form_M_parts = [&]() {
-        if (w >= 2) {
+        if (w == 2 || w == 3) {
             const int k0 = (w - 2) * (DK / 2);
             f32x4 m = zero4();
             mmk<DK / 2>(m, &sm.Kb[0][k0], LK, 1, &sm.Kt[0][k0], 1, LK, lane);
@@ -492,7 +499,7 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
                 pw = sq;
             }
             tile_store(&sm.Tm[0][0], LM, tt, lane);
-        } else if (!ADJ) {
+        } else if (!ADJ && w < 4) {
             auto part = [&](auto kc, int k0, float* dst) {
                 constexpr int K = decltype(kc)::value;
 #pragma unroll
@@ -512,6 +519,8 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     };
     // delta = T (V - Kb (c S0)) for column tile w, into LDS
     auto form_delta = [&]() {
+        if (w >= 4)
+            return;
         f32x4 d = zero4();
         float ta[4], rb[4];
 #pragma unroll
@@ -611,7 +620,7 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
     state_init(a.gS_T);
     // this block's chunk-start states, loaded one chunk ahead with the inputs
     // Thread (tid / 16, tid % 16) takes the four columns 4 (tid % 16) .. + 3
-    // of row quads tid / 16 + 16 jq: four 16-byte pieces per quad, which it
+    // of row quads tid / 16 + (NT / 16) jq: four 16-byte pieces per quad, which it
     // writes to LDS as four 16-byte rows (a 4 x 4 transpose in registers).
     static_assert(NCK % 4 == 0 && NC == 64, "chunk-start state pieces");
     f32x4 ck[NCK];
@@ -623,7 +632,7 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             for (int jq = 0; jq < NCK / 4; ++jq)
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    ck[4 * jq + u] = src[(ck_rq + 16 * jq) * NC + 4 * ck_cg + u];
+                    ck[4 * jq + u] = src[(ck_rq + (NT / 16) * jq) * NC + 4 * ck_cg + u];
         }
         issue(c, true);
     };
@@ -640,7 +649,7 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
             for (int jq = 0; jq < NCK / 4; ++jq)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = 4 * (ck_rq + 16 * jq) + r;
+                    const int row = 4 * (ck_rq + (NT / 16) * jq) + r;
                     const f32x4 v{ck[4 * jq][r], ck[4 * jq + 1][r], ck[4 * jq + 2][r], ck[4 * jq + 3][r]};
                     *reinterpret_cast<f32x4*>(&sm.S0[row][4 * ck_cg]) = v * sm.cS[row];
                 }
@@ -684,39 +693,41 @@ __global__ __launch_bounds__(256, 1) void kdn_bwd_chunk_kernel(BwdArgs args)
                     }
                 }
             }
-            f32x4 acc[1];
-            acc[0] = zero4();
-            // T^T for dR = T^T ddelta, read ahead: A(m, k) = T(k, m), k = 4 g + r
-            float tA[4];
+            if (w < 4) {  // ddelta and dR: one column tile per wave of the first four
+                f32x4 acc[1];
+                acc[0] = zero4();
+                // T^T for dR = T^T ddelta, read ahead: A(m, k) = T(k, m), k = 4 g + r
+                float tA[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                tA[r] = sm.Tm[4 * g4 + r][i16];
-            mm_stream<DK / 4 + C / 4>(
-                acc,
-                [&](int st, float& av, float& bv, float& cv) {
-                    if (st < DK / 4) {  // Kt E = (Kt G'_15) dS_C
-                        const int k = 4 * st + g4;
-                        av = sm.Kt[i16][k];
-                        cv = sm.gL[k];
-                        bv = sm.E[k][16 * w + i16];
-                    } else {  // A^T dO
-                        const int k = 4 * (st - DK / 4) + g4;
-                        av = sm.Am[k][i16];
-                        bv = sm.dO[k][16 * w + i16];
-                    }
-                },
-                [&](int) { return 0; }, [&](int st) { return st < DK / 4; });
-            // dR = T^T ddelta, ddelta's accumulator as the B operand
-            f32x4 dR = zero4();
+                for (int r = 0; r < 4; ++r)
+                    tA[r] = sm.Tm[4 * g4 + r][i16];
+                mm_stream<DK / 4 + C / 4>(
+                    acc,
+                    [&](int st, float& av, float& bv, float& cv) {
+                        if (st < DK / 4) {  // Kt E = (Kt G'_15) dS_C
+                            const int k = 4 * st + g4;
+                            av = sm.Kt[i16][k];
+                            cv = sm.gL[k];
+                            bv = sm.E[k][16 * w + i16];
+                        } else {  // A^T dO
+                            const int k = 4 * (st - DK / 4) + g4;
+                            av = sm.Am[k][i16];
+                            bv = sm.dO[k][16 * w + i16];
+                        }
+                    },
+                    [&](int) { return 0; }, [&](int st) { return st < DK / 4; });
+                // dR = T^T ddelta, ddelta's accumulator as the B operand
+                f32x4 dR = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dR = __builtin_amdgcn_mfma_f32_16x16x4f32(tA[r], acc[0][r], dR, 0, 0, 0);
-            tile_store(&sm.mR[0][16 * w], LC, -dR, lane);
+                for (int r = 0; r < 4; ++r)
+                    dR = __builtin_amdgcn_mfma_f32_16x16x4f32(tA[r], acc[0][r], dR, 0, 0, 0);
+                tile_store(&sm.mR[0][16 * w], LC, -dR, lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g4 + r;
-                if (!ADJ && t < len)
-                    dvg[tok_of(t0 + t) * dv + col0 + 16 * w + i16] = from_f32<IO>(dR[r]);
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * g4 + r;
+                    if (!ADJ && t < len)
+                        dvg[tok_of(t0 + t) * dv + col0 + 16 * w + i16] = from_f32<IO>(dR[r]);
+                }
             }
         }
         barrier();  // -dR; every wave's reads of all E rows done
@@ -970,18 +981,25 @@ __global__ __launch_bounds__(DK) void kdn_bwd_chunk_finish_kernel(BwdArgs args, 
 template <typename IO, bool ISO, int DK>
 static hipError_t launch_t(const BwdArgs& a, bool adj, hipStream_t stream)
 {
-    auto kern = kdn_bwd_chunk_kernel<IO, ISO, DK, false>;
+    // four waves; the adjoint-only mode at d_k = 128 runs eight (two per
+    // SIMD, 16 state rows each: its register set fits the 256 of two waves
+    // per SIMD, the full pass's does not)
+    constexpr int NWA = DK == 128 ? 8 : 4;
+    auto kern = kdn_bwd_chunk_kernel<IO, ISO, DK, false, 4>;
+    int nw = 4;
     if (adj) {  // the sequence split runs Diagonal with bf16 io only
-        if constexpr (sizeof(IO) == 2 && !ISO)
-            kern = kdn_bwd_chunk_kernel<IO, ISO, DK, true>;
-        else
+        if constexpr (sizeof(IO) == 2 && !ISO) {
+            kern = kdn_bwd_chunk_kernel<IO, ISO, DK, true, NWA>;
+            nw = NWA;
+        } else {
             return hipErrorInvalidValue;
+        }
     }
     const size_t smem = sizeof(Smem<DK>);
     hipError_t e = set_lds_limit_once(kern, smem);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(kern, dim3(a.dv / NC, a.B * a.H), dim3(256), smem, stream, a);
+    hipLaunchKernelGGL(kern, dim3(a.dv / NC, a.B * a.H), dim3(64 * nw), smem, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
