@@ -133,27 +133,59 @@ def test_bwd_empty_sequence_passes_adjoints_through():
 
 
 # ---------------------------------------------------------------------------
-# full workloads, sampled (batch, head) problems: the backward of the launch
-# configuration bench.py --bwd times, against the oracle on each sampled
-# head's own slice (heads are independent problems)
+# full workloads: the backward of the launch configuration bench.py --bwd
+# times.  Configs 1 and 2 are compared whole (the oracle runs the whole batch;
+# every (b, h) problem is independent); config 3 keeps every state of a
+# 65536-token head in the oracle (8.6 GB each), so there one head is compared.
 # ---------------------------------------------------------------------------
-def _bwd_full(ora, widx, n_heads, heads=None):
-    from kdn_testutil import sample_heads
-    w = inputs.workload(widx)
+GRADS = ("dq", "dk", "dv", "dalpha", "domega", "dr")
+
+
+def _full_inputs(w):
     x = dict(inputs.make_fwd_inputs(w))
     for n in ("S0", "p0", "b0"):
         x.pop(n, None)
     rng = np.random.default_rng(w.seed + 77)
     do = rng.standard_normal((w.B, w.T, w.H, w.dv)).astype(np.float32)
     x["do"] = inputs.round_bf16(do) if w.io == "bf16" else do
+    return x
+
+
+def _bwd_whole(ora, widx):
+    """Every element of every gradient against the oracle run on the whole
+    batch, by relative L2 over the whole tensor; the worst single (b, h)
+    problem of each gradient is printed, and held to the same bar for all
+    but dmu (one number per problem, printed only)."""
+    from kdn_testutil import per_head_rel
+    w = inputs.workload(widx)
+    x = _full_inputs(w)
     g = _run(w.variant, w.io, x)
-    heads = heads or sample_heads(w.B, w.H, n_heads, seed=100 + widx)
+    for n in GRADS:
+        assert np.isfinite(g[n]).all(), n
+    ref = ora.bwd(w.variant, *[x[n] for n in ("q", "k", "v", "alpha", "omega", "r", "do")])
+    del x
+    err = {n: rel_l2(g[n], ref[n]) for n in GRADS + ("dS0", "dvar0", "dmu")}
+    worst = {n: float(per_head_rel(g[n], ref[n], (0, 2)).max()) for n in GRADS}
+    for n in ("dS0", "dvar0", "dmu"):
+        worst[n] = float(per_head_rel(g[n], ref[n], (0, 1)).max())
+    fmt = lambda d: {k: "%.2e" % v for k, v in d.items()}
+    print("bwd %s whole-tensor rel-L2 %s; worst (b,h) %s" % (w.name, fmt(err), fmt(worst)),
+          flush=True)
+    assert max(err.values()) <= TOL[w.io], err
+    worst.pop("dmu")
+    assert max(worst.values()) <= TOL[w.io], worst
+
+
+def _bwd_heads(ora, widx, heads):
+    w = inputs.workload(widx)
+    x = _full_inputs(w)
+    g = _run(w.variant, w.io, x)
     sl = lambda a, b, h: np.ascontiguousarray(a[b:b + 1, :, h:h + 1])
     refs = {bh: ora.bwd(w.variant, *[sl(x[n], *bh) for n in ("q", "k", "v", "alpha", "omega", "r",
                                                               "do")])
             for bh in heads}
     err = {}
-    for n in ("dq", "dk", "dv", "dalpha", "domega", "dr"):
+    for n in GRADS:
         err[n] = rel_l2(np.concatenate([sl(g[n], *bh).ravel() for bh in heads]),
                         np.concatenate([refs[bh][n].ravel() for bh in heads]))
     for n in ("dS0", "dvar0", "dmu"):
@@ -162,24 +194,23 @@ def _bwd_full(ora, widx, n_heads, heads=None):
     print("bwd %s heads=%s errors %s" % (w.name, heads, {k: "%.2e" % v for k, v in err.items()}),
           flush=True)
     assert max(err.values()) <= TOL[w.io], err
-    for n in ("dq", "dk", "dv", "dalpha", "domega", "dr"):
+    for n in GRADS:
         assert np.isfinite(g[n]).all(), n
 
 
 @pytest.mark.timeout(400)
 def test_bwd_config2_diag_full(ora):
-    _bwd_full(ora, 2, 3)
+    _bwd_whole(ora, 2)
 
 
 @pytest.mark.timeout(400)
 def test_bwd_config1_iso_full(ora):
-    _bwd_full(ora, 1, 3)
+    _bwd_whole(ora, 1)
 
 
 @pytest.mark.timeout(600)
 def test_bwd_config3_long_full(ora):
-    # T = 65536: one head (the oracle keeps every state, 8.6 GB for it)
-    _bwd_full(ora, 3, 1, heads=[(0, 11)])
+    _bwd_heads(ora, 3, heads=[(0, 11)])
 
 
 @pytest.mark.parametrize("regime,io", [("mu0", "f32"), ("slow_decay", "f32"), ("fast_decay", "f32"),
