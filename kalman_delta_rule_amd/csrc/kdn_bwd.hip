@@ -742,44 +742,78 @@ __global__ __launch_bounds__(DK) void kdn_bwd_gr_summary_kernel(BwdArgs args, in
 }
 
 // pass 2: the gradient after every chunk's last token, from the last chunk;
-// the initial variance's gradient at the end.  The chain is serial in the
-// chunks, but its maps are not: they are read GU chunks ahead into a second
-// register set while the current GU are applied, so a long sequence waits
-// for memory once per GU chunks rather than once per chunk.
-constexpr int GU = 16;
-__global__ __launch_bounds__(256) void kdn_bwd_gr_carry_kernel(BwdArgs args, int width, int nchunks)
+// the initial variance's gradient at the end.  One lane per row ((b,h) and
+// channel), up to GR_WAVES wavefronts per workgroup, each over its own
+// contiguous run of chunks.  Every wave but the first composes its run's
+// maps into one (g -> A g + B, the run's last chunk applied first); the
+// waves exchange those through LDS, so that each applies the runs after its
+// own to the final gradient; then every wave walks its run again, writing
+// the gradient each chunk receives.  Two serial passes over nchunks / waves
+// maps instead of one over nchunks.  Inside a run the maps are read GU chunks
+// ahead into a second register set while the current GU are applied.
+constexpr int GU = 16, GR_WAVES = 8;
+
+// Walk chunks c_end - 1 down to c_begin of one row (maps and out point at the
+// row's chunk 0, chunk c at c * width) from m = (A, B): m <- (A_c A, A_c B +
+// B_c).  From (1, 0) that composes the run's maps; from (1, g) its second
+// component is the carried gradient, stored (when STORE) as each chunk's
+// before that chunk's map is applied.
+template <bool STORE>
+__device__ __forceinline__ float2 gr_run(const float2* maps, float* out, size_t width, int c_begin,
+                                         int c_end, float2 m)
 {
-    const BwdArgs a = args;
-    const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;  // (b,h) * width + channel
-    if (row >= (size_t)a.B * a.H * width)
-        return;
-    const size_t bh = row / width, i = row % width;
-    const float2* maps = reinterpret_cast<const float2*>(a.gr_sum);
-    auto at = [&](int c) { return (bh * nchunks + c) * width + i; };
     float2 cur[GU], nxt[GU];
     auto fetch = [&](float2 (&dst)[GU], int top) {
 #pragma unroll
         for (int u = 0; u < GU; ++u)
-            dst[u] = top - u >= 0 ? maps[at(top - u)] : make_float2(1.f, 0.f);
+            dst[u] = top - u >= c_begin ? maps[(size_t)(top - u) * width] : make_float2(1.f, 0.f);
     };
-    float gbar = a.gvar_T ? a.gvar_T[row] : 0.f;
-    fetch(cur, nchunks - 1);
-    for (int top = nchunks - 1; top >= 0; top -= GU) {
-        if (top - GU >= 0)
+    if (c_begin < c_end)
+        fetch(cur, c_end - 1);
+    for (int top = c_end - 1; top >= c_begin; top -= GU) {
+        if (top - GU >= c_begin)
             fetch(nxt, top - GU);
 #pragma unroll
         for (int u = 0; u < GU; ++u) {
-            if (top - u >= 0) {
-                a.gr_carry[at(top - u)] = gbar;
-                gbar = cur[u].x * gbar + cur[u].y;
+            if (top - u >= c_begin) {
+                if constexpr (STORE)
+                    out[(size_t)(top - u) * width] = m.y;
+                m = make_float2(cur[u].x * m.x, cur[u].x * m.y + cur[u].y);
             }
         }
 #pragma unroll
         for (int u = 0; u < GU; ++u)
             cur[u] = nxt[u];
     }
-    if (a.gvar0)
-        a.gvar0[row] = gbar;
+    return m;
+}
+
+__global__ __launch_bounds__(64 * GR_WAVES) void kdn_bwd_gr_carry_kernel(BwdArgs args, int width,
+                                                                        int nchunks)
+{
+    const BwdArgs a = args;
+    __shared__ float2 run_map[GR_WAVES][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+    const size_t rows = (size_t)a.B * a.H * width, r = (size_t)blockIdx.x * 64 + lane;
+    const bool live = r < rows;
+    const size_t row = live ? r : 0;  // lanes past the last row read row 0 and store nothing
+    const size_t base = (row / width * nchunks) * width + row % width;
+    const int per = (nchunks + nwave - 1) / nwave;
+    const int c_begin = min(nchunks, wv * per), c_end = min(nchunks, c_begin + per);
+    const float2* maps = reinterpret_cast<const float2*>(a.gr_sum) + base;
+    const float2 id = make_float2(1.f, 0.f);
+    run_map[wv][lane] = wv > 0 ? gr_run<false>(maps, nullptr, width, c_begin, c_end, id) : id;
+    __syncthreads();
+    float g = live && a.gvar_T ? a.gvar_T[row] : 0.f;
+    for (int w2 = nwave - 1; w2 > wv; --w2) {
+        const float2 m = run_map[w2][lane];
+        g = m.x * g + m.y;
+    }
+    float2 e = id;
+    if (live)
+        e = gr_run<true>(maps, a.gr_carry + base, width, c_begin, c_end, make_float2(1.f, g));
+    if (live && wv == 0 && a.gvar0)
+        a.gvar0[row] = e.y;
 }
 
 // pass 3: replay every chunk from its carried gradient, writing dk, dalpha,
@@ -998,7 +1032,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream)
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL(kdn_bwd_gr_carry_kernel, dim3((bh * width + 255) / 256), dim3(256), 0,
+    // one wave per run of at least 64 chunks, up to GR_WAVES
+    const int nwave = std::min(GR_WAVES, std::max(1, ngc / 64));
+    hipLaunchKernelGGL(kdn_bwd_gr_carry_kernel, dim3((bh * width + 63) / 64), dim3(64 * nwave), 0,
                        stream, a, width, ngc);
     e = hipGetLastError();
     if (e != hipSuccess)

@@ -12,7 +12,7 @@ namespace kdn {
 constexpr int GAIN_CHUNK = 64;  // tokens per gain-scan chunk
 constexpr int BWD_L = 16;       // backward: tokens per recompute chunk (checkpoint spacing)
 constexpr int BWD_COLS = 16;    // backward: value columns per memory workgroup
-constexpr int GR_C = 64;        // backward: tokens per chunk of the gain backward's affine scan
+constexpr int GR_C = 32;        // backward: tokens per chunk of the gain backward's affine scan
 constexpr int SP_MAX = 8;       // split over the sequence: segments at most
 constexpr size_t GAIN_STATIC_FLOATS = (size_t)8 << 20;  // the static gain-scan scratch (32 MiB)
 

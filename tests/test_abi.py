@@ -366,9 +366,11 @@ def test_bwd_validation(L):
         common = (r64(B * H * nch * dk * dv) + (0 if chunked else r64(ntok * dv))
                   + r64(4 * nblk * ntok * dk))
         scan = lambda width: r64(B * H * 1 * width * 5)  # the gain scan: one 64-token chunk
-        # the gain backward's scan: (A, B) and carry per chunk and width, a
-        # scalar per token, an information-scale part per chunk
-        grad = lambda width: r64(B * H * width * 2) + r64(B * H * width) + r64(ntok) + r64(B * H)
+        # the gain backward's scan over 32-token chunks (two here): (A, B) and
+        # carry per chunk and width, a scalar per token, an information-scale
+        # part per chunk
+        grad = lambda width: (r64(B * H * 2 * width * 2) + r64(B * H * 2 * width) + r64(ntok)
+                              + r64(B * H * 2))
         # Diagonal chunked: the checkpoint walk's final state and variance
         walk = r64(B * H * dk * dv) + r64(B * H * dk) if chunked else 0
         diag = 2 * r64(ntok * dk) + r64(ntok) + scan(dk) + grad(dk) + common + walk
@@ -380,12 +382,12 @@ def test_bwd_validation(L):
     # long T) adds two variance planes and six state planes of the segments
     # (config 3's shape: 8 segments; T = 2048 with 16 or 64 heads: 2)
     def base(iso, B, T, H, dk, dv):
-        ntok, nch, ngc = B * T * H, (T + 15) // 16, (T + 63) // 64
+        ntok, nch, ngc, ngr = B * T * H, (T + 15) // 16, (T + 63) // 64, (T + 31) // 32
         width = 1 if iso else dk
         pieces = r64(ntok * 4) if iso else 2 * r64(ntok * dk) + r64(ntok)
         walk = 0 if iso else r64(B * H * dk * dv) + r64(B * H * dk)
-        return (pieces + r64(B * H * ngc * width * 5) + r64(B * H * ngc * width * 2)
-                + r64(B * H * ngc * width) + r64(ntok) + r64(B * H * ngc)
+        return (pieces + r64(B * H * ngc * width * 5) + r64(B * H * ngr * width * 2)
+                + r64(B * H * ngr * width) + r64(ntok) + r64(B * H * ngr)
                 + r64(B * H * nch * dk * dv) + r64(4 * (dv // 64) * ntok * dk) + walk)
     for (B, T, H, d, S) in ((1, 65536, 16, 128, 8), (1, 2048, 16, 128, 2), (4, 2048, 16, 128, 2),
                             (1, 8192, 1, 64, 8), (1, 4096, 2, 64, 4)):

@@ -118,6 +118,15 @@ def test_bwd_per_head_mu_c0_without_state(ora, variant):
     _check(g, ref, "bf16", (variant, "mu_h c0_h"))
 
 
+@pytest.mark.parametrize("variant,T", [("diag", 4100), ("iso", 4100), ("diag", 8230)])
+def test_bwd_long_gain_carry_runs(ora, variant, T):
+    # sequences whose 32-token gain-backward chunks (129 and 258 of them)
+    # split into two and four uneven runs for the carry pass, ragged last
+    # chunk included; fp32 io, so the bar is the tight one
+    x = _case(variant, "f32", 1, T, 2, 64, 64, seed=700 + T)
+    _check(_run(variant, "f32", x), _oracle(ora, variant, x), "f32", (variant, T))
+
+
 def test_bwd_empty_sequence_passes_adjoints_through():
     B, H, dk, dv = 2, 2, 128, 64
     z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt, device="cuda")
