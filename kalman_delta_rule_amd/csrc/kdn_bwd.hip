@@ -647,9 +647,14 @@ __global__ __launch_bounds__(DK) void kdn_bwd_gr_summary_kernel(BwdArgs args, in
     if constexpr (!ISO) {
         // One pass over the chunk's data: the token sums' terms and, per
         // token, the map's pieces At = alpha^2 / den^2, B1 = alpha^2 kapbar k
-        // / d and Ct = alpha^2 k^2 (Bt = B1 + dbar Ct once the sums are in),
-        // kept in registers for the reverse composition.
-        float At[GR_C], B1[GR_C], Ct[GR_C];
+        // / d and Ct = alpha^2 k^2 (Bt = B1 + dbar Ct once the sums are in).
+        // The composite is A = prod_t At and B = sum_t Q_t Bt with Q_t the
+        // product of At over the tokens before t, so it is formed in token
+        // order: Q, sum_t Q_t B1 and the weights W_t = Q_t Ct run along, and
+        // sum_t W_t dbar_t is added once the sums are in (one register per
+        // token rather than three).
+        float W[GR_C];
+        float Q = 1.f, Bq = 0.f;
 #pragma unroll
         for (int tb = 0; tb < GR_C; tb += GT) {
             float kb[GT], kk[GT], al[GT], pp[GT], om[GT], dd[GT], rt[GT];
@@ -668,9 +673,12 @@ __global__ __launch_bounds__(DK) void kdn_bwd_gr_summary_kernel(BwdArgs args, in
                     g.red[t][i] = kb[u] * ph * kk[u] * id;  // kapbar kap
                 const float den = 1.f + (mu / rt[u]) * kk[u] * kk[u] * ph;
                 const float a2 = al[u] * al[u];
-                At[t] = a2 * rcp(den * den);
-                B1[t] = a2 * (kb[u] * kk[u] * id);
-                Ct[t] = a2 * (kk[u] * kk[u]);
+                W[t] = 0.f;
+                if (t < nv) {
+                    W[t] = Q * (a2 * (kk[u] * kk[u]));
+                    Bq += Q * (a2 * (kb[u] * kk[u] * id));
+                    Q *= a2 * rcp(den * den);
+                }
             }
         }
         __syncthreads();
@@ -681,14 +689,12 @@ __global__ __launch_bounds__(DK) void kdn_bwd_gr_summary_kernel(BwdArgs args, in
             g.tok[i] = -sum * rcp(a.dd[tok0 + i * tstride]);
         }
         __syncthreads();
+        A = Q;
+        Bc = Bq;
 #pragma unroll
-        for (int t = GR_C - 1; t >= 0; --t) {
-            if (t < nv) {
-                const float Bt = B1[t] + g.tok[t] * Ct[t];
-                A = At[t] * A;
-                Bc = At[t] * Bc + Bt;
-            }
-        }
+        for (int t = 0; t < GR_C; ++t)
+            if (t < nv)
+                Bc += W[t] * g.tok[t];
     } else {
     gr_token_sums<IO, ISO, DK>(a, g, kstride, tok0, tstride, nv, i);
     for (int tb = nv - 1; tb >= 0; tb -= GT) {
